@@ -430,7 +430,10 @@ static int run_unit(const layer_cfg *c, long P0,
         double ms = 0.0;
         for (int ch = 0; ch < d_v; ch++) ms += r[ch] * r[ch];
         ms /= d_v;
-        const double inv = 1.0 / sqrt(ms + c->eps_norm);
+        /* An all-zero read with eps_norm = 0 is 0/0; its output is taken as
+         * zero, the value every eps_norm > 0 gives for a zero read. */
+        const double den = ms + c->eps_norm;
+        const double inv = den > 0.0 ? 1.0 / sqrt(den) : 0.0;
         const float *gt = g + th * d_v;
         float *ot = out + th * d_v;
         for (int ch = 0; ch < d_v; ch++) {

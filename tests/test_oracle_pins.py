@@ -693,3 +693,20 @@ def test_state_access_accounting_golden(orc):
     top8 = g["cases"][0]
     ratio = g["mamba2_340M_active_M_elems"] / (top8["total_M_elems"] * 16 / M)
     assert round(ratio) == g["ratio_to_mamba2_340M_top8"]
+
+
+def test_zero_read_with_zero_eps_is_zero(orc):
+    """A token whose read slots are all still empty reads r = 0; with
+    eps_norm = 0 the RMSNorm is 0/0 and the output is taken as 0, the value
+    any eps_norm > 0 gives for a zero read."""
+    d_v = 8
+    S = np.zeros((1, 1, 16, d_v), np.float32)
+    m = np.zeros((1, 1, 16), np.float32)
+    gi = _given(1, 1, 1, 1, [3], [0.5], [9], [0.7])   # read an unwritten slot
+    g = rng(40).standard_normal((1, 1, 1, d_v)).astype(np.float32)
+    for eps in (0.0, 1e-6):
+        out = orc.scan_given(*gi, np.ones((1, 1, 1, d_v), np.float32),
+                             np.zeros((1, 1, 1), np.float32), g, S.copy(),
+                             m.copy(), d_p=4, U=2, state_bf16=False,
+                             eps_norm=eps)
+        assert np.array_equal(out, np.zeros_like(out))
