@@ -1,0 +1,310 @@
+"""Benchmark of the RAM-Net layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for a prefill workload, one ramnet_scan_prefill call (address decoding for
+every token, CAPE, the Gated Sparse Update, read, RMSNorm and gate over all
+B x T x H token-heads); for the decode workload, one ramnet_step_decode call
+(one token for each of B sequences, all heads).  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload prefill_top8|prefill_top32|large_state|decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("tokens/sec per RAM-Net layer (prefill scan + decode step), "
+          "% of HBM roofline")
+HBM_PEAK_GBS = 8000.0
+
+
+def byte_model(w, kind: str):
+    """Algorithmic bytes per launch of each kernel (what the method must
+    move, per the token-head byte model; no address round trip, no re-reads).
+      decode_addresses: q and k logits, 2*U*d_p*b_in per token-head.
+      scan:             v, g (2*d_v*b_in), gamma (b_in) in, out (d_v*b_s),
+                        plus the state and mass read and written once per
+                        (batch, head) unit when it is held on chip, or the
+                        touched rows (3*K*d_v*b_s + 2*K*4 per token-head)
+                        when it is updated in HBM.
+    """
+    b_in = 2 if w.in_dtype == "bf16" else 4
+    b_s = 2 if w.state_dtype == "bf16" else 4
+    T = 1 if kind == "decode" else w.T
+    n = w.B * T * w.H
+    units = w.B * w.H
+    dec = n * 2 * w.L * b_in
+    io = n * (2 * w.d_v * b_in + b_in + w.d_v * b_s)
+    once = units * 2 * (w.M * w.d_v * b_s + 4 * w.M)
+    rows = n * (3 * w.K * w.d_v * b_s + 2 * w.K * 4)
+    # The state is read and written once per launch if that is smaller than
+    # the rows the token-heads touch (prefill of a small state); otherwise
+    # only the touched rows count (decode, large state).
+    state = min(once, rows)
+    return {"decode_addresses": dec, "scan": io + state,
+            "total": dec + io + state, "state_term": state}
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def cpu_baseline(w, kind: str, budget_s: float = 12.0):
+    """Times the CPU oracle (as it is: brute-force Top-K, fp64, OpenMP over
+    (batch, head) units) on a bounded sample of the same workload: a prefix
+    of the sequences sized to about `budget_s` seconds, or the whole batch
+    when that is cheaper; reports tokens/s."""
+    import oracle
+    from sparse_slot_recurrent_amd import synth
+    oracle.load()
+    threads = oracle.max_threads()
+    sb = w.state_dtype == "bf16"
+    if kind == "decode":
+        steps = 0
+        S = m = pos = None
+        t_all = 0.0
+        x0 = synth.make_inputs(w, T=1)
+        S, m, pos = x0["S0"].copy(), x0["m0"].copy(), x0["pos0"].copy()
+        while t_all < budget_s and steps < w.steps:
+            s = synth.make_decode_step(w, steps)
+            a = {n: s[n][:, None] for n in s}
+            t0 = time.perf_counter()
+            oracle.layer(a["q"], a["k"], a["v"], a["gamma"], a["g"], S, m,
+                         d_p=w.d_p, U=w.U, K=w.K, state_bf16=sb, pos0=pos,
+                         want_addresses=False)
+            t_all += time.perf_counter() - t0
+            pos = pos + 1
+            steps += 1
+        return {"value": w.B * steps / t_all, "unit": "tokens/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{steps} decode steps of all {w.B} sequences x "
+                          f"{w.H} heads, {t_all:.1f} s of oracle time",
+                "cpu": cpu_info()}
+    H = w.H
+    B = max(1, min(w.B, threads // H))
+    T = min(w.T, 64)
+    while True:
+        x = synth.make_inputs(w, B=B, T=T, H=H)
+        S, m = x["S0"].copy(), x["m0"].copy()
+        t0 = time.perf_counter()
+        oracle.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S, m,
+                     d_p=w.d_p, U=w.U, K=w.K, state_bf16=sb, pos0=x["pos0"],
+                     want_addresses=False)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or (T == w.T and B == w.B):
+            break
+        grow = max(2.0, min(8.0, budget_s / 2 / max(dt, 1e-3)))
+        if T < w.T:
+            T = min(w.T, int(T * grow))
+        else:
+            B = min(w.B, int(B * grow) + 1)
+    return {"value": B * T / dt, "unit": "tokens/s",
+            "cores": min(threads, B * H), "kind": "oracle",
+            "sample": f"B={B} x T={T} tokens x {H} heads of the workload "
+                      f"(brute-force Top-K, fp64), {dt:.1f} s",
+            "cpu": cpu_info()}
+
+
+def to_dev(torch, a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def time_loop(torch, fn, steps):
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        fn(i)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(torch, rn, w, steps, warmup):
+    from sparse_slot_recurrent_amd import synth
+    x = synth.make_inputs(w)
+    d = {n: to_dev(torch, x[n], w.in_dtype) for n in ("q", "k", "v", "gamma", "g")}
+    S = to_dev(torch, x["S0"], w.state_dtype)
+    mass = to_dev(torch, x["m0"], "f32")
+    pos0 = torch.from_numpy(x["pos0"]).cuda()
+    del x
+    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, w.T, w.H, w.d_v), dtype=sdt, device="cuda")
+    plan = rn.PrefillPlan(w.B, w.T, w.H, w.d_p, w.U, w.K, w.d_v,
+                          rn.BF16 if w.in_dtype == "bf16" else rn.F32,
+                          rn.BF16 if w.state_dtype == "bf16" else rn.F32,
+                          cape=w.cape, eps_gsu=w.eps_gsu, eps_norm=w.eps_norm)
+    addr = rn.new_addresses((w.B, w.T, w.H, w.K), "cuda")
+
+    def step(_):
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["g"], S, mass, out, pos0=pos0)
+
+    def dec(_):
+        rn.decode_addresses(d["q"], d["k"], d_p=w.d_p, U=w.U, K=w.K,
+                            cape=w.cape, pos0=pos0, out=addr)
+
+    def scan(_):
+        plan(d["q"], d["k"], d["v"], d["gamma"], d["g"], S, mass, out,
+             pos0=pos0, addr_in=addr)
+
+    for _ in range(warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps)
+    torch.cuda.synchronize()
+    # per-kernel averages over the same number of launches, same stream
+    dec(0)
+    ms_dec = time_loop(torch, dec, steps)
+    scan(0)
+    ms_scan = time_loop(torch, scan, steps)
+    torch.cuda.synchronize()
+    tokens = w.B * w.T
+    return ms, {"decode_addresses": ms_dec, "scan": ms_scan}, tokens
+
+
+def bench_decode(torch, rn, w, steps, warmup):
+    from sparse_slot_recurrent_amd import synth
+    init = synth.make_inputs(w, T=1)
+    S = to_dev(torch, init["S0"], "bf16")
+    mass = to_dev(torch, init["m0"], "f32")
+    pos0 = torch.from_numpy(init["pos0"]).cuda()
+    del init
+    # distinct per-step inputs for every timed step, drawn on the device
+    n_in = steps + warmup
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    bdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+
+    def normal(*shape, sigma=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * sigma).to(bdt)
+
+    q = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
+    k = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
+    v = normal(n_in, w.B, w.H, w.d_v)
+    gam = normal(n_in, w.B, w.H)
+    g = normal(n_in, w.B, w.H, w.d_v)
+    pos = (pos0[None, :] + torch.arange(n_in, device="cuda", dtype=torch.int32)[:, None]).contiguous()
+    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, w.H, w.d_v), dtype=sdt, device="cuda")
+    plan = rn.StepPlan(w.B, w.H, w.d_p, w.U, w.K, w.d_v,
+                       rn.BF16 if w.in_dtype == "bf16" else rn.F32,
+                       rn.BF16 if w.state_dtype == "bf16" else rn.F32,
+                       cape=w.cape, eps_gsu=w.eps_gsu, eps_norm=w.eps_norm)
+    addr = rn.new_addresses((w.B, 1, w.H, w.K), "cuda")
+
+    def step(i):
+        plan(q[i], k[i], v[i], gam[i], g[i], pos[i], S, mass, out)
+
+    for i in range(warmup):
+        step(steps + i)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps)
+
+    def dec(i):
+        rn.decode_addresses(q[i][:, None], k[i][:, None], d_p=w.d_p, U=w.U,
+                            K=w.K, cape=w.cape, pos0=pos[i], out=addr)
+
+    ms_dec = time_loop(torch, dec, steps)
+    # the step's scan on given addresses: prefill path with T = 1
+    pplan = rn.PrefillPlan(w.B, 1, w.H, w.d_p, w.U, w.K, w.d_v,
+                           rn.BF16, rn.BF16, cape=w.cape)
+    out4 = out[:, None]
+
+    def scan(i):
+        pplan(q[i][:, None], k[i][:, None], v[i][:, None], gam[i][:, None],
+              g[i][:, None], S, mass, out4, addr_in=addr)
+
+    ms_scan = time_loop(torch, scan, steps)
+    torch.cuda.synchronize()
+    return ms, {"decode_addresses": ms_dec, "scan": ms_scan}, w.B
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="prefill_top8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): every "
+              "(batch, head) unit is independent, so more GPUs would each run "
+              "this same kernel on their own share of B x H.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_slot_recurrent_amd import ramnet as rn
+    from sparse_slot_recurrent_amd import synth
+    rn.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = synth.WORKLOADS[args.workload]
+    kind = "decode" if w.steps else "prefill"
+    steps = args.steps or (w.steps if kind == "decode" else 10)
+    warmup = args.warmup if args.warmup is not None else (16 if kind == "decode" else 2)
+    torch.cuda.set_device(0)
+    torch.cuda.synchronize()
+    if kind == "decode":
+        ms, kms, tokens = bench_decode(torch, rn, w, steps, warmup)
+    else:
+        ms, kms, tokens = bench_prefill(torch, rn, w, steps, warmup)
+    value = tokens / (ms / 1e3)
+    bm = byte_model(w, kind)
+    dom = max(kms, key=kms.get)
+    achieved = bm[dom] / (kms[dom] / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": 1 if kind == "decode" else w.T,
+                   "H": w.H, "M": w.M, "d_p": w.d_p, "U": w.U, "K": w.K,
+                   "d_v": w.d_v, "in_dtype": w.in_dtype,
+                   "state_dtype": w.state_dtype, "cape": w.cape,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernels_ms": kms,
+        "algorithmic_bytes": bm,
+        "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, kind)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

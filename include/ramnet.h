@@ -1,0 +1,164 @@
+/*
+ * ramnet.h: C ABI of the RAM-Net layer recurrence on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer (RAM-Net project page, muoncat.github.io/ramnet_web, "RAM-Net:
+ * Linear-Time Sequence Modeling with Sparsely Addressable State"):
+ *   1. Address Decoder, Product Softmax ("Product Softmax", "Soft Radix
+ *      Address" paragraphs): a key or query carries U blocks of d_p logits;
+ *      a softmax over each block is one base-d_p digit's distribution and a
+ *      slot's weight is the product of its U digit probabilities, over
+ *      M = d_p^U slots.  The K heaviest slots are found exactly by a
+ *      level-by-level prefix search (the exact Top-K paragraph after
+ *      "Waveform Modulation").  Block u is digit u counted from the most
+ *      significant one.  Weights are the raw products (not renormalised).
+ *      Equal weights rank by the smaller slot index.
+ *   2. CAPE ("Cyclic Address Positional Embedding" paragraphs): a token at
+ *      position P moves every digit of its read and write slots by
+ *      (P mod d_p), cyclically within d_p values.  Weights are unchanged.
+ *   3. Gated Sparse Update ("Gated Sparse Update" paragraphs, four steps),
+ *      for each of the K write slots i with weight w at a token with gate
+ *      gamma and value v:
+ *          alpha = (1 - w)^(exp(gamma))      (retention; 0 when w >= 1)
+ *          m_i   = alpha * m_i + w           (mass, stored fp32)
+ *          lam   = w / (m_i + eps_gsu)       (rate)
+ *          S_i   = S_i + lam * (v - S_i)     (content, stored in state dtype)
+ *      A slot with w = 0, and every slot that is not addressed, keeps its
+ *      content and mass bit-for-bit.
+ *   4. Read ("three stages" paragraph): after the token's K writes,
+ *      r = sum_j rho_j * S_{r_j} over the K read slots, then RMSNorm over d_v
+ *      (eps_norm, optional weight omega) and the output gate sigmoid(g):
+ *          out = r / sqrt(mean(r^2) + eps_norm) * omega * sigmoid(g)
+ *      (out = 0 for an all-zero read with eps_norm = 0).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are contiguous, row-major, in DEVICE memory, caller-owned.
+ *     The library allocates no device memory; scratch space comes from the
+ *     caller's `workspace` (size from ramnet_workspace_bytes).
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream).  Validation runs synchronously on the
+ *     host before anything is enqueued; on any error nothing is enqueued and
+ *     no buffer is touched.
+ *   - Errors are returned as ramnet_status; ramnet_last_error() gives a
+ *     message for the calling thread's last failure.
+ *   - S and mass are updated in place.  Inputs are never written.  `out`
+ *     and the address outputs must not overlap any other buffer.
+ *   - Calls that share S/mass must be ordered by the caller (same stream).
+ *     There is no global state; calls on different buffers may run
+ *     concurrently.
+ */
+#ifndef RAMNET_H
+#define RAMNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RAMNET_VERSION 1
+/* Largest supported K (Top-K per address). */
+#define RAMNET_KMAX 64
+
+typedef enum {
+    RAMNET_OK = 0,
+    RAMNET_EINVAL = -1,       /* bad shape, NULL or misaligned pointer, overlap */
+    RAMNET_EUNSUPPORTED = -2, /* valid request this build does not implement */
+    RAMNET_EWORKSPACE = -3,   /* workspace missing or too small */
+    RAMNET_EHIP = -4          /* the HIP runtime reported an error */
+} ramnet_status;
+
+typedef enum { RAMNET_F32 = 0, RAMNET_BF16 = 1 } ramnet_dtype;
+
+typedef enum { RAMNET_OP_DECODE = 0, RAMNET_OP_PREFILL = 1, RAMNET_OP_STEP = 2 }
+    ramnet_op;
+
+typedef struct {
+    int32_t B, T, H;      /* batch, tokens per sequence, heads; T = 1 for a step */
+    int32_t d_p, U;       /* digit base and digit count; 2 <= d_p <= 8 */
+    int64_t M;            /* slots per head; must equal d_p^U, <= 2^30 */
+    int32_t K;            /* slots per read/write, 1 <= K <= min(M, RAMNET_KMAX) */
+    int32_t d_v;          /* value channels; 64, 128, 192 or 256 */
+    int32_t in_dtype;     /* ramnet_dtype of q, k, v, gamma, g */
+    int32_t state_dtype;  /* ramnet_dtype of S and out (mass is always fp32) */
+    int32_t cape;         /* 1: CAPE on every head; 0: content-only addresses */
+    float eps_gsu;        /* epsilon of the update rate; >= 0 (1e-6 typical) */
+    float eps_norm;       /* epsilon of the RMSNorm; >= 0 (1e-6 typical) */
+} ramnet_params;
+
+/* Sparse addresses, each [B,T,H,K] (a step: [B,H,K]).  Slots are post-CAPE
+ * indices in [0, M).  Per address the K entries are ordered by weight
+ * (heaviest first), equal weights by the smaller pre-CAPE slot index. */
+typedef struct {
+    int32_t *w_idx;   /* write slots (from the key) */
+    float *w_wt;      /* write weights */
+    int32_t *r_idx;   /* read slots (from the query) */
+    float *r_wt;      /* read weights */
+} ramnet_addr;
+
+/* Address Decoder + CAPE only (steps 1-2 above).
+ *   q, k  [B,T,H,U*d_p] in in_dtype: query and key logits.
+ *   pos0  [B] int32 or NULL (= 0): position of token t is pos0[b] + t.
+ *   out   all four arrays required.
+ * The Top-K decision is taken in fp64; weights are returned rounded to
+ * fp32. */
+ramnet_status ramnet_decode_addresses(const ramnet_params *p, const void *q,
+                                      const void *k, const int32_t *pos0,
+                                      const ramnet_addr *out, void *stream);
+
+/* Bytes of workspace `op` needs for `p` (0 for an invalid p).  For
+ * RAMNET_OP_PREFILL and RAMNET_OP_STEP the figure assumes addr_out is NULL;
+ * with addr_out given, 0 bytes are needed. */
+size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op);
+
+/* Prefill (project page, GPU-execution paragraphs: addresses for all tokens
+ * in parallel, then the recurrence in causal order): steps 1-4 for every
+ * token of B sequences of T tokens, H heads each.
+ *   q, k      [B,T,H,U*d_p] in_dtype      v, g   [B,T,H,d_v] in_dtype
+ *   gamma     [B,T,H] in_dtype            norm_w [d_v] fp32 or NULL (= 1)
+ *   pos0      [B] int32 or NULL (= 0)
+ *   S         [B,H,M,d_v] state_dtype, in/out
+ *   mass      [B,H,M] fp32, in/out
+ *   out       [B,T,H,d_v] state_dtype
+ *   addr_in   NULL: decode q, k.  Otherwise the addresses to use (post-CAPE
+ *             slots and weights); q, k and pos0 are then ignored.  Slots must
+ *             be distinct within an address; a slot outside [0, M) is
+ *             skipped (treated as weight 0).
+ *   addr_out  NULL, or where to export the addresses used.
+ *   workspace ramnet_workspace_bytes(p, RAMNET_OP_PREFILL) bytes, or NULL
+ *             when that figure is 0 for this call. */
+ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
+                                  const void *k, const void *v,
+                                  const void *gamma, const void *g,
+                                  const float *norm_w, const int32_t *pos0,
+                                  void *S, float *mass, void *out,
+                                  const ramnet_addr *addr_in,
+                                  const ramnet_addr *addr_out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* One decoding step (project page, decoding paragraph: the current token's
+ * slots are accessed directly, without a pass over the state): steps 1-4
+ * for one token of each of B sequences.  p->T must be 1.
+ *   q, k [B,H,U*d_p]; v, g [B,H,d_v]; gamma [B,H] (in_dtype)
+ *   pos  [B] int32: position of this token; required when p->cape
+ *   S, mass as for prefill; out [B,H,d_v] state_dtype
+ *   addr_out NULL or [B,H,K] each. */
+ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
+                                 const void *k, const void *v,
+                                 const void *gamma, const void *g,
+                                 const float *norm_w, const int32_t *pos,
+                                 void *S, float *mass, void *out,
+                                 const ramnet_addr *addr_out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+const char *ramnet_status_str(ramnet_status s);
+const char *ramnet_last_error(void);
+int32_t ramnet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAMNET_H */

@@ -1,0 +1,352 @@
+// C ABI of the RAM-Net layer (declared in include/ramnet.h): host-side
+// validation, workspace layout and kernel dispatch.  Nothing here touches
+// the GPU until every argument has been checked.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "launch.h"
+#include "ramnet.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ramnet_status fail(ramnet_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+ramnet_status ok() {
+    g_last_error.clear();
+    return RAMNET_OK;
+}
+
+constexpr int64_t kMaxSlots = int64_t(1) << 30;
+constexpr int64_t kMaxTokenHeads = int64_t(1) << 40;
+
+ramnet_status check_params(const ramnet_params *p, bool step) {
+    if (!p) return fail(RAMNET_EINVAL, "params is NULL");
+    if (p->B < 0 || p->T < 0 || p->H < 0)
+        return fail(RAMNET_EINVAL, "B, T, H must be >= 0 (got %d, %d, %d)", p->B, p->T, p->H);
+    if (step && p->T != 1) return fail(RAMNET_EINVAL, "a decode step needs T == 1 (got %d)", p->T);
+    if (static_cast<int64_t>(p->B) * p->T * p->H > kMaxTokenHeads)
+        return fail(RAMNET_EINVAL, "B*T*H exceeds 2^40");
+    if (p->d_p < 2 || p->U < 1) return fail(RAMNET_EINVAL, "need d_p >= 2 and U >= 1");
+    int64_t M = 1;
+    for (int u = 0; u < p->U; ++u) {
+        M *= p->d_p;
+        if (M > kMaxSlots) return fail(RAMNET_EINVAL, "d_p^U exceeds 2^30 slots");
+    }
+    if (p->M != M)
+        return fail(RAMNET_EINVAL, "M = %lld but d_p^U = %lld", static_cast<long long>(p->M),
+                    static_cast<long long>(M));
+    if (p->K < 1 || p->K > M) return fail(RAMNET_EINVAL, "K = %d outside [1, M]", p->K);
+    if (p->d_v < 1) return fail(RAMNET_EINVAL, "d_v must be >= 1");
+    if (p->in_dtype != RAMNET_F32 && p->in_dtype != RAMNET_BF16)
+        return fail(RAMNET_EINVAL, "unknown in_dtype %d", p->in_dtype);
+    if (p->state_dtype != RAMNET_F32 && p->state_dtype != RAMNET_BF16)
+        return fail(RAMNET_EINVAL, "unknown state_dtype %d", p->state_dtype);
+    if (p->cape != 0 && p->cape != 1) return fail(RAMNET_EINVAL, "cape must be 0 or 1");
+    if (!(p->eps_gsu >= 0.f) || !isfinite(p->eps_gsu) || !(p->eps_norm >= 0.f) ||
+        !isfinite(p->eps_norm))
+        return fail(RAMNET_EINVAL, "eps_gsu and eps_norm must be finite and >= 0");
+    if (p->K > RAMNET_KMAX)
+        return fail(RAMNET_EUNSUPPORTED, "K = %d exceeds RAMNET_KMAX = %d", p->K, RAMNET_KMAX);
+    if (p->d_p > 8) return fail(RAMNET_EUNSUPPORTED, "d_p = %d > 8 is not built", p->d_p);
+    if (p->d_v % 64 != 0 || p->d_v > 256)
+        return fail(RAMNET_EUNSUPPORTED, "d_v = %d: only 64, 128, 192, 256 are built", p->d_v);
+    return RAMNET_OK;
+}
+
+struct Span {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const char *name, const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{name, lo, lo + bytes};
+}
+
+bool overlaps(const Span &a, const Span &b) {
+    return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+ramnet_status check_ptr(const char *name, const void *p, bool required) {
+    if (!p) {
+        if (required) return fail(RAMNET_EINVAL, "%s is NULL", name);
+        return RAMNET_OK;
+    }
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+        return fail(RAMNET_EINVAL, "%s is not 16-byte aligned", name);
+    return RAMNET_OK;
+}
+
+// Written buffers must not overlap each other or any other buffer.
+ramnet_status check_overlaps(const Span *spans, int n, int first_written) {
+    for (int i = first_written; i < n; ++i)
+        for (int j = 0; j < n; ++j)
+            if (i != j && overlaps(spans[i], spans[j]))
+                return fail(RAMNET_EINVAL, "%s overlaps %s", spans[i].name, spans[j].name);
+    return RAMNET_OK;
+}
+
+size_t in_bytes(const ramnet_params *p) { return p->in_dtype == RAMNET_BF16 ? 2 : 4; }
+size_t st_bytes(const ramnet_params *p) { return p->state_dtype == RAMNET_BF16 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: decoded addresses when the caller neither supplies nor exports
+// them.  Four [n, K] arrays, each 256-byte aligned.
+size_t addr_workspace_bytes(int64_t n, int K) {
+    return 4 * align256(static_cast<size_t>(n) * K * 4);
+}
+
+ramnet_addr carve_addr(void *ws, int64_t n, int K) {
+    const size_t one = align256(static_cast<size_t>(n) * K * 4);
+    char *base = static_cast<char *>(ws);
+    return ramnet_addr{reinterpret_cast<int32_t *>(base), reinterpret_cast<float *>(base + one),
+                       reinterpret_cast<int32_t *>(base + 2 * one),
+                       reinterpret_cast<float *>(base + 3 * one)};
+}
+
+ramnet_status check_addr(const char *what, const ramnet_addr *a) {
+    ramnet_status s;
+    std::string nm = what;
+    if ((s = check_ptr((nm + ".w_idx").c_str(), a->w_idx, true))) return s;
+    if ((s = check_ptr((nm + ".w_wt").c_str(), a->w_wt, true))) return s;
+    if ((s = check_ptr((nm + ".r_idx").c_str(), a->r_idx, true))) return s;
+    if ((s = check_ptr((nm + ".r_wt").c_str(), a->r_wt, true))) return s;
+    return RAMNET_OK;
+}
+
+ramnet_status hip_status(hipError_t e, const char *where) {
+    if (e == hipSuccess) return ok();
+    return fail(RAMNET_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+ramnet::DecodeArgs decode_args(const ramnet_params *p, const void *q, const void *k,
+                               const int32_t *pos0, int64_t n, int T, const ramnet_addr &o) {
+    ramnet::DecodeArgs d{};
+    d.q = q;
+    d.k = k;
+    d.n = n;
+    d.T = T;
+    d.H = p->H;
+    d.U = p->U;
+    d.K = p->K;
+    d.d_p = p->d_p;
+    d.pos0 = pos0;
+    d.cape = p->cape;
+    d.in_bf16 = p->in_dtype == RAMNET_BF16;
+    d.w_idx = o.w_idx;
+    d.w_wt = o.w_wt;
+    d.r_idx = o.r_idx;
+    d.r_wt = o.r_wt;
+    return d;
+}
+
+// Shared body of prefill (T tokens) and the decode step (T = 1).
+ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const void *k,
+                        const void *v, const void *gamma, const void *g, const float *norm_w,
+                        const int32_t *pos, void *S, float *mass, void *out,
+                        const ramnet_addr *addr_in, const ramnet_addr *addr_out, void *ws,
+                        size_t ws_bytes, void *stream) {
+    ramnet_status s = check_params(p, step);
+    if (s) return s;
+    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
+    const int64_t units = static_cast<int64_t>(p->B) * p->H;
+    const bool decode = addr_in == nullptr;
+    if (n == 0) return ok();
+    if (decode) {
+        if ((s = check_ptr("q", q, true)) || (s = check_ptr("k", k, true))) return s;
+        if (step && p->cape && !pos) return fail(RAMNET_EINVAL, "pos is required when cape = 1");
+        if ((s = check_ptr(step ? "pos" : "pos0", pos, false))) return s;
+    } else if ((s = check_addr("addr_in", addr_in))) {
+        return s;
+    }
+    if ((s = check_ptr("v", v, true)) || (s = check_ptr("gamma", gamma, true)) ||
+        (s = check_ptr("g", g, true)) || (s = check_ptr("norm_w", norm_w, false)) ||
+        (s = check_ptr("S", S, true)) || (s = check_ptr("mass", mass, true)) ||
+        (s = check_ptr("out", out, true)))
+        return s;
+    if (addr_out && (s = check_addr("addr_out", addr_out))) return s;
+
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    const size_t nK4 = static_cast<size_t>(n) * p->K * 4;
+    Span sp[16];
+    int ns = 0;
+    // read-only buffers first
+    if (decode) {
+        sp[ns++] = span("q", q, n * L * in_bytes(p));
+        sp[ns++] = span("k", k, n * L * in_bytes(p));
+        if (pos) sp[ns++] = span(step ? "pos" : "pos0", pos, p->B * sizeof(int32_t));
+    } else {
+        sp[ns++] = span("addr_in.w_idx", addr_in->w_idx, nK4);
+        sp[ns++] = span("addr_in.w_wt", addr_in->w_wt, nK4);
+        sp[ns++] = span("addr_in.r_idx", addr_in->r_idx, nK4);
+        sp[ns++] = span("addr_in.r_wt", addr_in->r_wt, nK4);
+    }
+    sp[ns++] = span("v", v, n * p->d_v * in_bytes(p));
+    sp[ns++] = span("gamma", gamma, n * in_bytes(p));
+    sp[ns++] = span("g", g, n * p->d_v * in_bytes(p));
+    if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
+    const int first_written = ns;
+    sp[ns++] = span("S", S, units * p->M * p->d_v * st_bytes(p));
+    sp[ns++] = span("mass", mass, units * p->M * sizeof(float));
+    sp[ns++] = span("out", out, n * p->d_v * st_bytes(p));
+    if (addr_out) {
+        sp[ns++] = span("addr_out.w_idx", addr_out->w_idx, nK4);
+        sp[ns++] = span("addr_out.w_wt", addr_out->w_wt, nK4);
+        sp[ns++] = span("addr_out.r_idx", addr_out->r_idx, nK4);
+        sp[ns++] = span("addr_out.r_wt", addr_out->r_wt, nK4);
+    }
+    const bool need_ws = decode && !addr_out;
+    if (need_ws) {
+        const size_t need = addr_workspace_bytes(n, p->K);
+        if (!ws || ws_bytes < need)
+            return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        ws ? ws_bytes : size_t(0));
+        if ((s = check_ptr("workspace", ws, true))) return s;
+        sp[ns++] = span("workspace", ws, need);
+    }
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ramnet_addr addr;
+    if (decode) {
+        addr = addr_out ? *addr_out : carve_addr(ws, n, p->K);
+        hipError_t e = ramnet::launch_decode(decode_args(p, q, k, pos, n, p->T, addr), st);
+        if (e != hipSuccess) return hip_status(e, "address decoder launch");
+    } else {
+        addr = *addr_in;
+    }
+    ramnet::ScanArgs a{};
+    a.B = p->B;
+    a.T = p->T;
+    a.H = p->H;
+    a.M = p->M;
+    a.K = p->K;
+    a.d_v = p->d_v;
+    a.in_bf16 = p->in_dtype == RAMNET_BF16;
+    a.state_bf16 = p->state_dtype == RAMNET_BF16;
+    a.v = v;
+    a.gamma = gamma;
+    a.g = g;
+    a.norm_w = norm_w;
+    a.w_idx = addr.w_idx;
+    a.w_wt = addr.w_wt;
+    a.r_idx = addr.r_idx;
+    a.r_wt = addr.r_wt;
+    a.S = S;
+    a.mass = mass;
+    a.out = out;
+    a.eps_gsu = p->eps_gsu;
+    a.eps_norm = p->eps_norm;
+    hipError_t e = ramnet::launch_scan_serial(a, st);
+    if (e != hipSuccess) return hip_status(e, "scan launch");
+    if (!decode && addr_out) {
+        for (int i = 0; i < 4; ++i) {
+            void *dst = i == 0 ? static_cast<void *>(addr_out->w_idx)
+                      : i == 1 ? static_cast<void *>(addr_out->w_wt)
+                      : i == 2 ? static_cast<void *>(addr_out->r_idx)
+                               : static_cast<void *>(addr_out->r_wt);
+            const void *src = i == 0 ? static_cast<const void *>(addr_in->w_idx)
+                            : i == 1 ? static_cast<const void *>(addr_in->w_wt)
+                            : i == 2 ? static_cast<const void *>(addr_in->r_idx)
+                                     : static_cast<const void *>(addr_in->r_wt);
+            e = hipMemcpyAsync(dst, src, nK4, hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return hip_status(e, "address export copy");
+        }
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ramnet_status ramnet_decode_addresses(const ramnet_params *p, const void *q, const void *k,
+                                      const int32_t *pos0, const ramnet_addr *out,
+                                      void *stream) {
+    ramnet_status s = check_params(p, false);
+    if (s) return s;
+    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
+    if (!out) return fail(RAMNET_EINVAL, "out is NULL");
+    if (n == 0) return ok();
+    if ((s = check_ptr("q", q, true)) || (s = check_ptr("k", k, true)) ||
+        (s = check_ptr("pos0", pos0, false)) || (s = check_addr("out", out)))
+        return s;
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    const size_t nK4 = static_cast<size_t>(n) * p->K * 4;
+    Span sp[9];
+    int ns = 0;
+    sp[ns++] = span("q", q, n * L * in_bytes(p));
+    sp[ns++] = span("k", k, n * L * in_bytes(p));
+    if (pos0) sp[ns++] = span("pos0", pos0, p->B * sizeof(int32_t));
+    const int first_written = ns;
+    sp[ns++] = span("out.w_idx", out->w_idx, nK4);
+    sp[ns++] = span("out.w_wt", out->w_wt, nK4);
+    sp[ns++] = span("out.r_idx", out->r_idx, nK4);
+    sp[ns++] = span("out.r_wt", out->r_wt, nK4);
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+    hipError_t e = ramnet::launch_decode(decode_args(p, q, k, pos0, n, p->T, *out),
+                                         static_cast<hipStream_t>(stream));
+    return hip_status(e, "address decoder launch");
+}
+
+size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
+    const std::string saved = g_last_error;
+    const bool step = op == RAMNET_OP_STEP;
+    const ramnet_status s = check_params(p, step);
+    g_last_error = saved;
+    if (s != RAMNET_OK) return 0;
+    if (op == RAMNET_OP_DECODE) return 0;
+    if (op != RAMNET_OP_PREFILL && op != RAMNET_OP_STEP) return 0;
+    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
+    return addr_workspace_bytes(n, p->K);
+}
+
+ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q, const void *k,
+                                  const void *v, const void *gamma, const void *g,
+                                  const float *norm_w, const int32_t *pos0, void *S, float *mass,
+                                  void *out, const ramnet_addr *addr_in,
+                                  const ramnet_addr *addr_out, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return run_layer(p, false, q, k, v, gamma, g, norm_w, pos0, S, mass, out, addr_in, addr_out,
+                     workspace, workspace_bytes, stream);
+}
+
+ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q, const void *k,
+                                 const void *v, const void *gamma, const void *g,
+                                 const float *norm_w, const int32_t *pos, void *S, float *mass,
+                                 void *out, const ramnet_addr *addr_out, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    return run_layer(p, true, q, k, v, gamma, g, norm_w, pos, S, mass, out, nullptr, addr_out,
+                     workspace, workspace_bytes, stream);
+}
+
+const char *ramnet_status_str(ramnet_status s) {
+    switch (s) {
+        case RAMNET_OK: return "ok";
+        case RAMNET_EINVAL: return "invalid argument";
+        case RAMNET_EUNSUPPORTED: return "unsupported configuration";
+        case RAMNET_EWORKSPACE: return "workspace missing or too small";
+        case RAMNET_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *ramnet_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ramnet_version(void) { return RAMNET_VERSION; }
+
+}  // extern "C"

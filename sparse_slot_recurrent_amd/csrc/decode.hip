@@ -1,0 +1,197 @@
+// Address Decoder for gfx950: Product Softmax + exact prefix-tree Top-K +
+// CAPE, one address per lane.
+//
+// RAM-Net project page, "Product Softmax" / "Multilevel Decision Tree" and
+// the exact Top-K paragraph: each level fixes one more digit (most
+// significant first); extending the K kept prefixes by the d_p values of the
+// next digit gives K*d_p candidates, of which the K best are kept.  A prefix
+// that drops out already trails K others that share every later factor, so
+// the search returns the exact Top-K of all M slots.
+//
+// Design: the kept prefixes are held sorted (weight desc, prefix asc).  With
+// the next digit's probabilities sorted the same way, the candidates form
+// d_p sorted lists (one per digit value), and the new beam is the first K
+// entries of their merge.  Each lane merges its own lists; the beams live in
+// LDS, column-interleaved by lane ([buffer][rank][lane]), so the data-
+// dependent rank index never causes a bank conflict.  The decision is taken
+// in fp64 so that it agrees with an fp64 reference except at exact ties.
+#include "device_common.h"
+#include "launch.h"
+
+namespace ramnet {
+namespace {
+
+template <typename WT>
+__device__ __forceinline__ bool ranks_before(WT wa, int ia, WT wb, int ib) {
+    return wa > wb || (wa == wb && ia < ib);
+}
+
+__device__ __forceinline__ double wexp(double x) { return exp(x); }
+
+template <int DP>
+__device__ __forceinline__ int cape_move(int slot, int64_t pos, int U) {
+    const unsigned s = static_cast<unsigned>(((pos % DP) + DP) % DP);
+    if (s == 0) return slot;
+    unsigned x = static_cast<unsigned>(slot), moved = 0, place = 1;
+    for (int u = 0; u < U; ++u) {
+        const unsigned d = x % DP;
+        x /= DP;
+        moved += ((d + s) % DP) * place;
+        place *= DP;
+    }
+    return static_cast<int>(moved);
+}
+
+template <int DP, typename WT, typename TIn>
+__global__ __launch_bounds__(kWave) void decode_kernel(
+    const TIn *__restrict__ q, const TIn *__restrict__ k, int64_t n, int T, int H,
+    int U, int K, const int32_t *__restrict__ pos0, int cape,
+    int32_t *__restrict__ w_idx, float *__restrict__ w_wt,
+    int32_t *__restrict__ r_idx, float *__restrict__ r_wt) {
+    extern __shared__ unsigned char smem[];
+    const int lane = threadIdx.x;
+    WT *bw = reinterpret_cast<WT *>(smem);                          // [2][K][64]
+    int32_t *bp = reinterpret_cast<int32_t *>(bw + 2 * K * kWave);  // [2][K][64]
+    const int64_t a = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    if (a >= n) return;  // no barrier below: lanes are independent
+    const bool key = blockIdx.y == 0;
+    const TIn *lg = (key ? k : q) + a * (U * DP);
+    auto BW = [&](int buf, int r) -> WT & { return bw[(buf * K + r) * kWave + lane]; };
+    auto BP = [&](int buf, int r) -> int32_t & { return bp[(buf * K + r) * kWave + lane]; };
+
+    int cur = 0, nb = 1;
+    BW(0, 0) = WT(1);
+    BP(0, 0) = 0;
+    for (int u = 0; u < U; ++u) {
+        // Digit u's distribution: softmax over its d_p logits.
+        WT pr[DP];
+        int dg[DP];
+        float l[DP];
+#pragma unroll
+        for (int d = 0; d < DP; ++d) l[d] = to_f32(lg[u * DP + d]);
+        float mx = l[0];
+#pragma unroll
+        for (int d = 1; d < DP; ++d) mx = fmaxf(mx, l[d]);
+        WT sum = 0;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) {
+            pr[d] = wexp(static_cast<WT>(l[d]) - static_cast<WT>(mx));
+            sum += pr[d];
+        }
+#pragma unroll
+        for (int d = 0; d < DP; ++d) {
+            pr[d] /= sum;
+            dg[d] = d;
+        }
+        // Sort digit values by (probability desc, value asc); stable
+        // insertion network over compile-time positions.
+#pragma unroll
+        for (int i = 1; i < DP; ++i) {
+#pragma unroll
+            for (int j = i; j > 0; --j) {
+                const bool sw = pr[j] > pr[j - 1];
+                const WT tp = pr[j];
+                const int td = dg[j];
+                pr[j] = sw ? pr[j - 1] : pr[j];
+                dg[j] = sw ? dg[j - 1] : dg[j];
+                pr[j - 1] = sw ? tp : pr[j - 1];
+                dg[j - 1] = sw ? td : dg[j - 1];
+            }
+        }
+        // Merge the d_p candidate lists into the next beam.
+        const int nn = min(K, nb * DP);
+        const int nxt = cur ^ 1;
+        int h[DP];
+        WT cw[DP];
+        int cp[DP];
+        const WT b0 = BW(cur, 0);
+        const int p0 = BP(cur, 0);
+#pragma unroll
+        for (int d = 0; d < DP; ++d) {
+            h[d] = 0;
+            cw[d] = b0 * pr[d];
+            cp[d] = p0 * DP + dg[d];
+        }
+        for (int r = 0; r < nn; ++r) {
+            int best = 0;
+            WT bwv = cw[0];
+            int bpv = cp[0];
+#pragma unroll
+            for (int d = 1; d < DP; ++d) {
+                const bool bt = ranks_before(cw[d], cp[d], bwv, bpv);
+                best = bt ? d : best;
+                bwv = bt ? cw[d] : bwv;
+                bpv = bt ? cp[d] : bpv;
+            }
+            BW(nxt, r) = bwv;
+            BP(nxt, r) = bpv;
+            int hb = 0;
+#pragma unroll
+            for (int d = 0; d < DP; ++d)
+                if (d == best) hb = ++h[d];
+            const bool more = hb < nb;
+            const WT nw = more ? BW(cur, hb) : WT(0);
+            const int np = more ? BP(cur, hb) : 0;
+#pragma unroll
+            for (int d = 0; d < DP; ++d) {
+                if (d == best) {
+                    cw[d] = more ? nw * pr[d] : WT(-1);  // exhausted list
+                    cp[d] = np * DP + dg[d];
+                }
+            }
+        }
+        cur = nxt;
+        nb = nn;
+    }
+
+    const int64_t b = a / (static_cast<int64_t>(T) * H);
+    const int64_t t = (a / H) % T;
+    const int64_t pos = (pos0 ? pos0[b] : 0) + t;
+    int32_t *oi = (key ? w_idx : r_idx) + a * K;
+    float *ow = (key ? w_wt : r_wt) + a * K;
+    for (int r = 0; r < K; ++r) {
+        const int slot = BP(cur, r);
+        oi[r] = cape ? cape_move<DP>(slot, pos, U) : slot;
+        ow[r] = static_cast<float>(BW(cur, r));
+    }
+}
+
+template <int DP, typename TIn>
+hipError_t launch_dp(const DecodeArgs &d, hipStream_t st) {
+    using WT = double;
+    const size_t lds = static_cast<size_t>(2) * d.K * kWave * (sizeof(WT) + sizeof(int32_t));
+    auto kern = decode_kernel<DP, WT, TIn>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    dim3 grid(static_cast<unsigned>((d.n + kWave - 1) / kWave), 2);
+    hipLaunchKernelGGL(kern, grid, dim3(kWave), lds, st,
+                       static_cast<const TIn *>(d.q), static_cast<const TIn *>(d.k), d.n,
+                       d.T, d.H, d.U, d.K, d.pos0, d.cape, d.w_idx, d.w_wt, d.r_idx,
+                       d.r_wt);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_in(const DecodeArgs &d, hipStream_t st) {
+    switch (d.d_p) {
+        case 2: return launch_dp<2, TIn>(d, st);
+        case 3: return launch_dp<3, TIn>(d, st);
+        case 4: return launch_dp<4, TIn>(d, st);
+        case 5: return launch_dp<5, TIn>(d, st);
+        case 6: return launch_dp<6, TIn>(d, st);
+        case 7: return launch_dp<7, TIn>(d, st);
+        case 8: return launch_dp<8, TIn>(d, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &d, hipStream_t st) {
+    if (d.n == 0) return hipSuccess;
+    return d.in_bf16 ? launch_in<bf16_t>(d, st) : launch_in<float>(d, st);
+}
+
+}  // namespace ramnet

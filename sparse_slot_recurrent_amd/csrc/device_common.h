@@ -1,0 +1,63 @@
+// Device-side helpers shared by the gfx950 kernels of the RAM-Net layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ramnet {
+
+constexpr int kWave = 64;
+
+// bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{static_cast<uint16_t>((u >> 16) | 0x40u)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16_t{static_cast<uint16_t>(u >> 16)};
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return bf16_rne(x); }
+
+// Value after a round trip through storage type T.
+template <typename T> __device__ __forceinline__ float stored(float x) {
+    return to_f32(from_f32<T>(x));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Broadcast from a lane chosen by a wave-uniform index.
+__device__ __forceinline__ int bcast(int x, int lane) {
+    return __builtin_amdgcn_readlane(x, lane);
+}
+__device__ __forceinline__ float bcast(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// Retention of the Gated Sparse Update: (1 - w)^(exp(gamma)) for 0 < w,
+// written as exp(exp(gamma) * log1p(-w)); 0 for w >= 1.
+__device__ __forceinline__ float retention(float w, float exp_gamma) {
+    if (w >= 1.0f) return 0.0f;
+    return expf(exp_gamma * log1pf(-w));
+}
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace ramnet

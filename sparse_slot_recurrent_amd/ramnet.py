@@ -1,0 +1,245 @@
+"""Python binding of libramnet.so (include/ramnet.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the layer runs in the HIP kernels behind the
+C ABI.  If the library is not built this module raises on import of the
+library (no fallback path exists).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import NamedTuple, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libramnet.so")
+
+F32, BF16 = 0, 1
+OP_DECODE, OP_PREFILL, OP_STEP = 0, 1, 2
+STATUS = {0: "RAMNET_OK", -1: "RAMNET_EINVAL", -2: "RAMNET_EUNSUPPORTED",
+          -3: "RAMNET_EWORKSPACE", -4: "RAMNET_EHIP"}
+EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
+            "ramnet_scan_prefill", "ramnet_step_decode", "ramnet_status_str",
+            "ramnet_last_error", "ramnet_version")
+
+
+class Params(C.Structure):
+    _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("H", C.c_int32),
+                ("d_p", C.c_int32), ("U", C.c_int32), ("M", C.c_int64),
+                ("K", C.c_int32), ("d_v", C.c_int32),
+                ("in_dtype", C.c_int32), ("state_dtype", C.c_int32),
+                ("cape", C.c_int32), ("eps_gsu", C.c_float),
+                ("eps_norm", C.c_float)]
+
+
+class Addr(C.Structure):
+    _fields_ = [("w_idx", C.c_void_p), ("w_wt", C.c_void_p),
+                ("r_idx", C.c_void_p), ("r_wt", C.c_void_p)]
+
+
+class RamnetError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libramnet.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = C.CDLL(path)
+    P = C.c_void_p
+    pp = C.POINTER(Params)
+    pa = C.POINTER(Addr)
+    lib.ramnet_decode_addresses.argtypes = [pp, P, P, P, pa, P]
+    lib.ramnet_decode_addresses.restype = C.c_int
+    lib.ramnet_workspace_bytes.argtypes = [pp, C.c_int32]
+    lib.ramnet_workspace_bytes.restype = C.c_size_t
+    lib.ramnet_scan_prefill.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
+                                        pa, P, C.c_size_t, P]
+    lib.ramnet_scan_prefill.restype = C.c_int
+    lib.ramnet_step_decode.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
+                                       P, C.c_size_t, P]
+    lib.ramnet_step_decode.restype = C.c_int
+    lib.ramnet_status_str.argtypes = [C.c_int]
+    lib.ramnet_status_str.restype = C.c_char_p
+    lib.ramnet_last_error.restype = C.c_char_p
+    lib.ramnet_version.restype = C.c_int32
+    _lib = lib
+    return lib
+
+
+def _raise(status: int):
+    if status != 0:
+        msg = load_library().ramnet_last_error().decode()
+        raise RamnetError(status, msg)
+
+
+def make_params(B, T, H, d_p, U, K, d_v, in_dtype=BF16, state_dtype=F32,
+                cape=1, eps_gsu=1e-6, eps_norm=1e-6, M=None) -> Params:
+    return Params(B, T, H, d_p, U, d_p ** U if M is None else M, K, d_v,
+                  in_dtype, state_dtype, cape, eps_gsu, eps_norm)
+
+
+def workspace_bytes(p: Params, op: int) -> int:
+    return int(load_library().ramnet_workspace_bytes(C.byref(p), op))
+
+
+# ---------------------------------------------------------------- torch layer
+
+def _torch():
+    import torch
+    return torch
+
+
+class Addresses(NamedTuple):
+    w_idx: "object"
+    w_wt: "object"
+    r_idx: "object"
+    r_wt: "object"
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("RAM-Net tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("RAM-Net tensors must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _addr_struct(a: Optional[Addresses]):
+    if a is None:
+        return None
+    return Addr(a.w_idx.data_ptr(), a.w_wt.data_ptr(), a.r_idx.data_ptr(),
+                a.r_wt.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def new_addresses(shape_bthk, device) -> Addresses:
+    torch = _torch()
+    return Addresses(torch.empty(shape_bthk, dtype=torch.int32, device=device),
+                     torch.empty(shape_bthk, dtype=torch.float32, device=device),
+                     torch.empty(shape_bthk, dtype=torch.int32, device=device),
+                     torch.empty(shape_bthk, dtype=torch.float32, device=device))
+
+
+def decode_addresses(q, k, *, d_p: int, U: int, K: int, cape: int = 1,
+                     pos0=None, out: Optional[Addresses] = None) -> Addresses:
+    """q, k [B,T,H,U*d_p] -> Addresses, each [B,T,H,K] (post-CAPE slots),
+    written into `out` when given."""
+    B, T, H, L = q.shape
+    assert L == U * d_p and k.shape == q.shape
+    p = make_params(B, T, H, d_p, U, K, 64, in_dtype=_dt(q), cape=cape)
+    if out is None:
+        out = new_addresses((B, T, H, K), q.device)
+    a = _addr_struct(out)
+    _raise(load_library().ramnet_decode_addresses(
+        C.byref(p), _ptr(q), _ptr(k), _ptr(pos0), C.byref(a), _stream()))
+    return out
+
+
+class PrefillPlan:
+    """Validated shapes plus a reusable workspace for repeated prefill calls
+    of one shape (the benchmark's timed loop allocates nothing)."""
+
+    def __init__(self, B, T, H, d_p, U, K, d_v, in_dtype, state_dtype, cape=1,
+                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda"):
+        torch = _torch()
+        self.p = make_params(B, T, H, d_p, U, K, d_v, in_dtype, state_dtype,
+                             cape, eps_gsu, eps_norm)
+        nbytes = workspace_bytes(self.p, OP_PREFILL)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                     device=device)
+        self.ws_bytes = nbytes
+
+    def __call__(self, q, k, v, gamma, g, S, mass, out, *, norm_w=None,
+                 pos0=None, addr_in: Optional[Addresses] = None,
+                 addr_out: Optional[Addresses] = None):
+        ai = _addr_struct(addr_in)
+        ao = _addr_struct(addr_out)
+        _raise(load_library().ramnet_scan_prefill(
+            C.byref(self.p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g),
+            _ptr(norm_w), _ptr(pos0), _ptr(S), _ptr(mass), _ptr(out),
+            C.byref(ai) if ai is not None else None,
+            C.byref(ao) if ao is not None else None,
+            C.c_void_p(self.workspace.data_ptr()), self.ws_bytes, _stream()))
+        return out
+
+
+def scan_prefill(q, k, v, gamma, g, S, mass, *, d_p: int, U: int, K: int,
+                 cape: int = 1, norm_w=None, pos0=None, eps_gsu=1e-6,
+                 eps_norm=1e-6, addr_in: Optional[Addresses] = None,
+                 export_addresses: bool = False):
+    """Runs the layer over [B,T,H]; S [B,H,M,d_v] and mass [B,H,M] are
+    updated in place.  Returns out [B,T,H,d_v] (and the addresses used when
+    export_addresses)."""
+    torch = _torch()
+    B, T, H, d_v = v.shape
+    plan = PrefillPlan(B, T, H, d_p, U, K, d_v, _dt(v), _dt(S), cape, eps_gsu,
+                       eps_norm, device=v.device)
+    out = torch.empty((B, T, H, d_v), dtype=S.dtype, device=v.device)
+    ao = new_addresses((B, T, H, K), v.device) if export_addresses else None
+    plan(q, k, v, gamma, g, S, mass, out, norm_w=norm_w, pos0=pos0,
+         addr_in=addr_in, addr_out=ao)
+    return (out, ao) if export_addresses else out
+
+
+class StepPlan:
+    """A decode step of one shape with its workspace, reusable per step."""
+
+    def __init__(self, B, H, d_p, U, K, d_v, in_dtype, state_dtype, cape=1,
+                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda"):
+        torch = _torch()
+        self.p = make_params(B, 1, H, d_p, U, K, d_v, in_dtype, state_dtype,
+                             cape, eps_gsu, eps_norm)
+        nbytes = workspace_bytes(self.p, OP_STEP)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                     device=device)
+        self.ws_bytes = nbytes
+
+    def __call__(self, q, k, v, gamma, g, pos, S, mass, out, *, norm_w=None,
+                 addr_out: Optional[Addresses] = None):
+        ao = _addr_struct(addr_out)
+        _raise(load_library().ramnet_step_decode(
+            C.byref(self.p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g),
+            _ptr(norm_w), _ptr(pos), _ptr(S), _ptr(mass), _ptr(out),
+            C.byref(ao) if ao is not None else None,
+            C.c_void_p(self.workspace.data_ptr()), self.ws_bytes, _stream()))
+        return out
+
+
+def step_decode(q, k, v, gamma, g, pos, S, mass, *, d_p: int, U: int, K: int,
+                cape: int = 1, norm_w=None, eps_gsu=1e-6, eps_norm=1e-6,
+                export_addresses: bool = False):
+    """One token per sequence: q, k [B,H,U*d_p]; v, g [B,H,d_v]; gamma [B,H];
+    pos [B] int32.  Returns out [B,H,d_v] (and the addresses)."""
+    torch = _torch()
+    B, H, d_v = v.shape
+    plan = StepPlan(B, H, d_p, U, K, d_v, _dt(v), _dt(S), cape, eps_gsu,
+                    eps_norm, device=v.device)
+    out = torch.empty((B, H, d_v), dtype=S.dtype, device=v.device)
+    ao = new_addresses((B, H, K), v.device) if export_addresses else None
+    plan(q, k, v, gamma, g, pos, S, mass, out, norm_w=norm_w, addr_out=ao)
+    return (out, ao) if export_addresses else out

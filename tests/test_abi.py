@@ -1,0 +1,181 @@
+"""C ABI checks that run without a GPU: the library loads, exports every
+entry point include/ramnet.h declares, and rejects bad arguments on the host
+before anything is enqueued (no call here reaches the HIP runtime)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ramnet.h")
+
+
+@pytest.fixture(scope="module")
+def rn():
+    from sparse_slot_recurrent_amd import ramnet
+    if not os.path.exists(ramnet.LIB_PATH):
+        from sparse_slot_recurrent_amd import build
+        build.build()
+    ramnet.load_library()
+    return ramnet
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ramnet_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ramnet_decode_addresses", "ramnet_scan_prefill",
+              "ramnet_step_decode", "ramnet_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(rn):
+    lib = rn.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    assert set(declared_functions()) == set(rn.EXPORTED)
+
+
+def test_version_and_status_strings(rn):
+    lib = rn.load_library()
+    assert lib.ramnet_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert lib.ramnet_status_str(code).decode() != "unknown status"
+
+
+def good(rn, **kw):
+    base = dict(B=2, T=8, H=2, d_p=4, U=5, K=8, d_v=64, in_dtype=rn.BF16,
+                state_dtype=rn.F32, cape=1)
+    base.update(kw)
+    return rn.make_params(**base)
+
+
+FAKE = 1 << 40  # aligned, never dereferenced: validation fails first
+
+
+def call_prefill(rn, p, q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
+                 gamma=FAKE + (3 << 32), g=FAKE + (4 << 32), S=FAKE + (5 << 32),
+                 mass=FAKE + (6 << 32), out=FAKE + (7 << 32), ws=None,
+                 ws_bytes=0, addr_in=None, norm_w=None, pos0=None):
+    lib = rn.load_library()
+    P = lambda x: None if x is None else C.c_void_p(x)
+    st = lib.ramnet_scan_prefill(C.byref(p), P(q), P(k), P(v), P(gamma), P(g),
+                                 P(norm_w), P(pos0), P(S), P(mass), P(out),
+                                 addr_in, None, P(ws), ws_bytes, None)
+    return st, lib.ramnet_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code,msg", [
+    ("M", 1000, -1, "d_p^U"),
+    ("K", 0, -1, "K"),
+    ("K", 2000, -1, "K"),
+    ("d_p", 1, -1, "d_p"),
+    ("U", 0, -1, "U"),
+    ("B", -1, -1, ">= 0"),
+    ("in_dtype", 7, -1, "in_dtype"),
+    ("state_dtype", 3, -1, "state_dtype"),
+    ("cape", 2, -1, "cape"),
+    ("eps_gsu", -1.0, -1, "eps"),
+    ("eps_norm", float("nan"), -1, "eps"),
+    ("d_v", 96, -2, "d_v"),
+    ("d_v", 512, -2, "d_v"),
+])
+def test_bad_params_rejected(rn, field, value, code, msg):
+    p = good(rn)
+    setattr(p, field, value)
+    st, err = call_prefill(rn, p)
+    assert st == code, err
+    assert msg in err
+
+
+def test_unsupported_k_and_dp(rn):
+    p = good(rn, d_p=2, U=10, K=65)
+    st, err = call_prefill(rn, p)
+    assert st == -2 and "KMAX" in err
+    p = good(rn, d_p=16, U=2, K=8)
+    st, err = call_prefill(rn, p)
+    assert st == -2 and "d_p" in err
+
+
+def test_slot_count_limit(rn):
+    p = good(rn, d_p=2, U=31, K=8)
+    st, err = call_prefill(rn, p)
+    assert st == -1 and "2^30" in err
+
+
+def test_null_and_misaligned_pointers(rn):
+    p = good(rn)
+    st, err = call_prefill(rn, p, v=None)
+    assert st == -1 and "v is NULL" in err
+    st, err = call_prefill(rn, p, S=FAKE + (5 << 32) + 4)
+    assert st == -1 and "S is not 16-byte aligned" in err
+
+
+def test_workspace_required_and_sized(rn):
+    p = good(rn)
+    need = rn.workspace_bytes(p, rn.OP_PREFILL)
+    n = 2 * 8 * 2
+    assert need >= 4 * n * 8 * 4
+    st, err = call_prefill(rn, p)
+    assert st == -3 and "workspace" in err
+    st, err = call_prefill(rn, p, ws=FAKE + (9 << 32), ws_bytes=need - 1)
+    assert st == -3
+    assert rn.workspace_bytes(p, rn.OP_DECODE) == 0
+    bad = good(rn, K=0)
+    assert rn.workspace_bytes(bad, rn.OP_PREFILL) == 0
+
+
+def test_overlapping_output_rejected(rn):
+    p = good(rn)
+    need = rn.workspace_bytes(p, rn.OP_PREFILL)
+    st, err = call_prefill(rn, p, out=FAKE + (5 << 32) + 4096,
+                           ws=FAKE + (9 << 32), ws_bytes=need)
+    assert st == -1 and "overlaps" in err
+    st, err = call_prefill(rn, p, mass=FAKE, ws=FAKE + (9 << 32), ws_bytes=need)
+    assert st == -1 and "overlaps" in err
+
+
+def test_empty_inputs_are_a_no_op(rn):
+    for kw in (dict(T=0), dict(B=0), dict(H=0)):
+        p = good(rn, **kw)
+        st, err = call_prefill(rn, p, q=None, k=None, v=None, gamma=None,
+                               g=None, S=None, mass=None, out=None)
+        assert st == 0, err
+    lib = rn.load_library()
+    p = good(rn, T=0)
+    out = rn.Addr(None, None, None, None)
+    assert lib.ramnet_decode_addresses(C.byref(p), None, None, None,
+                                       C.byref(out), None) == 0
+
+
+def test_step_requires_t1_and_pos(rn):
+    lib = rn.load_library()
+    p = good(rn, T=2)
+    P = C.c_void_p
+    st = lib.ramnet_step_decode(C.byref(p), *[P(FAKE + (i << 32)) for i in range(5)],
+                                None, None, *[P(FAKE + ((5 + i) << 32)) for i in range(3)],
+                                None, None, 0, None)
+    assert st == -1 and "T == 1" in lib.ramnet_last_error().decode()
+    p = good(rn, T=1)
+    st = lib.ramnet_step_decode(C.byref(p), *[P(FAKE + (i << 32)) for i in range(5)],
+                                None, None, *[P(FAKE + ((5 + i) << 32)) for i in range(3)],
+                                None, None, 0, None)
+    assert st == -1 and "pos is required" in lib.ramnet_last_error().decode()
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding must not import or load the oracle, and must raise when
+    the HIP library is missing."""
+    src = open(os.path.join(ROOT, "sparse_slot_recurrent_amd", "ramnet.py")).read()
+    assert "oracle" not in src
+    import importlib
+    from sparse_slot_recurrent_amd import ramnet
+    mod = importlib.reload(ramnet)
+    with pytest.raises(RuntimeError, match="missing"):
+        mod._lib = None
+        mod.load_library(os.path.join(ROOT, "does_not_exist.so"))
