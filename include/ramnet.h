@@ -108,9 +108,10 @@ ramnet_status ramnet_decode_addresses(const ramnet_params *p, const void *q,
                                       const void *k, const int32_t *pos0,
                                       const ramnet_addr *out, void *stream);
 
-/* Bytes of workspace `op` needs for `p` (0 for an invalid p).  For
- * RAMNET_OP_PREFILL and RAMNET_OP_STEP the figure assumes addr_out is NULL;
- * with addr_out given, 0 bytes are needed. */
+/* Bytes of workspace `op` needs for `p` (0 for an invalid p): enough for any
+ * call with these parameters.  (A call that exports its addresses through
+ * addr_out, or takes them from addr_in, needs less; the call reports
+ * RAMNET_EWORKSPACE with the exact figure if given too little.) */
 size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op);
 
 /* Prefill (project page, GPU-execution paragraphs: addresses for all tokens
@@ -127,8 +128,14 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op);
  *             be distinct within an address; a slot outside [0, M) is
  *             skipped (treated as weight 0).
  *   addr_out  NULL, or where to export the addresses used.
- *   workspace ramnet_workspace_bytes(p, RAMNET_OP_PREFILL) bytes, or NULL
- *             when that figure is 0 for this call. */
+ *   workspace ramnet_workspace_bytes(p, RAMNET_OP_PREFILL) bytes.  It holds
+ *             the decoded addresses (unless addr_out is given) and, on the
+ *             slot-grouped path, the un-normalised reads and per-token sums
+ *             of squares between the recurrence and the RMSNorm kernel.
+ *             Its contents on entry do not matter.
+ * Results of the slot-grouped path (long sequences whose state slice fits
+ * on chip) can differ between runs in the last bits of fp32 additions: reads
+ * of one token are accumulated in LDS in arrival order. */
 ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
                                   const void *k, const void *v,
                                   const void *gamma, const void *g,

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libramnet.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "scan_serial.hip"]
+SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -104,10 +104,30 @@ size_t st_bytes(const ramnet_params *p) { return p->state_dtype == RAMNET_BF16 ?
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: decoded addresses when the caller neither supplies nor exports
-// them.  Four [n, K] arrays, each 256-byte aligned.
-size_t addr_workspace_bytes(int64_t n, int K) {
-    return 4 * align256(static_cast<size_t>(n) * K * 4);
+// How a layer call runs and what scratch it needs.
+struct LayerPlan {
+    bool chunked;
+    ramnet::ChunkPlan cp;
+    size_t addr_bytes;   // decoded addresses kept in the workspace
+    size_t chunk_bytes;  // chunked-path scratch
+    size_t total() const { return addr_bytes + chunk_bytes; }
+};
+
+
+LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
+    LayerPlan lp{};
+    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
+    const int64_t units = static_cast<int64_t>(p->B) * p->H;
+    const bool sbf = p->state_dtype == RAMNET_BF16;
+    lp.chunked = false;
+    if (!step) {
+        lp.cp = ramnet::plan_chunked(p->M, p->K, p->d_v, p->B, p->T, p->H, sbf);
+        lp.chunked = lp.cp.ok;
+    }
+    lp.addr_bytes = addr_in_ws ? 4 * align256(static_cast<size_t>(n) * p->K * 4) : 0;
+    lp.chunk_bytes =
+        lp.chunked ? ramnet::chunk_workspace_bytes(lp.cp, n, units, p->M, p->d_v, sbf) : 0;
+    return lp;
 }
 
 ramnet_addr carve_addr(void *ws, int64_t n, int K) {
@@ -209,9 +229,9 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sp[ns++] = span("addr_out.r_idx", addr_out->r_idx, nK4);
         sp[ns++] = span("addr_out.r_wt", addr_out->r_wt, nK4);
     }
-    const bool need_ws = decode && !addr_out;
-    if (need_ws) {
-        const size_t need = addr_workspace_bytes(n, p->K);
+    const LayerPlan lp = plan_layer(p, step, decode && !addr_out);
+    const size_t need = lp.total();
+    if (need > 0) {
         if (!ws || ws_bytes < need)
             return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                         ws ? ws_bytes : size_t(0));
@@ -223,7 +243,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     hipStream_t st = static_cast<hipStream_t>(stream);
     ramnet_addr addr;
     if (decode) {
-        addr = addr_out ? *addr_out : carve_addr(ws, n, p->K);
+        addr = lp.addr_bytes ? carve_addr(ws, n, p->K) : *addr_out;
         hipError_t e = ramnet::launch_decode(decode_args(p, q, k, pos, n, p->T, addr), st);
         if (e != hipSuccess) return hip_status(e, "address decoder launch");
     } else {
@@ -251,7 +271,28 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     a.out = out;
     a.eps_gsu = p->eps_gsu;
     a.eps_norm = p->eps_norm;
-    hipError_t e = ramnet::launch_scan_serial(a, st);
+    hipError_t e;
+    if (lp.chunked) {
+        ramnet::ChunkArgs c{};
+        static_cast<ramnet::ScanArgs &>(c) = a;
+        char *cw = static_cast<char *>(ws) + lp.addr_bytes;
+        const bool sbf = p->state_dtype == RAMNET_BF16;
+        if (sbf) {
+            c.rbuf = reinterpret_cast<float *>(cw);
+            cw += align256(static_cast<size_t>(n) * p->d_v * 4);
+        } else {
+            c.rbuf = static_cast<float *>(out);  // fp32 output holds r until normalised
+        }
+        c.sumsq = reinterpret_cast<float *>(cw);
+        cw += align256(static_cast<size_t>(n) * (p->d_v / lp.cp.CG) * 4);
+        c.mass_ws = reinterpret_cast<float *>(cw);
+        c.CG = lp.cp.CG;
+        c.C = lp.cp.C;
+        c.EPT = lp.cp.EPT;
+        e = ramnet::launch_scan_chunked(c, st);
+    } else {
+        e = ramnet::launch_scan_serial(a, st);
+    }
     if (e != hipSuccess) return hip_status(e, "scan launch");
     if (!decode && addr_out) {
         for (int i = 0; i < 4; ++i) {
@@ -311,8 +352,7 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
     if (s != RAMNET_OK) return 0;
     if (op == RAMNET_OP_DECODE) return 0;
     if (op != RAMNET_OP_PREFILL && op != RAMNET_OP_STEP) return 0;
-    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
-    return addr_workspace_bytes(n, p->K);
+    return plan_layer(p, step, true).total();
 }
 
 ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q, const void *k,

@@ -18,12 +18,10 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+// fp32 -> bf16, round to nearest, ties to even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{static_cast<uint16_t>((u >> 16) | 0x40u)};
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bf16_t{static_cast<uint16_t>(u >> 16)};
+    return bf16_t{__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))};
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
@@ -59,5 +57,17 @@ __device__ __forceinline__ float retention(float w, float exp_gamma) {
 }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Retention with the hardware base-2 log and exp: (1 - w)^(exp(gamma)) =
+// 2^(exp(gamma) * log2(1 - w)).  1 - w is rounded to u; the rounding error
+// e = (1 - u) - w is exact (1 >= w), and log2(1 - w) = log2(u) + e / (u ln 2)
+// to first order, which keeps the exponent accurate for small w.
+__device__ __forceinline__ float retention_fast(float w, float exp_gamma) {
+    if (w >= 1.0f) return 0.0f;
+    const float u = 1.0f - w;
+    const float e = (1.0f - u) - w;
+    const float l2 = __builtin_amdgcn_logf(u) + e * __builtin_amdgcn_rcpf(u) * 1.44269504088896341f;
+    return __builtin_amdgcn_exp2f(exp_gamma * l2);
+}
 
 }  // namespace ramnet

