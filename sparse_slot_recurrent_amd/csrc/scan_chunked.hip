@@ -15,10 +15,12 @@
 //      staged in LDS, and the chunk's 2*C*K events (K writes, then K reads
 //      per token) are counted per slot;
 //   2. the counts are scanned into bucket offsets and every event is
-//      scattered into its slot's bucket;
-//   3. thread s sorts its bucket by (token, write before read) and replays
-//      it: a write updates mass and row, a read leaves a snapshot of the row
-//      (storage dtype) in the token's read position;
+//      scattered into its slot's bucket; each event then counts the bucket's
+//      keys below its own (token, write before read) and moves to that rank,
+//      so every bucket is in causal order without a serial sort;
+//   3. thread s replays its bucket: a write updates mass and row, a read
+//      leaves a snapshot of the row (storage dtype) in the token's read
+//      position;
 //   4. one thread per (token, channel) sums rho_k * snapshot_k over the K
 //      reads in rank order; r (fp32) and its sum of squares over the slice go
 //      to global memory.
@@ -105,7 +107,49 @@ __device__ __forceinline__ void store_row(bf16_t *p, int swz, const float (&x)[C
     }
 }
 
-template <typename TIn, typename TS, int CG, int EPT>
+// A 16-byte chunk of a row as fp32 values.
+__device__ __forceinline__ void unpack_chunk(const uint4 &u, float (&v)[4]) {
+    v[0] = __uint_as_float(u.x);
+    v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z);
+    v[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ void unpack_chunk(const uint4 &u, float (&v)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+}
+
+// floor(e / K) for 0 <= e < 2^24 with a precomputed m = ceil(2^32 / K).
+__device__ __forceinline__ int div_by(uint32_t e, uint64_t m) {
+    return static_cast<int>((static_cast<uint64_t>(e) * m) >> 32);
+}
+
+// One event of a slot's replay: a write updates mass and row; a read leaves
+// a snapshot of the row (storage dtype) in its token's read position.
+template <typename TS, int CG>
+__device__ __forceinline__ void replay_event(uint32_t kk, float wv, int K, float eps,
+                                             const float *egb, const float *vbuf, TS *snap,
+                                             float (&x)[CG], float &m) {
+    const int t = static_cast<int>(kk >> 7);
+    if (kk & 64u) {
+        const int row = t * K + static_cast<int>(kk & 63u);
+        store_row<CG>(snap + row * CG, row_swz<TS, CG>(row), x);
+    } else {
+        const float alpha = retention_fast(wv, egb[t]);
+        m = fmaf(alpha, m, wv);
+        const float lam = wv * __builtin_amdgcn_rcpf(m + eps);
+        float vt[CG];
+        load_row<CG>(vbuf + t * CG, row_swz<float, CG>(t), vt);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) x[c] = stored<TS>(fmaf(lam, vt[c] - x[c], x[c]));
+    }
+}
+
+template <typename TIn, typename TS, int CG, int EPT, int NB>
 __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -127,6 +171,7 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
     const int b = unit / a.H, h = unit % a.H;
     const int M = static_cast<int>(a.M);
     const int K = a.K, C = a.C, d_v = a.d_v;
+    const uint64_t kdiv = ((uint64_t(1) << 32) + K - 1) / K;
     const ChunkLayout L = chunk_layout(M, CG, C, K, sizeof(TS));
     int *hist = reinterpret_cast<int *>(smem + L.h_off);
     uint32_t *ekey = reinterpret_cast<uint32_t *>(smem + L.k_off);
@@ -178,7 +223,7 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
             if (e < 2 * nw) {
                 const bool rd = e >= nw;
                 const int ee = rd ? e - nw : e;
-                const int t = ee / K, k = ee - t * K;
+                const int t = div_by(ee, kdiv), k = ee - t * K;
                 const int64_t idx = (th_unit + static_cast<int64_t>(t0 + t) * a.H) * K + k;
                 pf_slot[j] = rd ? a.r_idx[idx] : a.w_idx[idx];
                 pf_wt[j] = rd ? a.r_wt[idx] : a.w_wt[idx];
@@ -220,14 +265,13 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
             if (e < 2 * nw) {
                 const bool rd = e >= nw;
                 const int ee = rd ? e - nw : e;
-                const int t = ee / K, k = ee - t * K;
+                const int t = div_by(ee, kdiv), k = ee - t * K;
                 const int s = pf_slot[j];
-                if (rd) rho[ee] = pf_wt[j];
                 // A zero-weight write changes nothing (alpha = 1, lambda = 0);
                 // a slot outside [0, M) (caller-given addresses) is skipped and
                 // a skipped read contributes nothing.
                 const bool ok = static_cast<uint32_t>(s) < static_cast<uint32_t>(M) && (rd || pf_wt[j] > 0.f);
-                if (rd && !ok) rho[ee] = 0.f;
+                if (rd) rho[ee] = ok ? pf_wt[j] : 0.f;
                 if (ok) {
                     ekk[j] = (((static_cast<uint32_t>(t) << 1) | (rd ? 1u : 0u)) << 6) |
                              static_cast<uint32_t>(k);
@@ -261,72 +305,88 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
             if (hi == M && lo < hi) hist[M] = base;
         }
         __syncthreads();
-        // ---- 2b. scatter events into their buckets
+        // ---- 2b. scatter events into their buckets (arrival order) ...
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (erank[j] >= 0) ekey[hist[pf_slot[j]] + erank[j]] = ekk[j];
+        __syncthreads();
+        // ---- 2c. ... then move each to its causal rank within the bucket:
+        //          the number of the bucket's keys below its own (keys are
+        //          unique within a slot: one write and one read per token)
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             if (erank[j] >= 0) {
-                const int pos = hist[pf_slot[j]] + erank[j];
-                ekey[pos] = ekk[j];
-                ewt[pos] = pf_wt[j];
+                const int beg = hist[pf_slot[j]], n = hist[pf_slot[j] + 1] - beg;
+                int r = 0;
+                for (int i = 0; i < n; ++i) r += ekey[beg + i] < ekk[j] ? 1 : 0;
+                erank[j] = beg + r;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            if (erank[j] >= 0) {
+                ekey[erank[j]] = ekk[j];
+                ewt[erank[j]] = pf_wt[j];
             }
         }
         __syncthreads();
         // ---- 3. next chunk's loads go out now and land during the replay
         if (t0 + C < a.T) prefetch(t0 + C);
-        // Replay: thread s sorts its bucket by (token, write before read) and
-        // applies the events to its row in registers.  A read leaves a
-        // snapshot of the row (storage dtype) for its token.
+        // Replay: thread s applies its bucket, already in causal order, to
+        // its row in registers.
         if (owner) {
             const int beg = hist[tid], n = hist[tid + 1] - beg;
-            for (int i = 1; i < n; ++i) {
-                const uint32_t kk = ekey[beg + i];
-                const float ww = ewt[beg + i];
-                int j = i - 1;
-                while (j >= 0 && ekey[beg + j] > kk) {
-                    ekey[beg + j + 1] = ekey[beg + j];
-                    ewt[beg + j + 1] = ewt[beg + j];
-                    --j;
-                }
-                ekey[beg + j + 1] = kk;
-                ewt[beg + j + 1] = ww;
-            }
-            for (int i = 0; i < n; ++i) {
-                const uint32_t kk = ekey[beg + i];
-                const int t = static_cast<int>(kk >> 7);
-                if (kk & 64u) {
-                    const int row = t * K + static_cast<int>(kk & 63u);
-                    store_row<CG>(snap + row * CG, row_swz<TS, CG>(row), x);
-                } else {
-                    const float wv = ewt[beg + i];
-                    const float alpha = retention_fast(wv, egb[t]);
-                    m = fmaf(alpha, m, wv);
-                    const float lam = wv * __builtin_amdgcn_rcpf(m + a.eps_gsu);
-                    float vt[CG];
-                    load_row<CG>(vbuf + t * CG, row_swz<float, CG>(t), vt);
+            uint32_t kk[NB];
+            float ww[NB];
 #pragma unroll
-                    for (int c = 0; c < CG; ++c) x[c] = stored<TS>(fmaf(lam, vt[c] - x[c], x[c]));
-                }
+            for (int i = 0; i < NB; ++i) {
+                kk[i] = i < n ? ekey[beg + i] : 0u;
+                ww[i] = i < n ? ewt[beg + i] : 0.f;
             }
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                if (i < n) replay_event<TS, CG>(kk[i], ww[i], K, a.eps_gsu, egb, vbuf, snap, x, m);
+            for (int i = NB; i < n; ++i)
+                replay_event<TS, CG>(ekey[beg + i], ewt[beg + i], K, a.eps_gsu, egb, vbuf, snap, x, m);
         }
         __syncthreads();
-        // ---- 4. reads: r = sum_k rho_k * snapshot_k (k in rank order), its
-        //         sum of squares over the slice, both to global memory
-        for (int i = tid; i < Cc * CG; i += kNT) {
-            const int t = i / CG, c = i % CG;
-            float r = 0.f;
-            for (int k = 0; k < K; ++k) {
-                // A read with weight 0 adds nothing; skipped reads (slot
-                // outside [0, M)) have weight 0 and no snapshot.
-                const int row = t * K + k;
-                const float rw = rho[row];
-                if (rw != 0.f) r = fmaf(rw, to_f32(snap[swz_index<TS, CG>(row, c)]), r);
-            }
-            const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
-            a.rbuf[th * d_v + cg * CG + c] = r;
-            float ss = r * r;
+        // ---- 4. reads: r = sum_k rho_k * snapshot_k (k in rank order) for one
+        //         16-byte chunk of channels per thread; r and the sum of
+        //         squares over the slice go to global memory
+        {
+            constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per chunk
+            constexpr int NCH = CG / EPC;                            // chunks per row
+            for (int i = tid; i < Cc * NCH; i += kNT) {
+                const int t = i / NCH, j = i % NCH;
+                float r[EPC];
 #pragma unroll
-            for (int off = CG / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-            if (c == 0) a.sumsq[th * ncg + cg] = ss;
+                for (int c = 0; c < EPC; ++c) r[c] = 0.f;
+                for (int k = 0; k < K; ++k) {
+                    // A read with weight 0 adds nothing; skipped reads (slot
+                    // outside [0, M)) have weight 0 and no snapshot.
+                    const int row = t * K + k;
+                    const float rw = rho[row];
+                    if (rw != 0.f) {
+                        const uint4 u = reinterpret_cast<const uint4 *>(snap + row * CG)[j ^ row_swz<TS, CG>(row)];
+                        float sv[EPC];
+                        unpack_chunk(u, sv);
+#pragma unroll
+                        for (int c = 0; c < EPC; ++c) r[c] = fmaf(rw, sv[c], r[c]);
+                    }
+                }
+                const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
+                float *dst = a.rbuf + th * d_v + cg * CG + j * EPC;
+#pragma unroll
+                for (int c = 0; c < EPC; c += 4)
+                    *reinterpret_cast<float4 *>(dst + c) = make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
+                float ss = 0.f;
+#pragma unroll
+                for (int c = 0; c < EPC; ++c) ss = fmaf(r[c], r[c], ss);
+#pragma unroll
+                for (int off = NCH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                if (j == 0) a.sumsq[th * ncg + cg] = ss;
+            }
         }
         for (int i = tid; i <= M; i += kNT) hist[i] = 0;
         __syncthreads();
@@ -376,7 +436,8 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__
 template <typename TIn, typename TS, int CG, int EPT>
 hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const size_t lds = chunk_layout(a.M, CG, a.C, a.K, sizeof(TS)).total;
-    auto kern = scan_chunked_kernel<TIn, TS, CG, EPT>;
+    constexpr int NB = EPT >= 8 ? 16 : 8;  // bucket entries held in registers
+    auto kern = scan_chunked_kernel<TIn, TS, CG, EPT, NB>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
