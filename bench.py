@@ -51,8 +51,11 @@ def byte_model(w, kind: str):
     # the rows the token-heads touch (prefill of a small state); otherwise
     # only the touched rows count (decode, large state).
     state = min(once, rows)
-    return {"decode_addresses": dec, "scan": io + state,
-            "total": dec + io + state, "state_term": state}
+    out = {"decode_addresses": dec, "scan": io + state,
+           "total": dec + io + state, "state_term": state}
+    if kind == "decode":
+        out["step_fused"] = out["total"]  # one kernel does the whole step
+    return out
 
 
 def cpu_info():
@@ -186,14 +189,17 @@ def bench_prefill(torch, rn, w, steps, warmup):
 
 
 def bench_decode(torch, rn, w, steps, warmup):
+    """1024 dependent decoding steps (one fused kernel each) from a
+    pre-filled state, captured in one HIP graph; eager launches are timed
+    too.  Returns (ms per step from the graph, per-kernel ms, tokens per
+    step, extra fields)."""
     from sparse_slot_recurrent_amd import synth
     init = synth.make_inputs(w, T=1)
     S = to_dev(torch, init["S0"], "bf16")
     mass = to_dev(torch, init["m0"], "f32")
     pos0 = torch.from_numpy(init["pos0"]).cuda()
     del init
-    # distinct per-step inputs for every timed step, drawn on the device
-    n_in = steps + warmup
+    # distinct per-step inputs for every step, drawn on the device
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
     bdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
@@ -201,45 +207,48 @@ def bench_decode(torch, rn, w, steps, warmup):
     def normal(*shape, sigma=1.0):
         return (torch.randn(*shape, generator=gen, device="cuda") * sigma).to(bdt)
 
-    q = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
-    k = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
-    v = normal(n_in, w.B, w.H, w.d_v)
-    gam = normal(n_in, w.B, w.H)
-    g = normal(n_in, w.B, w.H, w.d_v)
-    pos = (pos0[None, :] + torch.arange(n_in, device="cuda", dtype=torch.int32)[:, None]).contiguous()
+    q = normal(steps, w.B, w.H, w.L, sigma=w.logit_sigma)
+    k = normal(steps, w.B, w.H, w.L, sigma=w.logit_sigma)
+    v = normal(steps, w.B, w.H, w.d_v)
+    gam = normal(steps, w.B, w.H)
+    g = normal(steps, w.B, w.H, w.d_v)
+    pos = (pos0[None, :] + torch.arange(steps, device="cuda", dtype=torch.int32)[:, None]).contiguous()
     sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
     out = torch.empty((w.B, w.H, w.d_v), dtype=sdt, device="cuda")
     plan = rn.StepPlan(w.B, w.H, w.d_p, w.U, w.K, w.d_v,
                        rn.BF16 if w.in_dtype == "bf16" else rn.F32,
                        rn.BF16 if w.state_dtype == "bf16" else rn.F32,
                        cape=w.cape, eps_gsu=w.eps_gsu, eps_norm=w.eps_norm)
-    addr = rn.new_addresses((w.B, 1, w.H, w.K), "cuda")
 
     def step(i):
         plan(q[i], k[i], v[i], gam[i], g[i], pos[i], S, mass, out)
 
-    for i in range(warmup):
-        step(steps + i)
+    for i in range(min(warmup, steps)):
+        step(i)
     torch.cuda.synchronize()
-    ms = time_loop(torch, step, steps)
-
-    def dec(i):
-        rn.decode_addresses(q[i][:, None], k[i][:, None], d_p=w.d_p, U=w.U,
-                            K=w.K, cape=w.cape, pos0=pos[i], out=addr)
-
-    ms_dec = time_loop(torch, dec, steps)
-    # the step's scan on given addresses: prefill path with T = 1
-    pplan = rn.PrefillPlan(w.B, 1, w.H, w.d_p, w.U, w.K, w.d_v,
-                           rn.BF16, rn.BF16, cape=w.cape)
-    out4 = out[:, None]
-
-    def scan(i):
-        pplan(q[i][:, None], k[i][:, None], v[i][:, None], gam[i][:, None],
-              g[i][:, None], S, mass, out4, addr_in=addr)
-
-    ms_scan = time_loop(torch, scan, steps)
+    ms_eager = time_loop(torch, step, steps)
     torch.cuda.synchronize()
-    return ms, {"decode_addresses": ms_dec, "scan": ms_scan}, w.B
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(st)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(st)
+    e1.synchronize()
+    ms_graph = e0.elapsed_time(e1) / (reps * steps)
+    return ms_graph, {"step_fused": ms_graph}, w.B, {"ms_per_step_eager": ms_eager}
 
 
 def main():
@@ -265,11 +274,12 @@ def main():
     w = synth.WORKLOADS[args.workload]
     kind = "decode" if w.steps else "prefill"
     steps = args.steps or (w.steps if kind == "decode" else 10)
-    warmup = args.warmup if args.warmup is not None else (16 if kind == "decode" else 2)
+    warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
+    extra = {}
     if kind == "decode":
-        ms, kms, tokens = bench_decode(torch, rn, w, steps, warmup)
+        ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)
     else:
         ms, kms, tokens = bench_prefill(torch, rn, w, steps, warmup)
     value = tokens / (ms / 1e3)
@@ -301,6 +311,7 @@ def main():
         "algorithmic_bytes": bm,
         "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
+    line.update(extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, kind)
     print(json.dumps(line), flush=True)

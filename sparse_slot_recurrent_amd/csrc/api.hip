@@ -124,7 +124,9 @@ LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
         lp.cp = ramnet::plan_chunked(p->M, p->K, p->d_v, p->B, p->T, p->H, sbf);
         lp.chunked = lp.cp.ok;
     }
-    lp.addr_bytes = addr_in_ws ? 4 * align256(static_cast<size_t>(n) * p->K * 4) : 0;
+    // The fused decoding step keeps its addresses on chip.
+    const bool fused_step = step && ramnet::step_fused_supported(p->K, p->d_p, p->U, p->d_v, p->state_dtype == RAMNET_BF16);
+    lp.addr_bytes = addr_in_ws && !fused_step ? 4 * align256(static_cast<size_t>(n) * p->K * 4) : 0;
     lp.chunk_bytes =
         lp.chunked ? ramnet::chunk_workspace_bytes(lp.cp, n, units, p->M, p->d_v, sbf) : 0;
     return lp;
@@ -241,6 +243,36 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     if ((s = check_overlaps(sp, ns, first_written))) return s;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (step && ramnet::step_fused_supported(p->K, p->d_p, p->U, p->d_v, p->state_dtype == RAMNET_BF16)) {
+        ramnet::StepArgs sa{};
+        sa.B = p->B;
+        sa.H = p->H;
+        sa.M = p->M;
+        sa.K = p->K;
+        sa.d_v = p->d_v;
+        sa.U = p->U;
+        sa.d_p = p->d_p;
+        sa.cape = p->cape;
+        sa.in_bf16 = p->in_dtype == RAMNET_BF16;
+        sa.state_bf16 = p->state_dtype == RAMNET_BF16;
+        sa.q = q;
+        sa.k = k;
+        sa.v = v;
+        sa.gamma = gamma;
+        sa.g = g;
+        sa.norm_w = norm_w;
+        sa.pos = pos;
+        sa.S = S;
+        sa.mass = mass;
+        sa.out = out;
+        sa.out_idx[0] = addr_out ? addr_out->w_idx : nullptr;
+        sa.out_idx[1] = addr_out ? addr_out->r_idx : nullptr;
+        sa.out_wt[0] = addr_out ? addr_out->w_wt : nullptr;
+        sa.out_wt[1] = addr_out ? addr_out->r_wt : nullptr;
+        sa.eps_gsu = p->eps_gsu;
+        sa.eps_norm = p->eps_norm;
+        return hip_status(ramnet::launch_step_fused(sa, st), "decode step launch");
+    }
     ramnet_addr addr;
     if (decode) {
         addr = lp.addr_bytes ? carve_addr(ws, n, p->K) : *addr_out;

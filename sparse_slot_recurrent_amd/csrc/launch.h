@@ -90,6 +90,25 @@ __host__ __device__ inline ChunkLayout chunk_layout(int64_t M, int CG, int C, in
     return L;
 }
 
+// One fused decoding step (decode + CAPE + GSU + read + norm + gate).
+struct StepArgs {
+    int B, H;
+    int64_t M;
+    int K, d_v, U, d_p, cape;
+    bool in_bf16, state_bf16;
+    const void *q, *k, *v, *gamma, *g;
+    const float *norm_w;
+    const int32_t *pos;
+    void *S;
+    float *mass;
+    void *out;
+    int32_t *out_idx[2];  // write, read addresses [B,H,K] or NULL
+    float *out_wt[2];
+    float eps_gsu, eps_norm;
+};
+bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
+hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
+
 ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16);
 hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st);
 

@@ -1,0 +1,528 @@
+// One decoding step for gfx950, fused: address decoding, CAPE, the Gated
+// Sparse Update, the read, RMSNorm and the gate for one token of each of B
+// sequences (RAM-Net project page, GPU-execution paragraphs: decoding
+// accesses the current token's slots directly, with no pass over the state).
+//
+// One wave serves UPW = 32 / KP (batch, head) units, KP = K rounded up to a
+// power of two.
+//  * Decoding: each of the wave's 2 * UPW addresses (key -> write, query ->
+//    read) gets KP lanes; lane r holds entry r of the kept prefixes (sorted
+//    by weight desc, prefix asc).  Per level, lane r's candidates are its
+//    prefix extended by each digit value; candidate list a (prefix x p_u[a])
+//    is sorted across the lanes because the prefixes are.  The next beam is
+//    the first K entries of the merge of the d_p lists, built by a tree of
+//    bitonic merges: list B reversed against list A, the better of each
+//    pair, then log2(KP) compare-exchange stages.  This replaces K serial
+//    merge steps per level by log2(KP) parallel ones.  The decision is taken
+//    in fp64 (softmax summed in digit order, as the reference definition
+//    writes it).  The digit distributions of all levels are computed first,
+//    one (address, level, digit) per lane, and kept in LDS.
+//  * Update and read, one round trip to HBM: the masses of the write slots
+//    and every write row and read row of the wave's units are loaded at
+//    once.  Rows move in 16-byte pieces (12 where 16 would not tile a wave):
+//    LPR lanes per row, 64 / LPR rows per load instruction.  The read is
+//    taken from the rows as they were before this token's writes, plus, for
+//    each write slot, the read's weight on that slot times the change the
+//    write made; this equals the read after the writes without a second
+//    pass over memory.  Every load is consumed before the first store.  The
+//    sub-row partial reads are summed through LDS; RMSNorm over d_v by a
+//    wave reduction; the gate.
+#include "device_common.h"
+#include "launch.h"
+
+namespace ramnet {
+namespace {
+
+// Most digits an address has: U * d_p with d_p^U <= 2^30 peaks at 80 (d_p 8).
+constexpr int kMaxDigits = 80;
+
+__device__ __forceinline__ int cape_move_rt(int slot, int64_t pos, int U, int dp) {
+    const unsigned s = static_cast<unsigned>(((pos % dp) + dp) % dp);
+    if (s == 0) return slot;
+    unsigned x = static_cast<unsigned>(slot), moved = 0, place = 1;
+    for (int u = 0; u < U; ++u) {
+        const unsigned d = x % dp;
+        x /= dp;
+        moved += ((d + s) % dp) * place;
+        place *= dp;
+    }
+    return static_cast<int>(moved);
+}
+
+// CPL adjacent channels of one row as a single vector access.
+template <typename T, int CPL>
+struct RowVec {
+    T e[CPL];
+};
+
+// (weight, prefix) entries; invalid entries have weight -1 and prefix -1.
+struct Ent {
+    double w;
+    int p;
+};
+
+// Weight desc, then prefix asc.  Valid weights are >= 0 and an invalid
+// prefix is the largest unsigned value, so invalid entries rank last.
+// Branch-free: both comparisons are evaluated.
+__device__ __forceinline__ bool better(const Ent &a, const Ent &b) {
+    const bool gt = a.w > b.w, eq = a.w == b.w;
+    const bool lt = static_cast<unsigned>(a.p) < static_cast<unsigned>(b.p);
+    return gt | (eq & lt);
+}
+
+// Value of lane (r ^ J) within groups of KP lanes, by DPP inside 16-lane
+// rows (xor 1 and 2: quad permutes; xor 4: row shift left or right by 4;
+// xor 8: row rotate by 8) and ds_swizzle across the two rows of a 32-lane
+// group (xor 16).  J == KP - 1 reverses the group (row mirrors).
+template <int KP, int J>
+__device__ __forceinline__ int xchg(int v) {
+    if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (J == 4) {
+        const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // lane i+4
+        const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // lane i-4
+        return (__lane_id() & 4) ? dn : up;
+    } else if constexpr (J == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+    else if constexpr (J == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);
+    else if constexpr (J == 7 && KP == 8) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    else if constexpr (J == 15 && KP == 16) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+    else if constexpr (J == 31 && KP == 32)
+        return __builtin_amdgcn_ds_swizzle(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false), 0x401F);
+    else return __shfl_xor(v, J, kWave);
+}
+
+template <int KP, int J>
+__device__ __forceinline__ Ent xchg_e(const Ent &e) {
+    Ent o;
+    const int lo = xchg<KP, J>(__double2loint(e.w));
+    const int hi = xchg<KP, J>(__double2hiint(e.w));
+    o.w = __hiloint2double(hi, lo);
+    o.p = xchg<KP, J>(e.p);
+    return o;
+}
+
+template <int KP, int J>
+__device__ __forceinline__ Ent bitonic_stage(Ent e, int r) {
+    const Ent o = xchg_e<KP, J>(e);
+    const bool keep_better = (r & J) == 0;
+    const bool ob = better(o, e);
+    return (keep_better == ob) ? o : e;
+}
+
+// Sorts a bitonic sequence held one entry per lane across KP lanes into
+// rank order (best at r = 0).
+template <int KP>
+__device__ __forceinline__ Ent bitonic_finish(Ent e, int r) {
+    if constexpr (KP >= 32) e = bitonic_stage<KP, 16>(e, r);
+    if constexpr (KP >= 16) e = bitonic_stage<KP, 8>(e, r);
+    if constexpr (KP >= 8) e = bitonic_stage<KP, 4>(e, r);
+    e = bitonic_stage<KP, 2>(e, r);
+    e = bitonic_stage<KP, 1>(e, r);
+    return e;
+}
+
+// First KP entries, in rank order, of two rank-ordered lists A and B held
+// one entry per lane.
+template <int KP>
+__device__ __forceinline__ Ent merge_top(const Ent &a, const Ent &b, int r) {
+    const Ent brev = xchg_e<KP, KP - 1>(b);   // lane r sees B[KP-1-r]
+    const Ent c = better(brev, a) ? brev : a;  // bitonic: the top KP of A u B
+    return bitonic_finish<KP>(c, r);
+}
+
+// Row access geometry for d_v channels of type TS: each lane moves VW bytes
+// of one row (16, or 12 where 16-byte pieces would not tile the wave), LPR
+// lanes cover a row and one instruction moves RPI = 64 / LPR rows.
+template <typename TS, int DV>
+struct RowGeom {
+    static constexpr int kRowBytes = DV * static_cast<int>(sizeof(TS));
+    static constexpr int VW = (kWave % (kRowBytes / 16) == 0) ? 16 : 12;
+    static constexpr int NW = VW / 4;
+    static constexpr int LPR = kRowBytes / VW;
+    static constexpr int RPI = kWave / LPR;
+    static constexpr int CPL = VW / static_cast<int>(sizeof(TS));
+    static_assert(kRowBytes % VW == 0 && kWave % LPR == 0, "row geometry");
+};
+
+// Row registers one unit needs per address kind, and how many units are held
+// at once (rows of at most 128 registers in flight per lane).
+template <typename TS, int KP, int DV>
+struct RowPlan {
+    using G = RowGeom<TS, DV>;
+    static constexpr int UPW = kWave / (2 * KP);
+    static constexpr int NJ = (KP + G::RPI - 1) / G::RPI;  // row loads per unit and kind
+    static constexpr int PER = NJ * G::NW;
+    static constexpr bool kFits = PER <= 64;
+    static constexpr int UB = PER <= 16 ? (UPW < 4 ? UPW : 4) : PER <= 32 ? (UPW < 2 ? UPW : 2) : 1;
+};
+
+template <int NW>
+struct alignas(NW == 4 ? 16 : 4) Words {
+    uint32_t w[NW];
+};
+
+template <typename TS, int NW>
+__device__ __forceinline__ void unpack(const Words<NW> &x, float *f) {
+    if constexpr (sizeof(TS) == 2) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            f[2 * i] = __uint_as_float(x.w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(x.w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) f[i] = __uint_as_float(x.w[i]);
+    }
+}
+
+// Rounds to TS; f is replaced by the stored values.
+template <typename TS, int NW>
+__device__ __forceinline__ Words<NW> pack(float *f) {
+    Words<NW> x;
+    if constexpr (sizeof(TS) == 2) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t lo = bf16_rne(f[2 * i]).bits, hi = bf16_rne(f[2 * i + 1]).bits;
+            x.w[i] = lo | (hi << 16);
+            f[2 * i] = __uint_as_float(lo << 16);
+            f[2 * i + 1] = __uint_as_float(hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) x.w[i] = __float_as_uint(f[i]);
+    }
+    return x;
+}
+
+// Byte offsets of the kernel's LDS arrays.
+struct StepLds {
+    int idx, wt, lg, pr, lam, cr, red, total;
+};
+__host__ __device__ constexpr StepLds step_lds(int UPW, int K, int L, int RPI, int DV) {
+    StepLds o{};
+    o.idx = 0;                                   // int   [UPW][2][K]
+    o.wt = o.idx + UPW * 2 * K * 4;              // float [UPW][2][K]
+    o.lg = o.wt + UPW * 2 * K * 4;               // float [UPW][2][L]
+    o.pr = (o.lg + UPW * 2 * L * 4 + 7) & ~7;    // double[UPW][2][L]
+    o.lam = o.pr + UPW * 2 * L * 8;              // float [UPW][K]
+    o.cr = o.lam + UPW * K * 4;                  // float [UPW][K]
+    o.red = o.cr + UPW * K * 4;                  // float [RPI][DV]
+    o.total = o.red + RPI * DV * 4;
+    return o;
+}
+
+template <typename TIn, typename TS, int KP, int DV>
+__global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
+    using G = RowGeom<TS, DV>;
+    using P = RowPlan<TS, KP, DV>;
+    constexpr int UPW = P::UPW, NW = G::NW, CPL = G::CPL, LPR = G::LPR, RPI = G::RPI;
+    constexpr int NJ = P::NJ, UB = P::UB;
+    constexpr int CPO = DV / kWave;  // output channels per lane
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x;
+    const int K = a.K, U = a.U, dp = a.d_p;
+    const int64_t M = a.M;
+    const int units = a.B * a.H;
+    const int u0 = blockIdx.x * UPW;
+    const int nu = min(UPW, units - u0);
+    const int L = U * dp;
+    const StepLds lo = step_lds(UPW, K, L, RPI, DV);
+    int *sidx = reinterpret_cast<int *>(smem + lo.idx);
+    float *swt = reinterpret_cast<float *>(smem + lo.wt);
+    float *slg = reinterpret_cast<float *>(smem + lo.lg);
+    double *spr = reinterpret_cast<double *>(smem + lo.pr);
+    float *slam = reinterpret_cast<float *>(smem + lo.lam);
+    float *scr = reinterpret_cast<float *>(smem + lo.cr);
+    float *sred = reinterpret_cast<float *>(smem + lo.red);
+
+    // every logit the wave decodes, fetched at once
+    for (int i = lane; i < UPW * 2 * L; i += kWave) {
+        const int g = i / L, e = i - g * L;
+        const int unit = min(u0 + g / 2, units - 1);
+        const TIn *src = static_cast<const TIn *>(g % 2 ? a.q : a.k);
+        slg[i] = to_f32(src[static_cast<int64_t>(unit) * L + e]);
+    }
+    __syncthreads();
+    // digit distributions of every block, one (address, block, digit) per
+    // lane: exp(l - max) in fp64, then the division by the sum taken in
+    // digit order
+    for (int i = lane; i < UPW * 2 * L; i += kWave) {
+        const float *lv = slg + (i - i % dp);
+        float mx = lv[0];
+        for (int d = 1; d < dp; ++d) mx = fmaxf(mx, lv[d]);
+        spr[i] = exp(static_cast<double>(slg[i]) - static_cast<double>(mx));
+    }
+    __syncthreads();
+    double prv[(UPW * 2 * kMaxDigits + kWave - 1) / kWave];
+#pragma unroll
+    for (int t = 0; t < (UPW * 2 * kMaxDigits + kWave - 1) / kWave; ++t) {
+        const int i = lane + t * kWave;
+        if (i < UPW * 2 * L) {
+            const double *ev = spr + (i - i % dp);
+            double sum = 0.0;
+            for (int d = 0; d < dp; ++d) sum += ev[d];
+            prv[t] = spr[i] / sum;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < (UPW * 2 * kMaxDigits + kWave - 1) / kWave; ++t) {
+        const int i = lane + t * kWave;
+        if (i < UPW * 2 * L) spr[i] = prv[t];
+    }
+    __syncthreads();
+
+    // ---------------- decoding: group g = address, lane r = beam rank
+    {
+        const int g = lane / KP, r = lane % KP;
+        const int ul = g / 2, which = g % 2;  // which 0: key -> write, 1: query -> read
+        const int unit = min(u0 + ul, units - 1);  // spare groups decode a copy, never stored
+        const double *pg = spr + g * L;
+        Ent beam;
+        beam.w = r == 0 ? 1.0 : -1.0;
+        beam.p = r == 0 ? 0 : -1;
+        for (int u = 0; u < U; ++u) {
+            double pr[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) pr[d] = d < dp ? pg[u * dp + d] : 0.0;
+            // candidate lists and their merge tree
+            Ent lst[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const bool ok = beam.p >= 0 && d < dp;
+                lst[d].w = ok ? beam.w * pr[d] : -1.0;
+                lst[d].p = ok ? beam.p * dp + d : -1;
+            }
+            Ent res = merge_top<KP>(lst[0], lst[1], r);
+            if (dp > 2) res = merge_top<KP>(res, merge_top<KP>(lst[2], lst[3], r), r);
+            if (dp > 4)
+                res = merge_top<KP>(res, merge_top<KP>(merge_top<KP>(lst[4], lst[5], r),
+                                                       merge_top<KP>(lst[6], lst[7], r), r), r);
+            if (r >= K) {  // keep K entries
+                res.w = -1.0;
+                res.p = -1;
+            }
+            beam = res;
+        }
+        // CAPE and hand-off
+        const int b = unit / a.H;
+        const int64_t pos = a.pos ? a.pos[b] : 0;
+        if (u0 + ul < units && r < K) {
+            const int slot = a.cape ? cape_move_rt(beam.p, pos, U, dp) : beam.p;
+            const float wt = static_cast<float>(beam.w);
+            sidx[(ul * 2 + which) * K + r] = slot;
+            swt[(ul * 2 + which) * K + r] = wt;
+            if (a.out_idx[which]) {
+                a.out_idx[which][static_cast<int64_t>(unit) * K + r] = slot;
+                a.out_wt[which][static_cast<int64_t>(unit) * K + r] = wt;
+            }
+        }
+    }
+    __syncthreads();
+
+    const TIn *v = static_cast<const TIn *>(a.v);
+    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    const TIn *gg = static_cast<const TIn *>(a.g);
+    TS *S = static_cast<TS *>(a.S);
+    TS *out = static_cast<TS *>(a.out);
+    const int npair = nu * K;  // <= 32
+
+    // ---------------- mass of every write pair: lane l < npair holds pair
+    // (unit l / K, rank l % K); the load is issued before the row loads
+    const int pu = lane / K, pk = lane - (lane / K) * K;
+    float wgt = 0.f, mold = 0.f;
+    float *mp = nullptr;
+    int wsl = 0;
+    if (lane < npair) {
+        wsl = sidx[(pu * 2) * K + pk];
+        wgt = swt[(pu * 2) * K + pk];
+        if (wgt > 0.f) {  // w = 0: alpha = 1, lambda = 0, nothing changes
+            mp = a.mass + static_cast<int64_t>(u0 + pu) * M + wsl;
+            mold = *mp;
+        }
+    }
+
+    // row lanes: sub-row `sub` of each row instruction, channels c0..c0+CPL
+    const int sub = lane / LPR, c0 = (lane - sub * LPR) * CPL;
+
+#pragma unroll
+    for (int b0 = 0; b0 < UPW; b0 += UB) {
+        // ---- every write row and read row of UB units, in flight at once
+        Words<NW> wrow[UB][NJ], rrow[UB][NJ];
+        float vin[UB][CPL];
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+            const int ul = b0 + i;
+            if (ul < nu) {
+                const TS *Su = S + static_cast<int64_t>(u0 + ul) * M * DV;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int k = j * RPI + sub;
+                    if (k < K) {
+                        const int ws = sidx[(ul * 2) * K + k], rs = sidx[(ul * 2 + 1) * K + k];
+                        wrow[i][j] = *reinterpret_cast<const Words<NW> *>(Su + static_cast<int64_t>(ws) * DV + c0);
+                        rrow[i][j] = *reinterpret_cast<const Words<NW> *>(Su + static_cast<int64_t>(rs) * DV + c0);
+                    }
+                }
+                const TIn *vu = v + static_cast<int64_t>(u0 + ul) * DV + c0;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) vin[i][c] = to_f32(vu[c]);
+            }
+        }
+
+        if (b0 == 0) {
+            // ---- masses and rates (pair lanes); the read's weight on each
+            // write slot of its unit, for the read-after-write correction
+            float lam = 0.f, cr = 0.f;
+            if (lane < npair) {
+                if (wgt > 0.f) {
+                    const float eg = expf(to_f32(gam[u0 + pu]));
+                    const float mnew = fmaf(retention_fast(wgt, eg), mold, wgt);
+                    *mp = mnew;
+                    lam = wgt * __builtin_amdgcn_rcpf(mnew + a.eps_gsu);
+                }
+                const int rb = (pu * 2 + 1) * K;
+                for (int kk = 0; kk < K; ++kk)
+                    if (sidx[rb + kk] == wsl) cr += swt[rb + kk];
+                slam[lane] = lam;
+                scr[lane] = cr;
+            }
+            __syncthreads();
+        }
+
+        // ---- per unit: the read of the old contents, the update, the
+        // read's share of the change, RMSNorm and the gate
+#pragma unroll
+        for (int i = 0; i < UB; ++i) {
+            const int ul = b0 + i;
+            if (ul >= nu) break;
+            float acc[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+            // all loads are consumed before the first store of the unit
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int k = j * RPI + sub;
+                if (k < K) {
+                    const float rho = swt[(ul * 2 + 1) * K + k];
+                    float x[CPL];
+                    unpack<TS, NW>(rrow[i][j], x);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[c] = fmaf(rho, x[c], acc[c]);
+                }
+            }
+            TS *Su = S + static_cast<int64_t>(u0 + ul) * M * DV;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int k = j * RPI + sub;
+                if (k < K) {
+                    const float lam = slam[ul * K + k];
+                    if (lam != 0.f) {
+                        const float cr = scr[ul * K + k];
+                        float x[CPL], y[CPL];
+                        unpack<TS, NW>(wrow[i][j], x);
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) y[c] = fmaf(lam, vin[i][c] - x[c], x[c]);
+                        const Words<NW> nw = pack<TS, NW>(y);
+                        const int ws = sidx[(ul * 2) * K + k];
+                        *reinterpret_cast<Words<NW> *>(Su + static_cast<int64_t>(ws) * DV + c0) = nw;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) acc[c] = fmaf(cr, y[c] - x[c], acc[c]);
+                    }
+                }
+            }
+            // sum over the RPI sub-rows, then one lane per CPO output channels
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) sred[sub * DV + c0 + c] = acc[c];
+            __syncthreads();
+            const int unit = u0 + ul;
+            float r[CPO];
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPO; ++c) {
+                const int ch = lane * CPO + c;
+                float t = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < RPI; ++s2) t += sred[s2 * DV + ch];
+                r[c] = t;
+                ss = fmaf(t, t, ss);
+            }
+            __syncthreads();
+            ss = wave_sum(ss);
+            const float den = ss / static_cast<float>(DV) + a.eps_norm;
+            const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
+            const TIn *gu = gg + static_cast<int64_t>(unit) * DV + lane * CPO;
+            TS *ou = out + static_cast<int64_t>(unit) * DV + lane * CPO;
+#pragma unroll
+            for (int c = 0; c < CPO; ++c) {
+                const float om = a.norm_w ? a.norm_w[lane * CPO + c] : 1.0f;
+                ou[c] = from_f32<TS>(r[c] * inv * om * sigmoid(to_f32(gu[c])));
+            }
+        }
+    }
+}
+
+template <typename TIn, typename TS, int KP, int DV>
+hipError_t launch_kd(const StepArgs &a, hipStream_t st) {
+    using P = RowPlan<TS, KP, DV>;
+    if constexpr (!P::kFits) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr int UPW = P::UPW;
+        const StepLds lo = step_lds(UPW, a.K, a.U * a.d_p, RowGeom<TS, DV>::RPI, DV);
+        const int units = a.B * a.H;
+        const unsigned grid = static_cast<unsigned>((units + UPW - 1) / UPW);
+        hipLaunchKernelGGL((step_fused_kernel<TIn, TS, KP, DV>), dim3(grid), dim3(kWave),
+                           static_cast<size_t>(lo.total), st, a);
+        return hipGetLastError();
+    }
+}
+
+template <typename TIn, typename TS, int KP>
+hipError_t launch_k(const StepArgs &a, hipStream_t st) {
+    switch (a.d_v) {
+        case 64: return launch_kd<TIn, TS, KP, 64>(a, st);
+        case 128: return launch_kd<TIn, TS, KP, 128>(a, st);
+        case 192: return launch_kd<TIn, TS, KP, 192>(a, st);
+        case 256: return launch_kd<TIn, TS, KP, 256>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename TIn, typename TS>
+hipError_t launch_ts(const StepArgs &a, hipStream_t st) {
+    if (a.K <= 8) return launch_k<TIn, TS, 8>(a, st);
+    if (a.K <= 16) return launch_k<TIn, TS, 16>(a, st);
+    return launch_k<TIn, TS, 32>(a, st);
+}
+
+template <typename TS, int KP>
+constexpr bool fits_any(int d_v) {
+    return d_v == 64    ? RowPlan<TS, KP, 64>::kFits
+           : d_v == 128 ? RowPlan<TS, KP, 128>::kFits
+           : d_v == 192 ? RowPlan<TS, KP, 192>::kFits
+                        : RowPlan<TS, KP, 256>::kFits;
+}
+
+template <typename TS>
+bool fits(int K, int d_v) {
+    return K <= 8 ? fits_any<TS, 8>(d_v) : K <= 16 ? fits_any<TS, 16>(d_v) : fits_any<TS, 32>(d_v);
+}
+
+}  // namespace
+
+bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16) {
+    if (K < 1 || K > 32 || d_p > 8 || U * d_p > kMaxDigits) return false;
+    if (d_v != 64 && d_v != 128 && d_v != 192 && d_v != 256) return false;
+    return state_bf16 ? fits<bf16_t>(K, d_v) : fits<float>(K, d_v);
+}
+
+hipError_t launch_step_fused(const StepArgs &a, hipStream_t st) {
+    if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
+    if (!step_fused_supported(a.K, a.d_p, a.U, a.d_v, a.state_bf16)) return hipErrorInvalidValue;
+    if (a.in_bf16)
+        return a.state_bf16 ? launch_ts<bf16_t, bf16_t>(a, st) : launch_ts<bf16_t, float>(a, st);
+    return a.state_bf16 ? launch_ts<float, bf16_t>(a, st) : launch_ts<float, float>(a, st);
+}
+
+}  // namespace ramnet
