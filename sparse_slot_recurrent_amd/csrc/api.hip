@@ -127,8 +127,7 @@ LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
     // The fused decoding step keeps its addresses on chip.
     const bool fused_step = step && ramnet::step_fused_supported(p->K, p->d_p, p->U, p->d_v, p->state_dtype == RAMNET_BF16);
     lp.addr_bytes = addr_in_ws && !fused_step ? 4 * align256(static_cast<size_t>(n) * p->K * 4) : 0;
-    lp.chunk_bytes =
-        lp.chunked ? ramnet::chunk_workspace_bytes(lp.cp, n, units, p->M, p->d_v, sbf) : 0;
+    lp.chunk_bytes = lp.chunked ? ramnet::chunk_workspace_bytes(lp.cp) : 0;
     return lp;
 }
 
@@ -307,20 +306,19 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     if (lp.chunked) {
         ramnet::ChunkArgs c{};
         static_cast<ramnet::ScanArgs &>(c) = a;
+        c.p = lp.cp;
         char *cw = static_cast<char *>(ws) + lp.addr_bytes;
-        const bool sbf = p->state_dtype == RAMNET_BF16;
-        if (sbf) {
+        if (lp.cp.ws_rbuf) {
             c.rbuf = reinterpret_cast<float *>(cw);
-            cw += align256(static_cast<size_t>(n) * p->d_v * 4);
+            cw += lp.cp.ws_rbuf;
         } else {
             c.rbuf = static_cast<float *>(out);  // fp32 output holds r until normalised
         }
         c.sumsq = reinterpret_cast<float *>(cw);
-        cw += align256(static_cast<size_t>(n) * (p->d_v / lp.cp.CG) * 4);
+        cw += lp.cp.ws_sumsq;
         c.mass_ws = reinterpret_cast<float *>(cw);
-        c.CG = lp.cp.CG;
-        c.C = lp.cp.C;
-        c.EPT = lp.cp.EPT;
+        cw += lp.cp.ws_mass;
+        c.plan = reinterpret_cast<unsigned char *>(cw);
         e = ramnet::launch_scan_chunked(c, st);
     } else {
         e = ramnet::launch_scan_serial(a, st);

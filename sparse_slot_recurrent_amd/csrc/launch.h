@@ -41,54 +41,42 @@ size_t scan_state_lds_bytes(int64_t M, int d_v, bool state_bf16);
 bool scan_state_fits_lds(int64_t M, int d_v, bool state_bf16);
 hipError_t launch_scan_serial(const ScanArgs &a, hipStream_t st);
 
-// Slot-grouped chunked recurrence (state slice in LDS) + RMSNorm/gate
-// epilogue.  r (fp32 [B,T,H,d_v]) and per-slice square sums
-// ([B,T,H,d_v/CG]) pass through global memory between the two kernels.
-struct ChunkArgs : ScanArgs {
-    float *rbuf;     // may alias out when the output is fp32
-    float *sumsq;
-    float *mass_ws;  // final mass, copied to `mass` by the epilogue kernel
-    int CG, C, EPT;
-};
-
-
-
+// Slot-grouped chunked recurrence, in three kernels: a plan kernel groups
+// every chunk's events by slot (all chunks at once, they do not depend on
+// the state), the scan kernel replays the plans chunk after chunk for one
+// (unit, channel slice) per workgroup, and an epilogue applies RMSNorm and
+// the gate.  r (fp32 [B,T,H,d_v]) and per-slice square sums ([B,T,H,d_v/CG])
+// pass through global memory between the last two.
 struct ChunkPlan {
     bool ok;
-    int CG, C, EPT;
-    size_t lds;
+    bool resident;      // slot rows live in registers (M <= 1024); else in HBM
+    int CG;             // channels per slice
+    int C;              // tokens per chunk
+    int EV;             // C * K: events of one kind per chunk
+    int ENT;            // most slots one chunk touches
+    int HT;             // plan hash table size, 0: the slot is its own index
+    int ncg;            // d_v / CG
+    int64_t n_chunks;
+    // one (unit, chunk) plan record and its sections (byte offsets)
+    size_t rec_bytes, o_ent, o_map, o_wtv, o_ww, o_wa, o_rv, o_rr;
+    size_t lds_plan, lds_scan;
+    size_t ws_rbuf, ws_sumsq, ws_mass, ws_plan;  // workspace section sizes
+};
+
+struct ChunkArgs : ScanArgs {
+    ChunkPlan p;
+    float *rbuf;     // may alias out when the output is fp32
+    float *sumsq;
+    float *mass_ws;  // per-slice mass ([ncg][units][M] in HBM mode, else [units][M])
+    unsigned char *plan;
 };
 
 constexpr size_t kChunkLdsLimit = 160 * 1024;
 
-// Workspace bytes of the chunked path beyond the addresses: r (when the
-// output is not fp32), per-slice square sums, final mass.
-size_t chunk_workspace_bytes(const ChunkPlan &p, int64_t n, int64_t units, int64_t M, int d_v,
-                             bool state_bf16);
-
-struct ChunkLayout {
-    size_t h_off, k_off, w_off, v_off, e_off, r_off, n_off, x_off, total;
-};
-
-__host__ __device__ inline size_t chunk_align16(size_t x) { return (x + 15) & ~size_t(15); }
-
-// LDS layout of one chunked-scan workgroup: bucket counts/offsets, event keys
-// and weights, staged values, exp(gamma), read weights, read snapshots, scan
-// scratch.
-__host__ __device__ inline ChunkLayout chunk_layout(int64_t M, int CG, int C, int K, int sbytes) {
-    ChunkLayout L;
-    size_t o = 0;
-    L.h_off = o; o = chunk_align16(o + static_cast<size_t>(M + 1) * 4);
-    L.k_off = o; o = chunk_align16(o + static_cast<size_t>(2) * C * K * 4);
-    L.w_off = o; o = chunk_align16(o + static_cast<size_t>(2) * C * K * 4);
-    L.v_off = o; o = chunk_align16(o + static_cast<size_t>(C) * CG * 4);
-    L.e_off = o; o = chunk_align16(o + static_cast<size_t>(C) * 4);
-    L.r_off = o; o = chunk_align16(o + static_cast<size_t>(C) * K * 4);
-    L.n_off = o; o = chunk_align16(o + static_cast<size_t>(C) * K * CG * sbytes);
-    L.x_off = o; o = chunk_align16(o + 32 * 4);
-    L.total = o;
-    return L;
-}
+ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16);
+// Workspace bytes of the chunked path beyond the addresses.
+size_t chunk_workspace_bytes(const ChunkPlan &p);
+hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st);
 
 // One fused decoding step (decode + CAPE + GSU + read + norm + gate).
 struct StepArgs {
@@ -108,8 +96,5 @@ struct StepArgs {
 };
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
-
-ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16);
-hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st);
 
 }  // namespace ramnet

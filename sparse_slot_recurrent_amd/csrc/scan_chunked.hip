@@ -1,41 +1,58 @@
 // Slot-grouped prefill recurrence for gfx950.
 //
 // RAM-Net project page, GPU-execution paragraphs: with every token's
-// addresses known, read and write events are grouped by slot; each slot
-// replays its own events in causal order, different slots and channels run
-// in parallel, and slots without events cost nothing.  The Gated Sparse
-// Update and the read are those of the "Gated Sparse Update" and "three
-// stages" paragraphs.
+// addresses known, events are grouped by slot, each slot applies its own
+// events in causal order, different slots and channels run in parallel and
+// untouched slots cost nothing.  The Gated Sparse Update and the read are
+// those of the "Gated Sparse Update" and "three stages" paragraphs.
 //
-// Organisation.  One workgroup owns one (batch, head) unit and a slice of CG
-// channels of its state; thread s holds slot s's row slice and mass in
-// registers for the whole sequence.  The sequence is cut into chunks of C
-// tokens.  Per chunk:
-//   1. the chunk's values (this slice), exp(gamma) and read weights are
-//      staged in LDS, and the chunk's 2*C*K events (K writes, then K reads
-//      per token) are counted per slot;
-//   2. the counts are scanned into bucket offsets and every event is
-//      scattered into its slot's bucket; each event then counts the bucket's
-//      keys below its own (token, write before read) and moves to that rank,
-//      so every bucket is in causal order without a serial sort;
-//   3. thread s replays its bucket: a write updates mass and row, a read
-//      leaves a snapshot of the row (storage dtype) in the token's read
-//      position;
-//   4. one thread per (token, channel) sums rho_k * snapshot_k over the K
-//      reads in rank order; r (fp32) and its sum of squares over the slice go
-//      to global memory.
-// The next chunk's addresses, values and gates are loaded during step 3.  The
-// mass recurrence is the same in every channel slice, so each workgroup of a
-// unit computes it.  A small second kernel sums the slices' squares per token
-// and applies RMSNorm and the gate.
+// The sequence of each (batch, head) unit is cut into chunks of C tokens.
+//
+// plan_kernel: one workgroup per (unit, chunk), all chunks at once, since
+// grouping does not depend on the state.
+//   * Every valid write (slot in [0, M), weight > 0) and read (slot in
+//     [0, M)) finds its slot's entry in a table (the slot itself when M is
+//     small, else an LDS hash table); entries count their writes.
+//   * Entries are numbered in table order and given the offsets of their
+//     write lists; writes are bucketed, then put in causal order by counting
+//     the bucket's earlier tokens.  Each write gets its retention
+//     alpha = (1 - w)^exp(gamma_t).
+//   * Each read is resolved to the version of its slot it sees: the row
+//     before the chunk (version 0) or after the chunk's i-th write to the
+//     slot (version i).  Only versions that some read sees get a row in the
+//     scan's version buffer.
+// scan_kernel: one workgroup per (unit, slice of CG channels), chunk after
+// chunk.
+//   * The plan and the slice's values are staged in LDS (loaded one chunk
+//     ahead into registers).
+//   * The owner of each touched slot stores version 0 if a read sees it,
+//     then applies the slot's writes in order (mass, lambda, row), storing
+//     the versions reads see.  With M <= 1024, thread s owns slot s and keeps
+//     its row slice and mass in registers for the whole sequence; for larger
+//     M the touched rows are gathered from HBM and written back, and each
+//     slice keeps its own copy of the mass.
+//   * One thread per (token, 16-byte piece of the slice) sums rho * version
+//     over the token's K reads in address order; r and the slice's sum of
+//     squares go to global memory.
+// rms_gate_kernel: sums the slices' squares per token, applies RMSNorm and
+// the gate, and copies the final mass.
 #include "device_common.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace ramnet {
 namespace {
 
-constexpr int kNT = 1024;           // threads per workgroup
+constexpr int kNT = 1024;  // threads per workgroup
 constexpr int kWavesPerBlock = kNT / kWave;
+constexpr int kMaxEV = 3072;                        // events of one kind per chunk
+constexpr int kEPTPlan = 2 * kMaxEV / kNT;          // events per plan thread
+constexpr int kEVT = (kMaxEV + kNT - 1) / kNT;      // plan entries per scan thread
+constexpr int kEPN = 2 * kMaxEV / kNT;              // touched slots per thread (HBM rows)
+
+__host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
     const int lane = lane_id();
@@ -45,6 +62,25 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
         if (lane >= off) x += y;
     }
     return x;
+}
+
+// Exclusive prefix of x over the block (thread order); the block total goes
+// to `total`.  Every thread must call it.
+__device__ int block_excl_scan(int x, int *wtot, int &total) {
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const int incl = wave_incl_scan(x);
+    if (lane == kWave - 1) wtot[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        int y = lane < kWavesPerBlock ? wtot[lane] : 0;
+        y = wave_incl_scan(y);
+        if (lane < kWavesPerBlock) wtot[lane] = y;
+    }
+    __syncthreads();
+    const int base = wid > 0 ? wtot[wid - 1] : 0;
+    total = wtot[kWavesPerBlock - 1];
+    __syncthreads();
+    return base + incl - x;
 }
 
 // LDS rows are stored in 16-byte chunks whose order is XOR-swizzled by the
@@ -128,33 +164,305 @@ __device__ __forceinline__ int div_by(uint32_t e, uint64_t m) {
     return static_cast<int>((static_cast<uint64_t>(e) * m) >> 32);
 }
 
-// One event of a slot's replay: a write updates mass and row; a read leaves
-// a snapshot of the row (storage dtype) in its token's read position.
+// LDS of the plan kernel (byte offsets).
+struct PlanLds {
+    size_t key, cf, wo, bk, sk, need, wtot, total;
+};
+__host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
+    PlanLds L{};
+    const size_t ht = p.HT ? static_cast<size_t>(p.HT) : static_cast<size_t>(M);
+    size_t o = 0;
+    L.key = o; o = al16(o + (p.HT ? ht * 4 : 0));                         // slot of a hash entry
+    L.cf = o; o = al16(o + ht * 4);                                       // writes | read flag; entry id
+    L.wo = o; o = al16(o + static_cast<size_t>(p.ENT + 1) * 4);          // entry -> write offset
+    L.bk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // writes, arrival order
+    L.sk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // writes, causal order
+    L.need = o; o = al16(o + static_cast<size_t>(p.ENT + p.EV + 1) * 4);  // versions read
+    L.wtot = o; o = al16(o + 32 * 4);
+    L.total = o;
+    return L;
+}
+
+// Header of a (unit, chunk) plan record.
+struct PlanHdr {
+    int nt;    // touched slots (entries)
+    int nver;  // version rows
+    int nwt;   // valid writes
+    int pad;
+};
+
+constexpr int kReadFlag = 1 << 30;
+
+template <typename TIn>
+__global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const ChunkPlan &P = a.p;
+    const int tid = threadIdx.x;
+    const int unit = static_cast<int>(blockIdx.x / P.n_chunks);
+    const int chunk = static_cast<int>(blockIdx.x % P.n_chunks);
+    const int b = unit / a.H, h = unit % a.H;
+    const int t0 = chunk * P.C, Cc = min(P.C, a.T - t0);
+    const int K = a.K, nev = Cc * K;
+    const int M = static_cast<int>(a.M);
+    const bool hashed = P.HT != 0;
+    const int HT = hashed ? P.HT : M;
+    const int hsh = 32 - (__ffs(HT) - 1);  // hashed: HT is a power of two
+    const uint64_t kdiv = ((uint64_t(1) << 32) + K - 1) / K;
+    const PlanLds L = plan_lds(P, a.M);
+    int *tkey = reinterpret_cast<int *>(smem + L.key);
+    int *tcf = reinterpret_cast<int *>(smem + L.cf);
+    int *ewo = reinterpret_cast<int *>(smem + L.wo);
+    int *bk = reinterpret_cast<int *>(smem + L.bk);
+    int *sk = reinterpret_cast<int *>(smem + L.sk);
+    int *need = reinterpret_cast<int *>(smem + L.need);
+    int *wtot = reinterpret_cast<int *>(smem + L.wtot);
+
+    unsigned char *rec = a.plan + static_cast<int64_t>(blockIdx.x) * P.rec_bytes;
+    int *entp = reinterpret_cast<int *>(rec + P.o_ent);  // [ENT][4]: slot, offset, writes, x0 row
+    int *emap = reinterpret_cast<int *>(rec + P.o_map);
+    int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
+    float *ww = reinterpret_cast<float *>(rec + P.o_ww);
+    float *wa = reinterpret_cast<float *>(rec + P.o_wa);
+    int *rv = reinterpret_cast<int *>(rec + P.o_rv);
+    float *rr = reinterpret_cast<float *>(rec + P.o_rr);
+    const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
+    const TIn *gam = static_cast<const TIn *>(a.gamma);
+
+    for (int i = tid; i < HT; i += kNT) {
+        tcf[i] = 0;
+        if (hashed) tkey[i] = -1;
+    }
+    for (int i = tid; i <= P.ENT + P.EV; i += kNT) need[i] = 0;
+    __syncthreads();
+
+    // ---- 1. every event finds its slot's entry; writes count, reads flag.
+    //         Event j of this thread: e = tid + j * kNT; writes e < nev,
+    //         reads e - nev, both indexed t * K + k within the chunk.
+    int pos[kEPTPlan], ar[kEPTPlan];
+    float wt[kEPTPlan], al[kEPTPlan];
+#pragma unroll
+    for (int j = 0; j < kEPTPlan; ++j) {
+        const int e = tid + j * kNT;
+        pos[j] = -1;
+        ar[j] = 0;
+        wt[j] = 0.f;
+        al[j] = 0.f;
+        if (e < 2 * nev) {
+            const bool rd = e >= nev;
+            const int ee = rd ? e - nev : e;
+            const int t = div_by(ee, kdiv), k = ee - t * K;
+            const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
+            const int s = rd ? a.r_idx[th * K + k] : a.w_idx[th * K + k];
+            const float w = rd ? a.r_wt[th * K + k] : a.w_wt[th * K + k];
+            wt[j] = w;
+            // A zero-weight write changes nothing (alpha = 1, lambda = 0); a
+            // slot outside [0, M) (caller-given addresses) is skipped, and a
+            // skipped read contributes nothing.
+            if (static_cast<uint32_t>(s) < static_cast<uint32_t>(M) && (rd || w > 0.f)) {
+                int p = s;
+                if (hashed) {  // linear probing; the table is at most 3/4 full
+                    uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
+                    for (;;) {
+                        const int old = atomicCAS(&tkey[hp], -1, s);
+                        if (old == -1 || old == s) break;
+                        hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
+                    }
+                    p = static_cast<int>(hp);
+                }
+                pos[j] = p;
+                if (rd) {
+                    atomicOr(&tcf[p], kReadFlag);
+                } else {
+                    ar[j] = atomicAdd(&tcf[p], 1) & (kReadFlag - 1);
+                    al[j] = retention_fast(w, expf(to_f32(gam[th])));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. entries in table order: ids and write offsets from one scan of
+    //         (1 + writes << 16) over the touched positions
+    int nt, nwt;
+    {
+        const int per = (HT + kNT - 1) / kNT;
+        const int lo = min(tid * per, HT), hi = min(lo + per, HT);
+        int local = 0;
+        for (int p = lo; p < hi; ++p) {
+            const int c = tcf[p];
+            if (c) local += 1 + ((c & (kReadFlag - 1)) << 16);
+        }
+        int total;
+        int base = block_excl_scan(local, wtot, total);
+        for (int p = lo; p < hi; ++p) {
+            const int c = tcf[p];
+            int eid = -1;
+            if (c) {
+                const int nw = c & (kReadFlag - 1);
+                eid = base & 0xffff;
+                const int wo = base >> 16;
+                ewo[eid] = wo;
+                entp[4 * eid] = hashed ? tkey[p] : p;
+                entp[4 * eid + 1] = wo;
+                entp[4 * eid + 2] = nw;
+                tcf[p] = eid;
+                base += 1 + (nw << 16);
+            }
+            if (P.resident) emap[p] = eid;
+        }
+        nt = total & 0xffff;
+        nwt = total >> 16;
+        if (tid == 0) ewo[nt] = nwt;
+    }
+    __syncthreads();
+
+    // ---- 3. writes into their entries' buckets, arrival order ...
+#pragma unroll
+    for (int j = 0; j < kEPTPlan; ++j) {
+        const int e = tid + j * kNT;
+        if (pos[j] >= 0 && e < nev) bk[ewo[tcf[pos[j]]] + ar[j]] = e;
+    }
+    __syncthreads();
+    // ... then causal order: a write's rank is the number of the bucket's
+    // writes with a smaller event index (token-major; one write per slot and
+    // token)
+    int spos[kEPTPlan];
+#pragma unroll
+    for (int j = 0; j < kEPTPlan; ++j) {
+        const int e = tid + j * kNT;
+        spos[j] = -1;
+        if (pos[j] >= 0 && e < nev) {
+            const int eid = tcf[pos[j]];
+            const int wo = ewo[eid], n = ewo[eid + 1] - wo;
+            int r = 0;
+            for (int i = 0; i < n; ++i) r += bk[wo + i] < e ? 1 : 0;
+            spos[j] = wo + r;
+            sk[wo + r] = e;
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. each read sees version c of its slot: c = the number of the
+    //         slot's writes at tokens <= its own (writes come first within a
+    //         token).  Entry eid's versions are numbered ewo[eid] + eid + c.
+    int gv[kEPTPlan];
+#pragma unroll
+    for (int j = 0; j < kEPTPlan; ++j) {
+        const int e = tid + j * kNT;
+        gv[j] = -1;
+        if (pos[j] >= 0 && e >= nev) {
+            const int eid = tcf[pos[j]];
+            const int wo = ewo[eid], n = ewo[eid + 1] - wo;
+            const int tr = div_by(e - nev, kdiv);
+            int c = 0;
+            while (c < n && div_by(sk[wo + c], kdiv) <= tr) ++c;
+            gv[j] = wo + eid + c;
+            need[gv[j]] = 1;
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. version rows: exclusive scan of the flags over nt + nwt + 1
+    //         positions; version g has a row iff need[g + 1] > need[g]
+    int nver;
+    {
+        const int N = nt + nwt + 1;
+        const int per = (N + kNT - 1) / kNT;
+        const int lo = min(tid * per, N), hi = min(lo + per, N);
+        int local = 0;
+        for (int i = lo; i < hi; ++i) local += need[i];
+        int base = block_excl_scan(local, wtot, nver);
+        for (int i = lo; i < hi; ++i) {
+            const int c = need[i];
+            need[i] = base;
+            base += c;
+        }
+    }
+    __syncthreads();
+
+    // ---- 6. the record
+    if (tid == 0) {
+        PlanHdr hd{nt, nver, nwt, 0};
+        *reinterpret_cast<PlanHdr *>(rec) = hd;
+    }
+    for (int eid = tid; eid < nt; eid += kNT) {
+        const int g = ewo[eid] + eid;
+        entp[4 * eid + 3] = need[g + 1] > need[g] ? need[g] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kEPTPlan; ++j) {
+        const int e = tid + j * kNT;
+        if (e >= 2 * nev) continue;
+        if (e < nev) {
+            if (spos[j] >= 0) {
+                const int eid = tcf[pos[j]];
+                const int wo = ewo[eid];
+                const int g = wo + eid + (spos[j] - wo) + 1;  // version after this write
+                const int vr = need[g + 1] > need[g] ? need[g] : -1;
+                const int t = div_by(e, kdiv);
+                wtv[spos[j]] = t | ((vr + 1) << 10);
+                ww[spos[j]] = wt[j];
+                wa[spos[j]] = al[j];
+            }
+        } else {
+            rv[e - nev] = gv[j] >= 0 ? need[gv[j]] : -1;
+            rr[e - nev] = gv[j] >= 0 ? wt[j] : 0.f;
+        }
+    }
+}
+
+// LDS of the scan kernel (byte offsets).
+struct ScanLds {
+    size_t v, wtv, ww, wa, rv, rr, ent, ver, total;
+};
+__host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes) {
+    ScanLds L{};
+    size_t o = 0;
+    L.v = o; o = al16(o + static_cast<size_t>(p.C) * p.CG * 4);             // values of the slice
+    L.wtv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                 // write: token | row
+    L.ww = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // write weight
+    L.wa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // write retention
+    L.rv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read: version row
+    L.rr = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read weight
+    L.ent = o; o = al16(o + (p.resident ? static_cast<size_t>(p.ENT) * 16 : 0));
+    L.ver = o; o = al16(o + static_cast<size_t>(p.EV) * p.CG * sbytes);    // version rows
+    L.total = o;
+    return L;
+}
+
+// Applies one touched slot's chunk: version 0 if a read sees it, then the
+// writes in causal order (mass, lambda, row), storing the versions reads see.
 template <typename TS, int CG>
-__device__ __forceinline__ void replay_event(uint32_t kk, float wv, int K, float eps,
-                                             const float *egb, const float *vbuf, TS *snap,
-                                             float (&x)[CG], float &m) {
-    const int t = static_cast<int>(kk >> 7);
-    if (kk & 64u) {
-        const int row = t * K + static_cast<int>(kk & 63u);
-        store_row<CG>(snap + row * CG, row_swz<TS, CG>(row), x);
-    } else {
-        const float alpha = retention_fast(wv, egb[t]);
-        m = fmaf(alpha, m, wv);
-        const float lam = wv * __builtin_amdgcn_rcpf(m + eps);
+__device__ __forceinline__ void walk_slot(int wo, int nw, int x0r, float (&x)[CG], float &m,
+                                          float eps, const int *wtv, const float *ww,
+                                          const float *wa, const float *vbuf, TS *ver) {
+    if (x0r >= 0) store_row<CG>(ver + x0r * CG, row_swz<TS, CG>(x0r), x);
+    for (int i = 0; i < nw; ++i) {
+        const int tv = wtv[wo + i];
+        const int t = tv & 1023, vr = (tv >> 10) - 1;
+        const float w = ww[wo + i];
+        m = fmaf(wa[wo + i], m, w);
+        const float lam = w * __builtin_amdgcn_rcpf(m + eps);
         float vt[CG];
         load_row<CG>(vbuf + t * CG, row_swz<float, CG>(t), vt);
 #pragma unroll
         for (int c = 0; c < CG; ++c) x[c] = stored<TS>(fmaf(lam, vt[c] - x[c], x[c]));
+        if (vr >= 0) store_row<CG>(ver + vr * CG, row_swz<TS, CG>(vr), x);
     }
 }
 
-template <typename TIn, typename TS, int CG, int EPT, int NB>
-__global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
+// CG values of a row slice in HBM.
+template <typename TS, int CG>
+struct HRow {
+    TS e[CG];
+};
+
+template <typename TIn, typename TS, int CG, bool RES>
+__global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
+    const ChunkPlan &P = a.p;
     const int tid = threadIdx.x;
-    const int wid = tid / kWave, lane = tid % kWave;
-    const int ncg = a.d_v / CG;
+    const int ncg = P.ncg;
     const int units = a.B * a.H;
     int unit, cg;
     {
@@ -170,63 +478,65 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
     }
     const int b = unit / a.H, h = unit % a.H;
     const int M = static_cast<int>(a.M);
-    const int K = a.K, C = a.C, d_v = a.d_v;
-    const uint64_t kdiv = ((uint64_t(1) << 32) + K - 1) / K;
-    const ChunkLayout L = chunk_layout(M, CG, C, K, sizeof(TS));
-    int *hist = reinterpret_cast<int *>(smem + L.h_off);
-    uint32_t *ekey = reinterpret_cast<uint32_t *>(smem + L.k_off);
-    float *ewt = reinterpret_cast<float *>(smem + L.w_off);
-    float *vbuf = reinterpret_cast<float *>(smem + L.v_off);
-    float *egb = reinterpret_cast<float *>(smem + L.e_off);
-    float *rho = reinterpret_cast<float *>(smem + L.r_off);
-    TS *snap = reinterpret_cast<TS *>(smem + L.n_off);
-    int *wtot = reinterpret_cast<int *>(smem + L.x_off);  // per-wave totals
+    const int K = a.K, C = P.C, d_v = a.d_v, EV = P.EV;
+    const int nchunks = static_cast<int>(P.n_chunks);
+    const ScanLds L = scan_lds(P, a.M, sizeof(TS));
+    float *vbuf = reinterpret_cast<float *>(smem + L.v);
+    int *s_wtv = reinterpret_cast<int *>(smem + L.wtv);
+    float *s_ww = reinterpret_cast<float *>(smem + L.ww);
+    float *s_wa = reinterpret_cast<float *>(smem + L.wa);
+    int *s_rv = reinterpret_cast<int *>(smem + L.rv);
+    float *s_rr = reinterpret_cast<float *>(smem + L.rr);
+    int4 *s_ent = reinterpret_cast<int4 *>(smem + L.ent);
+    TS *ver = reinterpret_cast<TS *>(smem + L.ver);
 
     const TIn *v = static_cast<const TIn *>(a.v);
-    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    TS *S = static_cast<TS *>(a.S);
     const int64_t th_unit = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
+    const unsigned char *plan0 = a.plan + static_cast<int64_t>(unit) * P.n_chunks * P.rec_bytes;
 
-    // Thread s owns slot s: its row slice and mass stay in registers for the
-    // whole sequence.
-    const bool owner = tid < M;
+    // Resident state: thread s owns slot s's row slice and mass.
     float x[CG];
     float m = 0.f;
-    {
-        const TS *Sg = static_cast<const TS *>(a.S) + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG;
-        if (owner) {
-            TS tmp[CG];
+    if constexpr (RES) {
+        if (tid < M) {
+            const HRow<TS, CG> r = *reinterpret_cast<const HRow<TS, CG> *>(
+                S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG);
 #pragma unroll
-            for (int c = 0; c < CG; ++c) tmp[c] = Sg[c];
-#pragma unroll
-            for (int c = 0; c < CG; ++c) x[c] = to_f32(tmp[c]);
+            for (int c = 0; c < CG; ++c) x[c] = to_f32(r.e[c]);
             m = a.mass[static_cast<int64_t>(unit) * M + tid];
-        } else {
-#pragma unroll
-            for (int c = 0; c < CG; ++c) x[c] = 0.f;
         }
     }
+    float *mws = a.mass_ws + (static_cast<int64_t>(cg) * units + unit) * M;  // HBM mode
 
-    // Next chunk's inputs, loaded one chunk ahead into registers.
-    constexpr int VPT = (CG * 512 + kNT - 1) / kNT;  // values per thread (C <= 512)
-    int pf_slot[EPT];
-    float pf_wt[EPT];
-    float pf_v[VPT];
-    float pf_g = 0.f;
-    auto prefetch = [&](int t0) {
-        const int Cc = min(C, a.T - t0);
-        const int nw = Cc * K;
+    // The next chunk's plan and values, loaded one chunk ahead.
+    constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
+    int pf_wtv[kEVT], pf_rv[kEVT];
+    float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT], pf_v[VPT];
+    int4 pf_ent = make_int4(0, 0, 0, -1);
+    int pf_map = -1, pf_nt = 0;
+    auto prefetch = [&](int c) {
+        const unsigned char *rec = plan0 + static_cast<int64_t>(c) * P.rec_bytes;
+        const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
+        const int *wtv = reinterpret_cast<const int *>(rec + P.o_wtv);
+        const float *ww = reinterpret_cast<const float *>(rec + P.o_ww);
+        const float *wa = reinterpret_cast<const float *>(rec + P.o_wa);
+        const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
+        const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
+        const int4 *ent = reinterpret_cast<const int4 *>(rec + P.o_ent);
+        const int nwt = reinterpret_cast<const PlanHdr *>(rec)->nwt;
+        pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int e = tid + j * kNT;
-            pf_slot[j] = -1;
-            pf_wt[j] = 0.f;
-            if (e < 2 * nw) {
-                const bool rd = e >= nw;
-                const int ee = rd ? e - nw : e;
-                const int t = div_by(ee, kdiv), k = ee - t * K;
-                const int64_t idx = (th_unit + static_cast<int64_t>(t0 + t) * a.H) * K + k;
-                pf_slot[j] = rd ? a.r_idx[idx] : a.w_idx[idx];
-                pf_wt[j] = rd ? a.r_wt[idx] : a.w_wt[idx];
+        for (int j = 0; j < kEVT; ++j) {
+            const int i = tid + j * kNT;
+            if (i < nwt) {
+                pf_wtv[j] = wtv[i];
+                pf_ww[j] = ww[i];
+                pf_wa[j] = wa[i];
+            }
+            if (i < nev) {
+                pf_rv[j] = rv[i];
+                pf_rr[j] = rr[i];
             }
         }
 #pragma unroll
@@ -234,172 +544,160 @@ __global__ __launch_bounds__(kNT) void scan_chunked_kernel(ChunkArgs a) {
             const int i = tid + j * kNT;
             pf_v[j] = 0.f;
             if (i < Cc * CG) {
-                const int t = i / CG, c = i % CG;
-                pf_v[j] = to_f32(v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + c]);
+                const int t = i / CG, cc = i % CG;
+                pf_v[j] = to_f32(v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + cc]);
             }
         }
-        if (tid < Cc) pf_g = to_f32(gam[th_unit + static_cast<int64_t>(t0 + tid) * a.H]);
+        if constexpr (RES) {
+            if (tid < M) pf_map = reinterpret_cast<const int *>(rec + P.o_map)[tid];
+            if (tid < P.ENT) pf_ent = ent[tid];
+        }
     };
 
-    for (int i = tid; i <= M; i += kNT) hist[i] = 0;
     prefetch(0);
-    __syncthreads();
-
-    for (int t0 = 0; t0 < a.T; t0 += C) {
-        const int Cc = min(C, a.T - t0);
-        const int nw = Cc * K;
-        // ---- 1. stage values, gates and read weights; count events per slot
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
+        // ---- 1. stage this chunk's plan and values
+#pragma unroll
+        for (int j = 0; j < kEVT; ++j) {
+            const int i = tid + j * kNT;
+            if (i < EV) {
+                s_wtv[i] = pf_wtv[j];
+                s_ww[i] = pf_ww[j];
+                s_wa[i] = pf_wa[j];
+                s_rv[i] = pf_rv[j];
+                s_rr[i] = pf_rr[j];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int i = tid + j * kNT;
             if (i < Cc * CG) vbuf[swz_index<float, CG>(i / CG, i % CG)] = pf_v[j];
         }
-        if (tid < Cc) egb[tid] = expf(pf_g);
-        int erank[EPT];
-        uint32_t ekk[EPT];
+        const int my_e = pf_map, nt = pf_nt;
+        if constexpr (RES) {
+            if (tid < P.ENT) s_ent[tid] = pf_ent;
+        }
+        __syncthreads();
+        // ---- 2. the next chunk's loads go out now and land during the walk
+        if (c + 1 < nchunks) prefetch(c + 1);
+        // ---- 3. walk the touched slots
+        if constexpr (RES) {
+            if (tid < M && my_e >= 0) {
+                const int4 en = s_ent[my_e];
+                walk_slot<TS, CG>(en.y, en.z, en.w, x, m, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
+            }
+        } else {
+            // touched rows from HBM, EB at a time: entries, then rows, then
+            // the walks and the write-backs
+            const int4 *ent = reinterpret_cast<const int4 *>(
+                plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
+            constexpr int RW = CG * static_cast<int>(sizeof(TS)) / 4;  // registers per row
+            constexpr int EB = 16 / RW < 1 ? 1 : (16 / RW > kEPN ? kEPN : 16 / RW);
+            for (int j0 = 0; j0 < kEPN; j0 += EB) {
+                if (tid + j0 * kNT >= nt) break;
+                int4 en[EB];
+                HRow<TS, CG> rows[EB];
+                float ms[EB];
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int e = tid + j * kNT;
-            erank[j] = -1;
-            ekk[j] = 0;
-            if (e < 2 * nw) {
-                const bool rd = e >= nw;
-                const int ee = rd ? e - nw : e;
-                const int t = div_by(ee, kdiv), k = ee - t * K;
-                const int s = pf_slot[j];
-                // A zero-weight write changes nothing (alpha = 1, lambda = 0);
-                // a slot outside [0, M) (caller-given addresses) is skipped and
-                // a skipped read contributes nothing.
-                const bool ok = static_cast<uint32_t>(s) < static_cast<uint32_t>(M) && (rd || pf_wt[j] > 0.f);
-                if (rd) rho[ee] = ok ? pf_wt[j] : 0.f;
-                if (ok) {
-                    ekk[j] = (((static_cast<uint32_t>(t) << 1) | (rd ? 1u : 0u)) << 6) |
-                             static_cast<uint32_t>(k);
-                    erank[j] = atomicAdd(&hist[s], 1);
+                for (int j = 0; j < EB; ++j) {
+                    const int eid = tid + (j0 + j) * kNT;
+                    if (eid < nt) en[j] = ent[eid];
+                }
+#pragma unroll
+                for (int j = 0; j < EB; ++j) {
+                    const int eid = tid + (j0 + j) * kNT;
+                    if (eid < nt) {
+                        const int64_t slot = en[j].x;
+                        rows[j] = *reinterpret_cast<const HRow<TS, CG> *>(
+                            S + (static_cast<int64_t>(unit) * M + slot) * d_v + cg * CG);
+                        ms[j] = mws[slot];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < EB; ++j) {
+                    const int eid = tid + (j0 + j) * kNT;
+                    if (eid < nt) {
+                        float xr[CG];
+#pragma unroll
+                        for (int cc = 0; cc < CG; ++cc) xr[cc] = to_f32(rows[j].e[cc]);
+                        float mm = ms[j];
+                        walk_slot<TS, CG>(en[j].y, en[j].z, en[j].w, xr, mm, a.eps_gsu, s_wtv, s_ww,
+                                          s_wa, vbuf, ver);
+                        if (en[j].z > 0) {
+                            HRow<TS, CG> o;
+#pragma unroll
+                            for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(xr[cc]);
+                            *reinterpret_cast<HRow<TS, CG> *>(
+                                S + (static_cast<int64_t>(unit) * M + en[j].x) * d_v + cg * CG) = o;
+                            mws[en[j].x] = mm;
+                        }
+                    }
                 }
             }
         }
         __syncthreads();
-        // ---- 2a. exclusive scan of the counts into bucket offsets
-        {
-            const int per = (M + kNT - 1) / kNT;
-            const int lo = min(tid * per, M);
-            const int hi = min(lo + per, M);
-            int local = 0;
-            for (int i = lo; i < hi; ++i) local += hist[i];
-            const int incl = wave_incl_scan(local);
-            if (lane == kWave - 1) wtot[wid] = incl;
-            __syncthreads();
-            if (wid == 0) {
-                int y = lane < kWavesPerBlock ? wtot[lane] : 0;
-                y = wave_incl_scan(y);
-                if (lane < kWavesPerBlock) wtot[lane] = y;
-            }
-            __syncthreads();
-            int base = (wid > 0 ? wtot[wid - 1] : 0) + incl - local;
-            for (int i = lo; i < hi; ++i) {
-                const int c = hist[i];
-                hist[i] = base;
-                base += c;
-            }
-            if (hi == M && lo < hi) hist[M] = base;
-        }
-        __syncthreads();
-        // ---- 2b. scatter events into their buckets (arrival order) ...
-#pragma unroll
-        for (int j = 0; j < EPT; ++j)
-            if (erank[j] >= 0) ekey[hist[pf_slot[j]] + erank[j]] = ekk[j];
-        __syncthreads();
-        // ---- 2c. ... then move each to its causal rank within the bucket:
-        //          the number of the bucket's keys below its own (keys are
-        //          unique within a slot: one write and one read per token)
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            if (erank[j] >= 0) {
-                const int beg = hist[pf_slot[j]], n = hist[pf_slot[j] + 1] - beg;
-                int r = 0;
-                for (int i = 0; i < n; ++i) r += ekey[beg + i] < ekk[j] ? 1 : 0;
-                erank[j] = beg + r;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            if (erank[j] >= 0) {
-                ekey[erank[j]] = ekk[j];
-                ewt[erank[j]] = pf_wt[j];
-            }
-        }
-        __syncthreads();
-        // ---- 3. next chunk's loads go out now and land during the replay
-        if (t0 + C < a.T) prefetch(t0 + C);
-        // Replay: thread s applies its bucket, already in causal order, to
-        // its row in registers.
-        if (owner) {
-            const int beg = hist[tid], n = hist[tid + 1] - beg;
-            uint32_t kk[NB];
-            float ww[NB];
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                kk[i] = i < n ? ekey[beg + i] : 0u;
-                ww[i] = i < n ? ewt[beg + i] : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-                if (i < n) replay_event<TS, CG>(kk[i], ww[i], K, a.eps_gsu, egb, vbuf, snap, x, m);
-            for (int i = NB; i < n; ++i)
-                replay_event<TS, CG>(ekey[beg + i], ewt[beg + i], K, a.eps_gsu, egb, vbuf, snap, x, m);
-        }
-        __syncthreads();
-        // ---- 4. reads: r = sum_k rho_k * snapshot_k (k in rank order) for one
-        //         16-byte chunk of channels per thread; r and the sum of
+        // ---- 4. reads: r = sum_k rho_k * version_k (k in address order) for
+        //         one 16-byte piece of the slice per thread; r and the sum of
         //         squares over the slice go to global memory
         {
-            constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per chunk
-            constexpr int NCH = CG / EPC;                            // chunks per row
+            constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per piece
+            constexpr int NCH = CG / EPC;                            // pieces per row
             for (int i = tid; i < Cc * NCH; i += kNT) {
                 const int t = i / NCH, j = i % NCH;
                 float r[EPC];
 #pragma unroll
-                for (int c = 0; c < EPC; ++c) r[c] = 0.f;
+                for (int cc = 0; cc < EPC; ++cc) r[cc] = 0.f;
                 for (int k = 0; k < K; ++k) {
-                    // A read with weight 0 adds nothing; skipped reads (slot
-                    // outside [0, M)) have weight 0 and no snapshot.
+                    // skipped reads have no row; a zero weight adds nothing
                     const int row = t * K + k;
-                    const float rw = rho[row];
-                    if (rw != 0.f) {
-                        const uint4 u = reinterpret_cast<const uint4 *>(snap + row * CG)[j ^ row_swz<TS, CG>(row)];
+                    const int vr = s_rv[row];
+                    const float rw = s_rr[row];
+                    if (vr >= 0 && rw != 0.f) {
+                        const uint4 u = reinterpret_cast<const uint4 *>(ver + vr * CG)[j ^ row_swz<TS, CG>(vr)];
                         float sv[EPC];
                         unpack_chunk(u, sv);
 #pragma unroll
-                        for (int c = 0; c < EPC; ++c) r[c] = fmaf(rw, sv[c], r[c]);
+                        for (int cc = 0; cc < EPC; ++cc) r[cc] = fmaf(rw, sv[cc], r[cc]);
                     }
                 }
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
                 float *dst = a.rbuf + th * d_v + cg * CG + j * EPC;
 #pragma unroll
-                for (int c = 0; c < EPC; c += 4)
-                    *reinterpret_cast<float4 *>(dst + c) = make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
+                for (int cc = 0; cc < EPC; cc += 4)
+                    *reinterpret_cast<float4 *>(dst + cc) = make_float4(r[cc], r[cc + 1], r[cc + 2], r[cc + 3]);
                 float ss = 0.f;
 #pragma unroll
-                for (int c = 0; c < EPC; ++c) ss = fmaf(r[c], r[c], ss);
+                for (int cc = 0; cc < EPC; ++cc) ss = fmaf(r[cc], r[cc], ss);
 #pragma unroll
                 for (int off = NCH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
                 if (j == 0) a.sumsq[th * ncg + cg] = ss;
             }
         }
-        for (int i = tid; i <= M; i += kNT) hist[i] = 0;
+        (void)nev;
         __syncthreads();
     }
 
-    if (owner) {
-        TS *Sg = static_cast<TS *>(a.S) + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG;
+    if constexpr (RES) {
+        if (tid < M) {
+            HRow<TS, CG> o;
 #pragma unroll
-        for (int c = 0; c < CG; ++c) Sg[c] = from_f32<TS>(x[c]);
-        // The mass goes to the workspace: other slices of this unit may not
-        // have read the initial mass yet; the epilogue kernel copies it over
-        // once every slice has finished.
-        if (cg == 0) a.mass_ws[static_cast<int64_t>(unit) * M + tid] = m;
+            for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(x[cc]);
+            *reinterpret_cast<HRow<TS, CG> *>(S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG) = o;
+            // Other slices of this unit may not have read the initial mass
+            // yet; the epilogue copies slice 0's final mass over.
+            if (cg == 0) a.mass_ws[static_cast<int64_t>(unit) * M + tid] = m;
+        }
+    }
+}
+
+// Every slice's copy of the mass starts from the caller's (HBM mode).
+__global__ void mass_fanout_kernel(const float *__restrict__ mass, float *__restrict__ mass_ws,
+                                   int64_t n, int ncg) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const float x = mass[i];
+        for (int c = 0; c < ncg; ++c) mass_ws[c * n + i] = x;
     }
 }
 
@@ -433,45 +731,50 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__
     }
 }
 
-template <typename TIn, typename TS, int CG, int EPT>
-hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
-    const size_t lds = chunk_layout(a.M, CG, a.C, a.K, sizeof(TS)).total;
-    constexpr int NB = EPT >= 8 ? 16 : 8;  // bucket entries held in registers
-    auto kern = scan_chunked_kernel<TIn, TS, CG, EPT, NB>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    const unsigned grid = static_cast<unsigned>(a.B) * a.H * (a.d_v / CG);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kNT), lds, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
-    const int64_t n_mass = static_cast<int64_t>(a.B) * a.H * a.M;
-    const int64_t work = max(n * (a.d_v / 4), n_mass);
-    const unsigned g2 = static_cast<unsigned>((work + 255) / 256);
-    hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf, a.sumsq,
-                       a.d_v / CG, static_cast<const TIn *>(a.g), a.norm_w,
-                       static_cast<TS *>(a.out), n, a.d_v, a.eps_norm, a.mass_ws, a.mass,
-                       n_mass);
-    return hipGetLastError();
+template <typename K>
+hipError_t set_lds(K kern, size_t lds) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
 }
 
 template <typename TIn, typename TS, int CG>
-hipError_t launch_ept(const ChunkArgs &a, hipStream_t st) {
-    switch (a.EPT) {
-        case 2: return launch_cfg<TIn, TS, CG, 2>(a, st);
-        case 4: return launch_cfg<TIn, TS, CG, 4>(a, st);
-        case 8: return launch_cfg<TIn, TS, CG, 8>(a, st);
-        default: return hipErrorInvalidValue;
+hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
+    const ChunkPlan &P = a.p;
+    const int64_t units = static_cast<int64_t>(a.B) * a.H;
+    auto pk = plan_kernel<TIn>;
+    hipError_t e = set_lds(pk, P.lds_plan);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kNT), P.lds_plan, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!P.resident) {
+        const int64_t nm = units * a.M;
+        const unsigned g = static_cast<unsigned>(std::min<int64_t>((nm + 255) / 256, 4096));
+        hipLaunchKernelGGL(mass_fanout_kernel, dim3(g), dim3(256), 0, st, a.mass, a.mass_ws, nm, P.ncg);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    auto sk = P.resident ? scan_kernel<TIn, TS, CG, true> : scan_kernel<TIn, TS, CG, false>;
+    e = set_lds(sk, P.lds_scan);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * P.ncg)), dim3(kNT), P.lds_scan, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = units * a.T;
+    const int64_t n_mass = units * a.M;
+    const int64_t work = std::max<int64_t>(n * (a.d_v / 4), n_mass);
+    const unsigned g2 = static_cast<unsigned>((work + 255) / 256);
+    hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf, a.sumsq,
+                       P.ncg, static_cast<const TIn *>(a.g), a.norm_w, static_cast<TS *>(a.out), n,
+                       a.d_v, a.eps_norm, a.mass_ws, a.mass, n_mass);
+    return hipGetLastError();
 }
 
 template <typename TIn, typename TS>
 hipError_t launch_cg(const ChunkArgs &a, hipStream_t st) {
-    switch (a.CG) {
-        case 8: return launch_ept<TIn, TS, 8>(a, st);
-        case 16: return launch_ept<TIn, TS, 16>(a, st);
+    switch (a.p.CG) {
+        case 8: return launch_cfg<TIn, TS, 8>(a, st);
+        case 16: return launch_cfg<TIn, TS, 16>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -483,10 +786,12 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool stat
     p.ok = false;
     const int sbytes = state_bf16 ? 2 : 4;
     const int64_t units = static_cast<int64_t>(B) * H;
-    // Thread s owns slot s, so the whole slot array must fit one workgroup.
-    if (T < 32 || units == 0 || M > kNT || K > 63) return p;
+    // Plan entries pack the token in 10 bits and table sums in 16.
+    if (T < 32 || units == 0 || K > 63 || M > (int64_t(1) << 22)) return p;
+    p.resident = M <= kNT;
     // Largest channel slice that still gives about one workgroup per CU,
-    // then the longest chunk (a multiple of 32 tokens) that fits LDS.
+    // then the longest chunk (a multiple of 32 tokens) whose plan and
+    // version rows fit LDS.
     const int cgs[2] = {16, 8};
     for (int ci = 0; ci < 2; ++ci) {
         const int CG = cgs[ci];
@@ -494,35 +799,52 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool stat
         const bool last = ci == 1;
         if (!last && units * (d_v / CG) < 256) continue;
         for (int C = 512; C >= 32; C -= 32) {
-            const int64_t ev = 2LL * C * K;
-            if (ev > 8LL * kNT) continue;  // at most 8 events per thread
-            const size_t lds = chunk_layout(M, CG, C, K, sbytes).total;
-            if (lds > kChunkLdsLimit) continue;
-            int ept = 1;
-            while (static_cast<int64_t>(ept) * kNT < ev) ept *= 2;
-            p.ok = true;
-            p.CG = CG;
-            p.C = C;
-            p.EPT = ept < 2 ? 2 : ept;
-            p.lds = lds;
-            return p;
+            const int EV = C * K;
+            if (EV > kMaxEV) continue;
+            ChunkPlan q = p;
+            q.CG = CG;
+            q.C = C;
+            q.EV = EV;
+            q.ENT = static_cast<int>(std::min<int64_t>(M, 2 * EV));
+            q.HT = 0;
+            if (M > 4096) {  // hash table at most 3/4 full
+                int ht = 1;
+                while (ht * 3 < 2 * EV * 4) ht *= 2;
+                q.HT = ht;
+            }
+            q.ncg = d_v / CG;
+            q.lds_plan = plan_lds(q, M).total;
+            q.lds_scan = scan_lds(q, M, sbytes).total;
+            if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
+            q.n_chunks = (T + C - 1) / C;
+            size_t o = 256;  // header
+            q.o_ent = o; o += al256(static_cast<size_t>(q.ENT) * 16);
+            q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 4 : 0);
+            q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
+            q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
+            q.o_wa = o; o += al256(static_cast<size_t>(EV) * 4);
+            q.o_rv = o; o += al256(static_cast<size_t>(EV) * 4);
+            q.o_rr = o; o += al256(static_cast<size_t>(EV) * 4);
+            q.rec_bytes = o;
+            const size_t n = static_cast<size_t>(units) * T;
+            q.ws_rbuf = state_bf16 ? al256(n * d_v * 4) : 0;
+            q.ws_sumsq = al256(n * q.ncg * 4);
+            q.ws_mass = al256(static_cast<size_t>(q.resident ? 1 : q.ncg) * units * M * 4);
+            q.ws_plan = al256(static_cast<size_t>(units) * q.n_chunks * q.rec_bytes);
+            q.ok = true;
+            return q;
         }
     }
     return p;
 }
 
-size_t chunk_workspace_bytes(const ChunkPlan &p, int64_t n, int64_t units, int64_t M, int d_v,
-                             bool state_bf16) {
-    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    size_t b = 0;
-    if (state_bf16) b += al(static_cast<size_t>(n) * d_v * 4);
-    b += al(static_cast<size_t>(n) * (d_v / p.CG) * 4);
-    b += al(static_cast<size_t>(units) * M * 4);
-    return b;
+size_t chunk_workspace_bytes(const ChunkPlan &p) {
+    return p.ws_rbuf + p.ws_sumsq + p.ws_mass + p.ws_plan;
 }
 
 hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st) {
     if (static_cast<int64_t>(a.B) * a.H * a.T == 0) return hipSuccess;
+    if (!a.p.ok) return hipErrorInvalidValue;
     if (a.in_bf16)
         return a.state_bf16 ? launch_cg<bf16_t, bf16_t>(a, st) : launch_cg<bf16_t, float>(a, st);
     return a.state_bf16 ? launch_cg<float, bf16_t>(a, st) : launch_cg<float, float>(a, st);
