@@ -32,7 +32,9 @@ def byte_model(w, kind: str):
     """Algorithmic bytes per launch of each kernel (what the method must
     move, per the token-head byte model; no address round trip, no re-reads).
       decode_addresses: q and k logits, 2*U*d_p*b_in per token-head.
-      scan:             v, g (2*d_v*b_in), gamma (b_in) in, out (d_v*b_s),
+      scan_stage:       (the plan, scan and RMSNorm/gate kernels of one
+                        prefill call with given addresses)
+                        v, g (2*d_v*b_in), gamma (b_in) in, out (d_v*b_s),
                         plus the state and mass read and written once per
                         (batch, head) unit when it is held on chip, or the
                         touched rows (3*K*d_v*b_s + 2*K*4 per token-head)
@@ -51,7 +53,7 @@ def byte_model(w, kind: str):
     # the rows the token-heads touch (prefill of a small state); otherwise
     # only the touched rows count (decode, large state).
     state = min(once, rows)
-    out = {"decode_addresses": dec, "scan": io + state,
+    out = {"decode_addresses": dec, "scan_stage": io + state,
            "total": dec + io + state, "state_term": state}
     if kind == "decode":
         out["step_fused"] = out["total"]  # one kernel does the whole step
@@ -185,7 +187,7 @@ def bench_prefill(torch, rn, w, steps, warmup):
     ms_scan = time_loop(torch, scan, steps)
     torch.cuda.synchronize()
     tokens = w.B * w.T
-    return ms, {"decode_addresses": ms_dec, "scan": ms_scan}, tokens
+    return ms, {"decode_addresses": ms_dec, "scan_stage": ms_scan}, tokens
 
 
 def bench_decode(torch, rn, w, steps, warmup):

@@ -54,6 +54,7 @@ struct ChunkPlan {
     int C;              // tokens per chunk
     int EV;             // C * K: events of one kind per chunk
     int ENT;            // most slots one chunk touches
+    int ENTA;           // ENT rounded up to 64 (stride of the entry arrays)
     int HT;             // plan hash table size, 0: the slot is its own index
     int ncg;            // d_v / CG
     int64_t n_chunks;

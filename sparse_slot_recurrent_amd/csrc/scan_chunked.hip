@@ -47,7 +47,8 @@ namespace {
 constexpr int kNT = 1024;  // threads per workgroup
 constexpr int kWavesPerBlock = kNT / kWave;
 constexpr int kMaxEV = 3072;                        // events of one kind per chunk
-constexpr int kEPTPlan = 2 * kMaxEV / kNT;          // events per plan thread
+constexpr int kPT = 512;                            // plan kernel threads
+constexpr int kEPW = kMaxEV / kPT;                  // writes (and reads) per plan thread
 constexpr int kEVT = (kMaxEV + kNT - 1) / kNT;      // plan entries per scan thread
 constexpr int kEPN = 2 * kMaxEV / kNT;              // touched slots per thread (HBM rows)
 
@@ -64,23 +65,43 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-// Exclusive prefix of x over the block (thread order); the block total goes
-// to `total`.  Every thread must call it.
+// Exclusive prefix of x over a block of NT threads (thread order); the block
+// total goes to `total`.  Every thread must call it.
+template <int NT>
 __device__ int block_excl_scan(int x, int *wtot, int &total) {
+    constexpr int NW = NT / kWave;
     const int lane = lane_id(), wid = threadIdx.x / kWave;
     const int incl = wave_incl_scan(x);
     if (lane == kWave - 1) wtot[wid] = incl;
     __syncthreads();
     if (wid == 0) {
-        int y = lane < kWavesPerBlock ? wtot[lane] : 0;
+        int y = lane < NW ? wtot[lane] : 0;
         y = wave_incl_scan(y);
-        if (lane < kWavesPerBlock) wtot[lane] = y;
+        if (lane < NW) wtot[lane] = y;
     }
     __syncthreads();
     const int base = wid > 0 ? wtot[wid - 1] : 0;
-    total = wtot[kWavesPerBlock - 1];
+    total = wtot[NW - 1];
     __syncthreads();
     return base + incl - x;
+}
+
+// In-place exclusive scan of a[0, n) by a block of NT threads, each taking
+// a contiguous run; returns the sum.  Callers synchronise before reading a.
+template <int NT>
+__device__ int block_scan_array(int *a, int n, int *wtot) {
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(static_cast<int>(threadIdx.x) * per, n), hi = min(lo + per, n);
+    int local = 0;
+    for (int i = lo; i < hi; ++i) local += a[i];
+    int total;
+    int base = block_excl_scan<NT>(local, wtot, total);
+    for (int i = lo; i < hi; ++i) {
+        const int c = a[i];
+        a[i] = base;
+        base += c;
+    }
+    return total;
 }
 
 // LDS rows are stored in 16-byte chunks whose order is XOR-swizzled by the
@@ -166,7 +187,7 @@ __device__ __forceinline__ int div_by(uint32_t e, uint64_t m) {
 
 // LDS of the plan kernel (byte offsets).
 struct PlanLds {
-    size_t key, cf, wo, bk, sk, need, wtot, total;
+    size_t key, cf, wo, bk, sk, sa, need, wtot, total;
 };
 __host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
     PlanLds L{};
@@ -177,6 +198,7 @@ __host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
     L.wo = o; o = al16(o + static_cast<size_t>(p.ENT + 1) * 4);          // entry -> write offset
     L.bk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // writes, arrival order
     L.sk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // writes, causal order
+    L.sa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // staged write retention
     L.need = o; o = al16(o + static_cast<size_t>(p.ENT + p.EV + 1) * 4);  // versions read
     L.wtot = o; o = al16(o + 32 * 4);
     L.total = o;
@@ -194,13 +216,16 @@ struct PlanHdr {
 constexpr int kReadFlag = 1 << 30;
 
 template <typename TIn>
-__global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
     const int tid = threadIdx.x;
-    const int unit = static_cast<int>(blockIdx.x / P.n_chunks);
-    const int chunk = static_cast<int>(blockIdx.x % P.n_chunks);
-    const int b = unit / a.H, h = unit % a.H;
+    // the heads of one (sequence, chunk) are neighbours: their addresses
+    // share cache lines
+    const int h = static_cast<int>(blockIdx.x % a.H);
+    const int chunk = static_cast<int>((blockIdx.x / a.H) % P.n_chunks);
+    const int b = static_cast<int>(blockIdx.x / a.H / P.n_chunks);
+    const int unit = b * a.H + h;
     const int t0 = chunk * P.C, Cc = min(P.C, a.T - t0);
     const int K = a.K, nev = Cc * K;
     const int M = static_cast<int>(a.M);
@@ -215,10 +240,14 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
     int *bk = reinterpret_cast<int *>(smem + L.bk);
     int *sk = reinterpret_cast<int *>(smem + L.sk);
     int *need = reinterpret_cast<int *>(smem + L.need);
+    int *sa = reinterpret_cast<int *>(smem + L.sa);
     int *wtot = reinterpret_cast<int *>(smem + L.wtot);
 
-    unsigned char *rec = a.plan + static_cast<int64_t>(blockIdx.x) * P.rec_bytes;
-    int *entp = reinterpret_cast<int *>(rec + P.o_ent);  // [ENT][4]: slot, offset, writes, x0 row
+    unsigned char *rec = a.plan + (static_cast<int64_t>(unit) * P.n_chunks + chunk) * P.rec_bytes;
+    int *ent_slot = reinterpret_cast<int *>(rec + P.o_ent);  // per entry: slot, write offset,
+    int *ent_wo = ent_slot + P.ENTA;                          // writes, version-0 row
+    int *ent_nw = ent_wo + P.ENTA;
+    int *ent_x0 = ent_nw + P.ENTA;
     int *emap = reinterpret_cast<int *>(rec + P.o_map);
     int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
     float *ww = reinterpret_cast<float *>(rec + P.o_ww);
@@ -228,55 +257,61 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
     const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
     const TIn *gam = static_cast<const TIn *>(a.gamma);
 
-    for (int i = tid; i < HT; i += kNT) {
+    // ---- 0. this thread's events, e = tid + j * kPT (index t * K + k within
+    //         the chunk), writes and reads alike; the loads go out first
+    int ws[kEPW], rs[kEPW];
+    float wt[kEPW], rt[kEPW], eg[kEPW];
+#pragma unroll
+    for (int j = 0; j < kEPW; ++j) {
+        const int e = tid + j * kPT;
+        ws[j] = -1;
+        rs[j] = -1;
+        if (e < nev) {
+            const int t = div_by(e, kdiv), k = e - t * K;
+            const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
+            ws[j] = a.w_idx[th * K + k];
+            wt[j] = a.w_wt[th * K + k];
+            rs[j] = a.r_idx[th * K + k];
+            rt[j] = a.r_wt[th * K + k];
+            eg[j] = to_f32(gam[th]);
+        }
+    }
+    for (int i = tid; i < HT; i += kPT) {
         tcf[i] = 0;
         if (hashed) tkey[i] = -1;
     }
-    for (int i = tid; i <= P.ENT + P.EV; i += kNT) need[i] = 0;
+    for (int i = tid; i <= P.ENT + P.EV; i += kPT) need[i] = 0;
     __syncthreads();
 
     // ---- 1. every event finds its slot's entry; writes count, reads flag.
-    //         Event j of this thread: e = tid + j * kNT; writes e < nev,
-    //         reads e - nev, both indexed t * K + k within the chunk.
-    int pos[kEPTPlan], ar[kEPTPlan];
-    float wt[kEPTPlan], al[kEPTPlan];
+    //         A zero-weight write changes nothing (alpha = 1, lambda = 0); a
+    //         slot outside [0, M) (caller-given addresses) is skipped, and a
+    //         skipped read contributes nothing.
+    auto entry_of = [&](int s) -> int {
+        if (!hashed) return s;
+        uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
+        for (;;) {  // linear probing; the table is at most 3/4 full
+            const int old = atomicCAS(&tkey[hp], -1, s);
+            if (old == -1 || old == s) return static_cast<int>(hp);
+            hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
+        }
+    };
+    int wpos[kEPW], ar[kEPW], rpos[kEPW];
+    float al[kEPW];
 #pragma unroll
-    for (int j = 0; j < kEPTPlan; ++j) {
-        const int e = tid + j * kNT;
-        pos[j] = -1;
+    for (int j = 0; j < kEPW; ++j) {
+        wpos[j] = -1;
+        rpos[j] = -1;
         ar[j] = 0;
-        wt[j] = 0.f;
         al[j] = 0.f;
-        if (e < 2 * nev) {
-            const bool rd = e >= nev;
-            const int ee = rd ? e - nev : e;
-            const int t = div_by(ee, kdiv), k = ee - t * K;
-            const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
-            const int s = rd ? a.r_idx[th * K + k] : a.w_idx[th * K + k];
-            const float w = rd ? a.r_wt[th * K + k] : a.w_wt[th * K + k];
-            wt[j] = w;
-            // A zero-weight write changes nothing (alpha = 1, lambda = 0); a
-            // slot outside [0, M) (caller-given addresses) is skipped, and a
-            // skipped read contributes nothing.
-            if (static_cast<uint32_t>(s) < static_cast<uint32_t>(M) && (rd || w > 0.f)) {
-                int p = s;
-                if (hashed) {  // linear probing; the table is at most 3/4 full
-                    uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
-                    for (;;) {
-                        const int old = atomicCAS(&tkey[hp], -1, s);
-                        if (old == -1 || old == s) break;
-                        hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
-                    }
-                    p = static_cast<int>(hp);
-                }
-                pos[j] = p;
-                if (rd) {
-                    atomicOr(&tcf[p], kReadFlag);
-                } else {
-                    ar[j] = atomicAdd(&tcf[p], 1) & (kReadFlag - 1);
-                    al[j] = retention_fast(w, expf(to_f32(gam[th])));
-                }
-            }
+        if (static_cast<uint32_t>(ws[j]) < static_cast<uint32_t>(M) && wt[j] > 0.f) {
+            wpos[j] = entry_of(ws[j]);
+            ar[j] = atomicAdd(&tcf[wpos[j]], 1) & (kReadFlag - 1);
+            al[j] = retention_fast(wt[j], expf(eg[j]));
+        }
+        if (static_cast<uint32_t>(rs[j]) < static_cast<uint32_t>(M)) {
+            rpos[j] = entry_of(rs[j]);
+            atomicOr(&tcf[rpos[j]], kReadFlag);
         }
     }
     __syncthreads();
@@ -285,7 +320,7 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
     //         (1 + writes << 16) over the touched positions
     int nt, nwt;
     {
-        const int per = (HT + kNT - 1) / kNT;
+        const int per = (HT + kPT - 1) / kPT;
         const int lo = min(tid * per, HT), hi = min(lo + per, HT);
         int local = 0;
         for (int p = lo; p < hi; ++p) {
@@ -293,7 +328,7 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
             if (c) local += 1 + ((c & (kReadFlag - 1)) << 16);
         }
         int total;
-        int base = block_excl_scan(local, wtot, total);
+        int base = block_excl_scan<kPT>(local, wtot, total);
         for (int p = lo; p < hi; ++p) {
             const int c = tcf[p];
             int eid = -1;
@@ -302,9 +337,7 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
                 eid = base & 0xffff;
                 const int wo = base >> 16;
                 ewo[eid] = wo;
-                entp[4 * eid] = hashed ? tkey[p] : p;
-                entp[4 * eid + 1] = wo;
-                entp[4 * eid + 2] = nw;
+                ent_slot[eid] = hashed ? tkey[p] : p;
                 tcf[p] = eid;
                 base += 1 + (nw << 16);
             }
@@ -318,21 +351,19 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
 
     // ---- 3. writes into their entries' buckets, arrival order ...
 #pragma unroll
-    for (int j = 0; j < kEPTPlan; ++j) {
-        const int e = tid + j * kNT;
-        if (pos[j] >= 0 && e < nev) bk[ewo[tcf[pos[j]]] + ar[j]] = e;
-    }
+    for (int j = 0; j < kEPW; ++j)
+        if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPT;
     __syncthreads();
     // ... then causal order: a write's rank is the number of the bucket's
     // writes with a smaller event index (token-major; one write per slot and
     // token)
-    int spos[kEPTPlan];
+    int spos[kEPW];
 #pragma unroll
-    for (int j = 0; j < kEPTPlan; ++j) {
-        const int e = tid + j * kNT;
+    for (int j = 0; j < kEPW; ++j) {
         spos[j] = -1;
-        if (pos[j] >= 0 && e < nev) {
-            const int eid = tcf[pos[j]];
+        if (wpos[j] >= 0) {
+            const int e = tid + j * kPT;
+            const int eid = tcf[wpos[j]];
             const int wo = ewo[eid], n = ewo[eid + 1] - wo;
             int r = 0;
             for (int i = 0; i < n; ++i) r += bk[wo + i] < e ? 1 : 0;
@@ -345,15 +376,14 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
     // ---- 4. each read sees version c of its slot: c = the number of the
     //         slot's writes at tokens <= its own (writes come first within a
     //         token).  Entry eid's versions are numbered ewo[eid] + eid + c.
-    int gv[kEPTPlan];
+    int gv[kEPW];
 #pragma unroll
-    for (int j = 0; j < kEPTPlan; ++j) {
-        const int e = tid + j * kNT;
+    for (int j = 0; j < kEPW; ++j) {
         gv[j] = -1;
-        if (pos[j] >= 0 && e >= nev) {
-            const int eid = tcf[pos[j]];
+        if (rpos[j] >= 0) {
+            const int eid = tcf[rpos[j]];
             const int wo = ewo[eid], n = ewo[eid + 1] - wo;
-            const int tr = div_by(e - nev, kdiv);
+            const int tr = div_by(tid + j * kPT, kdiv);
             int c = 0;
             while (c < n && div_by(sk[wo + c], kdiv) <= tr) ++c;
             gv[j] = wo + eid + c;
@@ -364,50 +394,43 @@ __global__ __launch_bounds__(kNT) void plan_kernel(ChunkArgs a) {
 
     // ---- 5. version rows: exclusive scan of the flags over nt + nwt + 1
     //         positions; version g has a row iff need[g + 1] > need[g]
-    int nver;
-    {
-        const int N = nt + nwt + 1;
-        const int per = (N + kNT - 1) / kNT;
-        const int lo = min(tid * per, N), hi = min(lo + per, N);
-        int local = 0;
-        for (int i = lo; i < hi; ++i) local += need[i];
-        int base = block_excl_scan(local, wtot, nver);
-        for (int i = lo; i < hi; ++i) {
-            const int c = need[i];
-            need[i] = base;
-            base += c;
-        }
-    }
+    const int nver = block_scan_array<kPT>(need, nt + nwt + 1, wtot);
     __syncthreads();
 
-    // ---- 6. the record
+    // ---- 6. the record: entries, writes staged in LDS in causal order, then
+    //         everything stored with consecutive lanes on consecutive words
     if (tid == 0) {
         PlanHdr hd{nt, nver, nwt, 0};
         *reinterpret_cast<PlanHdr *>(rec) = hd;
     }
-    for (int eid = tid; eid < nt; eid += kNT) {
+    for (int eid = tid; eid < nt; eid += kPT) {
         const int g = ewo[eid] + eid;
-        entp[4 * eid + 3] = need[g + 1] > need[g] ? need[g] : -1;
+        ent_wo[eid] = ewo[eid];
+        ent_nw[eid] = ewo[eid + 1] - ewo[eid];
+        ent_x0[eid] = need[g + 1] > need[g] ? need[g] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kEPTPlan; ++j) {
-        const int e = tid + j * kNT;
-        if (e >= 2 * nev) continue;
-        if (e < nev) {
-            if (spos[j] >= 0) {
-                const int eid = tcf[pos[j]];
-                const int wo = ewo[eid];
-                const int g = wo + eid + (spos[j] - wo) + 1;  // version after this write
-                const int vr = need[g + 1] > need[g] ? need[g] : -1;
-                const int t = div_by(e, kdiv);
-                wtv[spos[j]] = t | ((vr + 1) << 10);
-                ww[spos[j]] = wt[j];
-                wa[spos[j]] = al[j];
-            }
-        } else {
-            rv[e - nev] = gv[j] >= 0 ? need[gv[j]] : -1;
-            rr[e - nev] = gv[j] >= 0 ? wt[j] : 0.f;
+    for (int j = 0; j < kEPW; ++j) {
+        const int e = tid + j * kPT;
+        if (spos[j] >= 0) {
+            const int eid = tcf[wpos[j]];
+            const int wo = ewo[eid];
+            const int g = wo + eid + (spos[j] - wo) + 1;  // version after this write
+            const int vr = need[g + 1] > need[g] ? need[g] : -1;
+            bk[spos[j]] = div_by(e, kdiv) | ((vr + 1) << 10);
+            sk[spos[j]] = __float_as_int(wt[j]);
+            sa[spos[j]] = __float_as_int(al[j]);
         }
+        if (e < nev) {
+            rv[e] = gv[j] >= 0 ? need[gv[j]] : -1;
+            rr[e] = gv[j] >= 0 ? rt[j] : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < nwt; i += kPT) {
+        wtv[i] = bk[i];
+        ww[i] = __int_as_float(sk[i]);
+        wa[i] = __int_as_float(sa[i]);
     }
 }
 
@@ -513,7 +536,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
     int pf_wtv[kEVT], pf_rv[kEVT];
     float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT], pf_v[VPT];
-    int4 pf_ent = make_int4(0, 0, 0, -1);
+    int4 pf_ent = make_int4(0, 0, 0, -1);  // write offset, writes, version-0 row
     int pf_map = -1, pf_nt = 0;
     auto prefetch = [&](int c) {
         const unsigned char *rec = plan0 + static_cast<int64_t>(c) * P.rec_bytes;
@@ -523,7 +546,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const float *wa = reinterpret_cast<const float *>(rec + P.o_wa);
         const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
         const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
-        const int4 *ent = reinterpret_cast<const int4 *>(rec + P.o_ent);
+        const int *ent_wo = reinterpret_cast<const int *>(rec + P.o_ent) + P.ENTA;
         const int nwt = reinterpret_cast<const PlanHdr *>(rec)->nwt;
         pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
 #pragma unroll
@@ -550,7 +573,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
         if constexpr (RES) {
             if (tid < M) pf_map = reinterpret_cast<const int *>(rec + P.o_map)[tid];
-            if (tid < P.ENT) pf_ent = ent[tid];
+            if (tid < P.ENT) pf_ent = make_int4(ent_wo[tid], ent_wo[P.ENTA + tid], ent_wo[2 * P.ENTA + tid], 0);
         }
     };
 
@@ -585,13 +608,12 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         if constexpr (RES) {
             if (tid < M && my_e >= 0) {
                 const int4 en = s_ent[my_e];
-                walk_slot<TS, CG>(en.y, en.z, en.w, x, m, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
+                walk_slot<TS, CG>(en.x, en.y, en.z, x, m, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
             }
         } else {
             // touched rows from HBM, EB at a time: entries, then rows, then
             // the walks and the write-backs
-            const int4 *ent = reinterpret_cast<const int4 *>(
-                plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
+            const int *ent = reinterpret_cast<const int *>(plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
             constexpr int RW = CG * static_cast<int>(sizeof(TS)) / 4;  // registers per row
             constexpr int EB = 16 / RW < 1 ? 1 : (16 / RW > kEPN ? kEPN : 16 / RW);
             for (int j0 = 0; j0 < kEPN; j0 += EB) {
@@ -602,7 +624,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < EB; ++j) {
                     const int eid = tid + (j0 + j) * kNT;
-                    if (eid < nt) en[j] = ent[eid];
+                    if (eid < nt)
+                        en[j] = make_int4(ent[eid], ent[P.ENTA + eid], ent[2 * P.ENTA + eid], ent[3 * P.ENTA + eid]);
                 }
 #pragma unroll
                 for (int j = 0; j < EB; ++j) {
@@ -701,6 +724,12 @@ __global__ void mass_fanout_kernel(const float *__restrict__ mass, float *__rest
     }
 }
 
+// Four values of type T as one vector access.
+template <typename T>
+struct alignas(4 * sizeof(T)) Quad {
+    T e[4];
+};
+
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g), four channels per
 // thread; the per-token square sums of the channel slices are added in
 // slice order.
@@ -722,13 +751,15 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__
     for (int j = 0; j < ncg; ++j) tot += sumsq[th * ncg + j];
     const float den = tot / static_cast<float>(d_v) + eps;
     const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-    const float4 r = *reinterpret_cast<const float4 *>(rbuf + th * d_v + c0);
-    const float rv[4] = {r.x, r.y, r.z, r.w};
+    const Quad<float> r = *reinterpret_cast<const Quad<float> *>(rbuf + th * d_v + c0);
+    const Quad<TIn> gv = *reinterpret_cast<const Quad<TIn> *>(g + th * d_v + c0);
+    Quad<TO> o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float om = norm_w ? norm_w[c0 + j] : 1.0f;
-        out[th * d_v + c0 + j] = from_f32<TO>(rv[j] * inv * om * sigmoid(to_f32(g[th * d_v + c0 + j])));
+        o.e[j] = from_f32<TO>(r.e[j] * inv * om * sigmoid(to_f32(gv.e[j])));
     }
+    *reinterpret_cast<Quad<TO> *>(out + th * d_v + c0) = o;
 }
 
 template <typename K>
@@ -744,7 +775,7 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     auto pk = plan_kernel<TIn>;
     hipError_t e = set_lds(pk, P.lds_plan);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kNT), P.lds_plan, st, a);
+    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPT), P.lds_plan, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!P.resident) {
@@ -818,7 +849,8 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool stat
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
             q.n_chunks = (T + C - 1) / C;
             size_t o = 256;  // header
-            q.o_ent = o; o += al256(static_cast<size_t>(q.ENT) * 16);
+            q.ENTA = (q.ENT + 63) & ~63;
+            q.o_ent = o; o += al256(static_cast<size_t>(q.ENTA) * 16);
             q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 4 : 0);
             q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
