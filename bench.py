@@ -260,6 +260,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="prefill_top8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device once (a plain copy "
+                         "kernel of known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): every "
@@ -279,6 +282,13 @@ def main():
     warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     extra = {}
     if kind == "decode":
         ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)

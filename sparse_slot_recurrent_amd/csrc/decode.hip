@@ -42,23 +42,31 @@ __device__ __forceinline__ int cape_move(int slot, int64_t pos, int U) {
     return static_cast<int>(moved);
 }
 
-template <int DP, typename WT, typename TIn>
+// KC: beam capacity (K rounded up to 8, 16, 32 or 64).  The beam being read
+// lives in LDS, column-interleaved by lane; up to KC = 32 the beam being
+// built is held in registers (its rank index is a compile-time constant of
+// the unrolled merge), which halves the LDS a wave needs and so doubles the
+// waves a CU can hold.
+template <int DP, int KC, typename WT, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, int64_t n, int T, int H,
     int U, int K, const int32_t *__restrict__ pos0, int cape,
     int32_t *__restrict__ w_idx, float *__restrict__ w_wt,
     int32_t *__restrict__ r_idx, float *__restrict__ r_wt) {
+    constexpr bool kRegs = KC <= 32;
     extern __shared__ unsigned char smem[];
     const int lane = threadIdx.x;
-    WT *bw = reinterpret_cast<WT *>(smem);                          // [2][K][64]
-    int32_t *bp = reinterpret_cast<int32_t *>(bw + 2 * K * kWave);  // [2][K][64]
+    WT *bw = reinterpret_cast<WT *>(smem);                                      // [bufs][KC][64]
+    int32_t *bp = reinterpret_cast<int32_t *>(bw + (kRegs ? 1 : 2) * KC * kWave);  // [bufs][KC][64]
     const int64_t a = static_cast<int64_t>(blockIdx.x) * kWave + lane;
     if (a >= n) return;  // no barrier below: lanes are independent
     const bool key = blockIdx.y == 0;
     const TIn *lg = (key ? k : q) + a * (U * DP);
-    auto BW = [&](int buf, int r) -> WT & { return bw[(buf * K + r) * kWave + lane]; };
-    auto BP = [&](int buf, int r) -> int32_t & { return bp[(buf * K + r) * kWave + lane]; };
+    auto BW = [&](int buf, int r) -> WT & { return bw[(buf * KC + r) * kWave + lane]; };
+    auto BP = [&](int buf, int r) -> int32_t & { return bp[(buf * KC + r) * kWave + lane]; };
 
+    WT nxw[kRegs ? KC : 1];
+    int32_t nxp[kRegs ? KC : 1];
     int cur = 0, nb = 1;
     BW(0, 0) = WT(1);
     BP(0, 0) = 0;
@@ -99,20 +107,21 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
             }
         }
         // Merge the d_p candidate lists into the next beam.
-        const int nn = min(K, nb * DP);
+        const int nn = min(K, nb * DP);  // the same in every lane
+        const int rd = kRegs ? 0 : cur;
         const int nxt = cur ^ 1;
         int h[DP];
         WT cw[DP];
         int cp[DP];
-        const WT b0 = BW(cur, 0);
-        const int p0 = BP(cur, 0);
+        const WT b0 = BW(rd, 0);
+        const int p0 = BP(rd, 0);
 #pragma unroll
         for (int d = 0; d < DP; ++d) {
             h[d] = 0;
             cw[d] = b0 * pr[d];
             cp[d] = p0 * DP + dg[d];
         }
-        for (int r = 0; r < nn; ++r) {
+        auto step = [&](WT &ow, int32_t &op) {
             int best = 0;
             WT bwv = cw[0];
             int bpv = cp[0];
@@ -123,15 +132,15 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
                 bwv = bt ? cw[d] : bwv;
                 bpv = bt ? cp[d] : bpv;
             }
-            BW(nxt, r) = bwv;
-            BP(nxt, r) = bpv;
+            ow = bwv;
+            op = bpv;
             int hb = 0;
 #pragma unroll
             for (int d = 0; d < DP; ++d)
                 if (d == best) hb = ++h[d];
             const bool more = hb < nb;
-            const WT nw = more ? BW(cur, hb) : WT(0);
-            const int np = more ? BP(cur, hb) : 0;
+            const WT nw = more ? BW(rd, hb) : WT(0);
+            const int np = more ? BP(rd, hb) : 0;
 #pragma unroll
             for (int d = 0; d < DP; ++d) {
                 if (d == best) {
@@ -139,8 +148,24 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
                     cp[d] = np * DP + dg[d];
                 }
             }
+        };
+        if constexpr (kRegs) {
+#pragma unroll
+            for (int r = 0; r < KC; ++r)
+                if (r < nn) step(nxw[r], nxp[r]);
+            if (u + 1 < U) {
+#pragma unroll
+                for (int r = 0; r < KC; ++r) {
+                    if (r < nn) {
+                        BW(0, r) = nxw[r];
+                        BP(0, r) = nxp[r];
+                    }
+                }
+            }
+        } else {
+            for (int r = 0; r < nn; ++r) step(BW(nxt, r), BP(nxt, r));
+            cur = nxt;
         }
-        cur = nxt;
         nb = nn;
     }
 
@@ -149,18 +174,29 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int64_t pos = (pos0 ? pos0[b] : 0) + t;
     int32_t *oi = (key ? w_idx : r_idx) + a * K;
     float *ow = (key ? w_wt : r_wt) + a * K;
-    for (int r = 0; r < K; ++r) {
-        const int slot = BP(cur, r);
-        oi[r] = cape ? cape_move<DP>(slot, pos, U) : slot;
-        ow[r] = static_cast<float>(BW(cur, r));
+    if constexpr (kRegs) {
+#pragma unroll
+        for (int r = 0; r < KC; ++r) {
+            if (r < K) {
+                oi[r] = cape ? cape_move<DP>(nxp[r], pos, U) : nxp[r];
+                ow[r] = static_cast<float>(nxw[r]);
+            }
+        }
+    } else {
+        for (int r = 0; r < K; ++r) {
+            const int slot = BP(cur, r);
+            oi[r] = cape ? cape_move<DP>(slot, pos, U) : slot;
+            ow[r] = static_cast<float>(BW(cur, r));
+        }
     }
 }
 
-template <int DP, typename TIn>
-hipError_t launch_dp(const DecodeArgs &d, hipStream_t st) {
+template <int DP, int KC, typename TIn>
+hipError_t launch_kc(const DecodeArgs &d, hipStream_t st) {
     using WT = double;
-    const size_t lds = static_cast<size_t>(2) * d.K * kWave * (sizeof(WT) + sizeof(int32_t));
-    auto kern = decode_kernel<DP, WT, TIn>;
+    constexpr int bufs = KC <= 32 ? 1 : 2;
+    const size_t lds = static_cast<size_t>(bufs) * KC * kWave * (sizeof(WT) + sizeof(int32_t));
+    auto kern = decode_kernel<DP, KC, WT, TIn>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -171,6 +207,14 @@ hipError_t launch_dp(const DecodeArgs &d, hipStream_t st) {
                        d.T, d.H, d.U, d.K, d.pos0, d.cape, d.w_idx, d.w_wt, d.r_idx,
                        d.r_wt);
     return hipGetLastError();
+}
+
+template <int DP, typename TIn>
+hipError_t launch_dp(const DecodeArgs &d, hipStream_t st) {
+    if (d.K <= 8) return launch_kc<DP, 8, TIn>(d, st);
+    if (d.K <= 16) return launch_kc<DP, 16, TIn>(d, st);
+    if (d.K <= 32) return launch_kc<DP, 32, TIn>(d, st);
+    return launch_kc<DP, 64, TIn>(d, st);
 }
 
 template <typename TIn>
