@@ -35,6 +35,14 @@ template <typename T> __device__ __forceinline__ float stored(float x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroup barrier ordering LDS only: global loads in flight (prefetches)
+// stay in flight across it.  Not for global-memory hand-offs between threads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Broadcast from a lane chosen by a wave-uniform index.
 __device__ __forceinline__ int bcast(int x, int lane) {
     return __builtin_amdgcn_readlane(x, lane);

@@ -73,16 +73,16 @@ __device__ int block_excl_scan(int x, int *wtot, int &total) {
     const int lane = lane_id(), wid = threadIdx.x / kWave;
     const int incl = wave_incl_scan(x);
     if (lane == kWave - 1) wtot[wid] = incl;
-    __syncthreads();
+    lds_barrier();
     if (wid == 0) {
         int y = lane < NW ? wtot[lane] : 0;
         y = wave_incl_scan(y);
         if (lane < NW) wtot[lane] = y;
     }
-    __syncthreads();
+    lds_barrier();
     const int base = wid > 0 ? wtot[wid - 1] : 0;
     total = wtot[NW - 1];
-    __syncthreads();
+    lds_barrier();
     return base + incl - x;
 }
 
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         if (hashed) tkey[i] = -1;
     }
     for (int i = tid; i <= P.ENT + P.EV; i += kPT) need[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
     // ---- 1. every event finds its slot's entry; writes count, reads flag.
     //         A zero-weight write changes nothing (alpha = 1, lambda = 0); a
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             atomicOr(&tcf[rpos[j]], kReadFlag);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 2. entries in table order: ids and write offsets from one scan of
     //         (1 + writes << 16) over the touched positions
@@ -347,13 +347,13 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         nwt = total >> 16;
         if (tid == 0) ewo[nt] = nwt;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. writes into their entries' buckets, arrival order ...
 #pragma unroll
     for (int j = 0; j < kEPW; ++j)
         if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPT;
-    __syncthreads();
+    lds_barrier();
     // ... then causal order: a write's rank is the number of the bucket's
     // writes with a smaller event index (token-major; one write per slot and
     // token)
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             sk[wo + r] = e;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4. each read sees version c of its slot: c = the number of the
     //         slot's writes at tokens <= its own (writes come first within a
@@ -390,12 +390,12 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             need[gv[j]] = 1;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 5. version rows: exclusive scan of the flags over nt + nwt + 1
     //         positions; version g has a row iff need[g + 1] > need[g]
     const int nver = block_scan_array<kPT>(need, nt + nwt + 1, wtot);
-    __syncthreads();
+    lds_barrier();
 
     // ---- 6. the record: entries, writes staged in LDS in causal order, then
     //         everything stored with consecutive lanes on consecutive words
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             rr[e] = gv[j] >= 0 ? rt[j] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < nwt; i += kPT) {
         wtv[i] = bk[i];
         ww[i] = __int_as_float(sk[i]);
@@ -535,7 +535,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     // The next chunk's plan and values, loaded one chunk ahead.
     constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
     int pf_wtv[kEVT], pf_rv[kEVT];
-    float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT], pf_v[VPT];
+    float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT];
+    TIn pf_v[VPT];  // raw: converting at load time would wait for each load
     int4 pf_ent = make_int4(0, 0, 0, -1);  // write offset, writes, version-0 row
     int pf_map = -1, pf_nt = 0;
     auto prefetch = [&](int c) {
@@ -547,12 +548,14 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
         const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
         const int *ent_wo = reinterpret_cast<const int *>(rec + P.o_ent) + P.ENTA;
-        const int nwt = reinterpret_cast<const PlanHdr *>(rec)->nwt;
         pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
+        // every load is independent of every other (no wait on the header):
+        // the write list is read to its capacity, entries past its end are
+        // never used
 #pragma unroll
         for (int j = 0; j < kEVT; ++j) {
             const int i = tid + j * kNT;
-            if (i < nwt) {
+            if (i < EV) {
                 pf_wtv[j] = wtv[i];
                 pf_ww[j] = ww[i];
                 pf_wa[j] = wa[i];
@@ -564,12 +567,9 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * kNT;
-            pf_v[j] = 0.f;
-            if (i < Cc * CG) {
-                const int t = i / CG, cc = i % CG;
-                pf_v[j] = to_f32(v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + cc]);
-            }
+            const int i = min(tid + j * kNT, Cc * CG - 1);  // in range; extra lanes unused
+            const int t = i / CG, cc = i % CG;
+            pf_v[j] = v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + cc];
         }
         if constexpr (RES) {
             if (tid < M) pf_map = reinterpret_cast<const int *>(rec + P.o_map)[tid];
@@ -595,13 +595,13 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int i = tid + j * kNT;
-            if (i < Cc * CG) vbuf[swz_index<float, CG>(i / CG, i % CG)] = pf_v[j];
+            if (i < Cc * CG) vbuf[swz_index<float, CG>(i / CG, i % CG)] = to_f32(pf_v[j]);
         }
         const int my_e = pf_map, nt = pf_nt;
         if constexpr (RES) {
             if (tid < P.ENT) s_ent[tid] = pf_ent;
         }
-        __syncthreads();
+        lds_barrier();
         // ---- 2. the next chunk's loads go out now and land during the walk
         if (c + 1 < nchunks) prefetch(c + 1);
         // ---- 3. walk the touched slots
@@ -659,7 +659,9 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                 }
             }
         }
-        __syncthreads();
+        // HBM mode: this chunk's row write-backs must be visible to the
+        // threads that gather the next chunk's rows
+        if constexpr (RES) lds_barrier(); else __syncthreads();
         // ---- 4. reads: r = sum_k rho_k * version_k (k in address order) for
         //         one 16-byte piece of the slice per thread; r and the sum of
         //         squares over the slice go to global memory
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
             }
         }
         (void)nev;
-        __syncthreads();
+        lds_barrier();
     }
 
     if constexpr (RES) {
