@@ -57,6 +57,7 @@ struct ChunkPlan {
     int ENTA;           // ENT rounded up to 64 (stride of the entry arrays)
     int HT;             // plan hash table size, 0: the slot is its own index
     int ncg;            // d_v / CG
+    int RG;             // lanes per (token, 16-byte piece) in the read reduction
     int64_t n_chunks;
     // one (unit, chunk) plan record and its sections (byte offsets)
     size_t rec_bytes, o_ent, o_map, o_wtv, o_ww, o_wa, o_rv, o_rr;

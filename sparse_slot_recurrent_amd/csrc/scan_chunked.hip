@@ -662,18 +662,23 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         // HBM mode: this chunk's row write-backs must be visible to the
         // threads that gather the next chunk's rows
         if constexpr (RES) lds_barrier(); else __syncthreads();
-        // ---- 4. reads: r = sum_k rho_k * version_k (k in address order) for
-        //         one 16-byte piece of the slice per thread; r and the sum of
-        //         squares over the slice go to global memory
+        // ---- 4. reads: r = sum_k rho_k * version_k for one 16-byte piece of
+        //         the slice; G = P.RG lanes share a (token, piece), lane g
+        //         taking reads k = g, g + G, ... in order, combined by a
+        //         butterfly (a fixed order); r and the sum of squares over the
+        //         slice go to global memory
         {
             constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per piece
             constexpr int NCH = CG / EPC;                            // pieces per row
-            for (int i = tid; i < Cc * NCH; i += kNT) {
-                const int t = i / NCH, j = i % NCH;
+            const int G = P.RG;
+            const int nitems = Cc * NCH * G;  // whole groups and tokens per wave
+            for (int i = tid; i < nitems; i += kNT) {
+                const int g = i % G, item = i / G;
+                const int t = item / NCH, j = item % NCH;
                 float r[EPC];
 #pragma unroll
                 for (int cc = 0; cc < EPC; ++cc) r[cc] = 0.f;
-                for (int k = 0; k < K; ++k) {
+                for (int k = g; k < K; k += G) {
                     // skipped reads have no row; a zero weight adds nothing
                     const int row = t * K + k;
                     const int vr = s_rv[row];
@@ -686,17 +691,22 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                         for (int cc = 0; cc < EPC; ++cc) r[cc] = fmaf(rw, sv[cc], r[cc]);
                     }
                 }
-                const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
-                float *dst = a.rbuf + th * d_v + cg * CG + j * EPC;
+                for (int off = 1; off < G; off <<= 1) {
 #pragma unroll
-                for (int cc = 0; cc < EPC; cc += 4)
-                    *reinterpret_cast<float4 *>(dst + cc) = make_float4(r[cc], r[cc + 1], r[cc + 2], r[cc + 3]);
+                    for (int cc = 0; cc < EPC; ++cc) r[cc] += __shfl_xor(r[cc], off, kWave);
+                }
+                const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
+                if (g == 0) {
+                    float *dst = a.rbuf + th * d_v + cg * CG + j * EPC;
+#pragma unroll
+                    for (int cc = 0; cc < EPC; cc += 4)
+                        *reinterpret_cast<float4 *>(dst + cc) = make_float4(r[cc], r[cc + 1], r[cc + 2], r[cc + 3]);
+                }
                 float ss = 0.f;
 #pragma unroll
                 for (int cc = 0; cc < EPC; ++cc) ss = fmaf(r[cc], r[cc], ss);
-#pragma unroll
-                for (int off = NCH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-                if (j == 0) a.sumsq[th * ncg + cg] = ss;
+                for (int off = G; off < NCH * G; off <<= 1) ss += __shfl_xor(ss, off, kWave);
+                if (g == 0 && j == 0) a.sumsq[th * ncg + cg] = ss;
             }
         }
         (void)nev;
@@ -846,6 +856,14 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool stat
                 q.HT = ht;
             }
             q.ncg = d_v / CG;
+            // lanes per (token, 16-byte piece) in the read reduction: enough
+            // to keep the workgroup busy, one group per wave at most
+            {
+                const int nch = CG * sbytes / 16;
+                int g = 1;
+                while (g < 16 && g < K && static_cast<int64_t>(C) * nch * g * 2 <= kNT) g *= 2;
+                q.RG = g;
+            }
             q.lds_plan = plan_lds(q, M).total;
             q.lds_scan = scan_lds(q, M, sbytes).total;
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
