@@ -130,12 +130,12 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op);
  *   addr_out  NULL, or where to export the addresses used.
  *   workspace ramnet_workspace_bytes(p, RAMNET_OP_PREFILL) bytes.  It holds
  *             the decoded addresses (unless addr_out is given) and, on the
- *             slot-grouped path, the un-normalised reads and per-token sums
- *             of squares between the recurrence and the RMSNorm kernel.
- *             Its contents on entry do not matter.
- * Results of the slot-grouped path (long sequences whose state slice fits
- * on chip) can differ between runs in the last bits of fp32 additions: reads
- * of one token are accumulated in LDS in arrival order. */
+ *             slot-grouped path (T >= 32, M <= 2^22, K <= 63), the per-chunk
+ *             slot-grouping plans, the un-normalised reads, per-token sums of
+ *             squares and per-slice mass copies.  Its contents on entry do
+ *             not matter.
+ * Results are deterministic: every sum is taken in a fixed order, so repeated
+ * calls on the same inputs give the same bits. */
 ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
                                   const void *k, const void *v,
                                   const void *gamma, const void *g,
