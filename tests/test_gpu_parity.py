@@ -183,6 +183,67 @@ def test_prefill_with_oracle_addresses(rn, orc, name):
     assert np.array_equal(to_np(addr.w_idx), ref["w_idx"])
 
 
+@pytest.mark.parametrize("d_p,U,K,d_v,st_dt,T,pool", [
+    (4, 5, 16, 64, "f32", 300, 40),     # slot rows in registers; ~8 writes per slot and token-chunk
+    (4, 6, 8, 64, "bf16", 700, 300),    # 4096 slots: rows in HBM, slot-indexed plan table
+    (4, 8, 16, 64, "bf16", 300, 5000),  # 65536 slots: rows in HBM, hashed plan table
+])
+def test_chunked_given_addresses_edge_cases(rn, orc, d_p, U, K, d_v, st_dt, T, pool):
+    """Caller-given addresses through the slot-grouped path: two chunks with
+    a ragged tail, slots drawn from a small pool (long per-slot write lists
+    within a chunk), slots outside [0, M) and zero weights, which the ABI
+    skips.  The oracle gets a skipped entry as slot 0 with weight 0, which
+    changes nothing and reads nothing (project page, Gated Sparse Update:
+    w = 0 gives alpha = 1 and lambda = 0)."""
+    B, H = 1, 2
+    w = synth.Workload("given", B=B, T=T, H=H, d_p=d_p, U=U, K=K, d_v=d_v,
+                       in_dtype="f32", state_dtype=st_dt, logit_sigma=1.0,
+                       seed=21, s0_sigma=0.5, m0_uniform=(0.0, 2.0))
+    x = synth.make_inputs(w)
+    M = d_p ** U
+    rng = np.random.default_rng(77)
+    slots = rng.choice(M, size=pool, replace=False)
+
+    def addresses():
+        n = B * T * H
+        idx = np.stack([rng.choice(slots, size=K, replace=False) for _ in range(n)])
+        idx = idx.reshape(B, T, H, K).astype(np.int32)
+        wt = rng.uniform(0.0, 1.0, idx.shape).astype(np.float32)
+        wt[rng.random(idx.shape) < 0.05] = 0.0
+        bad = rng.random(idx.shape) < 0.05
+        nb = int(bad.sum())
+        idx_g = idx.copy()
+        idx_g[bad] = np.where(rng.random(nb) < 0.5, -1 - rng.integers(0, 3, nb),
+                              M + rng.integers(0, 3, nb))
+        idx_o, wt_o = idx.copy(), wt.copy()
+        idx_o[bad] = 0
+        wt_o[bad] = 0.0
+        return idx_g, wt, idx_o, wt_o
+
+    wi_g, ww_g, wi_o, ww_o = addresses()
+    ri_g, rw_g, ri_o, rw_o = addresses()
+    S_ref, m_ref = x["S0"].copy(), x["m0"].copy()
+    ref = orc.scan_given(wi_o, ww_o, ri_o, rw_o, x["v"], x["gamma"], x["g"],
+                         S_ref, m_ref, d_p=d_p, U=U, state_bf16=st_dt == "bf16")
+    ai = rn.Addresses(*(torch.from_numpy(a).cuda() for a in (wi_g, ww_g, ri_g, rw_g)))
+    out, _, d = run_gpu(rn, w, x, addr_in=ai, export=False)
+    bf = st_dt == "bf16"
+    assert_close(to_np(out), ref, bf, "out")
+    assert_close(to_np(d["S"]), S_ref, bf, "S", slot_state=True)
+    assert_close(to_np(d["mass"]), m_ref, False, "mass")
+    # rows no valid write touched are bit-unchanged
+    touched = np.zeros((B, H, M), bool)
+    valid = (wi_g >= 0) & (wi_g < M) & (ww_g > 0)
+    for b in range(B):
+        for h in range(H):
+            touched[b, h, wi_g[b, :, h][valid[b, :, h]]] = True
+    S0 = x["S0"]
+    S_gpu = to_np(d["S"])
+    if bf:
+        S0 = synth.round_bf16(S0)
+    assert np.array_equal(S_gpu[~touched], S0[~touched])
+
+
 def test_norm_weight_and_cape_off(rn, orc):
     w = synth.WORKLOADS["prefill_top8"].replace(cape=0)
     x = synth.make_inputs(w, B=1, T=100, H=4)
