@@ -110,16 +110,23 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
         const int nn = min(K, nb * DP);  // the same in every lane
         const int rd = kRegs ? 0 : cur;
         const int nxt = cur ^ 1;
+        // List d's head candidate (cw, cp) and, loaded one step ahead, the
+        // beam entry after its head (nbw, nbp), so that advancing a list
+        // does not wait for LDS.
         int h[DP];
-        WT cw[DP];
-        int cp[DP];
+        WT cw[DP], nbw[DP];
+        int cp[DP], nbp[DP];
         const WT b0 = BW(rd, 0);
         const int p0 = BP(rd, 0);
+        const WT b1 = nb > 1 ? BW(rd, 1) : WT(0);
+        const int p1 = nb > 1 ? BP(rd, 1) : 0;
 #pragma unroll
         for (int d = 0; d < DP; ++d) {
             h[d] = 0;
             cw[d] = b0 * pr[d];
             cp[d] = p0 * DP + dg[d];
+            nbw[d] = b1;
+            nbp[d] = p1;
         }
         auto step = [&](WT &ow, int32_t &op) {
             int best = 0;
@@ -134,18 +141,15 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
             }
             ow = bwv;
             op = bpv;
-            int hb = 0;
-#pragma unroll
-            for (int d = 0; d < DP; ++d)
-                if (d == best) hb = ++h[d];
-            const bool more = hb < nb;
-            const WT nw = more ? BW(rd, hb) : WT(0);
-            const int np = more ? BP(rd, hb) : 0;
 #pragma unroll
             for (int d = 0; d < DP; ++d) {
                 if (d == best) {
-                    cw[d] = more ? nw * pr[d] : WT(-1);  // exhausted list
-                    cp[d] = np * DP + dg[d];
+                    const int hb = ++h[d];
+                    cw[d] = hb < nb ? nbw[d] * pr[d] : WT(-1);  // -1: exhausted list
+                    cp[d] = nbp[d] * DP + dg[d];
+                    const bool more = hb + 1 < nb;
+                    nbw[d] = more ? BW(rd, hb + 1) : WT(0);
+                    nbp[d] = more ? BP(rd, hb + 1) : 0;
                 }
             }
         };
