@@ -69,7 +69,7 @@ struct ChunkArgs : ScanArgs {
     ChunkPlan p;
     float *rbuf;     // may alias out when the output is fp32
     float *sumsq;
-    float *mass_ws;  // per-slice mass ([ncg][units][M] in HBM mode, else [units][M])
+    float *mass_ws;  // final mass [units][M]; HBM mode: per-slice copies [units][M][ncg]
     unsigned char *plan;
 };
 

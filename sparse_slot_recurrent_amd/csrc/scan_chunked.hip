@@ -530,7 +530,9 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
             m = a.mass[static_cast<int64_t>(unit) * M + tid];
         }
     }
-    float *mws = a.mass_ws + (static_cast<int64_t>(cg) * units + unit) * M;  // HBM mode
+    // HBM mode: slice cg's mass copy of slot s is mass_ws[(unit * M + s) * ncg +
+    // cg], so the slices' copies of a slot share a cache line
+    float *mws = a.mass_ws + static_cast<int64_t>(unit) * M * ncg + cg;
 
     // The next chunk's plan and values, loaded one chunk ahead.
     constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
@@ -577,7 +579,24 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
     };
 
+    // HBM mode: this thread's touched-slot entries of a chunk (slot, write
+    // offset, writes, version-0 row), loaded one chunk ahead
+    int3 pf_en[RES ? 1 : kEPN];  // slot, write offset, writes | (version-0 row + 1) << 16
+    auto prefetch_ent = [&](int c) {
+        if constexpr (!RES) {
+            const int *ent = reinterpret_cast<const int *>(plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
+#pragma unroll
+            for (int j = 0; j < kEPN; ++j) {
+                const int eid = tid + j * kNT;
+                if (eid < P.ENT)
+                    pf_en[j] = make_int3(ent[eid], ent[P.ENTA + eid],
+                                         ent[2 * P.ENTA + eid] | ((ent[3 * P.ENTA + eid] + 1) << 16));
+            }
+        }
+    };
+
     prefetch(0);
+    prefetch_ent(0);
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
         // ---- 1. stage this chunk's plan and values
@@ -611,49 +630,43 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                 walk_slot<TS, CG>(en.x, en.y, en.z, x, m, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
             }
         } else {
-            // touched rows from HBM, EB at a time: entries, then rows, then
-            // the walks and the write-backs
-            const int *ent = reinterpret_cast<const int *>(plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
+            // touched rows from HBM, EB at a time (entries already in
+            // registers): rows and masses, then the walks and write-backs
             constexpr int RW = CG * static_cast<int>(sizeof(TS)) / 4;  // registers per row
             constexpr int EB = 16 / RW < 1 ? 1 : (16 / RW > kEPN ? kEPN : 16 / RW);
+#pragma unroll
             for (int j0 = 0; j0 < kEPN; j0 += EB) {
                 if (tid + j0 * kNT >= nt) break;
-                int4 en[EB];
                 HRow<TS, CG> rows[EB];
                 float ms[EB];
 #pragma unroll
                 for (int j = 0; j < EB; ++j) {
                     const int eid = tid + (j0 + j) * kNT;
-                    if (eid < nt)
-                        en[j] = make_int4(ent[eid], ent[P.ENTA + eid], ent[2 * P.ENTA + eid], ent[3 * P.ENTA + eid]);
-                }
-#pragma unroll
-                for (int j = 0; j < EB; ++j) {
-                    const int eid = tid + (j0 + j) * kNT;
-                    if (eid < nt) {
-                        const int64_t slot = en[j].x;
+                    if (j0 + j < kEPN && eid < nt) {
+                        const int64_t slot = pf_en[j0 + j].x;
                         rows[j] = *reinterpret_cast<const HRow<TS, CG> *>(
                             S + (static_cast<int64_t>(unit) * M + slot) * d_v + cg * CG);
-                        ms[j] = mws[slot];
+                        ms[j] = mws[slot * ncg];
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < EB; ++j) {
                     const int eid = tid + (j0 + j) * kNT;
-                    if (eid < nt) {
+                    if (j0 + j < kEPN && eid < nt) {
+                        const int3 en = pf_en[j0 + j];
+                        const int nw = en.z & 0xffff, x0r = (en.z >> 16) - 1;
                         float xr[CG];
 #pragma unroll
                         for (int cc = 0; cc < CG; ++cc) xr[cc] = to_f32(rows[j].e[cc]);
                         float mm = ms[j];
-                        walk_slot<TS, CG>(en[j].y, en[j].z, en[j].w, xr, mm, a.eps_gsu, s_wtv, s_ww,
-                                          s_wa, vbuf, ver);
-                        if (en[j].z > 0) {
+                        walk_slot<TS, CG>(en.y, nw, x0r, xr, mm, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
+                        if (nw > 0) {
                             HRow<TS, CG> o;
 #pragma unroll
                             for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(xr[cc]);
                             *reinterpret_cast<HRow<TS, CG> *>(
-                                S + (static_cast<int64_t>(unit) * M + en[j].x) * d_v + cg * CG) = o;
-                            mws[en[j].x] = mm;
+                                S + (static_cast<int64_t>(unit) * M + en.x) * d_v + cg * CG) = o;
+                            mws[static_cast<int64_t>(en.x) * ncg] = mm;
                         }
                     }
                 }
@@ -662,6 +675,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         // HBM mode: this chunk's row write-backs must be visible to the
         // threads that gather the next chunk's rows
         if constexpr (RES) lds_barrier(); else __syncthreads();
+        if (c + 1 < nchunks) prefetch_ent(c + 1);  // lands during the reduction
         // ---- 4. reads: r = sum_k rho_k * version_k for one 16-byte piece of
         //         the slice; G = P.RG lanes share a (token, piece), lane g
         //         taking reads k = g, g + G, ... in order, combined by a
@@ -732,7 +746,7 @@ __global__ void mass_fanout_kernel(const float *__restrict__ mass, float *__rest
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const float x = mass[i];
-        for (int c = 0; c < ncg; ++c) mass_ws[c * n + i] = x;
+        for (int c = 0; c < ncg; ++c) mass_ws[i * ncg + c] = x;
     }
 }
 
@@ -752,10 +766,11 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__
                                                        const float *__restrict__ norm_w,
                                                        TO *out, int64_t n, int d_v, float eps,
                                                        const float *__restrict__ mass_ws,
-                                                       float *__restrict__ mass, int64_t n_mass) {
+                                                       int mass_stride, float *__restrict__ mass,
+                                                       int64_t n_mass) {
     const int q4 = d_v / 4;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < n_mass) mass[i] = mass_ws[i];
+    if (i < n_mass) mass[i] = mass_ws[i * mass_stride];
     if (i >= n * q4) return;
     const int64_t th = i / q4;
     const int c0 = static_cast<int>(i - th * q4) * 4;
@@ -809,7 +824,7 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const unsigned g2 = static_cast<unsigned>((work + 255) / 256);
     hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf, a.sumsq,
                        P.ncg, static_cast<const TIn *>(a.g), a.norm_w, static_cast<TS *>(a.out), n,
-                       a.d_v, a.eps_norm, a.mass_ws, a.mass, n_mass);
+                       a.d_v, a.eps_norm, a.mass_ws, P.resident ? 1 : P.ncg, a.mass, n_mass);
     return hipGetLastError();
 }
 
