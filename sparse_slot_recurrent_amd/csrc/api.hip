@@ -273,9 +273,14 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         return hip_status(ramnet::launch_step_fused(sa, st), "decode step launch");
     }
     ramnet_addr addr;
+    // Addresses kept in the workspace for the slot-grouped path are laid out
+    // [B,H,T,K], so that each head's chunk of addresses is contiguous.
+    bool unit_major = false;
     if (decode) {
         addr = lp.addr_bytes ? carve_addr(ws, n, p->K) : *addr_out;
-        hipError_t e = ramnet::launch_decode(decode_args(p, q, k, pos, n, p->T, addr), st);
+        ramnet::DecodeArgs da = decode_args(p, q, k, pos, n, p->T, addr);
+        unit_major = da.unit_major = lp.addr_bytes && lp.chunked;
+        hipError_t e = ramnet::launch_decode(da, st);
         if (e != hipSuccess) return hip_status(e, "address decoder launch");
     } else {
         addr = *addr_in;
@@ -297,6 +302,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     a.w_wt = addr.w_wt;
     a.r_idx = addr.r_idx;
     a.r_wt = addr.r_wt;
+    a.addr_unit_major = unit_major;
     a.S = S;
     a.mass = mass;
     a.out = out;

@@ -50,7 +50,7 @@ __device__ __forceinline__ int cape_move(int slot, int64_t pos, int U) {
 template <int DP, int KC, typename WT, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, int64_t n, int T, int H,
-    int U, int K, const int32_t *__restrict__ pos0, int cape,
+    int U, int K, const int32_t *__restrict__ pos0, int cape, bool unit_major,
     int32_t *__restrict__ w_idx, float *__restrict__ w_wt,
     int32_t *__restrict__ r_idx, float *__restrict__ r_wt) {
     constexpr bool kRegs = KC <= 32;
@@ -176,8 +176,10 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int64_t b = a / (static_cast<int64_t>(T) * H);
     const int64_t t = (a / H) % T;
     const int64_t pos = (pos0 ? pos0[b] : 0) + t;
-    int32_t *oi = (key ? w_idx : r_idx) + a * K;
-    float *ow = (key ? w_wt : r_wt) + a * K;
+    // [B,T,H,K], or [B,H,T,K] so that a head's addresses are contiguous
+    const int64_t o = unit_major ? ((b * H + a % H) * T + t) : a;
+    int32_t *oi = (key ? w_idx : r_idx) + o * K;
+    float *ow = (key ? w_wt : r_wt) + o * K;
     if constexpr (kRegs) {
 #pragma unroll
         for (int r = 0; r < KC; ++r) {
@@ -208,8 +210,8 @@ hipError_t launch_kc(const DecodeArgs &d, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((d.n + kWave - 1) / kWave), 2);
     hipLaunchKernelGGL(kern, grid, dim3(kWave), lds, st,
                        static_cast<const TIn *>(d.q), static_cast<const TIn *>(d.k), d.n,
-                       d.T, d.H, d.U, d.K, d.pos0, d.cape, d.w_idx, d.w_wt, d.r_idx,
-                       d.r_wt);
+                       d.T, d.H, d.U, d.K, d.pos0, d.cape, d.unit_major, d.w_idx, d.w_wt,
+                       d.r_idx, d.r_wt);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct DecodeArgs {
     const int32_t *pos0;  // position of token t of sequence b: pos0[b] + t
     int cape;
     bool in_bf16;
+    bool unit_major;  // write addresses as [B,H,T,K] (else [B,T,H,K])
     int32_t *w_idx, *r_idx;
     float *w_wt, *r_wt;
 };
@@ -30,6 +31,7 @@ struct ScanArgs {
     const float *norm_w;
     const int32_t *w_idx, *r_idx;
     const float *w_wt, *r_wt;
+    bool addr_unit_major;  // addresses are [B,H,T,K] (else [B,T,H,K])
     void *S;
     float *mass;
     void *out;

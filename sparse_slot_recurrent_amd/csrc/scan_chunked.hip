@@ -269,10 +269,11 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         if (e < nev) {
             const int t = div_by(e, kdiv), k = e - t * K;
             const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
-            ws[j] = a.w_idx[th * K + k];
-            wt[j] = a.w_wt[th * K + k];
-            rs[j] = a.r_idx[th * K + k];
-            rt[j] = a.r_wt[th * K + k];
+            const int64_t ai = (a.addr_unit_major ? static_cast<int64_t>(unit) * a.T + t0 + t : th) * K + k;
+            ws[j] = a.w_idx[ai];
+            wt[j] = a.w_wt[ai];
+            rs[j] = a.r_idx[ai];
+            rt[j] = a.r_wt[ai];
             eg[j] = to_f32(gam[th]);
         }
     }
