@@ -437,41 +437,75 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
 // LDS of the scan kernel (byte offsets).
 struct ScanLds {
-    size_t v, wtv, ww, wa, rv, rr, ent, ver, total;
+    size_t v, wtv, wwa, rv, rr, ent, ver, total;
 };
+__host__ __device__ inline size_t al256d(size_t x) { return (x + 255) & ~size_t(255); }
 __host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes) {
     ScanLds L{};
     size_t o = 0;
-    L.v = o; o = al16(o + static_cast<size_t>(p.C) * p.CG * 4);             // values of the slice
+    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (p.CG + 4) * 4);       // values, rows padded by 16 B
     L.wtv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                 // write: token | row
-    L.ww = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // write weight
-    L.wa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // write retention
+    L.wwa = o; o = al16(o + static_cast<size_t>(p.EV) * 8);                 // write: weight, retention
     L.rv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read: version row
     L.rr = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read weight
     L.ent = o; o = al16(o + (p.resident ? static_cast<size_t>(p.ENT) * 16 : 0));
-    L.ver = o; o = al16(o + static_cast<size_t>(p.EV) * p.CG * sbytes);    // version rows
+    L.ver = o = al256d(o); o = al16(o + static_cast<size_t>(p.EV) * p.CG * sbytes);  // version rows
     L.total = o;
     return L;
+}
+
+// Version row `r` ([rows][CG] TS at a row-size-aligned LDS byte offset, 16-byte
+// chunks XOR-swizzled by the row): chunk j is at the returned offset ^ (j << 4).
+template <typename T, int CG>
+__device__ __forceinline__ uint32_t row_chunk0(uint32_t base, int r) {
+    return base + static_cast<uint32_t>(r) * (CG * sizeof(T)) + (row_swz<T, CG>(r) << 4);
+}
+template <int CG>
+__device__ __forceinline__ void store_row_x(unsigned char *lds, uint32_t a0, const float (&x)[CG], float) {
+#pragma unroll
+    for (int j = 0; j < CG / 4; ++j)
+        *reinterpret_cast<float4 *>(lds + (a0 ^ (j << 4))) =
+            make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+}
+template <int CG>
+__device__ __forceinline__ void store_row_x(unsigned char *lds, uint32_t a0, const float (&x)[CG], bf16_t) {
+#pragma unroll
+    for (int j = 0; j < CG / 8; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = static_cast<uint32_t>(bf16_rne(x[8 * j + 2 * q]).bits) |
+                   (static_cast<uint32_t>(bf16_rne(x[8 * j + 2 * q + 1]).bits) << 16);
+        *reinterpret_cast<uint4 *>(lds + (a0 ^ (j << 4))) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 }
 
 // Applies one touched slot's chunk: version 0 if a read sees it, then the
 // writes in causal order (mass, lambda, row), storing the versions reads see.
 template <typename TS, int CG>
 __device__ __forceinline__ void walk_slot(int wo, int nw, int x0r, float (&x)[CG], float &m,
-                                          float eps, const int *wtv, const float *ww,
-                                          const float *wa, const float *vbuf, TS *ver) {
-    if (x0r >= 0) store_row<CG>(ver + x0r * CG, row_swz<TS, CG>(x0r), x);
+                                          float eps, const int *wtv, const float2 *wwa,
+                                          const float *vbuf, unsigned char *lds, uint32_t ver_off) {
+    if (x0r >= 0) store_row_x<CG>(lds, row_chunk0<TS, CG>(ver_off, x0r), x, TS{});
     for (int i = 0; i < nw; ++i) {
         const int tv = wtv[wo + i];
         const int t = tv & 1023, vr = (tv >> 10) - 1;
-        const float w = ww[wo + i];
-        m = fmaf(wa[wo + i], m, w);
-        const float lam = w * __builtin_amdgcn_rcpf(m + eps);
+        const float2 wa = wwa[wo + i];  // weight, retention
+        m = fmaf(wa.y, m, wa.x);
+        const float lam = wa.x * __builtin_amdgcn_rcpf(m + eps);
+        const float4 *vrow = reinterpret_cast<const float4 *>(vbuf + t * (CG + 4));
         float vt[CG];
-        load_row<CG>(vbuf + t * CG, row_swz<float, CG>(t), vt);
+#pragma unroll
+        for (int j = 0; j < CG / 4; ++j) {
+            const float4 f = vrow[j];
+            vt[4 * j] = f.x;
+            vt[4 * j + 1] = f.y;
+            vt[4 * j + 2] = f.z;
+            vt[4 * j + 3] = f.w;
+        }
 #pragma unroll
         for (int c = 0; c < CG; ++c) x[c] = stored<TS>(fmaf(lam, vt[c] - x[c], x[c]));
-        if (vr >= 0) store_row<CG>(ver + vr * CG, row_swz<TS, CG>(vr), x);
+        if (vr >= 0) store_row_x<CG>(lds, row_chunk0<TS, CG>(ver_off, vr), x, TS{});
     }
 }
 
@@ -507,8 +541,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     const ScanLds L = scan_lds(P, a.M, sizeof(TS));
     float *vbuf = reinterpret_cast<float *>(smem + L.v);
     int *s_wtv = reinterpret_cast<int *>(smem + L.wtv);
-    float *s_ww = reinterpret_cast<float *>(smem + L.ww);
-    float *s_wa = reinterpret_cast<float *>(smem + L.wa);
+    float2 *s_wwa = reinterpret_cast<float2 *>(smem + L.wwa);
+    const uint32_t ver_off = static_cast<uint32_t>(L.ver);
     int *s_rv = reinterpret_cast<int *>(smem + L.rv);
     float *s_rr = reinterpret_cast<float *>(smem + L.rr);
     int4 *s_ent = reinterpret_cast<int4 *>(smem + L.ent);
@@ -606,8 +640,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
             const int i = tid + j * kNT;
             if (i < EV) {
                 s_wtv[i] = pf_wtv[j];
-                s_ww[i] = pf_ww[j];
-                s_wa[i] = pf_wa[j];
+                s_wwa[i] = make_float2(pf_ww[j], pf_wa[j]);
                 s_rv[i] = pf_rv[j];
                 s_rr[i] = pf_rr[j];
             }
@@ -615,7 +648,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int i = tid + j * kNT;
-            if (i < Cc * CG) vbuf[swz_index<float, CG>(i / CG, i % CG)] = to_f32(pf_v[j]);
+            if (i < Cc * CG) vbuf[(i / CG) * (CG + 4) + i % CG] = to_f32(pf_v[j]);
         }
         const int my_e = pf_map, nt = pf_nt;
         if constexpr (RES) {
@@ -628,13 +661,13 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         if constexpr (RES) {
             if (tid < M && my_e >= 0) {
                 const int4 en = s_ent[my_e];
-                walk_slot<TS, CG>(en.x, en.y, en.z, x, m, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
+                walk_slot<TS, CG>(en.x, en.y, en.z, x, m, a.eps_gsu, s_wtv, s_wwa, vbuf, smem, ver_off);
             }
         } else {
             // touched rows from HBM, EB at a time (entries already in
             // registers): rows and masses, then the walks and write-backs
             constexpr int RW = CG * static_cast<int>(sizeof(TS)) / 4;  // registers per row
-            constexpr int EB = 16 / RW < 1 ? 1 : (16 / RW > kEPN ? kEPN : 16 / RW);
+            constexpr int EB = 8 / RW < 1 ? 1 : (8 / RW > kEPN ? kEPN : 8 / RW);
 #pragma unroll
             for (int j0 = 0; j0 < kEPN; j0 += EB) {
                 if (tid + j0 * kNT >= nt) break;
@@ -660,7 +693,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
                         for (int cc = 0; cc < CG; ++cc) xr[cc] = to_f32(rows[j].e[cc]);
                         float mm = ms[j];
-                        walk_slot<TS, CG>(en.y, nw, x0r, xr, mm, a.eps_gsu, s_wtv, s_ww, s_wa, vbuf, ver);
+                        walk_slot<TS, CG>(en.y, nw, x0r, xr, mm, a.eps_gsu, s_wtv, s_wwa, vbuf, smem, ver_off);
                         if (nw > 0) {
                             HRow<TS, CG> o;
 #pragma unroll
