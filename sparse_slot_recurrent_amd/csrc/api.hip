@@ -121,7 +121,7 @@ LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
     const bool sbf = p->state_dtype == RAMNET_BF16;
     lp.chunked = false;
     if (!step) {
-        lp.cp = ramnet::plan_chunked(p->M, p->K, p->d_v, p->B, p->T, p->H, sbf);
+        lp.cp = ramnet::plan_chunked(p->M, p->K, p->d_v, p->B, p->T, p->H, p->in_dtype == RAMNET_BF16, sbf);
         lp.chunked = lp.cp.ok;
     }
     // The fused decoding step keeps its addresses on chip.

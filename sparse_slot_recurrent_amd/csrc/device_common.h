@@ -51,6 +51,27 @@ __device__ __forceinline__ float bcast(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// Value held by lane (lane ^ J), J in {1, 2, 4, 8, 16}: DPP inside 16-lane
+// rows (xor 1 and 2: quad permutes; xor 4: row shift left or right by 4;
+// xor 8: row rotate by 8), ds_swizzle across the two rows of a 32-lane half
+// (xor 16).
+template <int J>
+__device__ __forceinline__ int lane_xor(int v) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16, "lane_xor");
+    if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (J == 4) {
+        const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // lane i+4
+        const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // lane i-4
+        return (__lane_id() & 4) ? dn : up;
+    } else if constexpr (J == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+    else return __builtin_amdgcn_ds_swizzle(v, 0x401F);
+}
+template <int J>
+__device__ __forceinline__ float lane_xor(float v) {
+    return __int_as_float(lane_xor<J>(__float_as_int(v)));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);

@@ -59,7 +59,7 @@ struct ChunkPlan {
     int ENTA;           // ENT rounded up to 64 (stride of the entry arrays)
     int HT;             // plan hash table size, 0: the slot is its own index
     int ncg;            // d_v / CG
-    int RG;             // lanes per (token, 16-byte piece) in the read reduction
+    int RG;             // lanes per token in the read reduction
     int64_t n_chunks;
     // one (unit, chunk) plan record and its sections (byte offsets)
     size_t rec_bytes, o_ent, o_map, o_wtv, o_ww, o_wa, o_rv, o_rr;
@@ -77,7 +77,8 @@ struct ChunkArgs : ScanArgs {
 
 constexpr size_t kChunkLdsLimit = 160 * 1024;
 
-ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16);
+ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16,
+                       bool state_bf16);
 // Workspace bytes of the chunked path beyond the addresses.
 size_t chunk_workspace_bytes(const ChunkPlan &p);
 hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st);

@@ -248,7 +248,8 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     int *ent_wo = ent_slot + P.ENTA;                          // writes, version-0 row
     int *ent_nw = ent_wo + P.ENTA;
     int *ent_x0 = ent_nw + P.ENTA;
-    int *emap = reinterpret_cast<int *>(rec + P.o_map);
+    int *dwo = reinterpret_cast<int *>(rec + P.o_map);  // resident mode, per slot: write
+    int *dnx = dwo + M;                                 // offset; writes | (version-0 row + 1) << 16
     int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
     float *ww = reinterpret_cast<float *>(rec + P.o_ww);
     float *wa = reinterpret_cast<float *>(rec + P.o_wa);
@@ -338,11 +339,10 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
                 eid = base & 0xffff;
                 const int wo = base >> 16;
                 ewo[eid] = wo;
-                ent_slot[eid] = hashed ? tkey[p] : p;
-                tcf[p] = eid;
+                if (!P.resident) ent_slot[eid] = hashed ? tkey[p] : p;
                 base += 1 + (nw << 16);
             }
-            if (P.resident) emap[p] = eid;
+            tcf[p] = eid;  // -1: untouched
         }
         nt = total & 0xffff;
         nwt = total >> 16;
@@ -404,11 +404,25 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         PlanHdr hd{nt, nver, nwt, 0};
         *reinterpret_cast<PlanHdr *>(rec) = hd;
     }
-    for (int eid = tid; eid < nt; eid += kPT) {
-        const int g = ewo[eid] + eid;
-        ent_wo[eid] = ewo[eid];
-        ent_nw[eid] = ewo[eid + 1] - ewo[eid];
-        ent_x0[eid] = need[g + 1] > need[g] ? need[g] : -1;
+    if (P.resident) {
+        for (int p = tid; p < M; p += kPT) {
+            const int eid = tcf[p];
+            int wo = 0, nx = 0;
+            if (eid >= 0) {
+                const int g = ewo[eid] + eid;
+                wo = ewo[eid];
+                nx = (ewo[eid + 1] - wo) | ((need[g + 1] > need[g] ? need[g] + 1 : 0) << 16);
+            }
+            dwo[p] = wo;
+            dnx[p] = nx;
+        }
+    } else {
+        for (int eid = tid; eid < nt; eid += kPT) {
+            const int g = ewo[eid] + eid;
+            ent_wo[eid] = ewo[eid];
+            ent_nw[eid] = ewo[eid + 1] - ewo[eid];
+            ent_x0[eid] = need[g + 1] > need[g] ? need[g] : -1;
+        }
     }
 #pragma unroll
     for (int j = 0; j < kEPW; ++j) {
@@ -437,18 +451,17 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
 // LDS of the scan kernel (byte offsets).
 struct ScanLds {
-    size_t v, wtv, wwa, rv, rr, ent, ver, total;
+    size_t v, wtv, wwa, rv, rr, ver, total;
 };
 __host__ __device__ inline size_t al256d(size_t x) { return (x + 255) & ~size_t(255); }
-__host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes) {
+__host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes, int ibytes) {
     ScanLds L{};
     size_t o = 0;
-    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (p.CG + 4) * 4);       // values, rows padded by 16 B
+    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (p.CG * ibytes + 16));  // values (input dtype), rows padded by 16 B
     L.wtv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                 // write: token | row
     L.wwa = o; o = al16(o + static_cast<size_t>(p.EV) * 8);                 // write: weight, retention
     L.rv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read: version row
     L.rr = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read weight
-    L.ent = o; o = al16(o + (p.resident ? static_cast<size_t>(p.ENT) * 16 : 0));
     L.ver = o = al256d(o); o = al16(o + static_cast<size_t>(p.EV) * p.CG * sbytes);  // version rows
     L.total = o;
     return L;
@@ -480,12 +493,40 @@ __device__ __forceinline__ void store_row_x(unsigned char *lds, uint32_t a0, con
     }
 }
 
+// Value row t of the chunk (input dtype, rows padded by 16 B) as fp32.
+template <int CG>
+__device__ __forceinline__ void value_row(const float *vbuf, int t, float (&vt)[CG]) {
+    const float4 *r = reinterpret_cast<const float4 *>(vbuf + t * (CG + 4));
+#pragma unroll
+    for (int j = 0; j < CG / 4; ++j) {
+        const float4 f = r[j];
+        vt[4 * j] = f.x;
+        vt[4 * j + 1] = f.y;
+        vt[4 * j + 2] = f.z;
+        vt[4 * j + 3] = f.w;
+    }
+}
+template <int CG>
+__device__ __forceinline__ void value_row(const bf16_t *vbuf, int t, float (&vt)[CG]) {
+    const uint4 *r = reinterpret_cast<const uint4 *>(vbuf + t * (CG + 8));
+#pragma unroll
+    for (int j = 0; j < CG / 8; ++j) {
+        const uint4 u = r[j];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            vt[8 * j + 2 * q] = __uint_as_float(w[q] << 16);
+            vt[8 * j + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+    }
+}
+
 // Applies one touched slot's chunk: version 0 if a read sees it, then the
 // writes in causal order (mass, lambda, row), storing the versions reads see.
-template <typename TS, int CG>
+template <typename TS, int CG, typename TV>
 __device__ __forceinline__ void walk_slot(int wo, int nw, int x0r, float (&x)[CG], float &m,
                                           float eps, const int *wtv, const float2 *wwa,
-                                          const float *vbuf, unsigned char *lds, uint32_t ver_off) {
+                                          const TV *vbuf, unsigned char *lds, uint32_t ver_off) {
     if (x0r >= 0) store_row_x<CG>(lds, row_chunk0<TS, CG>(ver_off, x0r), x, TS{});
     for (int i = 0; i < nw; ++i) {
         const int tv = wtv[wo + i];
@@ -493,16 +534,8 @@ __device__ __forceinline__ void walk_slot(int wo, int nw, int x0r, float (&x)[CG
         const float2 wa = wwa[wo + i];  // weight, retention
         m = fmaf(wa.y, m, wa.x);
         const float lam = wa.x * __builtin_amdgcn_rcpf(m + eps);
-        const float4 *vrow = reinterpret_cast<const float4 *>(vbuf + t * (CG + 4));
         float vt[CG];
-#pragma unroll
-        for (int j = 0; j < CG / 4; ++j) {
-            const float4 f = vrow[j];
-            vt[4 * j] = f.x;
-            vt[4 * j + 1] = f.y;
-            vt[4 * j + 2] = f.z;
-            vt[4 * j + 3] = f.w;
-        }
+        value_row<CG>(vbuf, t, vt);
 #pragma unroll
         for (int c = 0; c < CG; ++c) x[c] = stored<TS>(fmaf(lam, vt[c] - x[c], x[c]));
         if (vr >= 0) store_row_x<CG>(lds, row_chunk0<TS, CG>(ver_off, vr), x, TS{});
@@ -538,14 +571,14 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     const int M = static_cast<int>(a.M);
     const int K = a.K, C = P.C, d_v = a.d_v, EV = P.EV;
     const int nchunks = static_cast<int>(P.n_chunks);
-    const ScanLds L = scan_lds(P, a.M, sizeof(TS));
-    float *vbuf = reinterpret_cast<float *>(smem + L.v);
+    const ScanLds L = scan_lds(P, a.M, sizeof(TS), sizeof(TIn));
+    TIn *vbuf = reinterpret_cast<TIn *>(smem + L.v);
+    constexpr int VROW = CG + 16 / static_cast<int>(sizeof(TIn));  // padded value row
     int *s_wtv = reinterpret_cast<int *>(smem + L.wtv);
     float2 *s_wwa = reinterpret_cast<float2 *>(smem + L.wwa);
     const uint32_t ver_off = static_cast<uint32_t>(L.ver);
     int *s_rv = reinterpret_cast<int *>(smem + L.rv);
     float *s_rr = reinterpret_cast<float *>(smem + L.rr);
-    int4 *s_ent = reinterpret_cast<int4 *>(smem + L.ent);
     TS *ver = reinterpret_cast<TS *>(smem + L.ver);
 
     const TIn *v = static_cast<const TIn *>(a.v);
@@ -574,8 +607,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     int pf_wtv[kEVT], pf_rv[kEVT];
     float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT];
     TIn pf_v[VPT];  // raw: converting at load time would wait for each load
-    int4 pf_ent = make_int4(0, 0, 0, -1);  // write offset, writes, version-0 row
-    int pf_map = -1, pf_nt = 0;
+    int pf_dwo = 0, pf_dnx = 0, pf_nt = 0;  // resident: this slot's write offset, writes | x0
     auto prefetch = [&](int c) {
         const unsigned char *rec = plan0 + static_cast<int64_t>(c) * P.rec_bytes;
         const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
@@ -584,7 +616,6 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const float *wa = reinterpret_cast<const float *>(rec + P.o_wa);
         const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
         const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
-        const int *ent_wo = reinterpret_cast<const int *>(rec + P.o_ent) + P.ENTA;
         pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
         // every load is independent of every other (no wait on the header):
         // the write list is read to its capacity, entries past its end are
@@ -609,8 +640,10 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
             pf_v[j] = v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + cc];
         }
         if constexpr (RES) {
-            if (tid < M) pf_map = reinterpret_cast<const int *>(rec + P.o_map)[tid];
-            if (tid < P.ENT) pf_ent = make_int4(ent_wo[tid], ent_wo[P.ENTA + tid], ent_wo[2 * P.ENTA + tid], 0);
+            if (tid < M) {
+                pf_dwo = reinterpret_cast<const int *>(rec + P.o_map)[tid];
+                pf_dnx = reinterpret_cast<const int *>(rec + P.o_map)[M + tid];
+            }
         }
     };
 
@@ -648,21 +681,17 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int i = tid + j * kNT;
-            if (i < Cc * CG) vbuf[(i / CG) * (CG + 4) + i % CG] = to_f32(pf_v[j]);
+            if (i < Cc * CG) vbuf[(i / CG) * VROW + i % CG] = pf_v[j];
         }
-        const int my_e = pf_map, nt = pf_nt;
-        if constexpr (RES) {
-            if (tid < P.ENT) s_ent[tid] = pf_ent;
-        }
+        const int my_wo = pf_dwo, my_nx = pf_dnx, nt = pf_nt;
         lds_barrier();
         // ---- 2. the next chunk's loads go out now and land during the walk
         if (c + 1 < nchunks) prefetch(c + 1);
         // ---- 3. walk the touched slots
         if constexpr (RES) {
-            if (tid < M && my_e >= 0) {
-                const int4 en = s_ent[my_e];
-                walk_slot<TS, CG>(en.x, en.y, en.z, x, m, a.eps_gsu, s_wtv, s_wwa, vbuf, smem, ver_off);
-            }
+            if (tid < M && my_nx != 0)
+                walk_slot<TS, CG>(my_wo, my_nx & 0xffff, (my_nx >> 16) - 1, x, m, a.eps_gsu, s_wtv, s_wwa, vbuf,
+                                  smem, ver_off);
         } else {
             // touched rows from HBM, EB at a time (entries already in
             // registers): rows and masses, then the walks and write-backs
@@ -710,51 +739,62 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         // threads that gather the next chunk's rows
         if constexpr (RES) lds_barrier(); else __syncthreads();
         if (c + 1 < nchunks) prefetch_ent(c + 1);  // lands during the reduction
-        // ---- 4. reads: r = sum_k rho_k * version_k for one 16-byte piece of
-        //         the slice; G = P.RG lanes share a (token, piece), lane g
-        //         taking reads k = g, g + G, ... in order, combined by a
-        //         butterfly (a fixed order); r and the sum of squares over the
-        //         slice go to global memory
+        // ---- 4. reads: r = sum_k rho_k * version_k over the slice; G = P.RG
+        //         lanes share a token, lane g taking reads k = g, g + G, ...
+        //         in order (whole rows), combined by a butterfly (a fixed
+        //         order, the same bits in every lane); r and the slice's sum
+        //         of squares go to global memory
         {
-            constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per piece
+            constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
             constexpr int NCH = CG / EPC;                            // pieces per row
             const int G = P.RG;
-            const int nitems = Cc * NCH * G;  // whole groups and tokens per wave
-            for (int i = tid; i < nitems; i += kNT) {
-                const int g = i % G, item = i / G;
-                const int t = item / NCH, j = item % NCH;
-                float r[EPC];
+            for (int i = tid; i < Cc * G; i += kNT) {
+                const int g = i % G, t = i / G;
+                float r[CG];
 #pragma unroll
-                for (int cc = 0; cc < EPC; ++cc) r[cc] = 0.f;
+                for (int cc = 0; cc < CG; ++cc) r[cc] = 0.f;
                 for (int k = g; k < K; k += G) {
                     // skipped reads have no row; a zero weight adds nothing
                     const int row = t * K + k;
                     const int vr = s_rv[row];
                     const float rw = s_rr[row];
                     if (vr >= 0 && rw != 0.f) {
-                        const uint4 u = reinterpret_cast<const uint4 *>(ver + vr * CG)[j ^ row_swz<TS, CG>(vr)];
-                        float sv[EPC];
-                        unpack_chunk(u, sv);
+                        const uint32_t a0 = row_chunk0<TS, CG>(ver_off, vr);
 #pragma unroll
-                        for (int cc = 0; cc < EPC; ++cc) r[cc] = fmaf(rw, sv[cc], r[cc]);
+                        for (int j = 0; j < NCH; ++j) {
+                            const uint4 u = *reinterpret_cast<const uint4 *>(smem + (a0 ^ (j << 4)));
+                            float sv[EPC];
+                            unpack_chunk(u, sv);
+#pragma unroll
+                            for (int cc = 0; cc < EPC; ++cc) r[j * EPC + cc] = fmaf(rw, sv[cc], r[j * EPC + cc]);
+                        }
                     }
                 }
-                for (int off = 1; off < G; off <<= 1) {
 #pragma unroll
-                    for (int cc = 0; cc < EPC; ++cc) r[cc] += __shfl_xor(r[cc], off, kWave);
+                for (int cc = 0; cc < CG; ++cc) {
+                    if (G > 1) r[cc] += lane_xor<1>(r[cc]);
+                    if (G > 2) r[cc] += lane_xor<2>(r[cc]);
+                    if (G > 4) r[cc] += lane_xor<4>(r[cc]);
+                    if (G > 8) r[cc] += lane_xor<8>(r[cc]);
                 }
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
-                if (g == 0) {
-                    float *dst = a.rbuf + th * d_v + cg * CG + j * EPC;
+                float *dst = a.rbuf + th * d_v + cg * CG;
 #pragma unroll
-                    for (int cc = 0; cc < EPC; cc += 4)
-                        *reinterpret_cast<float4 *>(dst + cc) = make_float4(r[cc], r[cc + 1], r[cc + 2], r[cc + 3]);
+                for (int j = 0; j < NCH; ++j) {
+                    if (j % G == g) {
+#pragma unroll
+                        for (int cc = 0; cc < EPC; cc += 4)
+                            *reinterpret_cast<float4 *>(dst + j * EPC + cc) =
+                                make_float4(r[j * EPC + cc], r[j * EPC + cc + 1], r[j * EPC + cc + 2],
+                                            r[j * EPC + cc + 3]);
+                    }
                 }
-                float ss = 0.f;
+                if (g == 0) {
+                    float ss = 0.f;
 #pragma unroll
-                for (int cc = 0; cc < EPC; ++cc) ss = fmaf(r[cc], r[cc], ss);
-                for (int off = G; off < NCH * G; off <<= 1) ss += __shfl_xor(ss, off, kWave);
-                if (g == 0 && j == 0) a.sumsq[th * ncg + cg] = ss;
+                    for (int cc = 0; cc < CG; ++cc) ss = fmaf(r[cc], r[cc], ss);
+                    a.sumsq[th * ncg + cg] = ss;
+                }
             }
         }
         (void)nev;
@@ -873,7 +913,7 @@ hipError_t launch_cg(const ChunkArgs &a, hipStream_t st) {
 
 }  // namespace
 
-ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16) {
+ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16, bool state_bf16) {
     ChunkPlan p{};
     p.ok = false;
     const int sbytes = state_bf16 ? 2 : 4;
@@ -905,22 +945,21 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool stat
                 q.HT = ht;
             }
             q.ncg = d_v / CG;
-            // lanes per (token, 16-byte piece) in the read reduction: enough
-            // to keep the workgroup busy, one group per wave at most
+            // lanes per token in the read reduction: enough to keep the
+            // workgroup busy, within one 16-lane row
             {
-                const int nch = CG * sbytes / 16;
                 int g = 1;
-                while (g < 16 && g < K && static_cast<int64_t>(C) * nch * g * 2 <= kNT) g *= 2;
+                while (g < 16 && g < K && static_cast<int64_t>(C) * g * 2 <= kNT) g *= 2;
                 q.RG = g;
             }
             q.lds_plan = plan_lds(q, M).total;
-            q.lds_scan = scan_lds(q, M, sbytes).total;
+            q.lds_scan = scan_lds(q, M, sbytes, in_bf16 ? 2 : 4).total;
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
             q.n_chunks = (T + C - 1) / C;
             size_t o = 256;  // header
             q.ENTA = (q.ENT + 63) & ~63;
-            q.o_ent = o; o += al256(static_cast<size_t>(q.ENTA) * 16);
-            q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 4 : 0);
+            q.o_ent = o; o += al256(q.resident ? 0 : static_cast<size_t>(q.ENTA) * 16);
+            q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 8 : 0);
             q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_wa = o; o += al256(static_cast<size_t>(EV) * 4);

@@ -70,25 +70,16 @@ __device__ __forceinline__ bool better(const Ent &a, const Ent &b) {
     return gt | (eq & lt);
 }
 
-// Value of lane (r ^ J) within groups of KP lanes, by DPP inside 16-lane
-// rows (xor 1 and 2: quad permutes; xor 4: row shift left or right by 4;
-// xor 8: row rotate by 8) and ds_swizzle across the two rows of a 32-lane
-// group (xor 16).  J == KP - 1 reverses the group (row mirrors).
+// Value of lane (r ^ J) within groups of KP lanes (lane_xor), or, for
+// J == KP - 1, of the mirrored lane (row mirrors, plus the xor-16 swizzle
+// for 32-lane groups).
 template <int KP, int J>
 __device__ __forceinline__ int xchg(int v) {
-    if constexpr (J == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-    else if constexpr (J == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-    else if constexpr (J == 4) {
-        const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // lane i+4
-        const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // lane i-4
-        return (__lane_id() & 4) ? dn : up;
-    } else if constexpr (J == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
-    else if constexpr (J == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);
-    else if constexpr (J == 7 && KP == 8) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    if constexpr (J == 7 && KP == 8) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
     else if constexpr (J == 15 && KP == 16) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
     else if constexpr (J == 31 && KP == 32)
-        return __builtin_amdgcn_ds_swizzle(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false), 0x401F);
-    else return __shfl_xor(v, J, kWave);
+        return lane_xor<16>(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+    else return lane_xor<J>(v);
 }
 
 template <int KP, int J>
