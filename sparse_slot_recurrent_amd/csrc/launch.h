@@ -60,6 +60,7 @@ struct ChunkPlan {
     int HT;             // plan hash table size, 0: the slot is its own index
     int ncg;            // d_v / CG
     int RG;             // lanes per token in the read reduction
+    bool raw_values;    // values kept in LDS as the bf16 input (else fp32)
     int64_t n_chunks;
     // one (unit, chunk) plan record and its sections (byte offsets)
     size_t rec_bytes, o_ent, o_map, o_wtv, o_ww, o_wa, o_rv, o_rr;

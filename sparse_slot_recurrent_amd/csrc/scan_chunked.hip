@@ -40,6 +40,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace ramnet {
 namespace {
@@ -454,10 +455,10 @@ struct ScanLds {
     size_t v, wtv, wwa, rv, rr, ver, total;
 };
 __host__ __device__ inline size_t al256d(size_t x) { return (x + 255) & ~size_t(255); }
-__host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes, int ibytes) {
+__host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes, int vbytes) {
     ScanLds L{};
     size_t o = 0;
-    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (p.CG * ibytes + 16));  // values (input dtype), rows padded by 16 B
+    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (p.CG * vbytes + 16));  // values, rows padded by 16 B
     L.wtv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                 // write: token | row
     L.wwa = o; o = al16(o + static_cast<size_t>(p.EV) * 8);                 // write: weight, retention
     L.rv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read: version row
@@ -493,7 +494,7 @@ __device__ __forceinline__ void store_row_x(unsigned char *lds, uint32_t a0, con
     }
 }
 
-// Value row t of the chunk (input dtype, rows padded by 16 B) as fp32.
+// Value row t of the chunk (fp32 or bf16 in LDS, rows padded by 16 B), as fp32.
 template <int CG>
 __device__ __forceinline__ void value_row(const float *vbuf, int t, float (&vt)[CG]) {
     const float4 *r = reinterpret_cast<const float4 *>(vbuf + t * (CG + 4));
@@ -548,7 +549,10 @@ struct HRow {
     TS e[CG];
 };
 
-template <typename TIn, typename TS, int CG, bool RES>
+// VT: the value rows' type in LDS: fp32 (converted once at staging), or the
+// bf16 input itself (half the LDS, which buys a longer chunk, at a
+// conversion per write); the planner picks per configuration.
+template <typename TIn, typename TS, int CG, bool RES, typename VT>
 __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
@@ -571,9 +575,9 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     const int M = static_cast<int>(a.M);
     const int K = a.K, C = P.C, d_v = a.d_v, EV = P.EV;
     const int nchunks = static_cast<int>(P.n_chunks);
-    const ScanLds L = scan_lds(P, a.M, sizeof(TS), sizeof(TIn));
-    TIn *vbuf = reinterpret_cast<TIn *>(smem + L.v);
-    constexpr int VROW = CG + 16 / static_cast<int>(sizeof(TIn));  // padded value row
+    const ScanLds L = scan_lds(P, a.M, sizeof(TS), sizeof(VT));
+    VT *vbuf = reinterpret_cast<VT *>(smem + L.v);
+    constexpr int VROW = CG + 16 / static_cast<int>(sizeof(VT));  // padded value row
     int *s_wtv = reinterpret_cast<int *>(smem + L.wtv);
     float2 *s_wwa = reinterpret_cast<float2 *>(smem + L.wwa);
     const uint32_t ver_off = static_cast<uint32_t>(L.ver);
@@ -681,7 +685,10 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int i = tid + j * kNT;
-            if (i < Cc * CG) vbuf[(i / CG) * VROW + i % CG] = pf_v[j];
+            if (i < Cc * CG) {
+                if constexpr (std::is_same_v<VT, TIn>) vbuf[(i / CG) * VROW + i % CG] = pf_v[j];
+                else vbuf[(i / CG) * VROW + i % CG] = to_f32(pf_v[j]);
+            }
         }
         const int my_wo = pf_dwo, my_nx = pf_dnx, nt = pf_nt;
         lds_barrier();
@@ -886,7 +893,9 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    auto sk = P.resident ? scan_kernel<TIn, TS, CG, true> : scan_kernel<TIn, TS, CG, false>;
+    using VB = std::conditional_t<std::is_same_v<TIn, bf16_t>, bf16_t, float>;
+    auto sk = P.resident ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB> : scan_kernel<TIn, TS, CG, true, float>)
+                         : (P.raw_values ? scan_kernel<TIn, TS, CG, false, VB> : scan_kernel<TIn, TS, CG, false, float>);
     e = set_lds(sk, P.lds_scan);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * P.ncg)), dim3(kNT), P.lds_scan, st, a);
@@ -913,7 +922,8 @@ hipError_t launch_cg(const ChunkArgs &a, hipStream_t st) {
 
 }  // namespace
 
-ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16, bool state_bf16) {
+namespace {
+ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_bf16, int vbytes) {
     ChunkPlan p{};
     p.ok = false;
     const int sbytes = state_bf16 ? 2 : 4;
@@ -953,7 +963,8 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_b
                 q.RG = g;
             }
             q.lds_plan = plan_lds(q, M).total;
-            q.lds_scan = scan_lds(q, M, sbytes, in_bf16 ? 2 : 4).total;
+            q.lds_scan = scan_lds(q, M, sbytes, vbytes).total;
+            q.raw_values = vbytes == 2;
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
             q.n_chunks = (T + C - 1) / C;
             size_t o = 256;  // header
@@ -976,6 +987,15 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_b
         }
     }
     return p;
+}
+
+}  // namespace
+
+ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16, bool state_bf16) {
+    const ChunkPlan f = plan_with(M, K, d_v, B, T, H, state_bf16, 4);
+    if (!in_bf16) return f;
+    const ChunkPlan r = plan_with(M, K, d_v, B, T, H, state_bf16, 2);
+    return (r.ok && (!f.ok || r.C > f.C)) ? r : f;
 }
 
 size_t chunk_workspace_bytes(const ChunkPlan &p) {
