@@ -60,6 +60,48 @@ def byte_model(w, kind: str):
     return out
 
 
+STAGE_KERNELS = {
+    "decode_addresses": ("decode_kernel",),
+    "scan_stage": ("plan_kernel", "mass_fanout_kernel", "scan_kernel", "rms_gate_kernel"),
+    "step_fused": ("step_fused_kernel",),
+}
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources, to tell whether measured counters
+    still describe the kernels being run."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    here = os.path.dirname(os.path.abspath(__file__))
+    for path in sorted(glob.glob(os.path.join(here, "sparse_slot_recurrent_amd", "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of a stage from rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (scaled by a device copy of known size), recorded in
+    profiles/hbm_traffic.json; None when absent or when the kernel sources
+    changed since the counters were taken."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("_kernel_source_sha256") != kernel_source_hash() or workload not in rec:
+        return None
+    total, found = 0.0, False
+    for name, v in rec[workload]["kernels"].items():
+        if name.split("<")[0] in STAGE_KERNELS.get(stage, ()):
+            total += v["fetch_bytes"] + v["write_bytes"]
+            found = True
+    return total if found else None
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -318,7 +360,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, dom)},
         "kernels_ms": kms,
         "algorithmic_bytes": bm,
         "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
