@@ -42,15 +42,15 @@ def load():
         build()
     lib = C.CDLL(LIB)
     P = C.c_void_p
-    i32, i64, f64 = C.c_int, C.c_long, C.c_double
+    i32, i64, f64, u64 = C.c_int, C.c_long, C.c_double, C.c_uint64
     lib.oracle_slot_weights.argtypes = [P, i32, i32, P]
     lib.oracle_digit_probs.argtypes = [P, i32, i32, P, P]
     lib.oracle_decode_one.argtypes = [P, i32, i32, i32, i32, i32, i64, P, P,
                                       P, P, P]
     lib.oracle_decode_all.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
-                                      P, P, P, P, P, i32]
-    lib.oracle_cape.argtypes = [P, i64, i64, i32, i32, P]
-    lib.oracle_layer.argtypes = ([i32] * 7 + [i32, i32, f64, f64, i32]
+                                      u64, P, P, P, P, P, i32]
+    lib.oracle_cape.argtypes = [P, i64, i64, i32, i32, i32, P]
+    lib.oracle_layer.argtypes = ([i32] * 7 + [i32, i32, u64, f64, f64, i32]
                                  + [P] * 16 + [i32])
     lib.oracle_scan_given.argtypes = ([i32] * 7 + [i32, f64, f64]
                                       + [P] * 11 + [i32])
@@ -120,8 +120,10 @@ def decode_one(logits: np.ndarray, U: int, d_p: int, K: int,
 
 def decode_all(logits: np.ndarray, U: int, d_p: int, K: int, cape: int = 1,
                pos0: Optional[np.ndarray] = None, mode: int = TOPK_BRUTE,
-               nthreads: int = 0):
-    """Addresses of a [B,T,H,U*d_p] logit tensor: idx, wt [B,T,H,K], gap."""
+               nthreads: int = 0, content_heads: int = 0):
+    """Addresses of a [B,T,H,U*d_p] logit tensor: idx, wt [B,T,H,K], gap.
+    cape: 0 content-only, 1/2/3 CAPE form A/B/C; heads whose bit is set in
+    content_heads (bit 63 for heads >= 63) are content-only."""
     lg = _f32(logits)
     B, T, H, L = lg.shape
     assert L == U * d_p
@@ -129,16 +131,18 @@ def decode_all(logits: np.ndarray, U: int, d_p: int, K: int, cape: int = 1,
     wt = np.empty((B, T, H, K), np.float64)
     gap = np.empty((B, T, H), np.float64)
     p0 = None if pos0 is None else np.ascontiguousarray(pos0, dtype=np.int32)
-    _check(load().oracle_decode_all(B, T, H, U, d_p, K, mode, cape, _p(p0),
+    _check(load().oracle_decode_all(B, T, H, U, d_p, K, mode, cape,
+                                    int(content_heads), _p(p0),
                                     _p(lg), _p(idx), _p(wt), _p(gap),
                                     nthreads), "decode_all")
     return idx, wt, gap
 
 
-def cape(idx: np.ndarray, pos: int, U: int, d_p: int) -> np.ndarray:
+def cape(idx: np.ndarray, pos: int, U: int, d_p: int, form: int = 1) -> np.ndarray:
+    """Slots moved by CAPE form 1 (A), 2 (B) or 3 (C) at position pos."""
     a = np.ascontiguousarray(idx, dtype=np.int32)
     out = np.empty_like(a)
-    _check(load().oracle_cape(_p(a), a.size, int(pos), U, d_p, _p(out)), "cape")
+    _check(load().oracle_cape(_p(a), a.size, int(pos), U, d_p, form, _p(out)), "cape")
     return out
 
 
@@ -146,7 +150,7 @@ def layer(q, k, v, gamma, g, S, mass, *, d_p: int, U: int, K: int,
           state_bf16: bool, cape: int = 1, eps_gsu: float = 1e-6,
           eps_norm: float = 1e-6, norm_w=None, pos0=None,
           mode: int = TOPK_BRUTE, want_addresses: bool = True,
-          nthreads: int = 0):
+          nthreads: int = 0, content_heads: int = 0):
     """Runs the layer over [B,T,H].  S [B,H,M,d_v] and mass [B,H,M] are
     float32 arrays updated IN PLACE (their values must be representable in
     the storage dtype).  Returns dict(out, w_idx, w_wt, r_idx, r_wt, w_gap,
@@ -172,7 +176,7 @@ def layer(q, k, v, gamma, g, S, mass, *, d_p: int, U: int, K: int,
     nw = None if norm_w is None else _f32(norm_w)
     p0 = None if pos0 is None else np.ascontiguousarray(pos0, dtype=np.int32)
     rc = load().oracle_layer(
-        B, T, H, d_p, U, K, d_v, int(state_bf16), int(cape), eps_gsu,
+        B, T, H, d_p, U, K, d_v, int(state_bf16), int(cape), int(content_heads), eps_gsu,
         eps_norm, mode, _p(q), _p(k), _p(v), _p(gamma), _p(g), _p(nw), _p(p0),
         _p(S), _p(mass), _p(out), _p(res.get("w_idx")), _p(res.get("w_wt")),
         _p(res.get("r_idx")), _p(res.get("r_wt")), _p(res.get("w_gap")),

@@ -244,23 +244,43 @@ static int topk_tree(const double *probs, int U, int d_p, int K, int32_t *idx,
 /* CAPE                                                               */
 /* ------------------------------------------------------------------ */
 
-/* Move slot i by token position P: every digit advances by (P mod d_p),
- * wrapping within its d_p values.  This is a permutation of the M slots. */
-static long cape_move(long i, long P, int U, int d_p) {
-    long s = ((P % d_p) + d_p) % d_p;
-    if (s == 0) return i;
+/* Move slot i by token position P (project page, CAPE: addresses shift
+ * cyclically along the slot array with the position).  The pages leave the
+ * exact shift open; three readings, each a permutation of the M slots:
+ *   form 1 (A): every digit advances by (P mod d_p), wrapping within its d_p
+ *               values;
+ *   form 2 (B): digit u advances by digit u of P written in base d_p (most
+ *               significant first, U digits), each wrapping on its own (no
+ *               carry);
+ *   form 3 (C): the slot index advances by P, wrapping over all M slots. */
+static long cape_move(long i, long P, int U, int d_p, int form) {
+    const long M = ipow_l(d_p, U);
+    if (form == 3) return (long)((((unsigned long)i + (unsigned long)(((P % M) + M) % M))) % (unsigned long)M);
     long j = 0;
     for (int u = 0; u < U; u++) {
         long a = digit_of(i, u, U, d_p);
+        long s;
+        if (form == 2)
+            s = digit_of(((P % M) + M) % M, u, U, d_p);
+        else
+            s = ((P % d_p) + d_p) % d_p;
         j = j * d_p + (a + s) % d_p;
     }
     return j;
 }
 
-int oracle_cape(const int32_t *idx, long n, long P, int U, int d_p,
+int oracle_cape(const int32_t *idx, long n, long P, int U, int d_p, int form,
                 int32_t *out) {
-    for (long j = 0; j < n; j++) out[j] = (int32_t)cape_move(idx[j], P, U, d_p);
+    if (form < 1 || form > 3) return -1;
+    for (long j = 0; j < n; j++) out[j] = (int32_t)cape_move(idx[j], P, U, d_p, form);
     return 0;
+}
+
+/* CAPE form a head uses: 0 (content-only) when its bit of content_heads is
+ * set (heads 63 and above share bit 63), else `cape`. */
+static int head_cape(int cape, uint64_t content_heads, long h) {
+    const int bit = h < 63 ? (int)h : 63;
+    return ((content_heads >> bit) & 1u) ? 0 : cape;
 }
 
 /* ------------------------------------------------------------------ */
@@ -285,14 +305,14 @@ static int decode_one(const float *logits, int U, int d_p, int K, int mode,
     }
     if (rc) return rc;
     if (cape)
-        for (int j = 0; j < K; j++) idx[j] = (int32_t)cape_move(idx[j], P, U, d_p);
+        for (int j = 0; j < K; j++) idx[j] = (int32_t)cape_move(idx[j], P, U, d_p, cape);
     return 0;
 }
 
 int oracle_decode_one(const float *logits, int U, int d_p, int K, int mode,
                       int cape, long P, int32_t *idx, double *wt, double *gap,
                       long *n_exp, long *cand_per_level) {
-    if (U < 1 || d_p < 2 || K < 1 || K > ipow_l(d_p, U)) return -1;
+    if (U < 1 || d_p < 2 || K < 1 || K > ipow_l(d_p, U) || cape < 0 || cape > 3) return -1;
     double *probs = (double *)malloc(sizeof(double) * U * d_p);
     if (!probs) return -2;
     int rc = decode_one(logits, U, d_p, K, mode, cape, P, probs, idx, wt, gap,
@@ -304,10 +324,13 @@ int oracle_decode_one(const float *logits, int U, int d_p, int K, int mode,
 /* Decodes every address of a [B,T,H,U*d_p] logit tensor at positions
  * pos0[b] + t (pos0 NULL means 0).  idx/wt are [B,T,H,K], gap [B,T,H]. */
 int oracle_decode_all(int B, int T, int H, int U, int d_p, int K, int mode,
-                      int cape, const int32_t *pos0, const float *logits,
-                      int32_t *idx, double *wt, double *gap, int nthreads) {
+                      int cape, uint64_t content_heads, const int32_t *pos0,
+                      const float *logits, int32_t *idx, double *wt,
+                      double *gap, int nthreads) {
     long M = ipow_l(d_p, U);
-    if (B < 0 || T < 0 || H < 0 || U < 1 || d_p < 2 || K < 1 || K > M) return -1;
+    if (B < 0 || T < 0 || H < 0 || U < 1 || d_p < 2 || K < 1 || K > M || cape < 0 ||
+        cape > 3)
+        return -1;
     long n = (long)B * T * H;
     int L = U * d_p;
     int rc_all = 0;
@@ -324,7 +347,8 @@ int oracle_decode_all(int B, int T, int H, int U, int d_p, int K, int mode,
             long b = a / ((long)T * H);
             long t = (a / H) % T;
             long P = (pos0 ? pos0[b] : 0) + t;
-            int rc = decode_one(logits + a * L, U, d_p, K, mode, cape, P, probs,
+            int rc = decode_one(logits + a * L, U, d_p, K, mode,
+                                head_cape(cape, content_heads, a % H), P, probs,
                                 idx + a * K, wt + a * K, gap ? gap + a : NULL,
                                 NULL, NULL);
             if (rc) rc_all = rc;
@@ -463,7 +487,7 @@ static int check_cfg(int B, int T, int H, int d_p, int U, int K, int d_v) {
 
 /* Shared driver: units (b, h) are independent and run in parallel. */
 static int layer_driver(int B, int T, int H, int d_p, int U, int K, int d_v,
-                        int state_bf16, int cape, double eps_gsu,
+                        int state_bf16, int cape, uint64_t content_heads, double eps_gsu,
                         double eps_norm, int topk_mode,
                         const float *q, const float *k,
                         const int32_t *gw_idx, const double *gw_wt,
@@ -473,7 +497,7 @@ static int layer_driver(int B, int T, int H, int d_p, int U, int K, int d_v,
                         float *mass, float *out, int32_t *w_idx, double *w_wt,
                         int32_t *r_idx, double *r_wt, double *w_gap,
                         double *r_gap, int nthreads) {
-    if (check_cfg(B, T, H, d_p, U, K, d_v)) return -1;
+    if (check_cfg(B, T, H, d_p, U, K, d_v) || cape < 0 || cape > 3) return -1;
     layer_cfg c;
     memset(&c, 0, sizeof c);
     c.T = T; c.H = H; c.U = U; c.d_p = d_p; c.K = K; c.d_v = d_v;
@@ -491,7 +515,9 @@ static int layer_driver(int B, int T, int H, int d_p, int U, int K, int d_v,
         const long b = uidx / H, h = uidx % H;
         const long o = b * T * H + h;             /* first token-head of unit */
         const long P0 = pos0 ? pos0[b] : 0;
-        int rc = run_unit(&c, P0,
+        layer_cfg cu = c;
+        cu.cape = head_cape(cape, content_heads, h);
+        int rc = run_unit(&cu, P0,
                           q ? q + o * L : NULL, k ? k + o * L : NULL,
                           gw_idx ? gw_idx + o * K : NULL,
                           gw_wt ? gw_wt + o * K : NULL,
@@ -520,15 +546,16 @@ static int layer_driver(int B, int T, int H, int d_p, int U, int K, int d_v,
  *   [B,T,H] (brute mode only).
  * Returns 0, or a negative code for bad sizes / allocation failure. */
 int oracle_layer(int B, int T, int H, int d_p, int U, int K, int d_v,
-                 int state_bf16, int cape, double eps_gsu, double eps_norm,
+                 int state_bf16, int cape, uint64_t content_heads,
+                 double eps_gsu, double eps_norm,
                  int topk_mode, const float *q, const float *k, const float *v,
                  const float *gamma, const float *g, const float *norm_w,
                  const int32_t *pos0, float *S, float *mass, float *out,
                  int32_t *w_idx, double *w_wt, int32_t *r_idx, double *r_wt,
                  double *w_gap, double *r_gap, int nthreads) {
     if (!q || !k) return -1;
-    return layer_driver(B, T, H, d_p, U, K, d_v, state_bf16, cape, eps_gsu,
-                        eps_norm, topk_mode, q, k, NULL, NULL, NULL, NULL, v,
+    return layer_driver(B, T, H, d_p, U, K, d_v, state_bf16, cape, content_heads,
+                        eps_gsu, eps_norm, topk_mode, q, k, NULL, NULL, NULL, NULL, v,
                         gamma, g, norm_w, pos0, S, mass, out, w_idx, w_wt,
                         r_idx, r_wt, w_gap, r_gap, nthreads);
 }
@@ -549,7 +576,7 @@ int oracle_scan_given(int B, int T, int H, int d_p, int U, int K, int d_v,
     for (long j = 0; j < n; j++)
         if (w_idx[j] < 0 || w_idx[j] >= M || r_idx[j] < 0 || r_idx[j] >= M)
             return -1;
-    return layer_driver(B, T, H, d_p, U, K, d_v, state_bf16, 0, eps_gsu,
+    return layer_driver(B, T, H, d_p, U, K, d_v, state_bf16, 0, 0, eps_gsu,
                         eps_norm, TOPK_BRUTE, NULL, NULL, w_idx, w_wt, r_idx,
                         r_wt, v, gamma, g, norm_w, NULL, S, mass, out, NULL,
                         NULL, NULL, NULL, NULL, NULL, nthreads);

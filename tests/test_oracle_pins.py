@@ -304,6 +304,69 @@ def test_cape_keeps_weights_and_distinctness(orc):
         assert np.array_equal(i1, orc.cape(i0, P, 5, 4))
 
 
+# CAPE readings B (digit-wise shift by the position's own digits, no carry)
+# and C (rotation of the whole slot array by the position): project page,
+# CAPE, where the exact shift is left open.
+
+def test_cape_forms_b_c_are_permutations(orc):
+    for d_p, U in [(4, 5), (3, 4), (5, 2), (2, 7)]:
+        M = d_p ** U
+        idx = np.arange(M, dtype=np.int32)
+        for form in (2, 3):
+            for P in (1, 2, d_p, d_p + 1, M - 1, M + 3, 12345):
+                out = orc.cape(idx, P, U, d_p, form)
+                assert np.array_equal(np.sort(out), idx), (form, P)
+
+
+def test_cape_form_c_rotates_the_slot_array(orc):
+    for d_p, U in [(4, 5), (3, 3)]:
+        M = d_p ** U
+        idx = np.arange(M, dtype=np.int32)
+        one = orc.cape(idx, 1, U, d_p, 3)
+        assert one[M - 1] == 0 and np.array_equal(one[:-1], idx[1:])  # wraps once
+        assert np.array_equal(orc.cape(idx, M, U, d_p, 3), idx)       # full turn
+        assert np.array_equal(orc.cape(idx, 2 * M + 5, U, d_p, 3), orc.cape(idx, 5, U, d_p, 3))
+        for P, Q in [(1, 1), (7, M - 3), (M - 1, M - 1)]:
+            assert np.array_equal(orc.cape(orc.cape(idx, P, U, d_p, 3), Q, U, d_p, 3),
+                                  orc.cape(idx, P + Q, U, d_p, 3))
+
+
+def test_cape_form_b_moves_each_digit_by_its_own_position_digit(orc):
+    d_p, U = 4, 5
+    M = d_p ** U
+    idx = np.arange(M, dtype=np.int32)
+    # a position below d_p moves only the last (least significant) digit
+    for P in range(1, d_p):
+        out = orc.cape(idx, P, U, d_p, 2)
+        assert np.array_equal(out // d_p, idx // d_p)
+        assert np.array_equal(out % d_p, (idx % d_p + P) % d_p)
+    # a position a * d_p^(U-1) moves only the first digit, and such moves add
+    top = d_p ** (U - 1)
+    for a in range(1, d_p):
+        out = orc.cape(idx, a * top, U, d_p, 2)
+        assert np.array_equal(out % top, idx % top)
+        assert np.array_equal(out // top, (idx // top + a) % d_p)
+        for b in range(d_p):
+            assert np.array_equal(orc.cape(out, b * top, U, d_p, 2),
+                                  orc.cape(idx, ((a + b) % d_p) * top, U, d_p, 2))
+    # all position digits equal to s: every digit moves by s, which is form A
+    # at a position congruent to s
+    rep1 = sum(d_p ** u for u in range(U))
+    for s_ in range(d_p):
+        assert np.array_equal(orc.cape(idx, s_ * rep1, U, d_p, 2), orc.cape(idx, s_, U, d_p, 1))
+
+
+def test_cape_forms_agree_with_one_digit(orc):
+    """U = 1: every reading is the same cyclic shift of d_p slots."""
+    for d_p in (2, 5, 8):
+        idx = np.arange(d_p, dtype=np.int32)
+        for P in range(3 * d_p):
+            a = orc.cape(idx, P, 1, d_p, 1)
+            assert np.array_equal(a, (idx + P) % d_p)
+            assert np.array_equal(orc.cape(idx, P, 1, d_p, 2), a)
+            assert np.array_equal(orc.cape(idx, P, 1, d_p, 3), a)
+
+
 # ---------------------------------------------------------------- layer helpers
 
 def _small_inputs(seed, B, T, H, U, d_p, d_v, sigma=1.5, bf16=False):
@@ -574,6 +637,51 @@ def test_cape_off_equals_positions_multiple_of_dp(orc):
     r2 = _run(orc, x, S2, m2, d_p=d_p, U=U, K=K, state_bf16=False, cape=1,
               pos0=np.array([0, 4, 400], np.int32))
     assert np.array_equal(r1["out"], r2["out"]) and np.array_equal(S1, S2)
+
+
+def test_cape_form_c_relative_positions_only(orc):
+    """Form C is a rotation by the position, so as for form A, shifting every
+    position by c leaves the outputs bit-identical and rotates the final
+    state by c."""
+    B, T, H, U, d_p, K, d_v = 1, 40, 2, 4, 3, 5, 16
+    M = d_p ** U
+    x = _small_inputs(31, B, T, H, U, d_p, d_v)
+    S_a = np.zeros((B, H, M, d_v), np.float32)
+    m_a = np.zeros((B, H, M), np.float32)
+    ra = _run(orc, x, S_a, m_a, d_p=d_p, U=U, K=K, state_bf16=False, cape=3,
+              pos0=np.zeros(B, np.int32))
+    for c in (1, 7, M + 2):
+        S_b, m_b = np.zeros_like(S_a), np.zeros_like(m_a)
+        rb = _run(orc, x, S_b, m_b, d_p=d_p, U=U, K=K, state_bf16=False, cape=3,
+                  pos0=np.full(B, c, np.int32))
+        assert np.array_equal(ra["out"], rb["out"])
+        perm = orc.cape(np.arange(M, dtype=np.int32), c, U, d_p, 3)
+        assert np.array_equal(S_b[:, :, perm], S_a)
+
+
+def test_content_heads_mask_selects_per_head(orc):
+    """Project page, CAPE: some heads use CAPE, others content-only
+    addresses.  A head whose bit is set behaves exactly as with CAPE off; the
+    others exactly as with CAPE on (heads are independent units)."""
+    B, T, H, U, d_p, K, d_v = 2, 24, 3, 5, 4, 8, 16
+    M = d_p ** U
+    x = _small_inputs(32, B, T, H, U, d_p, d_v)
+    pos0 = np.array([5, 2], np.int32)
+    runs = {}
+    for name, cape, mask in [("off", 0, 0), ("on", 2, 0), ("mixed", 2, 0b101)]:
+        S = np.zeros((B, H, M, d_v), np.float32)
+        m = np.zeros((B, H, M), np.float32)
+        runs[name] = (_run(orc, x, S, m, d_p=d_p, U=U, K=K, state_bf16=False,
+                           cape=cape, content_heads=mask, pos0=pos0), S)
+    for h in range(H):
+        ref = "off" if (0b101 >> h) & 1 else "on"
+        assert np.array_equal(runs["mixed"][0]["out"][:, :, h], runs[ref][0]["out"][:, :, h])
+        assert np.array_equal(runs["mixed"][0]["w_idx"][:, :, h], runs[ref][0]["w_idx"][:, :, h])
+        assert np.array_equal(runs["mixed"][1][:, h], runs[ref][1][:, h])
+    assert not np.array_equal(runs["off"][0]["out"], runs["on"][0]["out"])
+    # the decoder alone follows the same mask
+    idx, _, _ = orc.decode_all(x["k"], U, d_p, K, cape=2, pos0=pos0, content_heads=0b101)
+    assert np.array_equal(idx, runs["mixed"][0]["w_idx"])
 
 
 # ---------------------------------------------------------------- resume
