@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RAMNET_VERSION 1
+#define RAMNET_VERSION 2
 /* Largest supported K (Top-K per address). */
 #define RAMNET_KMAX 64
 
@@ -83,9 +83,17 @@ typedef struct {
     int32_t d_v;          /* value channels; 64, 128, 192 or 256 */
     int32_t in_dtype;     /* ramnet_dtype of q, k, v, gamma, g */
     int32_t state_dtype;  /* ramnet_dtype of S and out (mass is always fp32) */
-    int32_t cape;         /* 1: CAPE on every head; 0: content-only addresses */
+    int32_t cape;         /* CAPE (project page, CAPE paragraph, which leaves the exact
+                           * shift open): 0 content-only addresses; at position P,
+                           * 1 every digit advances by P mod d_p; 2 digit u advances
+                           * by digit u of P in base d_p (no carry); 3 the slot index
+                           * advances by P, wrapping over the M slots */
     float eps_gsu;        /* epsilon of the update rate; >= 0 (1e-6 typical) */
     float eps_norm;       /* epsilon of the RMSNorm; >= 0 (1e-6 typical) */
+    uint64_t content_heads; /* bit h set: head h uses content-only addresses
+                             * (the page mixes CAPE and content heads); heads
+                             * 63 and above follow bit 63.  0: every head
+                             * uses `cape`. */
 } ramnet_params;
 
 /* Sparse addresses, each [B,T,H,K] (a step: [B,H,K]).  Slots are post-CAPE
@@ -149,7 +157,7 @@ ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
  * slots are accessed directly, without a pass over the state): steps 1-4
  * for one token of each of B sequences.  p->T must be 1.
  *   q, k [B,H,U*d_p]; v, g [B,H,d_v]; gamma [B,H] (in_dtype)
- *   pos  [B] int32: position of this token; required when p->cape
+ *   pos  [B] int32: position of this token; required when p->cape != 0
  *   S, mass as for prefill; out [B,H,d_v] state_dtype
  *   addr_out NULL or [B,H,K] each. */
 ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,

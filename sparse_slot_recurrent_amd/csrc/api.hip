@@ -54,7 +54,7 @@ ramnet_status check_params(const ramnet_params *p, bool step) {
         return fail(RAMNET_EINVAL, "unknown in_dtype %d", p->in_dtype);
     if (p->state_dtype != RAMNET_F32 && p->state_dtype != RAMNET_BF16)
         return fail(RAMNET_EINVAL, "unknown state_dtype %d", p->state_dtype);
-    if (p->cape != 0 && p->cape != 1) return fail(RAMNET_EINVAL, "cape must be 0 or 1");
+    if (p->cape < 0 || p->cape > 3) return fail(RAMNET_EINVAL, "cape must be 0, 1, 2 or 3");
     if (!(p->eps_gsu >= 0.f) || !isfinite(p->eps_gsu) || !(p->eps_norm >= 0.f) ||
         !isfinite(p->eps_norm))
         return fail(RAMNET_EINVAL, "eps_gsu and eps_norm must be finite and >= 0");
@@ -167,6 +167,8 @@ ramnet::DecodeArgs decode_args(const ramnet_params *p, const void *q, const void
     d.d_p = p->d_p;
     d.pos0 = pos0;
     d.cape = p->cape;
+    d.content_heads = p->content_heads;
+    d.M = p->M;
     d.in_bf16 = p->in_dtype == RAMNET_BF16;
     d.w_idx = o.w_idx;
     d.w_wt = o.w_wt;
@@ -189,7 +191,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     if (n == 0) return ok();
     if (decode) {
         if ((s = check_ptr("q", q, true)) || (s = check_ptr("k", k, true))) return s;
-        if (step && p->cape && !pos) return fail(RAMNET_EINVAL, "pos is required when cape = 1");
+        if (step && p->cape && !pos) return fail(RAMNET_EINVAL, "pos is required when cape != 0");
         if ((s = check_ptr(step ? "pos" : "pos0", pos, false))) return s;
     } else if ((s = check_addr("addr_in", addr_in))) {
         return s;
@@ -252,6 +254,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sa.U = p->U;
         sa.d_p = p->d_p;
         sa.cape = p->cape;
+        sa.content_heads = p->content_heads;
         sa.in_bf16 = p->in_dtype == RAMNET_BF16;
         sa.state_bf16 = p->state_dtype == RAMNET_BF16;
         sa.q = q;

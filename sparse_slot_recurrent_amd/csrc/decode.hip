@@ -28,20 +28,6 @@ __device__ __forceinline__ bool ranks_before(WT wa, int ia, WT wb, int ib) {
 
 __device__ __forceinline__ double wexp(double x) { return exp(x); }
 
-template <int DP>
-__device__ __forceinline__ int cape_move(int slot, int64_t pos, int U) {
-    const unsigned s = static_cast<unsigned>(((pos % DP) + DP) % DP);
-    if (s == 0) return slot;
-    unsigned x = static_cast<unsigned>(slot), moved = 0, place = 1;
-    for (int u = 0; u < U; ++u) {
-        const unsigned d = x % DP;
-        x /= DP;
-        moved += ((d + s) % DP) * place;
-        place *= DP;
-    }
-    return static_cast<int>(moved);
-}
-
 // KC: beam capacity (K rounded up to 8, 16, 32 or 64).  The beam being read
 // lives in LDS, column-interleaved by lane; up to KC = 32 the beam being
 // built is held in registers (its rank index is a compile-time constant of
@@ -50,7 +36,8 @@ __device__ __forceinline__ int cape_move(int slot, int64_t pos, int U) {
 template <int DP, int KC, typename WT, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, int64_t n, int T, int H,
-    int U, int K, const int32_t *__restrict__ pos0, int cape, bool unit_major,
+    int U, int K, const int32_t *__restrict__ pos0, int cape, uint64_t content_heads,
+    int64_t M, bool unit_major,
     int32_t *__restrict__ w_idx, float *__restrict__ w_wt,
     int32_t *__restrict__ r_idx, float *__restrict__ r_wt) {
     constexpr bool kRegs = KC <= 32;
@@ -176,6 +163,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int64_t b = a / (static_cast<int64_t>(T) * H);
     const int64_t t = (a / H) % T;
     const int64_t pos = (pos0 ? pos0[b] : 0) + t;
+    const int form = head_uses_cape(content_heads, static_cast<int>(a % H)) ? cape : 0;
     // [B,T,H,K], or [B,H,T,K] so that a head's addresses are contiguous
     const int64_t o = unit_major ? ((b * H + a % H) * T + t) : a;
     int32_t *oi = (key ? w_idx : r_idx) + o * K;
@@ -184,14 +172,14 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
 #pragma unroll
         for (int r = 0; r < KC; ++r) {
             if (r < K) {
-                oi[r] = cape ? cape_move<DP>(nxp[r], pos, U) : nxp[r];
+                oi[r] = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
                 ow[r] = static_cast<float>(nxw[r]);
             }
         }
     } else {
         for (int r = 0; r < K; ++r) {
             const int slot = BP(cur, r);
-            oi[r] = cape ? cape_move<DP>(slot, pos, U) : slot;
+            oi[r] = form ? cape_slot<DP>(slot, pos, U, DP, form, M) : slot;
             ow[r] = static_cast<float>(BW(cur, r));
         }
     }
@@ -210,8 +198,8 @@ hipError_t launch_kc(const DecodeArgs &d, hipStream_t st) {
     dim3 grid(static_cast<unsigned>((d.n + kWave - 1) / kWave), 2);
     hipLaunchKernelGGL(kern, grid, dim3(kWave), lds, st,
                        static_cast<const TIn *>(d.q), static_cast<const TIn *>(d.k), d.n,
-                       d.T, d.H, d.U, d.K, d.pos0, d.cape, d.unit_major, d.w_idx, d.w_wt,
-                       d.r_idx, d.r_wt);
+                       d.T, d.H, d.U, d.K, d.pos0, d.cape, d.content_heads, d.M, d.unit_major,
+                       d.w_idx, d.w_wt, d.r_idx, d.r_wt);
     return hipGetLastError();
 }
 

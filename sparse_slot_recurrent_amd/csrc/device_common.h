@@ -99,4 +99,34 @@ __device__ __forceinline__ float retention_fast(float w, float exp_gamma) {
     return __builtin_amdgcn_exp2f(exp_gamma * l2);
 }
 
+// CAPE (project page, CAPE paragraph): the slot a content address moves to
+// at position pos, by reading `form`: 1 every digit advances by pos mod dp;
+// 2 digit u advances by digit u of pos (base dp, U digits, no carry); 3 the
+// slot index advances by pos, wrapping over the M = dp^U slots.  Digits wrap
+// within their dp values.  DP > 0 fixes the base at compile time.
+template <int DP>
+__device__ __forceinline__ int cape_slot(int slot, int64_t pos, int U, int dp_rt, int form, int64_t M) {
+    const int dp = DP > 0 ? DP : dp_rt;
+    const int64_t pm = ((pos % M) + M) % M;
+    if (form == 3) return static_cast<int>((slot + pm) % M);
+    const unsigned s1 = static_cast<unsigned>(((pos % dp) + dp) % dp);
+    if (form == 1 && s1 == 0) return slot;
+    unsigned x = static_cast<unsigned>(slot), p = static_cast<unsigned>(pm), moved = 0, place = 1;
+    for (int u = 0; u < U; ++u) {
+        const unsigned d = x % dp;
+        const unsigned sh = form == 2 ? p % dp : s1;
+        x /= dp;
+        p /= dp;
+        moved += ((d + sh) % dp) * place;
+        place *= dp;
+    }
+    return static_cast<int>(moved);
+}
+
+// Whether head h uses CAPE: its bit of content_heads (bit 63 for h >= 63)
+// is clear.
+__device__ __forceinline__ bool head_uses_cape(uint64_t content_heads, int h) {
+    return !((content_heads >> (h < 63 ? h : 63)) & 1u);
+}
+
 }  // namespace ramnet

@@ -13,7 +13,9 @@ struct DecodeArgs {
     int64_t n;
     int T, H, U, K, d_p;
     const int32_t *pos0;  // position of token t of sequence b: pos0[b] + t
-    int cape;
+    int cape;               // 0 off, 1..3 the CAPE reading
+    uint64_t content_heads;  // bit h: head h is content-only (bit 63 for h >= 63)
+    int64_t M;
     bool in_bf16;
     bool unit_major;  // write addresses as [B,H,T,K] (else [B,T,H,K])
     int32_t *w_idx, *r_idx;
@@ -89,6 +91,7 @@ struct StepArgs {
     int B, H;
     int64_t M;
     int K, d_v, U, d_p, cape;
+    uint64_t content_heads;
     bool in_bf16, state_bf16;
     const void *q, *k, *v, *gamma, *g;
     const float *norm_w;

@@ -36,19 +36,6 @@ namespace {
 // Most digits an address has: U * d_p with d_p^U <= 2^30 peaks at 80 (d_p 8).
 constexpr int kMaxDigits = 80;
 
-__device__ __forceinline__ int cape_move_rt(int slot, int64_t pos, int U, int dp) {
-    const unsigned s = static_cast<unsigned>(((pos % dp) + dp) % dp);
-    if (s == 0) return slot;
-    unsigned x = static_cast<unsigned>(slot), moved = 0, place = 1;
-    for (int u = 0; u < U; ++u) {
-        const unsigned d = x % dp;
-        x /= dp;
-        moved += ((d + s) % dp) * place;
-        place *= dp;
-    }
-    return static_cast<int>(moved);
-}
-
 // CPL adjacent channels of one row as a single vector access.
 template <typename T, int CPL>
 struct RowVec {
@@ -299,7 +286,8 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         const int b = unit / a.H;
         const int64_t pos = a.pos ? a.pos[b] : 0;
         if (u0 + ul < units && r < K) {
-            const int slot = a.cape ? cape_move_rt(beam.p, pos, U, dp) : beam.p;
+            const int form = head_uses_cape(a.content_heads, unit % a.H) ? a.cape : 0;
+            const int slot = form ? cape_slot<0>(beam.p, pos, U, dp, form, M) : beam.p;
             const float wt = static_cast<float>(beam.w);
             sidx[(ul * 2 + which) * K + r] = slot;
             swt[(ul * 2 + which) * K + r] = wt;

@@ -29,7 +29,7 @@ class Params(C.Structure):
                 ("K", C.c_int32), ("d_v", C.c_int32),
                 ("in_dtype", C.c_int32), ("state_dtype", C.c_int32),
                 ("cape", C.c_int32), ("eps_gsu", C.c_float),
-                ("eps_norm", C.c_float)]
+                ("eps_norm", C.c_float), ("content_heads", C.c_uint64)]
 
 
 class Addr(C.Structure):
@@ -91,9 +91,12 @@ def _raise(status: int):
 
 
 def make_params(B, T, H, d_p, U, K, d_v, in_dtype=BF16, state_dtype=F32,
-                cape=1, eps_gsu=1e-6, eps_norm=1e-6, M=None) -> Params:
+                cape=1, eps_gsu=1e-6, eps_norm=1e-6, M=None,
+                content_heads=0) -> Params:
+    """cape: 0 content-only, 1/2/3 the CAPE reading; content_heads: bit h
+    set makes head h content-only."""
     return Params(B, T, H, d_p, U, d_p ** U if M is None else M, K, d_v,
-                  in_dtype, state_dtype, cape, eps_gsu, eps_norm)
+                  in_dtype, state_dtype, cape, eps_gsu, eps_norm, content_heads)
 
 
 def workspace_bytes(p: Params, op: int) -> int:
@@ -153,12 +156,14 @@ def new_addresses(shape_bthk, device) -> Addresses:
 
 
 def decode_addresses(q, k, *, d_p: int, U: int, K: int, cape: int = 1,
-                     pos0=None, out: Optional[Addresses] = None) -> Addresses:
+                     pos0=None, out: Optional[Addresses] = None,
+                     content_heads: int = 0) -> Addresses:
     """q, k [B,T,H,U*d_p] -> Addresses, each [B,T,H,K] (post-CAPE slots),
     written into `out` when given."""
     B, T, H, L = q.shape
     assert L == U * d_p and k.shape == q.shape
-    p = make_params(B, T, H, d_p, U, K, 64, in_dtype=_dt(q), cape=cape)
+    p = make_params(B, T, H, d_p, U, K, 64, in_dtype=_dt(q), cape=cape,
+                    content_heads=content_heads)
     if out is None:
         out = new_addresses((B, T, H, K), q.device)
     a = _addr_struct(out)
@@ -172,10 +177,10 @@ class PrefillPlan:
     of one shape (the benchmark's timed loop allocates nothing)."""
 
     def __init__(self, B, T, H, d_p, U, K, d_v, in_dtype, state_dtype, cape=1,
-                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda"):
+                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda", content_heads=0):
         torch = _torch()
         self.p = make_params(B, T, H, d_p, U, K, d_v, in_dtype, state_dtype,
-                             cape, eps_gsu, eps_norm)
+                             cape, eps_gsu, eps_norm, content_heads=content_heads)
         nbytes = workspace_bytes(self.p, OP_PREFILL)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
                                      device=device)
@@ -198,14 +203,14 @@ class PrefillPlan:
 def scan_prefill(q, k, v, gamma, g, S, mass, *, d_p: int, U: int, K: int,
                  cape: int = 1, norm_w=None, pos0=None, eps_gsu=1e-6,
                  eps_norm=1e-6, addr_in: Optional[Addresses] = None,
-                 export_addresses: bool = False):
+                 export_addresses: bool = False, content_heads: int = 0):
     """Runs the layer over [B,T,H]; S [B,H,M,d_v] and mass [B,H,M] are
     updated in place.  Returns out [B,T,H,d_v] (and the addresses used when
     export_addresses)."""
     torch = _torch()
     B, T, H, d_v = v.shape
     plan = PrefillPlan(B, T, H, d_p, U, K, d_v, _dt(v), _dt(S), cape, eps_gsu,
-                       eps_norm, device=v.device)
+                       eps_norm, device=v.device, content_heads=content_heads)
     out = torch.empty((B, T, H, d_v), dtype=S.dtype, device=v.device)
     ao = new_addresses((B, T, H, K), v.device) if export_addresses else None
     plan(q, k, v, gamma, g, S, mass, out, norm_w=norm_w, pos0=pos0,
@@ -217,10 +222,10 @@ class StepPlan:
     """A decode step of one shape with its workspace, reusable per step."""
 
     def __init__(self, B, H, d_p, U, K, d_v, in_dtype, state_dtype, cape=1,
-                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda"):
+                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda", content_heads=0):
         torch = _torch()
         self.p = make_params(B, 1, H, d_p, U, K, d_v, in_dtype, state_dtype,
-                             cape, eps_gsu, eps_norm)
+                             cape, eps_gsu, eps_norm, content_heads=content_heads)
         nbytes = workspace_bytes(self.p, OP_STEP)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
                                      device=device)
@@ -239,13 +244,13 @@ class StepPlan:
 
 def step_decode(q, k, v, gamma, g, pos, S, mass, *, d_p: int, U: int, K: int,
                 cape: int = 1, norm_w=None, eps_gsu=1e-6, eps_norm=1e-6,
-                export_addresses: bool = False):
+                export_addresses: bool = False, content_heads: int = 0):
     """One token per sequence: q, k [B,H,U*d_p]; v, g [B,H,d_v]; gamma [B,H];
     pos [B] int32.  Returns out [B,H,d_v] (and the addresses)."""
     torch = _torch()
     B, H, d_v = v.shape
     plan = StepPlan(B, H, d_p, U, K, d_v, _dt(v), _dt(S), cape, eps_gsu,
-                    eps_norm, device=v.device)
+                    eps_norm, device=v.device, content_heads=content_heads)
     out = torch.empty((B, H, d_v), dtype=S.dtype, device=v.device)
     ao = new_addresses((B, H, K), v.device) if export_addresses else None
     plan(q, k, v, gamma, g, pos, S, mass, out, norm_w=norm_w, addr_out=ao)

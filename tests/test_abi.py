@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(rn):
 
 def test_version_and_status_strings(rn):
     lib = rn.load_library()
-    assert lib.ramnet_version() == 1
+    assert lib.ramnet_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert lib.ramnet_status_str(code).decode() != "unknown status"
 
@@ -79,7 +79,8 @@ def call_prefill(rn, p, q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32),
     ("B", -1, -1, ">= 0"),
     ("in_dtype", 7, -1, "in_dtype"),
     ("state_dtype", 3, -1, "state_dtype"),
-    ("cape", 2, -1, "cape"),
+    ("cape", 4, -1, "cape"),
+    ("cape", -1, -1, "cape"),
     ("eps_gsu", -1.0, -1, "eps"),
     ("eps_norm", float("nan"), -1, "eps"),
     ("d_v", 96, -2, "d_v"),

@@ -87,31 +87,38 @@ def run_oracle(orc, w, x, mode=0, norm_w=None):
     return res, S, m
 
 
-def weights_fn(orc, w, x, logits_name, pos):
+def weights_fn(orc, w, x, logits_name, pos, content_heads=0):
     """Oracle fp64 weight of given post-CAPE slots of flat address f."""
     lg = x[logits_name].reshape(-1, w.L)
     B, T, H = x["gamma"].shape
+    M = w.d_p ** w.U
 
     def f(flat, slots):
         b = flat // (T * H)
         t = (flat // H) % T
+        h = flat % H
         P = int(pos[b]) + t
-        content = orc.cape(np.asarray(slots, np.int32), -P if w.cape else 0,
-                           w.U, w.d_p) if w.cape else np.asarray(slots)
+        form = 0 if (content_heads >> min(h, 63)) & 1 else w.cape
+        slots = np.asarray(slots, np.int64)
+        if form:
+            perm = orc.cape(np.arange(M, dtype=np.int32), P, w.U, w.d_p, form)
+            inv = np.empty(M, np.int64)
+            inv[perm] = np.arange(M)
+            slots = inv[slots]
         W = orc.slot_weights(lg[flat], w.U, w.d_p)
-        return W[content]
+        return W[slots]
     return f
 
 
-def check_layer(orc, w, x, out, addr, S, mass, ref, S_ref, m_ref):
+def check_layer(orc, w, x, out, addr, S, mass, ref, S_ref, m_ref, content_heads=0):
     """Tie-aware address check, then values before any legitimate
     divergence, then untouched rows bit-exact."""
     bf = w.state_dtype == "bf16"
     g_wi, g_ww, g_ri, g_rw = (to_np(a) for a in addr)
-    dw = compare_address_sets(g_wi, g_ww, ref["w_idx"], ref["w_wt"],
-                              ref["w_gap"], weights_fn(orc, w, x, "k", x["pos0"]))
-    dr = compare_address_sets(g_ri, g_rw, ref["r_idx"], ref["r_wt"],
-                              ref["r_gap"], weights_fn(orc, w, x, "q", x["pos0"]))
+    dw = compare_address_sets(g_wi, g_ww, ref["w_idx"], ref["w_wt"], ref["w_gap"],
+                              weights_fn(orc, w, x, "k", x["pos0"], content_heads))
+    dr = compare_address_sets(g_ri, g_rw, ref["r_idx"], ref["r_wt"], ref["r_gap"],
+                              weights_fn(orc, w, x, "q", x["pos0"], content_heads))
     B, T, H = x["gamma"].shape
     diverged = (dw | dr)                       # [B,T,H]
     first = np.where(diverged.any(1), diverged.argmax(1), T)  # [B,H]
@@ -251,6 +258,61 @@ def test_norm_weight_and_cape_off(rn, orc):
     out, addr, d = run_gpu(rn, w, x, norm_w=torch.from_numpy(nw).cuda())
     ref, S_ref, m_ref = run_oracle(orc, w, x, norm_w=nw)
     check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, S_ref, m_ref)
+
+
+@pytest.mark.parametrize("cape,mask", [(2, 0), (3, 0), (2, 0b0101), (3, 0b1000)])
+def test_cape_forms_and_content_heads(rn, orc, cape, mask):
+    """CAPE readings B (2) and C (3) and per-head content-only addresses:
+    the decoder alone and the whole prefill against the oracle."""
+    w = synth.WORKLOADS["prefill_top8"].replace(cape=cape)
+    x = synth.make_inputs(w, B=2, T=150, H=4)
+    d = gpu_inputs(w, x)
+    addr = rn.decode_addresses(d["q"], d["k"], d_p=w.d_p, U=w.U, K=w.K,
+                               cape=cape, pos0=d["pos0"], content_heads=mask)
+    torch.cuda.synchronize()
+    for lg, gi, gw in (("k", addr.w_idx, addr.w_wt), ("q", addr.r_idx, addr.r_wt)):
+        oi, ow, og = orc.decode_all(x[lg], w.U, w.d_p, w.K, cape=cape,
+                                    pos0=x["pos0"], content_heads=mask)
+        compare_address_sets(to_np(gi), to_np(gw), oi, ow, og,
+                             weights_fn(orc, w, x, lg, x["pos0"], mask))
+    res = rn.scan_prefill(d["q"], d["k"], d["v"], d["gamma"], d["g"], d["S"],
+                          d["mass"], d_p=w.d_p, U=w.U, K=w.K, cape=cape,
+                          pos0=d["pos0"], export_addresses=True, content_heads=mask)
+    torch.cuda.synchronize()
+    out, gaddr = res
+    S_ref, m_ref = x["S0"].copy(), x["m0"].copy()
+    ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S_ref, m_ref,
+                    d_p=w.d_p, U=w.U, K=w.K, state_bf16=False, cape=cape,
+                    pos0=x["pos0"], content_heads=mask)
+    check_layer(orc, w, x, out, gaddr, d["S"], d["mass"], ref, S_ref, m_ref, content_heads=mask)
+
+
+@pytest.mark.parametrize("cape,mask", [(2, 0b0011), (3, 0)])
+def test_step_decode_cape_forms(rn, orc, cape, mask):
+    """The fused decode step with CAPE readings B and C and mixed heads."""
+    w = synth.WORKLOADS["decode"].replace(cape=cape)
+    B = 8
+    init = synth.make_inputs(w, B=B, T=1)
+    S_d, m_d = dev(init["S0"], "bf16"), dev(init["m0"], "f32")
+    s = synth.make_decode_step(w, 0, B=B)
+    pos = init["pos0"]
+    out, ao = rn.step_decode(*(dev(s[n], "bf16") for n in ("q", "k", "v", "gamma", "g")),
+                             torch.from_numpy(pos).cuda(), S_d, m_d, d_p=w.d_p, U=w.U,
+                             K=w.K, cape=cape, export_addresses=True, content_heads=mask)
+    torch.cuda.synchronize()
+    x = {n: np.ascontiguousarray(s[n][:, None]) for n in s}
+    S_o, m_o = init["S0"].copy(), init["m0"].copy()
+    ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S_o, m_o, d_p=w.d_p,
+                    U=w.U, K=w.K, state_bf16=True, cape=cape, pos0=pos, content_heads=mask)
+    xs = dict(x, pos0=pos)
+    dw = compare_address_sets(to_np(ao.w_idx)[:, None], to_np(ao.w_wt)[:, None], ref["w_idx"],
+                              ref["w_wt"], ref["w_gap"],
+                              weights_fn(orc, w, xs, "k", pos, mask))
+    dr = compare_address_sets(to_np(ao.r_idx)[:, None], to_np(ao.r_wt)[:, None], ref["r_idx"],
+                              ref["r_wt"], ref["r_gap"],
+                              weights_fn(orc, w, xs, "q", pos, mask))
+    ok = ~(dw | dr)[:, 0]  # [B, H]
+    assert_close(to_np(out)[ok], ref["out"][:, 0][ok], True, "out")
 
 
 @pytest.mark.parametrize("d_p,U,K,d_v,in_dt,st_dt", [
