@@ -1,6 +1,8 @@
 """CPU oracle for the RAM-Net layer recurrence.  TEST INFRASTRUCTURE ONLY.
 
-A plain fp64 C implementation (ramnet_oracle.c) wrapped with ctypes.  Only the
+A plain fp64 C implementation (ramnet_oracle.c) wrapped with ctypes, and
+projections.py (numpy fp64) for the dense steps either side of the layer.
+Only the
 tests, the smoke check and the benchmark's CPU-baseline leg may import this
 package; the product path never does.
 """
