@@ -34,7 +34,10 @@
  * Conventions for every entry point:
  *   - Tensors are contiguous, row-major, in DEVICE memory, caller-owned.
  *     The library allocates no device memory; scratch space comes from the
- *     caller's `workspace` (size from ramnet_workspace_bytes).
+ *     caller's `workspace` (size from ramnet_workspace_bytes or
+ *     ramnet_layer_workspace_bytes).  The one exception: the first
+ *     projection call on a device creates that device's hipBLASLt handle,
+ *     which lives until the process ends.
  *   - Every device pointer must be 16-byte aligned.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL is the null stream).  Validation runs synchronously on the
@@ -45,8 +48,9 @@
  *   - S and mass are updated in place.  Inputs are never written.  `out`
  *     and the address outputs must not overlap any other buffer.
  *   - Calls that share S/mass must be ordered by the caller (same stream).
- *     There is no global state; calls on different buffers may run
- *     concurrently.
+ *     Calls on different buffers may run concurrently; the only global state
+ *     is the per-device hipBLASLt handle and its per-shape algorithm cache
+ *     (guarded by a lock).
  */
 #ifndef RAMNET_H
 #define RAMNET_H
@@ -58,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RAMNET_VERSION 2
+#define RAMNET_VERSION 3
 /* Largest supported K (Top-K per address). */
 #define RAMNET_KMAX 64
 
@@ -167,6 +171,65 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
                                  void *S, float *mass, void *out,
                                  const ramnet_addr *addr_out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * A whole layer: the dense projections either side of the recurrence (RAM-Net
+ * project page, layer outline: the token is projected to key, query and
+ * value, the GSU's gamma comes from the token by a learned projection, and
+ * the gated read is projected out), with the address weights re-parameterised
+ * as W = e^alpha * W' per head (paper digest, stability of the decoder: alpha
+ * sets the temperature of the Product Softmax).
+ *
+ * All weights are bf16, row-major [rows, cols], d_model = D:
+ *   w_q, w_k   [D, H*U*d_p]  W' of the query / key logits; column h*U*d_p + j
+ *              is logit j of head h.  The GEMM uses W = bf16(t_h * W'), with
+ *              t_h = fp32(e^alpha[h]), rounded once from the exact product.
+ *   w_v, w_g   [D, H*d_v]    values and output-gate logits (column h*d_v + c)
+ *   w_gamma    [D, H]        the GSU's gamma, one per head
+ *   w_o        [H*d_v, D]    output projection of the layer output
+ *   alpha      [H] fp32 or NULL (= 0, W = W')
+ * Each product is accumulated in fp32 and rounded to bf16 (hipBLASLt on the
+ * matrix cores); the layer output is rounded to bf16 before w_o.  p->in_dtype
+ * must be RAMNET_BF16 (q, k, v, gamma, g are the bf16 projections).
+ */
+typedef struct {
+    int32_t d_model;
+    const void *w_q, *w_k, *w_v, *w_g, *w_gamma, *w_o;
+    const float *alpha;
+} ramnet_proj;
+
+/* Workspace bytes of ramnet_layer_forward / ramnet_layer_step /
+ * ramnet_project_inputs for `p` and d_model (0 if either is invalid). */
+size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model);
+
+/* The five input projections of x [B,T,D] bf16 into q, k [B,T,H,U*d_p],
+ * v, g [B,T,H,d_v] and gamma [B,T,H], all bf16, exactly as
+ * ramnet_layer_forward computes them. */
+ramnet_status ramnet_project_inputs(const ramnet_params *p, const ramnet_proj *w,
+                                    const void *x, void *q, void *k, void *v,
+                                    void *gamma, void *g, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Prefill of a whole layer: x [B,T,D] bf16 -> y [B,T,D] bf16.  Projections,
+ * then ramnet_scan_prefill on them (norm_w, pos0, S, mass, addr_out as
+ * there), then the output projection.  workspace:
+ * ramnet_layer_workspace_bytes(p, D) bytes; it also holds the projected
+ * inputs and the layer output. */
+ramnet_status ramnet_layer_forward(const ramnet_params *p, const ramnet_proj *w,
+                                   const void *x, const float *norm_w,
+                                   const int32_t *pos0, void *S, float *mass,
+                                   void *y, const ramnet_addr *addr_out,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* One decoding step of a whole layer (p->T == 1): x [B,D] -> y [B,D], bf16,
+ * through ramnet_step_decode (pos, S, mass, addr_out as there). */
+ramnet_status ramnet_layer_step(const ramnet_params *p, const ramnet_proj *w,
+                                const void *x, const float *norm_w,
+                                const int32_t *pos, void *S, float *mass,
+                                void *y, const ramnet_addr *addr_out,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 const char *ramnet_status_str(ramnet_status s);
 const char *ramnet_last_error(void);

@@ -19,7 +19,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libramnet.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "step_fused.hip"]
+SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "step_fused.hip",
+           "proj.hip"]
+# hipBLASLt carries the dense projections around the layer.
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -54,7 +57,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -182,7 +182,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
                         const void *v, const void *gamma, const void *g, const float *norm_w,
                         const int32_t *pos, void *S, float *mass, void *out,
                         const ramnet_addr *addr_in, const ramnet_addr *addr_out, void *ws,
-                        size_t ws_bytes, void *stream) {
+                        size_t ws_bytes, void *stream, void *out_bf16 = nullptr) {
     ramnet_status s = check_params(p, step);
     if (s) return s;
     const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
@@ -273,7 +273,10 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sa.out_wt[1] = addr_out ? addr_out->r_wt : nullptr;
         sa.eps_gsu = p->eps_gsu;
         sa.eps_norm = p->eps_norm;
-        return hip_status(ramnet::launch_step_fused(sa, st), "decode step launch");
+        hipError_t e = ramnet::launch_step_fused(sa, st);
+        if (e == hipSuccess && out_bf16)
+            e = ramnet::launch_to_bf16(static_cast<const float *>(out), out_bf16, n * p->d_v, st);
+        return hip_status(e, "decode step launch");
     }
     ramnet_addr addr;
     // Addresses kept in the workspace for the slot-grouped path are laid out
@@ -328,9 +331,12 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         c.mass_ws = reinterpret_cast<float *>(cw);
         cw += lp.cp.ws_mass;
         c.plan = reinterpret_cast<unsigned char *>(cw);
+        c.out_bf16 = out_bf16;  // the epilogue writes bf16 directly
         e = ramnet::launch_scan_chunked(c, st);
     } else {
         e = ramnet::launch_scan_serial(a, st);
+        if (e == hipSuccess && out_bf16)
+            e = ramnet::launch_to_bf16(static_cast<const float *>(out), out_bf16, n * p->d_v, st);
     }
     if (e != hipSuccess) return hip_status(e, "scan launch");
     if (!decode && addr_out) {
@@ -350,9 +356,249 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     return ok();
 }
 
+// ---------------------------------------------------------------- whole layer
+
+// Workspace of the projected layer: tempered address weights, hipBLASLt
+// scratch, the projected inputs, the layer output (and its bf16 copy when
+// the state is fp32), then the layer's own workspace.
+struct FwdPlan {
+    size_t o_wq, o_wk, o_gemm, o_q, o_k, o_v, o_g, o_gamma, o_out, o_out16, o_layer, total;
+};
+
+FwdPlan plan_forward(const ramnet_params *p, int32_t d_model, bool step) {
+    FwdPlan f{};
+    const size_t n = static_cast<size_t>(p->B) * p->T * p->H;
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    const size_t HL = static_cast<size_t>(p->H) * L;
+    size_t o = 0;
+    f.o_wq = o; o += align256(static_cast<size_t>(d_model) * HL * 2);
+    f.o_wk = o; o += align256(static_cast<size_t>(d_model) * HL * 2);
+    f.o_gemm = o; o += ramnet::kGemmWorkspace;
+    f.o_q = o; o += align256(n * L * 2);
+    f.o_k = o; o += align256(n * L * 2);
+    f.o_v = o; o += align256(n * p->d_v * 2);
+    f.o_g = o; o += align256(n * p->d_v * 2);
+    f.o_gamma = o; o += align256(n * 2);
+    f.o_out = o; o += align256(n * p->d_v * st_bytes(p));
+    f.o_out16 = o; o += p->state_dtype == RAMNET_BF16 ? 0 : align256(n * p->d_v * 2);
+    f.o_layer = o; o += plan_layer(p, step, true).total();
+    f.total = o;
+    return f;
+}
+
+constexpr int32_t kMaxDModel = 1 << 16;
+
+ramnet_status check_proj(const ramnet_params *p, const ramnet_proj *w) {
+    if (!w) return fail(RAMNET_EINVAL, "w is NULL");
+    if (p->in_dtype != RAMNET_BF16)
+        return fail(RAMNET_EUNSUPPORTED, "the projections need in_dtype = RAMNET_BF16");
+    if (w->d_model < 8 || w->d_model > kMaxDModel || w->d_model % 8)
+        return fail(RAMNET_EINVAL, "d_model = %d: must be a multiple of 8 in [8, %d]", w->d_model,
+                    kMaxDModel);
+    ramnet_status s;
+    if ((s = check_ptr("w_q", w->w_q, true)) || (s = check_ptr("w_k", w->w_k, true)) ||
+        (s = check_ptr("w_v", w->w_v, true)) || (s = check_ptr("w_g", w->w_g, true)) ||
+        (s = check_ptr("w_gamma", w->w_gamma, true)) || (s = check_ptr("w_o", w->w_o, true)) ||
+        (s = check_ptr("alpha", w->alpha, false)))
+        return s;
+    return RAMNET_OK;
+}
+
+// Read-only spans of the weights.
+int weight_spans(const ramnet_params *p, const ramnet_proj *w, bool with_o, Span *sp) {
+    const size_t D = w->d_model;
+    const size_t HL = static_cast<size_t>(p->H) * p->U * p->d_p;
+    const size_t HV = static_cast<size_t>(p->H) * p->d_v;
+    int ns = 0;
+    sp[ns++] = span("w_q", w->w_q, D * HL * 2);
+    sp[ns++] = span("w_k", w->w_k, D * HL * 2);
+    sp[ns++] = span("w_v", w->w_v, D * HV * 2);
+    sp[ns++] = span("w_g", w->w_g, D * HV * 2);
+    sp[ns++] = span("w_gamma", w->w_gamma, D * p->H * 2);
+    if (with_o) sp[ns++] = span("w_o", w->w_o, HV * D * 2);
+    if (w->alpha) sp[ns++] = span("alpha", w->alpha, p->H * sizeof(float));
+    return ns;
+}
+
+struct Projected {
+    void *q, *k, *v, *g, *gamma;
+};
+
+// Validates every GEMM shape of the call (creating the handle), so that a
+// failure is reported before anything is enqueued.
+ramnet_status prepare_gemms(const ramnet_params *p, const ramnet_proj *w, int64_t rows,
+                            bool with_o) {
+    const int64_t HL = static_cast<int64_t>(p->H) * p->U * p->d_p;
+    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
+    const int64_t shapes[4][3] = {{rows, HL, w->d_model}, {rows, HV, w->d_model},
+                                  {rows, p->H, w->d_model}, {rows, w->d_model, HV}};
+    std::string err;
+    for (int i = 0; i < (with_o ? 4 : 3); ++i)
+        if (!ramnet::gemm_prepare(shapes[i][0], shapes[i][1], shapes[i][2], err))
+            return fail(RAMNET_EHIP, "%s", err.c_str());
+    return RAMNET_OK;
+}
+
+// Enqueues the tempered weights and the five input GEMMs.
+ramnet_status enqueue_inputs(const ramnet_params *p, const ramnet_proj *w, const void *x,
+                             int64_t rows, const Projected &o, char *ws, const FwdPlan &f,
+                             hipStream_t st) {
+    const int64_t D = w->d_model;
+    const int L = p->U * p->d_p;
+    const int64_t HL = static_cast<int64_t>(p->H) * L;
+    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
+    const void *wq = w->w_q, *wk = w->w_k;
+    if (w->alpha) {
+        hipError_t e = ramnet::launch_temper(w->w_q, w->alpha, ws + f.o_wq, D, static_cast<int>(HL), L, st);
+        if (e == hipSuccess)
+            e = ramnet::launch_temper(w->w_k, w->alpha, ws + f.o_wk, D, static_cast<int>(HL), L, st);
+        if (e != hipSuccess) return hip_status(e, "address weight launch");
+        wq = ws + f.o_wq;
+        wk = ws + f.o_wk;
+    }
+    void *gw = ws + f.o_gemm;
+    std::string err;
+    if (!ramnet::gemm_bf16(x, wq, o.q, rows, HL, D, gw, st, err) ||
+        !ramnet::gemm_bf16(x, wk, o.k, rows, HL, D, gw, st, err) ||
+        !ramnet::gemm_bf16(x, w->w_v, o.v, rows, HV, D, gw, st, err) ||
+        !ramnet::gemm_bf16(x, w->w_g, o.g, rows, HV, D, gw, st, err) ||
+        !ramnet::gemm_bf16(x, w->w_gamma, o.gamma, rows, p->H, D, gw, st, err))
+        return fail(RAMNET_EHIP, "%s", err.c_str());
+    return RAMNET_OK;
+}
+
+ramnet_status check_workspace(const FwdPlan &f, void *ws, size_t ws_bytes) {
+    if (!ws || ws_bytes < f.total)
+        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", f.total,
+                    ws ? ws_bytes : size_t(0));
+    return check_ptr("workspace", ws, true);
+}
+
+ramnet_status run_whole_layer(const ramnet_params *p, bool step, const ramnet_proj *w,
+                              const void *x, const float *norm_w, const int32_t *pos, void *S,
+                              float *mass, void *y, const ramnet_addr *addr_out, void *ws,
+                              size_t ws_bytes, void *stream) {
+    ramnet_status s = check_params(p, step);
+    if (s || (s = check_proj(p, w))) return s;
+    const int64_t rows = static_cast<int64_t>(p->B) * p->T;
+    const int64_t n = rows * p->H;
+    if (n == 0) return ok();
+    if (step && p->cape && !pos) return fail(RAMNET_EINVAL, "pos is required when cape != 0");
+    if ((s = check_ptr("x", x, true)) || (s = check_ptr("norm_w", norm_w, false)) ||
+        (s = check_ptr(step ? "pos" : "pos0", pos, false)) || (s = check_ptr("S", S, true)) ||
+        (s = check_ptr("mass", mass, true)) || (s = check_ptr("y", y, true)))
+        return s;
+    if (addr_out && (s = check_addr("addr_out", addr_out))) return s;
+    const FwdPlan f = plan_forward(p, w->d_model, step);
+    if ((s = check_workspace(f, ws, ws_bytes))) return s;
+    const size_t D = w->d_model;
+    const size_t nK4 = static_cast<size_t>(n) * p->K * 4;
+    Span sp[20];
+    int ns = weight_spans(p, w, true, sp);
+    sp[ns++] = span("x", x, rows * D * 2);
+    if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
+    if (pos) sp[ns++] = span(step ? "pos" : "pos0", pos, p->B * sizeof(int32_t));
+    const int first_written = ns;
+    sp[ns++] = span("S", S, static_cast<size_t>(p->B) * p->H * p->M * p->d_v * st_bytes(p));
+    sp[ns++] = span("mass", mass, static_cast<size_t>(p->B) * p->H * p->M * sizeof(float));
+    sp[ns++] = span("y", y, rows * D * 2);
+    if (addr_out) {
+        sp[ns++] = span("addr_out.w_idx", addr_out->w_idx, nK4);
+        sp[ns++] = span("addr_out.w_wt", addr_out->w_wt, nK4);
+        sp[ns++] = span("addr_out.r_idx", addr_out->r_idx, nK4);
+        sp[ns++] = span("addr_out.r_wt", addr_out->r_wt, nK4);
+    }
+    sp[ns++] = span("workspace", ws, f.total);
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+    if ((s = prepare_gemms(p, w, rows, true))) return s;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    const Projected o{wsb + f.o_q, wsb + f.o_k, wsb + f.o_v, wsb + f.o_g, wsb + f.o_gamma};
+    if ((s = enqueue_inputs(p, w, x, rows, o, wsb, f, st))) return s;
+    const bool st16 = p->state_dtype == RAMNET_BF16;
+    void *out = wsb + f.o_out;
+    void *out16 = st16 ? out : wsb + f.o_out16;
+    s = run_layer(p, step, o.q, o.k, o.v, o.gamma, o.g, norm_w, pos, S, mass, out, nullptr,
+                  addr_out, wsb + f.o_layer, f.total - f.o_layer, stream, st16 ? nullptr : out16);
+    if (s) return s;
+    std::string err;
+    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
+    if (!ramnet::gemm_bf16(out16, w->w_o, y, rows, w->d_model, HV, wsb + f.o_gemm, st, err))
+        return fail(RAMNET_EHIP, "%s", err.c_str());
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model) {
+    const std::string saved = g_last_error;
+    ramnet_status s = check_params(p, p && p->T == 1);
+    if (s == RAMNET_OK && (p->in_dtype != RAMNET_BF16 || d_model < 8 || d_model > kMaxDModel ||
+                           d_model % 8))
+        s = RAMNET_EINVAL;
+    g_last_error = saved;
+    if (s != RAMNET_OK) return 0;
+    const FwdPlan a = plan_forward(p, d_model, false);
+    if (p->T != 1) return a.total;
+    const FwdPlan b = plan_forward(p, d_model, true);
+    return a.total > b.total ? a.total : b.total;
+}
+
+ramnet_status ramnet_project_inputs(const ramnet_params *p, const ramnet_proj *w, const void *x,
+                                    void *q, void *k, void *v, void *gamma, void *g,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    ramnet_status s = check_params(p, false);
+    if (s || (s = check_proj(p, w))) return s;
+    const int64_t rows = static_cast<int64_t>(p->B) * p->T;
+    const int64_t n = rows * p->H;
+    if (n == 0) return ok();
+    if ((s = check_ptr("x", x, true)) || (s = check_ptr("q", q, true)) ||
+        (s = check_ptr("k", k, true)) || (s = check_ptr("v", v, true)) ||
+        (s = check_ptr("gamma", gamma, true)) || (s = check_ptr("g", g, true)))
+        return s;
+    const FwdPlan f = plan_forward(p, w->d_model, false);
+    // only the tempered weights and the GEMM scratch are used here
+    const size_t need = f.o_q;
+    if (!workspace || workspace_bytes < need)
+        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if ((s = check_ptr("workspace", workspace, true))) return s;
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    Span sp[16];
+    int ns = weight_spans(p, w, false, sp);
+    sp[ns++] = span("x", x, rows * static_cast<size_t>(w->d_model) * 2);
+    const int first_written = ns;
+    sp[ns++] = span("q", q, n * L * 2);
+    sp[ns++] = span("k", k, n * L * 2);
+    sp[ns++] = span("v", v, n * p->d_v * 2);
+    sp[ns++] = span("g", g, n * p->d_v * 2);
+    sp[ns++] = span("gamma", gamma, n * 2);
+    sp[ns++] = span("workspace", workspace, need);
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+    if ((s = prepare_gemms(p, w, rows, false))) return s;
+    return enqueue_inputs(p, w, x, rows, Projected{q, k, v, g, gamma},
+                          static_cast<char *>(workspace), f, static_cast<hipStream_t>(stream));
+}
+
+ramnet_status ramnet_layer_forward(const ramnet_params *p, const ramnet_proj *w, const void *x,
+                                   const float *norm_w, const int32_t *pos0, void *S, float *mass,
+                                   void *y, const ramnet_addr *addr_out, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    return run_whole_layer(p, false, w, x, norm_w, pos0, S, mass, y, addr_out, workspace,
+                           workspace_bytes, stream);
+}
+
+ramnet_status ramnet_layer_step(const ramnet_params *p, const ramnet_proj *w, const void *x,
+                                const float *norm_w, const int32_t *pos, void *S, float *mass,
+                                void *y, const ramnet_addr *addr_out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    return run_whole_layer(p, true, w, x, norm_w, pos, S, mass, y, addr_out, workspace,
+                           workspace_bytes, stream);
+}
+
 
 ramnet_status ramnet_decode_addresses(const ramnet_params *p, const void *q, const void *k,
                                       const int32_t *pos0, const ramnet_addr *out,

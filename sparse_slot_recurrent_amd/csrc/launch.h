@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace ramnet {
 
 // Address Decoder over n = B*T*H addresses of both q (read) and k (write).
@@ -37,6 +39,8 @@ struct ScanArgs {
     void *S;
     float *mass;
     void *out;
+    void *out_bf16;  // chunked path: if set, the normalised output goes here as
+                     // bf16 instead of to out (out still holds r meanwhile)
     float eps_gsu, eps_norm;
 };
 // LDS bytes the serial scan needs to keep one head's state on chip, and
@@ -105,5 +109,19 @@ struct StepArgs {
 };
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
+
+// Dense projections around the layer (proj.hip).
+constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch per call
+// Row-major C[m,n] = A[m,k] B[k,n]: bf16 in and out, fp32 accumulation.
+// Returns false with a message in err.
+bool gemm_bf16(const void *A, const void *B, void *C, int64_t m, int64_t n, int64_t k,
+               void *ws, hipStream_t st, std::string &err);
+// Creates the device's handle and picks the algorithm for a shape, so that
+// a sequence of GEMMs can be validated before any of it is enqueued.
+bool gemm_prepare(int64_t m, int64_t n, int64_t k, std::string &err);
+// w = bf16(e^alpha[h] * wp), column c of a [rows, cols] matrix in head c / L.
+hipError_t launch_temper(const void *wp, const float *alpha, void *w, int64_t rows, int cols,
+                         int L, hipStream_t st);
+hipError_t launch_to_bf16(const float *in, void *out, int64_t n, hipStream_t st);
 
 }  // namespace ramnet

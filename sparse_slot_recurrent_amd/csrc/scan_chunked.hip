@@ -905,9 +905,16 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const int64_t n_mass = units * a.M;
     const int64_t work = std::max<int64_t>(n * (a.d_v / 4), n_mass);
     const unsigned g2 = static_cast<unsigned>((work + 255) / 256);
-    hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf, a.sumsq,
-                       P.ncg, static_cast<const TIn *>(a.g), a.norm_w, static_cast<TS *>(a.out), n,
-                       a.d_v, a.eps_norm, a.mass_ws, P.resident ? 1 : P.ncg, a.mass, n_mass);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((rms_gate_kernel<TIn, bf16_t>), dim3(g2), dim3(256), 0, st, a.rbuf,
+                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.norm_w,
+                           static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm, a.mass_ws,
+                           P.resident ? 1 : P.ncg, a.mass, n_mass);
+    else
+        hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf,
+                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.norm_w,
+                           static_cast<TS *>(a.out), n, a.d_v, a.eps_norm, a.mass_ws,
+                           P.resident ? 1 : P.ncg, a.mass, n_mass);
     return hipGetLastError();
 }
 

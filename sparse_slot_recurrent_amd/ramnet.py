@@ -20,7 +20,9 @@ STATUS = {0: "RAMNET_OK", -1: "RAMNET_EINVAL", -2: "RAMNET_EUNSUPPORTED",
           -3: "RAMNET_EWORKSPACE", -4: "RAMNET_EHIP"}
 EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
             "ramnet_scan_prefill", "ramnet_step_decode", "ramnet_status_str",
-            "ramnet_last_error", "ramnet_version")
+            "ramnet_last_error", "ramnet_version",
+            "ramnet_layer_workspace_bytes", "ramnet_project_inputs",
+            "ramnet_layer_forward", "ramnet_layer_step")
 
 
 class Params(C.Structure):
@@ -35,6 +37,13 @@ class Params(C.Structure):
 class Addr(C.Structure):
     _fields_ = [("w_idx", C.c_void_p), ("w_wt", C.c_void_p),
                 ("r_idx", C.c_void_p), ("r_wt", C.c_void_p)]
+
+
+class Proj(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("w_q", C.c_void_p), ("w_k", C.c_void_p),
+                ("w_v", C.c_void_p), ("w_g", C.c_void_p),
+                ("w_gamma", C.c_void_p), ("w_o", C.c_void_p),
+                ("alpha", C.c_void_p)]
 
 
 class RamnetError(RuntimeError):
@@ -76,6 +85,16 @@ def load_library(path: str = LIB_PATH):
     lib.ramnet_step_decode.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
                                        P, C.c_size_t, P]
     lib.ramnet_step_decode.restype = C.c_int
+    pw = C.POINTER(Proj)
+    lib.ramnet_layer_workspace_bytes.argtypes = [pp, C.c_int32]
+    lib.ramnet_layer_workspace_bytes.restype = C.c_size_t
+    lib.ramnet_project_inputs.argtypes = [pp, pw, P, P, P, P, P, P, P,
+                                          C.c_size_t, P]
+    lib.ramnet_project_inputs.restype = C.c_int
+    for name in ("ramnet_layer_forward", "ramnet_layer_step"):
+        f = getattr(lib, name)
+        f.argtypes = [pp, pw, P, P, P, P, P, P, pa, P, C.c_size_t, P]
+        f.restype = C.c_int
     lib.ramnet_status_str.argtypes = [C.c_int]
     lib.ramnet_status_str.restype = C.c_char_p
     lib.ramnet_last_error.restype = C.c_char_p
@@ -255,3 +274,101 @@ def step_decode(q, k, v, gamma, g, pos, S, mass, *, d_p: int, U: int, K: int,
     ao = new_addresses((B, H, K), v.device) if export_addresses else None
     plan(q, k, v, gamma, g, pos, S, mass, out, norm_w=norm_w, addr_out=ao)
     return (out, ao) if export_addresses else out
+
+
+# ---------------------------------------------------------------- whole layer
+
+class LayerWeights(NamedTuple):
+    """bf16 row-major weights of the projections (include/ramnet.h,
+    ramnet_proj): w_q, w_k [D, H*U*d_p] (W' before the temperature), w_v,
+    w_g [D, H*d_v], w_gamma [D, H], w_o [H*d_v, D]; alpha [H] fp32 or None."""
+    w_q: "object"
+    w_k: "object"
+    w_v: "object"
+    w_g: "object"
+    w_gamma: "object"
+    w_o: "object"
+    alpha: "object" = None
+
+
+def _proj_struct(w: LayerWeights) -> Proj:
+    D = w.w_q.shape[0]
+    ps = [_ptr(t) for t in (w.w_q, w.w_k, w.w_v, w.w_g, w.w_gamma, w.w_o)]
+    return Proj(D, *ps, _ptr(w.alpha))
+
+
+def layer_workspace_bytes(p: Params, d_model: int) -> int:
+    return int(load_library().ramnet_layer_workspace_bytes(C.byref(p), d_model))
+
+
+class LayerPlan:
+    """A whole layer (projections, recurrence, output projection) of one
+    shape with its workspace: prefill for T > 1 calls, a decode step for
+    step=True (T = 1)."""
+
+    def __init__(self, B, T, H, d_p, U, K, d_v, d_model, state_dtype, cape=1,
+                 eps_gsu=1e-6, eps_norm=1e-6, device="cuda", content_heads=0,
+                 step=False):
+        torch = _torch()
+        self.step = step
+        if isinstance(state_dtype, torch.dtype):
+            state_dtype = BF16 if state_dtype == torch.bfloat16 else F32
+        self.p = make_params(B, 1 if step else T, H, d_p, U, K, d_v, BF16,
+                             state_dtype, cape, eps_gsu, eps_norm,
+                             content_heads=content_heads)
+        self.d_model = d_model
+        nbytes = layer_workspace_bytes(self.p, d_model)
+        if nbytes == 0:
+            raise ValueError("invalid layer parameters")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.ws_bytes = nbytes
+
+    def __call__(self, w: LayerWeights, x, S, mass, y, *, norm_w=None,
+                 pos=None, addr_out: Optional[Addresses] = None):
+        """x, y [B,T,D] (a step: [B,D]) bf16; pos = pos0 [B] for prefill,
+        the token positions [B] for a step."""
+        ws = _proj_struct(w)
+        ao = _addr_struct(addr_out)
+        f = (load_library().ramnet_layer_step if self.step
+             else load_library().ramnet_layer_forward)
+        _raise(f(C.byref(self.p), C.byref(ws), _ptr(x), _ptr(norm_w),
+                 _ptr(pos), _ptr(S), _ptr(mass), _ptr(y),
+                 C.byref(ao) if ao is not None else None,
+                 C.c_void_p(self.workspace.data_ptr()), self.ws_bytes,
+                 _stream()))
+        return y
+
+    def project_inputs(self, w: LayerWeights, x):
+        """The five bf16 projections of x as the layer computes them:
+        q, k [B,T,H,U*d_p], v, g [B,T,H,d_v], gamma [B,T,H]."""
+        torch = _torch()
+        p = self.p
+        B, T, H = p.B, p.T, p.H
+        L = p.U * p.d_p
+        mk = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=x.device)
+        q, k = mk(B, T, H, L), mk(B, T, H, L)
+        v, g, gamma = mk(B, T, H, p.d_v), mk(B, T, H, p.d_v), mk(B, T, H)
+        ws = _proj_struct(w)
+        _raise(load_library().ramnet_project_inputs(
+            C.byref(p), C.byref(ws), _ptr(x), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(gamma), _ptr(g), C.c_void_p(self.workspace.data_ptr()),
+            self.ws_bytes, _stream()))
+        return {"q": q, "k": k, "v": v, "g": g, "gamma": gamma}
+
+
+def layer_forward(w: LayerWeights, x, S, mass, *, d_p: int, U: int, K: int,
+                  cape: int = 1, norm_w=None, pos0=None, eps_gsu=1e-6,
+                  eps_norm=1e-6, export_addresses: bool = False,
+                  content_heads: int = 0):
+    """x [B,T,D] bf16 -> y [B,T,D] bf16 through the whole layer; S and mass
+    updated in place (and the addresses used when export_addresses)."""
+    torch = _torch()
+    B, T, D = x.shape
+    H = w.w_gamma.shape[1]
+    d_v = w.w_v.shape[1] // H
+    plan = LayerPlan(B, T, H, d_p, U, K, d_v, D, _dt(S), cape, eps_gsu,
+                     eps_norm, device=x.device, content_heads=content_heads)
+    y = torch.empty_like(x)
+    ao = new_addresses((B, T, H, K), x.device) if export_addresses else None
+    plan(w, x, S, mass, y, norm_w=norm_w, pos=pos0, addr_out=ao)
+    return (y, ao) if export_addresses else y

@@ -169,3 +169,65 @@ def make_decode_step(w: Workload, step: int, B: Optional[int] = None,
         "gamma": _store(normal((B, H)), w.in_dtype),
         "g": _store(normal((B, H, dv)), w.in_dtype),
     }
+
+
+# ---------------------------------------------------------------- whole layer
+#
+# Token activations and projection weights for a layer with its dense
+# projections.  Two kinds:
+#   grid  x = i/8 with i uniform on [-8, 8]; weights = j * 2^-e with j uniform
+#         on [-8, 8] and 2^-e the power of two that puts the projected logits
+#         near the workload's sigma (values near 1).  Every dot product is a
+#         short sum of dyadic numbers, exact in fp32 in any order.
+#   gauss x ~ N(0, 1), weights ~ N(0, sigma^2 / d_model), both bf16.
+# alpha: "pow2" draws alpha_h from {0, fp32(ln 2), -fp32(ln 2)}, whose e^alpha
+# round to 1, 2 and 1/2 in fp32; "general" draws alpha_h ~ U(-1, 1); None
+# leaves it out.
+# Draw order (PCG64([seed, 17])): x, w_q, w_k, w_v, w_g, w_gamma, w_o, alpha.
+
+LN2_F32 = float(np.float32(np.log(2.0)))
+
+
+def make_layer_weights(w: Workload, d_model: int, seed: Optional[int] = None,
+                       B: Optional[int] = None, T: Optional[int] = None,
+                       H: Optional[int] = None, kind: str = "grid",
+                       alpha: Optional[str] = "pow2") -> Dict[str, np.ndarray]:
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    H = w.H if H is None else H
+    rng = np.random.Generator(np.random.PCG64([w.seed if seed is None else seed, 17]))
+    L, dv, D = w.L, w.d_v, d_model
+
+    if kind == "grid":
+        def step(sigma):  # std of i/8 * j * s is about 3 s per term
+            return 2.0 ** np.round(np.log2(sigma / (3.0 * np.sqrt(D))))
+
+        def mat(shape, sigma):
+            return (rng.integers(-8, 9, size=shape) * step(sigma)).astype(np.float32)
+        x = (rng.integers(-8, 9, size=(B, T, D)) / 8.0).astype(np.float32)
+    elif kind == "gauss":
+        def mat(shape, sigma):
+            return round_bf16(rng.standard_normal(size=shape, dtype=np.float32)
+                              * np.float32(sigma / np.sqrt(D)))
+        x = round_bf16(rng.standard_normal(size=(B, T, D), dtype=np.float32))
+    else:
+        raise ValueError(kind)
+    out = {"x": x,
+           "w_q": mat((D, H * L), w.logit_sigma),
+           "w_k": mat((D, H * L), w.logit_sigma),
+           "w_v": mat((D, H * dv), 1.0),
+           "w_g": mat((D, H * dv), 1.0),
+           "w_gamma": mat((D, H), 1.0)}
+    if kind == "grid":
+        out["w_o"] = (rng.integers(-8, 9, size=(H * dv, D))
+                      * 2.0 ** np.round(np.log2(1.0 / (3.0 * np.sqrt(H * dv))))).astype(np.float32)
+    else:
+        out["w_o"] = round_bf16(rng.standard_normal(size=(H * dv, D), dtype=np.float32)
+                                * np.float32(1.0 / np.sqrt(H * dv)))
+    if alpha == "pow2":
+        out["alpha"] = (rng.integers(-1, 2, size=H) * LN2_F32).astype(np.float32)
+    elif alpha == "general":
+        out["alpha"] = rng.uniform(-1.0, 1.0, size=H).astype(np.float32)
+    elif alpha is not None:
+        raise ValueError(alpha)
+    return out

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(rn):
 
 def test_version_and_status_strings(rn):
     lib = rn.load_library()
-    assert lib.ramnet_version() == 2
+    assert lib.ramnet_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert lib.ramnet_status_str(code).decode() != "unknown status"
 
@@ -180,3 +180,61 @@ def test_product_path_has_no_cpu_fallback():
     with pytest.raises(RuntimeError, match="missing"):
         mod._lib = None
         mod.load_library(os.path.join(ROOT, "does_not_exist.so"))
+
+
+def call_forward(rn, p, d_model=256, ws_bytes=None, **kw):
+    lib = rn.load_library()
+    w = rn.Proj(d_model, *[FAKE + ((20 + i) << 32) for i in range(6)], None)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    need = rn.layer_workspace_bytes(p, d_model)
+    ws = FAKE + (40 << 32)
+    st = lib.ramnet_layer_forward(C.byref(p), C.byref(w), C.c_void_p(FAKE),
+                                  None, None, C.c_void_p(FAKE + (5 << 32)),
+                                  C.c_void_p(FAKE + (6 << 32)),
+                                  C.c_void_p(FAKE + (7 << 32)), None,
+                                  C.c_void_p(ws), need if ws_bytes is None else ws_bytes,
+                                  None)
+    return st, lib.ramnet_last_error().decode()
+
+
+def test_layer_workspace_query(rn):
+    p = good(rn)
+    big = rn.layer_workspace_bytes(p, 1024)
+    assert big > rn.layer_workspace_bytes(p, 256) > rn.workspace_bytes(p, rn.OP_PREFILL)
+    assert rn.layer_workspace_bytes(p, 12) == 0           # not a multiple of 8
+    assert rn.layer_workspace_bytes(good(rn, in_dtype=rn.F32), 256) == 0
+    step = good(rn, T=1)
+    assert rn.layer_workspace_bytes(step, 256) > 0
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(d_model=12), -1, "d_model"),
+    (dict(d_model=0), -1, "d_model"),
+    (dict(w_o=None), -1, "w_o is NULL"),
+    (dict(w_q=FAKE + 8), -1, "w_q is not 16-byte aligned"),
+    (dict(ws_bytes=1000), -3, "workspace"),
+])
+def test_layer_forward_bad_arguments(rn, kw, code, msg):
+    p = good(rn)
+    st, err = call_forward(rn, p, **kw)
+    assert st == code, err
+    assert msg in err
+
+
+def test_layer_forward_needs_bf16_inputs(rn):
+    st, err = call_forward(rn, good(rn, in_dtype=rn.F32))
+    assert st == -2 and "in_dtype" in err
+
+
+def test_layer_forward_rejects_overlaps(rn):
+    p = good(rn)
+    # y on top of a weight
+    lib = rn.load_library()
+    w = rn.Proj(256, *[FAKE + ((20 + i) << 32) for i in range(6)], None)
+    need = rn.layer_workspace_bytes(p, 256)
+    st = lib.ramnet_layer_forward(C.byref(p), C.byref(w), C.c_void_p(FAKE), None, None,
+                                  C.c_void_p(FAKE + (5 << 32)), C.c_void_p(FAKE + (6 << 32)),
+                                  C.c_void_p(FAKE + (21 << 32) + 256), None,
+                                  C.c_void_p(FAKE + (40 << 32)), need, None)
+    assert st == -1 and "overlaps" in lib.ramnet_last_error().decode()
