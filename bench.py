@@ -8,7 +8,9 @@ B x T x H token-heads); for the decode workload, one ramnet_step_decode call
 before the timed region.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload prefill_top8|prefill_top32|large_state|decode]
+                       [--workload prefill_top8|prefill_top32|large_state|decode
+                                   |layer_top8|layer_decode]
+The layer_* workloads add the dense projections either side (the whole layer).
 """
 from __future__ import annotations
 
@@ -295,6 +297,113 @@ def bench_decode(torch, rn, w, steps, warmup):
     return ms_graph, {"step_fused": ms_graph}, w.B, {"ms_per_step_eager": ms_eager}
 
 
+# Whole-layer workloads: a configuration's recurrence with its dense
+# projections, at a model width chosen for that configuration (d_model 1024
+# for the 340M-like layer; 2048 = H*d_v for the 16-head decode layer).
+LAYERS = {"layer_top8": ("prefill_top8", 1024), "layer_decode": ("decode", 2048)}
+
+
+def layer_model(w, D, kind: str):
+    """Algorithmic flops and bytes of the two projection stages (bf16
+    operands and results; x read once, weights read once)."""
+    T = 1 if kind == "decode" else w.T
+    rows = w.B * T
+    n_in = w.H * (2 * w.L + 2 * w.d_v + 1)
+    hv = w.H * w.d_v
+    return {
+        "project_inputs_flop": 2 * rows * D * n_in,
+        "project_inputs_bytes": 2 * (rows * D + D * n_in + rows * n_in),
+        "project_output_flop": 2 * rows * hv * D,
+        "project_output_bytes": 2 * (rows * hv + hv * D + rows * D),
+    }
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_layer(torch, rn, w, D, steps, warmup):
+    """A whole layer: ramnet_layer_forward (prefill) or ramnet_layer_step
+    (1024 dependent steps in one HIP graph).  Per-stage times: the input
+    projections alone, the recurrence alone on projected inputs, and the
+    output projection as the remainder."""
+    from sparse_slot_recurrent_amd import synth
+    decode = bool(w.steps)
+    T = 1 if decode else w.T
+    wd = synth.make_layer_weights(w, D, T=1, kind="gauss", alpha="general")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    W = rn.LayerWeights(bf(wd["w_q"]), bf(wd["w_k"]), bf(wd["w_v"]), bf(wd["w_g"]),
+                        bf(wd["w_gamma"]), bf(wd["w_o"]), torch.from_numpy(wd["alpha"]).cuda())
+    st = synth.make_inputs(w, T=1)
+    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    S = torch.from_numpy(st["S0"]).to(sdt).cuda()
+    mass = torch.from_numpy(st["m0"]).cuda()
+    pos0 = torch.from_numpy(st["pos0"]).cuda()
+    del st
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    plan = rn.LayerPlan(w.B, T, w.H, w.d_p, w.U, w.K, w.d_v, D, sdt, cape=w.cape,
+                        eps_gsu=w.eps_gsu, eps_norm=w.eps_norm, step=decode)
+    if decode:
+        xs = torch.randn(steps, w.B, D, generator=gen, device="cuda").to(torch.bfloat16)
+        pos = (pos0[None, :] + torch.arange(steps, device="cuda", dtype=torch.int32)[:, None]).contiguous()
+        y = torch.empty((w.B, D), dtype=torch.bfloat16, device="cuda")
+
+        def step(i):
+            plan(W, xs[i], S, mass, y, pos=pos[i])
+        for i in range(min(warmup, steps)):
+            step(i)
+        torch.cuda.synchronize()
+        ms_eager = time_loop(torch, step, steps)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / (3 * steps)
+        return ms, {"layer_step": ms}, w.B, {"ms_per_step_eager": ms_eager}
+    x = torch.randn(w.B, T, D, generator=gen, device="cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    inp = plan.project_inputs(W, x)
+    pre = rn.PrefillPlan(w.B, T, w.H, w.d_p, w.U, w.K, w.d_v, rn.BF16,
+                         rn.BF16 if sdt == torch.bfloat16 else rn.F32, cape=w.cape,
+                         eps_gsu=w.eps_gsu, eps_norm=w.eps_norm)
+    out = torch.empty((w.B, T, w.H, w.d_v), dtype=sdt, device="cuda")
+
+    def step(_):
+        plan(W, x, S, mass, y, pos=pos0)
+
+    def proj(_):
+        plan.project_inputs(W, x)
+
+    def rec(_):
+        pre(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["g"], S, mass, out, pos0=pos0)
+    for _ in range(warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps)
+    proj(0)
+    ms_proj = time_loop(torch, proj, steps)
+    rec(0)
+    ms_rec = time_loop(torch, rec, steps)
+    torch.cuda.synchronize()
+    kms = {"project_inputs": ms_proj, "recurrence": ms_rec,
+           "project_output_and_rest": max(ms - ms_proj - ms_rec, 0.0)}
+    return ms, kms, w.B * T, {}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,7 +427,12 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    w = synth.WORKLOADS[args.workload]
+    d_model = None
+    if args.workload in LAYERS:
+        base, d_model = LAYERS[args.workload]
+        w = synth.WORKLOADS[base]
+    else:
+        w = synth.WORKLOADS[args.workload]
     kind = "decode" if w.steps else "prefill"
     steps = args.steps or (w.steps if kind == "decode" else 10)
     warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
@@ -332,14 +446,46 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     extra = {}
-    if kind == "decode":
+    if d_model is not None:
+        ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
+    elif kind == "decode":
         ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)
     else:
         ms, kms, tokens = bench_prefill(torch, rn, w, steps, warmup)
     value = tokens / (ms / 1e3)
     bm = byte_model(w, kind)
     dom = max(kms, key=kms.get)
-    achieved = bm[dom] / (kms[dom] / 1e3) / 1e9
+    roof = None
+    if d_model is not None:
+        lm = layer_model(w, d_model, kind)
+        extra["layer_model"] = lm
+        extra["d_model"] = d_model
+        if "project_inputs" in kms:
+            tf = lm["project_inputs_flop"] / (kms["project_inputs"] / 1e3) / 1e12
+            extra["project_inputs_tflops"] = tf
+            rec = bm["total"] / (kms["recurrence"] / 1e3) / 1e9
+            extra["recurrence_gbs"] = rec
+            if dom == "project_inputs":
+                roof = {"bound": "mfma", "kernel": dom, "achieved": tf,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+            elif dom == "recurrence":
+                roof = {"bound": "hbm", "kernel": dom, "achieved": rec,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": rec / HBM_PEAK_GBS, "traffic": None}
+        if roof is None:
+            # one graph-replayed step: the whole layer's bytes (recurrence
+            # plus both projections) over the step time
+            by = bm["total"] + lm["project_inputs_bytes"] + lm["project_output_bytes"]
+            a = by / (ms / 1e3) / 1e9
+            roof = {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None}
+    else:
+        achieved = bm[dom] / (kms[dom] / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": measured_traffic(w.name, dom)}
     line = {
         "metric": METRIC,
         "value": value,
@@ -351,23 +497,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16+f32" if d_model else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": 1 if kind == "decode" else w.T,
+        "config": {"workload": args.workload, "B": w.B, "T": 1 if kind == "decode" else w.T,
                    "H": w.H, "M": w.M, "d_p": w.d_p, "U": w.U, "K": w.K,
                    "d_v": w.d_v, "in_dtype": w.in_dtype,
                    "state_dtype": w.state_dtype, "cape": w.cape,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, dom)},
+        "roofline": roof,
         "kernels_ms": kms,
         "algorithmic_bytes": bm,
         "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
     line.update(extra)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and d_model is None:
         line["cpu_baseline"] = cpu_baseline(w, kind)
     print(json.dumps(line), flush=True)
 
