@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RAMNET_VERSION 3
+#define RAMNET_VERSION 4
 /* Largest supported K (Top-K per address). */
 #define RAMNET_KMAX 64
 
@@ -180,23 +180,44 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
  * as W = e^alpha * W' per head (paper digest, stability of the decoder: alpha
  * sets the temperature of the Product Softmax).
  *
- * All weights are bf16, row-major [rows, cols], d_model = D:
- *   w_q, w_k   [D, H*U*d_p]  W' of the query / key logits; column h*U*d_p + j
- *              is logit j of head h.  The GEMM uses W = bf16(t_h * W'), with
- *              t_h = fp32(e^alpha[h]), rounded once from the exact product.
- *   w_v, w_g   [D, H*d_v]    values and output-gate logits (column h*d_v + c)
- *   w_gamma    [D, H]        the GSU's gamma, one per head
- *   w_o        [H*d_v, D]    output projection of the layer output
+ * All weights are bf16, [out, in] row-major (one output's weights contiguous
+ * over its inputs, as a linear layer y = x W^T stores them), d_model = D:
+ *   w_q, w_k   [H*U*d_p, D]  W' of the query / key logits; row h*U*d_p + j
+ *              gives logit j of head h.  The GEMM uses W = bf16(t_h * W'),
+ *              with t_h = fp32(e^alpha[h]), rounded once from the exact
+ *              product.
+ *   w_v, w_g   [H*d_v, D]    values and output-gate logits (row h*d_v + c)
+ *   w_gamma    [H, D]        the GSU's gamma, one per head
+ *   w_o        [D, H*d_v]    output projection of the layer output
  *   alpha      [H] fp32 or NULL (= 0, W = W')
- * Each product is accumulated in fp32 and rounded to bf16 (hipBLASLt on the
- * matrix cores); the layer output is rounded to bf16 before w_o.  p->in_dtype
- * must be RAMNET_BF16 (q, k, v, gamma, g are the bf16 projections).
+ *   w_in_packed  NULL, or the five input weights packed by
+ *              ramnet_pack_weights (then w_q .. w_gamma and alpha are not
+ *              read).  Packing once saves re-packing on every call, which
+ *              matters for decoding steps.
+ * The five input projections are one GEMM against the packed [N, D] matrix
+ * (rows: q, k, v, g, gamma; each block starts at a multiple of 8 rows, zero
+ * padding between); the layer reads its inputs in place from the packed
+ * result [B*T, N].  Each product is accumulated in fp32 and rounded to bf16
+ * (hipBLASLt on the matrix cores); the layer output is rounded to bf16
+ * before w_o.  p->in_dtype must be RAMNET_BF16 (q, k, v, gamma, g are the
+ * bf16 projections).
  */
 typedef struct {
     int32_t d_model;
     const void *w_q, *w_k, *w_v, *w_g, *w_gamma, *w_o;
     const float *alpha;
+    const void *w_in_packed;
 } ramnet_proj;
+
+/* Bytes of the packed input weights for `p` and d_model (0 if invalid). */
+size_t ramnet_packed_weights_bytes(const ramnet_params *p, int32_t d_model);
+
+/* Packs w->w_q, w_k (as W = bf16(t_h * W')), w_v, w_g, w_gamma into
+ * `packed` (ramnet_packed_weights_bytes bytes, bf16 [N, d_model]).  w->w_o
+ * and w->w_in_packed are not read. */
+ramnet_status ramnet_pack_weights(const ramnet_params *p, const ramnet_proj *w,
+                                  void *packed, size_t packed_bytes,
+                                  void *stream);
 
 /* Workspace bytes of ramnet_layer_forward / ramnet_layer_step /
  * ramnet_project_inputs for `p` and d_model (0 if either is invalid). */

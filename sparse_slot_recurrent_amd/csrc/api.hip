@@ -177,12 +177,28 @@ ramnet::DecodeArgs decode_args(const ramnet_params *p, const void *q, const void
     return d;
 }
 
+// Elements between consecutive tokens (b, t) of each layer input; 0 means
+// the contiguous layout of the public entry points.  The whole-layer path
+// reads all five from one packed projection buffer.
+struct Strides {
+    int64_t qk = 0, v = 0, g = 0, gamma = 0;
+};
+
+// Bytes a [B*T rows] input with `width` elements per head spans.
+size_t in_span(const ramnet_params *p, int64_t ld, size_t width) {
+    const size_t rows = static_cast<size_t>(p->B) * p->T;
+    const size_t hw = static_cast<size_t>(p->H) * width;
+    if (!ld) return rows * hw * in_bytes(p);
+    return ((rows - 1) * static_cast<size_t>(ld) + hw) * in_bytes(p);
+}
+
 // Shared body of prefill (T tokens) and the decode step (T = 1).
 ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const void *k,
                         const void *v, const void *gamma, const void *g, const float *norm_w,
                         const int32_t *pos, void *S, float *mass, void *out,
                         const ramnet_addr *addr_in, const ramnet_addr *addr_out, void *ws,
-                        size_t ws_bytes, void *stream, void *out_bf16 = nullptr) {
+                        size_t ws_bytes, void *stream, void *out_bf16 = nullptr,
+                        const Strides &sd = Strides{}) {
     ramnet_status s = check_params(p, step);
     if (s) return s;
     const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
@@ -209,8 +225,8 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     int ns = 0;
     // read-only buffers first
     if (decode) {
-        sp[ns++] = span("q", q, n * L * in_bytes(p));
-        sp[ns++] = span("k", k, n * L * in_bytes(p));
+        sp[ns++] = span("q", q, in_span(p, sd.qk, L));
+        sp[ns++] = span("k", k, in_span(p, sd.qk, L));
         if (pos) sp[ns++] = span(step ? "pos" : "pos0", pos, p->B * sizeof(int32_t));
     } else {
         sp[ns++] = span("addr_in.w_idx", addr_in->w_idx, nK4);
@@ -218,9 +234,9 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sp[ns++] = span("addr_in.r_idx", addr_in->r_idx, nK4);
         sp[ns++] = span("addr_in.r_wt", addr_in->r_wt, nK4);
     }
-    sp[ns++] = span("v", v, n * p->d_v * in_bytes(p));
-    sp[ns++] = span("gamma", gamma, n * in_bytes(p));
-    sp[ns++] = span("g", g, n * p->d_v * in_bytes(p));
+    sp[ns++] = span("v", v, in_span(p, sd.v, p->d_v));
+    sp[ns++] = span("gamma", gamma, in_span(p, sd.gamma, 1));
+    sp[ns++] = span("g", g, in_span(p, sd.g, p->d_v));
     if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
     const int first_written = ns;
     sp[ns++] = span("S", S, units * p->M * p->d_v * st_bytes(p));
@@ -273,6 +289,10 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sa.out_wt[1] = addr_out ? addr_out->r_wt : nullptr;
         sa.eps_gsu = p->eps_gsu;
         sa.eps_norm = p->eps_norm;
+        sa.ld_qk = sd.qk;
+        sa.ld_v = sd.v;
+        sa.ld_g = sd.g;
+        sa.ld_gamma = sd.gamma;
         hipError_t e = ramnet::launch_step_fused(sa, st);
         if (e == hipSuccess && out_bf16)
             e = ramnet::launch_to_bf16(static_cast<const float *>(out), out_bf16, n * p->d_v, st);
@@ -286,6 +306,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         addr = lp.addr_bytes ? carve_addr(ws, n, p->K) : *addr_out;
         ramnet::DecodeArgs da = decode_args(p, q, k, pos, n, p->T, addr);
         unit_major = da.unit_major = lp.addr_bytes && lp.chunked;
+        da.ld = sd.qk;
         hipError_t e = ramnet::launch_decode(da, st);
         if (e != hipSuccess) return hip_status(e, "address decoder launch");
     } else {
@@ -314,6 +335,9 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
     a.out = out;
     a.eps_gsu = p->eps_gsu;
     a.eps_norm = p->eps_norm;
+    a.ld_v = sd.v;
+    a.ld_g = sd.g;
+    a.ld_gamma = sd.gamma;
     hipError_t e;
     if (lp.chunked) {
         ramnet::ChunkArgs c{};
@@ -358,27 +382,27 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
 
 // ---------------------------------------------------------------- whole layer
 
-// Workspace of the projected layer: tempered address weights, hipBLASLt
-// scratch, the projected inputs, the layer output (and its bf16 copy when
-// the state is fp32), then the layer's own workspace.
+ramnet::PackLayout layout_of(const ramnet_params *p, int32_t d_model) {
+    return ramnet::pack_layout(p->H, p->U * p->d_p, p->d_v, d_model);
+}
+
+// Workspace of the projected layer: the packed input weights (unless the
+// caller packed them), hipBLASLt scratch, the packed projections [rows, N],
+// the layer output (and its bf16 copy when the state is fp32), then the
+// layer's own workspace.
 struct FwdPlan {
-    size_t o_wq, o_wk, o_gemm, o_q, o_k, o_v, o_g, o_gamma, o_out, o_out16, o_layer, total;
+    size_t o_pack, o_gemm, o_proj, o_out, o_out16, o_layer, total;
 };
 
 FwdPlan plan_forward(const ramnet_params *p, int32_t d_model, bool step) {
     FwdPlan f{};
-    const size_t n = static_cast<size_t>(p->B) * p->T * p->H;
-    const size_t L = static_cast<size_t>(p->U) * p->d_p;
-    const size_t HL = static_cast<size_t>(p->H) * L;
+    const ramnet::PackLayout pl = layout_of(p, d_model);
+    const size_t rows = static_cast<size_t>(p->B) * p->T;
+    const size_t n = rows * p->H;
     size_t o = 0;
-    f.o_wq = o; o += align256(static_cast<size_t>(d_model) * HL * 2);
-    f.o_wk = o; o += align256(static_cast<size_t>(d_model) * HL * 2);
+    f.o_pack = o; o += align256(static_cast<size_t>(pl.D) * pl.N * 2);
     f.o_gemm = o; o += ramnet::kGemmWorkspace;
-    f.o_q = o; o += align256(n * L * 2);
-    f.o_k = o; o += align256(n * L * 2);
-    f.o_v = o; o += align256(n * p->d_v * 2);
-    f.o_g = o; o += align256(n * p->d_v * 2);
-    f.o_gamma = o; o += align256(n * 2);
+    f.o_proj = o; o += align256(rows * pl.N * 2);
     f.o_out = o; o += align256(n * p->d_v * st_bytes(p));
     f.o_out16 = o; o += p->state_dtype == RAMNET_BF16 ? 0 : align256(n * p->d_v * 2);
     f.o_layer = o; o += plan_layer(p, step, true).total();
@@ -388,88 +412,91 @@ FwdPlan plan_forward(const ramnet_params *p, int32_t d_model, bool step) {
 
 constexpr int32_t kMaxDModel = 1 << 16;
 
-ramnet_status check_proj(const ramnet_params *p, const ramnet_proj *w) {
-    if (!w) return fail(RAMNET_EINVAL, "w is NULL");
+ramnet_status check_d_model(const ramnet_params *p, int32_t d_model) {
     if (p->in_dtype != RAMNET_BF16)
         return fail(RAMNET_EUNSUPPORTED, "the projections need in_dtype = RAMNET_BF16");
-    if (w->d_model < 8 || w->d_model > kMaxDModel || w->d_model % 8)
-        return fail(RAMNET_EINVAL, "d_model = %d: must be a multiple of 8 in [8, %d]", w->d_model,
+    if (d_model < 8 || d_model > kMaxDModel || d_model % 8)
+        return fail(RAMNET_EINVAL, "d_model = %d: must be a multiple of 8 in [8, %d]", d_model,
                     kMaxDModel);
+    return RAMNET_OK;
+}
+
+// The separate input weights (needed unless a packed matrix is given).
+ramnet_status check_input_weights(const ramnet_proj *w) {
     ramnet_status s;
     if ((s = check_ptr("w_q", w->w_q, true)) || (s = check_ptr("w_k", w->w_k, true)) ||
         (s = check_ptr("w_v", w->w_v, true)) || (s = check_ptr("w_g", w->w_g, true)) ||
-        (s = check_ptr("w_gamma", w->w_gamma, true)) || (s = check_ptr("w_o", w->w_o, true)) ||
-        (s = check_ptr("alpha", w->alpha, false)))
+        (s = check_ptr("w_gamma", w->w_gamma, true)) || (s = check_ptr("alpha", w->alpha, false)))
         return s;
     return RAMNET_OK;
 }
 
-// Read-only spans of the weights.
-int weight_spans(const ramnet_params *p, const ramnet_proj *w, bool with_o, Span *sp) {
-    const size_t D = w->d_model;
-    const size_t HL = static_cast<size_t>(p->H) * p->U * p->d_p;
-    const size_t HV = static_cast<size_t>(p->H) * p->d_v;
-    int ns = 0;
-    sp[ns++] = span("w_q", w->w_q, D * HL * 2);
-    sp[ns++] = span("w_k", w->w_k, D * HL * 2);
-    sp[ns++] = span("w_v", w->w_v, D * HV * 2);
-    sp[ns++] = span("w_g", w->w_g, D * HV * 2);
-    sp[ns++] = span("w_gamma", w->w_gamma, D * p->H * 2);
-    if (with_o) sp[ns++] = span("w_o", w->w_o, HV * D * 2);
-    if (w->alpha) sp[ns++] = span("alpha", w->alpha, p->H * sizeof(float));
-    return ns;
+ramnet_status check_proj(const ramnet_params *p, const ramnet_proj *w, bool need_o) {
+    if (!w) return fail(RAMNET_EINVAL, "w is NULL");
+    ramnet_status s;
+    if ((s = check_d_model(p, w->d_model))) return s;
+    if (w->w_in_packed) {
+        if ((s = check_ptr("w_in_packed", w->w_in_packed, true))) return s;
+    } else if ((s = check_input_weights(w))) {
+        return s;
+    }
+    if (need_o && (s = check_ptr("w_o", w->w_o, true))) return s;
+    return RAMNET_OK;
 }
 
-struct Projected {
-    void *q, *k, *v, *g, *gamma;
-};
+// Read-only spans of the weights a call uses.
+int weight_spans(const ramnet_params *p, const ramnet_proj *w, bool with_o, Span *sp) {
+    const size_t D = w->d_model;
+    const ramnet::PackLayout pl = layout_of(p, w->d_model);
+    int ns = 0;
+    if (w->w_in_packed) {
+        sp[ns++] = span("w_in_packed", w->w_in_packed, D * pl.N * 2);
+    } else {
+        sp[ns++] = span("w_q", w->w_q, D * pl.HL * 2);
+        sp[ns++] = span("w_k", w->w_k, D * pl.HL * 2);
+        sp[ns++] = span("w_v", w->w_v, D * pl.HV * 2);
+        sp[ns++] = span("w_g", w->w_g, D * pl.HV * 2);
+        sp[ns++] = span("w_gamma", w->w_gamma, D * p->H * 2);
+        if (w->alpha) sp[ns++] = span("alpha", w->alpha, p->H * sizeof(float));
+    }
+    if (with_o) sp[ns++] = span("w_o", w->w_o, static_cast<size_t>(pl.HV) * D * 2);
+    return ns;
+}
 
 // Validates every GEMM shape of the call (creating the handle), so that a
 // failure is reported before anything is enqueued.
 ramnet_status prepare_gemms(const ramnet_params *p, const ramnet_proj *w, int64_t rows,
                             bool with_o) {
-    const int64_t HL = static_cast<int64_t>(p->H) * p->U * p->d_p;
-    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
-    const int64_t shapes[4][3] = {{rows, HL, w->d_model}, {rows, HV, w->d_model},
-                                  {rows, p->H, w->d_model}, {rows, w->d_model, HV}};
+    const ramnet::PackLayout pl = layout_of(p, w->d_model);
     std::string err;
-    for (int i = 0; i < (with_o ? 4 : 3); ++i)
-        if (!ramnet::gemm_prepare(shapes[i][0], shapes[i][1], shapes[i][2], err))
-            return fail(RAMNET_EHIP, "%s", err.c_str());
-    return RAMNET_OK;
-}
-
-// Enqueues the tempered weights and the five input GEMMs.
-ramnet_status enqueue_inputs(const ramnet_params *p, const ramnet_proj *w, const void *x,
-                             int64_t rows, const Projected &o, char *ws, const FwdPlan &f,
-                             hipStream_t st) {
-    const int64_t D = w->d_model;
-    const int L = p->U * p->d_p;
-    const int64_t HL = static_cast<int64_t>(p->H) * L;
-    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
-    const void *wq = w->w_q, *wk = w->w_k;
-    if (w->alpha) {
-        hipError_t e = ramnet::launch_temper(w->w_q, w->alpha, ws + f.o_wq, D, static_cast<int>(HL), L, st);
-        if (e == hipSuccess)
-            e = ramnet::launch_temper(w->w_k, w->alpha, ws + f.o_wk, D, static_cast<int>(HL), L, st);
-        if (e != hipSuccess) return hip_status(e, "address weight launch");
-        wq = ws + f.o_wq;
-        wk = ws + f.o_wk;
-    }
-    void *gw = ws + f.o_gemm;
-    std::string err;
-    if (!ramnet::gemm_bf16(x, wq, o.q, rows, HL, D, gw, st, err) ||
-        !ramnet::gemm_bf16(x, wk, o.k, rows, HL, D, gw, st, err) ||
-        !ramnet::gemm_bf16(x, w->w_v, o.v, rows, HV, D, gw, st, err) ||
-        !ramnet::gemm_bf16(x, w->w_g, o.g, rows, HV, D, gw, st, err) ||
-        !ramnet::gemm_bf16(x, w->w_gamma, o.gamma, rows, p->H, D, gw, st, err))
+    if (!ramnet::gemm_prepare(rows, pl.N, w->d_model, err) ||
+        (with_o && !ramnet::gemm_prepare(rows, w->d_model, pl.HV, err)))
         return fail(RAMNET_EHIP, "%s", err.c_str());
     return RAMNET_OK;
 }
 
-ramnet_status check_workspace(const FwdPlan &f, void *ws, size_t ws_bytes) {
-    if (!ws || ws_bytes < f.total)
-        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", f.total,
+// Enqueues the packing of the input weights (unless given packed) and the
+// one input GEMM into proj [rows, N].
+ramnet_status enqueue_inputs(const ramnet_params *p, const ramnet_proj *w, const void *x,
+                             int64_t rows, void *proj, char *ws, const FwdPlan &f,
+                             hipStream_t st) {
+    const ramnet::PackLayout pl = layout_of(p, w->d_model);
+    const void *packed = w->w_in_packed;
+    if (!packed) {
+        const hipError_t e = ramnet::launch_pack(w->w_q, w->w_k, w->w_v, w->w_g, w->w_gamma,
+                                                 w->alpha, ws + f.o_pack, pl, st);
+        if (e != hipSuccess) return hip_status(e, "weight packing launch");
+        packed = ws + f.o_pack;
+    }
+    std::string err;
+    if (!ramnet::gemm_bf16(x, packed, proj, rows, pl.N, w->d_model, ws + f.o_gemm, st, err))
+        return fail(RAMNET_EHIP, "%s", err.c_str());
+    return RAMNET_OK;
+}
+
+ramnet_status check_workspace(size_t need, void *ws, size_t ws_bytes) {
+    if (!ws || ws_bytes < need)
+        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     ws ? ws_bytes : size_t(0));
     return check_ptr("workspace", ws, true);
 }
@@ -479,7 +506,7 @@ ramnet_status run_whole_layer(const ramnet_params *p, bool step, const ramnet_pr
                               float *mass, void *y, const ramnet_addr *addr_out, void *ws,
                               size_t ws_bytes, void *stream) {
     ramnet_status s = check_params(p, step);
-    if (s || (s = check_proj(p, w))) return s;
+    if (s || (s = check_proj(p, w, true))) return s;
     const int64_t rows = static_cast<int64_t>(p->B) * p->T;
     const int64_t n = rows * p->H;
     if (n == 0) return ok();
@@ -490,7 +517,7 @@ ramnet_status run_whole_layer(const ramnet_params *p, bool step, const ramnet_pr
         return s;
     if (addr_out && (s = check_addr("addr_out", addr_out))) return s;
     const FwdPlan f = plan_forward(p, w->d_model, step);
-    if ((s = check_workspace(f, ws, ws_bytes))) return s;
+    if ((s = check_workspace(f.total, ws, ws_bytes))) return s;
     const size_t D = w->d_model;
     const size_t nK4 = static_cast<size_t>(n) * p->K * 4;
     Span sp[20];
@@ -514,17 +541,21 @@ ramnet_status run_whole_layer(const ramnet_params *p, bool step, const ramnet_pr
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *wsb = static_cast<char *>(ws);
-    const Projected o{wsb + f.o_q, wsb + f.o_k, wsb + f.o_v, wsb + f.o_g, wsb + f.o_gamma};
-    if ((s = enqueue_inputs(p, w, x, rows, o, wsb, f, st))) return s;
+    char *proj = wsb + f.o_proj;
+    if ((s = enqueue_inputs(p, w, x, rows, proj, wsb, f, st))) return s;
+    // the layer reads its five inputs in place from the packed projections
+    const ramnet::PackLayout pl = layout_of(p, w->d_model);
+    Strides sd;
+    sd.qk = sd.v = sd.g = sd.gamma = pl.N;
     const bool st16 = p->state_dtype == RAMNET_BF16;
     void *out = wsb + f.o_out;
     void *out16 = st16 ? out : wsb + f.o_out16;
-    s = run_layer(p, step, o.q, o.k, o.v, o.gamma, o.g, norm_w, pos, S, mass, out, nullptr,
-                  addr_out, wsb + f.o_layer, f.total - f.o_layer, stream, st16 ? nullptr : out16);
+    s = run_layer(p, step, proj, proj + 2 * pl.o_k, proj + 2 * pl.o_v, proj + 2 * pl.o_gamma,
+                  proj + 2 * pl.o_g, norm_w, pos, S, mass, out, nullptr, addr_out,
+                  wsb + f.o_layer, f.total - f.o_layer, stream, st16 ? nullptr : out16, sd);
     if (s) return s;
     std::string err;
-    const int64_t HV = static_cast<int64_t>(p->H) * p->d_v;
-    if (!ramnet::gemm_bf16(out16, w->w_o, y, rows, w->d_model, HV, wsb + f.o_gemm, st, err))
+    if (!ramnet::gemm_bf16(out16, w->w_o, y, rows, w->d_model, pl.HV, wsb + f.o_gemm, st, err))
         return fail(RAMNET_EHIP, "%s", err.c_str());
     return ok();
 }
@@ -536,9 +567,7 @@ extern "C" {
 size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model) {
     const std::string saved = g_last_error;
     ramnet_status s = check_params(p, p && p->T == 1);
-    if (s == RAMNET_OK && (p->in_dtype != RAMNET_BF16 || d_model < 8 || d_model > kMaxDModel ||
-                           d_model % 8))
-        s = RAMNET_EINVAL;
+    if (s == RAMNET_OK) s = check_d_model(p, d_model);
     g_last_error = saved;
     if (s != RAMNET_OK) return 0;
     const FwdPlan a = plan_forward(p, d_model, false);
@@ -547,11 +576,45 @@ size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model) {
     return a.total > b.total ? a.total : b.total;
 }
 
+size_t ramnet_packed_weights_bytes(const ramnet_params *p, int32_t d_model) {
+    const std::string saved = g_last_error;
+    ramnet_status s = check_params(p, false);
+    if (s == RAMNET_OK) s = check_d_model(p, d_model);
+    g_last_error = saved;
+    if (s != RAMNET_OK) return 0;
+    const ramnet::PackLayout pl = layout_of(p, d_model);
+    return static_cast<size_t>(pl.D) * pl.N * 2;
+}
+
+ramnet_status ramnet_pack_weights(const ramnet_params *p, const ramnet_proj *w, void *packed,
+                                  size_t packed_bytes, void *stream) {
+    ramnet_status s = check_params(p, false);
+    if (s) return s;
+    if (!w) return fail(RAMNET_EINVAL, "w is NULL");
+    if ((s = check_d_model(p, w->d_model)) || (s = check_input_weights(w)) ||
+        (s = check_ptr("packed", packed, true)))
+        return s;
+    const ramnet::PackLayout pl = layout_of(p, w->d_model);
+    const size_t need = static_cast<size_t>(pl.D) * pl.N * 2;
+    if (packed_bytes < need)
+        return fail(RAMNET_EINVAL, "packed needs %zu bytes, %zu given", need, packed_bytes);
+    ramnet_proj wi = *w;
+    wi.w_in_packed = nullptr;
+    Span sp[8];
+    int ns = weight_spans(p, &wi, false, sp);
+    const int first_written = ns;
+    sp[ns++] = span("packed", packed, need);
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+    return hip_status(ramnet::launch_pack(w->w_q, w->w_k, w->w_v, w->w_g, w->w_gamma, w->alpha,
+                                          packed, pl, static_cast<hipStream_t>(stream)),
+                      "weight packing launch");
+}
+
 ramnet_status ramnet_project_inputs(const ramnet_params *p, const ramnet_proj *w, const void *x,
                                     void *q, void *k, void *v, void *gamma, void *g,
                                     void *workspace, size_t workspace_bytes, void *stream) {
     ramnet_status s = check_params(p, false);
-    if (s || (s = check_proj(p, w))) return s;
+    if (s || (s = check_proj(p, w, false))) return s;
     const int64_t rows = static_cast<int64_t>(p->B) * p->T;
     const int64_t n = rows * p->H;
     if (n == 0) return ok();
@@ -560,12 +623,9 @@ ramnet_status ramnet_project_inputs(const ramnet_params *p, const ramnet_proj *w
         (s = check_ptr("gamma", gamma, true)) || (s = check_ptr("g", g, true)))
         return s;
     const FwdPlan f = plan_forward(p, w->d_model, false);
-    // only the tempered weights and the GEMM scratch are used here
-    const size_t need = f.o_q;
-    if (!workspace || workspace_bytes < need)
-        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : size_t(0));
-    if ((s = check_ptr("workspace", workspace, true))) return s;
+    // the packed weights, the GEMM scratch and the packed projections
+    const size_t need = f.o_out;
+    if ((s = check_workspace(need, workspace, workspace_bytes))) return s;
     const size_t L = static_cast<size_t>(p->U) * p->d_p;
     Span sp[16];
     int ns = weight_spans(p, w, false, sp);
@@ -579,8 +639,12 @@ ramnet_status ramnet_project_inputs(const ramnet_params *p, const ramnet_proj *w
     sp[ns++] = span("workspace", workspace, need);
     if ((s = check_overlaps(sp, ns, first_written))) return s;
     if ((s = prepare_gemms(p, w, rows, false))) return s;
-    return enqueue_inputs(p, w, x, rows, Projected{q, k, v, g, gamma},
-                          static_cast<char *>(workspace), f, static_cast<hipStream_t>(stream));
+    char *wsb = static_cast<char *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = enqueue_inputs(p, w, x, rows, wsb + f.o_proj, wsb, f, st))) return s;
+    return hip_status(ramnet::launch_split(wsb + f.o_proj, q, k, v, g, gamma, rows,
+                                           layout_of(p, w->d_model), st),
+                      "projection split launch");
 }
 
 ramnet_status ramnet_layer_forward(const ramnet_params *p, const ramnet_proj *w, const void *x,

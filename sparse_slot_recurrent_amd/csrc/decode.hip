@@ -37,7 +37,7 @@ template <int DP, int KC, typename WT, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, int64_t n, int T, int H,
     int U, int K, const int32_t *__restrict__ pos0, int cape, uint64_t content_heads,
-    int64_t M, bool unit_major,
+    int64_t M, bool unit_major, int64_t ld,
     int32_t *__restrict__ w_idx, float *__restrict__ w_wt,
     int32_t *__restrict__ r_idx, float *__restrict__ r_wt) {
     constexpr bool kRegs = KC <= 32;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int64_t a = static_cast<int64_t>(blockIdx.x) * kWave + lane;
     if (a >= n) return;  // no barrier below: lanes are independent
     const bool key = blockIdx.y == 0;
-    const TIn *lg = (key ? k : q) + a * (U * DP);
+    const TIn *lg = (key ? k : q) + (a / H) * ld + (a % H) * (U * DP);
     auto BW = [&](int buf, int r) -> WT & { return bw[(buf * KC + r) * kWave + lane]; };
     auto BP = [&](int buf, int r) -> int32_t & { return bp[(buf * KC + r) * kWave + lane]; };
 
@@ -199,7 +199,7 @@ hipError_t launch_kc(const DecodeArgs &d, hipStream_t st) {
     hipLaunchKernelGGL(kern, grid, dim3(kWave), lds, st,
                        static_cast<const TIn *>(d.q), static_cast<const TIn *>(d.k), d.n,
                        d.T, d.H, d.U, d.K, d.pos0, d.cape, d.content_heads, d.M, d.unit_major,
-                       d.w_idx, d.w_wt, d.r_idx, d.r_wt);
+                       d.ld ? d.ld : static_cast<int64_t>(d.H) * d.U * d.d_p, d.w_idx, d.w_wt, d.r_idx, d.r_wt);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct DecodeArgs {
     int64_t M;
     bool in_bf16;
     bool unit_major;  // write addresses as [B,H,T,K] (else [B,T,H,K])
+    int64_t ld;       // elements between tokens (b, t) of q and k; 0: H*U*d_p
     int32_t *w_idx, *r_idx;
     float *w_wt, *r_wt;
 };
@@ -42,6 +43,9 @@ struct ScanArgs {
     void *out_bf16;  // chunked path: if set, the normalised output goes here as
                      // bf16 instead of to out (out still holds r meanwhile)
     float eps_gsu, eps_norm;
+    // elements between tokens (b, t) of v, g and gamma; 0: contiguous
+    // (H*d_v, H*d_v, H).  Head h of a token starts at h*d_v (h for gamma).
+    int64_t ld_v, ld_g, ld_gamma;
 };
 // LDS bytes the serial scan needs to keep one head's state on chip, and
 // whether that fits a workgroup.
@@ -106,22 +110,38 @@ struct StepArgs {
     int32_t *out_idx[2];  // write, read addresses [B,H,K] or NULL
     float *out_wt[2];
     float eps_gsu, eps_norm;
+    // elements between sequences b of q and k, v, g, gamma; 0: contiguous
+    int64_t ld_qk, ld_v, ld_g, ld_gamma;
 };
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
 
 // Dense projections around the layer (proj.hip).
 constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch per call
-// Row-major C[m,n] = A[m,k] B[k,n]: bf16 in and out, fp32 accumulation.
+// Row-major C[m,n] = A[m,k] W[n,k]^T (W as [out, in]): bf16 in and out,
+// fp32 accumulation.
 // Returns false with a message in err.
 bool gemm_bf16(const void *A, const void *B, void *C, int64_t m, int64_t n, int64_t k,
                void *ws, hipStream_t st, std::string &err);
 // Creates the device's handle and picks the algorithm for a shape, so that
 // a sequence of GEMMs can be validated before any of it is enqueued.
 bool gemm_prepare(int64_t m, int64_t n, int64_t k, std::string &err);
-// w = bf16(e^alpha[h] * wp), column c of a [rows, cols] matrix in head c / L.
-hipError_t launch_temper(const void *wp, const float *alpha, void *w, int64_t rows, int cols,
-                         int L, hipStream_t st);
+// Row layout of the packed input weights [N, D] (= column layout of the
+// packed projections [rows, N]): q at 0, k at o_k, v at o_v, g at o_g, gamma
+// at o_gamma; every block starts at a multiple of 8, padding is zero.
+struct PackLayout {
+    int64_t D;
+    int H, L, HL, HV;
+    int o_k, o_v, o_g, o_gamma, N;
+};
+PackLayout pack_layout(int H, int L, int d_v, int64_t D);
+// Packs w_q, w_k (tempered by e^alpha, if alpha is set), w_v, w_g, w_gamma.
+hipError_t launch_pack(const void *wq, const void *wk, const void *wv, const void *wg,
+                       const void *wgam, const float *alpha, void *out, const PackLayout &pl,
+                       hipStream_t st);
+// Packed projections [rows, N] -> contiguous q, k, v, g, gamma.
+hipError_t launch_split(const void *in, void *q, void *k, void *v, void *g, void *gam,
+                        int64_t rows, const PackLayout &pl, hipStream_t st);
 hipError_t launch_to_bf16(const float *in, void *out, int64_t n, hipStream_t st);
 
 }  // namespace ramnet

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     int *rv = reinterpret_cast<int *>(rec + P.o_rv);
     float *rr = reinterpret_cast<float *>(rec + P.o_rr);
     const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
-    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    const TIn *gam = static_cast<const TIn *>(a.gamma) + static_cast<int64_t>(b) * a.T * a.ld_gamma + h;
 
     // ---- 0. this thread's events, e = tid + j * kPT (index t * K + k within
     //         the chunk), writes and reads alike; the loads go out first
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             wt[j] = a.w_wt[ai];
             rs[j] = a.r_idx[ai];
             rt[j] = a.r_wt[ai];
-            eg[j] = to_f32(gam[th]);
+            eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
         }
     }
     for (int i = tid; i < HT; i += kPT) {
@@ -585,7 +585,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     float *s_rr = reinterpret_cast<float *>(smem + L.rr);
     TS *ver = reinterpret_cast<TS *>(smem + L.ver);
 
-    const TIn *v = static_cast<const TIn *>(a.v);
+    // this unit's token 0 in the values
+    const TIn *v = static_cast<const TIn *>(a.v) + static_cast<int64_t>(b) * a.T * a.ld_v + h * d_v;
     TS *S = static_cast<TS *>(a.S);
     const int64_t th_unit = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
     const unsigned char *plan0 = a.plan + static_cast<int64_t>(unit) * P.n_chunks * P.rec_bytes;
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         for (int j = 0; j < VPT; ++j) {
             const int i = min(tid + j * kNT, Cc * CG - 1);  // in range; extra lanes unused
             const int t = i / CG, cc = i % CG;
-            pf_v[j] = v[(th_unit + static_cast<int64_t>(t0 + t) * a.H) * d_v + cg * CG + cc];
+            pf_v[j] = v[static_cast<int64_t>(t0 + t) * a.ld_v + cg * CG + cc];
         }
         if constexpr (RES) {
             if (tid < M) {
@@ -843,7 +844,8 @@ struct alignas(4 * sizeof(T)) Quad {
 template <typename TIn, typename TO>
 __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__ rbuf,
                                                        const float *__restrict__ sumsq, int ncg,
-                                                       const TIn *__restrict__ g,
+                                                       const TIn *__restrict__ g, int H,
+                                                       int64_t ld_g,
                                                        const float *__restrict__ norm_w,
                                                        TO *out, int64_t n, int d_v, float eps,
                                                        const float *__restrict__ mass_ws,
@@ -860,7 +862,7 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__
     const float den = tot / static_cast<float>(d_v) + eps;
     const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
     const Quad<float> r = *reinterpret_cast<const Quad<float> *>(rbuf + th * d_v + c0);
-    const Quad<TIn> gv = *reinterpret_cast<const Quad<TIn> *>(g + th * d_v + c0);
+    const Quad<TIn> gv = *reinterpret_cast<const Quad<TIn> *>(g + (th / H) * ld_g + (th % H) * d_v + c0);
     Quad<TO> o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -907,12 +909,12 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const unsigned g2 = static_cast<unsigned>((work + 255) / 256);
     if (a.out_bf16)
         hipLaunchKernelGGL((rms_gate_kernel<TIn, bf16_t>), dim3(g2), dim3(256), 0, st, a.rbuf,
-                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.norm_w,
+                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm, a.mass_ws,
                            P.resident ? 1 : P.ncg, a.mass, n_mass);
     else
         hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf,
-                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.norm_w,
+                           a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<TS *>(a.out), n, a.d_v, a.eps_norm, a.mass_ws,
                            P.resident ? 1 : P.ncg, a.mass, n_mass);
     return hipGetLastError();
@@ -1009,9 +1011,13 @@ size_t chunk_workspace_bytes(const ChunkPlan &p) {
     return p.ws_rbuf + p.ws_sumsq + p.ws_mass + p.ws_plan;
 }
 
-hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st) {
-    if (static_cast<int64_t>(a.B) * a.H * a.T == 0) return hipSuccess;
-    if (!a.p.ok) return hipErrorInvalidValue;
+hipError_t launch_scan_chunked(const ChunkArgs &args, hipStream_t st) {
+    if (static_cast<int64_t>(args.B) * args.H * args.T == 0) return hipSuccess;
+    if (!args.p.ok) return hipErrorInvalidValue;
+    ChunkArgs a = args;
+    if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_g) a.ld_g = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_gamma) a.ld_gamma = a.H;
     if (a.in_bf16)
         return a.state_bf16 ? launch_cg<bf16_t, bf16_t>(a, st) : launch_cg<bf16_t, float>(a, st);
     return a.state_bf16 ? launch_cg<float, bf16_t>(a, st) : launch_cg<float, float>(a, st);

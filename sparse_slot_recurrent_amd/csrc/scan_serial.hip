@@ -59,12 +59,13 @@ __global__ __launch_bounds__(kWave) void scan_serial_kernel(ScanArgs a) {
             ri = a.r_idx[th * K + lane];
             rw = a.r_wt[th * K + lane];
         }
-        const float eg = expf(to_f32(gam[th]));
+        const int64_t row = static_cast<int64_t>(b) * a.T + t;  // token (b, t)
+        const float eg = expf(to_f32(gam[row * a.ld_gamma + h]));
         float vv[CPL], gg[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            vv[j] = to_f32(v[th * d_v + lane + kWave * j]);
-            gg[j] = to_f32(g[th * d_v + lane + kWave * j]);
+            vv[j] = to_f32(v[row * a.ld_v + h * d_v + lane + kWave * j]);
+            gg[j] = to_f32(g[row * a.ld_g + h * d_v + lane + kWave * j]);
         }
         // Gated Sparse Update of the K write slots.
         for (int kk = 0; kk < K; ++kk) {
@@ -162,8 +163,12 @@ bool scan_state_fits_lds(int64_t M, int d_v, bool state_bf16) {
     return scan_state_lds_bytes(M, d_v, state_bf16) <= kLdsBytes;
 }
 
-hipError_t launch_scan_serial(const ScanArgs &a, hipStream_t st) {
-    if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
+hipError_t launch_scan_serial(const ScanArgs &args, hipStream_t st) {
+    if (static_cast<int64_t>(args.B) * args.H == 0) return hipSuccess;
+    ScanArgs a = args;
+    if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_g) a.ld_g = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_gamma) a.ld_gamma = a.H;
     if (a.in_bf16)
         return a.state_bf16 ? launch_ts<bf16_t, bf16_t>(a, st) : launch_ts<bf16_t, float>(a, st);
     return a.state_bf16 ? launch_ts<float, bf16_t>(a, st) : launch_ts<float, float>(a, st);

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         const int g = i / L, e = i - g * L;
         const int unit = min(u0 + g / 2, units - 1);
         const TIn *src = static_cast<const TIn *>(g % 2 ? a.q : a.k);
-        slg[i] = to_f32(src[static_cast<int64_t>(unit) * L + e]);
+        slg[i] = to_f32(src[(unit / a.H) * a.ld_qk + (unit % a.H) * L + e]);
     }
     __syncthreads();
     // digit distributions of every block, one (address, block, digit) per
@@ -343,7 +343,8 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                         rrow[i][j] = *reinterpret_cast<const Words<NW> *>(Su + static_cast<int64_t>(rs) * DV + c0);
                     }
                 }
-                const TIn *vu = v + static_cast<int64_t>(u0 + ul) * DV + c0;
+                const int un = u0 + ul;
+                const TIn *vu = v + static_cast<int64_t>(un / a.H) * a.ld_v + (un % a.H) * DV + c0;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) vin[i][c] = to_f32(vu[c]);
             }
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
             float lam = 0.f, cr = 0.f;
             if (lane < npair) {
                 if (wgt > 0.f) {
-                    const float eg = expf(to_f32(gam[u0 + pu]));
+                    const int un = u0 + pu;
+                    const float eg = expf(to_f32(gam[static_cast<int64_t>(un / a.H) * a.ld_gamma + un % a.H]));
                     const float mnew = fmaf(retention_fast(wgt, eg), mold, wgt);
                     *mp = mnew;
                     lam = wgt * __builtin_amdgcn_rcpf(mnew + a.eps_gsu);
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
             ss = wave_sum(ss);
             const float den = ss / static_cast<float>(DV) + a.eps_norm;
             const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-            const TIn *gu = gg + static_cast<int64_t>(unit) * DV + lane * CPO;
+            const TIn *gu = gg + static_cast<int64_t>(unit / a.H) * a.ld_g + (unit % a.H) * DV + lane * CPO;
             TS *ou = out + static_cast<int64_t>(unit) * DV + lane * CPO;
 #pragma unroll
             for (int c = 0; c < CPO; ++c) {
@@ -496,9 +498,15 @@ bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16) {
     return state_bf16 ? fits<bf16_t>(K, d_v) : fits<float>(K, d_v);
 }
 
-hipError_t launch_step_fused(const StepArgs &a, hipStream_t st) {
-    if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
-    if (!step_fused_supported(a.K, a.d_p, a.U, a.d_v, a.state_bf16)) return hipErrorInvalidValue;
+hipError_t launch_step_fused(const StepArgs &args, hipStream_t st) {
+    if (static_cast<int64_t>(args.B) * args.H == 0) return hipSuccess;
+    if (!step_fused_supported(args.K, args.d_p, args.U, args.d_v, args.state_bf16))
+        return hipErrorInvalidValue;
+    StepArgs a = args;
+    if (!a.ld_qk) a.ld_qk = static_cast<int64_t>(a.H) * a.U * a.d_p;
+    if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_g) a.ld_g = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_gamma) a.ld_gamma = a.H;
     if (a.in_bf16)
         return a.state_bf16 ? launch_ts<bf16_t, bf16_t>(a, st) : launch_ts<bf16_t, float>(a, st);
     return a.state_bf16 ? launch_ts<float, bf16_t>(a, st) : launch_ts<float, float>(a, st);

@@ -22,7 +22,8 @@ EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
             "ramnet_scan_prefill", "ramnet_step_decode", "ramnet_status_str",
             "ramnet_last_error", "ramnet_version",
             "ramnet_layer_workspace_bytes", "ramnet_project_inputs",
-            "ramnet_layer_forward", "ramnet_layer_step")
+            "ramnet_layer_forward", "ramnet_layer_step",
+            "ramnet_packed_weights_bytes", "ramnet_pack_weights")
 
 
 class Params(C.Structure):
@@ -43,7 +44,7 @@ class Proj(C.Structure):
     _fields_ = [("d_model", C.c_int32), ("w_q", C.c_void_p), ("w_k", C.c_void_p),
                 ("w_v", C.c_void_p), ("w_g", C.c_void_p),
                 ("w_gamma", C.c_void_p), ("w_o", C.c_void_p),
-                ("alpha", C.c_void_p)]
+                ("alpha", C.c_void_p), ("w_in_packed", C.c_void_p)]
 
 
 class RamnetError(RuntimeError):
@@ -91,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     lib.ramnet_project_inputs.argtypes = [pp, pw, P, P, P, P, P, P, P,
                                           C.c_size_t, P]
     lib.ramnet_project_inputs.restype = C.c_int
+    lib.ramnet_packed_weights_bytes.argtypes = [pp, C.c_int32]
+    lib.ramnet_packed_weights_bytes.restype = C.c_size_t
+    lib.ramnet_pack_weights.argtypes = [pp, pw, P, C.c_size_t, P]
+    lib.ramnet_pack_weights.restype = C.c_int
     for name in ("ramnet_layer_forward", "ramnet_layer_step"):
         f = getattr(lib, name)
         f.argtypes = [pp, pw, P, P, P, P, P, P, pa, P, C.c_size_t, P]
@@ -279,9 +284,10 @@ def step_decode(q, k, v, gamma, g, pos, S, mass, *, d_p: int, U: int, K: int,
 # ---------------------------------------------------------------- whole layer
 
 class LayerWeights(NamedTuple):
-    """bf16 row-major weights of the projections (include/ramnet.h,
-    ramnet_proj): w_q, w_k [D, H*U*d_p] (W' before the temperature), w_v,
-    w_g [D, H*d_v], w_gamma [D, H], w_o [H*d_v, D]; alpha [H] fp32 or None."""
+    """bf16 weights of the projections, [out, in] like a linear layer's
+    (include/ramnet.h, ramnet_proj): w_q, w_k [H*U*d_p, D] (W' before the
+    temperature), w_v, w_g [H*d_v, D], w_gamma [H, D], w_o [D, H*d_v];
+    alpha [H] fp32 or None."""
     w_q: "object"
     w_k: "object"
     w_v: "object"
@@ -289,16 +295,32 @@ class LayerWeights(NamedTuple):
     w_gamma: "object"
     w_o: "object"
     alpha: "object" = None
+    packed: "object" = None   # from pack_weights: replaces w_q .. alpha
 
 
 def _proj_struct(w: LayerWeights) -> Proj:
-    D = w.w_q.shape[0]
+    D = w.w_o.shape[0]
     ps = [_ptr(t) for t in (w.w_q, w.w_k, w.w_v, w.w_g, w.w_gamma, w.w_o)]
-    return Proj(D, *ps, _ptr(w.alpha))
+    return Proj(D, *ps, _ptr(w.alpha), _ptr(w.packed))
 
 
 def layer_workspace_bytes(p: Params, d_model: int) -> int:
     return int(load_library().ramnet_layer_workspace_bytes(C.byref(p), d_model))
+
+
+def pack_weights(p: Params, w: LayerWeights) -> LayerWeights:
+    """Packs the input weights once (ramnet_pack_weights); returns weights
+    that carry the packed matrix."""
+    torch = _torch()
+    D = w.w_o.shape[0]
+    nbytes = int(load_library().ramnet_packed_weights_bytes(C.byref(p), D))
+    if nbytes == 0:
+        raise ValueError("invalid layer parameters")
+    packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.w_o.device)
+    ws = _proj_struct(w._replace(packed=None))
+    _raise(load_library().ramnet_pack_weights(C.byref(p), C.byref(ws), _ptr(packed),
+                                              nbytes, _stream()))
+    return w._replace(packed=packed)
 
 
 class LayerPlan:
@@ -364,8 +386,8 @@ def layer_forward(w: LayerWeights, x, S, mass, *, d_p: int, U: int, K: int,
     updated in place (and the addresses used when export_addresses)."""
     torch = _torch()
     B, T, D = x.shape
-    H = w.w_gamma.shape[1]
-    d_v = w.w_v.shape[1] // H
+    H = w.w_gamma.shape[0]
+    d_v = w.w_v.shape[0] // H
     plan = LayerPlan(B, T, H, d_p, U, K, d_v, D, _dt(S), cape, eps_gsu,
                      eps_norm, device=x.device, content_heads=content_heads)
     y = torch.empty_like(x)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(rn):
 
 def test_version_and_status_strings(rn):
     lib = rn.load_library()
-    assert lib.ramnet_version() == 3
+    assert lib.ramnet_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert lib.ramnet_status_str(code).decode() != "unknown status"
 
@@ -184,7 +184,7 @@ def test_product_path_has_no_cpu_fallback():
 
 def call_forward(rn, p, d_model=256, ws_bytes=None, **kw):
     lib = rn.load_library()
-    w = rn.Proj(d_model, *[FAKE + ((20 + i) << 32) for i in range(6)], None)
+    w = rn.Proj(d_model, *[FAKE + ((20 + i) << 32) for i in range(6)], None, None)
     for k, v in kw.items():
         setattr(w, k, v)
     need = rn.layer_workspace_bytes(p, d_model)
@@ -231,10 +231,28 @@ def test_layer_forward_rejects_overlaps(rn):
     p = good(rn)
     # y on top of a weight
     lib = rn.load_library()
-    w = rn.Proj(256, *[FAKE + ((20 + i) << 32) for i in range(6)], None)
+    w = rn.Proj(256, *[FAKE + ((20 + i) << 32) for i in range(6)], None, None)
     need = rn.layer_workspace_bytes(p, 256)
     st = lib.ramnet_layer_forward(C.byref(p), C.byref(w), C.c_void_p(FAKE), None, None,
                                   C.c_void_p(FAKE + (5 << 32)), C.c_void_p(FAKE + (6 << 32)),
                                   C.c_void_p(FAKE + (21 << 32) + 256), None,
                                   C.c_void_p(FAKE + (40 << 32)), need, None)
     assert st == -1 and "overlaps" in lib.ramnet_last_error().decode()
+
+
+def test_packed_weights_size(rn):
+    # H = 2, U*d_p = 20, d_v = 64: q at 0, k at 40, v at 80, g at 208,
+    # gamma at 336, N = 344 (blocks start at multiples of 8 columns)
+    p = good(rn)
+    lib = rn.load_library()
+    assert lib.ramnet_packed_weights_bytes(C.byref(p), 256) == 256 * 344 * 2
+    assert lib.ramnet_packed_weights_bytes(C.byref(p), 100) == 0
+
+
+def test_pack_rejects_short_buffer(rn):
+    p = good(rn)
+    lib = rn.load_library()
+    w = rn.Proj(256, *[FAKE + ((20 + i) << 32) for i in range(6)], None, None)
+    st = lib.ramnet_pack_weights(C.byref(p), C.byref(w), C.c_void_p(FAKE + (40 << 32)),
+                                 1000, None)
+    assert st == -1 and "packed needs" in lib.ramnet_last_error().decode()

@@ -44,11 +44,14 @@ def bf(a):
 
 
 def gpu_weights(rn, d):
+    """The library takes weights as [out, in]; the generator and the oracle
+    write them as [in, out] (x W)."""
     alpha = None
     if "alpha" in d:
         alpha = torch.from_numpy(d["alpha"]).cuda()
-    return rn.LayerWeights(bf(d["w_q"]), bf(d["w_k"]), bf(d["w_v"]), bf(d["w_g"]),
-                           bf(d["w_gamma"]), bf(d["w_o"]), alpha)
+    t = lambda a: bf(np.ascontiguousarray(np.asarray(a).T))
+    return rn.LayerWeights(t(d["w_q"]), t(d["w_k"]), t(d["w_v"]), t(d["w_g"]),
+                           t(d["w_gamma"]), t(d["w_o"]), alpha)
 
 
 def oracle_weights(d):
@@ -268,3 +271,27 @@ def test_layer_step_matches_oracle(rn, P):
     assert_close(gS[alive], S_ref[alive], True, "S", slot_state=True)
     assert_close(gm[alive], m_ref[alive], False, "mass")
     assert alive.sum() >= B // 2
+
+
+def test_packed_weights_give_the_same_layer(rn, P):
+    """Packing once (ramnet_pack_weights) and passing the packed matrix gives
+    bit-identical results to packing inside every call."""
+    w = synth.WORKLOADS["prefill_top8"].replace(pos0_max=100)
+    B, T, H = 2, 96, 8
+    d = synth.make_layer_weights(w, D_MODEL, B=B, T=T, H=H, kind="gauss", alpha="general")
+    st = synth.make_inputs(w, B=B, T=T, H=H)
+    W = gpu_weights(rn, d)
+    plan = rn.LayerPlan(B, T, H, w.d_p, w.U, w.K, w.d_v, D_MODEL, torch.float32)
+    Wp = rn.pack_weights(plan.p, W)
+    x = bf(d["x"])
+    pos0 = torch.from_numpy(st["pos0"]).cuda()
+    res = []
+    for weights in (W, Wp):
+        S = torch.from_numpy(st["S0"]).cuda()
+        mass = torch.from_numpy(st["m0"]).cuda()
+        y = torch.empty_like(x)
+        plan(weights, x, S, mass, y, pos=pos0)
+        torch.cuda.synchronize()
+        res.append((to_np(y), to_np(S), to_np(mass)))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
