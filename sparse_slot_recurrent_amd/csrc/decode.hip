@@ -169,11 +169,33 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     int32_t *oi = (key ? w_idx : r_idx) + o * K;
     float *ow = (key ? w_wt : r_wt) + o * K;
     if constexpr (kRegs) {
+        if (K % 4 == 0) {
+            // whole 16-byte pieces: a lane's row goes out in K/4 stores
+            // instead of K, so rows are complete sooner
 #pragma unroll
-        for (int r = 0; r < KC; ++r) {
-            if (r < K) {
-                oi[r] = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
-                ow[r] = static_cast<float>(nxw[r]);
+            for (int r = 0; r < KC; r += 4) {
+                if (r < K) {
+                    int4 vi;
+                    float4 vw;
+                    vi.x = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
+                    vi.y = form ? cape_slot<DP>(nxp[r + 1], pos, U, DP, form, M) : nxp[r + 1];
+                    vi.z = form ? cape_slot<DP>(nxp[r + 2], pos, U, DP, form, M) : nxp[r + 2];
+                    vi.w = form ? cape_slot<DP>(nxp[r + 3], pos, U, DP, form, M) : nxp[r + 3];
+                    vw.x = static_cast<float>(nxw[r]);
+                    vw.y = static_cast<float>(nxw[r + 1]);
+                    vw.z = static_cast<float>(nxw[r + 2]);
+                    vw.w = static_cast<float>(nxw[r + 3]);
+                    *reinterpret_cast<int4 *>(oi + r) = vi;
+                    *reinterpret_cast<float4 *>(ow + r) = vw;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < KC; ++r) {
+                if (r < K) {
+                    oi[r] = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
+                    ow[r] = static_cast<float>(nxw[r]);
+                }
             }
         }
     } else {
