@@ -118,12 +118,15 @@ def test_projections_exact_on_grid(rn, P, case):
         assert np.array_equal(to_np(got[nm]), ref[nm]), nm
 
 
-def test_projections_gaussian_within_accumulation_bound(rn, P):
+@pytest.mark.parametrize("B,T", [(2, 200), (1, 200), (3, 1)])
+def test_projections_gaussian_within_accumulation_bound(rn, P, B, T):
     """Arbitrary bf16 inputs: an fp32 sum of D terms in any order is within
     D * 2^-24 * sum|x_i W_i| of the exact one, and rounding that to bf16 adds
-    at most one bf16 ulp of the result; most results agree exactly."""
+    at most one bf16 ulp of the result; most results agree exactly.  The
+    row counts cover prefill-sized and decoding-sized GEMMs (different
+    library kernels)."""
     w = synth.WORKLOADS["prefill_top8"]
-    B, T, H, D = 2, 200, 8, 512
+    H, D = 8, 512
     d = synth.make_layer_weights(w, D, B=B, T=T, H=H, kind="gauss", alpha="general")
     plan = rn.LayerPlan(B, T, H, w.d_p, w.U, w.K, w.d_v, D, torch.float32)
     got = plan.project_inputs(gpu_weights(rn, d), bf(d["x"]))
@@ -141,7 +144,7 @@ def test_projections_gaussian_within_accumulation_bound(rn, P):
         bad = diff > bound
         assert not bad.any(), (nm, int(bad.sum()), np.argwhere(bad)[:3].tolist())
         frac = float((diff > 0).mean())
-        assert frac < 0.01, (nm, frac)
+        assert frac < 0.01 or diff.size < 200, (nm, frac)
 
 
 def run_forward(rn, P, case, cape=1, content_heads=0, alpha="pow2", norm=False):
