@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RAMNET_VERSION 4
+#define RAMNET_VERSION 5
 /* Largest supported K (Top-K per address). */
 #define RAMNET_KMAX 64
 
@@ -76,8 +76,12 @@ typedef enum {
 
 typedef enum { RAMNET_F32 = 0, RAMNET_BF16 = 1 } ramnet_dtype;
 
-typedef enum { RAMNET_OP_DECODE = 0, RAMNET_OP_PREFILL = 1, RAMNET_OP_STEP = 2 }
-    ramnet_op;
+typedef enum {
+    RAMNET_OP_DECODE = 0,
+    RAMNET_OP_PREFILL = 1,
+    RAMNET_OP_STEP = 2,
+    RAMNET_OP_BACKWARD = 3
+} ramnet_op;
 
 typedef struct {
     int32_t B, T, H;      /* batch, tokens per sequence, heads; T = 1 for a step */
@@ -171,6 +175,43 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
                                  void *S, float *mass, void *out,
                                  const ramnet_addr *addr_out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* Backward pass of a prefill (training; the project page's GPU-execution
+ * paragraph treats training and prefill alike).  The pages give no backward
+ * formulas: this is the exact derivative of steps 1-4 with the Top-K
+ * selection held fixed (it is piecewise constant), the power-decay retention
+ * differentiated exactly (the paper digest's proxy gradient is not defined
+ * there and is not used), and each fp32 storage rounding passing its
+ * gradient through.  The gradients are those of
+ *   sum(out * dout) + sum(S_final * dS_final) + sum(mass_final * dmass_final)
+ * with respect to the inputs and the state the forward started from.
+ * Built for an fp32 state with d_v = 64, M <= 1024 and U*d_p <= 64
+ * (RAMNET_EUNSUPPORTED otherwise).
+ *   q, k, v, gamma, g, norm_w, pos0   the forward's inputs (q, k only read
+ *             when dq, dk are given)
+ *   S0, mass0 [B,H,M,d_v], [B,H,M] fp32: the state before the forward
+ *   addr      the forward's addresses (its addr_out), [B,T,H,K] each
+ *   dout      [B,T,H,d_v] fp32; dS_final, dmass_final fp32 or NULL (= 0)
+ *   dq, dk    [B,T,H,U*d_p] fp32 or NULL; dv, dg [B,T,H,d_v] fp32;
+ *   dgamma    [B,T,H] fp32; dnorm_w [d_v] fp32 or NULL; dS0, dmass0 like
+ *             S0, mass0
+ *   workspace ramnet_workspace_bytes(p, RAMNET_OP_BACKWARD) bytes: the
+ *             forward is replayed from S0 and, per token-head, each write's
+ *             row and mass before it and each read's row are recorded
+ *             ((2 K d_v + 3 K) fp32).
+ * Every sum is taken in a fixed order: repeated calls give the same bits. */
+ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q,
+                                   const void *k, const void *v,
+                                   const void *gamma, const void *g,
+                                   const float *norm_w, const int32_t *pos0,
+                                   const float *S0, const float *mass0,
+                                   const ramnet_addr *addr, const float *dout,
+                                   const float *dS_final,
+                                   const float *dmass_final, float *dq,
+                                   float *dk, float *dv, float *dgamma,
+                                   float *dg, float *dnorm_w, float *dS0,
+                                   float *dmass0, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * A whole layer: the dense projections either side of the recurrence (RAM-Net

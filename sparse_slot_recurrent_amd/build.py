@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libramnet.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "step_fused.hip",
-           "proj.hip"]
+           "proj.hip", "backward.hip"]
 # hipBLASLt carries the dense projections around the layer.
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 

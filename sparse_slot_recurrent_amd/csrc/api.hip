@@ -700,8 +700,132 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
     g_last_error = saved;
     if (s != RAMNET_OK) return 0;
     if (op == RAMNET_OP_DECODE) return 0;
+    if (op == RAMNET_OP_BACKWARD)
+        return ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, p->state_dtype == RAMNET_BF16)
+                   ? ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K)
+                   : 0;
     if (op != RAMNET_OP_PREFILL && op != RAMNET_OP_STEP) return 0;
     return plan_layer(p, step, true).total();
+}
+
+ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const void *k,
+                                   const void *v, const void *gamma, const void *g,
+                                   const float *norm_w, const int32_t *pos0, const float *S0,
+                                   const float *mass0, const ramnet_addr *addr, const float *dout,
+                                   const float *dS_final, const float *dmass_final, float *dq,
+                                   float *dk, float *dv, float *dgamma, float *dg, float *dnorm_w,
+                                   float *dS0, float *dmass0, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    ramnet_status s = check_params(p, false);
+    if (s) return s;
+    if (p->state_dtype != RAMNET_F32)
+        return fail(RAMNET_EUNSUPPORTED, "the backward pass needs an fp32 state");
+    if (!ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, false))
+        return fail(RAMNET_EUNSUPPORTED,
+                    "the backward pass is built for d_v = 64, M <= 1024 and U*d_p <= 64");
+    const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
+    const int64_t units = static_cast<int64_t>(p->B) * p->H;
+    if (n == 0) return ok();
+    if (!addr) return fail(RAMNET_EINVAL, "addr is NULL");
+    if ((s = check_ptr("v", v, true)) || (s = check_ptr("gamma", gamma, true)) ||
+        (s = check_ptr("g", g, true)) || (s = check_ptr("norm_w", norm_w, false)) ||
+        (s = check_ptr("pos0", pos0, false)) || (s = check_ptr("S0", S0, true)) ||
+        (s = check_ptr("mass0", mass0, true)) || (s = check_addr("addr", addr)) ||
+        (s = check_ptr("dout", dout, true)) || (s = check_ptr("dS_final", dS_final, false)) ||
+        (s = check_ptr("dmass_final", dmass_final, false)) || (s = check_ptr("dq", dq, false)) ||
+        (s = check_ptr("dk", dk, false)) || (s = check_ptr("dv", dv, true)) ||
+        (s = check_ptr("dgamma", dgamma, true)) ||
+        (s = check_ptr("dg", dg, true)) || (s = check_ptr("dnorm_w", dnorm_w, false)) ||
+        (s = check_ptr("dS0", dS0, true)) || (s = check_ptr("dmass0", dmass0, true)))
+        return s;
+    if (dq && (s = check_ptr("q", q, true))) return s;
+    if (dk && (s = check_ptr("k", k, true))) return s;
+    const size_t need = ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K);
+    if (!workspace || workspace_bytes < need)
+        return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if ((s = check_ptr("workspace", workspace, true))) return s;
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    const size_t nK4 = static_cast<size_t>(n) * p->K * 4;
+    const size_t nv = static_cast<size_t>(n) * p->d_v;
+    const size_t st = static_cast<size_t>(units) * p->M;
+    Span sp[32];
+    int ns = 0;
+    if (dq) sp[ns++] = span("q", q, n * L * in_bytes(p));
+    if (dk) sp[ns++] = span("k", k, n * L * in_bytes(p));
+    sp[ns++] = span("v", v, nv * in_bytes(p));
+    sp[ns++] = span("gamma", gamma, n * in_bytes(p));
+    sp[ns++] = span("g", g, nv * in_bytes(p));
+    if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
+    if (pos0) sp[ns++] = span("pos0", pos0, p->B * sizeof(int32_t));
+    sp[ns++] = span("S0", S0, st * p->d_v * 4);
+    sp[ns++] = span("mass0", mass0, st * 4);
+    sp[ns++] = span("addr.w_idx", addr->w_idx, nK4);
+    sp[ns++] = span("addr.w_wt", addr->w_wt, nK4);
+    sp[ns++] = span("addr.r_idx", addr->r_idx, nK4);
+    sp[ns++] = span("addr.r_wt", addr->r_wt, nK4);
+    sp[ns++] = span("dout", dout, nv * 4);
+    if (dS_final) sp[ns++] = span("dS_final", dS_final, st * p->d_v * 4);
+    if (dmass_final) sp[ns++] = span("dmass_final", dmass_final, st * 4);
+    const int first_written = ns;
+    if (dq) sp[ns++] = span("dq", dq, n * L * 4);
+    if (dk) sp[ns++] = span("dk", dk, n * L * 4);
+    sp[ns++] = span("dv", dv, nv * 4);
+    sp[ns++] = span("dgamma", dgamma, n * 4);
+    sp[ns++] = span("dg", dg, nv * 4);
+    if (dnorm_w) sp[ns++] = span("dnorm_w", dnorm_w, p->d_v * sizeof(float));
+    sp[ns++] = span("dS0", dS0, st * p->d_v * 4);
+    sp[ns++] = span("dmass0", dmass0, st * 4);
+    sp[ns++] = span("workspace", workspace, need);
+    if ((s = check_overlaps(sp, ns, first_written))) return s;
+
+    ramnet::BwdArgs a{};
+    a.B = p->B;
+    a.T = p->T;
+    a.H = p->H;
+    a.M = p->M;
+    a.K = p->K;
+    a.U = p->U;
+    a.d_p = p->d_p;
+    a.cape = p->cape;
+    a.content_heads = p->content_heads;
+    a.in_bf16 = p->in_dtype == RAMNET_BF16;
+    a.eps_gsu = p->eps_gsu;
+    a.eps_norm = p->eps_norm;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.gamma = gamma;
+    a.g = g;
+    a.norm_w = norm_w;
+    a.pos0 = pos0;
+    a.S0 = S0;
+    a.mass0 = mass0;
+    a.w_idx = addr->w_idx;
+    a.w_wt = addr->w_wt;
+    a.r_idx = addr->r_idx;
+    a.r_wt = addr->r_wt;
+    a.dout = dout;
+    a.dS_final = dS_final;
+    a.dmass_final = dmass_final;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dgamma = dgamma;
+    a.dg = dg;
+    a.dnorm_w = dnorm_w;
+    a.dS0 = dS0;
+    a.dmass0 = dmass0;
+    char *w = static_cast<char *>(workspace);
+    const size_t rows = align256(nK4 * p->d_v);
+    a.rec_w = reinterpret_cast<float *>(w);
+    a.rec_r = reinterpret_cast<float *>(w + rows);
+    a.rec_m = reinterpret_cast<float *>(w + 2 * rows);
+    a.dw = reinterpret_cast<float *>(w + 2 * rows + align256(nK4));
+    a.drho = reinterpret_cast<float *>(w + 2 * rows + 2 * align256(nK4));
+    a.dom_part = reinterpret_cast<float *>(w + 2 * rows + 3 * align256(nK4));
+    return hip_status(ramnet::launch_backward(a, static_cast<hipStream_t>(stream)),
+                      "backward launch");
 }
 
 ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q, const void *k,

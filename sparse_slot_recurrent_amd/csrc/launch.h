@@ -116,6 +116,30 @@ struct StepArgs {
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
 
+// Backward pass of the recurrence (backward.hip): fp32 state, d_v = 64,
+// M <= 1024, given the forward's addresses.
+struct BwdArgs {
+    int B, T, H;
+    int64_t M;
+    int K, U, d_p, cape;
+    uint64_t content_heads;
+    bool in_bf16;
+    float eps_gsu, eps_norm;
+    const void *q, *k, *v, *gamma, *g;
+    const float *norm_w;
+    const int32_t *pos0;
+    const float *S0, *mass0;
+    const int32_t *w_idx, *r_idx;
+    const float *w_wt, *r_wt;
+    const float *dout, *dS_final, *dmass_final;
+    float *dq, *dk, *dv, *dgamma, *dg, *dnorm_w, *dS0, *dmass0;
+    // workspace: per token-head records and weight gradients, per unit d omega
+    float *rec_w, *rec_r, *rec_m, *dw, *drho, *dom_part;
+};
+bool backward_supported(int64_t M, int d_v, int U, int d_p, bool state_bf16);
+size_t backward_workspace_bytes(int B, int T, int H, int K);
+hipError_t launch_backward(const BwdArgs &a, hipStream_t st);
+
 // Dense projections around the layer (proj.hip).
 constexpr size_t kGemmWorkspace = size_t(32) << 20;  // hipBLASLt scratch per call
 // Row-major C[m,n] = A[m,k] W[n,k]^T (W as [out, in]): bf16 in and out,

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libramnet.so")
 
 F32, BF16 = 0, 1
-OP_DECODE, OP_PREFILL, OP_STEP = 0, 1, 2
+OP_DECODE, OP_PREFILL, OP_STEP, OP_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "RAMNET_OK", -1: "RAMNET_EINVAL", -2: "RAMNET_EUNSUPPORTED",
           -3: "RAMNET_EWORKSPACE", -4: "RAMNET_EHIP"}
 EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
@@ -23,7 +23,8 @@ EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
             "ramnet_last_error", "ramnet_version",
             "ramnet_layer_workspace_bytes", "ramnet_project_inputs",
             "ramnet_layer_forward", "ramnet_layer_step",
-            "ramnet_packed_weights_bytes", "ramnet_pack_weights")
+            "ramnet_packed_weights_bytes", "ramnet_pack_weights",
+            "ramnet_scan_backward")
 
 
 class Params(C.Structure):
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.ramnet_project_inputs.argtypes = [pp, pw, P, P, P, P, P, P, P,
                                           C.c_size_t, P]
     lib.ramnet_project_inputs.restype = C.c_int
+    lib.ramnet_scan_backward.argtypes = [pp] + [P] * 9 + [pa] + [P] * 11 + [P, C.c_size_t, P]
+    lib.ramnet_scan_backward.restype = C.c_int
     lib.ramnet_packed_weights_bytes.argtypes = [pp, C.c_int32]
     lib.ramnet_packed_weights_bytes.restype = C.c_size_t
     lib.ramnet_pack_weights.argtypes = [pp, pw, P, C.c_size_t, P]
@@ -394,3 +397,35 @@ def layer_forward(w: LayerWeights, x, S, mass, *, d_p: int, U: int, K: int,
     ao = new_addresses((B, T, H, K), x.device) if export_addresses else None
     plan(w, x, S, mass, y, norm_w=norm_w, pos=pos0, addr_out=ao)
     return (y, ao) if export_addresses else y
+
+
+# ---------------------------------------------------------------- backward
+
+def scan_backward(q, k, v, gamma, g, S0, mass0, addr: Addresses, dout, *,
+                  d_p: int, U: int, K: int, cape: int = 1, norm_w=None,
+                  pos0=None, eps_gsu=1e-6, eps_norm=1e-6, content_heads: int = 0,
+                  dS_final=None, dmass_final=None, want_logits: bool = True):
+    """Gradients of a prefill (ramnet_scan_backward) given the forward's
+    inputs, the state it started from (S0, mass0: fp32) and the addresses it
+    used.  Returns a dict of fp32 tensors dq, dk (None unless want_logits),
+    dv, dgamma, dg, dnorm_w, dS0, dmass0."""
+    torch = _torch()
+    B, T, H, d_v = v.shape
+    p = make_params(B, T, H, d_p, U, K, d_v, _dt(v), F32, cape, eps_gsu,
+                    eps_norm, content_heads=content_heads)
+    nbytes = workspace_bytes(p, OP_BACKWARD)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=v.device)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=v.device)
+    L = U * d_p
+    out = {"dq": f32(B, T, H, L) if want_logits else None,
+           "dk": f32(B, T, H, L) if want_logits else None,
+           "dv": f32(B, T, H, d_v), "dgamma": f32(B, T, H), "dg": f32(B, T, H, d_v),
+           "dnorm_w": f32(d_v), "dS0": torch.empty_like(S0), "dmass0": torch.empty_like(mass0)}
+    a = _addr_struct(addr)
+    _raise(load_library().ramnet_scan_backward(
+        C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g), _ptr(norm_w),
+        _ptr(pos0), _ptr(S0), _ptr(mass0), C.byref(a), _ptr(dout), _ptr(dS_final),
+        _ptr(dmass_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dgamma"]), _ptr(out["dg"]), _ptr(out["dnorm_w"]), _ptr(out["dS0"]),
+        _ptr(out["dmass0"]), C.c_void_p(ws.data_ptr()), nbytes, _stream()))
+    return out

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(rn):
 
 def test_version_and_status_strings(rn):
     lib = rn.load_library()
-    assert lib.ramnet_version() == 4
+    assert lib.ramnet_version() == 5
     for code in (0, -1, -2, -3, -4):
         assert lib.ramnet_status_str(code).decode() != "unknown status"
 

@@ -1,0 +1,160 @@
+"""GPU parity of the backward pass (ramnet_scan_backward) against the torch
+fp64 autograd oracle (oracle/backward.py).
+
+The GPU replays its own forward (fp32 state) and walks back in fp32; the
+oracle differentiates an fp64 forward.  A unit whose GPU addresses
+legitimately differ from the oracle's at a near-tie follows another valid
+trajectory, and since gradients flow back over the whole sequence, such a
+unit is left out of the comparison entirely.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from sparse_slot_recurrent_amd import synth  # noqa: E402
+
+sys.path.insert(0, os.path.dirname(__file__))
+from parity import compare_address_sets, to_np  # noqa: E402
+
+# |gpu - oracle| <= GRAD_TOL * (|oracle| + rms of the oracle tensor): fp32
+# replay and adjoint against fp64 over a few hundred dependent steps (the
+# worst case seen on these cuts is 1.3e-6, on the logit gradients)
+GRAD_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def rn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_slot_recurrent_amd import ramnet
+    ramnet.load_library()
+    return ramnet
+
+
+@pytest.fixture(scope="module")
+def BWo():
+    import oracle
+    oracle.load()
+    from oracle import backward
+    return backward
+
+
+def dev(a, bf16=False):
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return (t.to(torch.bfloat16) if bf16 else t).cuda()
+
+
+CASES = {
+    "tiny": ("tiny", dict(B=1, T=256, H=1), {}),
+    "top8": ("prefill_top8", dict(B=1, T=96, H=2), {}),
+    "cape3_mask_norm": ("prefill_top8", dict(B=2, T=64, H=2), dict(cape=3, content_heads=0b10, norm=True)),
+    "dp2": ("tiny", dict(B=1, T=80, H=2), dict(d_p=2, U=8, K=5)),
+}
+
+
+def weights_of(orc, w, logits, pos0, T, H, cape, content_heads, U, d_p):
+    lg = logits.reshape(-1, U * d_p)
+    M = d_p ** U
+
+    def f(flat, slots):
+        b, t, h = flat // (T * H), (flat // H) % T, flat % H
+        form = 0 if (content_heads >> min(h, 63)) & 1 else cape
+        slots = np.asarray(slots, np.int64)
+        if form:
+            perm = orc.cape(np.arange(M, dtype=np.int32), int(pos0[b]) + t, U, d_p, form)
+            inv = np.empty(M, np.int64)
+            inv[perm] = np.arange(M)
+            slots = inv[slots]
+        return orc.slot_weights(lg[flat], U, d_p)[slots]
+    return f
+
+
+def close(name, got, ref, mask=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    rms = np.sqrt((ref ** 2).mean()) if ref.size else 0.0
+    err = np.abs(got - ref)
+    worst = float((err / (np.abs(ref) + rms + 1e-30)).max()) if ref.size else 0.0
+    assert np.isfinite(got).all(), name
+    assert (err <= GRAD_TOL * (np.abs(ref) + rms)).all(), (name, worst)
+    return worst
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_matches_oracle(rn, BWo, case):
+    import oracle as orc
+    name, cut, opt = CASES[case]
+    w = synth.WORKLOADS[name].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5), pos0_max=3000,
+                                      cape=opt.get("cape", 1), state_dtype="f32")
+    if "d_p" in opt:
+        w = w.replace(d_p=opt["d_p"], U=opt["U"], K=opt["K"])
+    B, T, H = cut["B"], cut["T"], cut["H"]
+    x = synth.make_inputs(w, B=B, T=T, H=H)
+    r = np.random.default_rng(99)
+    dout = r.standard_normal((B, T, H, w.d_v)).astype(np.float32)
+    dSf = r.standard_normal(x["S0"].shape).astype(np.float32)
+    dmf = r.standard_normal(x["m0"].shape).astype(np.float32)
+    norm_w = (1.0 + 0.25 * np.sin(np.arange(w.d_v))).astype(np.float32) if opt.get("norm") else None
+    mask = opt.get("content_heads", 0)
+    ref = BWo.layer_grads(x["q"], x["k"], x["v"], x["gamma"], x["g"], x["S0"], x["m0"], dout,
+                          d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=x["pos0"], norm_w=norm_w,
+                          content_heads=mask, dS_final=dSf, dm_final=dmf)
+    bf = w.in_dtype == "bf16"
+    d = {n: dev(x[n], bf) for n in ("q", "k", "v", "gamma", "g")}
+    S0, m0 = dev(x["S0"]), dev(x["m0"])
+    S, m = S0.clone(), m0.clone()
+    pos0 = torch.from_numpy(x["pos0"]).cuda()
+    nw = dev(norm_w) if norm_w is not None else None
+    _, addr = rn.scan_prefill(d["q"], d["k"], d["v"], d["gamma"], d["g"], S, m, d_p=w.d_p,
+                              U=w.U, K=w.K, cape=w.cape, pos0=pos0, norm_w=nw,
+                              export_addresses=True, content_heads=mask)
+    got = rn.scan_backward(d["q"], d["k"], d["v"], d["gamma"], d["g"], S0, m0, addr, dev(dout),
+                           d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, norm_w=nw, pos0=pos0,
+                           content_heads=mask, dS_final=dev(dSf), dmass_final=dev(dmf))
+    torch.cuda.synchronize()
+    g_wi, g_ww, g_ri, g_rw = (to_np(a) for a in addr)
+    # the oracle's weights, for the tie-aware comparison of the sets
+    _, o_ww, _ = orc.decode_all(x["k"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"], content_heads=mask)
+    _, o_rw, _ = orc.decode_all(x["q"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"], content_heads=mask)
+    dw = compare_address_sets(g_wi, g_ww, ref["w_idx"], o_ww, ref["w_gap"],
+                              weights_of(orc, w, x["k"], x["pos0"], T, H, w.cape, mask, w.U, w.d_p))
+    dr = compare_address_sets(g_ri, g_rw, ref["r_idx"], o_rw, ref["r_gap"],
+                              weights_of(orc, w, x["q"], x["pos0"], T, H, w.cape, mask, w.U, w.d_p))
+    clean = ~(dw | dr).any(1)            # [B, H]: units with the oracle's sets throughout
+    assert clean.mean() >= 0.5
+    tok = np.broadcast_to(clean[:, None, :], (B, T, H))
+    worst = {}
+    for n, m_ in (("dv", tok), ("dg", tok), ("dgamma", tok), ("dq", tok), ("dk", tok)):
+        worst[n] = close(n, to_np(got[n]), ref[n], m_)
+    worst["dS0"] = close("dS0", to_np(got["dS0"]), ref["dS0"], clean)
+    worst["dm0"] = close("dm0", to_np(got["dmass0"]), ref["dm0"], clean)
+    if clean.all():
+        worst["dnorm_w"] = close("dnorm_w", to_np(got["dnorm_w"]), ref["dnorm_w"])
+    print(case, {k: f"{v:.2e}" for k, v in worst.items()}, "clean units", int(clean.sum()), "of", clean.size)
+
+
+def test_backward_repeatable(rn):
+    """Two calls on the same inputs give the same bits."""
+    w = synth.WORKLOADS["prefill_top8"].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5))
+    B, T, H = 2, 64, 3
+    x = synth.make_inputs(w, B=B, T=T, H=H)
+    d = {n: dev(x[n], True) for n in ("q", "k", "v", "gamma", "g")}
+    S0, m0 = dev(x["S0"]), dev(x["m0"])
+    S, m = S0.clone(), m0.clone()
+    _, addr = rn.scan_prefill(d["q"], d["k"], d["v"], d["gamma"], d["g"], S, m, d_p=w.d_p,
+                              U=w.U, K=w.K, export_addresses=True)
+    dout = dev(np.random.default_rng(5).standard_normal((B, T, H, w.d_v)))
+    runs = [rn.scan_backward(d["q"], d["k"], d["v"], d["gamma"], d["g"], S0, m0, addr, dout,
+                             d_p=w.d_p, U=w.U, K=w.K) for _ in range(2)]
+    torch.cuda.synchronize()
+    for n in runs[0]:
+        if runs[0][n] is not None:
+            assert torch.equal(runs[0][n], runs[1][n]), n
