@@ -9,8 +9,9 @@ before the timed region.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload prefill_top8|prefill_top32|large_state|decode
-                                   |layer_top8|layer_decode]
-The layer_* workloads add the dense projections either side (the whole layer).
+                                   |layer_top8|layer_decode|backward_top8]
+The layer_* workloads add the dense projections either side (the whole layer);
+backward_top8 times the gradients of the Top-8 prefill.
 """
 from __future__ import annotations
 
@@ -330,6 +331,56 @@ def layer_model(w, D, kind: str):
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# Backward workloads: a prefill configuration's gradients (fp32 state).
+BACKWARD = {"backward_top8": "prefill_top8"}
+
+
+def backward_model(w):
+    """Algorithmic bytes of one backward call: per token-head the forward's
+    inputs it reads (v, g, gamma, both logit rows, the K write and K read
+    addresses as index and weight), dout, and the gradients it writes (dq, dk,
+    dv, dg, dgamma, fp32); per (batch, head) unit the state and mass read
+    once and their gradients written once.  The per-step state traffic stays
+    on chip (registers) and is not counted; the records of the replay are
+    implementation traffic and are reported separately."""
+    b_in = 2 if w.in_dtype == "bf16" else 4
+    n = w.B * w.T * w.H
+    units = w.B * w.H
+    per_th = (2 * w.d_v * b_in + b_in + 2 * w.L * b_in + 16 * w.K + 4 * w.d_v
+              + 4 * (2 * w.L + 2 * w.d_v + 1))
+    state = units * 2 * (w.M * w.d_v * 4 + 4 * w.M)
+    records = n * (2 * w.K * w.d_v * 4 + 4 * w.K) * 2  # written by the replay, read back
+    return {"backward": n * per_th + state, "records": records}
+
+
+def bench_backward(torch, rn, w, steps, warmup):
+    """ramnet_scan_backward on the forward's addresses (the forward runs once,
+    outside the timed region)."""
+    from sparse_slot_recurrent_amd import synth
+    x = synth.make_inputs(w.replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5)))
+    bf = w.in_dtype == "bf16"
+    d = {n: to_dev(torch, x[n], w.in_dtype) for n in ("q", "k", "v", "gamma", "g")}
+    S0 = to_dev(torch, x["S0"], "f32")
+    m0 = to_dev(torch, x["m0"], "f32")
+    pos0 = torch.from_numpy(x["pos0"]).cuda()
+    del x
+    S, m = S0.clone(), m0.clone()
+    _, addr = rn.scan_prefill(d["q"], d["k"], d["v"], d["gamma"], d["g"], S, m, d_p=w.d_p,
+                              U=w.U, K=w.K, cape=w.cape, pos0=pos0, export_addresses=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    dout = torch.randn(w.B, w.T, w.H, w.d_v, generator=gen, device="cuda")
+
+    def step(_):
+        rn.scan_backward(d["q"], d["k"], d["v"], d["gamma"], d["g"], S0, m0, addr, dout,
+                         d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=pos0)
+    for _ in range(warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps)
+    torch.cuda.synchronize()
+    return ms, {"backward": ms}, w.B * w.T, {}
+
 
 def bench_layer(torch, rn, w, D, steps, warmup):
     """A whole layer: ramnet_layer_forward (prefill, packing the input
@@ -437,7 +488,10 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     d_model = None
-    if args.workload in LAYERS:
+    backward = args.workload in BACKWARD
+    if backward:
+        w = synth.WORKLOADS[BACKWARD[args.workload]]
+    elif args.workload in LAYERS:
         base, d_model = LAYERS[args.workload]
         w = synth.WORKLOADS[base]
     else:
@@ -455,7 +509,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     extra = {}
-    if d_model is not None:
+    if backward:
+        ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
+    elif d_model is not None:
         ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
     elif kind == "decode":
         ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)
@@ -465,7 +521,14 @@ def main():
     bm = byte_model(w, kind)
     dom = max(kms, key=kms.get)
     roof = None
-    if d_model is not None:
+    if backward:
+        bw = backward_model(w)
+        extra["backward_model"] = bw
+        a = bw["backward"] / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "backward", "achieved": a, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
+                "with_records_gbs": (bw["backward"] + bw["records"]) / (ms / 1e3) / 1e9}
+    elif d_model is not None:
         lm = layer_model(w, d_model, kind)
         extra["layer_model"] = lm
         extra["d_model"] = d_model
@@ -531,7 +594,7 @@ def main():
         "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
     }
     line.update(extra)
-    if not args.no_cpu_baseline and d_model is None:
+    if not args.no_cpu_baseline and d_model is None and not backward:
         line["cpu_baseline"] = cpu_baseline(w, kind)
     print(json.dumps(line), flush=True)
 
