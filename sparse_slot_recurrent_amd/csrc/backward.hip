@@ -9,22 +9,23 @@
 //   bwd_record_kernel   replays the forward from (S0, m0) and records, per
 //                       token, each write's row and mass before the write
 //                       and each read's row after the writes (fp32, in the
-//                       workspace: 2 K d_v + K floats per token-head).
+//                       workspace: 2 K d_v + K floats per token-head).  The
+//                       sequence goes in chunks whose events are grouped by
+//                       slot, each thread walking its own slot's events.
 //   bwd_out_kernel      for all tokens at once (the recorded read rows are all
 //                       it needs): out = y omega sigmoid(g), y = r / rms(r):
 //                         dg, d omega, dr = (dy - y mean(dy y)) / rms(r);
 //                         r = sum_k rho_k S_jk:  drho_k = <dr, S_jk>.
-//   bwd_adjoint_kernel  walks the tokens backwards with thread s holding
-//                       dS[s] (64 registers) and dm[s]; each token's inputs,
-//                       dr and recorded write rows are loaded one token
-//                       ahead and staged in LDS (double-buffered, one barrier
-//                       per token):
+//   bwd_adjoint_kernel  walks the chunks backwards, thread s holding dS[s]
+//                       (64 registers) and dm[s] and walking its slot's
+//                       events of the chunk in reverse time order:
 //                         dS_jk += rho_k dr
 //                         each write, S+ = S- + lam (v - S-),
 //                         m+ = alpha m- + w, lam = w / (m+ + eps),
 //                         alpha = (1 - w)^e, e = exp(gamma):
 //                           dv += lam dS+, dlam = <dS+, v - S->,
-//                           dS- = (1 - lam) dS+,
+//                           dS- = (1 - lam) dS+,   (lam dS+ per write
+//                           goes out; bwd_sum_kernel adds a token's writes)
 //                           dm+ total = dm+ - dlam w / (m+ + eps)^2,
 //                           dw = dlam / (m+ + eps) + dm+ total
 //                                - dm+ total m- e alpha / (1 - w),
@@ -49,63 +50,159 @@ struct Row4 {
     float e[4];
 };
 
-// One token's staged inputs of the serial kernels (double-buffered by token
-// parity, so one barrier per token suffices).
-struct Staged {
-    int w[kKMax], r[kKMax];
-    float wt[kKMax], rt[kKMax], v[kBwdDv], dr[kBwdDv], mm[kKMax];
-    float gam;
+// ---------------------------------------------------------------- slot grouping
+//
+// Both serial kernels take the sequence in chunks of C tokens.  A chunk's
+// 2 C K events (its writes and reads) are grouped by slot with a counting
+// sort in LDS; the thread owning a slot then sorts its few events by time
+// and walks them on its own, with no barrier between tokens (the project
+// page's GPU-execution grouping of events by slot, here for the replay and
+// the adjoint).  An event code is t << 7 | read << 6 | k: ascending order is
+// the forward order (a token's write before its read).
+
+constexpr int kEvMax = 2048;  // events per chunk: 2 C K
+
+struct ChunkLds {
+    int cnt[kBwdNT];       // events per slot, then their offsets
+    int wtot[kBwdNT / kWave];
+    int list[kEvMax];
 };
 
-// The next token's inputs, loaded into registers one token ahead: thread
-// s < K its address pair, s < 64 channel s of v (and of dr), thread 0 gamma.
-struct Prefetch {
-    int w = 0, r = 0;
-    float wt = 0.f, rt = 0.f, v = 0.f, dr = 0.f, mm = 0.f, gam = 0.f;
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Exclusive prefix over the block's threads in thread order.
+__device__ int block_excl_scan_i(int x, int *wtot) {
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const int incl = wave_incl_scan_i(x);
+    if (lane == kWave - 1) wtot[wid] = incl;
+    lds_barrier();
+    if (wid == 0) {
+        int y = lane < nw ? wtot[lane] : 0;
+        y = wave_incl_scan_i(y);
+        if (lane < nw) wtot[lane] = y;
+    }
+    lds_barrier();
+    const int base = wid > 0 ? wtot[wid - 1] : 0;
+    lds_barrier();
+    return base + incl - x;
+}
+
+// Groups the chunk's events by slot: afterwards cnt[s] is slot s's event
+// count and its events are list[base, base + cnt[s]), base returned to
+// thread s (in arbitrary order).  widx/ridx: the chunk's staged write and
+// read slots, [Cc * K] each.
+__device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int nev, int M) {
+    const int s = threadIdx.x;
+    if (s < M) g.cnt[s] = 0;
+    lds_barrier();
+    constexpr int kPer = kEvMax / kBwdNT;
+    int slot[kPer], rank[kPer], code[kPer];
+    const int K2 = 2 * nev;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = s + j * static_cast<int>(blockDim.x);
+        slot[j] = -1;
+        if (e < K2) {
+            const bool rd = e >= nev;
+            const int i = rd ? e - nev : e;
+            const int sl = rd ? ridx[i] : widx[i];
+            if (sl >= 0 && sl < M) {
+                slot[j] = sl;
+                rank[j] = atomicAdd(&g.cnt[sl], 1);
+                code[j] = i;  // t * K + k; the kind goes in below
+                code[j] |= rd ? (1 << 30) : 0;
+            }
+        }
+    }
+    lds_barrier();
+    const int n = s < M ? g.cnt[s] : 0;
+    const int base = block_excl_scan_i(n, g.wtot);
+    if (s < M) g.cnt[s] = base;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if (slot[j] >= 0) g.list[g.cnt[slot[j]] + rank[j]] = code[j];
+    lds_barrier();
+    if (s < M) g.cnt[s] = n;
+    return base;
+}
+
+// Event i = t * K + k, read flag in bit 30 -> sort key t << 7 | read << 6 | k.
+__device__ __forceinline__ int ev_key(int code, int K) {
+    const int i = code & ((1 << 30) - 1), t = i / K, k = i - t * K;
+    return (t << 7) | ((code >> 30) & 1) << 6 | k;
+}
+
+// Insertion sort of a thread's own event keys (ascending), in place.
+__device__ __forceinline__ void sort_keys(int *p, int n) {
+    for (int i = 1; i < n; ++i) {
+        const int x = p[i];
+        int j = i - 1;
+        while (j >= 0 && p[j] > x) {
+            p[j + 1] = p[j];
+            --j;
+        }
+        p[j + 1] = x;
+    }
+}
+
+// Tokens per chunk: C K write events at most kEvMax / 2.
+__host__ __device__ inline int bwd_chunk(int K) {
+    int c = 32;
+    while (c > 1 && c * K > kEvMax / 2) c /= 2;
+    return c;
+}
+
+// A chunk's staged token data.
+struct ChunkTok {
+    int widx[kEvMax / 2], ridx[kEvMax / 2];
+    float wt[kEvMax / 2], rt[kEvMax / 2];
+    float v[32][kBwdDv];
+    float dr[32][kBwdDv];
+    float gam[32];
 };
 
 template <typename TIn, bool ADJ>
-__device__ __forceinline__ void prefetch_token(const BwdArgs &a, int64_t th, int64_t rec, int s,
-                                               Prefetch &p) {
-    const int K = a.K;
-    if (s < K) {
-        p.w = a.w_idx[th * K + s];
-        p.wt = a.w_wt[th * K + s];
-        p.r = a.r_idx[th * K + s];
-        if (ADJ) {
-            p.rt = a.r_wt[th * K + s];
-            p.mm = a.rec_m[rec + s];
-        }
+__device__ void stage_chunk(const BwdArgs &a, ChunkTok &ct, int b, int h, int t0, int Cc) {
+    const int K = a.K, s = threadIdx.x, nt = blockDim.x;
+    const TIn *v = static_cast<const TIn *>(a.v);
+    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    for (int i = s; i < Cc * K; i += nt) {
+        const int t = i / K, k = i - t * K;
+        const int64_t e = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * K + k;
+        ct.widx[i] = a.w_idx[e];
+        ct.wt[i] = a.w_wt[e];
+        ct.ridx[i] = a.r_idx[e];
+        ct.rt[i] = a.r_wt[e];
     }
-    if (s < kBwdDv) {
-        p.v = to_f32(static_cast<const TIn *>(a.v)[th * kBwdDv + s]);
-        if (ADJ) p.dr = a.dr[th * kBwdDv + s];
+    for (int i = s; i < Cc * kBwdDv; i += nt) {
+        const int t = i / kBwdDv, c = i - t * kBwdDv;
+        const int64_t th = (static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h;
+        ct.v[t][c] = to_f32(v[th * kBwdDv + c]);
+        if (ADJ) ct.dr[t][c] = a.dr[th * kBwdDv + c];
     }
-    if (s == 0) p.gam = to_f32(static_cast<const TIn *>(a.gamma)[th]);
-}
-
-__device__ __forceinline__ void stage_token(Staged &st, const Prefetch &p, int s, int K) {
-    if (s < K) {
-        st.w[s] = p.w;
-        st.wt[s] = p.wt;
-        st.r[s] = p.r;
-        st.rt[s] = p.rt;
-        st.mm[s] = p.mm;
-    }
-    if (s < kBwdDv) {
-        st.v[s] = p.v;
-        st.dr[s] = p.dr;
-    }
-    if (s == 0) st.gam = p.gam;
+    for (int t = s; t < Cc; t += nt)
+        ct.gam[t] = to_f32(gam[(static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h]);
 }
 
 template <typename TIn>
 __global__ __launch_bounds__(kBwdNT) void bwd_record_kernel(BwdArgs a) {
-    __shared__ Staged stg[2];
+    __shared__ ChunkLds g;
+    __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x, K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
     const bool own = s < M;
+    const int C = bwd_chunk(K);
     float row[kBwdDv];
     float m = 0.f;
     if (own) {
@@ -118,40 +215,36 @@ __global__ __launch_bounds__(kBwdNT) void bwd_record_kernel(BwdArgs a) {
         }
         m = a.mass0[static_cast<int64_t>(unit) * M + s];
     }
-    auto th_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * a.H + h; };
-    Prefetch pf;
-    prefetch_token<TIn, false>(a, th_of(0), 0, s, pf);
-    for (int t = 0; t < T; ++t) {
-        Staged &st = stg[t & 1];
-        stage_token(st, pf, s, K);
-        if (t + 1 < T) prefetch_token<TIn, false>(a, th_of(t + 1), 0, s, pf);
-        __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += C) {
+        const int Cc = min(C, T - t0), nev = Cc * K;
+        stage_chunk<TIn, false>(a, ct, b, h, t0, Cc);
+        lds_barrier();
+        const int base = group_events(g, ct.widx, ct.ridx, nev, M);
         if (own) {
-            const int64_t rec = (static_cast<int64_t>(unit) * T + t) * K;
-            for (int k = 0; k < K; ++k) {
-                if (st.w[k] != s) continue;  // write slots are distinct: at most one
-                Row4 *dst = reinterpret_cast<Row4 *>(a.rec_w + (rec + k) * kBwdDv);
+            const int n = g.cnt[s];
+            int *ev = g.list + base;
+            for (int i = 0; i < n; ++i) ev[i] = ev_key(ev[i], K);
+            sort_keys(ev, n);
+            for (int i = 0; i < n; ++i) {
+                const int key = ev[i], t = key >> 7, k = key & 63, e = t * K + k;
+                const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+                Row4 *dst = reinterpret_cast<Row4 *>((key & 64 ? a.rec_r : a.rec_w) + rec * kBwdDv);
 #pragma unroll
                 for (int j = 0; j < kBwdDv / 4; ++j)
                     dst[j] = Row4{{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]}};
-                a.rec_m[rec + k] = m;
-                const float w = st.wt[k];
+                if (key & 64) continue;  // a read: recorded
+                a.rec_m[rec] = m;
+                const float w = ct.wt[e];
                 if (w > 0.f) {
-                    const float alpha = retention(w, expf(st.gam));
+                    const float alpha = retention(w, expf(ct.gam[t]));
                     m = fmaf(alpha, m, w);
                     const float lam = w / (m + a.eps_gsu);
 #pragma unroll
-                    for (int c = 0; c < kBwdDv; ++c) row[c] = fmaf(lam, st.v[c] - row[c], row[c]);
+                    for (int c = 0; c < kBwdDv; ++c) row[c] = fmaf(lam, ct.v[t][c] - row[c], row[c]);
                 }
             }
-            for (int k = 0; k < K; ++k) {
-                if (st.r[k] != s) continue;
-                Row4 *dst = reinterpret_cast<Row4 *>(a.rec_r + (rec + k) * kBwdDv);
-#pragma unroll
-                for (int j = 0; j < kBwdDv / 4; ++j)
-                    dst[j] = Row4{{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]}};
-            }
         }
+        lds_barrier();
     }
 }
 
@@ -202,17 +295,13 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
 
 template <typename TIn>
 __global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
-    __shared__ Staged stg[2];
-    // dynamic: per token parity q, the writes' rows before them [K][64],
-    // lam dS+ per write [K][64], and the gamma terms [K]
-    extern __shared__ float dyn[];
+    __shared__ ChunkLds g;
+    __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x, K = a.K, T = a.T;
-    auto sSm = [&](int q, int k) { return dyn + (static_cast<int64_t>(q) * K + k) * kBwdDv; };
-    auto sdv = [&](int q, int k) { return dyn + (static_cast<int64_t>(2 + q) * K + k) * kBwdDv; };
-    float *sdgk = dyn + 4 * K * kBwdDv;  // [2][K]
     const int M = static_cast<int>(a.M);
     const bool own = s < M;
+    const int C = bwd_chunk(K);
     const int64_t srow = (static_cast<int64_t>(unit) * M + s) * kBwdDv;
     float dS[kBwdDv];
     float dm = 0.f;
@@ -228,98 +317,70 @@ __global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
         }
     }
     if (own && a.dmass_final) dm = a.dmass_final[static_cast<int64_t>(unit) * M + s];
-    auto th_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * a.H + h; };
-    auto rec_of = [&](int t) { return (static_cast<int64_t>(unit) * T + t) * K; };
-    // the recorded rows of the writes: thread s < 16 K holds 16 bytes
-    const bool rows_lane = s < K * (kBwdDv / 4);
-    Row4 pf_row{};
-    auto prefetch_rows = [&](int t) {
-        if (rows_lane) pf_row = reinterpret_cast<const Row4 *>(a.rec_w + rec_of(t) * kBwdDv)[s];
-    };
-    // token t's sums of lam dS+ and of the gamma terms (wave 0, after the
-    // next token's barrier)
-    auto finish = [&](int t) {
-        const int q = t & 1;
-        const Staged &st = stg[q];
-        const int64_t th = th_of(t);
-        if (s < kBwdDv) {
-            float acc = 0.f;
-            for (int k = 0; k < K; ++k)
-                if (st.wt[k] > 0.f && st.w[k] >= 0 && st.w[k] < M) acc += sdv(q, k)[s];
-            a.dv[th * kBwdDv + s] = acc;
-        }
-        if (s == 0) {
-            float acc = 0.f;
-            for (int k = 0; k < K; ++k)
-                if (st.wt[k] > 0.f && st.w[k] >= 0 && st.w[k] < M) acc += sdgk[q * K + k];
-            a.dgamma[th] = acc;
-        }
-    };
-    Prefetch pf;
-    prefetch_token<TIn, true>(a, th_of(T - 1), rec_of(T - 1), s, pf);
-    prefetch_rows(T - 1);
-    for (int t = T - 1; t >= 0; --t) {
-        const int q = t & 1;
-        Staged &st = stg[q];
-        stage_token(st, pf, s, K);
-        if (rows_lane) {
-            const int k = s / (kBwdDv / 4), j = s % (kBwdDv / 4);
-            *reinterpret_cast<Row4 *>(sSm(q, k) + 4 * j) = pf_row;
-        }
-        if (t > 0) {
-            prefetch_token<TIn, true>(a, th_of(t - 1), rec_of(t - 1), s, pf);
-            prefetch_rows(t - 1);
-        }
-        __syncthreads();
-        if (t + 1 < T) finish(t + 1);
+    const int nch = (T + C - 1) / C;
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const int t0 = ci * C, Cc = min(C, T - t0), nev = Cc * K;
+        stage_chunk<TIn, true>(a, ct, b, h, t0, Cc);
+        lds_barrier();
+        const int base = group_events(g, ct.widx, ct.ridx, nev, M);
         if (own) {
-            const int64_t th = th_of(t);
-            // the read came after the writes: its adjoint goes in first
-            for (int k = 0; k < K; ++k) {
-                if (st.r[k] != s) continue;
-                const float rho = st.rt[k];
+            const int n = g.cnt[s];
+            int *ev = g.list + base;
+            for (int i = 0; i < n; ++i) ev[i] = ev_key(ev[i], K);
+            sort_keys(ev, n);
+            // backwards: a token's read before its write
+            for (int i = n - 1; i >= 0; --i) {
+                const int key = ev[i], t = key >> 7, k = key & 63, e = t * K + k;
+                if (key & 64) {
+                    const float rho = ct.rt[e];
 #pragma unroll
-                for (int c = 0; c < kBwdDv; ++c) dS[c] = fmaf(rho, st.dr[c], dS[c]);
-            }
-            for (int k = K - 1; k >= 0; --k) {
-                if (st.w[k] != s) continue;
-                const float w = st.wt[k];
+                    for (int c = 0; c < kBwdDv; ++c) dS[c] = fmaf(rho, ct.dr[t][c], dS[c]);
+                    continue;
+                }
+                const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+                const float w = ct.wt[e];
                 float dw = 0.f, dgk = 0.f;
+                float *dvk = a.dvk + rec * kBwdDv;
                 if (w > 0.f) {
-                    const float mm = st.mm[k];
-                    const float e = expf(st.gam);
-                    const float alpha = retention(w, e);
+                    const float mm = a.rec_m[rec];
+                    const float eg = expf(ct.gam[t]);
+                    const float alpha = retention(w, eg);
                     const float mp = fmaf(alpha, mm, w);
                     const float den = mp + a.eps_gsu;
                     const float lam = w / den;
+                    const Row4 *sm = reinterpret_cast<const Row4 *>(a.rec_w + rec * kBwdDv);
                     float dl = 0.f;
-                    {
-                        const float *sm = sSm(q, k);
 #pragma unroll
-                        for (int c = 0; c < kBwdDv; ++c) dl = fmaf(dS[c], st.v[c] - sm[c], dl);
+                    for (int j = 0; j < kBwdDv / 4; ++j) {
+                        const Row4 x = sm[j];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) dl = fmaf(dS[4 * j + c], ct.v[t][4 * j + c] - x.e[c], dl);
                     }
-                    float *dvk = sdv(q, k);
 #pragma unroll
-                    for (int c = 0; c < kBwdDv; ++c) {
-                        dvk[c] = lam * dS[c];
-                        dS[c] *= 1.0f - lam;
+                    for (int j = 0; j < kBwdDv / 4; ++j) {
+                        reinterpret_cast<Row4 *>(dvk)[j] =
+                            Row4{{lam * dS[4 * j], lam * dS[4 * j + 1], lam * dS[4 * j + 2], lam * dS[4 * j + 3]}};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) dS[4 * j + c] *= 1.0f - lam;
                     }
                     const float dmt = dm - dl * w / (den * den);
                     const float dalpha = dmt * mm;
                     dm = dmt * alpha;
                     dw = dl / den + dmt;
                     if (w < 1.0f && alpha > 0.f) {
-                        dw -= dalpha * e * alpha / (1.0f - w);
-                        dgk = dalpha * alpha * log1pf(-w) * e;
+                        dw -= dalpha * eg * alpha / (1.0f - w);
+                        dgk = dalpha * alpha * log1pf(-w) * eg;
                     }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kBwdDv / 4; ++j) reinterpret_cast<Row4 *>(dvk)[j] = Row4{{0.f, 0.f, 0.f, 0.f}};
                 }
-                sdgk[q * K + k] = dgk;
-                a.dw[th * K + k] = dw;
+                a.dgk[rec] = dgk;
+                a.dw[((static_cast<int64_t>(b) * T + t0 + t) * a.H + h) * K + k] = dw;
             }
         }
+        lds_barrier();
     }
-    __syncthreads();
-    finish(0);
     if (own) {
         Row4 *dst = reinterpret_cast<Row4 *>(a.dS0 + srow);
 #pragma unroll
@@ -327,6 +388,27 @@ __global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
             dst[j] = Row4{{dS[4 * j], dS[4 * j + 1], dS[4 * j + 2], dS[4 * j + 3]}};
         a.dmass0[static_cast<int64_t>(unit) * M + s] = dm;
     }
+}
+
+// dv and dgamma of every token: the sums over its writes of lam dS+ and of
+// the gamma terms, in write order (one wave per token-head, lane = channel).
+__global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
+    const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
+    const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+    const int c = threadIdx.x % kWave, K = a.K;
+    if (th >= n) return;
+    const int64_t b = th / (static_cast<int64_t>(a.T) * a.H), t = (th / a.H) % a.T;
+    const int h = static_cast<int>(th % a.H);
+    const int64_t rec = ((b * a.H + h) * a.T + t) * K;
+    float acc = 0.f, gacc = 0.f;
+    for (int k = 0; k < K; ++k) {
+        const int slot = a.w_idx[th * K + k];
+        if (!(a.w_wt[th * K + k] > 0.f) || slot < 0 || slot >= a.M) continue;
+        acc += a.dvk[(rec + k) * kBwdDv + c];
+        gacc += a.dgk[rec + k];
+    }
+    a.dv[th * kBwdDv + c] = acc;
+    if (c == 0) a.dgamma[th] = gacc;
 }
 
 // The position whose CAPE move undoes the move at pos (forms 1 and 3: the
@@ -391,19 +473,26 @@ __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
     for (int j = 0; j < L; ++j) out[i * L + j] = dl[j];
 }
 
-__global__ __launch_bounds__(kBwdDv) void bwd_omega_kernel(const float *part, int units,
-                                                          float *out) {
-    const int c = threadIdx.x;
+// Sums the partials [n][64] in a fixed order: 16 groups of 64 threads take
+// interleaved partials, then group 0 adds the 16 group sums in order.
+__global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int n, float *out) {
+    __shared__ float gsum[16][kBwdDv];
+    const int c = threadIdx.x % kBwdDv, grp = threadIdx.x / kBwdDv;
     float acc = 0.f;
-    for (int u = 0; u < units; ++u) acc += part[static_cast<int64_t>(u) * kBwdDv + c];
-    out[c] = acc;
+    for (int u = grp; u < n; u += 16) acc += part[static_cast<int64_t>(u) * kBwdDv + c];
+    gsum[grp][c] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float tot = 0.f;
+        for (int j = 0; j < 16; ++j) tot += gsum[j][c];
+        out[c] = tot;
+    }
 }
 
 template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
-    const int nt = static_cast<int>(((a.M + kWave - 1) / kWave) * kWave);
-    const int threads = nt < kWave ? kWave : nt;
+    const int threads = kBwdNT;  // every thread takes a share of a chunk's events
     hipLaunchKernelGGL(bwd_record_kernel<TIn>, dim3(units), dim3(threads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -411,10 +500,16 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (4 * static_cast<size_t>(a.K) * kBwdDv + 2 * a.K) * sizeof(float);
-    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, dim3(units), dim3(threads), lds, st, a);
+    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, dim3(units), dim3(threads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    {
+        const int64_t n = static_cast<int64_t>(units) * a.T;
+        hipLaunchKernelGGL(bwd_sum_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
+                           st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (a.dq || a.dk) {
         const int64_t n = static_cast<int64_t>(units) * a.T;
         hipLaunchKernelGGL(bwd_logits_kernel<TIn>, dim3(static_cast<unsigned>((n + 255) / 256), 2),
@@ -423,7 +518,7 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (a.dnorm_w) {
-        hipLaunchKernelGGL(bwd_omega_kernel, dim3(1), dim3(kBwdDv), 0, st, a.dom_part,
+        hipLaunchKernelGGL(bwd_omega_kernel, dim3(1), dim3(1024), 0, st, a.dom_part,
                            units * kOutBlocks, a.dnorm_w);
         e = hipGetLastError();
     }
@@ -440,7 +535,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int K) {
     const size_t units = static_cast<size_t>(B) * H;
     const size_t n = units * T;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    return 2 * al(n * K * kBwdDv * 4) + 3 * al(n * K * 4) + al(units * kOutBlocks * kBwdDv * 4) +
+    return 3 * al(n * K * kBwdDv * 4) + 4 * al(n * K * 4) + al(units * kOutBlocks * kBwdDv * 4) +
            al(n * kBwdDv * 4);
 }
 

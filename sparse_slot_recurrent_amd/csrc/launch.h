@@ -134,7 +134,7 @@ struct BwdArgs {
     const float *dout, *dS_final, *dmass_final;
     float *dq, *dk, *dv, *dgamma, *dg, *dnorm_w, *dS0, *dmass0;
     // workspace: per token-head records and weight gradients, per unit d omega
-    float *rec_w, *rec_r, *rec_m, *dw, *drho, *dom_part, *dr;
+    float *rec_w, *rec_r, *rec_m, *dw, *drho, *dom_part, *dr, *dvk, *dgk;
 };
 bool backward_supported(int64_t M, int d_v, int U, int d_p, bool state_bf16);
 size_t backward_workspace_bytes(int B, int T, int H, int K);
