@@ -43,7 +43,8 @@ namespace ramnet {
 namespace {
 
 constexpr int kBwdDv = 64;
-constexpr int kBwdNT = 1024;
+constexpr int kBwdNT = 1024;  // largest M
+constexpr int kSlotsPerWG = 256;  // the serial kernels split a unit's slots over workgroups
 constexpr int kKMax = 64;
 
 struct Row4 {
@@ -63,8 +64,8 @@ struct Row4 {
 constexpr int kEvMax = 2048;  // events per chunk: 2 C K
 
 struct ChunkLds {
-    int cnt[kBwdNT];       // events per slot, then their offsets
-    int wtot[kBwdNT / kWave];
+    int cnt[kSlotsPerWG];  // events per slot, then their offsets
+    int wtot[kSlotsPerWG / kWave];
     int list[kEvMax];
 };
 
@@ -96,15 +97,16 @@ __device__ int block_excl_scan_i(int x, int *wtot) {
     return base + incl - x;
 }
 
-// Groups the chunk's events by slot: afterwards cnt[s] is slot s's event
-// count and its events are list[base, base + cnt[s]), base returned to
-// thread s (in arbitrary order).  widx/ridx: the chunk's staged write and
-// read slots, [Cc * K] each.
-__device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int nev, int M) {
+// Groups the chunk's events on this workgroup's slots [slot0, slot0 + NT)
+// by slot: afterwards cnt[s] is slot slot0 + s's event count and its events
+// are list[base, base + cnt[s]), base returned to thread s (in arbitrary
+// order).  widx/ridx: the chunk's staged write and read slots, [Cc K] each.
+__device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int nev, int slot0,
+                            int nslots) {
     const int s = threadIdx.x;
-    if (s < M) g.cnt[s] = 0;
+    g.cnt[s] = 0;
     lds_barrier();
-    constexpr int kPer = kEvMax / kBwdNT;
+    constexpr int kPer = kEvMax / kSlotsPerWG;
     int slot[kPer], rank[kPer], code[kPer];
     const int K2 = 2 * nev;
 #pragma unroll
@@ -114,8 +116,8 @@ __device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int n
         if (e < K2) {
             const bool rd = e >= nev;
             const int i = rd ? e - nev : e;
-            const int sl = rd ? ridx[i] : widx[i];
-            if (sl >= 0 && sl < M) {
+            const int sl = (rd ? ridx[i] : widx[i]) - slot0;
+            if (sl >= 0 && sl < nslots) {
                 slot[j] = sl;
                 rank[j] = atomicAdd(&g.cnt[sl], 1);
                 code[j] = i;  // t * K + k; the kind goes in below
@@ -124,15 +126,15 @@ __device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int n
         }
     }
     lds_barrier();
-    const int n = s < M ? g.cnt[s] : 0;
+    const int n = g.cnt[s];
     const int base = block_excl_scan_i(n, g.wtot);
-    if (s < M) g.cnt[s] = base;
+    g.cnt[s] = base;
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         if (slot[j] >= 0) g.list[g.cnt[slot[j]] + rank[j]] = code[j];
     lds_barrier();
-    if (s < M) g.cnt[s] = n;
+    g.cnt[s] = n;
     return base;
 }
 
@@ -155,9 +157,10 @@ __device__ __forceinline__ void sort_keys(int *p, int n) {
     }
 }
 
-// Tokens per chunk: C K write events at most kEvMax / 2.
+// Tokens per chunk: at most 64, and C K write events at most kEvMax / 2.
+constexpr int kChunkMax = 64;
 __host__ __device__ inline int bwd_chunk(int K) {
-    int c = 32;
+    int c = kChunkMax;
     while (c > 1 && c * K > kEvMax / 2) c /= 2;
     return c;
 }
@@ -166,60 +169,106 @@ __host__ __device__ inline int bwd_chunk(int K) {
 struct ChunkTok {
     int widx[kEvMax / 2], ridx[kEvMax / 2];
     float wt[kEvMax / 2], rt[kEvMax / 2];
-    float v[32][kBwdDv];
-    float dr[32][kBwdDv];
-    float gam[32];
+    float v[kChunkMax][kBwdDv];
+    float dr[kChunkMax][kBwdDv];
+    float gam[kChunkMax];
+};
+
+// The same data for the next chunk, loaded into registers while this chunk
+// is walked (thread s takes entries s, s + NT, ...).
+constexpr int kPfA = kEvMax / 2 / kSlotsPerWG;
+constexpr int kPfV = kChunkMax * kBwdDv / kSlotsPerWG;
+struct ChunkPf {
+    int w[kPfA], r[kPfA];
+    float wt[kPfA], rt[kPfA], v[kPfV], dr[kPfV], gam;
 };
 
 template <typename TIn, bool ADJ>
-__device__ void stage_chunk(const BwdArgs &a, ChunkTok &ct, int b, int h, int t0, int Cc) {
-    const int K = a.K, s = threadIdx.x, nt = blockDim.x;
+__device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf &p, int b, int h, int t0,
+                                           int Cc) {
+    const int K = a.K, s = threadIdx.x;
     const TIn *v = static_cast<const TIn *>(a.v);
     const TIn *gam = static_cast<const TIn *>(a.gamma);
-    for (int i = s; i < Cc * K; i += nt) {
-        const int t = i / K, k = i - t * K;
-        const int64_t e = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * K + k;
-        ct.widx[i] = a.w_idx[e];
-        ct.wt[i] = a.w_wt[e];
-        ct.ridx[i] = a.r_idx[e];
-        ct.rt[i] = a.r_wt[e];
+#pragma unroll
+    for (int j = 0; j < kPfA; ++j) {
+        const int i = s + j * kSlotsPerWG;
+        if (i < Cc * K) {
+            const int t = i / K, k = i - t * K;
+            const int64_t e = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * K + k;
+            p.w[j] = a.w_idx[e];
+            p.wt[j] = a.w_wt[e];
+            p.r[j] = a.r_idx[e];
+            if (ADJ) p.rt[j] = a.r_wt[e];
+        }
     }
-    for (int i = s; i < Cc * kBwdDv; i += nt) {
-        const int t = i / kBwdDv, c = i - t * kBwdDv;
-        const int64_t th = (static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h;
-        ct.v[t][c] = to_f32(v[th * kBwdDv + c]);
-        if (ADJ) ct.dr[t][c] = a.dr[th * kBwdDv + c];
+#pragma unroll
+    for (int j = 0; j < kPfV; ++j) {
+        const int i = s + j * kSlotsPerWG;
+        if (i < Cc * kBwdDv) {
+            const int t = i / kBwdDv, c = i - t * kBwdDv;
+            const int64_t th = (static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h;
+            p.v[j] = to_f32(v[th * kBwdDv + c]);
+            if (ADJ) p.dr[j] = a.dr[th * kBwdDv + c];
+        }
     }
-    for (int t = s; t < Cc; t += nt)
-        ct.gam[t] = to_f32(gam[(static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h]);
+    if (s < Cc) p.gam = to_f32(gam[(static_cast<int64_t>(b) * a.T + t0 + s) * a.H + h]);
+}
+
+template <bool ADJ>
+__device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int Cc, int K) {
+    const int s = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kPfA; ++j) {
+        const int i = s + j * kSlotsPerWG;
+        if (i < Cc * K) {
+            ct.widx[i] = p.w[j];
+            ct.wt[i] = p.wt[j];
+            ct.ridx[i] = p.r[j];
+            if (ADJ) ct.rt[i] = p.rt[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPfV; ++j) {
+        const int i = s + j * kSlotsPerWG;
+        if (i < Cc * kBwdDv) {
+            ct.v[i / kBwdDv][i % kBwdDv] = p.v[j];
+            if (ADJ) ct.dr[i / kBwdDv][i % kBwdDv] = p.dr[j];
+        }
+    }
+    if (s < Cc) ct.gam[s] = p.gam;
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(kBwdNT) void bwd_record_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
     __shared__ ChunkLds g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x, K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
-    const bool own = s < M;
+    const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
+    const int nslots = min(kSlotsPerWG, M - slot0);
+    const bool own = s < nslots;
     const int C = bwd_chunk(K);
     float row[kBwdDv];
     float m = 0.f;
     if (own) {
-        const Row4 *src = reinterpret_cast<const Row4 *>(a.S0 + (static_cast<int64_t>(unit) * M + s) * kBwdDv);
+        const Row4 *src = reinterpret_cast<const Row4 *>(a.S0 + (static_cast<int64_t>(unit) * M + slot) * kBwdDv);
 #pragma unroll
         for (int j = 0; j < kBwdDv / 4; ++j) {
             const Row4 x = src[j];
 #pragma unroll
             for (int c = 0; c < 4; ++c) row[4 * j + c] = x.e[c];
         }
-        m = a.mass0[static_cast<int64_t>(unit) * M + s];
+        m = a.mass0[static_cast<int64_t>(unit) * M + slot];
     }
+    ChunkPf pf;
+    load_chunk<TIn, false>(a, pf, b, h, 0, min(C, T));
     for (int t0 = 0; t0 < T; t0 += C) {
         const int Cc = min(C, T - t0), nev = Cc * K;
-        stage_chunk<TIn, false>(a, ct, b, h, t0, Cc);
+        store_chunk<false>(ct, pf, Cc, K);
         lds_barrier();
-        const int base = group_events(g, ct.widx, ct.ridx, nev, M);
+        if (t0 + C < T) load_chunk<TIn, false>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
+        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots);
         if (own) {
             const int n = g.cnt[s];
             int *ev = g.list + base;
@@ -294,15 +343,17 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
     __shared__ ChunkLds g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x, K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
-    const bool own = s < M;
+    const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
+    const int nslots = min(kSlotsPerWG, M - slot0);
+    const bool own = s < nslots;
     const int C = bwd_chunk(K);
-    const int64_t srow = (static_cast<int64_t>(unit) * M + s) * kBwdDv;
+    const int64_t srow = (static_cast<int64_t>(unit) * M + slot) * kBwdDv;
     float dS[kBwdDv];
     float dm = 0.f;
 #pragma unroll
@@ -316,13 +367,16 @@ __global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
             for (int c = 0; c < 4; ++c) dS[4 * j + c] = x.e[c];
         }
     }
-    if (own && a.dmass_final) dm = a.dmass_final[static_cast<int64_t>(unit) * M + s];
+    if (own && a.dmass_final) dm = a.dmass_final[static_cast<int64_t>(unit) * M + slot];
     const int nch = (T + C - 1) / C;
+    ChunkPf pf;
+    load_chunk<TIn, true>(a, pf, b, h, (nch - 1) * C, T - (nch - 1) * C);
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int t0 = ci * C, Cc = min(C, T - t0), nev = Cc * K;
-        stage_chunk<TIn, true>(a, ct, b, h, t0, Cc);
+        store_chunk<true>(ct, pf, Cc, K);
         lds_barrier();
-        const int base = group_events(g, ct.widx, ct.ridx, nev, M);
+        if (ci > 0) load_chunk<TIn, true>(a, pf, b, h, t0 - C, C);
+        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots);
         if (own) {
             const int n = g.cnt[s];
             int *ev = g.list + base;
@@ -386,7 +440,7 @@ __global__ __launch_bounds__(kBwdNT) void bwd_adjoint_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < kBwdDv / 4; ++j)
             dst[j] = Row4{{dS[4 * j], dS[4 * j + 1], dS[4 * j + 2], dS[4 * j + 3]}};
-        a.dmass0[static_cast<int64_t>(unit) * M + s] = dm;
+        a.dmass0[static_cast<int64_t>(unit) * M + slot] = dm;
     }
 }
 
@@ -424,53 +478,67 @@ __device__ __forceinline__ int64_t cape_inverse_pos(int64_t pos, int form, int d
     return static_cast<int64_t>(inv);
 }
 
-template <typename TIn>
+// One level (digit block) at a time, so that the level's d_p probabilities
+// and gradients stay in registers.
+template <typename TIn, int DP>
 __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
-    constexpr int kMaxL = 64;
     const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const bool key = blockIdx.y == 0;
     float *out = key ? a.dk : a.dq;
     if (!out) return;
-    const int U = a.U, dp = a.d_p, L = U * dp, K = a.K;
-    const TIn *lg = static_cast<const TIn *>(key ? a.k : a.q) + i * L;
+    const int U = a.U, K = a.K;
+    const TIn *lg = static_cast<const TIn *>(key ? a.k : a.q) + i * U * DP;
     const int32_t *idx = (key ? a.w_idx : a.r_idx) + i * K;
     const float *wt = (key ? a.w_wt : a.r_wt) + i * K;
     const float *gr = (key ? a.dw : a.drho) + i * K;
-    float p[kMaxL], dl[kMaxL];
-    for (int u = 0; u < U; ++u) {
-        float mx = to_f32(lg[u * dp]);
-        for (int d = 1; d < dp; ++d) mx = fmaxf(mx, to_f32(lg[u * dp + d]));
-        float sum = 0.f;
-        for (int d = 0; d < dp; ++d) {
-            p[u * dp + d] = expf(to_f32(lg[u * dp + d]) - mx);
-            sum += p[u * dp + d];
-        }
-        for (int d = 0; d < dp; ++d) {
-            p[u * dp + d] /= sum;
-            dl[u * dp + d] = 0.f;
-        }
-    }
     const int64_t b = i / (static_cast<int64_t>(a.T) * a.H), t = (i / a.H) % a.T;
     const int h = static_cast<int>(i % a.H);
     const int form = head_uses_cape(a.content_heads, h) ? a.cape : 0;
     const int64_t pos = (a.pos0 ? a.pos0[b] : 0) + t;
-    const int64_t ipos = cape_inverse_pos(pos, form, dp, U, a.M);
-    for (int k = 0; k < K; ++k) {
-        const int slot = idx[k];
-        if (slot < 0 || slot >= a.M) continue;
-        const float coef = gr[k] * wt[k];
-        int content = form ? cape_slot<0>(slot, ipos, U, dp, form, a.M) : slot;
-        // digits from the least significant (u = U - 1) up
-        for (int u = U - 1; u >= 0; --u) {
-            const int digit = content % dp;
-            content /= dp;
-            for (int d = 0; d < dp; ++d) dl[u * dp + d] -= coef * p[u * dp + d];
-            dl[u * dp + digit] += coef;
+    const int64_t ipos = cape_inverse_pos(pos, form, DP, U, a.M);
+    int place = 1;  // DP^(U - 1 - u)
+    for (int u = 1; u < U; ++u) place *= DP;
+    for (int u = 0; u < U; ++u, place /= DP) {
+        float p[DP], dl[DP];
+        float mx = to_f32(lg[u * DP]);
+#pragma unroll
+        for (int d = 1; d < DP; ++d) mx = fmaxf(mx, to_f32(lg[u * DP + d]));
+        float sum = 0.f;
+#pragma unroll
+        for (int d = 0; d < DP; ++d) {
+            p[d] = expf(to_f32(lg[u * DP + d]) - mx);
+            sum += p[d];
+            dl[d] = 0.f;
         }
+#pragma unroll
+        for (int d = 0; d < DP; ++d) p[d] /= sum;
+        for (int k = 0; k < K; ++k) {
+            const int slot = idx[k];
+            if (slot < 0 || slot >= a.M) continue;
+            const float coef = gr[k] * wt[k];
+            const int content = form ? cape_slot<DP>(slot, ipos, U, DP, form, a.M) : slot;
+            const int digit = (content / place) % DP;
+#pragma unroll
+            for (int d = 0; d < DP; ++d) dl[d] = fmaf(-coef, p[d], dl[d] + (d == digit ? coef : 0.f));
+        }
+#pragma unroll
+        for (int d = 0; d < DP; ++d) out[i * U * DP + u * DP + d] = dl[d];
     }
-    for (int j = 0; j < L; ++j) out[i * L + j] = dl[j];
+}
+
+template <typename TIn>
+hipError_t launch_logits(const BwdArgs &a, dim3 grid, hipStream_t st) {
+    switch (a.d_p) {
+#define RAMNET_LOGITS_DP(D) \
+    case D: hipLaunchKernelGGL((bwd_logits_kernel<TIn, D>), grid, dim3(256), 0, st, a); break;
+        RAMNET_LOGITS_DP(2) RAMNET_LOGITS_DP(3) RAMNET_LOGITS_DP(4) RAMNET_LOGITS_DP(5)
+        RAMNET_LOGITS_DP(6) RAMNET_LOGITS_DP(7) RAMNET_LOGITS_DP(8)
+#undef RAMNET_LOGITS_DP
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // Sums the partials [n][64] in a fixed order: 16 groups of 64 threads take
@@ -492,15 +560,15 @@ __global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int 
 template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
-    const int threads = kBwdNT;  // every thread takes a share of a chunk's events
-    hipLaunchKernelGGL(bwd_record_kernel<TIn>, dim3(units), dim3(threads), 0, st, a);
+    const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
+    hipLaunchKernelGGL(bwd_record_kernel<TIn>, grid, dim3(kSlotsPerWG), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, dim3(units), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, grid, dim3(kSlotsPerWG), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
@@ -512,9 +580,7 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     }
     if (a.dq || a.dk) {
         const int64_t n = static_cast<int64_t>(units) * a.T;
-        hipLaunchKernelGGL(bwd_logits_kernel<TIn>, dim3(static_cast<unsigned>((n + 255) / 256), 2),
-                           dim3(256), 0, st, a);
-        e = hipGetLastError();
+        e = launch_logits<TIn>(a, dim3(static_cast<unsigned>((n + 255) / 256), 2), st);
         if (e != hipSuccess) return e;
     }
     if (a.dnorm_w) {
