@@ -131,7 +131,7 @@ def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
     z = lambda t: np.zeros(t.shape) if t.grad is None else t.grad.numpy()
     return {
         "out": out.detach().numpy(), "S": S_f.detach().numpy(), "mass": m_f.detach().numpy(),
-        "loss": float(loss), "w_idx": w_idx, "r_idx": r_idx, "w_gap": w_gap, "r_gap": r_gap,
+        "loss": float(loss.detach()), "w_idx": w_idx, "r_idx": r_idx, "w_gap": w_gap, "r_gap": r_gap,
         "dq": z(tq), "dk": z(tk), "dv": z(tv), "dgamma": z(tgam), "dg": z(tg),
         "dS0": z(tS0), "dm0": z(tm0), "dnorm_w": z(tom),
     }

@@ -256,3 +256,38 @@ def test_pack_rejects_short_buffer(rn):
     st = lib.ramnet_pack_weights(C.byref(p), C.byref(w), C.c_void_p(FAKE + (40 << 32)),
                                  1000, None)
     assert st == -1 and "packed needs" in lib.ramnet_last_error().decode()
+
+
+def call_backward(rn, p, **kw):
+    lib = rn.load_library()
+    ptrs = {n: C.c_void_p(FAKE + ((50 + i) << 32)) for i, n in enumerate(
+        ["q", "k", "v", "gamma", "g", "S0", "mass0", "dout", "dv", "dgamma", "dg",
+         "dS0", "dmass0", "ws"])}
+    for n, v in kw.items():
+        ptrs[n] = None if v is None else C.c_void_p(v)
+    a = rn.Addr(*[FAKE + ((80 + i) << 32) for i in range(4)])
+    need = rn.workspace_bytes(p, rn.OP_BACKWARD)
+    st = lib.ramnet_scan_backward(C.byref(p), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["gamma"],
+                                  ptrs["g"], None, None, ptrs["S0"], ptrs["mass0"], C.byref(a),
+                                  ptrs["dout"], None, None, None, None, ptrs["dv"],
+                                  ptrs["dgamma"], ptrs["dg"], None, ptrs["dS0"], ptrs["dmass0"],
+                                  ptrs["ws"], kw.get("ws_bytes", need), None)
+    return st, lib.ramnet_last_error().decode()
+
+
+def test_backward_scope_and_arguments(rn):
+    p = good(rn, d_v=64, state_dtype=rn.F32)
+    assert rn.workspace_bytes(p, rn.OP_BACKWARD) > 0
+    st, err = call_backward(rn, good(rn, state_dtype=rn.BF16))
+    assert st == -2 and "fp32 state" in err
+    st, err = call_backward(rn, good(rn, d_v=128))
+    assert st == -2 and "d_v = 64" in err
+    assert rn.workspace_bytes(good(rn, d_v=128), rn.OP_BACKWARD) == 0
+    st, err = call_backward(rn, good(rn, d_p=4, U=6))   # M = 4096
+    assert st == -2
+    st, err = call_backward(rn, p, dout=None)
+    assert st == -1 and "dout is NULL" in err
+    st, err = call_backward(rn, p, ws_bytes=16)
+    assert st == -3 and "workspace" in err
+    st, err = call_backward(rn, p, dv=FAKE + ((50 + 7) << 32))   # dv on dout
+    assert st == -1 and "overlaps" in err
