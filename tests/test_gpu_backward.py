@@ -158,3 +158,51 @@ def test_backward_repeatable(rn):
     for n in runs[0]:
         if runs[0][n] is not None:
             assert torch.equal(runs[0][n], runs[1][n]), n
+
+
+def test_full_size_directional_derivatives(rn):
+    """At the Top-8 benchmark's full size (B 8, T 4096, H 8), the gradients of
+    v, gamma, g, S0 and m0 against central differences of the GPU forward's
+    loss along random directions.  Those inputs do not move the addresses,
+    so the loss is smooth along them.  Tolerance: the forward is fp32, so
+    the difference quotient carries about 1e-7 * |L| / eps of rounding; the
+    worst error seen is 4.5e-6 of sum |grad| |direction| (gamma)."""
+    w = synth.WORKLOADS["prefill_top8"].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5))
+    B, T, H = w.B, w.T, w.H
+    x = synth.make_inputs(w)
+    d = {n: dev(x[n], True) for n in ("q", "k", "v", "gamma", "g")}
+    base = {n: dev(x[n]) for n in ("v", "gamma", "g")}  # fp32 copies to perturb
+    S0, m0 = dev(x["S0"]), dev(x["m0"])
+    pos0 = torch.from_numpy(x["pos0"]).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    dout = torch.randn(B, T, H, w.d_v, generator=gen, device="cuda")
+    plan = rn.PrefillPlan(B, T, H, w.d_p, w.U, w.K, w.d_v, rn.F32, rn.F32, cape=w.cape)
+    out = torch.empty(B, T, H, w.d_v, device="cuda")
+    addr = rn.new_addresses((B, T, H, w.K), "cuda")
+    q32, k32 = dev(x["q"]), dev(x["k"])
+
+    def loss(v, gamma, g, S, m):
+        S, m = S.clone(), m.clone()
+        plan(q32, k32, v, gamma, g, S, m, out, pos0=pos0)
+        return float((out.double() * dout.double()).sum())
+
+    S, m = S0.clone(), m0.clone()
+    plan(q32, k32, base["v"], base["gamma"], base["g"], S, m, out, pos0=pos0, addr_out=addr)
+    gr = rn.scan_backward(q32, k32, base["v"], base["gamma"], base["g"], S0, m0, addr, dout,
+                          d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=pos0, want_logits=False)
+    args = {"v": base["v"], "gamma": base["gamma"], "g": base["g"], "S": S0, "m": m0}
+    grads = {"v": gr["dv"], "gamma": gr["dgamma"], "g": gr["dg"], "S": gr["dS0"], "m": gr["dmass0"]}
+    for n, eps in (("v", 1e-3), ("gamma", 1e-3), ("g", 1e-3), ("S", 1e-3), ("m", 1e-3)):
+        dirn = torch.randn(args[n].shape, generator=gen, device="cuda")
+        if n == "m":
+            dirn = dirn.abs()  # the mass stays positive
+        ap, am = dict(args), dict(args)
+        ap[n] = args[n] + eps * dirn
+        am[n] = args[n] - eps * dirn
+        fd = (loss(**ap) - loss(**am)) / (2 * eps)
+        an = float((grads[n].double() * dirn.double()).sum())
+        scale = float((grads[n].double().abs() * dirn.double().abs()).sum())
+        print(f"{n}: difference quotient {fd:.6g}, gradient {an:.6g}, |error| / scale "
+              f"{abs(fd - an) / scale:.2e}")
+        assert abs(fd - an) <= 1e-4 * scale, (n, fd, an, scale)
