@@ -3,8 +3,10 @@
 // formulas, so the adjoint below is the exact derivative of the forward
 // steps, Top-K selection held fixed).
 //
-// For a state held in fp32 with d_v = 64 channels and M <= 1024 slots, one
-// workgroup per (batch, head) unit, thread s owning slot s:
+// For a state held in fp32 with d_v = 64 channels and M <= 1024 slots.  A
+// slot's adjoint depends only on its own events, so the two serial kernels
+// give each (batch, head) unit up to four workgroups of 256 slots, thread s
+// owning one slot:
 //
 //   bwd_record_kernel   replays the forward from (S0, m0) and records, per
 //                       token, each write's row and mass before the write
@@ -35,7 +37,9 @@
 //                       Product Softmax: w = prod_u p_u(a_u) gives
 //                       dl_u,d = sum_k dw_k w_k ([d = a_u(k)] - p_u(d)), with
 //                       a(k) the selected slot's content digits (CAPE undone).
-//   bwd_omega_kernel    sums the units' d omega in unit order.
+//   bwd_sum_kernel      adds each token's lam dS+ and gamma terms over its
+//                       writes, in write order.
+//   bwd_omega_kernel    sums the d omega partials in a fixed order.
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,7 +49,6 @@ namespace {
 constexpr int kBwdDv = 64;
 constexpr int kBwdNT = 1024;  // largest M
 constexpr int kSlotsPerWG = 256;  // the serial kernels split a unit's slots over workgroups
-constexpr int kKMax = 64;
 
 struct Row4 {
     float e[4];
