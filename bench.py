@@ -9,9 +9,10 @@ before the timed region.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload prefill_top8|prefill_top32|large_state|decode
-                                   |layer_top8|layer_decode|backward_top8]
+                                   |layer_top8|layer_decode|backward_top8
+                                   |backward_top32]
 The layer_* workloads add the dense projections either side (the whole layer);
-backward_top8 times the gradients of the Top-8 prefill.
+backward_top8 / backward_top32 time the gradients of those prefills.
 """
 from __future__ import annotations
 
@@ -332,7 +333,7 @@ def layer_model(w, D, kind: str):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 # Backward workloads: a prefill configuration's gradients (fp32 state).
-BACKWARD = {"backward_top8": "prefill_top8"}
+BACKWARD = {"backward_top8": "prefill_top8", "backward_top32": "prefill_top32"}
 
 
 def backward_model(w):
@@ -348,7 +349,8 @@ def backward_model(w):
     units = w.B * w.H
     per_th = (2 * w.d_v * b_in + b_in + 2 * w.L * b_in + 16 * w.K + 4 * w.d_v
               + 4 * (2 * w.L + 2 * w.d_v + 1))
-    state = units * 2 * (w.M * w.d_v * 4 + 4 * w.M)
+    b_s = 2 if w.state_dtype == "bf16" else 4
+    state = units * (w.M * w.d_v * (b_s + 4) + 8 * w.M)  # S0 read, dS0 (fp32) written
     records = n * (2 * w.K * w.d_v * 4 + 4 * w.K) * 2  # written by the replay, read back
     return {"backward": n * per_th + state, "records": records}
 
@@ -360,7 +362,7 @@ def bench_backward(torch, rn, w, steps, warmup):
     x = synth.make_inputs(w.replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5)))
     bf = w.in_dtype == "bf16"
     d = {n: to_dev(torch, x[n], w.in_dtype) for n in ("q", "k", "v", "gamma", "g")}
-    S0 = to_dev(torch, x["S0"], "f32")
+    S0 = to_dev(torch, x["S0"], w.state_dtype)
     m0 = to_dev(torch, x["m0"], "f32")
     pos0 = torch.from_numpy(x["pos0"]).cuda()
     del x

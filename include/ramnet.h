@@ -185,16 +185,18 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
  * gradient through.  The gradients are those of
  *   sum(out * dout) + sum(S_final * dS_final) + sum(mass_final * dmass_final)
  * with respect to the inputs and the state the forward started from.
- * Built for an fp32 state with d_v = 64, M <= 1024 and U*d_p <= 64
- * (RAMNET_EUNSUPPORTED otherwise).
+ * Built for d_v = 64, M <= 1024 and U*d_p <= 64 (RAMNET_EUNSUPPORTED
+ * otherwise); the state may be fp32 or bf16 (the replay rounds it as the
+ * forward does), the gradients are fp32.
  *   q, k, v, gamma, g, norm_w, pos0   the forward's inputs (q, k only read
  *             when dq, dk are given)
- *   S0, mass0 [B,H,M,d_v], [B,H,M] fp32: the state before the forward
+ *   S0, mass0 [B,H,M,d_v] state_dtype, [B,H,M] fp32: the state before the
+ *             forward
  *   addr      the forward's addresses (its addr_out), [B,T,H,K] each
  *   dout      [B,T,H,d_v] fp32; dS_final, dmass_final fp32 or NULL (= 0)
  *   dq, dk    [B,T,H,U*d_p] fp32 or NULL; dv, dg [B,T,H,d_v] fp32;
- *   dgamma    [B,T,H] fp32; dnorm_w [d_v] fp32 or NULL; dS0, dmass0 like
- *             S0, mass0
+ *   dgamma    [B,T,H] fp32; dnorm_w [d_v] fp32 or NULL; dS0 [B,H,M,d_v]
+ *             fp32, dmass0 [B,H,M] fp32
  *   workspace ramnet_workspace_bytes(p, RAMNET_OP_BACKWARD) bytes: the
  *             forward is replayed from S0 and, per token-head, each write's
  *             row and mass before it and each read's row are recorded
@@ -204,7 +206,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q,
                                    const void *k, const void *v,
                                    const void *gamma, const void *g,
                                    const float *norm_w, const int32_t *pos0,
-                                   const float *S0, const float *mass0,
+                                   const void *S0, const float *mass0,
                                    const ramnet_addr *addr, const float *dout,
                                    const float *dS_final,
                                    const float *dmass_final, float *dq,

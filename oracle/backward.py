@@ -20,8 +20,11 @@ Readings fixed here (the pages do not define the backward pass):
   * the power-decay retention is differentiated exactly.  The paper digest
     mentions a proxy gradient for it but does not give one ("parity
     unpinned" for that proxy, which is not implemented);
-  * states are differentiated in fp64 without the fp32 storage rounding
-    the forward applies (a rounding step passes its gradient through).
+  * with round_storage, each stored state row is rounded to its storage
+    dtype (bf16 or fp32) and each mass to fp32 after every write, as the C
+    oracle's forward does, and a rounding step passes its gradient through
+    unchanged; without it the forward is plain fp64 (smooth, for finite
+    differences).
 
 The loss whose gradients are returned is
   sum(out * dout) + sum(S_final * dS_final) + sum(m_final * dm_final).
@@ -58,6 +61,18 @@ def slot_weights(logits, content, U: int, d_p: int):
     return w
 
 
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def stored(x, bf16: bool):
+    """x rounded to bf16 or fp32 in the forward, gradient passed through."""
+    v = x.detach().numpy()
+    r = _round_bf16(v) if bf16 else v.astype(np.float32).astype(np.float64)
+    return x + torch.as_tensor(r - v)
+
+
 def retention(w, e):
     """(1 - w)^e, 0 for w >= 1 (where the factor reaches 0)."""
     if float(w.detach()) >= 1.0:
@@ -68,7 +83,7 @@ def retention(w, e):
 def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
                 cape: int = 1, pos0=None, norm_w=None, eps_gsu: float = 1e-6,
                 eps_norm: float = 1e-6, content_heads: int = 0, dS_final=None,
-                dm_final=None):
+                dm_final=None, round_storage: bool = False, state_bf16: bool = False):
     """Inputs as for oracle.layer (q, k [B,T,H,U*d_p], v, g [B,T,H,d_v],
     gamma [B,T,H], S0 [B,H,M,d_v], m0 [B,H,M]) plus dout [B,T,H,d_v].
     Returns a dict of fp64 numpy arrays: out, S, mass (the forward), the
@@ -111,8 +126,12 @@ def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
                         continue
                     i = int(wi[j])
                     mass[i] = retention(w, e) * mass[i] + w
+                    if round_storage:
+                        mass[i] = stored(mass[i], False)
                     lam = w / (mass[i] + eps_gsu)
                     rows[i] = rows[i] + lam * (tv[b, t, h] - rows[i])
+                    if round_storage:
+                        rows[i] = stored(rows[i], state_bf16)
                 r = sum(rw[j] * rows[int(ri[j])] for j in range(K))
                 inv = torch.rsqrt(torch.mean(r * r) + eps_norm)
                 unit_out.append(r * inv * tom * torch.sigmoid(tg[b, t, h]))

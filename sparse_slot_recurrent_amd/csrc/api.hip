@@ -710,7 +710,7 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
 
 ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const void *k,
                                    const void *v, const void *gamma, const void *g,
-                                   const float *norm_w, const int32_t *pos0, const float *S0,
+                                   const float *norm_w, const int32_t *pos0, const void *S0,
                                    const float *mass0, const ramnet_addr *addr, const float *dout,
                                    const float *dS_final, const float *dmass_final, float *dq,
                                    float *dk, float *dv, float *dgamma, float *dg, float *dnorm_w,
@@ -718,9 +718,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
                                    size_t workspace_bytes, void *stream) {
     ramnet_status s = check_params(p, false);
     if (s) return s;
-    if (p->state_dtype != RAMNET_F32)
-        return fail(RAMNET_EUNSUPPORTED, "the backward pass needs an fp32 state");
-    if (!ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, false))
+    if (!ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, p->state_dtype == RAMNET_BF16))
         return fail(RAMNET_EUNSUPPORTED,
                     "the backward pass is built for d_v = 64, M <= 1024 and U*d_p <= 64");
     const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
@@ -758,7 +756,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     sp[ns++] = span("g", g, nv * in_bytes(p));
     if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
     if (pos0) sp[ns++] = span("pos0", pos0, p->B * sizeof(int32_t));
-    sp[ns++] = span("S0", S0, st * p->d_v * 4);
+    sp[ns++] = span("S0", S0, st * p->d_v * st_bytes(p));
     sp[ns++] = span("mass0", mass0, st * 4);
     sp[ns++] = span("addr.w_idx", addr->w_idx, nK4);
     sp[ns++] = span("addr.w_wt", addr->w_wt, nK4);
@@ -790,6 +788,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     a.cape = p->cape;
     a.content_heads = p->content_heads;
     a.in_bf16 = p->in_dtype == RAMNET_BF16;
+    a.state_bf16 = p->state_dtype == RAMNET_BF16;
     a.eps_gsu = p->eps_gsu;
     a.eps_norm = p->eps_norm;
     a.q = q;

@@ -3,7 +3,9 @@
 // formulas, so the adjoint below is the exact derivative of the forward
 // steps, Top-K selection held fixed).
 //
-// For a state held in fp32 with d_v = 64 channels and M <= 1024 slots.  A
+// For d_v = 64 channels and M <= 1024 slots, the state in fp32 or bf16 (the
+// replay rounds it as the forward does; each rounding passes its gradient
+// through; the adjoint runs in fp32).  A
 // slot's adjoint depends only on its own events, so the two serial kernels
 // give each (batch, head) unit up to four workgroups of 256 slots, thread s
 // owning one slot:
@@ -241,7 +243,7 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int 
     if (s < Cc) ct.gam[s] = p.gam;
 }
 
-template <typename TIn>
+template <typename TIn, typename TS>
 __global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
     __shared__ ChunkLds g;
     __shared__ ChunkTok ct;
@@ -255,13 +257,9 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
     float row[kBwdDv];
     float m = 0.f;
     if (own) {
-        const Row4 *src = reinterpret_cast<const Row4 *>(a.S0 + (static_cast<int64_t>(unit) * M + slot) * kBwdDv);
+        const TS *src = static_cast<const TS *>(a.S0) + (static_cast<int64_t>(unit) * M + slot) * kBwdDv;
 #pragma unroll
-        for (int j = 0; j < kBwdDv / 4; ++j) {
-            const Row4 x = src[j];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) row[4 * j + c] = x.e[c];
-        }
+        for (int c = 0; c < kBwdDv; ++c) row[c] = to_f32(src[c]);
         m = a.mass0[static_cast<int64_t>(unit) * M + slot];
     }
     ChunkPf pf;
@@ -292,7 +290,7 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
                     m = fmaf(alpha, m, w);
                     const float lam = w / (m + a.eps_gsu);
 #pragma unroll
-                    for (int c = 0; c < kBwdDv; ++c) row[c] = fmaf(lam, ct.v[t][c] - row[c], row[c]);
+                    for (int c = 0; c < kBwdDv; ++c) row[c] = stored<TS>(fmaf(lam, ct.v[t][c] - row[c], row[c]));
                 }
             }
         }
@@ -564,7 +562,10 @@ template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
     const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
-    hipLaunchKernelGGL(bwd_record_kernel<TIn>, grid, dim3(kSlotsPerWG), 0, st, a);
+    if (a.state_bf16)
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t>), grid, dim3(kSlotsPerWG), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, float>), grid, dim3(kSlotsPerWG), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
@@ -596,8 +597,8 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
 
 }  // namespace
 
-bool backward_supported(int64_t M, int d_v, int U, int d_p, bool state_bf16) {
-    return !state_bf16 && d_v == kBwdDv && M <= kBwdNT && U * d_p <= 64;
+bool backward_supported(int64_t M, int d_v, int U, int d_p, bool) {
+    return d_v == kBwdDv && M <= kBwdNT && U * d_p <= 64;
 }
 
 size_t backward_workspace_bytes(int B, int T, int H, int K) {

@@ -116,19 +116,20 @@ struct StepArgs {
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
 
-// Backward pass of the recurrence (backward.hip): fp32 state, d_v = 64,
-// M <= 1024, given the forward's addresses.
+// Backward pass of the recurrence (backward.hip): d_v = 64, M <= 1024,
+// given the forward's addresses; gradients in fp32.
 struct BwdArgs {
     int B, T, H;
     int64_t M;
     int K, U, d_p, cape;
     uint64_t content_heads;
-    bool in_bf16;
+    bool in_bf16, state_bf16;
     float eps_gsu, eps_norm;
     const void *q, *k, *v, *gamma, *g;
     const float *norm_w;
     const int32_t *pos0;
-    const float *S0, *mass0;
+    const void *S0;  // state dtype
+    const float *mass0;
     const int32_t *w_idx, *r_idx;
     const float *w_wt, *r_wt;
     const float *dout, *dS_final, *dmass_final;

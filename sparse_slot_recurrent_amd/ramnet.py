@@ -406,12 +406,12 @@ def scan_backward(q, k, v, gamma, g, S0, mass0, addr: Addresses, dout, *,
                   pos0=None, eps_gsu=1e-6, eps_norm=1e-6, content_heads: int = 0,
                   dS_final=None, dmass_final=None, want_logits: bool = True):
     """Gradients of a prefill (ramnet_scan_backward) given the forward's
-    inputs, the state it started from (S0, mass0: fp32) and the addresses it
-    used.  Returns a dict of fp32 tensors dq, dk (None unless want_logits),
-    dv, dgamma, dg, dnorm_w, dS0, dmass0."""
+    inputs, the state it started from (S0 in the state dtype, mass0 fp32)
+    and the addresses it used.  Returns a dict of fp32 tensors dq, dk (None
+    unless want_logits), dv, dgamma, dg, dnorm_w, dS0, dmass0."""
     torch = _torch()
     B, T, H, d_v = v.shape
-    p = make_params(B, T, H, d_p, U, K, d_v, _dt(v), F32, cape, eps_gsu,
+    p = make_params(B, T, H, d_p, U, K, d_v, _dt(v), _dt(S0), cape, eps_gsu,
                     eps_norm, content_heads=content_heads)
     nbytes = workspace_bytes(p, OP_BACKWARD)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=v.device)
@@ -420,7 +420,8 @@ def scan_backward(q, k, v, gamma, g, S0, mass0, addr: Addresses, dout, *,
     out = {"dq": f32(B, T, H, L) if want_logits else None,
            "dk": f32(B, T, H, L) if want_logits else None,
            "dv": f32(B, T, H, d_v), "dgamma": f32(B, T, H), "dg": f32(B, T, H, d_v),
-           "dnorm_w": f32(d_v), "dS0": torch.empty_like(S0), "dmass0": torch.empty_like(mass0)}
+           "dnorm_w": f32(d_v), "dS0": torch.empty(S0.shape, dtype=torch.float32, device=v.device),
+           "dmass0": torch.empty_like(mass0)}
     a = _addr_struct(addr)
     _raise(load_library().ramnet_scan_backward(
         C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g), _ptr(norm_w),

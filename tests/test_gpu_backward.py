@@ -26,6 +26,11 @@ from parity import compare_address_sets, to_np  # noqa: E402
 # replay and adjoint against fp64 over a few hundred dependent steps (the
 # worst case seen on these cuts is 1.3e-6, on the logit gradients)
 GRAD_TOL = 1e-5
+# bf16 state: both sides round every stored row to 8 significant bits, the
+# GPU from an fp32 value and the oracle from an fp64 one; where the two
+# roundings part (rarely), the trajectories differ by one bf16 ulp (2^-8);
+# the worst case seen on the Top-32 cut is 1.6e-4
+GRAD_TOL_BF16 = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -52,6 +57,7 @@ def dev(a, bf16=False):
 
 CASES = {
     "tiny": ("tiny", dict(B=1, T=256, H=1), {}),
+    "top32_bf16_state": ("prefill_top32", dict(B=1, T=64, H=2), {}),
     "top8": ("prefill_top8", dict(B=1, T=96, H=2), {}),
     "cape3_mask_norm": ("prefill_top8", dict(B=2, T=64, H=2), dict(cape=3, content_heads=0b10, norm=True)),
     "dp2": ("tiny", dict(B=1, T=80, H=2), dict(d_p=2, U=8, K=5)),
@@ -75,7 +81,8 @@ def weights_of(orc, w, logits, pos0, T, H, cape, content_heads, U, d_p):
     return f
 
 
-def close(name, got, ref, mask=None):
+def close(name, got, ref, mask=None, tol=None):
+    tol = GRAD_TOL if tol is None else tol
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     if mask is not None:
@@ -84,7 +91,7 @@ def close(name, got, ref, mask=None):
     err = np.abs(got - ref)
     worst = float((err / (np.abs(ref) + rms + 1e-30)).max()) if ref.size else 0.0
     assert np.isfinite(got).all(), name
-    assert (err <= GRAD_TOL * (np.abs(ref) + rms)).all(), (name, worst)
+    assert (err <= tol * (np.abs(ref) + rms)).all(), (name, worst)
     return worst
 
 
@@ -93,7 +100,7 @@ def test_backward_matches_oracle(rn, BWo, case):
     import oracle as orc
     name, cut, opt = CASES[case]
     w = synth.WORKLOADS[name].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5), pos0_max=3000,
-                                      cape=opt.get("cape", 1), state_dtype="f32")
+                                      cape=opt.get("cape", 1))
     if "d_p" in opt:
         w = w.replace(d_p=opt["d_p"], U=opt["U"], K=opt["K"])
     B, T, H = cut["B"], cut["T"], cut["H"]
@@ -104,12 +111,14 @@ def test_backward_matches_oracle(rn, BWo, case):
     dmf = r.standard_normal(x["m0"].shape).astype(np.float32)
     norm_w = (1.0 + 0.25 * np.sin(np.arange(w.d_v))).astype(np.float32) if opt.get("norm") else None
     mask = opt.get("content_heads", 0)
+    sbf = w.state_dtype == "bf16"
     ref = BWo.layer_grads(x["q"], x["k"], x["v"], x["gamma"], x["g"], x["S0"], x["m0"], dout,
                           d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=x["pos0"], norm_w=norm_w,
-                          content_heads=mask, dS_final=dSf, dm_final=dmf)
+                          content_heads=mask, dS_final=dSf, dm_final=dmf, round_storage=True,
+                          state_bf16=sbf)
     bf = w.in_dtype == "bf16"
     d = {n: dev(x[n], bf) for n in ("q", "k", "v", "gamma", "g")}
-    S0, m0 = dev(x["S0"]), dev(x["m0"])
+    S0, m0 = dev(x["S0"], sbf), dev(x["m0"])
     S, m = S0.clone(), m0.clone()
     pos0 = torch.from_numpy(x["pos0"]).cuda()
     nw = dev(norm_w) if norm_w is not None else None
@@ -131,13 +140,14 @@ def test_backward_matches_oracle(rn, BWo, case):
     clean = ~(dw | dr).any(1)            # [B, H]: units with the oracle's sets throughout
     assert clean.mean() >= 0.5
     tok = np.broadcast_to(clean[:, None, :], (B, T, H))
+    tol = GRAD_TOL_BF16 if sbf else GRAD_TOL
     worst = {}
     for n, m_ in (("dv", tok), ("dg", tok), ("dgamma", tok), ("dq", tok), ("dk", tok)):
-        worst[n] = close(n, to_np(got[n]), ref[n], m_)
-    worst["dS0"] = close("dS0", to_np(got["dS0"]), ref["dS0"], clean)
-    worst["dm0"] = close("dm0", to_np(got["dmass0"]), ref["dm0"], clean)
+        worst[n] = close(n, to_np(got[n]), ref[n], m_, tol)
+    worst["dS0"] = close("dS0", to_np(got["dS0"]), ref["dS0"], clean, tol)
+    worst["dm0"] = close("dm0", to_np(got["dmass0"]), ref["dm0"], clean, tol)
     if clean.all():
-        worst["dnorm_w"] = close("dnorm_w", to_np(got["dnorm_w"]), ref["dnorm_w"])
+        worst["dnorm_w"] = close("dnorm_w", to_np(got["dnorm_w"]), ref["dnorm_w"], None, tol)
     print(case, {k: f"{v:.2e}" for k, v in worst.items()}, "clean units", int(clean.sum()), "of", clean.size)
 
 

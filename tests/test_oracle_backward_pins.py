@@ -57,6 +57,29 @@ def test_forward_matches_c_oracle(orc):
     np.testing.assert_allclose(res["mass"], m, rtol=1e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_rounded_forward_equals_c_oracle_exactly(orc, bf16):
+    """With the storage rounding the torch forward takes the C oracle's
+    steps in the same order and precision, so the state, mass and outputs
+    agree to the bit (outputs stored in the state dtype)."""
+    B, T, H, U, d_p, K, d_v = 1, 30, 2, 3, 4, 4, 8
+    x = inputs(4, B, T, H, U, d_p, d_v)
+    if bf16:
+        x["S0"] = BW._round_bf16(x["S0"])
+    res = run(x, d_p=d_p, U=U, K=K, round_storage=True, state_bf16=bf16)
+    S = x["S0"].astype(np.float32).copy()
+    m = x["m0"].astype(np.float32).copy()
+    ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S, m, d_p=d_p, U=U, K=K,
+                    state_bf16=bf16, pos0=x["pos0"].astype(np.int32),
+                    norm_w=x["norm_w"].astype(np.float32))
+    assert np.array_equal(res["S"], S.astype(np.float64))
+    assert np.array_equal(res["mass"], m.astype(np.float64))
+    if bf16:  # rounded from fp64 values that may differ in their last bits
+        np.testing.assert_allclose(BW._round_bf16(res["out"]), ref["out"], rtol=2 ** -7, atol=0)
+    else:
+        np.testing.assert_allclose(res["out"].astype(np.float32), ref["out"], rtol=1e-7, atol=0)
+
+
 @pytest.mark.parametrize("cape,state", [(1, True), (0, False), (3, True)])
 def test_gradients_match_finite_differences(cape, state):
     """Every gradient against central differences of the loss along a random
