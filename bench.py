@@ -81,16 +81,22 @@ STAGE_KERNELS = {
 }
 
 
+# Sources of the kernels whose HBM counters profiles/hbm_traffic.json holds:
+# the decoder, the prefill stages and the fused step, with their shared
+# device helpers and argument structs.
+TRAFFIC_SOURCES = ("decode.hip", "scan_chunked.hip", "scan_serial.hip", "step_fused.hip",
+                   "device_common.h", "launch.h")
+
+
 def kernel_source_hash():
-    """sha256 over the kernel sources, to tell whether measured counters
-    still describe the kernels being run."""
-    import glob
+    """sha256 over the measured kernels' sources, to tell whether recorded
+    counters still describe the kernels being run."""
     import hashlib
     h = hashlib.sha256()
     here = os.path.dirname(os.path.abspath(__file__))
-    for path in sorted(glob.glob(os.path.join(here, "sparse_slot_recurrent_amd", "csrc", "*"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
+    for name in TRAFFIC_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(here, "sparse_slot_recurrent_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
