@@ -11,10 +11,14 @@
 // Design: the kept prefixes are held sorted (weight desc, prefix asc).  With
 // the next digit's probabilities sorted the same way, the candidates form
 // d_p sorted lists (one per digit value), and the new beam is the first K
-// entries of their merge.  Each lane merges its own lists; the beams live in
-// LDS, column-interleaved by lane ([buffer][rank][lane]), so the data-
-// dependent rank index never causes a bank conflict.  The decision is taken
-// in fp64 so that it agrees with an fp64 reference except at exact ties.
+// entries of their merge; the first digit's beam is its sorted values.  Each
+// lane merges its own lists: a step takes the best list head, then advances
+// that list alone, its beam position, probability and digit gathered by
+// selects, so that lanes choosing different lists never diverge.  The beams
+// live in LDS, column-interleaved by lane ([buffer][rank][lane]), so the
+// data-dependent rank index never causes a bank conflict.  The decision is
+// taken in fp64 so that it agrees with an fp64 reference except at exact
+// ties.
 #include "device_common.h"
 #include "launch.h"
 
@@ -55,8 +59,6 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     WT nxw[kRegs ? KC : 1];
     int32_t nxp[kRegs ? KC : 1];
     int cur = 0, nb = 1;
-    BW(0, 0) = WT(1);
-    BP(0, 0) = 0;
     for (int u = 0; u < U; ++u) {
         // Digit u's distribution: softmax over its d_p logits.
         WT pr[DP];
@@ -93,27 +95,47 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
                 dg[j - 1] = sw ? td : dg[j - 1];
             }
         }
-        // Merge the d_p candidate lists into the next beam.
         const int nn = min(K, nb * DP);  // the same in every lane
         const int rd = kRegs ? 0 : cur;
         const int nxt = cur ^ 1;
-        // List d's head candidate (cw, cp) and, loaded one step ahead, the
-        // beam entry after its head (nbw, nbp), so that advancing a list
-        // does not wait for LDS.
+        if (u == 0) {
+            // The first digit's beam is its sorted values themselves.
+#pragma unroll
+            for (int r = 0; r < (DP < KC ? DP : KC); ++r) {
+                if (r < nn) {
+                    if constexpr (kRegs) {
+                        nxw[r] = pr[r];
+                        nxp[r] = dg[r];
+                        if (U > 1) {
+                            BW(0, r) = pr[r];
+                            BP(0, r) = dg[r];
+                        }
+                    } else {
+                        BW(nxt, r) = pr[r];
+                        BP(nxt, r) = dg[r];
+                    }
+                }
+            }
+            if constexpr (!kRegs) cur = nxt;
+            nb = nn;
+            continue;
+        }
+        // Merge the d_p candidate lists into the next beam.
+        // List d (beam entries times the digit of rank d) has its head at
+        // beam entry h[d]; (cw, cp) is that head's candidate.  A step takes
+        // the best head, then gathers that list's entry, probability and
+        // digit by selects and loads only its next beam entry, so that no
+        // lane-divergent per-list branch is needed.
         int h[DP];
-        WT cw[DP], nbw[DP];
-        int cp[DP], nbp[DP];
+        WT cw[DP];
+        int cp[DP];
         const WT b0 = BW(rd, 0);
         const int p0 = BP(rd, 0);
-        const WT b1 = nb > 1 ? BW(rd, 1) : WT(0);
-        const int p1 = nb > 1 ? BP(rd, 1) : 0;
 #pragma unroll
         for (int d = 0; d < DP; ++d) {
             h[d] = 0;
             cw[d] = b0 * pr[d];
             cp[d] = p0 * DP + dg[d];
-            nbw[d] = b1;
-            nbp[d] = p1;
         }
         auto step = [&](WT &ow, int32_t &op) {
             int best = 0;
@@ -128,16 +150,28 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
             }
             ow = bwv;
             op = bpv;
+            int hb = h[0], db = dg[0];
+            WT pb = pr[0];
+#pragma unroll
+            for (int d = 1; d < DP; ++d) {
+                const bool sel = best == d;
+                hb = sel ? h[d] : hb;
+                db = sel ? dg[d] : db;
+                pb = sel ? pr[d] : pb;
+            }
+            ++hb;
+            WT ncw = WT(-1);  // -1: exhausted list
+            int ncp = 0;
+            if (hb < nb) {
+                ncw = BW(rd, hb) * pb;
+                ncp = BP(rd, hb) * DP + db;
+            }
 #pragma unroll
             for (int d = 0; d < DP; ++d) {
-                if (d == best) {
-                    const int hb = ++h[d];
-                    cw[d] = hb < nb ? nbw[d] * pr[d] : WT(-1);  // -1: exhausted list
-                    cp[d] = nbp[d] * DP + dg[d];
-                    const bool more = hb + 1 < nb;
-                    nbw[d] = more ? BW(rd, hb + 1) : WT(0);
-                    nbp[d] = more ? BP(rd, hb + 1) : 0;
-                }
+                const bool sel = best == d;
+                h[d] = sel ? hb : h[d];
+                cw[d] = sel ? ncw : cw[d];
+                cp[d] = sel ? ncp : cp[d];
             }
         };
         if constexpr (kRegs) {
