@@ -479,10 +479,15 @@ __device__ __forceinline__ int64_t cape_inverse_pos(int64_t pos, int form, int d
     return static_cast<int64_t>(inv);
 }
 
-// One level (digit block) at a time, so that the level's d_p probabilities
-// and gradients stay in registers.
+// One thread per (token-head, q or k).  Slot after slot: the content index
+// and the coefficient d_w * w are formed once, then the slot's digits are
+// peeled from the last level up (a compile-time base), each adding to its
+// level's d_p gradients.  The levels live in registers indexed from the
+// last one (level U - 1 - j is entry j), U * d_p <= 64; every (level,
+// digit) sum still runs over the slots in rank order.
 template <typename TIn, int DP>
 __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
+    constexpr int UMAX = 64 / DP;
     const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -498,34 +503,48 @@ __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
     const int h = static_cast<int>(i % a.H);
     const int form = head_uses_cape(a.content_heads, h) ? a.cape : 0;
     const int64_t pos = (a.pos0 ? a.pos0[b] : 0) + t;
-    const int64_t ipos = cape_inverse_pos(pos, form, DP, U, a.M);
-    int place = 1;  // DP^(U - 1 - u)
-    for (int u = 1; u < U; ++u) place *= DP;
-    for (int u = 0; u < U; ++u, place /= DP) {
-        float p[DP], dl[DP];
-        float mx = to_f32(lg[u * DP]);
+    const CapeShift sh = cape_shift<DP>(cape_inverse_pos(pos, form, DP, U, a.M), DP, a.M);
+    float p[UMAX][DP], dl[UMAX][DP];
 #pragma unroll
-        for (int d = 1; d < DP; ++d) mx = fmaxf(mx, to_f32(lg[u * DP + d]));
-        float sum = 0.f;
+    for (int j = 0; j < UMAX; ++j) {
+        if (j < U) {
+            const TIn *l = lg + (U - 1 - j) * DP;
+            float mx = to_f32(l[0]);
 #pragma unroll
-        for (int d = 0; d < DP; ++d) {
-            p[d] = expf(to_f32(lg[u * DP + d]) - mx);
-            sum += p[d];
-            dl[d] = 0.f;
+            for (int d = 1; d < DP; ++d) mx = fmaxf(mx, to_f32(l[d]));
+            float sum = 0.f;
+#pragma unroll
+            for (int d = 0; d < DP; ++d) {
+                p[j][d] = expf(to_f32(l[d]) - mx);
+                sum += p[j][d];
+                dl[j][d] = 0.f;
+            }
+#pragma unroll
+            for (int d = 0; d < DP; ++d) p[j][d] /= sum;
         }
+    }
+    for (int k = 0; k < K; ++k) {
+        const int slot = idx[k];
+        if (slot < 0 || slot >= a.M) continue;
+        const float coef = gr[k] * wt[k];
+        unsigned c = static_cast<unsigned>(form ? cape_slot_at<DP>(slot, sh, U, DP, form, a.M) : slot);
 #pragma unroll
-        for (int d = 0; d < DP; ++d) p[d] /= sum;
-        for (int k = 0; k < K; ++k) {
-            const int slot = idx[k];
-            if (slot < 0 || slot >= a.M) continue;
-            const float coef = gr[k] * wt[k];
-            const int content = form ? cape_slot<DP>(slot, ipos, U, DP, form, a.M) : slot;
-            const int digit = (content / place) % DP;
+        for (int j = 0; j < UMAX; ++j) {
+            if (j < U) {
+                const unsigned digit = c % DP;
+                c /= DP;
 #pragma unroll
-            for (int d = 0; d < DP; ++d) dl[d] = fmaf(-coef, p[d], dl[d] + (d == digit ? coef : 0.f));
+                for (int d = 0; d < DP; ++d)
+                    dl[j][d] = fmaf(-coef, p[j][d], dl[j][d] + (static_cast<unsigned>(d) == digit ? coef : 0.f));
+            }
         }
+    }
 #pragma unroll
-        for (int d = 0; d < DP; ++d) out[i * U * DP + u * DP + d] = dl[d];
+    for (int j = 0; j < UMAX; ++j) {
+        if (j < U) {
+#pragma unroll
+            for (int d = 0; d < DP; ++d) out[i * U * DP + (U - 1 - j) * DP + d] = dl[j][d];
+        }
     }
 }
 

@@ -198,6 +198,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int64_t t = (a / H) % T;
     const int64_t pos = (pos0 ? pos0[b] : 0) + t;
     const int form = head_uses_cape(content_heads, static_cast<int>(a % H)) ? cape : 0;
+    const CapeShift sh = cape_shift<DP>(pos, DP, M);
     // [B,T,H,K], or [B,H,T,K] so that a head's addresses are contiguous
     const int64_t o = unit_major ? ((b * H + a % H) * T + t) : a;
     int32_t *oi = (key ? w_idx : r_idx) + o * K;
@@ -211,10 +212,10 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
                 if (r < K) {
                     int4 vi;
                     float4 vw;
-                    vi.x = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
-                    vi.y = form ? cape_slot<DP>(nxp[r + 1], pos, U, DP, form, M) : nxp[r + 1];
-                    vi.z = form ? cape_slot<DP>(nxp[r + 2], pos, U, DP, form, M) : nxp[r + 2];
-                    vi.w = form ? cape_slot<DP>(nxp[r + 3], pos, U, DP, form, M) : nxp[r + 3];
+                    vi.x = form ? cape_slot_at<DP>(nxp[r], sh, U, DP, form, M) : nxp[r];
+                    vi.y = form ? cape_slot_at<DP>(nxp[r + 1], sh, U, DP, form, M) : nxp[r + 1];
+                    vi.z = form ? cape_slot_at<DP>(nxp[r + 2], sh, U, DP, form, M) : nxp[r + 2];
+                    vi.w = form ? cape_slot_at<DP>(nxp[r + 3], sh, U, DP, form, M) : nxp[r + 3];
                     vw.x = static_cast<float>(nxw[r]);
                     vw.y = static_cast<float>(nxw[r + 1]);
                     vw.z = static_cast<float>(nxw[r + 2]);
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
 #pragma unroll
             for (int r = 0; r < KC; ++r) {
                 if (r < K) {
-                    oi[r] = form ? cape_slot<DP>(nxp[r], pos, U, DP, form, M) : nxp[r];
+                    oi[r] = form ? cape_slot_at<DP>(nxp[r], sh, U, DP, form, M) : nxp[r];
                     ow[r] = static_cast<float>(nxw[r]);
                 }
             }
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     } else {
         for (int r = 0; r < K; ++r) {
             const int slot = BP(cur, r);
-            oi[r] = form ? cape_slot<DP>(slot, pos, U, DP, form, M) : slot;
+            oi[r] = form ? cape_slot_at<DP>(slot, sh, U, DP, form, M) : slot;
             ow[r] = static_cast<float>(BW(cur, r));
         }
     }

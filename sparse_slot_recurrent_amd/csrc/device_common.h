@@ -103,24 +103,42 @@ __device__ __forceinline__ float retention_fast(float w, float exp_gamma) {
 // at position pos, by reading `form`: 1 every digit advances by pos mod dp;
 // 2 digit u advances by digit u of pos (base dp, U digits, no carry); 3 the
 // slot index advances by pos, wrapping over the M = dp^U slots.  Digits wrap
-// within their dp values.  DP > 0 fixes the base at compile time.
+// within their dp values (M <= 2^30).  DP > 0 fixes the base at compile
+// time.  cape_shift holds the position-dependent part (pos mod M, pos mod
+// dp), so that callers moving many slots at one position reduce pos once.
+struct CapeShift {
+    unsigned pm, s1;
+};
 template <int DP>
-__device__ __forceinline__ int cape_slot(int slot, int64_t pos, int U, int dp_rt, int form, int64_t M) {
+__device__ __forceinline__ CapeShift cape_shift(int64_t pos, int dp_rt, int64_t M) {
     const int dp = DP > 0 ? DP : dp_rt;
-    const int64_t pm = ((pos % M) + M) % M;
-    if (form == 3) return static_cast<int>((slot + pm) % M);
-    const unsigned s1 = static_cast<unsigned>(((pos % dp) + dp) % dp);
-    if (form == 1 && s1 == 0) return slot;
-    unsigned x = static_cast<unsigned>(slot), p = static_cast<unsigned>(pm), moved = 0, place = 1;
+    return CapeShift{static_cast<unsigned>(((pos % M) + M) % M),
+                     static_cast<unsigned>(((pos % dp) + dp) % dp)};
+}
+// The slot content address `slot` (in [0, M)) moves to under shift sh.
+template <int DP>
+__device__ __forceinline__ int cape_slot_at(int slot, CapeShift sh, int U, int dp_rt, int form,
+                                            int64_t M) {
+    const int dp = DP > 0 ? DP : dp_rt;
+    if (form == 3) {
+        const unsigned x = static_cast<unsigned>(slot) + sh.pm;  // both below M <= 2^30
+        return static_cast<int>(x >= static_cast<unsigned>(M) ? x - static_cast<unsigned>(M) : x);
+    }
+    if (form == 1 && sh.s1 == 0) return slot;
+    unsigned x = static_cast<unsigned>(slot), p = sh.pm, moved = 0, place = 1;
     for (int u = 0; u < U; ++u) {
         const unsigned d = x % dp;
-        const unsigned sh = form == 2 ? p % dp : s1;
+        const unsigned s = form == 2 ? p % dp : sh.s1;
         x /= dp;
         p /= dp;
-        moved += ((d + sh) % dp) * place;
+        moved += ((d + s) % dp) * place;
         place *= dp;
     }
     return static_cast<int>(moved);
+}
+template <int DP>
+__device__ __forceinline__ int cape_slot(int slot, int64_t pos, int U, int dp_rt, int form, int64_t M) {
+    return cape_slot_at<DP>(slot, cape_shift<DP>(pos, dp_rt, M), U, dp_rt, form, M);
 }
 
 // Whether head h uses CAPE: its bit of content_heads (bit 63 for h >= 63)
