@@ -108,18 +108,36 @@ __device__ __forceinline__ float retention_fast(float w, float exp_gamma) {
 // dp), so that callers moving many slots at one position reduce pos once.
 struct CapeShift {
     unsigned pm, s1;
+    unsigned dm;  // DP == 0: ceil(2^32 / dp), so that x / dp = mulhi(x, dm) for x < 2^30
 };
 template <int DP>
 __device__ __forceinline__ CapeShift cape_shift(int64_t pos, int dp_rt, int64_t M) {
     const int dp = DP > 0 ? DP : dp_rt;
-    return CapeShift{static_cast<unsigned>(((pos % M) + M) % M),
-                     static_cast<unsigned>(((pos % dp) + dp) % dp)};
+    CapeShift sh;
+    if (pos >= 0 && pos <= 0xffffffffll) {  // the usual case, in 32-bit arithmetic
+        const unsigned p = static_cast<unsigned>(pos);
+        sh.pm = p % static_cast<unsigned>(M);
+        sh.s1 = p % static_cast<unsigned>(dp);
+    } else {
+        sh.pm = static_cast<unsigned>(((pos % M) + M) % M);
+        sh.s1 = static_cast<unsigned>(((pos % dp) + dp) % dp);
+    }
+    sh.dm = DP > 0 ? 0u : 0xffffffffu / static_cast<unsigned>(dp) + 1u;
+    return sh;
+}
+// x / dp for x < 2^30 and 2 <= dp <= 8: e = dm * dp - 2^32 is at most 4 for
+// these bases, so the error term x * e / 2^32 stays below 1 and the
+// multiply-high is exact (checked for every such x and dp).
+template <int DP>
+__device__ __forceinline__ unsigned cape_div(unsigned x, const CapeShift &sh) {
+    if constexpr (DP > 0) return x / DP;
+    else return __umulhi(x, sh.dm);
 }
 // The slot content address `slot` (in [0, M)) moves to under shift sh.
 template <int DP>
 __device__ __forceinline__ int cape_slot_at(int slot, CapeShift sh, int U, int dp_rt, int form,
                                             int64_t M) {
-    const int dp = DP > 0 ? DP : dp_rt;
+    const unsigned dp = DP > 0 ? DP : dp_rt;
     if (form == 3) {
         const unsigned x = static_cast<unsigned>(slot) + sh.pm;  // both below M <= 2^30
         return static_cast<int>(x >= static_cast<unsigned>(M) ? x - static_cast<unsigned>(M) : x);
@@ -127,11 +145,16 @@ __device__ __forceinline__ int cape_slot_at(int slot, CapeShift sh, int U, int d
     if (form == 1 && sh.s1 == 0) return slot;
     unsigned x = static_cast<unsigned>(slot), p = sh.pm, moved = 0, place = 1;
     for (int u = 0; u < U; ++u) {
-        const unsigned d = x % dp;
-        const unsigned s = form == 2 ? p % dp : sh.s1;
-        x /= dp;
-        p /= dp;
-        moved += ((d + s) % dp) * place;
+        const unsigned xq = cape_div<DP>(x, sh), d = x - xq * dp;
+        unsigned s = sh.s1;
+        if (form == 2) {
+            const unsigned pq = cape_div<DP>(p, sh);
+            s = p - pq * dp;
+            p = pq;
+        }
+        x = xq;
+        const unsigned ds = d + s;  // below 2 dp
+        moved += (ds >= dp ? ds - dp : ds) * place;
         place *= dp;
     }
     return static_cast<int>(moved);
