@@ -7,8 +7,9 @@
 // replay rounds it as the forward does; each rounding passes its gradient
 // through; the adjoint runs in fp32).  A
 // slot's adjoint depends only on its own events, so the two serial kernels
-// give each (batch, head) unit up to four workgroups of 256 slots, thread s
-// owning one slot:
+// give each (batch, head) unit up to eight workgroups of 128 slots, two
+// adjacent threads sharing a slot (32 channels each; the one full-row dot
+// product is combined across the pair):
 //
 //   bwd_record_kernel   replays the forward from (S0, m0) and records, per
 //                       token, each write's row and mass before the write
@@ -20,8 +21,8 @@
 //                       it needs): out = y omega sigmoid(g), y = r / rms(r):
 //                         dg, d omega, dr = (dy - y mean(dy y)) / rms(r);
 //                         r = sum_k rho_k S_jk:  drho_k = <dr, S_jk>.
-//   bwd_adjoint_kernel  walks the chunks backwards, thread s holding dS[s]
-//                       (64 registers) and dm[s] and walking its slot's
+//   bwd_adjoint_kernel  walks the chunks backwards, a thread pair holding
+//                       dS[s] (32 registers each) and dm[s] and walking its slot's
 //                       events of the chunk in reverse time order:
 //                         dS_jk += rho_k dr
 //                         each write, S+ = S- + lam (v - S-),
@@ -50,7 +51,12 @@ namespace {
 
 constexpr int kBwdDv = 64;
 constexpr int kBwdNT = 1024;  // largest M
-constexpr int kSlotsPerWG = 256;  // the serial kernels split a unit's slots over workgroups
+// The serial kernels split a unit's slots over workgroups of kSlotsPerWG
+// slots; two adjacent lanes share a slot, each holding kCh of its channels.
+constexpr int kSlotsPerWG = 128;
+constexpr int kHalves = 2;
+constexpr int kCh = kBwdDv / kHalves;
+constexpr int kBwdThreads = kSlotsPerWG * kHalves;
 
 struct Row4 {
     float e[4];
@@ -70,7 +76,7 @@ constexpr int kEvMax = 2048;  // events per chunk: 2 C K
 
 struct ChunkLds {
     int cnt[kSlotsPerWG];  // events per slot, then their offsets
-    int wtot[kSlotsPerWG / kWave];
+    int wtot[kBwdThreads / kWave];
     int list[kEvMax];
 };
 
@@ -102,21 +108,23 @@ __device__ int block_excl_scan_i(int x, int *wtot) {
     return base + incl - x;
 }
 
-// Groups the chunk's events on this workgroup's slots [slot0, slot0 + NT)
-// by slot: afterwards cnt[s] is slot slot0 + s's event count and its events
-// are list[base, base + cnt[s]), base returned to thread s (in arbitrary
-// order).  widx/ridx: the chunk's staged write and read slots, [Cc K] each.
+// Groups the chunk's events on this workgroup's slots [slot0, slot0 +
+// kSlotsPerWG) by slot: afterwards cnt[s] is slot slot0 + s's event count
+// and its events are list[base, base + n) in arbitrary order; both threads
+// of slot s get base (returned) and n.  widx/ridx: the chunk's staged write
+// and read slots, [Cc K] each.
 __device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int nev, int slot0,
-                            int nslots) {
-    const int s = threadIdx.x;
-    g.cnt[s] = 0;
+                            int nslots, int &n) {
+    const int s = threadIdx.x / kHalves;
+    const bool first = threadIdx.x % kHalves == 0;
+    if (first) g.cnt[s] = 0;
     lds_barrier();
-    constexpr int kPer = kEvMax / kSlotsPerWG;
+    constexpr int kPer = kEvMax / kBwdThreads;
     int slot[kPer], rank[kPer], code[kPer];
     const int K2 = 2 * nev;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int e = s + j * static_cast<int>(blockDim.x);
+        const int e = static_cast<int>(threadIdx.x) + j * kBwdThreads;
         slot[j] = -1;
         if (e < K2) {
             const bool rd = e >= nev;
@@ -131,15 +139,15 @@ __device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int n
         }
     }
     lds_barrier();
-    const int n = g.cnt[s];
-    const int base = block_excl_scan_i(n, g.wtot);
-    g.cnt[s] = base;
+    n = g.cnt[s];
+    const int pre = block_excl_scan_i(first ? n : 0, g.wtot);  // thread order: slot order
+    if (first) g.cnt[s] = pre;
     lds_barrier();
+    const int base = g.cnt[s];
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
         if (slot[j] >= 0) g.list[g.cnt[slot[j]] + rank[j]] = code[j];
     lds_barrier();
-    g.cnt[s] = n;
     return base;
 }
 
@@ -180,9 +188,9 @@ struct ChunkTok {
 };
 
 // The same data for the next chunk, loaded into registers while this chunk
-// is walked (thread s takes entries s, s + NT, ...).
-constexpr int kPfA = kEvMax / 2 / kSlotsPerWG;
-constexpr int kPfV = kChunkMax * kBwdDv / kSlotsPerWG;
+// is walked (thread i takes entries i, i + NT, ...).
+constexpr int kPfA = kEvMax / 2 / kBwdThreads;
+constexpr int kPfV = kChunkMax * kBwdDv / kBwdThreads;
 struct ChunkPf {
     int w[kPfA], r[kPfA];
     float wt[kPfA], rt[kPfA], v[kPfV], dr[kPfV], gam;
@@ -196,7 +204,7 @@ __device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf &p, int b, 
     const TIn *gam = static_cast<const TIn *>(a.gamma);
 #pragma unroll
     for (int j = 0; j < kPfA; ++j) {
-        const int i = s + j * kSlotsPerWG;
+        const int i = s + j * kBwdThreads;
         if (i < Cc * K) {
             const int t = i / K, k = i - t * K;
             const int64_t e = ((static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h) * K + k;
@@ -208,7 +216,7 @@ __device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf &p, int b, 
     }
 #pragma unroll
     for (int j = 0; j < kPfV; ++j) {
-        const int i = s + j * kSlotsPerWG;
+        const int i = s + j * kBwdThreads;
         if (i < Cc * kBwdDv) {
             const int t = i / kBwdDv, c = i - t * kBwdDv;
             const int64_t th = (static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h;
@@ -224,7 +232,7 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int 
     const int s = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kPfA; ++j) {
-        const int i = s + j * kSlotsPerWG;
+        const int i = s + j * kBwdThreads;
         if (i < Cc * K) {
             ct.widx[i] = p.w[j];
             ct.wt[i] = p.wt[j];
@@ -234,7 +242,7 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int 
     }
 #pragma unroll
     for (int j = 0; j < kPfV; ++j) {
-        const int i = s + j * kSlotsPerWG;
+        const int i = s + j * kBwdThreads;
         if (i < Cc * kBwdDv) {
             ct.v[i / kBwdDv][i % kBwdDv] = p.v[j];
             if (ADJ) ct.dr[i / kBwdDv][i % kBwdDv] = p.dr[j];
@@ -243,23 +251,28 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int 
     if (s < Cc) ct.gam[s] = p.gam;
 }
 
+// Both serial kernels: thread 2 s + hf of a workgroup serves slot slot0 + s,
+// channels [hf kCh, hf kCh + kCh); the first thread of the pair sorts the
+// slot's events, then both walk them.
 template <typename TIn, typename TS>
-__global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_record_kernel(BwdArgs a) {
     __shared__ ChunkLds g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
-    const int s = threadIdx.x, K = a.K, T = a.T;
+    const int s = threadIdx.x / kHalves, c0 = (threadIdx.x % kHalves) * kCh;
+    const bool first = c0 == 0;
+    const int K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
     const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
     const int nslots = min(kSlotsPerWG, M - slot0);
     const bool own = s < nslots;
     const int C = bwd_chunk(K);
-    float row[kBwdDv];
+    float row[kCh];
     float m = 0.f;
     if (own) {
-        const TS *src = static_cast<const TS *>(a.S0) + (static_cast<int64_t>(unit) * M + slot) * kBwdDv;
+        const TS *src = static_cast<const TS *>(a.S0) + (static_cast<int64_t>(unit) * M + slot) * kBwdDv + c0;
 #pragma unroll
-        for (int c = 0; c < kBwdDv; ++c) row[c] = to_f32(src[c]);
+        for (int c = 0; c < kCh; ++c) row[c] = to_f32(src[c]);
         m = a.mass0[static_cast<int64_t>(unit) * M + slot];
     }
     ChunkPf pf;
@@ -269,28 +282,32 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_record_kernel(BwdArgs a) {
         store_chunk<false>(ct, pf, Cc, K);
         lds_barrier();
         if (t0 + C < T) load_chunk<TIn, false>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
-        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots);
-        if (own) {
-            const int n = g.cnt[s];
-            int *ev = g.list + base;
+        int n;
+        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
+        int *ev = g.list + base;
+        if (own && first) {
             for (int i = 0; i < n; ++i) ev[i] = ev_key(ev[i], K);
             sort_keys(ev, n);
+        }
+        lds_barrier();
+        if (own) {
             for (int i = 0; i < n; ++i) {
                 const int key = ev[i], t = key >> 7, k = key & 63, e = t * K + k;
                 const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
-                Row4 *dst = reinterpret_cast<Row4 *>((key & 64 ? a.rec_r : a.rec_w) + rec * kBwdDv);
+                Row4 *dst = reinterpret_cast<Row4 *>((key & 64 ? a.rec_r : a.rec_w) + rec * kBwdDv + c0);
 #pragma unroll
-                for (int j = 0; j < kBwdDv / 4; ++j)
+                for (int j = 0; j < kCh / 4; ++j)
                     dst[j] = Row4{{row[4 * j], row[4 * j + 1], row[4 * j + 2], row[4 * j + 3]}};
                 if (key & 64) continue;  // a read: recorded
-                a.rec_m[rec] = m;
+                if (first) a.rec_m[rec] = m;
                 const float w = ct.wt[e];
                 if (w > 0.f) {
                     const float alpha = retention(w, expf(ct.gam[t]));
                     m = fmaf(alpha, m, w);
                     const float lam = w / (m + a.eps_gsu);
 #pragma unroll
-                    for (int c = 0; c < kBwdDv; ++c) row[c] = stored<TS>(fmaf(lam, ct.v[t][c] - row[c], row[c]));
+                    for (int c = 0; c < kCh; ++c)
+                        row[c] = stored<TS>(fmaf(lam, ct.v[t][c0 + c] - row[c], row[c]));
                 }
             }
         }
@@ -344,25 +361,27 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_adjoint_kernel(BwdArgs a) {
     __shared__ ChunkLds g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
-    const int s = threadIdx.x, K = a.K, T = a.T;
+    const int s = threadIdx.x / kHalves, c0 = (threadIdx.x % kHalves) * kCh;
+    const bool first = c0 == 0;
+    const int K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
     const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
     const int nslots = min(kSlotsPerWG, M - slot0);
     const bool own = s < nslots;
     const int C = bwd_chunk(K);
-    const int64_t srow = (static_cast<int64_t>(unit) * M + slot) * kBwdDv;
-    float dS[kBwdDv];
+    const int64_t srow = (static_cast<int64_t>(unit) * M + slot) * kBwdDv + c0;
+    float dS[kCh];
     float dm = 0.f;
 #pragma unroll
-    for (int c = 0; c < kBwdDv; ++c) dS[c] = 0.f;
+    for (int c = 0; c < kCh; ++c) dS[c] = 0.f;
     if (own && a.dS_final) {
         const Row4 *src = reinterpret_cast<const Row4 *>(a.dS_final + srow);
 #pragma unroll
-        for (int j = 0; j < kBwdDv / 4; ++j) {
+        for (int j = 0; j < kCh / 4; ++j) {
             const Row4 x = src[j];
 #pragma unroll
             for (int c = 0; c < 4; ++c) dS[4 * j + c] = x.e[c];
@@ -377,25 +396,28 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
         store_chunk<true>(ct, pf, Cc, K);
         lds_barrier();
         if (ci > 0) load_chunk<TIn, true>(a, pf, b, h, t0 - C, C);
-        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots);
-        if (own) {
-            const int n = g.cnt[s];
-            int *ev = g.list + base;
+        int n;
+        const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
+        int *ev = g.list + base;
+        if (own && first) {
             for (int i = 0; i < n; ++i) ev[i] = ev_key(ev[i], K);
             sort_keys(ev, n);
+        }
+        lds_barrier();
+        if (own) {
             // backwards: a token's read before its write
             for (int i = n - 1; i >= 0; --i) {
                 const int key = ev[i], t = key >> 7, k = key & 63, e = t * K + k;
                 if (key & 64) {
                     const float rho = ct.rt[e];
 #pragma unroll
-                    for (int c = 0; c < kBwdDv; ++c) dS[c] = fmaf(rho, ct.dr[t][c], dS[c]);
+                    for (int c = 0; c < kCh; ++c) dS[c] = fmaf(rho, ct.dr[t][c0 + c], dS[c]);
                     continue;
                 }
                 const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
                 const float w = ct.wt[e];
                 float dw = 0.f, dgk = 0.f;
-                float *dvk = a.dvk + rec * kBwdDv;
+                float *dvk = a.dvk + rec * kBwdDv + c0;
                 if (w > 0.f) {
                     const float mm = a.rec_m[rec];
                     const float eg = expf(ct.gam[t]);
@@ -403,16 +425,18 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
                     const float mp = fmaf(alpha, mm, w);
                     const float den = mp + a.eps_gsu;
                     const float lam = w / den;
-                    const Row4 *sm = reinterpret_cast<const Row4 *>(a.rec_w + rec * kBwdDv);
+                    const Row4 *sm = reinterpret_cast<const Row4 *>(a.rec_w + rec * kBwdDv + c0);
                     float dl = 0.f;
 #pragma unroll
-                    for (int j = 0; j < kBwdDv / 4; ++j) {
+                    for (int j = 0; j < kCh / 4; ++j) {
                         const Row4 x = sm[j];
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) dl = fmaf(dS[4 * j + c], ct.v[t][4 * j + c] - x.e[c], dl);
+                        for (int c = 0; c < 4; ++c) dl = fmaf(dS[4 * j + c], ct.v[t][c0 + 4 * j + c] - x.e[c], dl);
                     }
+                    // the pair's halves of <dS+, v - S-> (both lanes get the same sum)
+                    dl += __shfl_xor(dl, 1, kWave);
 #pragma unroll
-                    for (int j = 0; j < kBwdDv / 4; ++j) {
+                    for (int j = 0; j < kCh / 4; ++j) {
                         reinterpret_cast<Row4 *>(dvk)[j] =
                             Row4{{lam * dS[4 * j], lam * dS[4 * j + 1], lam * dS[4 * j + 2], lam * dS[4 * j + 3]}};
 #pragma unroll
@@ -428,10 +452,12 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
                     }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < kBwdDv / 4; ++j) reinterpret_cast<Row4 *>(dvk)[j] = Row4{{0.f, 0.f, 0.f, 0.f}};
+                    for (int j = 0; j < kCh / 4; ++j) reinterpret_cast<Row4 *>(dvk)[j] = Row4{{0.f, 0.f, 0.f, 0.f}};
                 }
-                a.dgk[rec] = dgk;
-                a.dw[((static_cast<int64_t>(b) * T + t0 + t) * a.H + h) * K + k] = dw;
+                if (first) {
+                    a.dgk[rec] = dgk;
+                    a.dw[((static_cast<int64_t>(b) * T + t0 + t) * a.H + h) * K + k] = dw;
+                }
             }
         }
         lds_barrier();
@@ -439,9 +465,9 @@ __global__ __launch_bounds__(kSlotsPerWG) void bwd_adjoint_kernel(BwdArgs a) {
     if (own) {
         Row4 *dst = reinterpret_cast<Row4 *>(a.dS0 + srow);
 #pragma unroll
-        for (int j = 0; j < kBwdDv / 4; ++j)
+        for (int j = 0; j < kCh / 4; ++j)
             dst[j] = Row4{{dS[4 * j], dS[4 * j + 1], dS[4 * j + 2], dS[4 * j + 3]}};
-        a.dmass0[static_cast<int64_t>(unit) * M + slot] = dm;
+        if (first) a.dmass0[static_cast<int64_t>(unit) * M + slot] = dm;
     }
 }
 
@@ -582,16 +608,16 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
     const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
     if (a.state_bf16)
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t>), grid, dim3(kSlotsPerWG), 0, st, a);
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t>), grid, dim3(kBwdThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, float>), grid, dim3(kSlotsPerWG), 0, st, a);
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, float>), grid, dim3(kBwdThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, grid, dim3(kSlotsPerWG), 0, st, a);
+    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, grid, dim3(kBwdThreads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
