@@ -346,9 +346,24 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
         const float dyy = wave_sum(dy * y) / static_cast<float>(kBwdDv);
         const float dr = inv * (dy - y * dyy);
         a.dr[th * kBwdDv + c] = dr;
-        for (int k = 0; k < K; ++k) {
-            const float dk = wave_sum(dr * rr[k * kBwdDv]);
-            if (c == 0) a.drho[th * K + k] = dk;
+        if (K >= 16) {
+            // lane k takes <dr, S_jk> over its recorded row, dr broadcast
+            // channel by channel (cheaper than K wave reductions)
+            const int kk = c < K ? c : 0;
+            const Row4 *rk = reinterpret_cast<const Row4 *>(rr - c + kk * kBwdDv);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < kBwdDv / 4; ++j) {
+                const Row4 x = rk[j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = fmaf(bcast(dr, 4 * j + q), x.e[q], acc);
+            }
+            if (c < K) a.drho[th * K + c] = acc;
+        } else {
+            for (int k = 0; k < K; ++k) {
+                const float dk = wave_sum(dr * rr[k * kBwdDv]);
+                if (c == 0) a.drho[th * K + k] = dk;
+            }
         }
     }
     sdom[wave][c] = dom;
