@@ -823,7 +823,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     a.dw = reinterpret_cast<float *>(w + 2 * rows + align256(nK4));
     a.drho = reinterpret_cast<float *>(w + 2 * rows + 2 * align256(nK4));
     a.dom_part = reinterpret_cast<float *>(w + 2 * rows + 3 * align256(nK4));
-    char *w2 = w + 2 * rows + 3 * align256(nK4) + align256(static_cast<size_t>(units) * 16 * p->d_v * 4);
+    char *w2 = w + 2 * rows + 3 * align256(nK4) + align256(static_cast<size_t>(units) * ramnet::kBwdOutBlocks * p->d_v * 4);
     a.dr = reinterpret_cast<float *>(w2);
     w2 += align256(nv * 4);
     a.dvk = reinterpret_cast<float *>(w2);

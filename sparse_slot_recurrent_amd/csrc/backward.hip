@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_record_kernel(BwdArgs a) {
 // recorded read rows): one wave per token-head, lane c = channel c.  Writes
 // dg, dr (the read's adjoint, for the serial kernel) and d rho; each wave
 // sums its tokens' d omega, and the workgroup's sum goes to a partial.
-constexpr int kOutWaves = 4, kOutBlocks = 16;
+constexpr int kOutWaves = 16, kOutBlocks = kBwdOutBlocks;
 
 template <typename TIn>
 __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {

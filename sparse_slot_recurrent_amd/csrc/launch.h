@@ -87,6 +87,9 @@ struct ChunkArgs : ScanArgs {
 };
 
 constexpr size_t kChunkLdsLimit = 160 * 1024;
+// Token groups of the backward's output/read kernel: each (unit, group)
+// leaves one partial of d omega in the workspace.
+constexpr int kBwdOutBlocks = 16;
 
 ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16,
                        bool state_bf16);
