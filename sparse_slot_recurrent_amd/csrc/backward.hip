@@ -7,9 +7,9 @@
 // replay rounds it as the forward does; each rounding passes its gradient
 // through; the adjoint runs in fp32).  A
 // slot's adjoint depends only on its own events, so the two serial kernels
-// give each (batch, head) unit up to eight workgroups of 128 slots, two
-// adjacent threads sharing a slot (32 channels each; the one full-row dot
-// product is combined across the pair):
+// give each (batch, head) unit up to eight workgroups of 128 slots, two or
+// four adjacent threads sharing a slot (32 or 16 channels each; the one
+// full-row dot product is combined across them):
 //
 //   bwd_record_kernel   replays the forward from (S0, m0) and records, per
 //                       token, each write's row and mass before the write
@@ -21,8 +21,8 @@
 //                       it needs): out = y omega sigmoid(g), y = r / rms(r):
 //                         dg, d omega, dr = (dy - y mean(dy y)) / rms(r);
 //                         r = sum_k rho_k S_jk:  drho_k = <dr, S_jk>.
-//   bwd_adjoint_kernel  walks the chunks backwards, a thread pair holding
-//                       dS[s] (32 registers each) and dm[s] and walking its slot's
+//   bwd_adjoint_kernel  walks the chunks backwards, a slot's threads holding
+//                       dS[s] (their channels) and dm[s] and walking its slot's
 //                       events of the chunk in reverse time order:
 //                         dS_jk += rho_k dr
 //                         each write, S+ = S- + lam (v - S-),
@@ -52,11 +52,10 @@ namespace {
 constexpr int kBwdDv = 64;
 constexpr int kBwdNT = 1024;  // largest M
 // The serial kernels split a unit's slots over workgroups of kSlotsPerWG
-// slots; two adjacent lanes share a slot, each holding kCh of its channels.
+// slots; HV adjacent lanes share a slot (HV = 2 or 4), each holding
+// kBwdDv / HV of its channels.
 constexpr int kSlotsPerWG = 128;
-constexpr int kHalves = 2;
-constexpr int kCh = kBwdDv / kHalves;
-constexpr int kBwdThreads = kSlotsPerWG * kHalves;
+template <int HV> constexpr int kThreadsOf = kSlotsPerWG * HV;
 
 struct Row4 {
     float e[4];
@@ -74,9 +73,10 @@ struct Row4 {
 
 constexpr int kEvMax = 2048;  // events per chunk: 2 C K
 
+template <int HV>
 struct ChunkLds {
     int cnt[kSlotsPerWG];  // events per slot, then their offsets
-    int wtot[kBwdThreads / kWave];
+    int wtot[kThreadsOf<HV> / kWave];
     int list[kEvMax];
 };
 
@@ -113,10 +113,12 @@ __device__ int block_excl_scan_i(int x, int *wtot) {
 // and its events are list[base, base + n) in arbitrary order; both threads
 // of slot s get base (returned) and n.  widx/ridx: the chunk's staged write
 // and read slots, [Cc K] each.
-__device__ int group_events(ChunkLds &g, const int *widx, const int *ridx, int nev, int slot0,
+template <int HV>
+__device__ int group_events(ChunkLds<HV> &g, const int *widx, const int *ridx, int nev, int slot0,
                             int nslots, int &n) {
-    const int s = threadIdx.x / kHalves;
-    const bool first = threadIdx.x % kHalves == 0;
+    constexpr int kBwdThreads = kThreadsOf<HV>;
+    const int s = threadIdx.x / HV;
+    const bool first = threadIdx.x % HV == 0;
     if (first) g.cnt[s] = 0;
     lds_barrier();
     constexpr int kPer = kEvMax / kBwdThreads;
@@ -189,16 +191,18 @@ struct ChunkTok {
 
 // The same data for the next chunk, loaded into registers while this chunk
 // is walked (thread i takes entries i, i + NT, ...).
-constexpr int kPfA = kEvMax / 2 / kBwdThreads;
-constexpr int kPfV = kChunkMax * kBwdDv / kBwdThreads;
+template <int HV>
 struct ChunkPf {
+    static constexpr int kPfA = kEvMax / 2 / kThreadsOf<HV>;
+    static constexpr int kPfV = kChunkMax * kBwdDv / kThreadsOf<HV>;
     int w[kPfA], r[kPfA];
     float wt[kPfA], rt[kPfA], v[kPfV], dr[kPfV], gam;
 };
 
-template <typename TIn, bool ADJ>
-__device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf &p, int b, int h, int t0,
+template <typename TIn, bool ADJ, int HV>
+__device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf<HV> &p, int b, int h, int t0,
                                            int Cc) {
+    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV>::kPfA, kPfV = ChunkPf<HV>::kPfV;
     const int K = a.K, s = threadIdx.x;
     const TIn *v = static_cast<const TIn *>(a.v);
     const TIn *gam = static_cast<const TIn *>(a.gamma);
@@ -227,8 +231,9 @@ __device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf &p, int b, 
     if (s < Cc) p.gam = to_f32(gam[(static_cast<int64_t>(b) * a.T + t0 + s) * a.H + h]);
 }
 
-template <bool ADJ>
-__device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int Cc, int K) {
+template <bool ADJ, int HV>
+__device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf<HV> &p, int Cc, int K) {
+    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV>::kPfA, kPfV = ChunkPf<HV>::kPfV;
     const int s = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kPfA; ++j) {
@@ -251,15 +256,16 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf &p, int 
     if (s < Cc) ct.gam[s] = p.gam;
 }
 
-// Both serial kernels: thread 2 s + hf of a workgroup serves slot slot0 + s,
-// channels [hf kCh, hf kCh + kCh); the first thread of the pair sorts the
-// slot's events, then both walk them.
-template <typename TIn, typename TS>
-__global__ __launch_bounds__(kBwdThreads) void bwd_record_kernel(BwdArgs a) {
-    __shared__ ChunkLds g;
+// Both serial kernels: thread HV s + hf of a workgroup serves slot slot0 + s,
+// channels [hf kCh, hf kCh + kCh); the slot's first thread sorts its
+// events, then all HV walk them.
+template <typename TIn, typename TS, int HV>
+__global__ __launch_bounds__(kThreadsOf<HV>) void bwd_record_kernel(BwdArgs a) {
+    constexpr int kCh = kBwdDv / HV;
+    __shared__ ChunkLds<HV> g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
-    const int s = threadIdx.x / kHalves, c0 = (threadIdx.x % kHalves) * kCh;
+    const int s = threadIdx.x / HV, c0 = (threadIdx.x % HV) * kCh;
     const bool first = c0 == 0;
     const int K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
@@ -275,13 +281,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_record_kernel(BwdArgs a) {
         for (int c = 0; c < kCh; ++c) row[c] = to_f32(src[c]);
         m = a.mass0[static_cast<int64_t>(unit) * M + slot];
     }
-    ChunkPf pf;
-    load_chunk<TIn, false>(a, pf, b, h, 0, min(C, T));
+    ChunkPf<HV> pf;
+    load_chunk<TIn, false, HV>(a, pf, b, h, 0, min(C, T));
     for (int t0 = 0; t0 < T; t0 += C) {
         const int Cc = min(C, T - t0), nev = Cc * K;
-        store_chunk<false>(ct, pf, Cc, K);
+        store_chunk<false, HV>(ct, pf, Cc, K);
         lds_barrier();
-        if (t0 + C < T) load_chunk<TIn, false>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
+        if (t0 + C < T) load_chunk<TIn, false, HV>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
         int n;
         const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
         int *ev = g.list + base;
@@ -375,12 +381,13 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
     }
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(kBwdThreads) void bwd_adjoint_kernel(BwdArgs a) {
-    __shared__ ChunkLds g;
+template <typename TIn, int HV>
+__global__ __launch_bounds__(kThreadsOf<HV>) void bwd_adjoint_kernel(BwdArgs a) {
+    constexpr int kCh = kBwdDv / HV;
+    __shared__ ChunkLds<HV> g;
     __shared__ ChunkTok ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
-    const int s = threadIdx.x / kHalves, c0 = (threadIdx.x % kHalves) * kCh;
+    const int s = threadIdx.x / HV, c0 = (threadIdx.x % HV) * kCh;
     const bool first = c0 == 0;
     const int K = a.K, T = a.T;
     const int M = static_cast<int>(a.M);
@@ -404,13 +411,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_adjoint_kernel(BwdArgs a) {
     }
     if (own && a.dmass_final) dm = a.dmass_final[static_cast<int64_t>(unit) * M + slot];
     const int nch = (T + C - 1) / C;
-    ChunkPf pf;
-    load_chunk<TIn, true>(a, pf, b, h, (nch - 1) * C, T - (nch - 1) * C);
+    ChunkPf<HV> pf;
+    load_chunk<TIn, true, HV>(a, pf, b, h, (nch - 1) * C, T - (nch - 1) * C);
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int t0 = ci * C, Cc = min(C, T - t0), nev = Cc * K;
-        store_chunk<true>(ct, pf, Cc, K);
+        store_chunk<true, HV>(ct, pf, Cc, K);
         lds_barrier();
-        if (ci > 0) load_chunk<TIn, true>(a, pf, b, h, t0 - C, C);
+        if (ci > 0) load_chunk<TIn, true, HV>(a, pf, b, h, t0 - C, C);
         int n;
         const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
         int *ev = g.list + base;
@@ -448,8 +455,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_adjoint_kernel(BwdArgs a) {
 #pragma unroll
                         for (int c = 0; c < 4; ++c) dl = fmaf(dS[4 * j + c], ct.v[t][c0 + 4 * j + c] - x.e[c], dl);
                     }
-                    // the pair's halves of <dS+, v - S-> (both lanes get the same sum)
-                    dl += __shfl_xor(dl, 1, kWave);
+                    // the lanes' parts of <dS+, v - S-> (a butterfly: every lane of
+                    // the slot gets the same sum)
+#pragma unroll
+                    for (int o = 1; o < HV; o <<= 1) dl += __shfl_xor(dl, o, kWave);
 #pragma unroll
                     for (int j = 0; j < kCh / 4; ++j) {
                         reinterpret_cast<Row4 *>(dvk)[j] =
@@ -622,17 +631,27 @@ template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
     const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
+    // The replay takes four lanes per slot.  The adjoint, at 165 registers
+    // with four, then fits one workgroup per CU: it takes four lanes when
+    // the grid has at most one workgroup per CU, else two.
     if (a.state_bf16)
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t>), grid, dim3(kBwdThreads), 0, st, a);
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
     else
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, float>), grid, dim3(kBwdThreads), 0, st, a);
+        hipLaunchKernelGGL((bwd_record_kernel<TIn, float, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_adjoint_kernel<TIn>, grid, dim3(kBwdThreads), 0, st, a);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 0;
+    if (static_cast<int64_t>(grid.x) * grid.y <= ncu)
+        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 2>), grid, dim3(kThreadsOf<2>), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
