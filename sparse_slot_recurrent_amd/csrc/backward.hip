@@ -529,26 +529,47 @@ __device__ __forceinline__ int64_t cape_inverse_pos(int64_t pos, int form, int d
     return static_cast<int64_t>(inv);
 }
 
-// One thread per (token-head, q or k).  Slot after slot: the content index
-// and the coefficient d_w * w are formed once, then the slot's digits are
-// peeled from the last level up (a compile-time base), each adding to its
-// level's d_p gradients.  The levels live in registers indexed from the
-// last one (level U - 1 - j is entry j), U * d_p <= 64; every (level,
-// digit) sum still runs over the slots in rank order.
+// One thread per (token-head, q or k), a wave per 64 token-heads.  The
+// wave's slots and coefficients d_w * w are first staged in LDS with
+// coalesced loads (rows of K + 1 entries, so that the lanes' reads of their
+// own rows do not collide in banks).  Then slot after slot: the content
+// index is formed once, and the slot's digits are peeled from the last
+// level up (a compile-time base), each adding to its level's d_p
+// gradients.  The levels live in registers indexed from the last one (level
+// U - 1 - j is entry j), U * d_p <= 64; every (level, digit) sum still runs
+// over the slots in rank order.
 template <typename TIn, int DP>
-__global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kWave) void bwd_logits_kernel(BwdArgs a) {
     constexpr int UMAX = 64 / DP;
+    extern __shared__ unsigned char smem[];
     const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n) return;
     const bool key = blockIdx.y == 0;
     float *out = key ? a.dk : a.dq;
     if (!out) return;
-    const int U = a.U, K = a.K;
+    const int U = a.U, K = a.K, KS = K + 1;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kWave;
+    const int nb = static_cast<int>(min<int64_t>(kWave, n - i0));
+    int *sidx = reinterpret_cast<int *>(smem);
+    float *scoef = reinterpret_cast<float *>(smem + static_cast<size_t>(kWave) * KS * 4);
+    {
+        const int32_t *gidx = (key ? a.w_idx : a.r_idx) + i0 * K;
+        const float *gwt = (key ? a.w_wt : a.r_wt) + i0 * K;
+        const float *ggr = (key ? a.dw : a.drho) + i0 * K;
+        // e / K as mulhi(e, ceil(2^32 / K)): exact for e < 4096 (K = 1 apart)
+        const unsigned mk = K > 1 ? 0xffffffffu / static_cast<unsigned>(K) + 1u : 0u;
+        for (int e = threadIdx.x; e < nb * K; e += kWave) {
+            const int r = K > 1 ? static_cast<int>(__umulhi(static_cast<unsigned>(e), mk)) : e;
+            const int c = e - r * K;
+            sidx[r * KS + c] = gidx[e];
+            scoef[r * KS + c] = ggr[e] * gwt[e];
+        }
+    }
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) >= nb) return;
+    const int64_t i = i0 + threadIdx.x;
     const TIn *lg = static_cast<const TIn *>(key ? a.k : a.q) + i * U * DP;
-    const int32_t *idx = (key ? a.w_idx : a.r_idx) + i * K;
-    const float *wt = (key ? a.w_wt : a.r_wt) + i * K;
-    const float *gr = (key ? a.dw : a.drho) + i * K;
+    const int *idx = sidx + threadIdx.x * KS;
+    const float *coefs = scoef + threadIdx.x * KS;
     const int64_t b = i / (static_cast<int64_t>(a.T) * a.H), t = (i / a.H) % a.T;
     const int h = static_cast<int>(i % a.H);
     const int form = head_uses_cape(a.content_heads, h) ? a.cape : 0;
@@ -576,7 +597,7 @@ __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
     for (int k = 0; k < K; ++k) {
         const int slot = idx[k];
         if (slot < 0 || slot >= a.M) continue;
-        const float coef = gr[k] * wt[k];
+        const float coef = coefs[k];
         unsigned c = static_cast<unsigned>(form ? cape_slot_at<DP>(slot, sh, U, DP, form, a.M) : slot);
 #pragma unroll
         for (int j = 0; j < UMAX; ++j) {
@@ -600,9 +621,10 @@ __global__ __launch_bounds__(256) void bwd_logits_kernel(BwdArgs a) {
 
 template <typename TIn>
 hipError_t launch_logits(const BwdArgs &a, dim3 grid, hipStream_t st) {
+    const size_t lds = static_cast<size_t>(kWave) * (a.K + 1) * 8;  // slots and coefficients
     switch (a.d_p) {
 #define RAMNET_LOGITS_DP(D) \
-    case D: hipLaunchKernelGGL((bwd_logits_kernel<TIn, D>), grid, dim3(256), 0, st, a); break;
+    case D: hipLaunchKernelGGL((bwd_logits_kernel<TIn, D>), grid, dim3(kWave), lds, st, a); break;
         RAMNET_LOGITS_DP(2) RAMNET_LOGITS_DP(3) RAMNET_LOGITS_DP(4) RAMNET_LOGITS_DP(5)
         RAMNET_LOGITS_DP(6) RAMNET_LOGITS_DP(7) RAMNET_LOGITS_DP(8)
 #undef RAMNET_LOGITS_DP
@@ -663,7 +685,7 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     }
     if (a.dq || a.dk) {
         const int64_t n = static_cast<int64_t>(units) * a.T;
-        e = launch_logits<TIn>(a, dim3(static_cast<unsigned>((n + 255) / 256), 2), st);
+        e = launch_logits<TIn>(a, dim3(static_cast<unsigned>((n + kWave - 1) / kWave), 2), st);
         if (e != hipSuccess) return e;
     }
     if (a.dnorm_w) {
