@@ -505,14 +505,25 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
     const int64_t b = th / (static_cast<int64_t>(a.T) * a.H), t = (th / a.H) % a.T;
     const int h = static_cast<int>(th % a.H);
     const int64_t rec = ((b * a.H + h) * a.T + t) * K;
-    float acc = 0.f, gacc = 0.f;
-    for (int k = 0; k < K; ++k) {
-        const int slot = a.w_idx[th * K + k];
-        if (!(a.w_wt[th * K + k] > 0.f) || slot < 0 || slot >= a.M) continue;
-        acc += a.dvk[(rec + k) * kBwdDv + c];
-        gacc += a.dgk[rec + k];
+    // lane k tells whether write k counts; the mask is the same in every
+    // lane, so the row loads below go out together (K <= 64)
+    const int kk = c < K ? c : 0;
+    const int slot = a.w_idx[th * K + kk];
+    const bool mine = c < K && a.w_wt[th * K + kk] > 0.f && slot >= 0 && slot < a.M;
+    const uint64_t ok = __ballot(mine);
+    const float gk = mine ? a.dgk[rec + kk] : 0.f;
+    const float *dv = a.dvk + rec * kBwdDv + c;
+    float acc = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? dv[static_cast<int64_t>(k0 + j) * kBwdDv] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if ((ok >> (k0 + j)) & 1u) acc += x[j];
     }
     a.dv[th * kBwdDv + c] = acc;
+    const float gacc = wave_sum(gk);
     if (c == 0) a.dgamma[th] = gacc;
 }
 
