@@ -339,8 +339,17 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
     for (int t = blockIdx.y * kOutWaves + wave; t < T; t += kOutBlocks * kOutWaves) {
         const int64_t th = (static_cast<int64_t>(b) * T + t) * a.H + h;
         const float *rr = a.rec_r + (static_cast<int64_t>(unit) * T + t) * K * kBwdDv + c;
+        // lane k holds rho_k; rows load eight at a time (K <= 64)
+        const float rw = a.r_wt[th * K + (c < K ? c : 0)];
         float r = 0.f;
-        for (int k = 0; k < K; ++k) r = fmaf(a.r_wt[th * K + k], rr[k * kBwdDv], r);
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? rr[(k0 + j) * kBwdDv] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (k0 + j < K) r = fmaf(bcast(rw, k0 + j), x[j], r);
+        }
         const float den = wave_sum(r * r) / static_cast<float>(kBwdDv) + a.eps_norm;
         const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
         const float y = r * inv;
@@ -366,9 +375,17 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
             }
             if (c < K) a.drho[th * K + c] = acc;
         } else {
-            for (int k = 0; k < K; ++k) {
-                const float dk = wave_sum(dr * rr[k * kBwdDv]);
-                if (c == 0) a.drho[th * K + k] = dk;
+            for (int k0 = 0; k0 < K; k0 += 8) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? rr[(k0 + j) * kBwdDv] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (k0 + j < K) {
+                        const float dk = wave_sum(dr * x[j]);
+                        if (c == 0) a.drho[th * K + k0 + j] = dk;
+                    }
+                }
             }
         }
     }
