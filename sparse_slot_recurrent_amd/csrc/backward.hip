@@ -71,13 +71,15 @@ struct Row4 {
 // the adjoint).  An event code is t << 7 | read << 6 | k: ascending order is
 // the forward order (a token's write before its read).
 
-constexpr int kEvMax = 2048;  // events per chunk: 2 C K
+// EVM: a chunk's event capacity (2 C K), 2048 or 4096.  The larger halves
+// the chunks (and their barriers) at large K, but its LDS (83 KB) allows
+// one workgroup per CU; it is used when the grid has no more than that.
 
-template <int HV>
+template <int HV, int EVM>
 struct ChunkLds {
     int cnt[kSlotsPerWG];  // events per slot, then their offsets
     int wtot[kThreadsOf<HV> / kWave];
-    int list[kEvMax];
+    int list[EVM];
 };
 
 __device__ __forceinline__ int wave_incl_scan_i(int x) {
@@ -113,15 +115,15 @@ __device__ int block_excl_scan_i(int x, int *wtot) {
 // and its events are list[base, base + n) in arbitrary order; both threads
 // of slot s get base (returned) and n.  widx/ridx: the chunk's staged write
 // and read slots, [Cc K] each.
-template <int HV>
-__device__ int group_events(ChunkLds<HV> &g, const int *widx, const int *ridx, int nev, int slot0,
+template <int HV, int EVM>
+__device__ int group_events(ChunkLds<HV, EVM> &g, const int *widx, const int *ridx, int nev, int slot0,
                             int nslots, int &n) {
     constexpr int kBwdThreads = kThreadsOf<HV>;
     const int s = threadIdx.x / HV;
     const bool first = threadIdx.x % HV == 0;
     if (first) g.cnt[s] = 0;
     lds_barrier();
-    constexpr int kPer = kEvMax / kBwdThreads;
+    constexpr int kPer = EVM / kBwdThreads;
     int slot[kPer], rank[kPer], code[kPer];
     const int K2 = 2 * nev;
 #pragma unroll
@@ -172,18 +174,19 @@ __device__ __forceinline__ void sort_keys(int *p, int n) {
     }
 }
 
-// Tokens per chunk: at most 64, and C K write events at most kEvMax / 2.
+// Tokens per chunk: at most 64, and C K write events at most EVM / 2.
 constexpr int kChunkMax = 64;
-__host__ __device__ inline int bwd_chunk(int K) {
+__host__ __device__ inline int bwd_chunk(int K, int EVM) {
     int c = kChunkMax;
-    while (c > 1 && c * K > kEvMax / 2) c /= 2;
+    while (c > 1 && c * K > EVM / 2) c /= 2;
     return c;
 }
 
 // A chunk's staged token data.
+template <int EVM>
 struct ChunkTok {
-    int widx[kEvMax / 2], ridx[kEvMax / 2];
-    float wt[kEvMax / 2], rt[kEvMax / 2];
+    int widx[EVM / 2], ridx[EVM / 2];
+    float wt[EVM / 2], rt[EVM / 2];
     float v[kChunkMax][kBwdDv];
     float dr[kChunkMax][kBwdDv];
     float gam[kChunkMax];
@@ -191,18 +194,19 @@ struct ChunkTok {
 
 // The same data for the next chunk, loaded into registers while this chunk
 // is walked (thread i takes entries i, i + NT, ...).
-template <int HV>
+template <int HV, int EVM>
 struct ChunkPf {
-    static constexpr int kPfA = kEvMax / 2 / kThreadsOf<HV>;
+    static constexpr int kPfA = EVM / 2 / kThreadsOf<HV>;
     static constexpr int kPfV = kChunkMax * kBwdDv / kThreadsOf<HV>;
     int w[kPfA], r[kPfA];
     float wt[kPfA], rt[kPfA], v[kPfV], dr[kPfV], gam;
 };
 
-template <typename TIn, bool ADJ, int HV>
-__device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf<HV> &p, int b, int h, int t0,
+template <typename TIn, bool ADJ, int HV, int EVM>
+__device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf<HV, EVM> &p, int b, int h, int t0,
                                            int Cc) {
-    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV>::kPfA, kPfV = ChunkPf<HV>::kPfV;
+    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV, EVM>::kPfA,
+                  kPfV = ChunkPf<HV, EVM>::kPfV;
     const int K = a.K, s = threadIdx.x;
     const TIn *v = static_cast<const TIn *>(a.v);
     const TIn *gam = static_cast<const TIn *>(a.gamma);
@@ -231,9 +235,10 @@ __device__ __forceinline__ void load_chunk(const BwdArgs &a, ChunkPf<HV> &p, int
     if (s < Cc) p.gam = to_f32(gam[(static_cast<int64_t>(b) * a.T + t0 + s) * a.H + h]);
 }
 
-template <bool ADJ, int HV>
-__device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf<HV> &p, int Cc, int K) {
-    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV>::kPfA, kPfV = ChunkPf<HV>::kPfV;
+template <bool ADJ, int HV, int EVM>
+__device__ __forceinline__ void store_chunk(ChunkTok<EVM> &ct, const ChunkPf<HV, EVM> &p, int Cc, int K) {
+    constexpr int kBwdThreads = kThreadsOf<HV>, kPfA = ChunkPf<HV, EVM>::kPfA,
+                  kPfV = ChunkPf<HV, EVM>::kPfV;
     const int s = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kPfA; ++j) {
@@ -259,11 +264,11 @@ __device__ __forceinline__ void store_chunk(ChunkTok &ct, const ChunkPf<HV> &p, 
 // Both serial kernels: thread HV s + hf of a workgroup serves slot slot0 + s,
 // channels [hf kCh, hf kCh + kCh); the slot's first thread sorts its
 // events, then all HV walk them.
-template <typename TIn, typename TS, int HV>
+template <typename TIn, typename TS, int HV, int EVM>
 __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_record_kernel(BwdArgs a) {
     constexpr int kCh = kBwdDv / HV;
-    __shared__ ChunkLds<HV> g;
-    __shared__ ChunkTok ct;
+    __shared__ ChunkLds<HV, EVM> g;
+    __shared__ ChunkTok<EVM> ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x / HV, c0 = (threadIdx.x % HV) * kCh;
     const bool first = c0 == 0;
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_record_kernel(BwdArgs a) {
     const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
     const int nslots = min(kSlotsPerWG, M - slot0);
     const bool own = s < nslots;
-    const int C = bwd_chunk(K);
+    const int C = bwd_chunk(K, EVM);
     float row[kCh];
     float m = 0.f;
     if (own) {
@@ -281,13 +286,13 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_record_kernel(BwdArgs a) {
         for (int c = 0; c < kCh; ++c) row[c] = to_f32(src[c]);
         m = a.mass0[static_cast<int64_t>(unit) * M + slot];
     }
-    ChunkPf<HV> pf;
-    load_chunk<TIn, false, HV>(a, pf, b, h, 0, min(C, T));
+    ChunkPf<HV, EVM> pf;
+    load_chunk<TIn, false, HV, EVM>(a, pf, b, h, 0, min(C, T));
     for (int t0 = 0; t0 < T; t0 += C) {
         const int Cc = min(C, T - t0), nev = Cc * K;
-        store_chunk<false, HV>(ct, pf, Cc, K);
+        store_chunk<false, HV, EVM>(ct, pf, Cc, K);
         lds_barrier();
-        if (t0 + C < T) load_chunk<TIn, false, HV>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
+        if (t0 + C < T) load_chunk<TIn, false, HV, EVM>(a, pf, b, h, t0 + C, min(C, T - t0 - C));
         int n;
         const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
         int *ev = g.list + base;
@@ -398,11 +403,11 @@ __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
     }
 }
 
-template <typename TIn, int HV>
+template <typename TIn, int HV, int EVM>
 __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_adjoint_kernel(BwdArgs a) {
     constexpr int kCh = kBwdDv / HV;
-    __shared__ ChunkLds<HV> g;
-    __shared__ ChunkTok ct;
+    __shared__ ChunkLds<HV, EVM> g;
+    __shared__ ChunkTok<EVM> ct;
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int s = threadIdx.x / HV, c0 = (threadIdx.x % HV) * kCh;
     const bool first = c0 == 0;
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_adjoint_kernel(BwdArgs a) 
     const int slot0 = blockIdx.y * kSlotsPerWG, slot = slot0 + s;
     const int nslots = min(kSlotsPerWG, M - slot0);
     const bool own = s < nslots;
-    const int C = bwd_chunk(K);
+    const int C = bwd_chunk(K, EVM);
     const int64_t srow = (static_cast<int64_t>(unit) * M + slot) * kBwdDv + c0;
     float dS[kCh];
     float dm = 0.f;
@@ -428,13 +433,13 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_adjoint_kernel(BwdArgs a) 
     }
     if (own && a.dmass_final) dm = a.dmass_final[static_cast<int64_t>(unit) * M + slot];
     const int nch = (T + C - 1) / C;
-    ChunkPf<HV> pf;
-    load_chunk<TIn, true, HV>(a, pf, b, h, (nch - 1) * C, T - (nch - 1) * C);
+    ChunkPf<HV, EVM> pf;
+    load_chunk<TIn, true, HV, EVM>(a, pf, b, h, (nch - 1) * C, T - (nch - 1) * C);
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int t0 = ci * C, Cc = min(C, T - t0), nev = Cc * K;
-        store_chunk<true, HV>(ct, pf, Cc, K);
+        store_chunk<true, HV, EVM>(ct, pf, Cc, K);
         lds_barrier();
-        if (ci > 0) load_chunk<TIn, true, HV>(a, pf, b, h, t0 - C, C);
+        if (ci > 0) load_chunk<TIn, true, HV, EVM>(a, pf, b, h, t0 - C, C);
         int n;
         const int base = group_events(g, ct.widx, ct.ridx, nev, slot0, nslots, n);
         int *ev = g.list + base;
@@ -681,27 +686,37 @@ template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
     const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
-    // The replay takes four lanes per slot.  The adjoint, at 165 registers
-    // with four, then fits one workgroup per CU: it takes four lanes when
-    // the grid has at most one workgroup per CU, else two.
-    if (a.state_bf16)
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_record_kernel<TIn, float, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
+    // Whether the grid has at most one workgroup per CU: then the adjoint
+    // takes four lanes per slot (at 185 registers one workgroup fits a CU)
+    // and both serial kernels take 4096-event chunks; otherwise two lanes
+    // and 2048 events, two workgroups per CU.  The replay always takes four
+    // lanes per slot.
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 0;
+    const bool wide = static_cast<int64_t>(grid.x) * grid.y <= ncu;
+    if (a.state_bf16) {
+        if (wide)
+            hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t, 4, 4096>), grid, dim3(kThreadsOf<4>), 0, st, a);
+        else
+            hipLaunchKernelGGL((bwd_record_kernel<TIn, bf16_t, 4, 2048>), grid, dim3(kThreadsOf<4>), 0, st, a);
+    } else {
+        if (wide)
+            hipLaunchKernelGGL((bwd_record_kernel<TIn, float, 4, 4096>), grid, dim3(kThreadsOf<4>), 0, st, a);
+        else
+            hipLaunchKernelGGL((bwd_record_kernel<TIn, float, 4, 2048>), grid, dim3(kThreadsOf<4>), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        ncu = 0;
-    if (static_cast<int64_t>(grid.x) * grid.y <= ncu)
-        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 4>), grid, dim3(kThreadsOf<4>), 0, st, a);
+    if (wide)
+        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 4, 4096>), grid, dim3(kThreadsOf<4>), 0, st, a);
     else
-        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 2>), grid, dim3(kThreadsOf<2>), 0, st, a);
+        hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 2, 2048>), grid, dim3(kThreadsOf<2>), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     {
