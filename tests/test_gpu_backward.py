@@ -61,6 +61,15 @@ CASES = {
     "top8": ("prefill_top8", dict(B=1, T=96, H=2), {}),
     "cape3_mask_norm": ("prefill_top8", dict(B=2, T=64, H=2), dict(cape=3, content_heads=0b10, norm=True)),
     "dp2": ("tiny", dict(B=1, T=80, H=2), dict(d_p=2, U=8, K=5)),
+    # the largest K (8-bit base, 512 slots; three chunks at 32 tokens)
+    "kmax": ("tiny", dict(B=1, T=70, H=1), dict(d_p=8, U=3, K=64)),
+    # K = 1 (64 slots; two chunks at 64 tokens).  With one read per token
+    # the RMSNorm leaves the output independent of the read weight except
+    # through eps_norm, so d rho = <dr, S_j> is what remains after the 64
+    # fp32 terms cancel (dr is orthogonal to r = rho S_j up to eps): dq is
+    # compared to 1e-3 (worst seen 2.5e-4); dk, from the writes, keeps the
+    # standard tolerance.
+    "k1": ("tiny", dict(B=1, T=90, H=2), dict(d_p=4, U=3, K=1, dq_tol=1e-3)),
 }
 
 
@@ -143,7 +152,7 @@ def test_backward_matches_oracle(rn, BWo, case):
     tol = GRAD_TOL_BF16 if sbf else GRAD_TOL
     worst = {}
     for n, m_ in (("dv", tok), ("dg", tok), ("dgamma", tok), ("dq", tok), ("dk", tok)):
-        worst[n] = close(n, to_np(got[n]), ref[n], m_, tol)
+        worst[n] = close(n, to_np(got[n]), ref[n], m_, opt.get("dq_tol", tol) if n == "dq" else tol)
     worst["dS0"] = close("dS0", to_np(got["dS0"]), ref["dS0"], clean, tol)
     worst["dm0"] = close("dm0", to_np(got["dmass0"]), ref["dm0"], clean, tol)
     if clean.all():
