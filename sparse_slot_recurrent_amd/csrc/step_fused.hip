@@ -213,6 +213,20 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
     float *scr = reinterpret_cast<float *>(smem + lo.cr);
     float *sred = reinterpret_cast<float *>(smem + lo.red);
 
+    // the gates and norm weights of the wave's units do not depend on the
+    // addresses: their loads go out first and land during the decoding
+    const TIn *gg = static_cast<const TIn *>(a.g);
+    float gpre[UPW][CPO], ompre[CPO];
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const int unit = min(u0 + i, units - 1);
+        const TIn *gu = gg + static_cast<int64_t>(unit / a.H) * a.ld_g + (unit % a.H) * DV + lane * CPO;
+#pragma unroll
+        for (int c = 0; c < CPO; ++c) gpre[i][c] = to_f32(gu[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPO; ++c) ompre[c] = a.norm_w ? a.norm_w[lane * CPO + c] : 1.0f;
+
     // every logit the wave decodes, fetched at once
     for (int i = lane; i < UPW * 2 * L; i += kWave) {
         const int g = i / L, e = i - g * L;
@@ -301,7 +315,6 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
 
     const TIn *v = static_cast<const TIn *>(a.v);
     const TIn *gam = static_cast<const TIn *>(a.gamma);
-    const TIn *gg = static_cast<const TIn *>(a.g);
     TS *S = static_cast<TS *>(a.S);
     TS *out = static_cast<TS *>(a.out);
     const int npair = nu * K;  // <= 32
@@ -432,12 +445,10 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
             ss = wave_sum(ss);
             const float den = ss / static_cast<float>(DV) + a.eps_norm;
             const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-            const TIn *gu = gg + static_cast<int64_t>(unit / a.H) * a.ld_g + (unit % a.H) * DV + lane * CPO;
             TS *ou = out + static_cast<int64_t>(unit) * DV + lane * CPO;
 #pragma unroll
             for (int c = 0; c < CPO; ++c) {
-                const float om = a.norm_w ? a.norm_w[lane * CPO + c] : 1.0f;
-                ou[c] = from_f32<TS>(r[c] * inv * om * sigmoid(to_f32(gu[c])));
+                ou[c] = from_f32<TS>(r[c] * inv * ompre[c] * sigmoid(gpre[ul][c]));
             }
         }
     }
