@@ -180,7 +180,7 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
  * paragraph treats training and prefill alike).  The pages give no backward
  * formulas: this is the exact derivative of steps 1-4 with the Top-K
  * selection held fixed (it is piecewise constant), the power-decay retention
- * differentiated exactly (the paper digest's proxy gradient is not defined
+ * differentiated exactly (the AI Radio page's proxy gradient is not defined
  * there and is not used), and each fp32 storage rounding passing its
  * gradient through.  The gradients are those of
  *   sum(out * dout) + sum(S_final * dS_final) + sum(mass_final * dmass_final)
@@ -220,7 +220,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q,
  * project page, layer outline: the token is projected to key, query and
  * value, the GSU's gamma comes from the token by a learned projection, and
  * the gated read is projected out), with the address weights re-parameterised
- * as W = e^alpha * W' per head (paper digest, stability of the decoder: alpha
+ * as W = e^alpha * W' per head (AI Radio page, stability of the decoder: alpha
  * sets the temperature of the Product Softmax).
  *
  * All weights are bf16, [out, in] row-major (one output's weights contiguous

@@ -17,7 +17,7 @@ again here in torch so that autograd can differentiate them:
 Readings fixed here (the pages do not define the backward pass):
   * the Top-K selection is held fixed (it is piecewise constant in the
     logits); gradients reach the logits only through the selected weights;
-  * the power-decay retention is differentiated exactly.  The paper digest
+  * the power-decay retention is differentiated exactly.  The AI Radio page
     mentions a proxy gradient for it but does not give one ("parity
     unpinned" for that proxy, which is not implemented);
   * with round_storage, each stored state row is rounded to its storage

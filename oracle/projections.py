@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: plain numpy in fp64, no blocking or fusion.
 Follows two passages: the project page's outline of a layer (the token is
 projected to key, query and value; the GSU's gamma comes "from the current
 token by a learned projection" in its Gated Sparse Update section; the gated
-read is projected out), and the paper digest's note that the address weights
+read is projected out), and the AI Radio page's remark that the address weights
 are re-parameterised as W = e^alpha * W' with one learned alpha per head,
 which sets the temperature of the Product Softmax.
 

@@ -6,7 +6,7 @@
 //                   matrix, so that one GEMM projects a token to all of q, k,
 //                   v, g and gamma; the q and k columns carry the
 //                   re-parameterised address weights W = e^alpha W' of the
-//                   paper digest's stability note: head h's columns are
+//                   AI Radio page's stability remark: head h's columns are
 //                   scaled by t_h = fp32(e^alpha_h) and rounded to bf16 once,
 //                   from the exact product (a bf16 times an fp32 has at most
 //                   32 significant bits, so fp64 holds it).
