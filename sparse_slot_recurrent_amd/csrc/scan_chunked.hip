@@ -609,6 +609,13 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
 
     // The next chunk's plan and values, loaded one chunk ahead.
     constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
+    // value element tid + j NT of a chunk's slice is token vt0 + j TPJ,
+    // channel vcc: the thread's column is fixed and its rows step by TPJ
+    constexpr int TPJ = kNT / CG;
+    const int vt0 = static_cast<int>(static_cast<unsigned>(tid) / CG);
+    const int vcc = static_cast<int>(static_cast<unsigned>(tid) % CG);
+    const TIn *vcol = v + cg * CG + vcc;
+    const uint32_t ldv32 = static_cast<uint32_t>(a.ld_v);  // the launcher checks ld_v < 2^32
     int pf_wtv[kEVT], pf_rv[kEVT];
     float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT];
     TIn pf_v[VPT];  // raw: converting at load time would wait for each load
@@ -640,9 +647,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = min(tid + j * kNT, Cc * CG - 1);  // in range; extra lanes unused
-            const int t = i / CG, cc = i % CG;
-            pf_v[j] = v[static_cast<int64_t>(t0 + t) * a.ld_v + cg * CG + cc];
+            const int t = min(vt0 + j * TPJ, Cc - 1);  // in range; extra lanes unused
+            pf_v[j] = vcol[static_cast<uint64_t>(static_cast<uint32_t>(t0 + t)) * ldv32];
         }
         if constexpr (RES) {
             if (tid < M) {
@@ -685,10 +691,10 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int i = tid + j * kNT;
-            if (i < Cc * CG) {
-                if constexpr (std::is_same_v<VT, TIn>) vbuf[(i / CG) * VROW + i % CG] = pf_v[j];
-                else vbuf[(i / CG) * VROW + i % CG] = to_f32(pf_v[j]);
+            const int t = vt0 + j * TPJ;
+            if (t < Cc) {
+                if constexpr (std::is_same_v<VT, TIn>) vbuf[t * VROW + vcc] = pf_v[j];
+                else vbuf[t * VROW + vcc] = to_f32(pf_v[j]);
             }
         }
         const int my_wo = pf_dwo, my_nx = pf_dnx, nt = pf_nt;
@@ -1016,6 +1022,7 @@ hipError_t launch_scan_chunked(const ChunkArgs &args, hipStream_t st) {
     if (!args.p.ok) return hipErrorInvalidValue;
     ChunkArgs a = args;
     if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
+    if (a.ld_v > 0xffffffffll) return hipErrorInvalidValue;  // the scan's row steps are 32-bit
     if (!a.ld_g) a.ld_g = static_cast<int64_t>(a.H) * a.d_v;
     if (!a.ld_gamma) a.ld_gamma = a.H;
     if (a.in_bf16)
