@@ -71,9 +71,14 @@ struct ChunkPlan {
     int ncg;            // d_v / CG
     int RG;             // lanes per token in the read reduction
     bool raw_values;    // values kept in LDS as the bf16 input (else fp32)
+    // Resident mode: a slot with more than n0 writes in a chunk may be handed
+    // off after its first n0 writes to one of at most HMAX helper threads
+    // (busiest slots first), so that no wave waits on its busiest slot.
+    int n0;
+    int HMAX;
     int64_t n_chunks;
     // one (unit, chunk) plan record and its sections (byte offsets)
-    size_t rec_bytes, o_ent, o_map, o_wtv, o_ww, o_wa, o_rv, o_rr;
+    size_t rec_bytes, o_ent, o_map, o_hl, o_wtv, o_ww, o_wa, o_rv, o_rr;
     size_t lds_plan, lds_scan;
     size_t ws_rbuf, ws_sumsq, ws_mass, ws_plan;  // workspace section sizes
 };

@@ -52,6 +52,7 @@ constexpr int kPT = 512;                            // plan kernel threads
 constexpr int kEPW = kMaxEV / kPT;                  // writes (and reads) per plan thread
 constexpr int kEVT = (kMaxEV + kNT - 1) / kNT;      // plan entries per scan thread
 constexpr int kEPN = 2 * kMaxEV / kNT;              // touched slots per thread (HBM rows)
+constexpr int kHBins = 32;                          // write-count bins of the hand-off order
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -188,7 +189,7 @@ __device__ __forceinline__ int div_by(uint32_t e, uint64_t m) {
 
 // LDS of the plan kernel (byte offsets).
 struct PlanLds {
-    size_t key, cf, wo, bk, sk, sa, need, wtot, total;
+    size_t key, cf, wo, bk, sk, sa, need, wtot, hist, total;
 };
 __host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
     PlanLds L{};
@@ -202,6 +203,7 @@ __host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
     L.sa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // staged write retention
     L.need = o; o = al16(o + static_cast<size_t>(p.ENT + p.EV + 1) * 4);  // versions read
     L.wtot = o; o = al16(o + 32 * 4);
+    L.hist = o; o = al16(o + (2 * kHBins + 1) * 4);                       // hand-off bins, offsets, total
     L.total = o;
     return L;
 }
@@ -211,7 +213,7 @@ struct PlanHdr {
     int nt;    // touched slots (entries)
     int nver;  // version rows
     int nwt;   // valid writes
-    int pad;
+    int nh;    // resident mode: slots handed off after their first n0 writes
 };
 
 constexpr int kReadFlag = 1 << 30;
@@ -243,6 +245,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     int *need = reinterpret_cast<int *>(smem + L.need);
     int *sa = reinterpret_cast<int *>(smem + L.sa);
     int *wtot = reinterpret_cast<int *>(smem + L.wtot);
+    int *hist = reinterpret_cast<int *>(smem + L.hist);  // [kHBins] counts, offsets, total
 
     unsigned char *rec = a.plan + (static_cast<int64_t>(unit) * P.n_chunks + chunk) * P.rec_bytes;
     int *ent_slot = reinterpret_cast<int *>(rec + P.o_ent);  // per entry: slot, write offset,
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     int *ent_x0 = ent_nw + P.ENTA;
     int *dwo = reinterpret_cast<int *>(rec + P.o_map);  // resident mode, per slot: write
     int *dnx = dwo + M;                                 // offset; writes | (version-0 row + 1) << 16
+    int *hl = reinterpret_cast<int *>(rec + P.o_hl);    // handed-off slots: rest offset | rest << 16
     int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
     float *ww = reinterpret_cast<float *>(rec + P.o_ww);
     float *wa = reinterpret_cast<float *>(rec + P.o_wa);
@@ -284,6 +288,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         if (hashed) tkey[i] = -1;
     }
     for (int i = tid; i <= P.ENT + P.EV; i += kPT) need[i] = 0;
+    if (tid < 2 * kHBins) hist[tid] = 0;
     lds_barrier();
 
     // ---- 1. every event finds its slot's entry; writes count, reads flag.
@@ -401,11 +406,8 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
     // ---- 6. the record: entries, writes staged in LDS in causal order, then
     //         everything stored with consecutive lanes on consecutive words
-    if (tid == 0) {
-        PlanHdr hd{nt, nver, nwt, 0};
-        *reinterpret_cast<PlanHdr *>(rec) = hd;
-    }
-    if (P.resident) {
+    int nh = 0;
+    if (P.resident && P.HMAX == 0) {
         for (int p = tid; p < M; p += kPT) {
             const int eid = tcf[p];
             int wo = 0, nx = 0;
@@ -417,6 +419,59 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             dwo[p] = wo;
             dnx[p] = nx;
         }
+    } else if (P.resident) {
+        // Hand-off: the slots with more than n0 writes, busiest first (bins
+        // of the write count, the last bin holding every count beyond it),
+        // as many as there are spare rows at the end of the scan's version
+        // buffer and helper threads.  Positions within a bin come from LDS
+        // atomics, so they vary from run to run; a position decides only
+        // which thread applies a slot's writes, never the arithmetic.
+        constexpr int kSP = (kNT + kPT - 1) / kPT;  // slots per thread (M <= kNT)
+        int hbin[kSP], hrank[kSP];
+#pragma unroll
+        for (int j = 0; j < kSP; ++j) {
+            const int p = tid + j * kPT;
+            hbin[j] = -1;
+            if (P.HMAX > 0 && p < M && tcf[p] >= 0) {
+                const int nw = ewo[tcf[p] + 1] - ewo[tcf[p]];
+                if (nw > P.n0) {
+                    hbin[j] = kHBins - 1 - min(nw - P.n0 - 1, kHBins - 1);
+                    hrank[j] = atomicAdd(&hist[hbin[j]], 1);
+                }
+            }
+        }
+        lds_barrier();
+        if (tid < kWave) {  // offsets of the bins: one wave's prefix sum
+            const int c = tid < kHBins ? hist[tid] : 0;
+            const int inc = wave_incl_scan(c);
+            if (tid < kHBins) hist[kHBins + tid] = inc - c;
+            if (tid == kWave - 1) hist[2 * kHBins] = inc;  // total
+        }
+        lds_barrier();
+        nh = min(hist[2 * kHBins], min(P.HMAX, P.EV - nver));
+#pragma unroll
+        for (int j = 0; j < kSP; ++j) {
+            const int p = tid + j * kPT;
+            if (p < M) {
+                const int eid = tcf[p];
+                int wo = 0, nx = 0;
+                if (eid >= 0) {
+                    const int g = ewo[eid] + eid;
+                    const int nw = ewo[eid + 1] - ewo[eid];
+                    wo = ewo[eid];
+                    nx = nw | ((need[g + 1] > need[g] ? need[g] + 1 : 0) << 16);
+                    if (hbin[j] >= 0) {
+                        const int pos = hist[kHBins + hbin[j]] + hrank[j];
+                        if (pos < nh) {
+                            hl[pos] = (wo + P.n0) | ((nw - P.n0) << 16);
+                            wo |= (pos + 1) << 16;
+                        }
+                    }
+                }
+                dwo[p] = wo;
+                dnx[p] = nx;
+            }
+        }
     } else {
         for (int eid = tid; eid < nt; eid += kPT) {
             const int g = ewo[eid] + eid;
@@ -424,6 +479,10 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             ent_nw[eid] = ewo[eid + 1] - ewo[eid];
             ent_x0[eid] = need[g + 1] > need[g] ? need[g] : -1;
         }
+    }
+    if (tid == 0) {
+        PlanHdr hd{nt, nver, nwt, nh};
+        *reinterpret_cast<PlanHdr *>(rec) = hd;
     }
 #pragma unroll
     for (int j = 0; j < kEPW; ++j) {
@@ -452,7 +511,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
 // LDS of the scan kernel (byte offsets).
 struct ScanLds {
-    size_t v, wtv, wwa, rv, rr, ver, total;
+    size_t v, wtv, wwa, rv, rr, ver, hm, total;
 };
 __host__ __device__ inline size_t al256d(size_t x) { return (x + 255) & ~size_t(255); }
 __host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int sbytes, int vbytes) {
@@ -464,6 +523,7 @@ __host__ __device__ inline ScanLds scan_lds(const ChunkPlan &p, int64_t M, int s
     L.rv = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read: version row
     L.rr = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                  // read weight
     L.ver = o = al256d(o); o = al16(o + static_cast<size_t>(p.EV) * p.CG * sbytes);  // version rows
+    L.hm = o; o = al16(o + static_cast<size_t>(p.HMAX) * 4);                        // handed-off masses
     L.total = o;
     return L;
 }
@@ -491,6 +551,29 @@ __device__ __forceinline__ void store_row_x(unsigned char *lds, uint32_t a0, con
             w[q] = static_cast<uint32_t>(bf16_rne(x[8 * j + 2 * q]).bits) |
                    (static_cast<uint32_t>(bf16_rne(x[8 * j + 2 * q + 1]).bits) << 16);
         *reinterpret_cast<uint4 *>(lds + (a0 ^ (j << 4))) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+template <int CG>
+__device__ __forceinline__ void load_row_x(const unsigned char *lds, uint32_t a0, float (&x)[CG], float) {
+#pragma unroll
+    for (int j = 0; j < CG / 4; ++j) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(lds + (a0 ^ (j << 4)));
+        float f[4];
+        unpack_chunk(u, f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[4 * j + q] = f[q];
+    }
+}
+template <int CG>
+__device__ __forceinline__ void load_row_x(const unsigned char *lds, uint32_t a0, float (&x)[CG], bf16_t) {
+#pragma unroll
+    for (int j = 0; j < CG / 8; ++j) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(lds + (a0 ^ (j << 4)));
+        float f[8];
+        unpack_chunk(u, f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[8 * j + q] = f[q];
     }
 }
 
@@ -543,6 +626,79 @@ __device__ __forceinline__ void walk_slot(int wo, int nw, int x0r, float (&x)[CG
     }
 }
 
+// One 16-byte piece of a row slice (CP = 16 / sizeof(TS) channels) between
+// LDS and registers; piece h of the row whose piece 0 is at a0 is at a0 ^ (h << 4).
+template <int CP>
+__device__ __forceinline__ void load_piece(const unsigned char *lds, uint32_t a, float (&x)[CP]) {
+    unpack_chunk(*reinterpret_cast<const uint4 *>(lds + a), x);
+}
+__device__ __forceinline__ void store_piece(unsigned char *lds, uint32_t a, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(lds + a) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_piece(unsigned char *lds, uint32_t a, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w[q] = static_cast<uint32_t>(bf16_rne(x[2 * q]).bits) | (static_cast<uint32_t>(bf16_rne(x[2 * q + 1]).bits) << 16);
+    *reinterpret_cast<uint4 *>(lds + a) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+// Channels [c0, c0 + CP) of value row t (rows of VROW elements), as fp32.
+template <int CP>
+__device__ __forceinline__ void value_part(const float *vbuf, int off, float (&vt)[CP]) {
+#pragma unroll
+    for (int j = 0; j < CP / 4; ++j) {
+        const float4 f = reinterpret_cast<const float4 *>(vbuf + off)[j];
+        vt[4 * j] = f.x;
+        vt[4 * j + 1] = f.y;
+        vt[4 * j + 2] = f.z;
+        vt[4 * j + 3] = f.w;
+    }
+}
+template <int CP>
+__device__ __forceinline__ void value_part(const bf16_t *vbuf, int off, float (&vt)[CP]) {
+#pragma unroll
+    for (int j = 0; j < CP / 4; ++j) {
+        const uint2 u = reinterpret_cast<const uint2 *>(vbuf + off)[j];
+        vt[4 * j] = __uint_as_float(u.x << 16);
+        vt[4 * j + 1] = __uint_as_float(u.x & 0xffff0000u);
+        vt[4 * j + 2] = __uint_as_float(u.y << 16);
+        vt[4 * j + 3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+}
+
+// walk_slot for piece h of a row slice: the LH = CG / CP lanes that share a
+// slot each apply its writes to their own piece (each computing the same
+// mass and rate) and store their piece of the versions reads see.
+template <typename TS, int CG, typename TV>
+__device__ __forceinline__ void walk_piece(int wo, int nw, int h, float (&xp)[16 / sizeof(TS)], float &m,
+                                           float eps, const int *wtv, const float2 *wwa, const TV *vbuf,
+                                           unsigned char *lds, uint32_t ver_off) {
+    constexpr int CP = 16 / static_cast<int>(sizeof(TS));
+    constexpr int VROW = CG + 16 / static_cast<int>(sizeof(TV));
+    int tvn = 0;
+    float2 wan = make_float2(0.f, 0.f);
+    if (nw > 0) {
+        tvn = wtv[wo];
+        wan = wwa[wo];
+    }
+    for (int i = 0; i < nw; ++i) {
+        const int tv = tvn;
+        const int t = tv & 1023, vr = (tv >> 10) - 1;
+        const float2 wa = wan;
+        float vt[CP];
+        value_part<CP>(vbuf, t * VROW + h * CP, vt);
+        if (i + 1 < nw) {
+            tvn = wtv[wo + i + 1];
+            wan = wwa[wo + i + 1];
+        }
+        m = fmaf(wa.y, m, wa.x);
+        const float lam = wa.x * __builtin_amdgcn_rcpf(m + eps);
+#pragma unroll
+        for (int c = 0; c < CP; ++c) xp[c] = stored<TS>(fmaf(lam, vt[c] - xp[c], xp[c]));
+        if (vr >= 0) store_piece(lds, row_chunk0<TS, CG>(ver_off, vr) ^ (h << 4), xp);
+    }
+}
+
 // CG values of a row slice in HBM.
 template <typename TS, int CG>
 struct HRow {
@@ -552,7 +708,8 @@ struct HRow {
 // VT: the value rows' type in LDS: fp32 (converted once at staging), or the
 // bf16 input itself (half the LDS, which buys a longer chunk, at a
 // conversion per write); the planner picks per configuration.
-template <typename TIn, typename TS, int CG, bool RES, typename VT>
+// HAND: resident mode with the hand-off of the busiest slots (P.HMAX > 0).
+template <typename TIn, typename TS, int CG, bool RES, typename VT, bool HAND>
 __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
@@ -584,6 +741,9 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     int *s_rv = reinterpret_cast<int *>(smem + L.rv);
     float *s_rr = reinterpret_cast<float *>(smem + L.rr);
     TS *ver = reinterpret_cast<TS *>(smem + L.ver);
+    float *s_hm = reinterpret_cast<float *>(smem + L.hm);
+    constexpr int kCP = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
+    constexpr int kLH = CG / kCP;                            // lanes per handed-off slot
 
     // this unit's token 0 in the values
     const TIn *v = static_cast<const TIn *>(a.v) + static_cast<int64_t>(b) * a.T * a.ld_v + h * d_v;
@@ -620,6 +780,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT];
     TIn pf_v[VPT];  // raw: converting at load time would wait for each load
     int pf_dwo = 0, pf_dnx = 0, pf_nt = 0;  // resident: this slot's write offset, writes | x0
+    int pf_nh = 0, pf_hl = 0;               // resident: slots handed off; this thread's one
     auto prefetch = [&](int c) {
         const unsigned char *rec = plan0 + static_cast<int64_t>(c) * P.rec_bytes;
         const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
@@ -629,6 +790,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
         const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
         pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
+        if (HAND) pf_nh = reinterpret_cast<const PlanHdr *>(rec)->nh;
         // every load is independent of every other (no wait on the header):
         // the write list is read to its capacity, entries past its end are
         // never used
@@ -655,6 +817,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                 pf_dwo = reinterpret_cast<const int *>(rec + P.o_map)[tid];
                 pf_dnx = reinterpret_cast<const int *>(rec + P.o_map)[M + tid];
             }
+            // read to capacity like the write list; entries past nh unused
+            if (HAND && tid / kLH < P.HMAX) pf_hl = reinterpret_cast<const int *>(rec + P.o_hl)[tid / kLH];
         }
     };
 
@@ -697,15 +861,47 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                 else vbuf[t * VROW + vcc] = to_f32(pf_v[j]);
             }
         }
-        const int my_wo = pf_dwo, my_nx = pf_dnx, nt = pf_nt;
+        const int my_wo = HAND ? pf_dwo & 0xffff : pf_dwo, my_nx = pf_dnx, nt = pf_nt;
+        const int my_hp = HAND ? static_cast<int>(static_cast<uint32_t>(pf_dwo) >> 16) - 1 : -1;  // hand-off row
+        const int nh = HAND ? pf_nh : 0, my_hl = pf_hl;
         lds_barrier();
         // ---- 2. the next chunk's loads go out now and land during the walk
         if (c + 1 < nchunks) prefetch(c + 1);
         // ---- 3. walk the touched slots
         if constexpr (RES) {
-            if (tid < M && my_nx != 0)
-                walk_slot<TS, CG>(my_wo, my_nx & 0xffff, (my_nx >> 16) - 1, x, m, a.eps_gsu, s_wtv, s_wwa, vbuf,
-                                  smem, ver_off);
+            // the owner applies its slot's first writes (all of them unless
+            // the slot is handed off) ...
+            if (tid < M && my_nx != 0) {
+                const int nw = my_nx & 0xffff;
+                walk_slot<TS, CG>(my_wo, HAND && my_hp >= 0 ? P.n0 : nw, (my_nx >> 16) - 1, x, m, a.eps_gsu, s_wtv,
+                                  s_wwa, vbuf, smem, ver_off);
+                if (HAND && my_hp >= 0) {
+                    store_row_x<CG>(smem, row_chunk0<TS, CG>(ver_off, EV - 1 - my_hp), x, TS{});
+                    s_hm[my_hp] = m;
+                }
+            }
+            // ... then helper j applies the rest of the j-th busiest slot's
+            // writes to its row, parked in version row EV - 1 - j (the plan
+            // leaves those rows free), and the owner takes the row back
+            if (HAND && nh > 0) {
+                lds_barrier();
+                const int j = tid / kLH, hp = tid % kLH;  // helper j, piece hp
+                if (j < nh) {
+                    const uint32_t a0 = row_chunk0<TS, CG>(ver_off, EV - 1 - j) ^ (hp << 4);
+                    float xp[kCP];
+                    load_piece<kCP>(smem, a0, xp);
+                    float mm = s_hm[j];
+                    walk_piece<TS, CG>(my_hl & 0xffff, my_hl >> 16, hp, xp, mm, a.eps_gsu, s_wtv, s_wwa, vbuf,
+                                       smem, ver_off);
+                    store_piece(smem, a0, xp);
+                    if (hp == 0) s_hm[j] = mm;
+                }
+                lds_barrier();
+                if (my_hp >= 0) {
+                    load_row_x<CG>(smem, row_chunk0<TS, CG>(ver_off, EV - 1 - my_hp), x, TS{});
+                    m = s_hm[my_hp];
+                }
+            }
         } else {
             // touched rows from HBM, EB at a time (entries already in
             // registers): rows and masses, then the walks and write-backs
@@ -902,8 +1098,13 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     using VB = std::conditional_t<std::is_same_v<TIn, bf16_t>, bf16_t, float>;
-    auto sk = P.resident ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB> : scan_kernel<TIn, TS, CG, true, float>)
-                         : (P.raw_values ? scan_kernel<TIn, TS, CG, false, VB> : scan_kernel<TIn, TS, CG, false, float>);
+    auto sk = P.resident
+                  ? (P.HMAX > 0 ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, true>
+                                                : scan_kernel<TIn, TS, CG, true, float, true>)
+                                : (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, false>
+                                                : scan_kernel<TIn, TS, CG, true, float, false>))
+                  : (P.raw_values ? scan_kernel<TIn, TS, CG, false, VB, false>
+                                  : scan_kernel<TIn, TS, CG, false, float, false>);
     e = set_lds(sk, P.lds_scan);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * P.ncg)), dim3(kNT), P.lds_scan, st, a);
@@ -977,15 +1178,31 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
                 while (g < 16 && g < K && static_cast<int64_t>(C) * g * 2 <= kNT) g *= 2;
                 q.RG = g;
             }
+            q.n0 = 1;
+            q.HMAX = 0;
             q.lds_plan = plan_lds(q, M).total;
             q.lds_scan = scan_lds(q, M, sbytes, vbytes).total;
             q.raw_values = vbytes == 2;
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
+            if (q.resident && static_cast<int64_t>(C) * K >= 2 * M) {
+                // helpers for the busiest slots, where a chunk writes each
+                // slot at least twice on average (below that the hand-off's
+                // barriers cost about what it saves: Top-8, 1.75 writes per
+                // slot, ran 1-3% slower with it, Top-32, 3 writes, 7%
+                // faster): as many masses as the LDS left over holds, at
+                // most one helper group per thread group and slot
+                const size_t spare = (kChunkLdsLimit - q.lds_scan) / 16 * 4;  // whole 16-byte pieces
+                const int lh = CG * sbytes / 16;  // lanes per handed-off slot, one 16-byte piece each
+                q.HMAX = static_cast<int>(std::min<int64_t>(std::min<int64_t>(M, kNT / lh), static_cast<int64_t>(spare)));
+                q.lds_scan = scan_lds(q, M, sbytes, vbytes).total;
+                if (q.lds_scan > kChunkLdsLimit) q.HMAX = 0, q.lds_scan = scan_lds(q, M, sbytes, vbytes).total;
+            }
             q.n_chunks = (T + C - 1) / C;
             size_t o = 256;  // header
             q.ENTA = (q.ENT + 63) & ~63;
             q.o_ent = o; o += al256(q.resident ? 0 : static_cast<size_t>(q.ENTA) * 16);
             q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 8 : 0);
+            q.o_hl = o; o += al256(static_cast<size_t>(q.HMAX) * 4);
             q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_wa = o; o += al256(static_cast<size_t>(EV) * 4);
