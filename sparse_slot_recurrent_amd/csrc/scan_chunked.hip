@@ -950,60 +950,109 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         if constexpr (RES) lds_barrier(); else __syncthreads();
         if (c + 1 < nchunks) prefetch_ent(c + 1);  // lands during the reduction
         // ---- 4. reads: r = sum_k rho_k * version_k over the slice; G = P.RG
-        //         lanes share a token, lane g taking reads k = g, g + G, ...
-        //         in order (whole rows), combined by a butterfly (a fixed
-        //         order, the same bits in every lane); r and the slice's sum
-        //         of squares go to global memory
+        //         lanes share a token.  With 1 < NCH <= G (NCH: pieces per row), lane
+        //         g takes piece g % NCH of reads k = g / NCH, g / NCH + G / NCH,
+        //         ... in order, and the G / NCH lanes of a piece are combined
+        //         by a butterfly; the lanes of a token then read neighbouring
+        //         pieces of one row.  Otherwise lane g takes whole rows of
+        //         reads k = g, g + G, ...  r and the slice's sum of squares go
+        //         to global memory.
         {
             constexpr int EPC = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
             constexpr int NCH = CG / EPC;                            // pieces per row
             const int G = P.RG;
-            for (int i = tid; i < Cc * G; i += kNT) {
-                const int g = i % G, t = i / G;
-                float r[CG];
+            if (NCH > 1 && G >= NCH) {
+                const int GR = G / NCH;  // lanes per piece
+                for (int i = tid; i < Cc * G; i += kNT) {
+                    const int g = i % G, t = i / G;
+                    const int jc = g % NCH, kr = g / NCH;
+                    float r[EPC];
 #pragma unroll
-                for (int cc = 0; cc < CG; ++cc) r[cc] = 0.f;
-                for (int k = g; k < K; k += G) {
-                    // skipped reads have no row; a zero weight adds nothing
-                    const int row = t * K + k;
-                    const int vr = s_rv[row];
-                    const float rw = s_rr[row];
-                    if (vr >= 0 && rw != 0.f) {
-                        const uint32_t a0 = row_chunk0<TS, CG>(ver_off, vr);
-#pragma unroll
-                        for (int j = 0; j < NCH; ++j) {
-                            const uint4 u = *reinterpret_cast<const uint4 *>(smem + (a0 ^ (j << 4)));
+                    for (int cc = 0; cc < EPC; ++cc) r[cc] = 0.f;
+                    for (int k = kr; k < K; k += GR) {
+                        // skipped reads have no row; a zero weight adds nothing
+                        const int row = t * K + k;
+                        const int vr = s_rv[row];
+                        const float rw = s_rr[row];
+                        if (vr >= 0 && rw != 0.f) {
+                            const uint4 u = *reinterpret_cast<const uint4 *>(
+                                smem + (row_chunk0<TS, CG>(ver_off, vr) ^ (jc << 4)));
                             float sv[EPC];
                             unpack_chunk(u, sv);
 #pragma unroll
-                            for (int cc = 0; cc < EPC; ++cc) r[j * EPC + cc] = fmaf(rw, sv[cc], r[j * EPC + cc]);
+                            for (int cc = 0; cc < EPC; ++cc) r[cc] = fmaf(rw, sv[cc], r[cc]);
                         }
                     }
-                }
 #pragma unroll
-                for (int cc = 0; cc < CG; ++cc) {
-                    if (G > 1) r[cc] += lane_xor<1>(r[cc]);
-                    if (G > 2) r[cc] += lane_xor<2>(r[cc]);
-                    if (G > 4) r[cc] += lane_xor<4>(r[cc]);
-                    if (G > 8) r[cc] += lane_xor<8>(r[cc]);
-                }
-                const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
-                float *dst = a.rbuf + th * d_v + cg * CG;
-#pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    if (j % G == g) {
-#pragma unroll
-                        for (int cc = 0; cc < EPC; cc += 4)
-                            *reinterpret_cast<float4 *>(dst + j * EPC + cc) =
-                                make_float4(r[j * EPC + cc], r[j * EPC + cc + 1], r[j * EPC + cc + 2],
-                                            r[j * EPC + cc + 3]);
+                    for (int cc = 0; cc < EPC; ++cc) {
+                        if (NCH <= 1 && G > 1) r[cc] += lane_xor<1>(r[cc]);
+                        if (NCH <= 2 && G > 2) r[cc] += lane_xor<2>(r[cc]);
+                        if (NCH <= 4 && G > 4) r[cc] += lane_xor<4>(r[cc]);
+                        if (NCH <= 8 && G > 8) r[cc] += lane_xor<8>(r[cc]);
                     }
-                }
-                if (g == 0) {
+                    const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
                     float ss = 0.f;
 #pragma unroll
-                    for (int cc = 0; cc < CG; ++cc) ss = fmaf(r[cc], r[cc], ss);
-                    a.sumsq[th * ncg + cg] = ss;
+                    for (int cc = 0; cc < EPC; ++cc) ss = fmaf(r[cc], r[cc], ss);
+                    if (NCH > 1) ss += lane_xor<1>(ss);
+                    if (NCH > 2) ss += lane_xor<2>(ss);
+                    if (NCH > 4) ss += lane_xor<4>(ss);
+                    if (kr == 0) {
+                        float *dst = a.rbuf + th * d_v + cg * CG + jc * EPC;
+#pragma unroll
+                        for (int cc = 0; cc < EPC; cc += 4)
+                            *reinterpret_cast<float4 *>(dst + cc) = make_float4(r[cc], r[cc + 1], r[cc + 2], r[cc + 3]);
+                        if (jc == 0) a.sumsq[th * ncg + cg] = ss;
+                    }
+                }
+            } else {
+                for (int i = tid; i < Cc * G; i += kNT) {
+                    const int g = i % G, t = i / G;
+                    float r[CG];
+#pragma unroll
+                    for (int cc = 0; cc < CG; ++cc) r[cc] = 0.f;
+                    for (int k = g; k < K; k += G) {
+                        // skipped reads have no row; a zero weight adds nothing
+                        const int row = t * K + k;
+                        const int vr = s_rv[row];
+                        const float rw = s_rr[row];
+                        if (vr >= 0 && rw != 0.f) {
+                            const uint32_t a0 = row_chunk0<TS, CG>(ver_off, vr);
+#pragma unroll
+                            for (int j = 0; j < NCH; ++j) {
+                                const uint4 u = *reinterpret_cast<const uint4 *>(smem + (a0 ^ (j << 4)));
+                                float sv[EPC];
+                                unpack_chunk(u, sv);
+#pragma unroll
+                                for (int cc = 0; cc < EPC; ++cc) r[j * EPC + cc] = fmaf(rw, sv[cc], r[j * EPC + cc]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < CG; ++cc) {
+                        if (G > 1) r[cc] += lane_xor<1>(r[cc]);
+                        if (G > 2) r[cc] += lane_xor<2>(r[cc]);
+                        if (G > 4) r[cc] += lane_xor<4>(r[cc]);
+                        if (G > 8) r[cc] += lane_xor<8>(r[cc]);
+                    }
+                    const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
+                    float *dst = a.rbuf + th * d_v + cg * CG;
+#pragma unroll
+                    for (int j = 0; j < NCH; ++j) {
+                        if (j % G == g) {
+#pragma unroll
+                            for (int cc = 0; cc < EPC; cc += 4)
+                                *reinterpret_cast<float4 *>(dst + j * EPC + cc) =
+                                    make_float4(r[j * EPC + cc], r[j * EPC + cc + 1], r[j * EPC + cc + 2],
+                                                r[j * EPC + cc + 3]);
+                        }
+                    }
+                    if (g == 0) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < CG; ++cc) ss = fmaf(r[cc], r[cc], ss);
+                        a.sumsq[th * ncg + cg] = ss;
+                    }
                 }
             }
         }
