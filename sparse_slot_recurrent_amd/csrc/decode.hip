@@ -25,9 +25,11 @@
 namespace ramnet {
 namespace {
 
+// Branch-free: both comparisons are evaluated and combined bitwise, so the
+// compiler emits no exec-mask branches inside the merge step.
 template <typename WT>
 __device__ __forceinline__ bool ranks_before(WT wa, int ia, WT wb, int ib) {
-    return wa > wb || (wa == wb && ia < ib);
+    return (wa > wb) | ((wa == wb) & (ia < ib));
 }
 
 __device__ __forceinline__ double wexp(double x) { return exp(x); }
@@ -160,12 +162,11 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
                 pb = sel ? pr[d] : pb;
             }
             ++hb;
-            WT ncw = WT(-1);  // -1: exhausted list
-            int ncp = 0;
-            if (hb < nb) {
-                ncw = BW(rd, hb) * pb;
-                ncp = BP(rd, hb) * DP + db;
-            }
+            // the entry is loaded from a valid position even when the list
+            // is exhausted (weight -1), so no branch guards the loads
+            const int hc = hb < nb ? hb : nb - 1;
+            const WT ncw = hb < nb ? BW(rd, hc) * pb : WT(-1);
+            const int ncp = BP(rd, hc) * DP + db;
 #pragma unroll
             for (int d = 0; d < DP; ++d) {
                 const bool sel = best == d;
