@@ -47,11 +47,13 @@ namespace {
 
 constexpr int kNT = 1024;  // threads per workgroup
 constexpr int kWavesPerBlock = kNT / kWave;
-constexpr int kMaxEV = 3072;                        // events of one kind per chunk
+constexpr int kMaxEV = 4096;                        // events of one kind per chunk
+constexpr int kMaxEVHbm = 3072;                     // the same with slot rows in HBM
 constexpr int kPT = 512;                            // plan kernel threads
-constexpr int kEPW = kMaxEV / kPT;                  // writes (and reads) per plan thread
-constexpr int kEVT = (kMaxEV + kNT - 1) / kNT;      // plan entries per scan thread
-constexpr int kEPN = 2 * kMaxEV / kNT;              // touched slots per thread (HBM rows)
+// Events per plan thread (EPW) and plan entries per scan thread (EVT) are
+// template parameters: EV / kPT and EV / kNT for chunks of at most 2048,
+// 3072 or 4096 events (EV rounded up to a multiple of 1024).
+constexpr int kEPN = 2 * kMaxEVHbm / kNT;           // touched slots per thread (HBM rows)
 constexpr int kHBins = 32;                          // write-count bins of the hand-off order
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -218,7 +220,7 @@ struct PlanHdr {
 
 constexpr int kReadFlag = 1 << 30;
 
-template <typename TIn>
+template <typename TIn, int EPW>
 __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
@@ -265,10 +267,10 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
     // ---- 0. this thread's events, e = tid + j * kPT (index t * K + k within
     //         the chunk), writes and reads alike; the loads go out first
-    int ws[kEPW], rs[kEPW];
-    float wt[kEPW], rt[kEPW], eg[kEPW];
+    int ws[EPW], rs[EPW];
+    float wt[EPW], rt[EPW], eg[EPW];
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j) {
+    for (int j = 0; j < EPW; ++j) {
         const int e = tid + j * kPT;
         ws[j] = -1;
         rs[j] = -1;
@@ -304,10 +306,10 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
         }
     };
-    int wpos[kEPW], ar[kEPW], rpos[kEPW];
-    float al[kEPW];
+    int wpos[EPW], ar[EPW], rpos[EPW];
+    float al[EPW];
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j) {
+    for (int j = 0; j < EPW; ++j) {
         wpos[j] = -1;
         rpos[j] = -1;
         ar[j] = 0;
@@ -358,15 +360,15 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
 
     // ---- 3. writes into their entries' buckets, arrival order ...
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j)
+    for (int j = 0; j < EPW; ++j)
         if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPT;
     lds_barrier();
     // ... then causal order: a write's rank is the number of the bucket's
     // writes with a smaller event index (token-major; one write per slot and
     // token)
-    int spos[kEPW];
+    int spos[EPW];
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j) {
+    for (int j = 0; j < EPW; ++j) {
         spos[j] = -1;
         if (wpos[j] >= 0) {
             const int e = tid + j * kPT;
@@ -383,9 +385,9 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     // ---- 4. each read sees version c of its slot: c = the number of the
     //         slot's writes at tokens <= its own (writes come first within a
     //         token).  Entry eid's versions are numbered ewo[eid] + eid + c.
-    int gv[kEPW];
+    int gv[EPW];
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j) {
+    for (int j = 0; j < EPW; ++j) {
         gv[j] = -1;
         if (rpos[j] >= 0) {
             const int eid = tcf[rpos[j]];
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
         *reinterpret_cast<PlanHdr *>(rec) = hd;
     }
 #pragma unroll
-    for (int j = 0; j < kEPW; ++j) {
+    for (int j = 0; j < EPW; ++j) {
         const int e = tid + j * kPT;
         if (spos[j] >= 0) {
             const int eid = tcf[wpos[j]];
@@ -709,7 +711,7 @@ struct HRow {
 // bf16 input itself (half the LDS, which buys a longer chunk, at a
 // conversion per write); the planner picks per configuration.
 // HAND: resident mode with the hand-off of the busiest slots (P.HMAX > 0).
-template <typename TIn, typename TS, int CG, bool RES, typename VT, bool HAND>
+template <typename TIn, typename TS, int CG, bool RES, typename VT, bool HAND, int EVT>
 __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
@@ -776,8 +778,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     const int vcc = static_cast<int>(static_cast<unsigned>(tid) % CG);
     const TIn *vcol = v + cg * CG + vcc;
     const uint32_t ldv32 = static_cast<uint32_t>(a.ld_v);  // the launcher checks ld_v < 2^32
-    int pf_wtv[kEVT], pf_rv[kEVT];
-    float pf_ww[kEVT], pf_wa[kEVT], pf_rr[kEVT];
+    int pf_wtv[EVT], pf_rv[EVT];
+    float pf_ww[EVT], pf_wa[EVT], pf_rr[EVT];
     TIn pf_v[VPT];  // raw: converting at load time would wait for each load
     int pf_dwo = 0, pf_dnx = 0, pf_nt = 0;  // resident: this slot's write offset, writes | x0
     int pf_nh = 0, pf_hl = 0;               // resident: slots handed off; this thread's one
@@ -795,7 +797,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         // the write list is read to its capacity, entries past its end are
         // never used
 #pragma unroll
-        for (int j = 0; j < kEVT; ++j) {
+        for (int j = 0; j < EVT; ++j) {
             const int i = tid + j * kNT;
             if (i < EV) {
                 pf_wtv[j] = wtv[i];
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
         // ---- 1. stage this chunk's plan and values
 #pragma unroll
-        for (int j = 0; j < kEVT; ++j) {
+        for (int j = 0; j < EVT; ++j) {
             const int i = tid + j * kNT;
             if (i < EV) {
                 s_wtv[i] = pf_wtv[j];
@@ -1129,11 +1131,28 @@ hipError_t set_lds(K kern, size_t lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
 }
 
+using ScanFn = void (*)(ChunkArgs);
+template <typename TIn, typename TS, int CG, typename VB, int EVT>
+ScanFn pick_scan(const ChunkPlan &P) {
+    if (P.resident)
+        return P.HMAX > 0 ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, true, EVT>
+                                          : scan_kernel<TIn, TS, CG, true, float, true, EVT>)
+                          : (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, false, EVT>
+                                          : scan_kernel<TIn, TS, CG, true, float, false, EVT>);
+    if constexpr (EVT * kNT <= kMaxEVHbm)  // HBM-mode chunks hold at most kMaxEVHbm events
+        return P.raw_values ? scan_kernel<TIn, TS, CG, false, VB, false, EVT>
+                            : scan_kernel<TIn, TS, CG, false, float, false, EVT>;
+    return nullptr;
+}
+
 template <typename TIn, typename TS, int CG>
 hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const ChunkPlan &P = a.p;
     const int64_t units = static_cast<int64_t>(a.B) * a.H;
-    auto pk = plan_kernel<TIn>;
+    const int tier = (P.EV + 1023) / 1024;  // 1..4
+    if (tier < 1 || tier > kMaxEV / 1024) return hipErrorInvalidValue;
+    auto pk = tier <= 2 ? plan_kernel<TIn, 2048 / kPT> : tier == 3 ? plan_kernel<TIn, 3072 / kPT>
+                                                                    : plan_kernel<TIn, 4096 / kPT>;
     hipError_t e = set_lds(pk, P.lds_plan);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPT), P.lds_plan, st, a);
@@ -1147,13 +1166,10 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     using VB = std::conditional_t<std::is_same_v<TIn, bf16_t>, bf16_t, float>;
-    auto sk = P.resident
-                  ? (P.HMAX > 0 ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, true>
-                                                : scan_kernel<TIn, TS, CG, true, float, true>)
-                                : (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, false>
-                                                : scan_kernel<TIn, TS, CG, true, float, false>))
-                  : (P.raw_values ? scan_kernel<TIn, TS, CG, false, VB, false>
-                                  : scan_kernel<TIn, TS, CG, false, float, false>);
+    const ScanFn sk = tier <= 2 ? pick_scan<TIn, TS, CG, VB, 2>(P)
+                      : tier == 3 ? pick_scan<TIn, TS, CG, VB, 3>(P)
+                                  : pick_scan<TIn, TS, CG, VB, 4>(P);
+    if (!sk) return hipErrorInvalidValue;
     e = set_lds(sk, P.lds_scan);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * P.ncg)), dim3(kNT), P.lds_scan, st, a);
@@ -1207,7 +1223,7 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
         if (!last && units * (d_v / CG) < 256) continue;
         for (int C = 512; C >= 32; C -= 32) {
             const int EV = C * K;
-            if (EV > kMaxEV) continue;
+            if (EV > (p.resident ? kMaxEV : kMaxEVHbm)) continue;
             ChunkPlan q = p;
             q.CG = CG;
             q.C = C;
