@@ -190,19 +190,24 @@ def test_prefill_with_oracle_addresses(rn, orc, name):
     assert np.array_equal(to_np(addr.w_idx), ref["w_idx"])
 
 
-@pytest.mark.parametrize("d_p,U,K,d_v,st_dt,T,pool", [
-    (4, 5, 16, 64, "f32", 300, 40),     # slot rows in registers; ~8 writes per slot and token-chunk
-    (4, 6, 8, 64, "bf16", 700, 300),    # 4096 slots: rows in HBM, slot-indexed plan table
-    (4, 8, 16, 64, "bf16", 300, 5000),  # 65536 slots: rows in HBM, hashed plan table
+@pytest.mark.parametrize("d_p,U,K,d_v,st_dt,T,pool,B,H", [
+    # slot rows in registers, 8-channel slices; ~8 writes per slot and
+    # token-chunk, busiest slots handed to helpers (two lanes per fp32 row)
+    (4, 5, 16, 64, "f32", 300, 40, 1, 2),
+    (4, 6, 8, 64, "bf16", 700, 300, 1, 2),    # 4096 slots: rows in HBM, slot-indexed plan table
+    (4, 8, 16, 64, "bf16", 300, 5000, 1, 2),  # 65536 slots: rows in HBM, hashed plan table
+    # 64 units: 16-channel slices, hand-off with four lanes per fp32 row
+    # (256 slots) and two lanes per bf16 row (1024 slots)
+    (4, 4, 8, 64, "f32", 300, 60, 8, 8),
+    (4, 5, 16, 64, "bf16", 300, 200, 8, 8),
 ])
-def test_chunked_given_addresses_edge_cases(rn, orc, d_p, U, K, d_v, st_dt, T, pool):
+def test_chunked_given_addresses_edge_cases(rn, orc, d_p, U, K, d_v, st_dt, T, pool, B, H):
     """Caller-given addresses through the slot-grouped path: two chunks with
     a ragged tail, slots drawn from a small pool (long per-slot write lists
     within a chunk), slots outside [0, M) and zero weights, which the ABI
     skips.  The oracle gets a skipped entry as slot 0 with weight 0, which
     changes nothing and reads nothing (project page, Gated Sparse Update:
     w = 0 gives alpha = 1 and lambda = 0)."""
-    B, H = 1, 2
     w = synth.Workload("given", B=B, T=T, H=H, d_p=d_p, U=U, K=K, d_v=d_v,
                        in_dtype="f32", state_dtype=st_dt, logit_sigma=1.0,
                        seed=21, s0_sigma=0.5, m0_uniform=(0.0, 2.0))
