@@ -108,6 +108,67 @@ __device__ __forceinline__ Ent merge_top(const Ent &a, const Ent &b, int r) {
     return bitonic_finish<KP>(c, r);
 }
 
+// Value of the lane mirrored within its block of S lanes (lane i of the
+// block sees lane S - 1 - i): quad permute, row half mirror, row mirror,
+// and for 32 lanes the row mirror of the other row.
+template <int S>
+__device__ __forceinline__ int mirror(int v) {
+    static_assert(S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "mirror");
+    if constexpr (S == 2) return lane_xor<1>(v);
+    else if constexpr (S == 4) return __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);
+    else if constexpr (S == 8) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    else if constexpr (S == 16) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+    else return lane_xor<16>(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+}
+template <int S>
+__device__ __forceinline__ Ent mirror_e(const Ent &e) {
+    Ent o;
+    const int lo = mirror<S>(__double2loint(e.w));
+    const int hi = mirror<S>(__double2hiint(e.w));
+    o.w = __hiloint2double(hi, lo);
+    o.p = mirror<S>(e.p);
+    return o;
+}
+// Two rank-ordered runs of S / 2 lanes in each block of S lanes: the first
+// half keeps the better of each mirrored pair (the top S / 2, bitonic), the
+// second half the worse.
+template <int S>
+__device__ __forceinline__ Ent mirror_stage(Ent e, int r) {
+    const Ent o = mirror_e<S>(e);
+    const bool keep_better = (r & (S / 2)) == 0;
+    return (keep_better == better(o, e)) ? o : e;
+}
+// Sorts the entries of each block of S lanes into rank order (best first):
+// runs of 2, 4, ... S lanes, each merge a mirror stage and the halving
+// stages of the bitonic finish.
+template <int KP, int S>
+__device__ __forceinline__ Ent bitonic_sort(Ent e, int r) {
+    e = mirror_stage<2>(e, r);
+    if constexpr (S >= 4) {
+        e = mirror_stage<4>(e, r);
+        e = bitonic_stage<KP, 1>(e, r);
+    }
+    if constexpr (S >= 8) {
+        e = mirror_stage<8>(e, r);
+        e = bitonic_stage<KP, 2>(e, r);
+        e = bitonic_stage<KP, 1>(e, r);
+    }
+    if constexpr (S >= 16) {
+        e = mirror_stage<16>(e, r);
+        e = bitonic_stage<KP, 4>(e, r);
+        e = bitonic_stage<KP, 2>(e, r);
+        e = bitonic_stage<KP, 1>(e, r);
+    }
+    if constexpr (S >= 32) {
+        e = mirror_stage<32>(e, r);
+        e = bitonic_stage<KP, 8>(e, r);
+        e = bitonic_stage<KP, 4>(e, r);
+        e = bitonic_stage<KP, 2>(e, r);
+        e = bitonic_stage<KP, 1>(e, r);
+    }
+    return e;
+}
+
 // Row access geometry for d_v channels of type TS: each lane moves VW bytes
 // of one row (16, or 12 where 16-byte pieces would not tile the wave), LPR
 // lanes cover a row and one instruction moves RPI = 64 / LPR rows.
@@ -273,7 +334,35 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         Ent beam;
         beam.w = r == 0 ? 1.0 : -1.0;
         beam.p = r == 0 ? 0 : -1;
+        int nb = 1;  // entries of the beam (the same in every lane)
         for (int u = 0; u < U; ++u) {
+            const int nc = nb * dp;  // candidates
+            if (nc <= KP) {
+                // every candidate has a lane of its own: lane r extends
+                // beam entry r / d_p by digit r % d_p, and one bitonic sort
+                // orders them (fewer stages than merging d_p lists)
+                const int bi = r / dp, d = r - bi * dp;
+                const int src = lane - r + (bi < nb ? bi : 0);
+                Ent c;
+                c.w = __hiloint2double(__shfl(__double2hiint(beam.w), src), __shfl(__double2loint(beam.w), src));
+                c.p = __shfl(beam.p, src);
+                const bool ok = r < nc;
+                c.w = ok ? c.w * pg[u * dp + (ok ? d : 0)] : -1.0;
+                c.p = ok ? c.p * dp + d : -1;
+                Ent res;
+                if (nc <= 2) res = bitonic_sort<KP, 2>(c, r);
+                else if (nc <= 4) res = bitonic_sort<KP, 4>(c, r);
+                else if (KP >= 8 && nc <= 8) res = bitonic_sort<KP, (KP >= 8 ? 8 : 2)>(c, r);
+                else if (KP >= 16 && nc <= 16) res = bitonic_sort<KP, (KP >= 16 ? 16 : 2)>(c, r);
+                else res = bitonic_sort<KP, KP>(c, r);
+                if (r >= K) {
+                    res.w = -1.0;
+                    res.p = -1;
+                }
+                beam = res;
+                nb = min(K, nc);
+                continue;
+            }
             double pr[8];
 #pragma unroll
             for (int d = 0; d < 8; ++d) pr[d] = d < dp ? pg[u * dp + d] : 0.0;
@@ -295,6 +384,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                 res.p = -1;
             }
             beam = res;
+            nb = min(K, nc);
         }
         // CAPE and hand-off
         const int b = unit / a.H;
