@@ -21,6 +21,9 @@
 //     before the chunk (version 0) or after the chunk's i-th write to the
 //     slot (version i).  Only versions that some read sees get a row in the
 //     scan's version buffer.
+//   * Where a chunk writes each slot at least twice on average, the slots
+//     with more than n0 writes are listed busiest first for the scan's
+//     helpers (hand-off below), as many as the version rows left free hold.
 // scan_kernel: one workgroup per (unit, slice of CG channels), chunk after
 // chunk.
 //   * The plan and the slice's values are staged in LDS (loaded one chunk
@@ -31,9 +34,14 @@
 //     its row slice and mass in registers for the whole sequence; for larger
 //     M the touched rows are gathered from HBM and written back, and each
 //     slice keeps its own copy of the mass.
-//   * One thread per (token, 16-byte piece of the slice) sums rho * version
-//     over the token's K reads in address order; r and the slice's sum of
-//     squares go to global memory.
+//   * Hand-off (rows on chip): a listed slot's owner applies its first n0
+//     writes and parks the row in a free version row; a helper, one lane per
+//     16-byte piece of the row, applies the rest; the owner takes it back.
+//     A wave then no longer waits for its busiest slot's whole chain.
+//   * The reads: lanes of a token sum rho * version over its K reads in
+//     address order, one 16-byte piece of every row each where a row slice
+//     has several, else splitting the reads and combining them by a fixed
+//     butterfly; r and the slice's sum of squares go to global memory.
 // rms_gate_kernel: sums the slices' squares per token, applies RMSNorm and
 // the gate, and copies the final mass.
 #include "device_common.h"
