@@ -13,7 +13,10 @@
 //    the first K entries of the merge of the d_p lists, built by a tree of
 //    bitonic merges: list B reversed against list A, the better of each
 //    pair, then log2(KP) compare-exchange stages.  This replaces K serial
-//    merge steps per level by log2(KP) parallel ones.  The decision is taken
+//    merge steps per level by log2(KP) parallel ones.  At the first levels,
+//    where every candidate can have a lane of its own (beam entries x d_p
+//    <= KP), one bitonic sort of the candidates gives the same beam in
+//    fewer stages.  The decision is taken
 //    in fp64 (softmax summed in digit order, as the reference definition
 //    writes it).  The digit distributions of all levels are computed first,
 //    one (address, level, digit) per lane, and kept in LDS.
