@@ -7,12 +7,22 @@ B x T x H token-heads); for the decode workload, one ramnet_step_decode call
 (one token for each of B sequences, all heads).  Inputs are resident in HBM
 before the timed region.  Prints one JSON line.
 
+Default: the headline is the largest single-GPU workload, the 4^8-slot
+prefill (large_state: B 2, T 32768, H 16, K 32); the line carries the other
+workloads as sub-records ("subrecords"), each the whole call with its own
+roofline and CPU baseline: the Top-8 and Top-32 prefills (--steps calls
+each) and the decode workload (1024 dependent steps in one HIP graph).
+Device peaks are measured first (a 256 MiB copy, an LDS read probe) and
+every roofline fraction is given against both the vendor's figure and the
+measured one.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload prefill_top8|prefill_top32|large_state|decode
                                    |layer_top8|layer_decode|backward_top8
                                    |backward_top32]
-The layer_* workloads add the dense projections either side (the whole layer);
-backward_top8 / backward_top32 time the gradients of those prefills.
+--workload runs that workload alone (no sub-records).  The layer_* workloads
+add the dense projections either side (the whole layer); backward_top8 /
+backward_top32 time the gradients of those prefills.
 """
 from __future__ import annotations
 
@@ -29,9 +39,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("tokens/sec per RAM-Net layer (prefill scan + decode step), "
           "% of HBM roofline")
-HBM_PEAK_GBS = 8000.0
-# LDS: 128 bytes per clock per compute unit, 256 units at 2.4 GHz.
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+# LDS has no vendor figure in bytes per second; this one is derived from
+# 128 bytes per clock per compute unit, 256 units at 2.4 GHz.  The measured
+# read bandwidth (probe below) is reported beside it.
 LDS_PEAK_GBS = 128 * 256 * 2.4
+HEADLINE = "large_state"
+SUBRECORDS = ("prefill_top8", "prefill_top32", "decode")
 
 
 
@@ -135,60 +149,121 @@ def cpu_info():
     return model
 
 
-def cpu_baseline(w, kind: str, budget_s: float = 12.0):
-    """Times the CPU oracle (as it is: brute-force Top-K, fp64, OpenMP over
-    (batch, head) units) on a bounded sample of the same workload: a prefix
-    of the sequences sized to about `budget_s` seconds, or the whole batch
-    when that is cheaper; reports tokens/s."""
+def cpu_baseline(w, kind: str, run_s: float = 2.5):
+    """Times the CPU oracle as it stands (plain C, fp64, prefix-tree Top-K,
+    OpenMP over the independent (batch, head) units) on a bounded sample of
+    the same workload: a prefix of the sequences (prefill) or of the steps
+    (decode) sized to about `run_s` seconds per run; one warm-up run, then
+    the median of three.  Reports tokens/s."""
     import oracle
     from sparse_slot_recurrent_amd import synth
     oracle.load()
     threads = oracle.max_threads()
     sb = w.state_dtype == "bf16"
+    tree = oracle.TOPK_TREE
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
     if kind == "decode":
-        steps = 0
-        S = m = pos = None
-        t_all = 0.0
         x0 = synth.make_inputs(w, T=1)
-        S, m, pos = x0["S0"].copy(), x0["m0"].copy(), x0["pos0"].copy()
-        while t_all < budget_s and steps < w.steps:
-            s = synth.make_decode_step(w, steps)
-            a = {n: s[n][:, None] for n in s}
-            t0 = time.perf_counter()
-            oracle.layer(a["q"], a["k"], a["v"], a["gamma"], a["g"], S, m,
-                         d_p=w.d_p, U=w.U, K=w.K, state_bf16=sb, pos0=pos,
-                         want_addresses=False)
-            t_all += time.perf_counter() - t0
-            pos = pos + 1
-            steps += 1
-        return {"value": w.B * steps / t_all, "unit": "tokens/s",
-                "cores": threads, "kind": "oracle",
-                "sample": f"{steps} decode steps of all {w.B} sequences x "
-                          f"{w.H} heads, {t_all:.1f} s of oracle time",
+        steps_in = []
+
+        def run(n):
+            S, m, pos = x0["S0"].copy(), x0["m0"].copy(), x0["pos0"].copy()
+            while len(steps_in) < n:
+                s = synth.make_decode_step(w, len(steps_in))
+                steps_in.append({k: np.ascontiguousarray(s[k][:, None]) for k in s})
+            t = 0.0
+            for i in range(n):
+                a = steps_in[i]
+                t += timed(lambda: oracle.layer(a["q"], a["k"], a["v"], a["gamma"], a["g"],
+                                                S, m, d_p=w.d_p, U=w.U, K=w.K,
+                                                state_bf16=sb, pos0=pos + i, mode=tree,
+                                                want_addresses=False))
+            return t
+        n = max(1, min(w.steps, int(run_s / max(run(1), 1e-4))))
+        run(n)  # warm-up
+        med = float(np.median([run(n) for _ in range(3)]))
+        return {"value": w.B * n / med, "unit": "tokens/s",
+                "cores": min(threads, w.B * w.H), "kind": "oracle",
+                "sample": f"{n} of {w.steps} decode steps, all {w.B} sequences x {w.H} "
+                          f"heads (prefix-tree Top-K, fp64); median of 3 runs of "
+                          f"{med:.2f} s after a warm-up",
                 "cpu": cpu_info()}
     H = w.H
     B = max(1, min(w.B, threads // H))
     T = min(w.T, 64)
+
+    def run(x):
+        S, m = x["S0"].copy(), x["m0"].copy()
+        return timed(lambda: oracle.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S, m,
+                                          d_p=w.d_p, U=w.U, K=w.K, state_bf16=sb,
+                                          pos0=x["pos0"], mode=tree, want_addresses=False))
     while True:
         x = synth.make_inputs(w, B=B, T=T, H=H)
-        S, m = x["S0"].copy(), x["m0"].copy()
-        t0 = time.perf_counter()
-        oracle.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S, m,
-                     d_p=w.d_p, U=w.U, K=w.K, state_bf16=sb, pos0=x["pos0"],
-                     want_addresses=False)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s / 4 or (T == w.T and B == w.B):
+        dt = run(x)
+        if dt >= run_s / 2 or (T == w.T and B == w.B):
             break
-        grow = max(2.0, min(8.0, budget_s / 2 / max(dt, 1e-3)))
+        grow = max(1.2, min(8.0, run_s / max(dt, 1e-3)))
         if T < w.T:
-            T = min(w.T, int(T * grow))
+            T = min(w.T, int(T * grow) + 1)
         else:
             B = min(w.B, int(B * grow) + 1)
-    return {"value": B * T / dt, "unit": "tokens/s",
+    x = synth.make_inputs(w, B=B, T=T, H=H)
+    run(x)  # warm-up
+    med = float(np.median([run(x) for _ in range(3)]))
+    return {"value": B * T / med, "unit": "tokens/s",
             "cores": min(threads, B * H), "kind": "oracle",
-            "sample": f"B={B} x T={T} tokens x {H} heads of the workload "
-                      f"(brute-force Top-K, fp64), {dt:.1f} s",
+            "sample": f"B={B} x T={T} tokens x {H} heads of the workload (prefix-tree "
+                      f"Top-K, fp64); median of 3 runs of {med:.2f} s after a warm-up",
             "cpu": cpu_info()}
+
+
+def measure_peaks(torch):
+    """Measured device peaks: HBM bandwidth of a 256 MiB device copy (bytes
+    read plus bytes written per second) and LDS read bandwidth (ds_read_b128
+    on every compute unit), each the best of 10 launches after 3 warm-ups,
+    timed with HIP events on the launch stream."""
+    import ctypes as C
+    path = os.path.join(ROOT, "sparse_slot_recurrent_amd", "libramnet_probe.so")
+    lib = C.CDLL(path)
+    lib.probe_hbm_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_void_p]
+    lib.probe_lds_read.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    st = torch.cuda.current_stream()
+    sp = C.c_void_p(st.cuda_stream)
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    blocks = 256 * 8
+
+    def best(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return min(ts)
+    t_copy = best(lambda: lib.probe_hbm_copy(C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()),
+                                             nbytes // 16, blocks, sp))
+    assert torch.equal(src, dst), "copy probe"
+    del src, dst
+    iters = 256
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    t_lds = best(lambda: lib.probe_lds_read(blocks, iters, C.c_void_p(out.data_ptr()), sp))
+    lds_bytes = blocks * 256 * iters * 16 * 16
+    return {"hbm_copy_gbs": 2 * nbytes / t_copy / 1e9, "lds_read_gbs": lds_bytes / t_lds / 1e9,
+            "hbm_vendor_gbs": HBM_PEAK_GBS, "lds_derived_gbs": LDS_PEAK_GBS,
+            "method": "256 MiB copy (read + write bytes) and ds_read_b128 on 2048 "
+                      "workgroups; best of 10 after 3 warm-ups"}
 
 
 def to_dev(torch, a, dtype):
@@ -472,13 +547,79 @@ def bench_layer(torch, rn, w, D, steps, warmup):
     return ms, kms, w.B * T, {}
 
 
+def prefill_roofline(w, kind, kms, bm, peaks):
+    """Roofline of the dominant stage: algorithmic bytes over its measured
+    time, against the HBM or the LDS peak, whichever term takes longer at
+    peak (LDS only for a state held on chip, in the scan stage); the
+    fraction against the vendor's (or derived) peak and against the
+    measured one."""
+    dom = max(kms, key=kms.get)
+    sec = kms[dom] / 1e3
+    lds = bm["lds_state"] if dom == "scan_stage" else 0
+    if lds / LDS_PEAK_GBS > bm.get(dom, 0) / HBM_PEAK_GBS:
+        a = lds / sec / 1e9
+        return {"bound": "lds", "kernel": dom, "achieved": a, "peak": LDS_PEAK_GBS,
+                "unit": "GB/s", "frac": a / LDS_PEAK_GBS,
+                "peak_measured": peaks.get("lds_read_gbs"),
+                "frac_measured": a / peaks["lds_read_gbs"] if peaks.get("lds_read_gbs") else None,
+                "hbm_frac": bm[dom] / sec / 1e9 / HBM_PEAK_GBS,
+                "traffic": measured_traffic(w.name, dom)}
+    a = bm[dom] / sec / 1e9
+    return {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a / HBM_PEAK_GBS, "peak_measured": peaks.get("hbm_copy_gbs"),
+            "frac_measured": a / peaks["hbm_copy_gbs"] if peaks.get("hbm_copy_gbs") else None,
+            "traffic": measured_traffic(w.name, dom)}
+
+
+def workload_config(name, w, kind):
+    return {"workload": name, "B": w.B, "T": 1 if kind == "decode" else w.T, "H": w.H,
+            "M": w.M, "d_p": w.d_p, "U": w.U, "K": w.K, "d_v": w.d_v,
+            "in_dtype": w.in_dtype, "state_dtype": w.state_dtype, "cape": w.cape,
+            "steps": w.steps if kind == "decode" else None, "parallelism": "single GPU"}
+
+
+def measure_workload(torch, rn, name, steps, warmup, peaks, cpu: bool):
+    """One workload's record: tokens/s of the whole call, per-stage times,
+    the roofline of the dominant stage and the CPU oracle beside it."""
+    from sparse_slot_recurrent_amd import synth
+    w = synth.WORKLOADS[name]
+    kind = "decode" if w.steps else "prefill"
+    extra = {}
+    if kind == "decode":
+        # the 1024 dependent steps of the workload, replayed as one graph
+        steps = w.steps
+        ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)
+    else:
+        ms, kms, tokens = bench_prefill(torch, rn, w, steps, warmup)
+    bm = byte_model(w, kind)
+    if kind == "decode":
+        a = bm["step_fused"] / (kms["step_fused"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "step_fused", "achieved": a, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": a / HBM_PEAK_GBS,
+                "peak_measured": peaks.get("hbm_copy_gbs"),
+                "frac_measured": a / peaks["hbm_copy_gbs"] if peaks.get("hbm_copy_gbs") else None,
+                "traffic": measured_traffic(w.name, "step_fused")}
+    else:
+        roof = prefill_roofline(w, kind, kms, bm, peaks)
+    rec = {"workload": name, "value": tokens / (ms / 1e3), "unit": "tokens/s",
+           "ms_per_step": ms, "steps": steps, "config": workload_config(name, w, kind),
+           "roofline": roof, "kernels_ms": kms, "algorithmic_bytes": bm,
+           "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    rec.update(extra)
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, kind)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="prefill_top8")
+    ap.add_argument("--workload", default=None,
+                    help="run one workload alone (default: the headline with sub-records)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-subrecords", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device to device once (a plain copy "
                          "kernel of known size, to scale hardware byte counters)")
@@ -495,18 +636,6 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    d_model = None
-    backward = args.workload in BACKWARD
-    if backward:
-        w = synth.WORKLOADS[BACKWARD[args.workload]]
-    elif args.workload in LAYERS:
-        base, d_model = LAYERS[args.workload]
-        w = synth.WORKLOADS[base]
-    else:
-        w = synth.WORKLOADS[args.workload]
-    kind = "decode" if w.steps else "prefill"
-    steps = args.steps or (w.steps if kind == "decode" else 10)
-    warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
     torch.cuda.set_device(0)
     torch.cuda.synchronize()
     if args.copy_probe:
@@ -516,95 +645,93 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    extra = {}
+    name = args.workload or HEADLINE
+    single = args.workload is not None
+    cpu = not args.no_cpu_baseline
+    d_model = None
+    if name in LAYERS:
+        # time hipBLASLt's candidates once per GEMM shape, before the timed
+        # region (the library's opt-in tuning)
+        os.environ["RAMNET_GEMM_TUNE"] = "1"
+    backward = name in BACKWARD
     if backward:
-        ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
-    elif d_model is not None:
-        ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
-    elif kind == "decode":
-        ms, kms, tokens, extra = bench_decode(torch, rn, w, steps, warmup)
+        w = synth.WORKLOADS[BACKWARD[name]]
+    elif name in LAYERS:
+        base, d_model = LAYERS[name]
+        w = synth.WORKLOADS[base]
     else:
-        ms, kms, tokens = bench_prefill(torch, rn, w, steps, warmup)
-    value = tokens / (ms / 1e3)
-    bm = byte_model(w, kind)
-    dom = max(kms, key=kms.get)
-    roof = None
-    if backward:
-        bw = backward_model(w)
-        extra["backward_model"] = bw
-        a = bw["backward"] / (ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": "backward", "achieved": a, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
-                "with_records_gbs": (bw["backward"] + bw["records"]) / (ms / 1e3) / 1e9}
-    elif d_model is not None:
-        lm = layer_model(w, d_model, kind)
-        extra["layer_model"] = lm
-        extra["d_model"] = d_model
-        if "projections" in kms:
-            flop = lm["project_inputs_flop"] + lm["project_output_flop"]
-            tf = flop / (kms["projections"] / 1e3) / 1e12
-            extra["projections_tflops"] = tf
-            rec = bm["total"] / (kms["recurrence"] / 1e3) / 1e9
-            extra["recurrence_gbs"] = rec
-            if dom == "projections":
-                roof = {"bound": "mfma", "kernel": dom, "achieved": tf,
-                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
-            elif dom == "recurrence":
-                roof = {"bound": "hbm", "kernel": dom, "achieved": rec,
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": rec / HBM_PEAK_GBS, "traffic": None}
-        if roof is None:
-            # one graph-replayed step: the whole layer's bytes (recurrence
-            # plus both projections) over the step time
-            by = bm["total"] + lm["project_inputs_bytes"] + lm["project_output_bytes"]
-            a = by / (ms / 1e3) / 1e9
-            roof = {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None}
-    else:
-        # the bound is whichever of the HBM and LDS terms takes longer at
-        # peak (LDS only for a state held on chip, in the scan stage)
-        sec = kms[dom] / 1e3
-        lds = bm["lds_state"] if dom == "scan_stage" else 0
-        if lds / LDS_PEAK_GBS > bm[dom] / HBM_PEAK_GBS:
-            achieved = lds / sec / 1e9
-            roof = {"bound": "lds", "kernel": dom, "achieved": achieved,
-                    "peak": LDS_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / LDS_PEAK_GBS, "hbm_frac": bm[dom] / sec / 1e9 / HBM_PEAK_GBS,
-                    "traffic": measured_traffic(w.name, dom)}
+        w = synth.WORKLOADS[name]
+    kind = "decode" if w.steps else "prefill"
+    steps = args.steps or (w.steps if kind == "decode" else 10)
+    warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
+    peaks = {} if single else measure_peaks(torch)
+    line = {"metric": METRIC}
+    if backward or d_model is not None:
+        extra = {}
+        if backward:
+            ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
+            bw = backward_model(w)
+            extra["backward_model"] = bw
+            a = bw["backward"] / (ms / 1e3) / 1e9
+            roof = {"bound": "hbm", "kernel": "backward", "achieved": a, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
+                    "with_records_gbs": (bw["backward"] + bw["records"]) / (ms / 1e3) / 1e9}
         else:
-            achieved = bm[dom] / sec / 1e9
-            roof = {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": measured_traffic(w.name, dom)}
-    line = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16+f32" if d_model else "f32",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "B": w.B, "T": 1 if kind == "decode" else w.T,
-                   "H": w.H, "M": w.M, "d_p": w.d_p, "U": w.U, "K": w.K,
-                   "d_v": w.d_v, "in_dtype": w.in_dtype,
-                   "state_dtype": w.state_dtype, "cape": w.cape,
-                   "parallelism": "single GPU"},
-        "roofline": roof,
-        "kernels_ms": kms,
-        "algorithmic_bytes": bm,
-        "whole_step_hbm_frac": bm["total"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-    }
-    line.update(extra)
-    if not args.no_cpu_baseline and d_model is None and not backward:
-        line["cpu_baseline"] = cpu_baseline(w, kind)
+            ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
+            roof = layer_roofline(w, d_model, kind, kms, ms, extra)
+        rec = {"workload": name, "value": tokens / (ms / 1e3), "unit": "tokens/s",
+               "ms_per_step": ms, "config": workload_config(name, w, kind), "roofline": roof,
+               "kernels_ms": kms}
+        rec.update(extra)
+    else:
+        rec = measure_workload(torch, rn, name, steps, warmup, peaks, cpu)
+        steps = rec["steps"]
+    line.update({
+        "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        # arithmetic: fp32 (Top-K decisions in fp64); storage in "config"
+        "dtype": "f32", "data": "synthetic",
+    })
+    for k in ("config", "roofline", "cpu_baseline", "kernels_ms", "algorithmic_bytes",
+              "whole_step_hbm_frac"):
+        if k in rec:
+            line[k] = rec[k]
+    for k, v in rec.items():
+        if k not in line and k not in ("workload", "steps"):
+            line[k] = v
+    if peaks:
+        line["device_peaks"] = peaks
+    if not single and not args.no_subrecords:
+        line["subrecords"] = [measure_workload(torch, rn, n, steps if n != "decode" else None,
+                                               warmup, peaks, cpu) for n in SUBRECORDS]
     print(json.dumps(line), flush=True)
+
+
+def layer_roofline(w, d_model, kind, kms, ms, extra):
+    """Roofline of a whole-layer workload: the projections against the bf16
+    matrix-core peak, or the recurrence against HBM, whichever stage is
+    longer; a graph-replayed step against HBM for its whole bytes."""
+    bm = byte_model(w, kind)
+    lm = layer_model(w, d_model, kind)
+    extra["layer_model"] = lm
+    extra["d_model"] = d_model
+    dom = max(kms, key=kms.get)
+    if "projections" in kms:
+        flop = lm["project_inputs_flop"] + lm["project_output_flop"]
+        tf = flop / (kms["projections"] / 1e3) / 1e12
+        extra["projections_tflops"] = tf
+        rec = bm["total"] / (kms["recurrence"] / 1e3) / 1e9
+        extra["recurrence_gbs"] = rec
+        if dom == "projections":
+            return {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        return {"bound": "hbm", "kernel": dom, "achieved": rec, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": rec / HBM_PEAK_GBS, "traffic": None}
+    by = bm["total"] + lm["project_inputs_bytes"] + lm["project_output_bytes"]
+    a = by / (ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": dom, "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a / HBM_PEAK_GBS, "traffic": None}
 
 
 if __name__ == "__main__":

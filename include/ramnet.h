@@ -244,6 +244,15 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q,
  * (hipBLASLt on the matrix cores); the layer output is rounded to bf16
  * before w_o.  p->in_dtype must be RAMNET_BF16 (q, k, v, gamma, g are the
  * bf16 projections).
+ * GEMM algorithms: by default hipBLASLt's first heuristic choice, so these
+ * calls stay asynchronous and give the same bits in every process.  With
+ * RAMNET_GEMM_TUNE=1 in the environment, the first call of each GEMM shape
+ * in a process (outside graph capture) instead times up to 24 candidates on
+ * its own operands and keeps the fastest: that call SYNCHRONISES THE HOST
+ * with the stream, its bits can differ from another process's (a different
+ * algorithm sums in another order), and a timing failure of the output GEMM
+ * is reported after the recurrence has already been enqueued (S and mass
+ * then hold the updated state).
  */
 typedef struct {
     int32_t d_model;

@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libramnet.so")
+# Device peak probes for the benchmark (HBM copy, LDS read), a library of
+# their own: they are measurement tools, not part of the C ABI.
+PROBE_SRC = "probe.hip"
+PROBE_LIB = os.path.join(PKG, "libramnet_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "step_fused.hip",
@@ -54,8 +58,13 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SRC]))
+    probe_obj = objs.pop()
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                   check=True)
+    os.replace(tmp, PROBE_LIB)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LIBS]
     if verbose:

@@ -14,11 +14,13 @@
 //                   tensors (for ramnet_project_inputs).
 //   gemm_bf16       row-major C[m,n] = A[m,k] W[n,k]^T, bf16 operands, fp32
 //                   accumulation, C rounded to bf16: hipBLASLt on the matrix
-//                   cores, one handle per device.  The first call of a shape
-//                   outside graph capture times hipBLASLt's candidate
-//                   algorithms on the call's own operands and keeps the
-//                   fastest for the process (RAMNET_GEMM_TUNE=0: take the
-//                   library's first choice).
+//                   cores, one handle per device, with the library's first
+//                   heuristic choice of algorithm (the same in every
+//                   process).  Opt-in (RAMNET_GEMM_TUNE=1 in the
+//                   environment): the first call of a shape outside graph
+//                   capture times hipBLASLt's candidates on the call's own
+//                   operands, synchronising the host, and keeps the fastest
+//                   for the process.
 //   to_bf16_kernel  fp32 layer output -> bf16, when the scan could not write
 //                   bf16 itself.
 #include <hipblaslt/hipblaslt.h>
@@ -153,9 +155,11 @@ struct GemmPlan {
 
 constexpr int kCandidates = 24;
 
+// Timing hipBLASLt's candidates is opt-in: it blocks the host, and the pick
+// (hence the rounding of the sums) can differ between processes.
 bool tuning_enabled() {
     const char *e = getenv("RAMNET_GEMM_TUNE");
-    return !(e && e[0] == '0');
+    return e && e[0] == '1';
 }
 
 std::mutex g_mu;

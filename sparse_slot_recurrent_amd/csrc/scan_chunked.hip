@@ -1101,9 +1101,11 @@ struct alignas(4 * sizeof(T)) Quad {
 
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g), four channels per
 // thread; the per-token square sums of the channel slices are added in
-// slice order.
+// slice order.  With an fp32 output, r is held in `out` itself (rbuf ==
+// out): each thread reads its own four values before it writes them, and
+// neither pointer is declared restrict.
 template <typename TIn, typename TO>
-__global__ __launch_bounds__(256) void rms_gate_kernel(const float *__restrict__ rbuf,
+__global__ __launch_bounds__(256) void rms_gate_kernel(const float *rbuf,
                                                        const float *__restrict__ sumsq, int ncg,
                                                        const TIn *__restrict__ g, int H,
                                                        int64_t ld_g,

@@ -163,11 +163,93 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr())
 
 
-def _addr_struct(a: Optional[Addresses]):
+def _torch_dtype(code):
+    torch = _torch()
+    return torch.bfloat16 if code == BF16 else torch.float32
+
+
+def _arg(t, name, shape, dtype, required=True):
+    """Device pointer of `t` after checking that it is a contiguous tensor
+    on the current GPU with the given shape and dtype (the C ABI derives
+    every extent from the parameters alone, so a mismatch here would become
+    an out-of-bounds access there)."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU, not {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current GPU "
+                         f"(cuda:{torch.cuda.current_device()})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _addr_struct(a: Optional[Addresses], shape=None, name="addresses"):
+    """Addresses as the C struct: int32 slots and fp32 weights, each of
+    `shape` ([B,T,H,K], or [B,H,K] for a step)."""
     if a is None:
         return None
-    return Addr(a.w_idx.data_ptr(), a.w_wt.data_ptr(), a.r_idx.data_ptr(),
-                a.r_wt.data_ptr())
+    torch = _torch()
+    ps = []
+    for f, dt in (("w_idx", torch.int32), ("w_wt", torch.float32),
+                  ("r_idx", torch.int32), ("r_wt", torch.float32)):
+        t = getattr(a, f)
+        ps.append(_arg(t, f"{name}.{f}", t.shape if shape is None else shape, dt).value)
+    return Addr(*ps)
+
+
+class _Shapes:
+    """The tensor shapes and dtypes a call with parameters p expects."""
+
+    def __init__(self, p: Params):
+        self.p = p
+        B, T, H = p.B, p.T, p.H
+        self.L = p.U * p.d_p
+        self.ind = _torch_dtype(p.in_dtype)
+        self.std = _torch_dtype(p.state_dtype)
+        self.tok = (B, T, H) if T != 0 else (B, 0, H)
+
+    def prefill(self, q, k, v, gamma, g, S, mass, out, norm_w, pos0, need_qk=True):
+        """Pointers of a prefill call's tensors, checked against p."""
+        torch = _torch()
+        p, tok = self.p, self.tok
+        f32 = torch.float32
+        return (_arg(q, "q", tok + (self.L,), self.ind, need_qk),
+                _arg(k, "k", tok + (self.L,), self.ind, need_qk),
+                _arg(v, "v", tok + (p.d_v,), self.ind),
+                _arg(gamma, "gamma", tok, self.ind),
+                _arg(g, "g", tok + (p.d_v,), self.ind),
+                _arg(norm_w, "norm_w", (p.d_v,), f32, False),
+                _arg(pos0, "pos0", (p.B,), torch.int32, False),
+                _arg(S, "S", (p.B, p.H, p.M, p.d_v), self.std),
+                _arg(mass, "mass", (p.B, p.H, p.M), f32),
+                _arg(out, "out", tok + (p.d_v,), self.std))
+
+    def step(self, q, k, v, gamma, g, pos, S, mass, out, norm_w):
+        torch = _torch()
+        p = self.p
+        u = (p.B, p.H)
+        f32 = torch.float32
+        return (_arg(q, "q", u + (self.L,), self.ind),
+                _arg(k, "k", u + (self.L,), self.ind),
+                _arg(v, "v", u + (p.d_v,), self.ind),
+                _arg(gamma, "gamma", u, self.ind),
+                _arg(g, "g", u + (p.d_v,), self.ind),
+                _arg(norm_w, "norm_w", (p.d_v,), f32, False),
+                _arg(pos, "pos", (p.B,), torch.int32, p.cape != 0),
+                _arg(S, "S", (p.B, p.H, p.M, p.d_v), self.std),
+                _arg(mass, "mass", (p.B, p.H, p.M), f32),
+                _arg(out, "out", u + (p.d_v,), self.std))
 
 
 def _stream():
@@ -187,15 +269,20 @@ def decode_addresses(q, k, *, d_p: int, U: int, K: int, cape: int = 1,
                      content_heads: int = 0) -> Addresses:
     """q, k [B,T,H,U*d_p] -> Addresses, each [B,T,H,K] (post-CAPE slots),
     written into `out` when given."""
+    if q.dim() != 4 or q.shape[-1] != U * d_p:
+        raise ValueError(f"q must be [B,T,H,U*d_p] with U*d_p = {U * d_p}, got {tuple(q.shape)}")
     B, T, H, L = q.shape
-    assert L == U * d_p and k.shape == q.shape
     p = make_params(B, T, H, d_p, U, K, 64, in_dtype=_dt(q), cape=cape,
                     content_heads=content_heads)
     if out is None:
         out = new_addresses((B, T, H, K), q.device)
-    a = _addr_struct(out)
+    a = _addr_struct(out, (B, T, H, K), "out")
+    torch = _torch()
+    pq = _arg(q, "q", (B, T, H, L), q.dtype)
+    pk = _arg(k, "k", (B, T, H, L), q.dtype)
+    pp = _arg(pos0, "pos0", (B,), torch.int32, False)
     _raise(load_library().ramnet_decode_addresses(
-        C.byref(p), _ptr(q), _ptr(k), _ptr(pos0), C.byref(a), _stream()))
+        C.byref(p), pq, pk, pp, C.byref(a), _stream()))
     return out
 
 
@@ -216,11 +303,14 @@ class PrefillPlan:
     def __call__(self, q, k, v, gamma, g, S, mass, out, *, norm_w=None,
                  pos0=None, addr_in: Optional[Addresses] = None,
                  addr_out: Optional[Addresses] = None):
-        ai = _addr_struct(addr_in)
-        ao = _addr_struct(addr_out)
+        p = self.p
+        shp = (p.B, p.T, p.H, p.K)
+        ai = _addr_struct(addr_in, shp, "addr_in")
+        ao = _addr_struct(addr_out, shp, "addr_out")
+        ptrs = _Shapes(p).prefill(q, k, v, gamma, g, S, mass, out, norm_w, pos0,
+                                  need_qk=addr_in is None)
         _raise(load_library().ramnet_scan_prefill(
-            C.byref(self.p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g),
-            _ptr(norm_w), _ptr(pos0), _ptr(S), _ptr(mass), _ptr(out),
+            C.byref(p), *ptrs[:5], ptrs[5], ptrs[6], ptrs[7], ptrs[8], ptrs[9],
             C.byref(ai) if ai is not None else None,
             C.byref(ao) if ao is not None else None,
             C.c_void_p(self.workspace.data_ptr()), self.ws_bytes, _stream()))
@@ -260,10 +350,11 @@ class StepPlan:
 
     def __call__(self, q, k, v, gamma, g, pos, S, mass, out, *, norm_w=None,
                  addr_out: Optional[Addresses] = None):
-        ao = _addr_struct(addr_out)
+        p = self.p
+        ao = _addr_struct(addr_out, (p.B, p.H, p.K), "addr_out")
+        ptrs = _Shapes(p).step(q, k, v, gamma, g, pos, S, mass, out, norm_w)
         _raise(load_library().ramnet_step_decode(
-            C.byref(self.p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g),
-            _ptr(norm_w), _ptr(pos), _ptr(S), _ptr(mass), _ptr(out),
+            C.byref(p), *ptrs,
             C.byref(ao) if ao is not None else None,
             C.c_void_p(self.workspace.data_ptr()), self.ws_bytes, _stream()))
         return out
@@ -352,12 +443,19 @@ class LayerPlan:
                  pos=None, addr_out: Optional[Addresses] = None):
         """x, y [B,T,D] (a step: [B,D]) bf16; pos = pos0 [B] for prefill,
         the token positions [B] for a step."""
+        torch = _torch()
+        p = self.p
         ws = _proj_struct(w)
-        ao = _addr_struct(addr_out)
+        xs = (p.B, self.d_model) if self.step else (p.B, p.T, self.d_model)
+        ao = _addr_struct(addr_out, xs[:-1] + (p.H, p.K), "addr_out")
+        f32, bf = torch.float32, torch.bfloat16
+        ptrs = (_arg(x, "x", xs, bf), _arg(norm_w, "norm_w", (p.d_v,), f32, False),
+                _arg(pos, "pos", (p.B,), torch.int32, self.step and p.cape != 0),
+                _arg(S, "S", (p.B, p.H, p.M, p.d_v), _torch_dtype(p.state_dtype)),
+                _arg(mass, "mass", (p.B, p.H, p.M), f32), _arg(y, "y", xs, bf))
         f = (load_library().ramnet_layer_step if self.step
              else load_library().ramnet_layer_forward)
-        _raise(f(C.byref(self.p), C.byref(ws), _ptr(x), _ptr(norm_w),
-                 _ptr(pos), _ptr(S), _ptr(mass), _ptr(y),
+        _raise(f(C.byref(p), C.byref(ws), *ptrs,
                  C.byref(ao) if ao is not None else None,
                  C.c_void_p(self.workspace.data_ptr()), self.ws_bytes,
                  _stream()))
@@ -422,11 +520,21 @@ def scan_backward(q, k, v, gamma, g, S0, mass0, addr: Addresses, dout, *,
            "dv": f32(B, T, H, d_v), "dgamma": f32(B, T, H), "dg": f32(B, T, H, d_v),
            "dnorm_w": f32(d_v), "dS0": torch.empty(S0.shape, dtype=torch.float32, device=v.device),
            "dmass0": torch.empty_like(mass0)}
-    a = _addr_struct(addr)
+    a = _addr_struct(addr, (B, T, H, K), "addr")
+    sh = _Shapes(p)
+    f32 = torch.float32
+    tok = (B, T, H)
+    ptr_in = (_arg(q, "q", tok + (L,), sh.ind, want_logits),
+              _arg(k, "k", tok + (L,), sh.ind, want_logits),
+              _arg(v, "v", tok + (d_v,), sh.ind), _arg(gamma, "gamma", tok, sh.ind),
+              _arg(g, "g", tok + (d_v,), sh.ind), _arg(norm_w, "norm_w", (d_v,), f32, False),
+              _arg(pos0, "pos0", (B,), torch.int32, False),
+              _arg(S0, "S0", (B, H, p.M, d_v), sh.std), _arg(mass0, "mass0", (B, H, p.M), f32))
+    ptr_d = (_arg(dout, "dout", tok + (d_v,), f32),
+             _arg(dS_final, "dS_final", (B, H, p.M, d_v), f32, False),
+             _arg(dmass_final, "dmass_final", (B, H, p.M), f32, False))
     _raise(load_library().ramnet_scan_backward(
-        C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(g), _ptr(norm_w),
-        _ptr(pos0), _ptr(S0), _ptr(mass0), C.byref(a), _ptr(dout), _ptr(dS_final),
-        _ptr(dmass_final), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        C.byref(p), *ptr_in, C.byref(a), *ptr_d, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
         _ptr(out["dgamma"]), _ptr(out["dg"]), _ptr(out["dnorm_w"]), _ptr(out["dS0"]),
         _ptr(out["dmass0"]), C.c_void_p(ws.data_ptr()), nbytes, _stream()))
     return out

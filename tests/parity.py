@@ -5,9 +5,13 @@ and (K+1)-th weight exceeds 1e-6, the GPU's slot set must equal the oracle's
 and matched weights agree within 1e-5 relative.  Where the margin is smaller,
 more than one set is correct: the GPU's set must hold every slot clearly
 heavier than the K-th weight and only slots within 1e-6 of it or heavier.
-A (batch, head) unit whose GPU set legitimately differs from the oracle's
-follows a different (equally valid) trajectory from that token on, so state
-and outputs are compared only before it.
+Where the GPU's set legitimately differs (a near-tie), the oracle's
+recurrence adopts the GPU's set: it runs on the GPU's slots with its own fp64
+weights of those slots, everywhere else on its own addresses.  Outputs, the
+final state and the mass are then compared for every token of every unit
+(project page, exact Top-K paragraph: at a tie more than one set is the Top-K;
+Gated Sparse Update: the recurrence depends on the addresses only through
+the chosen slots and their weights).
 
 Values: fp32 state |d| <= 1e-6 + 1e-5 |ref| elementwise; bf16 state
 |d| <= 2e-2 * max(|ref|, rms of the reference row).  For the bf16 slot state
@@ -73,6 +77,23 @@ def compare_address_sets(gpu_idx, gpu_wt, ora_idx, ora_wt, ora_gap,
             must = flat_o[f][flat_ow[f] > wk * (1 + TIE_REL)]
             assert set(must.tolist()) <= set(flat_g[f].tolist())
     return differ
+
+
+def adopt(gpu_idx, ora_idx, ora_wt, differ, weights_of):
+    """Oracle addresses [..., K] with the GPU's set adopted where `differ`
+    (from compare_address_sets) marks a legitimate near-tie difference: those
+    addresses take the GPU's slots, in the GPU's order, with the oracle's fp64
+    weights of those slots (`weights_of(flat_index, slots)`).  Returns int32
+    slots and fp64 weights."""
+    K = ora_idx.shape[-1]
+    idx = np.array(ora_idx, np.int32, copy=True)
+    wt = np.array(ora_wt, np.float64, copy=True)
+    fi, fw = idx.reshape(-1, K), wt.reshape(-1, K)
+    fg = np.asarray(gpu_idx).reshape(-1, K)
+    for f in np.nonzero(np.asarray(differ).reshape(-1))[0]:
+        fi[f] = fg[f]
+        fw[f] = weights_of(int(f), fg[f])
+    return idx, wt
 
 
 def bf16_ulp(x):

@@ -290,3 +290,15 @@ def test_backward_scope_and_arguments(rn):
     assert st == -3 and "workspace" in err
     st, err = call_backward(rn, p, dv=FAKE + ((50 + 7) << 32))   # dv on dout
     assert st == -1 and "overlaps" in err
+
+
+def test_binding_rejects_host_tensors(rn):
+    """The binding checks every tensor before a pointer reaches the C ABI:
+    a host tensor is refused (with a GPU, shapes and dtypes are checked too;
+    see the GPU parity tests)."""
+    import torch
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        rn._arg(torch.zeros(4), "x", (4,), torch.float32)
+    with pytest.raises(ValueError, match="is required"):
+        rn._arg(None, "x", (4,), torch.float32)
+    assert rn._arg(None, "x", (4,), torch.float32, required=False) is None

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 from sparse_slot_recurrent_amd import synth  # noqa: E402
 
 sys.path.insert(0, os.path.dirname(__file__))
-from parity import assert_close, compare_address_sets, to_np  # noqa: E402
+from parity import adopt, assert_close, compare_address_sets, to_np  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -110,35 +110,48 @@ def weights_fn(orc, w, x, logits_name, pos, content_heads=0):
     return f
 
 
-def check_layer(orc, w, x, out, addr, S, mass, ref, S_ref, m_ref, content_heads=0):
-    """Tie-aware address check, then values before any legitimate
-    divergence, then untouched rows bit-exact."""
+def check_layer(orc, w, x, out, addr, S, mass, ref, content_heads=0, norm_w=None):
+    """Tie-aware address check; then the oracle's recurrence on the adopted
+    addresses (its own, or the GPU's where a near-tie made both correct),
+    compared with every output, the final state and the mass of every unit
+    over the whole sequence; rows never written bit-exact.  Returns the
+    number of units that adopted at least one GPU set."""
     bf = w.state_dtype == "bf16"
     g_wi, g_ww, g_ri, g_rw = (to_np(a) for a in addr)
-    dw = compare_address_sets(g_wi, g_ww, ref["w_idx"], ref["w_wt"], ref["w_gap"],
-                              weights_fn(orc, w, x, "k", x["pos0"], content_heads))
-    dr = compare_address_sets(g_ri, g_rw, ref["r_idx"], ref["r_wt"], ref["r_gap"],
-                              weights_fn(orc, w, x, "q", x["pos0"], content_heads))
+    wf_k = weights_fn(orc, w, x, "k", x["pos0"], content_heads)
+    wf_q = weights_fn(orc, w, x, "q", x["pos0"], content_heads)
+    dw = compare_address_sets(g_wi, g_ww, ref["w_idx"], ref["w_wt"], ref["w_gap"], wf_k)
+    dr = compare_address_sets(g_ri, g_rw, ref["r_idx"], ref["r_wt"], ref["r_gap"], wf_q)
+    wi, ww = adopt(g_wi, ref["w_idx"], ref["w_wt"], dw, wf_k)
+    ri, rw = adopt(g_ri, ref["r_idx"], ref["r_wt"], dr, wf_q)
+    S_a, m_a = x["S0"].copy(), x["m0"].copy()
+    out_a = orc.scan_given(wi, ww, ri, rw, x["v"], x["gamma"], x["g"], S_a, m_a,
+                           d_p=w.d_p, U=w.U, state_bf16=bf, eps_gsu=w.eps_gsu,
+                           eps_norm=w.eps_norm, norm_w=norm_w)
     B, T, H = x["gamma"].shape
-    diverged = (dw | dr)                       # [B,T,H]
-    first = np.where(diverged.any(1), diverged.argmax(1), T)  # [B,H]
-    tmask = np.arange(T)[None, :, None] < first[:, None, :]   # [B,T,H]
-    assert_close(to_np(out), ref["out"], bf, "out", mask=tmask[..., None])
-    clean = first == T                                          # [B,H]
+    adopted = (dw | dr).any(1)                                   # [B,H]
+    if "out" in ref:
+        # where nothing was adopted, the recurrence on given addresses is the
+        # oracle's own layer, bit for bit
+        keep = ~adopted[:, None, :]
+        assert np.array_equal(out_a[np.broadcast_to(keep, (B, T, H))],
+                              ref["out"][np.broadcast_to(keep, (B, T, H))])
+    got = to_np(out)
+    assert got.shape[1] == out_a.shape[1] == T, "every token compared"
+    assert_close(got, out_a, bf, "out")
     gS, gm = to_np(S), to_np(mass)
-    assert_close(gS[clean], S_ref[clean], bf, "S", slot_state=True)
-    assert_close(gm[clean], m_ref[clean], False, "mass")
+    assert_close(gS, S_a, bf, "S", slot_state=True)
+    assert_close(gm, m_a, False, "mass")
     # rows never written: bit-exact
     for b in range(B):
         for h in range(H):
-            written = np.union1d(ref["w_idx"][b, :, h].ravel(),
-                                 g_wi[b, :, h].ravel())
+            written = np.union1d(wi[b, :, h].ravel(), g_wi[b, :, h].ravel())
             keep = np.ones(w.M, bool)
             keep[written] = False
             assert np.array_equal(gS[b, h][keep], x["S0"][b, h][keep])
             assert np.array_equal(gm[b, h][keep].view(np.uint32),
                                   x["m0"][b, h][keep].view(np.uint32))
-    return int((~clean).sum())
+    return int(adopted.sum())
 
 
 @pytest.mark.parametrize("name", list(CUTS))
@@ -167,9 +180,9 @@ def test_prefill_matches_oracle(rn, orc, name):
     w = synth.WORKLOADS[name]
     x = synth.make_inputs(w, **CUTS[name])
     out, addr, d = run_gpu(rn, w, x)
-    ref, S_ref, m_ref = run_oracle(orc, w, x)
-    n_div = check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, S_ref, m_ref)
-    print(f"{name}: units diverged at a near-tie: {n_div}")
+    ref, _, _ = run_oracle(orc, w, x)
+    n_div = check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref)
+    print(f"{name}: units with an adopted near-tie set: {n_div}")
 
 
 @pytest.mark.parametrize("name", list(CUTS))
@@ -261,8 +274,8 @@ def test_norm_weight_and_cape_off(rn, orc):
     x = synth.make_inputs(w, B=1, T=100, H=4)
     nw = np.random.default_rng(5).uniform(0.5, 1.5, w.d_v).astype(np.float32)
     out, addr, d = run_gpu(rn, w, x, norm_w=torch.from_numpy(nw).cuda())
-    ref, S_ref, m_ref = run_oracle(orc, w, x, norm_w=nw)
-    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, S_ref, m_ref)
+    ref, _, _ = run_oracle(orc, w, x, norm_w=nw)
+    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, norm_w=nw)
 
 
 @pytest.mark.parametrize("cape,mask", [(2, 0), (3, 0), (2, 0b0101), (3, 0b1000)])
@@ -289,35 +302,16 @@ def test_cape_forms_and_content_heads(rn, orc, cape, mask):
     ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S_ref, m_ref,
                     d_p=w.d_p, U=w.U, K=w.K, state_bf16=False, cape=cape,
                     pos0=x["pos0"], content_heads=mask)
-    check_layer(orc, w, x, out, gaddr, d["S"], d["mass"], ref, S_ref, m_ref, content_heads=mask)
+    check_layer(orc, w, x, out, gaddr, d["S"], d["mass"], ref, content_heads=mask)
 
 
 @pytest.mark.parametrize("cape,mask", [(2, 0b0011), (3, 0)])
 def test_step_decode_cape_forms(rn, orc, cape, mask):
-    """The fused decode step with CAPE readings B and C and mixed heads."""
+    """The fused decode step with CAPE readings B and C and mixed heads:
+    8 sequences x 16 heads, 3 steps, every unit compared."""
     w = synth.WORKLOADS["decode"].replace(cape=cape)
-    B = 8
-    init = synth.make_inputs(w, B=B, T=1)
-    S_d, m_d = dev(init["S0"], "bf16"), dev(init["m0"], "f32")
-    s = synth.make_decode_step(w, 0, B=B)
-    pos = init["pos0"]
-    out, ao = rn.step_decode(*(dev(s[n], "bf16") for n in ("q", "k", "v", "gamma", "g")),
-                             torch.from_numpy(pos).cuda(), S_d, m_d, d_p=w.d_p, U=w.U,
-                             K=w.K, cape=cape, export_addresses=True, content_heads=mask)
-    torch.cuda.synchronize()
-    x = {n: np.ascontiguousarray(s[n][:, None]) for n in s}
-    S_o, m_o = init["S0"].copy(), init["m0"].copy()
-    ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S_o, m_o, d_p=w.d_p,
-                    U=w.U, K=w.K, state_bf16=True, cape=cape, pos0=pos, content_heads=mask)
-    xs = dict(x, pos0=pos)
-    dw = compare_address_sets(to_np(ao.w_idx)[:, None], to_np(ao.w_wt)[:, None], ref["w_idx"],
-                              ref["w_wt"], ref["w_gap"],
-                              weights_fn(orc, w, xs, "k", pos, mask))
-    dr = compare_address_sets(to_np(ao.r_idx)[:, None], to_np(ao.r_wt)[:, None], ref["r_idx"],
-                              ref["r_wt"], ref["r_gap"],
-                              weights_fn(orc, w, xs, "q", pos, mask))
-    ok = ~(dw | dr)[:, 0]  # [B, H]
-    assert_close(to_np(out)[ok], ref["out"][:, 0][ok], True, "out")
+    n_div, n_u, n_steps = decode_steps_check(rn, orc, w, 8, 3, content_heads=mask)
+    assert n_steps == 3
 
 
 @pytest.mark.parametrize("d_p,U,K,d_v,in_dt,st_dt", [
@@ -335,8 +329,8 @@ def test_shapes_and_edge_parameters(rn, orc, d_p, U, K, d_v, in_dt, st_dt):
                        pos0_max=9)
     x = synth.make_inputs(w)
     out, addr, d = run_gpu(rn, w, x)
-    ref, S_ref, m_ref = run_oracle(orc, w, x)
-    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, S_ref, m_ref)
+    ref, _, _ = run_oracle(orc, w, x)
+    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref)
 
 
 def test_extreme_gates_and_zero_eps(rn, orc):
@@ -347,8 +341,8 @@ def test_extreme_gates_and_zero_eps(rn, orc):
     x["gamma"][0, :32] = -1000.0
     x["gamma"][0, 32:] = 1000.0
     out, addr, d = run_gpu(rn, w, x)
-    ref, S_ref, m_ref = run_oracle(orc, w, x)
-    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref, S_ref, m_ref)
+    ref, _, _ = run_oracle(orc, w, x)
+    check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref)
 
 
 def test_empty_calls_leave_state_untouched(rn):
@@ -402,82 +396,87 @@ def test_resume_and_steps(rn, name):
     assert_close(to_np(d2["S"]), to_np(dw["S"]), bf, "steps S", slot_state=True)
 
 
-def decode_steps_check(rn, orc, w, B, n_steps, units=None):
-    """Runs n_steps decode steps for all B x H units on the GPU and for
-    `units` (list of (b, h); None = all) in the oracle; compares addresses
-    (tie-aware), outputs of units not yet diverged at a near-tie, and the
-    final state of units that never diverged."""
+def decode_steps_check(rn, orc, w, B, n_steps, seqs=None, content_heads=0):
+    """Runs n_steps decode steps for all B x H units on the GPU and, for the
+    sequences `seqs` (None = all; every head of each), in the oracle.  Each
+    step: addresses tie-aware against the oracle's; then the oracle's GSU,
+    read, norm and gate on the adopted addresses (its own, or the GPU's where
+    a near-tie made both correct), so every step of every sampled unit is
+    compared, and the state and mass at the end.  Returns (units that
+    adopted a GPU set, units compared, steps compared)."""
     H = w.H
     init = synth.make_inputs(w, B=B, T=1)
     S_d = dev(init["S0"], "bf16")
     m_d = dev(init["m0"], "f32")
-    if units is None:
-        units = [(b, h) for b in range(B) for h in range(H)]
-    ub = np.array([u[0] for u in units])
-    uh = np.array([u[1] for u in units])
-    n_u = len(units)
-    # the oracle holds the sampled units as a [n_u, 1] batch of single heads
-    S_o = np.ascontiguousarray(init["S0"][ub, uh][:, None])
-    m_o = np.ascontiguousarray(init["m0"][ub, uh][:, None])
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs)
+    # the oracle holds the sampled sequences (all heads) as a batch
+    S_o = np.ascontiguousarray(init["S0"][seqs])
+    m_o = np.ascontiguousarray(init["m0"][seqs])
     pos = init["pos0"].copy()
-    alive = np.ones(n_u, bool)
+    adopted = np.zeros((len(seqs), H), bool)
     plan = rn.StepPlan(B, H, w.d_p, w.U, w.K, w.d_v, rn.BF16, rn.BF16,
-                       cape=w.cape, device="cuda")
+                       cape=w.cape, device="cuda", content_heads=content_heads)
     out = torch.empty((B, H, w.d_v), dtype=torch.bfloat16, device="cuda")
     ao = rn.new_addresses((B, H, w.K), "cuda")
+    done = 0
     for step in range(n_steps):
         s = synth.make_decode_step(w, step, B=B)
         plan(dev(s["q"], "bf16"), dev(s["k"], "bf16"), dev(s["v"], "bf16"),
              dev(s["gamma"], "bf16"), dev(s["g"], "bf16"),
              torch.from_numpy(pos).cuda(), S_d, m_d, out, addr_out=ao)
         torch.cuda.synchronize()
-        x = {n: np.ascontiguousarray(s[n][ub, uh][:, None, None]) for n in s}
-        p_u = np.ascontiguousarray(pos[ub])
-        ref = orc.layer(x["q"], x["k"], x["v"], x["gamma"], x["g"], S_o, m_o,
-                        d_p=w.d_p, U=w.U, K=w.K, state_bf16=True, pos0=p_u)
+        x = {n: np.ascontiguousarray(s[n][seqs][:, None]) for n in s}  # [b,1,H,*]
+        p_u = np.ascontiguousarray(pos[seqs])
         xs = dict(x, pos0=p_u)
-        sel = lambda a: to_np(a)[ub, uh][:, None, None]
-        dw = compare_address_sets(sel(ao.w_idx), sel(ao.w_wt), ref["w_idx"],
-                                  ref["w_wt"], ref["w_gap"],
-                                  weights_fn(orc, w, xs, "k", p_u))
-        dr = compare_address_sets(sel(ao.r_idx), sel(ao.r_wt), ref["r_idx"],
-                                  ref["r_wt"], ref["r_gap"],
-                                  weights_fn(orc, w, xs, "q", p_u))
-        alive &= ~(dw | dr)[:, 0, 0]
-        got = to_np(out)[ub, uh]
-        assert_close(got[alive], ref["out"][alive, 0, 0], True, f"out step {step}")
+        sel = lambda a: np.ascontiguousarray(to_np(a)[seqs][:, None])
+        g_wi, g_ww, g_ri, g_rw = (sel(a) for a in ao)
+        res = {}
+        for nm, lg in (("w", "k"), ("r", "q")):
+            oi, ow, og = orc.decode_all(x[lg], w.U, w.d_p, w.K, cape=w.cape, pos0=p_u,
+                                        content_heads=content_heads)
+            gi, gw = (g_wi, g_ww) if nm == "w" else (g_ri, g_rw)
+            wf = weights_fn(orc, w, xs, lg, p_u, content_heads)
+            d = compare_address_sets(gi, gw, oi, ow, og, wf)
+            res[nm] = adopt(gi, oi, ow, d, wf)
+            adopted |= d[:, 0]
+        ref = orc.scan_given(*res["w"], *res["r"], x["v"], x["gamma"], x["g"], S_o, m_o,
+                             d_p=w.d_p, U=w.U, state_bf16=True, eps_gsu=w.eps_gsu,
+                             eps_norm=w.eps_norm)
+        assert_close(to_np(out)[seqs], ref[:, 0], True, f"out step {step}")
         pos = pos + 1
-    Sg = to_np(S_d)[ub, uh]
-    mg = to_np(m_d)[ub, uh]
-    assert_close(Sg[alive], S_o[alive, 0], True, "S", slot_state=True)
-    assert_close(mg[alive], m_o[alive, 0], False, "mass")
-    return int((~alive).sum()), n_u
+        done += 1
+    assert_close(to_np(S_d)[seqs], S_o, True, "S", slot_state=True)
+    assert_close(to_np(m_d)[seqs], m_o, False, "mass")
+    return int(adopted.sum()), adopted.size, done
 
 
 def test_decode_steps_match_oracle(rn, orc):
     """Batched decode from a pre-filled random state: 6 steps, 64 sequences x
     16 heads, d_v = 128, K = 16, bf16 state; all units checked."""
-    n_div, n_u = decode_steps_check(rn, orc, synth.WORKLOADS["decode"], 64, 6)
-    print(f"decode cut: {n_div} of {n_u} units diverged at a near-tie")
+    n_div, n_u, n_steps = decode_steps_check(rn, orc, synth.WORKLOADS["decode"], 64, 6)
+    assert n_steps == 6
+    print(f"decode cut: {n_div} of {n_u} units adopted a near-tie set")
 
 
 def test_full_size_decode_sampled(rn, orc):
-    """The benchmark's decode shape (256 sequences x 16 heads), 200 steps,
-    with the oracle on 24 sampled units."""
+    """The decode workload in full: 256 sequences x 16 heads for all 1024
+    steps on the GPU, with the oracle on two sampled sequences (32 units)
+    for every step."""
     w = synth.WORKLOADS["decode"]
-    r = np.random.default_rng(99)
-    units = [(int(b), int(h)) for b, h in zip(r.integers(0, w.B, 24),
-                                              r.integers(0, w.H, 24))]
-    n_div, n_u = decode_steps_check(rn, orc, w, w.B, 200, units)
-    print(f"decode full size: {n_div} of {n_u} sampled units diverged")
+    seqs = np.random.default_rng(99).choice(w.B, size=2, replace=False)
+    n_div, n_u, n_steps = decode_steps_check(rn, orc, w, w.B, w.steps, seqs=seqs)
+    assert n_steps == w.steps == 1024
+    print(f"decode full size: {n_steps} steps, {n_div} of {n_u} sampled units "
+          f"adopted a near-tie set")
 
 
 @pytest.mark.parametrize("name", ["prefill_top8", "prefill_top32"])
 def test_full_size_prefill(rn, orc, name):
-    """The benchmark's prefill shape in full.  (1) the oracle's addresses
-    drive the GPU recurrence: every output and the whole final state are
-    compared; (2) the GPU decoder's addresses are checked tie-aware against
-    the oracle's for every token."""
+    """The benchmark's prefill shape in full, every unit.  (1) The oracle's
+    addresses drive the GPU recurrence (given addresses, token-major): every
+    output and the whole final state.  (2) The GPU's own call (decoder, then
+    the recurrence on its head-major addresses) against the oracle on the
+    adopted addresses: every token, state and mass."""
     w = synth.WORKLOADS[name]
     x = synth.make_inputs(w)
     ref, S_ref, m_ref = run_oracle(orc, w, x)
@@ -490,54 +489,84 @@ def test_full_size_prefill(rn, orc, name):
     assert_close(to_np(out), ref["out"], bf, "out")
     assert_close(to_np(d["S"]), S_ref, bf, "S", slot_state=True)
     assert_close(to_np(d["mass"]), m_ref, False, "mass")
-    del out, d
-    dg = gpu_inputs(w, x)
-    addr = rn.decode_addresses(dg["q"], dg["k"], d_p=w.d_p, U=w.U, K=w.K,
-                               cape=w.cape, pos0=dg["pos0"])
-    torch.cuda.synchronize()
-    n_diff = 0
-    for (gi, gw), (oi, ow, og), lg in (
-            ((addr.w_idx, addr.w_wt), (ref["w_idx"], ref["w_wt"], ref["w_gap"]), "k"),
-            ((addr.r_idx, addr.r_wt), (ref["r_idx"], ref["r_wt"], ref["r_gap"]), "q")):
-        n_diff += int(compare_address_sets(
-            to_np(gi), to_np(gw), oi, ow, og,
-            weights_fn(orc, w, x, lg, x["pos0"])).sum())
-    print(f"{name} full size: {2 * x['gamma'].size} addresses, "
-          f"{n_diff} near-tie sets differ")
+    del out, d, ai, S_ref, m_ref
+    out, addr, d = run_gpu(rn, w, x)
+    n_adopt = check_layer(orc, w, x, out, addr, d["S"], d["mass"], ref)
+    print(f"{name} full size: {x['gamma'].size} token-heads, "
+          f"{n_adopt} units adopted a near-tie set")
 
 
-def test_full_size_large_state_sampled(rn, orc):
-    """The large-state prefill (M = 4^8, T = 32768) on the GPU in full; the
-    oracle (prefix-tree mode, pinned equal to brute force) on two sampled
-    units over the whole sequence."""
+def _large_state_unit_check(orc, w, x, b, h, out, addr, S, mass):
+    """One (b, h) unit of the full-size 4^8-slot run against the oracle over
+    the whole sequence: tree-search addresses (pinned equal to brute force),
+    with brute-force margins where the GPU's set differs; the adopted
+    recurrence; every output, the unit's state and mass."""
+    xu = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1])
+          for n in ("q", "k", "v", "gamma", "g")}
+    xu["S0"] = np.ascontiguousarray(x["S0"][b:b + 1, h:h + 1])
+    xu["m0"] = np.ascontiguousarray(x["m0"][b:b + 1, h:h + 1])
+    xu["pos0"] = x["pos0"][b:b + 1].copy()
+    ref = {}
+    for nm, lg in (("w", "k"), ("r", "q")):
+        oi, ow, _ = orc.decode_all(xu[lg], w.U, w.d_p, w.K, cape=w.cape,
+                                   pos0=xu["pos0"], mode=orc.TOPK_TREE)
+        gap = np.full(oi.shape[:-1], np.inf)
+        gi = to_np(getattr(addr, nm + "_idx")[b:b + 1, :, h:h + 1])
+        diff = ~(np.sort(gi, -1) == np.sort(oi, -1)).all(-1)
+        for f in np.nonzero(diff.reshape(-1))[0]:
+            _, _, gp, _, _ = orc.decode_one(xu[lg].reshape(-1, w.L)[f], w.U, w.d_p, w.K,
+                                            cape=w.cape, pos=int(xu["pos0"][0]) + int(f))
+            gap.reshape(-1)[f] = gp
+        ref[nm + "_idx"], ref[nm + "_wt"], ref[nm + "_gap"] = oi, ow, gap
+    au = type(addr)(*[a[b:b + 1, :, h:h + 1].contiguous() for a in addr])
+    return check_layer(orc, w, xu, out[b:b + 1, :, h:h + 1].contiguous(), au,
+                       S[b:b + 1, h:h + 1].contiguous(),
+                       mass[b:b + 1, h:h + 1].contiguous(), ref)
+
+
+@pytest.fixture(scope="module")
+def large_state_inputs():
+    return synth.make_inputs(synth.WORKLOADS["large_state"])
+
+
+def test_full_size_large_state_sampled(rn, orc, large_state_inputs):
+    """The 4^8-slot prefill at full size (B 2, T 32768, H 16) in the
+    benchmark's launch configuration: the GPU's own call in full, and two
+    sampled units compared with the oracle over all 32768 tokens (addresses
+    tie-aware, then the adopted recurrence: every output, state, mass)."""
     w = synth.WORKLOADS["large_state"]
-    x = synth.make_inputs(w)
+    x = large_state_inputs
     out, addr, d = run_gpu(rn, w, x)
     for b, h in ((0, 0), (1, 11)):
-        xu = {n: np.ascontiguousarray(x[n][b:b + 1, :, h:h + 1])
-              for n in ("q", "k", "v", "gamma", "g")}
-        xu["S0"] = np.ascontiguousarray(x["S0"][b:b + 1, h:h + 1])
-        xu["m0"] = np.ascontiguousarray(x["m0"][b:b + 1, h:h + 1])
-        xu["pos0"] = x["pos0"][b:b + 1].copy()
-        ref, S_ref, m_ref = run_oracle(orc, w, xu, mode=orc.TOPK_TREE)
-        ref["w_gap"] = np.full(ref["w_idx"].shape[:-1], np.inf)
-        ref["r_gap"] = np.full(ref["r_idx"].shape[:-1], np.inf)
-        # gaps from brute force for the addresses whose sets differ
-        au = tuple(to_np(a)[b:b + 1, :, h:h + 1] for a in addr)
-        gi, oi = np.sort(au[0], -1), np.sort(ref["w_idx"], -1)
-        gr, orr = np.sort(au[2], -1), np.sort(ref["r_idx"], -1)
-        for nm, g_, o_ in (("k", gi, oi), ("q", gr, orr)):
-            bad = np.nonzero(~(g_ == o_).all(-1).reshape(-1))[0]
-            for f in bad:
-                _, _, gap, _, _ = orc.decode_one(xu[nm].reshape(-1, w.L)[f],
-                                                 w.U, w.d_p, w.K)
-                (ref["w_gap"] if nm == "k" else ref["r_gap"]).reshape(-1)[f] = gap
-        Sfull, mfull = d["S"], d["mass"]
-        n_div = check_layer(orc, w, xu, out[b:b + 1, :, h:h + 1].contiguous(),
-                            type(addr)(*[torch.from_numpy(a) for a in au]),
-                            Sfull[b:b + 1, h:h + 1].contiguous(),
-                            mfull[b:b + 1, h:h + 1].contiguous(), ref, S_ref, m_ref)
-        print(f"large_state unit ({b},{h}): diverged={n_div}")
+        n = _large_state_unit_check(orc, w, x, b, h, out, addr, d["S"], d["mass"])
+        print(f"large_state unit ({b},{h}): all {w.T} tokens compared, adopted "
+              f"near-tie sets: {bool(n)}")
+
+
+def test_large_state_given_addresses_full_length(rn, orc, large_state_inputs):
+    """The 4^8-slot, K = 32, bf16-row scan driven by the oracle's
+    tree-search addresses over the whole sequence (B 1, H 2, T 32768): every
+    output, the whole final state and mass, with no tie exemption."""
+    w = synth.WORKLOADS["large_state"]
+    x = {n: np.ascontiguousarray(large_state_inputs[n][:1, :, :2])
+         for n in ("q", "k", "v", "gamma", "g")}
+    x["S0"] = np.ascontiguousarray(large_state_inputs["S0"][:1, :2])
+    x["m0"] = np.ascontiguousarray(large_state_inputs["m0"][:1, :2])
+    x["pos0"] = large_state_inputs["pos0"][:1].copy()
+    wi, ww, _ = orc.decode_all(x["k"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"],
+                               mode=orc.TOPK_TREE)
+    ri, rw, _ = orc.decode_all(x["q"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"],
+                               mode=orc.TOPK_TREE)
+    S_ref, m_ref = x["S0"].copy(), x["m0"].copy()
+    ref = orc.scan_given(wi, ww, ri, rw, x["v"], x["gamma"], x["g"], S_ref, m_ref,
+                         d_p=w.d_p, U=w.U, state_bf16=True)
+    ai = rn.Addresses(*(torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in
+                        (wi, ww.astype(np.float32), ri, rw.astype(np.float32))))
+    out, _, d = run_gpu(rn, w, x, addr_in=ai, export=False)
+    assert out.shape[1] == w.T
+    assert_close(to_np(out), ref, True, "out")
+    assert_close(to_np(d["S"]), S_ref, True, "S", slot_state=True)
+    assert_close(to_np(d["mass"]), m_ref, False, "mass")
 
 
 @pytest.mark.parametrize("name", ["prefill_top8", "prefill_top32"])
@@ -568,3 +597,31 @@ def test_repeatability(rn):
     assert torch.equal(a1.w_idx, a2.w_idx) and torch.equal(a1.r_wt, a2.r_wt)
     assert_close(to_np(o2), to_np(o1), True, "out")
     assert_close(to_np(d2["S"]), to_np(d1["S"]), True, "S", slot_state=True)
+
+
+def test_binding_checks_shapes_and_dtypes(rn):
+    """Tensors whose shape or dtype disagree with the parameters are refused
+    by the binding before anything is enqueued (the C ABI derives every
+    extent from the parameters)."""
+    w = synth.WORKLOADS["tiny"]
+    x = synth.make_inputs(w, T=40)
+    d = gpu_inputs(w, x)
+    plan = rn.PrefillPlan(1, 40, 1, w.d_p, w.U, w.K, w.d_v, rn.F32, rn.F32)
+    out = torch.empty((1, 40, 1, w.d_v), device="cuda")
+    S0, m0 = d["S"].clone(), d["mass"].clone()
+    args = [d[n] for n in ("q", "k", "v", "gamma", "g")]
+    bad = [("S", d["S"][:, :, :512].contiguous()), ("mass", d["mass"].to(torch.bfloat16)),
+           ("out", out.double())]
+    for name, t in bad:
+        kw = {"S": d["S"], "mass": d["mass"], "out": out}
+        kw[name] = t
+        with pytest.raises(ValueError, match=name):
+            plan(*args, kw["S"], kw["mass"], kw["out"])
+    with pytest.raises(ValueError, match="pos0"):
+        plan(*args, d["S"], d["mass"], out, pos0=d["pos0"].long())
+    a = rn.new_addresses((1, 40, 1, w.K), "cuda")
+    with pytest.raises(ValueError, match="addr_in.w_wt"):
+        plan(*args, d["S"], d["mass"], out,
+             addr_in=a._replace(w_wt=a.w_wt.double()))
+    torch.cuda.synchronize()
+    assert torch.equal(d["S"], S0) and torch.equal(d["mass"], m0)
