@@ -161,6 +161,31 @@ ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
                                   const ramnet_addr *addr_out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * prefill as ramnet_scan_prefill, with the same arguments except that there
+ * is no workspace.  Its scratch is a static device array of
+ * RAMNET_NOALLOC_SCRATCH_BYTES bytes (64 MiB) that every GPU the library
+ * runs on holds from when the library is loaded until the process ends; the
+ * call itself allocates nothing (no hipMalloc, no allocating library call).
+ *   - A prefill whose scratch need exceeds that size is refused with
+ *     RAMNET_EWORKSPACE before anything is enqueued (the need is at most
+ *     ramnet_workspace_bytes(p, RAMNET_OP_PREFILL); exporting addresses
+ *     through addr_out, or giving addr_in, lowers it).
+ *   - Every call on one GPU uses that GPU's one array, whose contents on
+ *     entry do not matter.  Calls that may overlap in time on one GPU
+ *     (other streams, other host threads) race on it: serialise them, e.g.
+ *     on one stream.
+ * Results are bit-identical to ramnet_scan_prefill's on the same inputs. */
+#define RAMNET_NOALLOC_SCRATCH_BYTES (64u << 20)
+ramnet_status ramnet_scan_prefill_noalloc(const ramnet_params *p, const void *q,
+                                          const void *k, const void *v,
+                                          const void *gamma, const void *g,
+                                          const float *norm_w, const int32_t *pos0,
+                                          void *S, float *mass, void *out,
+                                          const ramnet_addr *addr_in,
+                                          const ramnet_addr *addr_out, void *stream);
+
 /* One decoding step (project page, decoding paragraph: the current token's
  * slots are accessed directly, without a pass over the state): steps 1-4
  * for one token of each of B sequences.  p->T must be 1.

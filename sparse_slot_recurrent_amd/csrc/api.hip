@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -562,6 +563,42 @@ ramnet_status run_whole_layer(const ramnet_params *p, bool step, const ramnet_pr
 
 }  // namespace
 
+// Scratch of ramnet_scan_prefill_noalloc: a static device array that every
+// GPU the library runs on holds until the process ends.  Host code never
+// passes `scratch` itself to a kernel or a copy (on the host the name is only
+// a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress gives on each device.
+static __device__ __align__(256) unsigned char scratch[RAMNET_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// The current device's address of `scratch`, looked up once per device
+// with that device current.
+ramnet_status scratch_of_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RAMNET_EUNSUPPORTED, "device %d: the static scratch is kept for devices 0..%d",
+                    dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(RAMNET_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RAMNET_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model) {
@@ -841,6 +878,28 @@ ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q, const v
                                   size_t workspace_bytes, void *stream) {
     return run_layer(p, false, q, k, v, gamma, g, norm_w, pos0, S, mass, out, addr_in, addr_out,
                      workspace, workspace_bytes, stream);
+}
+
+ramnet_status ramnet_scan_prefill_noalloc(const ramnet_params *p, const void *q, const void *k,
+                                          const void *v, const void *gamma, const void *g,
+                                          const float *norm_w, const int32_t *pos0, void *S,
+                                          float *mass, void *out, const ramnet_addr *addr_in,
+                                          const ramnet_addr *addr_out, void *stream) {
+    ramnet_status s = check_params(p, false);
+    if (s) return s;
+    // the scratch need is known from the parameters: refuse a call that does
+    // not fit before any HIP call is made
+    const LayerPlan lp = plan_layer(p, false, addr_in == nullptr && addr_out == nullptr);
+    if (lp.total() > RAMNET_NOALLOC_SCRATCH_BYTES)
+        return fail(RAMNET_EWORKSPACE,
+                    "this prefill needs %zu bytes of scratch; the static scratch of "
+                    "ramnet_scan_prefill_noalloc holds %zu (call ramnet_scan_prefill with a "
+                    "workspace, or split the batch)",
+                    lp.total(), static_cast<size_t>(RAMNET_NOALLOC_SCRATCH_BYTES));
+    void *ws = nullptr;
+    if ((s = scratch_of_current_device(&ws))) return s;
+    return run_layer(p, false, q, k, v, gamma, g, norm_w, pos0, S, mass, out, addr_in, addr_out, ws,
+                     RAMNET_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q, const void *k,

@@ -24,7 +24,8 @@ EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
             "ramnet_layer_workspace_bytes", "ramnet_project_inputs",
             "ramnet_layer_forward", "ramnet_layer_step",
             "ramnet_packed_weights_bytes", "ramnet_pack_weights",
-            "ramnet_scan_backward")
+            "ramnet_scan_backward", "ramnet_scan_prefill_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Params(C.Structure):
@@ -84,6 +85,9 @@ def load_library(path: str = LIB_PATH):
     lib.ramnet_scan_prefill.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
                                         pa, P, C.c_size_t, P]
     lib.ramnet_scan_prefill.restype = C.c_int
+    lib.ramnet_scan_prefill_noalloc.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
+                                                pa, P]
+    lib.ramnet_scan_prefill_noalloc.restype = C.c_int
     lib.ramnet_step_decode.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, pa,
                                        P, C.c_size_t, P]
     lib.ramnet_step_decode.restype = C.c_int
@@ -333,6 +337,27 @@ def scan_prefill(q, k, v, gamma, g, S, mass, *, d_p: int, U: int, K: int,
     plan(q, k, v, gamma, g, S, mass, out, norm_w=norm_w, pos0=pos0,
          addr_in=addr_in, addr_out=ao)
     return (out, ao) if export_addresses else out
+
+
+def scan_prefill_noalloc(q, k, v, gamma, g, S, mass, out, *, d_p: int, U: int,
+                        K: int, cape: int = 1, norm_w=None, pos0=None, eps_gsu=1e-6,
+                        eps_norm=1e-6, addr_in: Optional[Addresses] = None,
+                        addr_out: Optional[Addresses] = None, content_heads: int = 0):
+    """ramnet_scan_prefill_noalloc: the prefill with the library's static
+    scratch instead of a workspace (nothing is allocated on the device by
+    the call; `out` and the optional `addr_out` are the caller's)."""
+    B, T, H, d_v = v.shape
+    p = make_params(B, T, H, d_p, U, K, d_v, _dt(v), _dt(S), cape, eps_gsu,
+                    eps_norm, content_heads=content_heads)
+    shp = (B, T, H, K)
+    ai = _addr_struct(addr_in, shp, "addr_in")
+    ao = _addr_struct(addr_out, shp, "addr_out")
+    ptrs = _Shapes(p).prefill(q, k, v, gamma, g, S, mass, out, norm_w, pos0,
+                              need_qk=addr_in is None)
+    _raise(load_library().ramnet_scan_prefill_noalloc(
+        C.byref(p), *ptrs, C.byref(ai) if ai is not None else None,
+        C.byref(ao) if ao is not None else None, _stream()))
+    return out
 
 
 class StepPlan:
