@@ -23,8 +23,8 @@ PROBE_SRC = "probe.hip"
 PROBE_LIB = os.path.join(PKG, "libramnet_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "step_fused.hip",
-           "proj.hip", "backward.hip"]
+SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "scan_ranges.hip",
+           "step_fused.hip", "proj.hip", "backward.hip"]
 # hipBLASLt carries the dense projections around the layer.
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 

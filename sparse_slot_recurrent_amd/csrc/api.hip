@@ -356,6 +356,10 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         c.mass_ws = reinterpret_cast<float *>(cw);
         cw += lp.cp.ws_mass;
         c.plan = reinterpret_cast<unsigned char *>(cw);
+        cw += lp.cp.ws_plan;
+        c.partial = reinterpret_cast<float *>(cw);
+        cw += lp.cp.ws_partial;
+        c.spill = cw;
         c.out_bf16 = out_bf16;  // the epilogue writes bf16 directly
         e = ramnet::launch_scan_chunked(c, st);
     } else {

@@ -59,6 +59,13 @@ hipError_t launch_scan_serial(const ScanArgs &a, hipStream_t st);
 // (unit, channel slice) per workgroup, and an epilogue applies RMSNorm and
 // the gate.  r (fp32 [B,T,H,d_v]) and per-slice square sums ([B,T,H,d_v/CG])
 // pass through global memory between the last two.
+// Rows in HBM (M > 1024): the slot-range path (scan_ranges.hip).  The slots
+// of a unit are split into kRanges ranges (slot mod kRanges); one workgroup
+// per (unit, range) gathers, updates and writes back whole rows of its
+// range and sums its part of every token's read, the partial sums of the
+// ranges are added by an epilogue that applies RMSNorm and the gate.
+constexpr int kRanges = 8;
+
 struct ChunkPlan {
     bool ok;
     bool resident;      // slot rows live in registers (M <= 1024); else in HBM
@@ -77,18 +84,25 @@ struct ChunkPlan {
     int n0;
     int HMAX;
     int64_t n_chunks;
+    // rows in HBM: per range, the write and read lists staged in LDS (longer
+    // lists are read from the record), and the version rows held in LDS
+    // (later ones go to a spill area in the workspace)
+    int CAPW, CAPR, VCAP;
     // one (unit, chunk) plan record and its sections (byte offsets)
-    size_t rec_bytes, o_ent, o_map, o_hl, o_wtv, o_ww, o_wa, o_rv, o_rr;
+    size_t rec_bytes, o_ent, o_map, o_hl, o_wtv, o_ww, o_wa, o_rv, o_rr, o_rt;
     size_t lds_plan, lds_scan;
     size_t ws_rbuf, ws_sumsq, ws_mass, ws_plan;  // workspace section sizes
+    size_t ws_partial, ws_spill;                 // rows in HBM: partial reads, spilled versions
 };
 
 struct ChunkArgs : ScanArgs {
     ChunkPlan p;
     float *rbuf;     // may alias out when the output is fp32
     float *sumsq;
-    float *mass_ws;  // final mass [units][M]; HBM mode: per-slice copies [units][M][ncg]
+    float *mass_ws;  // rows on chip: final mass [units][M]
     unsigned char *plan;
+    float *partial;  // rows in HBM: [B,T,H][kRanges][d_v] partial reads
+    void *spill;     // rows in HBM: [units][kRanges][EV][d_v] version rows beyond VCAP
 };
 
 constexpr size_t kChunkLdsLimit = 160 * 1024;
@@ -98,6 +112,10 @@ constexpr int kBwdOutBlocks = 16;
 
 ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16,
                        bool state_bf16);
+// The rows-in-HBM plan (M > 1024) and launch (scan_ranges.hip).
+ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16,
+                      bool state_bf16);
+hipError_t launch_scan_ranges(const ChunkArgs &a, hipStream_t st);
 // Workspace bytes of the chunked path beyond the addresses.
 size_t chunk_workspace_bytes(const ChunkPlan &p);
 hipError_t launch_scan_chunked(const ChunkArgs &a, hipStream_t st);

@@ -44,6 +44,7 @@
 //     butterfly; r and the slice's sum of squares go to global memory.
 // rms_gate_kernel: sums the slices' squares per token, applies RMSNorm and
 // the gate, and copies the final mass.
+#include "chunk_common.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -53,68 +54,8 @@
 namespace ramnet {
 namespace {
 
-constexpr int kNT = 1024;  // threads per workgroup
-constexpr int kWavesPerBlock = kNT / kWave;
-constexpr int kMaxEV = 4096;                        // events of one kind per chunk
-constexpr int kMaxEVHbm = 3072;                     // the same with slot rows in HBM
-constexpr int kPT = 512;                            // plan kernel threads
-// Events per plan thread (EPW) and plan entries per scan thread (EVT) are
-// template parameters: EV / kPT and EV / kNT for chunks of at most 2048,
-// 3072 or 4096 events (EV rounded up to a multiple of 1024).
 constexpr int kEPN = 2 * kMaxEVHbm / kNT;           // touched slots per thread (HBM rows)
 constexpr int kHBins = 32;                          // write-count bins of the hand-off order
-
-__host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
-inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
-
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-// Exclusive prefix of x over a block of NT threads (thread order); the block
-// total goes to `total`.  Every thread must call it.
-template <int NT>
-__device__ int block_excl_scan(int x, int *wtot, int &total) {
-    constexpr int NW = NT / kWave;
-    const int lane = lane_id(), wid = threadIdx.x / kWave;
-    const int incl = wave_incl_scan(x);
-    if (lane == kWave - 1) wtot[wid] = incl;
-    lds_barrier();
-    if (wid == 0) {
-        int y = lane < NW ? wtot[lane] : 0;
-        y = wave_incl_scan(y);
-        if (lane < NW) wtot[lane] = y;
-    }
-    lds_barrier();
-    const int base = wid > 0 ? wtot[wid - 1] : 0;
-    total = wtot[NW - 1];
-    lds_barrier();
-    return base + incl - x;
-}
-
-// In-place exclusive scan of a[0, n) by a block of NT threads, each taking
-// a contiguous run; returns the sum.  Callers synchronise before reading a.
-template <int NT>
-__device__ int block_scan_array(int *a, int n, int *wtot) {
-    const int per = (n + NT - 1) / NT;
-    const int lo = min(static_cast<int>(threadIdx.x) * per, n), hi = min(lo + per, n);
-    int local = 0;
-    for (int i = lo; i < hi; ++i) local += a[i];
-    int total;
-    int base = block_excl_scan<NT>(local, wtot, total);
-    for (int i = lo; i < hi; ++i) {
-        const int c = a[i];
-        a[i] = base;
-        base += c;
-    }
-    return total;
-}
 
 // LDS rows are stored in 16-byte chunks whose order is XOR-swizzled by the
 // row index, so that lanes touching different rows spread over the banks
@@ -176,27 +117,6 @@ __device__ __forceinline__ void store_row(bf16_t *p, int swz, const float (&x)[C
     }
 }
 
-// A 16-byte chunk of a row as fp32 values.
-__device__ __forceinline__ void unpack_chunk(const uint4 &u, float (&v)[4]) {
-    v[0] = __uint_as_float(u.x);
-    v[1] = __uint_as_float(u.y);
-    v[2] = __uint_as_float(u.z);
-    v[3] = __uint_as_float(u.w);
-}
-__device__ __forceinline__ void unpack_chunk(const uint4 &u, float (&v)[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(w[q] << 16);
-        v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-    }
-}
-
-// floor(e / K) for 0 <= e < 2^24 with a precomputed m = ceil(2^32 / K).
-__device__ __forceinline__ int div_by(uint32_t e, uint64_t m) {
-    return static_cast<int>((static_cast<uint64_t>(e) * m) >> 32);
-}
-
 // LDS of the plan kernel (byte offsets).
 struct PlanLds {
     size_t key, cf, wo, bk, sk, sa, need, wtot, hist, total;
@@ -225,8 +145,6 @@ struct PlanHdr {
     int nwt;   // valid writes
     int nh;    // resident mode: slots handed off after their first n0 writes
 };
-
-constexpr int kReadFlag = 1 << 30;
 
 template <typename TIn, int EPW>
 __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
@@ -652,30 +570,6 @@ __device__ __forceinline__ void store_piece(unsigned char *lds, uint32_t a, cons
         w[q] = static_cast<uint32_t>(bf16_rne(x[2 * q]).bits) | (static_cast<uint32_t>(bf16_rne(x[2 * q + 1]).bits) << 16);
     *reinterpret_cast<uint4 *>(lds + a) = make_uint4(w[0], w[1], w[2], w[3]);
 }
-// Channels [c0, c0 + CP) of value row t (rows of VROW elements), as fp32.
-template <int CP>
-__device__ __forceinline__ void value_part(const float *vbuf, int off, float (&vt)[CP]) {
-#pragma unroll
-    for (int j = 0; j < CP / 4; ++j) {
-        const float4 f = reinterpret_cast<const float4 *>(vbuf + off)[j];
-        vt[4 * j] = f.x;
-        vt[4 * j + 1] = f.y;
-        vt[4 * j + 2] = f.z;
-        vt[4 * j + 3] = f.w;
-    }
-}
-template <int CP>
-__device__ __forceinline__ void value_part(const bf16_t *vbuf, int off, float (&vt)[CP]) {
-#pragma unroll
-    for (int j = 0; j < CP / 4; ++j) {
-        const uint2 u = reinterpret_cast<const uint2 *>(vbuf + off)[j];
-        vt[4 * j] = __uint_as_float(u.x << 16);
-        vt[4 * j + 1] = __uint_as_float(u.x & 0xffff0000u);
-        vt[4 * j + 2] = __uint_as_float(u.y << 16);
-        vt[4 * j + 3] = __uint_as_float(u.y & 0xffff0000u);
-    }
-}
-
 // walk_slot for piece h of a row slice: the LH = CG / CP lanes that share a
 // slot each apply its writes to their own piece (each computing the same
 // mass and rate) and store their piece of the versions reads see.
@@ -1299,6 +1193,7 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
 }  // namespace
 
 ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16, bool state_bf16) {
+    if (M > kNT) return plan_ranges(M, K, d_v, B, T, H, in_bf16, state_bf16);  // rows in HBM
     const ChunkPlan f = plan_with(M, K, d_v, B, T, H, state_bf16, 4);
     if (!in_bf16) return f;
     const ChunkPlan r = plan_with(M, K, d_v, B, T, H, state_bf16, 2);
@@ -1306,12 +1201,13 @@ ChunkPlan plan_chunked(int64_t M, int K, int d_v, int B, int T, int H, bool in_b
 }
 
 size_t chunk_workspace_bytes(const ChunkPlan &p) {
-    return p.ws_rbuf + p.ws_sumsq + p.ws_mass + p.ws_plan;
+    return p.ws_rbuf + p.ws_sumsq + p.ws_mass + p.ws_plan + p.ws_partial + p.ws_spill;
 }
 
 hipError_t launch_scan_chunked(const ChunkArgs &args, hipStream_t st) {
     if (static_cast<int64_t>(args.B) * args.H * args.T == 0) return hipSuccess;
     if (!args.p.ok) return hipErrorInvalidValue;
+    if (!args.p.resident) return launch_scan_ranges(args, st);
     ChunkArgs a = args;
     if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
     if (a.ld_v > 0xffffffffll) return hipErrorInvalidValue;  // the scan's row steps are 32-bit

@@ -1,0 +1,899 @@
+// Slot-grouped prefill recurrence with the state rows in HBM (M > 1024),
+// for gfx950.
+//
+// RAM-Net project page, GPU-execution paragraphs: with every token's
+// addresses known, events are grouped by slot, each slot applies its own
+// events in causal order, different slots run in parallel and untouched
+// slots cost nothing.  The Gated Sparse Update and the read are those of the
+// "Gated Sparse Update" and "three stages" paragraphs.
+//
+// A unit's (batch, head) slots are split into kRanges ranges by slot mod
+// kRanges, and its sequence into chunks of C tokens.
+//
+// plan_range_kernel: one workgroup per (unit, chunk), all chunks at once
+// (grouping does not depend on the state).  Every valid event finds its
+// slot's entry in an LDS table; entries are numbered range by range, so that
+// each range's entries, its write list (in (slot, token) order, each write
+// with its retention alpha = (1 - w)^exp(gamma_t)), the versions its reads
+// see and its reads (grouped by token) are contiguous sections of the record.
+// A read sees the row before the chunk (version 0) or after the slot's i-th
+// write in the chunk; only versions some read sees get a row.
+//
+// scan_range_kernel: one workgroup per (unit, range), chunk after chunk.
+//   * The range's write and read lists and the chunk's value rows are staged
+//     in LDS (loaded one chunk ahead).
+//   * Walk: every touched slot's row is gathered whole from HBM, one 16-byte
+//     piece per lane, together with its mass (one request per row and one
+//     per mass).  The lanes of a slot each apply its writes to their piece
+//     (each computing the same mass and rate), store the versions reads see
+//     in LDS (later ones in a spill area) and write the row and mass back.
+//     A slot belongs to one range, so the mass is updated in place.
+//   * Reads: per token, four channels per lane, the range's reads summed in
+//     address order (rho * version); every token's partial (zero when the
+//     range holds none of its reads) goes to the workspace.
+// gate_partials_kernel: one wave per token-head adds the kRanges partials in
+// range order, then RMSNorm over d_v and the sigmoid gate.
+#include "chunk_common.h"
+#include "device_common.h"
+#include "launch.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace ramnet {
+namespace {
+
+// Address-space qualifiers for the version rows: LDS and global memory are
+// named in the pointer types, so that no access to them is generic (the
+// host pass sees plain pointers).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define RN_LDS __attribute__((address_space(3)))
+#define RN_GLB __attribute__((address_space(1)))
+#else
+#define RN_LDS
+#define RN_GLB
+#endif
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Four channels of storage type T as one vector access.
+template <typename T> struct Vec4Of;
+template <> struct Vec4Of<float> { using type = u32x4; };
+template <> struct Vec4Of<bf16_t> { using type = u32x2; };
+template <typename T> using VecOf = typename Vec4Of<T>::type;
+
+constexpr int kR = kRanges;
+// The scan kernel runs kRT threads per (unit, range): one workgroup per
+// compute unit at the benchmark's size, 16 waves to hide the latency of the
+// row gathers.
+constexpr int kRT = 1024;
+constexpr int kPTW = 5;  // walk tasks (16-byte row pieces) per scan thread and round
+constexpr int kLW = 1;   // list entries per kind and thread staged (CAPW = CAPR = kLW * kRT)
+
+__device__ __forceinline__ int range_of(int slot) { return slot & (kR - 1); }
+
+// LDS of the plan kernel (byte offsets).
+struct RPlanLds {
+    size_t key, cf, wo, bk, sk, sa, need, rg, rt, misc, total;
+};
+__host__ __device__ inline RPlanLds rplan_lds(const ChunkPlan &p, int64_t M) {
+    RPlanLds L{};
+    const size_t ht = p.HT ? static_cast<size_t>(p.HT) : static_cast<size_t>(M);
+    const size_t need = std::max<size_t>(static_cast<size_t>(p.ENT) + p.EV + 1, kR * kPT);
+    size_t o = 0;
+    L.key = o; o = al16(o + (p.HT ? ht * 4 : 0));                 // slot of a hash entry
+    L.cf = o; o = al16(o + ht * 4);                               // writes | read flag; entry id
+    L.wo = o; o = al16(o + static_cast<size_t>(p.ENT + 1) * 4);  // entry -> writes, then offset
+    L.bk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // writes, arrival order; staging
+    L.sk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // writes, causal order; staging
+    L.sa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // staging
+    L.need = o; o = al16(o + need * 4);                           // (range, thread) counts; versions read
+    L.rg = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // range of each read (-1: skipped)
+    L.rt = o; o = al16(o + static_cast<size_t>(kR * p.C + 1) * 4);  // reads per (range, token)
+    L.misc = o; o = al16(o + (32 + 3 * (kR + 1)) * 4);            // scan totals; range bases
+    L.total = o;
+    return L;
+}
+
+// Record header: per range r (and r = kR for the end), the first entry,
+// write, read and version row of the range.
+struct RangeHdr {
+    int ebase[kR + 1], wbase[kR + 1], rbase[kR + 1], vbase[kR + 1];
+};
+
+template <typename TIn, int EPW>
+__global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const ChunkPlan &P = a.p;
+    const int tid = threadIdx.x;
+    // the heads of one (sequence, chunk) are neighbours: their addresses
+    // share cache lines
+    const int h = static_cast<int>(blockIdx.x % a.H);
+    const int chunk = static_cast<int>((blockIdx.x / a.H) % P.n_chunks);
+    const int b = static_cast<int>(blockIdx.x / a.H / P.n_chunks);
+    const int unit = b * a.H + h;
+    const int C = P.C, t0 = chunk * C, Cc = min(C, a.T - t0);
+    const int K = a.K, nev = Cc * K;
+    const int M = static_cast<int>(a.M);
+    const bool hashed = P.HT != 0;
+    const int HT = hashed ? P.HT : M;
+    const int hsh = 32 - (__ffs(HT) - 1);  // hashed: HT is a power of two
+    const uint64_t kdiv = ((uint64_t(1) << 32) + K - 1) / K;
+    const RPlanLds L = rplan_lds(P, a.M);
+    int *tkey = reinterpret_cast<int *>(smem + L.key);
+    int *tcf = reinterpret_cast<int *>(smem + L.cf);
+    int *ewo = reinterpret_cast<int *>(smem + L.wo);
+    int *bk = reinterpret_cast<int *>(smem + L.bk);
+    int *sk = reinterpret_cast<int *>(smem + L.sk);
+    int *sa = reinterpret_cast<int *>(smem + L.sa);
+    int *need = reinterpret_cast<int *>(smem + L.need);
+    int *rg = reinterpret_cast<int *>(smem + L.rg);
+    int *rt = reinterpret_cast<int *>(smem + L.rt);
+    int *wtot = reinterpret_cast<int *>(smem + L.misc);
+    int *rs0 = wtot + 32;       // first entry id of range r, r <= kR
+    int *vb = rs0 + (kR + 1);   // first version row of range r, r <= kR
+
+    unsigned char *rec = a.plan + (static_cast<int64_t>(unit) * P.n_chunks + chunk) * P.rec_bytes;
+    RangeHdr *hdr = reinterpret_cast<RangeHdr *>(rec);
+    int *rtoff = reinterpret_cast<int *>(rec + P.o_rt);       // [kR][C + 1], per range
+    int *ent_slot = reinterpret_cast<int *>(rec + P.o_ent);  // per entry: slot, write offset,
+    int *ent_wo = ent_slot + P.ENTA;                          // writes, version-0 row
+    int *ent_nw = ent_wo + P.ENTA;
+    int *ent_x0 = ent_nw + P.ENTA;
+    int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
+    float *ww = reinterpret_cast<float *>(rec + P.o_ww);
+    float *wa = reinterpret_cast<float *>(rec + P.o_wa);
+    int *rv = reinterpret_cast<int *>(rec + P.o_rv);
+    float *rr = reinterpret_cast<float *>(rec + P.o_rr);
+    const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
+    const TIn *gam = static_cast<const TIn *>(a.gamma) + static_cast<int64_t>(b) * a.T * a.ld_gamma + h;
+
+    // ---- 0. this thread's events, e = tid + j * kPT (index t * K + k within
+    //         the chunk), writes and reads alike; the loads go out first
+    int ws[EPW], rs[EPW];
+    float wt[EPW], rtw[EPW], eg[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        const int e = tid + j * kPT;
+        ws[j] = -1;
+        rs[j] = -1;
+        if (e < nev) {
+            const int t = div_by(e, kdiv), k = e - t * K;
+            const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
+            const int64_t ai = (a.addr_unit_major ? static_cast<int64_t>(unit) * a.T + t0 + t : th) * K + k;
+            ws[j] = a.w_idx[ai];
+            wt[j] = a.w_wt[ai];
+            rs[j] = a.r_idx[ai];
+            rtw[j] = a.r_wt[ai];
+            eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
+        }
+    }
+    for (int i = tid; i < HT; i += kPT) {
+        tcf[i] = 0;
+        if (hashed) tkey[i] = -1;
+    }
+    for (int i = tid; i <= kR * C; i += kPT) rt[i] = 0;
+    lds_barrier();
+
+    // ---- 1. every event finds its slot's entry; writes count, reads flag
+    //         and count per (range, token).  A zero-weight write changes
+    //         nothing (alpha = 1, lambda = 0); a slot outside [0, M)
+    //         (caller-given addresses) is skipped, and a skipped read
+    //         contributes nothing.
+    auto entry_of = [&](int s) -> int {
+        if (!hashed) return s;
+        uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
+        for (;;) {  // linear probing; the table is at most 3/4 full
+            const int old = atomicCAS(&tkey[hp], -1, s);
+            if (old == -1 || old == s) return static_cast<int>(hp);
+            hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
+        }
+    };
+    int wpos[EPW], ar[EPW], rpos[EPW];
+    float al[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        const int e = tid + j * kPT;
+        wpos[j] = -1;
+        rpos[j] = -1;
+        ar[j] = 0;
+        al[j] = 0.f;
+        if (static_cast<uint32_t>(ws[j]) < static_cast<uint32_t>(M) && wt[j] > 0.f) {
+            wpos[j] = entry_of(ws[j]);
+            ar[j] = atomicAdd(&tcf[wpos[j]], 1) & (kReadFlag - 1);
+            al[j] = retention_fast(wt[j], expf(eg[j]));
+        }
+        if (static_cast<uint32_t>(rs[j]) < static_cast<uint32_t>(M)) {
+            rpos[j] = entry_of(rs[j]);
+            atomicOr(&tcf[rpos[j]], kReadFlag);
+            atomicAdd(&rt[range_of(rs[j]) * C + div_by(e, kdiv)], 1);
+            rg[e] = range_of(rs[j]);
+        } else if (e < nev) {
+            rg[e] = -1;
+        }
+    }
+    lds_barrier();
+
+    // ---- 2. entry ids, range by range: one scan of the (range, thread)
+    //         counts of touched table positions; each thread numbers its run
+    //         of positions in table order within each range.  The entry's
+    //         slot goes to the record; its write count to ewo.
+    const int per = (HT + kPT - 1) / kPT;
+    const int lo = min(tid * per, HT), hi = min(lo + per, HT);
+    {
+        int cnt[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) cnt[r] = 0;
+        for (int p = lo; p < hi; ++p) {
+            if (tcf[p]) {
+                const int sr = range_of(hashed ? tkey[p] : p);
+#pragma unroll
+                for (int r = 0; r < kR; ++r) cnt[r] += sr == r ? 1 : 0;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) need[r * kPT + tid] = cnt[r];
+    }
+    lds_barrier();
+    const int nt = block_scan_array<kPT>(need, kR * kPT, wtot);
+    lds_barrier();
+    {
+        int nxt[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) nxt[r] = need[r * kPT + tid];
+        for (int p = lo; p < hi; ++p) {
+            const int c = tcf[p];
+            int eid = -1;
+            if (c) {
+                const int slot = hashed ? tkey[p] : p;
+                const int sr = range_of(slot);
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    if (sr == r) eid = nxt[r]++;
+                ewo[eid] = c & (kReadFlag - 1);
+                ent_slot[eid] = slot;
+            }
+            tcf[p] = eid;  // -1: untouched
+        }
+        if (tid < kR) rs0[tid] = need[tid * kPT];
+        if (tid == 0) rs0[kR] = nt;
+    }
+    lds_barrier();
+    // write offsets in entry order (range by range)
+    const int nwt = block_scan_array<kPT>(ewo, nt, wtot);
+    lds_barrier();
+    if (tid == 0) ewo[nt] = nwt;
+    for (int i = tid; i <= nt + nwt; i += kPT) need[i] = 0;
+    lds_barrier();
+
+    // ---- 3. writes into their entries' buckets, arrival order ...
+#pragma unroll
+    for (int j = 0; j < EPW; ++j)
+        if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPT;
+    lds_barrier();
+    // ... then causal order: a write's rank is the number of the bucket's
+    // writes with a smaller event index (one write per slot and token)
+    int spos[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        spos[j] = -1;
+        if (wpos[j] >= 0) {
+            const int e = tid + j * kPT;
+            const int eid = tcf[wpos[j]];
+            const int wo = ewo[eid], n = ewo[eid + 1] - wo;
+            int r = 0;
+            for (int i = 0; i < n; ++i) r += bk[wo + i] < e ? 1 : 0;
+            spos[j] = wo + r;
+            sk[wo + r] = e;
+        }
+    }
+    lds_barrier();
+
+    // ---- 4. each read sees version c of its slot: c = the number of the
+    //         slot's writes at tokens <= its own (writes come first within a
+    //         token).  Entry eid's versions are numbered ewo[eid] + eid + c.
+    int gv[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        gv[j] = -1;
+        if (rpos[j] >= 0) {
+            const int eid = tcf[rpos[j]];
+            const int wo = ewo[eid], n = ewo[eid + 1] - wo;
+            const int tr = div_by(tid + j * kPT, kdiv);
+            int c = 0;
+            while (c < n && div_by(sk[wo + c], kdiv) <= tr) ++c;
+            gv[j] = wo + eid + c;
+            need[gv[j]] = 1;
+        }
+    }
+    lds_barrier();
+
+    // ---- 5. version rows: exclusive scan of the flags over nt + nwt + 1
+    //         positions (range by range, as the entries); version g has a row
+    //         iff need[g + 1] > need[g].  Range r's rows start at vb[r]; the
+    //         scan gives reads, per (range, token), their list offsets.
+    const int nver = block_scan_array<kPT>(need, nt + nwt + 1, wtot);
+    lds_barrier();
+    const int nrd = block_scan_array<kPT>(rt, kR * C, wtot);
+    lds_barrier();
+    if (tid <= kR) {
+        const int e0 = rs0[tid];
+        vb[tid] = tid < kR ? need[ewo[e0] + e0] : nver;
+    }
+    if (tid == 0) rt[kR * C] = nrd;
+    lds_barrier();
+
+    // ---- 6. the record: header, per-range token offsets of the reads,
+    //         entries, then writes and reads staged in LDS in list order and
+    //         stored with consecutive lanes on consecutive words
+    if (tid == 0) {
+        RangeHdr hd;
+        for (int r = 0; r <= kR; ++r) {
+            hd.ebase[r] = rs0[r];
+            hd.wbase[r] = ewo[rs0[r]];
+            hd.rbase[r] = r < kR ? rt[r * C] : nrd;
+            hd.vbase[r] = vb[r];
+        }
+        *hdr = hd;
+    }
+    for (int i = tid; i < kR * (C + 1); i += kPT) {
+        const int r = i / (C + 1), t = i - r * (C + 1);
+        rtoff[i] = rt[r * C + t] - rt[r * C];  // t == C: the next range's start (or nrd)
+    }
+    for (int eid = tid; eid < nt; eid += kPT) {
+        int r = 0;
+#pragma unroll
+        for (int q = 1; q < kR; ++q) r += eid >= rs0[q] ? 1 : 0;
+        const int g = ewo[eid] + eid;
+        ent_wo[eid] = ewo[eid];
+        ent_nw[eid] = ewo[eid + 1] - ewo[eid];
+        ent_x0[eid] = need[g + 1] > need[g] ? need[g] - vb[r] : -1;
+    }
+    // reads: list position and (range-local version row, weight)
+    int rp[EPW], rvv[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        rp[j] = -1;
+        if (gv[j] >= 0) {
+            const int e = tid + j * kPT;
+            const int t = div_by(e, kdiv), k = e - t * K;
+            const int r = range_of(rs[j]);
+            int rank = 0;
+            for (int q = 0; q < k; ++q) rank += rg[t * K + q] == r ? 1 : 0;
+            rp[j] = rt[r * C + t] + rank;
+            rvv[j] = need[gv[j]] - vb[r];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        if (spos[j] >= 0) {
+            const int e = tid + j * kPT;
+            const int eid = tcf[wpos[j]];
+            const int wo = ewo[eid];
+            const int g = wo + eid + (spos[j] - wo) + 1;  // version after this write
+            const int vr = need[g + 1] > need[g] ? need[g] - vb[range_of(ws[j])] : -1;
+            bk[spos[j]] = div_by(e, kdiv) | ((vr + 1) << 10);
+            sk[spos[j]] = __float_as_int(wt[j]);
+            sa[spos[j]] = __float_as_int(al[j]);
+        }
+    }
+    lds_barrier();
+    for (int i = tid; i < nwt; i += kPT) {
+        wtv[i] = bk[i];
+        ww[i] = __int_as_float(sk[i]);
+        wa[i] = __int_as_float(sa[i]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        if (rp[j] >= 0) {
+            bk[rp[j]] = rvv[j];
+            sk[rp[j]] = __float_as_int(rtw[j]);
+        }
+    }
+    lds_barrier();
+    for (int i = tid; i < nrd; i += kPT) {
+        rv[i] = bk[i];
+        rr[i] = __int_as_float(sk[i]);
+    }
+}
+
+// LDS of the scan kernel (byte offsets).
+struct RScanLds {
+    size_t v, wtv, wwa, rv, rr, rt, ver, total;
+};
+__host__ __device__ inline RScanLds rscan_lds(const ChunkPlan &p, int d_v, int sbytes, int vbytes) {
+    RScanLds L{};
+    size_t o = 0;
+    L.v = o; o = al16(o + static_cast<size_t>(p.C) * (d_v * vbytes + 16));  // values, rows padded by 16 B
+    L.wtv = o; o = al16(o + static_cast<size_t>(p.CAPW) * 4);                // write: token | version row
+    L.wwa = o; o = al16(o + static_cast<size_t>(p.CAPW) * 8);                // write: weight, retention
+    L.rv = o; o = al16(o + static_cast<size_t>(p.CAPR) * 4);                 // read: version row
+    L.rr = o; o = al16(o + static_cast<size_t>(p.CAPR) * 4);                 // read weight
+    L.rt = o; o = al16(o + static_cast<size_t>(p.C + 1) * 4);                // reads per token
+    L.ver = o = (o + 255) & ~size_t(255);
+    o += static_cast<size_t>(p.VCAP) * d_v * sbytes;                        // version rows
+    L.total = o;
+    return L;
+}
+
+// Four channels of a version row as fp32 (8 bytes of bf16, 16 of fp32).
+__device__ __forceinline__ void load4(const float *p, float (&x)[4]) {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    x[0] = f.x;
+    x[1] = f.y;
+    x[2] = f.z;
+    x[3] = f.w;
+}
+__device__ __forceinline__ void load4(const bf16_t *p, float (&x)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// The same from a version row in LDS or in the spill area (Q: the pointer's
+// address-space qualifier).
+template <typename Q>
+__device__ __forceinline__ void load4q(const Q *p, float (&x)[4], float) {
+    const u32x4 u = *p;
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
+}
+template <typename Q>
+__device__ __forceinline__ void load4q(const Q *p, float (&x)[4], bf16_t) {
+    const u32x2 u = *p;
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+// A 16-byte row piece (CP channels) from fp32 values into storage type T.
+__device__ __forceinline__ uint4 pack_piece(const float (&x)[4], float) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                      __float_as_uint(x[3]));
+}
+__device__ __forceinline__ uint4 pack_piece(const float (&x)[8], bf16_t) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        w[q] = static_cast<uint32_t>(bf16_rne(x[2 * q]).bits) |
+               (static_cast<uint32_t>(bf16_rne(x[2 * q + 1]).bits) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// VPT: value elements per thread and chunk (C * d_v / kRT, at most VPT).
+template <typename TIn, typename TS, int VPT>
+__global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const ChunkPlan &P = a.p;
+    const int tid = threadIdx.x;
+    const int units = a.B * a.H;
+    int unit, r;
+    {
+        const int bid = blockIdx.x;
+        if (units % 8 == 0) {  // the ranges of one unit on one XCD (they share value rows)
+            const int xcd = bid % 8, j = bid / 8;
+            unit = (j / kR) * 8 + xcd;
+            r = j % kR;
+        } else {
+            unit = bid / kR;
+            r = bid % kR;
+        }
+    }
+    const int b = unit / a.H, h = unit % a.H;
+    const int M = static_cast<int>(a.M);
+    const int d_v = a.d_v, C = P.C, EV = P.EV;
+    const int nchunks = static_cast<int>(P.n_chunks);
+    constexpr int CP = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
+    const int NP = d_v / CP;                                // pieces per row
+    const int RL = d_v / 4;                                 // read lanes per token
+    const int TPP = kRT / RL;                               // tokens per read pass
+    constexpr int VPAD = 16 / static_cast<int>(sizeof(TIn));
+    const int VROW = d_v + VPAD;                            // padded value row (elements)
+    const RScanLds L = rscan_lds(P, d_v, sizeof(TS), sizeof(TIn));
+    TIn *vbuf = reinterpret_cast<TIn *>(smem + L.v);
+    RN_LDS int *s_wtv = (RN_LDS int *)(smem + L.wtv);
+    RN_LDS f32x2 *s_wwa = (RN_LDS f32x2 *)(smem + L.wwa);
+    RN_LDS int *s_rv = (RN_LDS int *)(smem + L.rv);
+    RN_LDS float *s_rr = (RN_LDS float *)(smem + L.rr);
+    int *s_rt = reinterpret_cast<int *>(smem + L.rt);
+    // version rows in LDS and the spill area in global memory, with their
+    // address spaces in the type so that no access to either is generic
+    // rows of 16-byte pieces (u32x4) in LDS and in the spill area
+    RN_LDS unsigned char *ver = (RN_LDS unsigned char *)(smem + L.ver);
+    const int CAPW = P.CAPW, CAPR = P.CAPR, VCAP = P.VCAP;
+
+    TS *S = static_cast<TS *>(a.S) + static_cast<int64_t>(unit) * M * d_v;
+    float *mass = a.mass + static_cast<int64_t>(unit) * M;
+    RN_GLB unsigned char *spill =
+        (RN_GLB unsigned char *)(static_cast<TS *>(a.spill) + (static_cast<int64_t>(unit) * kR + r) * EV * d_v);
+    const int rowb = d_v * static_cast<int>(sizeof(TS));  // bytes per version row
+    const TIn *v = static_cast<const TIn *>(a.v) + static_cast<int64_t>(b) * a.T * a.ld_v + h * d_v;
+    const int64_t th_unit = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
+    const unsigned char *plan0 = a.plan + static_cast<int64_t>(unit) * P.n_chunks * P.rec_bytes;
+    auto rec_of = [&](int c) { return plan0 + static_cast<int64_t>(c) * P.rec_bytes; };
+
+    // Version row vr: the first VCAP rows in LDS, later ones in the spill
+    // area.  The two are separate branches so that each access is a plain
+    // LDS or global instruction (a pointer that may be either would be a
+    // generic access, which waits for every load in flight).
+    auto ver_store = [&](int vr, int c, const uint4 &u) {
+        const u32x4 w = {u.x, u.y, u.z, u.w};
+        const int off = c * static_cast<int>(sizeof(TS));
+        if (vr < VCAP) *reinterpret_cast<RN_LDS u32x4 *>(ver + vr * rowb + off) = w;
+        else *reinterpret_cast<RN_GLB u32x4 *>(spill + static_cast<int64_t>(vr) * rowb + off) = w;
+    };
+
+    // ---- the pipeline: chunk c + 1's lists, values and entries are loaded
+    //      during chunk c's walk, its rows right after chunk c's write-backs
+    //      (during chunk c's reads), and headers two chunks ahead
+    struct Hdr {
+        int eb, ne, wb, nw, rb, nr;
+    };
+    auto load_header = [&](int c) {
+        const RangeHdr *hd = reinterpret_cast<const RangeHdr *>(rec_of(c));
+        Hdr x;
+        x.eb = hd->ebase[r];
+        x.ne = hd->ebase[r + 1] - x.eb;
+        x.wb = hd->wbase[r];
+        x.nw = hd->wbase[r + 1] - x.wb;
+        x.rb = hd->rbase[r];
+        x.nr = hd->rbase[r + 1] - x.rb;
+        return x;
+    };
+    int pf_wtv[kLW], pf_rv[kLW], pf_rt = 0;
+    float pf_ww[kLW], pf_wa[kLW], pf_rr[kLW];
+    TIn pf_v[VPT];
+    const int vcol = tid % d_v, vrow0 = tid / d_v, vstep = kRT / d_v;
+    auto load_values = [&](int c) {
+        const int t0 = c * C, Cc = min(C, a.T - t0);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int t = vrow0 + j * vstep;  // element tid + j kRT of the chunk's [C][d_v]
+            if (t < C) pf_v[j] = v[static_cast<int64_t>(t0 + min(t, Cc - 1)) * a.ld_v + vcol];
+        }
+    };
+    auto load_lists = [&](int c, const Hdr &hd) {
+        const unsigned char *rec = rec_of(c);
+#pragma unroll
+        for (int j = 0; j < kLW; ++j) {
+            const int i = tid + j * kRT;
+            if (i < min(hd.nw, CAPW)) {
+                pf_wtv[j] = reinterpret_cast<const int *>(rec + P.o_wtv)[hd.wb + i];
+                pf_ww[j] = reinterpret_cast<const float *>(rec + P.o_ww)[hd.wb + i];
+                pf_wa[j] = reinterpret_cast<const float *>(rec + P.o_wa)[hd.wb + i];
+            }
+            if (i < min(hd.nr, CAPR)) {
+                pf_rv[j] = reinterpret_cast<const int *>(rec + P.o_rv)[hd.rb + i];
+                pf_rr[j] = reinterpret_cast<const float *>(rec + P.o_rr)[hd.rb + i];
+            }
+        }
+        if (tid <= C) pf_rt = reinterpret_cast<const int *>(rec + P.o_rt)[r * (C + 1) + tid];
+    };
+    // entries of walk tasks task0 + tid + j kRT (task = entry * NP + piece):
+    // slot, write offset, writes | (version-0 row + 1) << 16
+    struct Ent {
+        int slot[kPTW], wo[kPTW], nx[kPTW];
+    };
+    auto load_entries = [&](int c, int task0, const Hdr &hd, Ent &pe) {
+        const int *ent = reinterpret_cast<const int *>(rec_of(c) + P.o_ent);
+#pragma unroll
+        for (int j = 0; j < kPTW; ++j) {
+            const int e = (task0 + tid + j * kRT) / NP;
+            pe.nx[j] = 0;
+            if (e < hd.ne) {
+                const int eid = hd.eb + e;
+                pe.slot[j] = ent[eid];
+                pe.wo[j] = ent[P.ENTA + eid];
+                pe.nx[j] = ent[2 * P.ENTA + eid] | ((ent[3 * P.ENTA + eid] + 1) << 16);
+            }
+        }
+    };
+    // every row piece and mass of a round at once
+    struct Rows {
+        uint4 raw[kPTW];
+        float m[kPTW];
+    };
+    auto gather = [&](int task0, const Hdr &hd, const Ent &pe, Rows &rw) {
+#pragma unroll
+        for (int j = 0; j < kPTW; ++j) {
+            const int task = task0 + tid + j * kRT;
+            const int e = task / NP, piece = task - e * NP;
+            if (e < hd.ne) {
+                rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v +
+                                                             piece * CP);
+                if (pe.nx[j] & 0xffff) rw.m[j] = mass[pe.slot[j]];
+            }
+        }
+    };
+
+    Hdr h_cur = load_header(0), h_nxt{};
+    Ent pe;
+    Rows rw;
+    load_values(0);
+    load_lists(0, h_cur);
+    load_entries(0, 0, h_cur, pe);
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C, Cc = min(C, a.T - t0);
+        const Hdr hc = h_cur;
+        // ---- 1. stage the lists, token offsets and values
+#pragma unroll
+        for (int j = 0; j < kLW; ++j) {
+            const int i = tid + j * kRT;
+            if (i < min(hc.nw, CAPW)) {
+                s_wtv[i] = pf_wtv[j];
+                s_wwa[i] = f32x2{pf_ww[j], pf_wa[j]};
+            }
+            if (i < min(hc.nr, CAPR)) {
+                s_rv[i] = pf_rv[j];
+                s_rr[i] = pf_rr[j];
+            }
+        }
+        if (tid <= C) s_rt[tid] = pf_rt;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int t = vrow0 + j * vstep;
+            if (t < Cc) vbuf[t * VROW + vcol] = pf_v[j];
+        }
+        lds_barrier();
+        const unsigned char *rec = rec_of(c);
+        const RN_GLB int *g_wtv = (const RN_GLB int *)(rec + P.o_wtv) + hc.wb;
+        const RN_GLB float *g_ww = (const RN_GLB float *)(rec + P.o_ww) + hc.wb;
+        const RN_GLB float *g_wa = (const RN_GLB float *)(rec + P.o_wa) + hc.wb;
+        const RN_GLB int *g_rv = (const RN_GLB int *)(rec + P.o_rv) + hc.rb;
+        const RN_GLB float *g_rr = (const RN_GLB float *)(rec + P.o_rr) + hc.rb;
+        // ---- 2. chunk c + 1's header and values go out now
+        if (c + 1 < nchunks) {
+            h_nxt = load_header(c + 1);
+            load_values(c + 1);
+        }
+        // ---- 3. walk the range's touched slots, kRT * kPTW row pieces per
+        //         round: gather the round's pieces and masses at once, apply
+        //         the writes, store the versions reads see, write back
+        for (int task0 = 0; task0 < hc.ne * NP; task0 += kRT * kPTW) {
+            if (task0 > 0) load_entries(c, task0, hc, pe);
+            gather(task0, hc, pe, rw);
+#pragma unroll
+            for (int j = 0; j < kPTW; ++j) {
+                const int task = task0 + tid + j * kRT;
+                const int e = task / NP, piece = task - e * NP;
+                if (e >= hc.ne) continue;
+                float x[CP];
+                unpack_chunk(rw.raw[j], x);
+                const int x0 = (pe.nx[j] >> 16) - 1;
+                // (x holds stored values: packing them again gives the same bits)
+                if (x0 >= 0) ver_store(x0, piece * CP, pack_piece(x, TS{}));
+                const int n = pe.nx[j] & 0xffff;
+                if (n == 0) continue;
+                float m = rw.m[j];
+                const int i0 = pe.wo[j] - hc.wb;  // range-local write list index
+                for (int i = i0; i < i0 + n; ++i) {
+                    int tv;
+                    f32x2 wa;
+                    if (i < CAPW) {
+                        tv = s_wtv[i];
+                        wa = s_wwa[i];
+                    } else {
+                        tv = g_wtv[i];
+                        wa = f32x2{g_ww[i], g_wa[i]};
+                    }
+                    const int t = tv & 1023, vr = (tv >> 10) - 1;
+                    float vt[CP];
+                    value_part<CP>(vbuf, t * VROW + piece * CP, vt);
+                    m = fmaf(wa.y, m, wa.x);
+                    const float lam = wa.x * __builtin_amdgcn_rcpf(m + a.eps_gsu);
+#pragma unroll
+                    for (int q = 0; q < CP; ++q) x[q] = stored<TS>(fmaf(lam, vt[q] - x[q], x[q]));
+                    if (vr >= 0) ver_store(vr, piece * CP, pack_piece(x, TS{}));
+                }
+                *reinterpret_cast<uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v + piece * CP) =
+                    pack_piece(x, TS{});
+                if (piece == 0) mass[pe.slot[j]] = m;
+            }
+        }
+        // row write-backs and spilled versions visible to this workgroup
+        __syncthreads();
+        // ---- 4. chunk c + 1's lists and entries go out now and land during
+        //         the reads
+        if (c + 1 < nchunks) {
+            load_lists(c + 1, h_nxt);
+            load_entries(c + 1, 0, h_nxt, pe);
+        }
+        // ---- 5. reads: lane q of a token sums channels [4q, 4q + 4) over the
+        //         range's reads of that token in address order; the partial
+        //         (zero if none) goes to the workspace
+        for (int tb = 0; tb < Cc; tb += TPP) {
+            const int t = tb + tid / RL, q = tid % RL;
+            if (t < Cc) {
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                const int j1 = s_rt[t + 1];
+                for (int j = s_rt[t]; j < j1; ++j) {
+                    int vr;
+                    float rho;
+                    if (j < CAPR) {
+                        vr = s_rv[j];
+                        rho = s_rr[j];
+                    } else {
+                        vr = g_rv[j];
+                        rho = g_rr[j];
+                    }
+                    float x[4];
+                    const int off = 4 * q * static_cast<int>(sizeof(TS));
+                    if (vr < VCAP)
+                        load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
+                    else
+                        load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
+                               x, TS{});
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho, x[u], acc[u]);
+                }
+                const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
+                *reinterpret_cast<float4 *>(a.partial + (th * kR + r) * d_v + 4 * q) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        // LDS is restaged and the spill area rewritten by the next chunk
+        // (every load of this chunk's reads has been consumed by now)
+        lds_barrier();
+        h_cur = h_nxt;
+    }
+}
+
+// out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g) with r the sum of the
+// kRanges partials in range order; one wave per token-head, channel
+// c = lane + 64 i.
+template <typename TIn, typename TO>
+__global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restrict__ partial,
+                                                            const TIn *__restrict__ g, int H,
+                                                            int64_t ld_g,
+                                                            const float *__restrict__ norm_w,
+                                                            TO *__restrict__ out, int64_t n, int d_v,
+                                                            float eps) {
+    const int64_t th = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (th >= n) return;  // whole waves
+    const int nc = d_v / kWave;
+    float rv[4];
+    float ss = 0.f;
+    const float *pp = partial + th * kR * d_v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < nc) {
+            const int c = lane + kWave * i;
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < kR; ++q) s += pp[q * d_v + c];
+            rv[i] = s;
+            ss = fmaf(s, s, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const float den = ss / static_cast<float>(d_v) + eps;
+    const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
+    const TIn *gp = g + (th / H) * ld_g + (th % H) * d_v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < nc) {
+            const int c = lane + kWave * i;
+            const float om = norm_w ? norm_w[c] : 1.0f;
+            out[th * d_v + c] = from_f32<TO>(rv[i] * inv * om * sigmoid(to_f32(gp[c])));
+        }
+    }
+}
+
+template <typename K>
+hipError_t set_lds(K kern, size_t lds) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+}
+
+template <typename TIn, typename TS>
+hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
+    const ChunkPlan &P = a.p;
+    const int64_t units = static_cast<int64_t>(a.B) * a.H;
+    auto pk = P.EV <= 2048 ? plan_range_kernel<TIn, 2048 / kPT> : plan_range_kernel<TIn, 3072 / kPT>;
+    hipError_t e = set_lds(pk, P.lds_plan);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPT), P.lds_plan, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int vpt = (P.C * a.d_v + kRT - 1) / kRT;
+    auto sk = vpt <= 4 ? scan_range_kernel<TIn, TS, 4>
+            : vpt <= 8 ? scan_range_kernel<TIn, TS, 8> : scan_range_kernel<TIn, TS, 16>;
+    if ((e = set_lds(sk, P.lds_scan)) != hipSuccess) return e;
+    hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * kR)), dim3(kRT), P.lds_scan, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n = units * a.T;
+    const unsigned g2 = static_cast<unsigned>((n * kWave + 255) / 256);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((gate_partials_kernel<TIn, bf16_t>), dim3(g2), dim3(256), 0, st, a.partial,
+                           static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
+                           static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm);
+    else
+        hipLaunchKernelGGL((gate_partials_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.partial,
+                           static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
+                           static_cast<TS *>(a.out), n, a.d_v, a.eps_norm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf16, bool state_bf16) {
+    ChunkPlan p{};
+    p.ok = false;
+    const int sbytes = state_bf16 ? 2 : 4;
+    const int vbytes = in_bf16 ? 2 : 4;
+    const int64_t units = static_cast<int64_t>(B) * H;
+    // plan entries pack the token in 10 bits; rows are whole 16-byte pieces
+    if (T < 32 || units == 0 || K > 63 || M > (int64_t(1) << 22) || M < kR) return p;
+    // value rows and read lanes tile a workgroup: d_v divides kRT
+    if (d_v % 64 || d_v > 256 || kRT % d_v) return p;
+    p.resident = false;
+    ChunkPlan best{};
+    best.ok = false;
+    for (int C = 512; C >= 32; C -= 32) {
+        const int EV = C * K;
+        if (EV > kMaxEVHbm || static_cast<int64_t>(C) * d_v > 16 * kRT || C + 1 > kRT) continue;
+        ChunkPlan q = p;
+        q.C = C;
+        q.EV = EV;
+        q.CG = d_v;
+        q.ncg = 1;
+        q.ENT = static_cast<int>(std::min<int64_t>(M, 2 * EV));
+        q.HT = 0;
+        if (M > 4096) {  // hash table at most 3/4 full
+            int ht = 1;
+            while (ht * 3 < 2 * EV * 4) ht *= 2;
+            q.HT = ht;
+        }
+        q.CAPW = q.CAPR = std::min(EV, kLW * kRT);
+        q.VCAP = 0;
+        q.lds_plan = rplan_lds(q, M).total;
+        const size_t fixed = rscan_lds(q, d_v, sbytes, vbytes).total;
+        if (q.lds_plan > kChunkLdsLimit || fixed > kChunkLdsLimit) continue;
+        q.VCAP = static_cast<int>(std::min<size_t>(EV, (kChunkLdsLimit - fixed) / (static_cast<size_t>(d_v) * sbytes)));
+        q.lds_scan = rscan_lds(q, d_v, sbytes, vbytes).total;
+        q.n_chunks = (T + C - 1) / C;
+        q.ENTA = (q.ENT + 63) & ~63;
+        size_t o = al256(sizeof(RangeHdr));
+        q.o_rt = o; o += al256(static_cast<size_t>(kR) * (C + 1) * 4);
+        q.o_ent = o; o += al256(static_cast<size_t>(q.ENTA) * 16);
+        q.o_map = q.o_hl = o;
+        q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
+        q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
+        q.o_wa = o; o += al256(static_cast<size_t>(EV) * 4);
+        q.o_rv = o; o += al256(static_cast<size_t>(EV) * 4);
+        q.o_rr = o; o += al256(static_cast<size_t>(EV) * 4);
+        q.rec_bytes = o;
+        const size_t n = static_cast<size_t>(units) * T;
+        q.ws_rbuf = q.ws_sumsq = q.ws_mass = 0;
+        q.ws_plan = al256(static_cast<size_t>(units) * q.n_chunks * q.rec_bytes);
+        q.ws_partial = al256(n * kR * d_v * 4);
+        q.ws_spill = al256(static_cast<size_t>(units) * kR * EV * d_v * sbytes);
+        q.ok = true;
+        // the longest chunk whose typical versions per range (2 EV / kR)
+        // stay in LDS; else the longest that fits at all
+        if (!best.ok) best = q;
+        if (q.VCAP >= std::min(EV, 2 * EV / kR)) return q;
+    }
+    return best;
+}
+
+hipError_t launch_scan_ranges(const ChunkArgs &args, hipStream_t st) {
+    if (static_cast<int64_t>(args.B) * args.H * args.T == 0) return hipSuccess;
+    if (!args.p.ok || args.p.resident) return hipErrorInvalidValue;
+    ChunkArgs a = args;
+    if (!a.ld_v) a.ld_v = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_g) a.ld_g = static_cast<int64_t>(a.H) * a.d_v;
+    if (!a.ld_gamma) a.ld_gamma = a.H;
+    if (a.in_bf16)
+        return a.state_bf16 ? launch_ranges_typed<bf16_t, bf16_t>(a, st) : launch_ranges_typed<bf16_t, float>(a, st);
+    return a.state_bf16 ? launch_ranges_typed<float, bf16_t>(a, st) : launch_ranges_typed<float, float>(a, st);
+}
+
+}  // namespace ramnet
