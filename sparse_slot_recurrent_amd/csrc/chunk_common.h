@@ -20,13 +20,17 @@ constexpr int kReadFlag = 1 << 30;  // plan tables: a read touches the slot
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP moves only
+// (no LDS permutes): shifts right by 1, 2, 4 and 8 lanes within each row of
+// 16 (a lane whose source lies outside its row adds 0), then row 0's last
+// lane is added to row 1 and row 2's to row 3, and lane 31 to rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
     return x;
 }
 
@@ -65,6 +69,41 @@ __device__ int block_scan_array(int *a, int n, int *wtot) {
         const int c = a[i];
         a[i] = base;
         base += c;
+    }
+    return total;
+}
+
+// In-place exclusive scan of a[0, n) by a block of NT threads, returning the
+// sum.  Wave w takes the w-th contiguous segment of the array and reads it
+// 64 consecutive words at a time (lane i word i: no LDS bank conflicts),
+// carrying its running total from one group of 64 to the next.  Callers
+// synchronise before reading a.
+template <int NT>
+__device__ int block_scan_striped(int *a, int n, int *wtot) {
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const int per = (n + NT - 1) / NT;  // groups of 64 per wave
+    const int lo = min(wid * per * kWave, n), hi = min(lo + per * kWave, n);
+    int tot = 0;
+    for (int i = lo + lane; i < hi; i += kWave) tot += a[i];
+    tot = wave_incl_scan(tot);
+    if (lane == kWave - 1) wtot[wid] = tot;
+    lds_barrier();
+    if (wid == 0) {
+        int y = lane < NW ? wtot[lane] : 0;
+        y = wave_incl_scan(y);
+        if (lane < NW) wtot[lane] = y;
+    }
+    lds_barrier();
+    int carry = wid > 0 ? wtot[wid - 1] : 0;
+    const int total = wtot[NW - 1];
+    lds_barrier();
+    for (int g = lo; g < hi; g += kWave) {
+        const int i = g + lane;
+        const int x = i < hi ? a[i] : 0;
+        const int incl = wave_incl_scan(x);
+        if (i < hi) a[i] = carry + incl - x;
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     return total;
 }

@@ -91,7 +91,7 @@ __host__ __device__ inline RPlanLds rplan_lds(const ChunkPlan &p, int64_t M) {
     L.need = o; o = al16(o + need * 4);                           // (range, thread) counts; versions read
     L.rg = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // range of each read (-1: skipped)
     L.rt = o; o = al16(o + static_cast<size_t>(kR * p.C + 1) * 4);  // reads per (range, token)
-    L.misc = o; o = al16(o + (32 + 3 * (kR + 1)) * 4);            // scan totals; range bases
+    L.misc = o; o = al16(o + (32 + 3 * (kR + 1)) * 4);            // scan totals; range bases, counts
     L.total = o;
     return L;
 }
@@ -215,53 +215,75 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     }
     lds_barrier();
 
-    // ---- 2. entry ids, range by range: one scan of the (range, thread)
-    //         counts of touched table positions; each thread numbers its run
-    //         of positions in table order within each range.  The entry's
-    //         slot goes to the record; its write count to ewo.
-    const int per = (HT + kPT - 1) / kPT;
-    const int lo = min(tid * per, HT), hi = min(lo + per, HT);
+    // ---- 2. entry ids, range by range and, within a range, written slots
+    //         before read-only ones (so that the scan's waves take either
+    //         write chains or none): one scan of the (range, thread) counts
+    //         of touched table positions, written and read-only counts packed
+    //         in the low and high 16 bits.  Thread tid takes positions tid,
+    //         tid + kPT, ... (neighbouring lanes on neighbouring words) and
+    //         numbers its entries in that order.  The entry's slot goes to
+    //         the record; its write count to ewo.
+    int *rsum = vb + (kR + 1);  // packed counts of the ranges before r, r <= kR
+    const int nstep = (HT + kPT - 1) / kPT;
     {
         int cnt[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r) cnt[r] = 0;
-        for (int p = lo; p < hi; ++p) {
-            if (tcf[p]) {
+        for (int q = 0; q < nstep; ++q) {
+            const int p = tid + q * kPT;
+            const int c = p < HT ? tcf[p] : 0;
+            if (c) {
                 const int sr = range_of(hashed ? tkey[p] : p);
+                const int inc = (c & (kReadFlag - 1)) ? 1 : 0x10000;
 #pragma unroll
-                for (int r = 0; r < kR; ++r) cnt[r] += sr == r ? 1 : 0;
+                for (int r = 0; r < kR; ++r) cnt[r] += sr == r ? inc : 0;
             }
         }
 #pragma unroll
         for (int r = 0; r < kR; ++r) need[r * kPT + tid] = cnt[r];
     }
     lds_barrier();
-    const int nt = block_scan_array<kPT>(need, kR * kPT, wtot);
+    const int ptot = block_scan_striped<kPT>(need, kR * kPT, wtot);
     lds_barrier();
+    if (tid <= kR) rsum[tid] = tid < kR ? need[tid * kPT] : ptot;
+    lds_barrier();
+    const int nt = (ptot & 0xffff) + (ptot >> 16);
     {
-        int nxt[kR];
+        int nx0[kR], nx1[kR];  // this thread's next written / read-only id per range
 #pragma unroll
-        for (int r = 0; r < kR; ++r) nxt[r] = need[r * kPT + tid];
-        for (int p = lo; p < hi; ++p) {
+        for (int r = 0; r < kR; ++r) {
+            const int pr = rsum[r], pn = rsum[r + 1], mine = need[r * kPT + tid];
+            const int base = (pr & 0xffff) + (pr >> 16);          // entries of earlier ranges
+            const int wr = (pn & 0xffff) - (pr & 0xffff);          // written entries of range r
+            nx0[r] = base + (mine & 0xffff) - (pr & 0xffff);
+            nx1[r] = base + wr + (mine >> 16) - (pr >> 16);
+        }
+        for (int q = 0; q < nstep; ++q) {
+            const int p = tid + q * kPT;
+            if (p >= HT) break;
             const int c = tcf[p];
             int eid = -1;
             if (c) {
                 const int slot = hashed ? tkey[p] : p;
                 const int sr = range_of(slot);
+                const bool written = (c & (kReadFlag - 1)) != 0;
 #pragma unroll
-                for (int r = 0; r < kR; ++r)
-                    if (sr == r) eid = nxt[r]++;
+                for (int r = 0; r < kR; ++r) {
+                    if (sr == r) {
+                        if (written) eid = nx0[r]++;
+                        else eid = nx1[r]++;
+                    }
+                }
                 ewo[eid] = c & (kReadFlag - 1);
                 ent_slot[eid] = slot;
             }
             tcf[p] = eid;  // -1: untouched
         }
-        if (tid < kR) rs0[tid] = need[tid * kPT];
-        if (tid == 0) rs0[kR] = nt;
+        if (tid <= kR) rs0[tid] = (rsum[tid] & 0xffff) + (rsum[tid] >> 16);
     }
     lds_barrier();
     // write offsets in entry order (range by range)
-    const int nwt = block_scan_array<kPT>(ewo, nt, wtot);
+    const int nwt = block_scan_striped<kPT>(ewo, nt, wtot);
     lds_barrier();
     if (tid == 0) ewo[nt] = nwt;
     for (int i = tid; i <= nt + nwt; i += kPT) need[i] = 0;
@@ -313,9 +335,9 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     //         positions (range by range, as the entries); version g has a row
     //         iff need[g + 1] > need[g].  Range r's rows start at vb[r]; the
     //         scan gives reads, per (range, token), their list offsets.
-    const int nver = block_scan_array<kPT>(need, nt + nwt + 1, wtot);
+    const int nver = block_scan_striped<kPT>(need, nt + nwt + 1, wtot);
     lds_barrier();
-    const int nrd = block_scan_array<kPT>(rt, kR * C, wtot);
+    const int nrd = block_scan_striped<kPT>(rt, kR * C, wtot);
     lds_barrier();
     if (tid <= kR) {
         const int e0 = rs0[tid];
@@ -492,6 +514,11 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     const int nchunks = static_cast<int>(P.n_chunks);
     constexpr int CP = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
     const int NP = d_v / CP;                                // pieces per row
+    // entry of a walk task (task = entry * NP + piece): a shift when NP is a
+    // power of two (d_v 64, 128, 256)
+    const int lnp = __ffs(NP) - 1;
+    const bool np_pow2 = (NP & (NP - 1)) == 0;
+    auto entry_of_task = [&](int task) { return np_pow2 ? task >> lnp : task / NP; };
     const int RL = d_v / 4;                                 // read lanes per token
     const int TPP = kRT / RL;                               // tokens per read pass
     constexpr int VPAD = 16 / static_cast<int>(sizeof(TIn));
@@ -585,7 +612,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         const int *ent = reinterpret_cast<const int *>(rec_of(c) + P.o_ent);
 #pragma unroll
         for (int j = 0; j < kPTW; ++j) {
-            const int e = (task0 + tid + j * kRT) / NP;
+            const int e = entry_of_task(task0 + tid + j * kRT);
             pe.nx[j] = 0;
             if (e < hd.ne) {
                 const int eid = hd.eb + e;
@@ -604,7 +631,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < kPTW; ++j) {
             const int task = task0 + tid + j * kRT;
-            const int e = task / NP, piece = task - e * NP;
+            const int e = entry_of_task(task), piece = task - e * NP;
             if (e < hd.ne) {
                 rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v +
                                                              piece * CP);
@@ -662,7 +689,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 #pragma unroll
             for (int j = 0; j < kPTW; ++j) {
                 const int task = task0 + tid + j * kRT;
-                const int e = task / NP, piece = task - e * NP;
+                const int e = entry_of_task(task), piece = task - e * NP;
                 if (e >= hc.ne) continue;
                 float x[CP];
                 unpack_chunk(rw.raw[j], x);
