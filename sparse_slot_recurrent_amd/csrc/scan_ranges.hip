@@ -77,17 +77,21 @@ __device__ __forceinline__ int range_of(int slot) { return slot & (kR - 1); }
 struct RPlanLds {
     size_t key, cf, wo, bk, sk, sa, need, rg, rt, misc, total;
 };
+// The plan kernel of the HBM-row path runs kPRT threads.
+constexpr int kPRT = 1024;
 __host__ __device__ inline RPlanLds rplan_lds(const ChunkPlan &p, int64_t M) {
     RPlanLds L{};
     const size_t ht = p.HT ? static_cast<size_t>(p.HT) : static_cast<size_t>(M);
-    const size_t need = std::max<size_t>(static_cast<size_t>(p.ENT) + p.EV + 1, kR * kPT);
+    const size_t need = std::max<size_t>(static_cast<size_t>(p.ENT) + p.EV + 1, kR * kPRT);
+    const size_t ev = al16(static_cast<size_t>(p.EV) * 4);
     size_t o = 0;
-    L.key = o; o = al16(o + (p.HT ? ht * 4 : 0));                 // slot of a hash entry
+    // the hash keys are dead once the entries are numbered (step 2); the
+    // write lists (bk, sk, sa: step 3 on) share their space
+    L.key = o;                                                    // slot of a hash entry
+    L.bk = o; L.sk = o + ev; L.sa = o + 2 * ev;                   // writes: arrival, causal order; staging
+    o = al16(o + std::max<size_t>(p.HT ? ht * 4 : 0, 3 * ev));
     L.cf = o; o = al16(o + ht * 4);                               // writes | read flag; entry id
     L.wo = o; o = al16(o + static_cast<size_t>(p.ENT + 1) * 4);  // entry -> writes, then offset
-    L.bk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // writes, arrival order; staging
-    L.sk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // writes, causal order; staging
-    L.sa = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // staging
     L.need = o; o = al16(o + need * 4);                           // (range, thread) counts; versions read
     L.rg = o; o = al16(o + static_cast<size_t>(p.EV) * 4);        // range of each read (-1: skipped)
     L.rt = o; o = al16(o + static_cast<size_t>(kR * p.C + 1) * 4);  // reads per (range, token)
@@ -103,7 +107,7 @@ struct RangeHdr {
 };
 
 template <typename TIn, int EPW>
-__global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
     const int tid = threadIdx.x;
@@ -149,13 +153,13 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
     const TIn *gam = static_cast<const TIn *>(a.gamma) + static_cast<int64_t>(b) * a.T * a.ld_gamma + h;
 
-    // ---- 0. this thread's events, e = tid + j * kPT (index t * K + k within
+    // ---- 0. this thread's events, e = tid + j * kPRT (index t * K + k within
     //         the chunk), writes and reads alike; the loads go out first
     int ws[EPW], rs[EPW];
     float wt[EPW], rtw[EPW], eg[EPW];
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
-        const int e = tid + j * kPT;
+        const int e = tid + j * kPRT;
         ws[j] = -1;
         rs[j] = -1;
         if (e < nev) {
@@ -169,11 +173,11 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
             eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
         }
     }
-    for (int i = tid; i < HT; i += kPT) {
+    for (int i = tid; i < HT; i += kPRT) {
         tcf[i] = 0;
         if (hashed) tkey[i] = -1;
     }
-    for (int i = tid; i <= kR * C; i += kPT) rt[i] = 0;
+    for (int i = tid; i <= kR * C; i += kPRT) rt[i] = 0;
     lds_barrier();
 
     // ---- 1. every event finds its slot's entry; writes count, reads flag
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     float al[EPW];
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
-        const int e = tid + j * kPT;
+        const int e = tid + j * kPRT;
         wpos[j] = -1;
         rpos[j] = -1;
         ar[j] = 0;
@@ -220,17 +224,17 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     //         write chains or none): one scan of the (range, thread) counts
     //         of touched table positions, written and read-only counts packed
     //         in the low and high 16 bits.  Thread tid takes positions tid,
-    //         tid + kPT, ... (neighbouring lanes on neighbouring words) and
+    //         tid + kPRT, ... (neighbouring lanes on neighbouring words) and
     //         numbers its entries in that order.  The entry's slot goes to
     //         the record; its write count to ewo.
     int *rsum = vb + (kR + 1);  // packed counts of the ranges before r, r <= kR
-    const int nstep = (HT + kPT - 1) / kPT;
+    const int nstep = (HT + kPRT - 1) / kPRT;
     {
         int cnt[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r) cnt[r] = 0;
         for (int q = 0; q < nstep; ++q) {
-            const int p = tid + q * kPT;
+            const int p = tid + q * kPRT;
             const int c = p < HT ? tcf[p] : 0;
             if (c) {
                 const int sr = range_of(hashed ? tkey[p] : p);
@@ -240,26 +244,26 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
             }
         }
 #pragma unroll
-        for (int r = 0; r < kR; ++r) need[r * kPT + tid] = cnt[r];
+        for (int r = 0; r < kR; ++r) need[r * kPRT + tid] = cnt[r];
     }
     lds_barrier();
-    const int ptot = block_scan_striped<kPT>(need, kR * kPT, wtot);
+    const int ptot = block_scan_striped<kPRT>(need, kR * kPRT, wtot);
     lds_barrier();
-    if (tid <= kR) rsum[tid] = tid < kR ? need[tid * kPT] : ptot;
+    if (tid <= kR) rsum[tid] = tid < kR ? need[tid * kPRT] : ptot;
     lds_barrier();
     const int nt = (ptot & 0xffff) + (ptot >> 16);
     {
         int nx0[kR], nx1[kR];  // this thread's next written / read-only id per range
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
-            const int pr = rsum[r], pn = rsum[r + 1], mine = need[r * kPT + tid];
+            const int pr = rsum[r], pn = rsum[r + 1], mine = need[r * kPRT + tid];
             const int base = (pr & 0xffff) + (pr >> 16);          // entries of earlier ranges
             const int wr = (pn & 0xffff) - (pr & 0xffff);          // written entries of range r
             nx0[r] = base + (mine & 0xffff) - (pr & 0xffff);
             nx1[r] = base + wr + (mine >> 16) - (pr >> 16);
         }
         for (int q = 0; q < nstep; ++q) {
-            const int p = tid + q * kPT;
+            const int p = tid + q * kPRT;
             if (p >= HT) break;
             const int c = tcf[p];
             int eid = -1;
@@ -283,16 +287,16 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     }
     lds_barrier();
     // write offsets in entry order (range by range)
-    const int nwt = block_scan_striped<kPT>(ewo, nt, wtot);
+    const int nwt = block_scan_striped<kPRT>(ewo, nt, wtot);
     lds_barrier();
     if (tid == 0) ewo[nt] = nwt;
-    for (int i = tid; i <= nt + nwt; i += kPT) need[i] = 0;
+    for (int i = tid; i <= nt + nwt; i += kPRT) need[i] = 0;
     lds_barrier();
 
     // ---- 3. writes into their entries' buckets, arrival order ...
 #pragma unroll
     for (int j = 0; j < EPW; ++j)
-        if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPT;
+        if (wpos[j] >= 0) bk[ewo[tcf[wpos[j]]] + ar[j]] = tid + j * kPRT;
     lds_barrier();
     // ... then causal order: a write's rank is the number of the bucket's
     // writes with a smaller event index (one write per slot and token)
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     for (int j = 0; j < EPW; ++j) {
         spos[j] = -1;
         if (wpos[j] >= 0) {
-            const int e = tid + j * kPT;
+            const int e = tid + j * kPRT;
             const int eid = tcf[wpos[j]];
             const int wo = ewo[eid], n = ewo[eid + 1] - wo;
             int r = 0;
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
         if (rpos[j] >= 0) {
             const int eid = tcf[rpos[j]];
             const int wo = ewo[eid], n = ewo[eid + 1] - wo;
-            const int tr = div_by(tid + j * kPT, kdiv);
+            const int tr = div_by(tid + j * kPRT, kdiv);
             int c = 0;
             while (c < n && div_by(sk[wo + c], kdiv) <= tr) ++c;
             gv[j] = wo + eid + c;
@@ -335,9 +339,9 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     //         positions (range by range, as the entries); version g has a row
     //         iff need[g + 1] > need[g].  Range r's rows start at vb[r]; the
     //         scan gives reads, per (range, token), their list offsets.
-    const int nver = block_scan_striped<kPT>(need, nt + nwt + 1, wtot);
+    const int nver = block_scan_striped<kPRT>(need, nt + nwt + 1, wtot);
     lds_barrier();
-    const int nrd = block_scan_striped<kPT>(rt, kR * C, wtot);
+    const int nrd = block_scan_striped<kPRT>(rt, kR * C, wtot);
     lds_barrier();
     if (tid <= kR) {
         const int e0 = rs0[tid];
@@ -359,11 +363,11 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
         }
         *hdr = hd;
     }
-    for (int i = tid; i < kR * (C + 1); i += kPT) {
+    for (int i = tid; i < kR * (C + 1); i += kPRT) {
         const int r = i / (C + 1), t = i - r * (C + 1);
         rtoff[i] = rt[r * C + t] - rt[r * C];  // t == C: the next range's start (or nrd)
     }
-    for (int eid = tid; eid < nt; eid += kPT) {
+    for (int eid = tid; eid < nt; eid += kPRT) {
         int r = 0;
 #pragma unroll
         for (int q = 1; q < kR; ++q) r += eid >= rs0[q] ? 1 : 0;
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
     for (int j = 0; j < EPW; ++j) {
         rp[j] = -1;
         if (gv[j] >= 0) {
-            const int e = tid + j * kPT;
+            const int e = tid + j * kPRT;
             const int t = div_by(e, kdiv), k = e - t * K;
             const int r = range_of(rs[j]);
             int rank = 0;
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
         if (spos[j] >= 0) {
-            const int e = tid + j * kPT;
+            const int e = tid + j * kPRT;
             const int eid = tcf[wpos[j]];
             const int wo = ewo[eid];
             const int g = wo + eid + (spos[j] - wo) + 1;  // version after this write
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
         }
     }
     lds_barrier();
-    for (int i = tid; i < nwt; i += kPT) {
+    for (int i = tid; i < nwt; i += kPRT) {
         wtv[i] = bk[i];
         ww[i] = __int_as_float(sk[i]);
         wa[i] = __int_as_float(sa[i]);
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kPT) void plan_range_kernel(ChunkArgs a) {
         }
     }
     lds_barrier();
-    for (int i = tid; i < nrd; i += kPT) {
+    for (int i = tid; i < nrd; i += kPRT) {
         rv[i] = bk[i];
         rr[i] = __int_as_float(sk[i]);
     }
@@ -824,10 +828,10 @@ template <typename TIn, typename TS>
 hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
     const ChunkPlan &P = a.p;
     const int64_t units = static_cast<int64_t>(a.B) * a.H;
-    auto pk = P.EV <= 2048 ? plan_range_kernel<TIn, 2048 / kPT> : plan_range_kernel<TIn, 3072 / kPT>;
+    auto pk = P.EV <= 2048 ? plan_range_kernel<TIn, 2048 / kPRT> : plan_range_kernel<TIn, 3072 / kPRT>;
     hipError_t e = set_lds(pk, P.lds_plan);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPT), P.lds_plan, st, a);
+    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPRT), P.lds_plan, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int vpt = (P.C * a.d_v + kRT - 1) / kRT;
     auto sk = vpt <= 4 ? scan_range_kernel<TIn, TS, 4>
