@@ -88,6 +88,7 @@ struct ChunkPlan {
     // lists are read from the record), and the version rows held in LDS
     // (later ones go to a spill area in the workspace)
     int CAPW, CAPR, VCAP;
+    int MSL;  // > 0: the masses of a range's slots (M / kRanges) live in LDS for the whole scan
     // one (unit, chunk) plan record and its sections (byte offsets)
     size_t rec_bytes, o_ent, o_map, o_hl, o_wtv, o_ww, o_wa, o_rv, o_rr, o_rt;
     size_t lds_plan, lds_scan;

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
 
 // LDS of the scan kernel (byte offsets).
 struct RScanLds {
-    size_t v, wtv, wwa, rv, rr, rt, ver, total;
+    size_t v, wtv, wwa, rv, rr, rt, ms, ver, total;
 };
 __host__ __device__ inline RScanLds rscan_lds(const ChunkPlan &p, int d_v, int sbytes, int vbytes) {
     RScanLds L{};
@@ -438,6 +438,7 @@ __host__ __device__ inline RScanLds rscan_lds(const ChunkPlan &p, int d_v, int s
     L.rv = o; o = al16(o + static_cast<size_t>(p.CAPR) * 4);                 // read: version row
     L.rr = o; o = al16(o + static_cast<size_t>(p.CAPR) * 4);                 // read weight
     L.rt = o; o = al16(o + static_cast<size_t>(p.C + 1) * 4);                // reads per token
+    L.ms = o; o = al16(o + static_cast<size_t>(p.MSL) * 4);                  // the range's masses
     L.ver = o = (o + 255) & ~size_t(255);
     o += static_cast<size_t>(p.VCAP) * d_v * sbytes;                        // version rows
     L.total = o;
@@ -533,6 +534,8 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     RN_LDS f32x2 *s_wwa = (RN_LDS f32x2 *)(smem + L.wwa);
     RN_LDS int *s_rv = (RN_LDS int *)(smem + L.rv);
     RN_LDS float *s_rr = (RN_LDS float *)(smem + L.rr);
+    RN_LDS float *ms = (RN_LDS float *)(smem + L.ms);  // mass of slot s: ms[s / kR] (MSL > 0)
+    const int MSL = P.MSL;
     int *s_rt = reinterpret_cast<int *>(smem + L.rt);
     // version rows in LDS and the spill area in global memory, with their
     // address spaces in the type so that no access to either is generic
@@ -639,11 +642,17 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             if (e < hd.ne) {
                 rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v +
                                                              piece * CP);
-                if (pe.nx[j] & 0xffff) rw.m[j] = mass[pe.slot[j]];
+                if (!MSL && (pe.nx[j] & 0xffff)) rw.m[j] = mass[pe.slot[j]];
             }
         }
     };
 
+    // the range's masses, in LDS for the whole sequence where they fit (they
+    // are seen by the first staging barrier)
+    for (int i = tid; i < MSL; i += kRT) {
+        const int slot = i * kR + r;
+        ms[i] = slot < M ? mass[slot] : 0.f;
+    }
     Hdr h_cur = load_header(0), h_nxt{};
     Ent pe;
     Rows rw;
@@ -702,7 +711,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 if (x0 >= 0) ver_store(x0, piece * CP, pack_piece(x, TS{}));
                 const int n = pe.nx[j] & 0xffff;
                 if (n == 0) continue;
-                float m = rw.m[j];
+                float m = MSL ? ms[pe.slot[j] / kR] : rw.m[j];
                 const int i0 = pe.wo[j] - hc.wb;  // range-local write list index
                 for (int i = i0; i < i0 + n; ++i) {
                     int tv;
@@ -725,7 +734,10 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 }
                 *reinterpret_cast<uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v + piece * CP) =
                     pack_piece(x, TS{});
-                if (piece == 0) mass[pe.slot[j]] = m;
+                if (piece == 0) {
+                    if (MSL) ms[pe.slot[j] / kR] = m;
+                    else mass[pe.slot[j]] = m;
+                }
             }
         }
         // row write-backs and spilled versions visible to this workgroup
@@ -773,6 +785,10 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         // (every load of this chunk's reads has been consumed by now)
         lds_barrier();
         h_cur = h_nxt;
+    }
+    for (int i = tid; i < MSL; i += kRT) {
+        const int slot = i * kR + r;
+        if (slot < M) mass[slot] = ms[i];
     }
 }
 
@@ -835,6 +851,7 @@ hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int vpt = (P.C * a.d_v + kRT - 1) / kRT;
     auto sk = vpt <= 4 ? scan_range_kernel<TIn, TS, 4>
+            : vpt <= 6 ? scan_range_kernel<TIn, TS, 6>
             : vpt <= 8 ? scan_range_kernel<TIn, TS, 8> : scan_range_kernel<TIn, TS, 16>;
     if ((e = set_lds(sk, P.lds_scan)) != hipSuccess) return e;
     hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * kR)), dim3(kRT), P.lds_scan, st, a);
@@ -884,6 +901,8 @@ ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf
         }
         q.CAPW = q.CAPR = std::min(EV, kLW * kRT);
         q.VCAP = 0;
+        // the range's masses stay in LDS where they take at most 32 KiB
+        q.MSL = (M + kR - 1) / kR * 4 <= 32 * 1024 ? static_cast<int>((M + kR - 1) / kR) : 0;
         q.lds_plan = rplan_lds(q, M).total;
         const size_t fixed = rscan_lds(q, d_v, sbytes, vbytes).total;
         if (q.lds_plan > kChunkLdsLimit || fixed > kChunkLdsLimit) continue;
@@ -910,7 +929,7 @@ ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf
         // the longest chunk whose typical versions per range (2 EV / kR)
         // stay in LDS; else the longest that fits at all
         if (!best.ok) best = q;
-        if (q.VCAP >= std::min(EV, 2 * EV / kR)) return q;
+        if (q.VCAP >= std::min(EV, 3 * EV / (2 * kR))) return q;
     }
     return best;
 }
