@@ -55,10 +55,11 @@ hipError_t launch_scan_serial(const ScanArgs &a, hipStream_t st);
 
 // Slot-grouped chunked recurrence, in three kernels: a plan kernel groups
 // every chunk's events by slot (all chunks at once, they do not depend on
-// the state), the scan kernel replays the plans chunk after chunk for one
-// (unit, channel slice) per workgroup, and an epilogue applies RMSNorm and
-// the gate.  r (fp32 [B,T,H,d_v]) and per-slice square sums ([B,T,H,d_v/CG])
-// pass through global memory between the last two.
+// the state), the scan kernel replays the plans chunk after chunk, and an
+// epilogue applies RMSNorm and the gate.  Rows on chip (M <= 1024,
+// scan_chunked.hip): one workgroup per (unit, channel slice); r (fp32
+// [B,T,H,d_v]) and per-slice square sums ([B,T,H,d_v/CG]) pass through
+// global memory between the last two.
 // Rows in HBM (M > 1024): the slot-range path (scan_ranges.hip).  The slots
 // of a unit are split into kRanges ranges (slot mod kRanges); one workgroup
 // per (unit, range) gathers, updates and writes back whole rows of its
@@ -68,13 +69,13 @@ constexpr int kRanges = 8;
 
 struct ChunkPlan {
     bool ok;
-    bool resident;      // slot rows live in registers (M <= 1024); else in HBM
+    bool resident;      // slot rows live in registers (M <= 1024); else in HBM (slot ranges)
     int CG;             // channels per slice
     int C;              // tokens per chunk
     int EV;             // C * K: events of one kind per chunk
     int ENT;            // most slots one chunk touches
     int ENTA;           // ENT rounded up to 64 (stride of the entry arrays)
-    int HT;             // plan hash table size, 0: the slot is its own index
+    int HT;             // rows in HBM: plan hash table size, 0: the slot is its own index
     int ncg;            // d_v / CG
     int RG;             // lanes per token in the read reduction
     bool raw_values;    // values kept in LDS as the bf16 input (else fp32)

@@ -1,4 +1,6 @@
-// Slot-grouped prefill recurrence for gfx950.
+// Slot-grouped prefill recurrence for gfx950, with every slot row on chip
+// (M <= 1024 slots: one scan thread per slot).  Rows in HBM (more slots)
+// take the slot-range path of scan_ranges.hip.
 //
 // RAM-Net project page, GPU-execution paragraphs: with every token's
 // addresses known, events are grouped by slot, each slot applies its own
@@ -11,8 +13,8 @@
 // plan_kernel: one workgroup per (unit, chunk), all chunks at once, since
 // grouping does not depend on the state.
 //   * Every valid write (slot in [0, M), weight > 0) and read (slot in
-//     [0, M)) finds its slot's entry in a table (the slot itself when M is
-//     small, else an LDS hash table); entries count their writes.
+//     [0, M)) finds its slot's entry in an LDS table indexed by slot;
+//     entries count their writes.
 //   * Entries are numbered in table order and given the offsets of their
 //     write lists; writes are bucketed, then put in causal order by counting
 //     the bucket's earlier tokens.  Each write gets its retention
@@ -30,11 +32,9 @@
 //     ahead into registers).
 //   * The owner of each touched slot stores version 0 if a read sees it,
 //     then applies the slot's writes in order (mass, lambda, row), storing
-//     the versions reads see.  With M <= 1024, thread s owns slot s and keeps
-//     its row slice and mass in registers for the whole sequence; for larger
-//     M the touched rows are gathered from HBM and written back, and each
-//     slice keeps its own copy of the mass.
-//   * Hand-off (rows on chip): a listed slot's owner applies its first n0
+//     the versions reads see.  Thread s owns slot s and keeps its row slice
+//     and mass in registers for the whole sequence.
+//   * Hand-off: a listed slot's owner applies its first n0
 //     writes and parks the row in a free version row; a helper, one lane per
 //     16-byte piece of the row, applies the rest; the owner takes it back.
 //     A wave then no longer waits for its busiest slot's whole chain.
@@ -54,7 +54,6 @@
 namespace ramnet {
 namespace {
 
-constexpr int kEPN = 2 * kMaxEVHbm / kNT;           // touched slots per thread (HBM rows)
 constexpr int kHBins = 32;                          // write-count bins of the hand-off order
 
 // LDS rows are stored in 16-byte chunks whose order is XOR-swizzled by the
@@ -119,13 +118,12 @@ __device__ __forceinline__ void store_row(bf16_t *p, int swz, const float (&x)[C
 
 // LDS of the plan kernel (byte offsets).
 struct PlanLds {
-    size_t key, cf, wo, bk, sk, sa, need, wtot, hist, total;
+    size_t cf, wo, bk, sk, sa, need, wtot, hist, total;
 };
 __host__ __device__ inline PlanLds plan_lds(const ChunkPlan &p, int64_t M) {
     PlanLds L{};
-    const size_t ht = p.HT ? static_cast<size_t>(p.HT) : static_cast<size_t>(M);
+    const size_t ht = static_cast<size_t>(M);  // the table is indexed by slot
     size_t o = 0;
-    L.key = o; o = al16(o + (p.HT ? ht * 4 : 0));                         // slot of a hash entry
     L.cf = o; o = al16(o + ht * 4);                                       // writes | read flag; entry id
     L.wo = o; o = al16(o + static_cast<size_t>(p.ENT + 1) * 4);          // entry -> write offset
     L.bk = o; o = al16(o + static_cast<size_t>(p.EV) * 4);                // writes, arrival order
@@ -143,7 +141,7 @@ struct PlanHdr {
     int nt;    // touched slots (entries)
     int nver;  // version rows
     int nwt;   // valid writes
-    int nh;    // resident mode: slots handed off after their first n0 writes
+    int nh;    // slots handed off after their first n0 writes
 };
 
 template <typename TIn, int EPW>
@@ -160,12 +158,9 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     const int t0 = chunk * P.C, Cc = min(P.C, a.T - t0);
     const int K = a.K, nev = Cc * K;
     const int M = static_cast<int>(a.M);
-    const bool hashed = P.HT != 0;
-    const int HT = hashed ? P.HT : M;
-    const int hsh = 32 - (__ffs(HT) - 1);  // hashed: HT is a power of two
+    const int HT = M;  // table position = slot
     const uint64_t kdiv = ((uint64_t(1) << 32) + K - 1) / K;
     const PlanLds L = plan_lds(P, a.M);
-    int *tkey = reinterpret_cast<int *>(smem + L.key);
     int *tcf = reinterpret_cast<int *>(smem + L.cf);
     int *ewo = reinterpret_cast<int *>(smem + L.wo);
     int *bk = reinterpret_cast<int *>(smem + L.bk);
@@ -176,11 +171,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     int *hist = reinterpret_cast<int *>(smem + L.hist);  // [kHBins] counts, offsets, total
 
     unsigned char *rec = a.plan + (static_cast<int64_t>(unit) * P.n_chunks + chunk) * P.rec_bytes;
-    int *ent_slot = reinterpret_cast<int *>(rec + P.o_ent);  // per entry: slot, write offset,
-    int *ent_wo = ent_slot + P.ENTA;                          // writes, version-0 row
-    int *ent_nw = ent_wo + P.ENTA;
-    int *ent_x0 = ent_nw + P.ENTA;
-    int *dwo = reinterpret_cast<int *>(rec + P.o_map);  // resident mode, per slot: write
+    int *dwo = reinterpret_cast<int *>(rec + P.o_map);  // per slot: write
     int *dnx = dwo + M;                                 // offset; writes | (version-0 row + 1) << 16
     int *hl = reinterpret_cast<int *>(rec + P.o_hl);    // handed-off slots: rest offset | rest << 16
     int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
@@ -211,10 +202,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
         }
     }
-    for (int i = tid; i < HT; i += kPT) {
-        tcf[i] = 0;
-        if (hashed) tkey[i] = -1;
-    }
+    for (int i = tid; i < HT; i += kPT) tcf[i] = 0;
     for (int i = tid; i <= P.ENT + P.EV; i += kPT) need[i] = 0;
     if (tid < 2 * kHBins) hist[tid] = 0;
     lds_barrier();
@@ -223,15 +211,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     //         A zero-weight write changes nothing (alpha = 1, lambda = 0); a
     //         slot outside [0, M) (caller-given addresses) is skipped, and a
     //         skipped read contributes nothing.
-    auto entry_of = [&](int s) -> int {
-        if (!hashed) return s;
-        uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
-        for (;;) {  // linear probing; the table is at most 3/4 full
-            const int old = atomicCAS(&tkey[hp], -1, s);
-            if (old == -1 || old == s) return static_cast<int>(hp);
-            hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
-        }
-    };
+    auto entry_of = [&](int s) -> int { return s; };
     int wpos[EPW], ar[EPW], rpos[EPW];
     float al[EPW];
 #pragma unroll
@@ -273,7 +253,6 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
                 eid = base & 0xffff;
                 const int wo = base >> 16;
                 ewo[eid] = wo;
-                if (!P.resident) ent_slot[eid] = hashed ? tkey[p] : p;
                 base += 1 + (nw << 16);
             }
             tcf[p] = eid;  // -1: untouched
@@ -335,7 +314,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
     // ---- 6. the record: entries, writes staged in LDS in causal order, then
     //         everything stored with consecutive lanes on consecutive words
     int nh = 0;
-    if (P.resident && P.HMAX == 0) {
+    if (P.HMAX == 0) {
         for (int p = tid; p < M; p += kPT) {
             const int eid = tcf[p];
             int wo = 0, nx = 0;
@@ -347,7 +326,7 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
             dwo[p] = wo;
             dnx[p] = nx;
         }
-    } else if (P.resident) {
+    } else {
         // Hand-off: the slots with more than n0 writes, busiest first (bins
         // of the write count, the last bin holding every count beyond it),
         // as many as there are spare rows at the end of the scan's version
@@ -399,13 +378,6 @@ __global__ __launch_bounds__(kPT) void plan_kernel(ChunkArgs a) {
                 dwo[p] = wo;
                 dnx[p] = nx;
             }
-        }
-    } else {
-        for (int eid = tid; eid < nt; eid += kPT) {
-            const int g = ewo[eid] + eid;
-            ent_wo[eid] = ewo[eid];
-            ent_nw[eid] = ewo[eid + 1] - ewo[eid];
-            ent_x0[eid] = need[g + 1] > need[g] ? need[g] : -1;
         }
     }
     if (tid == 0) {
@@ -612,8 +584,8 @@ struct HRow {
 // VT: the value rows' type in LDS: fp32 (converted once at staging), or the
 // bf16 input itself (half the LDS, which buys a longer chunk, at a
 // conversion per write); the planner picks per configuration.
-// HAND: resident mode with the hand-off of the busiest slots (P.HMAX > 0).
-template <typename TIn, typename TS, int CG, bool RES, typename VT, bool HAND, int EVT>
+// HAND: the hand-off of the busiest slots (P.HMAX > 0).
+template <typename TIn, typename TS, int CG, typename VT, bool HAND, int EVT>
 __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
@@ -658,18 +630,13 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     // Resident state: thread s owns slot s's row slice and mass.
     float x[CG];
     float m = 0.f;
-    if constexpr (RES) {
-        if (tid < M) {
-            const HRow<TS, CG> r = *reinterpret_cast<const HRow<TS, CG> *>(
-                S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG);
+    if (tid < M) {
+        const HRow<TS, CG> r = *reinterpret_cast<const HRow<TS, CG> *>(
+            S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG);
 #pragma unroll
-            for (int c = 0; c < CG; ++c) x[c] = to_f32(r.e[c]);
-            m = a.mass[static_cast<int64_t>(unit) * M + tid];
-        }
+        for (int c = 0; c < CG; ++c) x[c] = to_f32(r.e[c]);
+        m = a.mass[static_cast<int64_t>(unit) * M + tid];
     }
-    // HBM mode: slice cg's mass copy of slot s is mass_ws[(unit * M + s) * ncg +
-    // cg], so the slices' copies of a slot share a cache line
-    float *mws = a.mass_ws + static_cast<int64_t>(unit) * M * ncg + cg;
 
     // The next chunk's plan and values, loaded one chunk ahead.
     constexpr int VPT = (CG * 512 + kNT - 1) / kNT;
@@ -716,7 +683,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
             const int t = min(vt0 + j * TPJ, Cc - 1);  // in range; extra lanes unused
             pf_v[j] = vcol[static_cast<uint64_t>(static_cast<uint32_t>(t0 + t)) * ldv32];
         }
-        if constexpr (RES) {
+        {
             if (tid < M) {
                 pf_dwo = reinterpret_cast<const int *>(rec + P.o_map)[tid];
                 pf_dnx = reinterpret_cast<const int *>(rec + P.o_map)[M + tid];
@@ -726,24 +693,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         }
     };
 
-    // HBM mode: this thread's touched-slot entries of a chunk (slot, write
-    // offset, writes, version-0 row), loaded one chunk ahead
-    int3 pf_en[RES ? 1 : kEPN];  // slot, write offset, writes | (version-0 row + 1) << 16
-    auto prefetch_ent = [&](int c) {
-        if constexpr (!RES) {
-            const int *ent = reinterpret_cast<const int *>(plan0 + static_cast<int64_t>(c) * P.rec_bytes + P.o_ent);
-#pragma unroll
-            for (int j = 0; j < kEPN; ++j) {
-                const int eid = tid + j * kNT;
-                if (eid < P.ENT)
-                    pf_en[j] = make_int3(ent[eid], ent[P.ENTA + eid],
-                                         ent[2 * P.ENTA + eid] | ((ent[3 * P.ENTA + eid] + 1) << 16));
-            }
-        }
-    };
-
     prefetch(0);
-    prefetch_ent(0);
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, Cc = min(C, a.T - t0), nev = Cc * K;
         // ---- 1. stage this chunk's plan and values
@@ -772,7 +722,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         // ---- 2. the next chunk's loads go out now and land during the walk
         if (c + 1 < nchunks) prefetch(c + 1);
         // ---- 3. walk the touched slots
-        if constexpr (RES) {
+        {
             // the owner applies its slot's first writes (all of them unless
             // the slot is handed off) ...
             if (tid < M && my_nx != 0) {
@@ -806,53 +756,8 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                     m = s_hm[my_hp];
                 }
             }
-        } else {
-            // touched rows from HBM, EB at a time (entries already in
-            // registers): rows and masses, then the walks and write-backs
-            constexpr int RW = CG * static_cast<int>(sizeof(TS)) / 4;  // registers per row
-            constexpr int EB = 8 / RW < 1 ? 1 : (8 / RW > kEPN ? kEPN : 8 / RW);
-#pragma unroll
-            for (int j0 = 0; j0 < kEPN; j0 += EB) {
-                if (tid + j0 * kNT >= nt) break;
-                HRow<TS, CG> rows[EB];
-                float ms[EB];
-#pragma unroll
-                for (int j = 0; j < EB; ++j) {
-                    const int eid = tid + (j0 + j) * kNT;
-                    if (j0 + j < kEPN && eid < nt) {
-                        const int64_t slot = pf_en[j0 + j].x;
-                        rows[j] = *reinterpret_cast<const HRow<TS, CG> *>(
-                            S + (static_cast<int64_t>(unit) * M + slot) * d_v + cg * CG);
-                        ms[j] = mws[slot * ncg];
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < EB; ++j) {
-                    const int eid = tid + (j0 + j) * kNT;
-                    if (j0 + j < kEPN && eid < nt) {
-                        const int3 en = pf_en[j0 + j];
-                        const int nw = en.z & 0xffff, x0r = (en.z >> 16) - 1;
-                        float xr[CG];
-#pragma unroll
-                        for (int cc = 0; cc < CG; ++cc) xr[cc] = to_f32(rows[j].e[cc]);
-                        float mm = ms[j];
-                        walk_slot<TS, CG>(en.y, nw, x0r, xr, mm, a.eps_gsu, s_wtv, s_wwa, vbuf, smem, ver_off);
-                        if (nw > 0) {
-                            HRow<TS, CG> o;
-#pragma unroll
-                            for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(xr[cc]);
-                            *reinterpret_cast<HRow<TS, CG> *>(
-                                S + (static_cast<int64_t>(unit) * M + en.x) * d_v + cg * CG) = o;
-                            mws[static_cast<int64_t>(en.x) * ncg] = mm;
-                        }
-                    }
-                }
-            }
         }
-        // HBM mode: this chunk's row write-backs must be visible to the
-        // threads that gather the next chunk's rows
-        if constexpr (RES) lds_barrier(); else __syncthreads();
-        if (c + 1 < nchunks) prefetch_ent(c + 1);  // lands during the reduction
+        lds_barrier();
         // ---- 4. reads: r = sum_k rho_k * version_k over the slice; G = P.RG
         //         lanes share a token.  With 1 < NCH <= G (NCH: pieces per row), lane
         //         g takes piece g % NCH of reads k = g / NCH, g / NCH + G / NCH,
@@ -964,26 +869,14 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         lds_barrier();
     }
 
-    if constexpr (RES) {
-        if (tid < M) {
-            HRow<TS, CG> o;
+    if (tid < M) {
+        HRow<TS, CG> o;
 #pragma unroll
-            for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(x[cc]);
-            *reinterpret_cast<HRow<TS, CG> *>(S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG) = o;
-            // Other slices of this unit may not have read the initial mass
-            // yet; the epilogue copies slice 0's final mass over.
-            if (cg == 0) a.mass_ws[static_cast<int64_t>(unit) * M + tid] = m;
-        }
-    }
-}
-
-// Every slice's copy of the mass starts from the caller's (HBM mode).
-__global__ void mass_fanout_kernel(const float *__restrict__ mass, float *__restrict__ mass_ws,
-                                   int64_t n, int ncg) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const float x = mass[i];
-        for (int c = 0; c < ncg; ++c) mass_ws[i * ncg + c] = x;
+        for (int cc = 0; cc < CG; ++cc) o.e[cc] = from_f32<TS>(x[cc]);
+        *reinterpret_cast<HRow<TS, CG> *>(S + (static_cast<int64_t>(unit) * M + tid) * d_v + cg * CG) = o;
+        // Other slices of this unit may not have read the initial mass
+        // yet; the epilogue copies slice 0's final mass over.
+        if (cg == 0) a.mass_ws[static_cast<int64_t>(unit) * M + tid] = m;
     }
 }
 
@@ -1038,15 +931,10 @@ hipError_t set_lds(K kern, size_t lds) {
 using ScanFn = void (*)(ChunkArgs);
 template <typename TIn, typename TS, int CG, typename VB, int EVT>
 ScanFn pick_scan(const ChunkPlan &P) {
-    if (P.resident)
-        return P.HMAX > 0 ? (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, true, EVT>
-                                          : scan_kernel<TIn, TS, CG, true, float, true, EVT>)
-                          : (P.raw_values ? scan_kernel<TIn, TS, CG, true, VB, false, EVT>
-                                          : scan_kernel<TIn, TS, CG, true, float, false, EVT>);
-    if constexpr (EVT * kNT <= kMaxEVHbm)  // HBM-mode chunks hold at most kMaxEVHbm events
-        return P.raw_values ? scan_kernel<TIn, TS, CG, false, VB, false, EVT>
-                            : scan_kernel<TIn, TS, CG, false, float, false, EVT>;
-    return nullptr;
+    return P.HMAX > 0 ? (P.raw_values ? scan_kernel<TIn, TS, CG, VB, true, EVT>
+                                      : scan_kernel<TIn, TS, CG, float, true, EVT>)
+                      : (P.raw_values ? scan_kernel<TIn, TS, CG, VB, false, EVT>
+                                      : scan_kernel<TIn, TS, CG, float, false, EVT>);
 }
 
 template <typename TIn, typename TS, int CG>
@@ -1056,19 +944,12 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
     const int tier = (P.EV + 1023) / 1024;  // 1..4
     if (tier < 1 || tier > kMaxEV / 1024) return hipErrorInvalidValue;
     auto pk = tier <= 2 ? plan_kernel<TIn, 2048 / kPT> : tier == 3 ? plan_kernel<TIn, 3072 / kPT>
-                                                                    : plan_kernel<TIn, 4096 / kPT>;
+                                                                      : plan_kernel<TIn, 4096 / kPT>;
     hipError_t e = set_lds(pk, P.lds_plan);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPT), P.lds_plan, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!P.resident) {
-        const int64_t nm = units * a.M;
-        const unsigned g = static_cast<unsigned>(std::min<int64_t>((nm + 255) / 256, 4096));
-        hipLaunchKernelGGL(mass_fanout_kernel, dim3(g), dim3(256), 0, st, a.mass, a.mass_ws, nm, P.ncg);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     using VB = std::conditional_t<std::is_same_v<TIn, bf16_t>, bf16_t, float>;
     const ScanFn sk = tier <= 2 ? pick_scan<TIn, TS, CG, VB, 2>(P)
                       : tier == 3 ? pick_scan<TIn, TS, CG, VB, 3>(P)
@@ -1087,12 +968,12 @@ hipError_t launch_cfg(const ChunkArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((rms_gate_kernel<TIn, bf16_t>), dim3(g2), dim3(256), 0, st, a.rbuf,
                            a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm, a.mass_ws,
-                           P.resident ? 1 : P.ncg, a.mass, n_mass);
+                           1, a.mass, n_mass);
     else
         hipLaunchKernelGGL((rms_gate_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.rbuf,
                            a.sumsq, P.ncg, static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<TS *>(a.out), n, a.d_v, a.eps_norm, a.mass_ws,
-                           P.resident ? 1 : P.ncg, a.mass, n_mass);
+                           1, a.mass, n_mass);
     return hipGetLastError();
 }
 
@@ -1113,9 +994,10 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
     p.ok = false;
     const int sbytes = state_bf16 ? 2 : 4;
     const int64_t units = static_cast<int64_t>(B) * H;
-    // Plan entries pack the token in 10 bits and table sums in 16.
-    if (T < 32 || units == 0 || K > 63 || M > (int64_t(1) << 22)) return p;
-    p.resident = M <= kNT;
+    // Plan entries pack the token in 10 bits and table sums in 16; thread s
+    // of the scan owns slot s (rows in HBM take the slot-range path).
+    if (T < 32 || units == 0 || K > 63 || M > kNT) return p;
+    p.resident = true;
     // Largest channel slice that still gives about one workgroup per CU,
     // then the longest chunk (a multiple of 32 tokens) whose plan and
     // version rows fit LDS.
@@ -1127,18 +1009,13 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
         if (!last && units * (d_v / CG) < 256) continue;
         for (int C = 512; C >= 32; C -= 32) {
             const int EV = C * K;
-            if (EV > (p.resident ? kMaxEV : kMaxEVHbm)) continue;
+            if (EV > kMaxEV) continue;
             ChunkPlan q = p;
             q.CG = CG;
             q.C = C;
             q.EV = EV;
             q.ENT = static_cast<int>(std::min<int64_t>(M, 2 * EV));
-            q.HT = 0;
-            if (M > 4096) {  // hash table at most 3/4 full
-                int ht = 1;
-                while (ht * 3 < 2 * EV * 4) ht *= 2;
-                q.HT = ht;
-            }
+            q.HT = 0;  // the plan's table is indexed by slot
             q.ncg = d_v / CG;
             // lanes per token in the read reduction: enough to keep the
             // workgroup busy, within one 16-lane row
@@ -1153,7 +1030,7 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
             q.lds_scan = scan_lds(q, M, sbytes, vbytes).total;
             q.raw_values = vbytes == 2;
             if (q.lds_plan > kChunkLdsLimit || q.lds_scan > kChunkLdsLimit) continue;
-            if (q.resident && static_cast<int64_t>(C) * K >= 2 * M) {
+            if (static_cast<int64_t>(C) * K >= 2 * M) {
                 // helpers for the busiest slots, where a chunk writes each
                 // slot at least twice on average (below that the hand-off's
                 // barriers cost about what it saves: Top-8, 1.75 writes per
@@ -1169,8 +1046,8 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
             q.n_chunks = (T + C - 1) / C;
             size_t o = 256;  // header
             q.ENTA = (q.ENT + 63) & ~63;
-            q.o_ent = o; o += al256(q.resident ? 0 : static_cast<size_t>(q.ENTA) * 16);
-            q.o_map = o; o += al256(q.resident ? static_cast<size_t>(M) * 8 : 0);
+            q.o_ent = o;
+            q.o_map = o; o += al256(static_cast<size_t>(M) * 8);
             q.o_hl = o; o += al256(static_cast<size_t>(q.HMAX) * 4);
             q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
             q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
@@ -1181,7 +1058,7 @@ ChunkPlan plan_with(int64_t M, int K, int d_v, int B, int T, int H, bool state_b
             const size_t n = static_cast<size_t>(units) * T;
             q.ws_rbuf = state_bf16 ? al256(n * d_v * 4) : 0;
             q.ws_sumsq = al256(n * q.ncg * 4);
-            q.ws_mass = al256(static_cast<size_t>(q.resident ? 1 : q.ncg) * units * M * 4);
+            q.ws_mass = al256(static_cast<size_t>(units) * M * 4);
             q.ws_plan = al256(static_cast<size_t>(units) * q.n_chunks * q.rec_bytes);
             q.ok = true;
             return q;
