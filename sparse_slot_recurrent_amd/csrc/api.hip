@@ -110,15 +110,17 @@ struct LayerPlan {
     bool chunked;
     ramnet::ChunkPlan cp;
     size_t addr_bytes;   // decoded addresses kept in the workspace
+    size_t fails_bytes;  // the decoder's failure words
     size_t chunk_bytes;  // chunked-path scratch
-    size_t total() const { return addr_bytes + chunk_bytes; }
+    size_t total() const { return addr_bytes + fails_bytes + chunk_bytes; }
 };
 
 
-LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
+// addr_in_ws: the decoded addresses are kept in the workspace; decodes: the
+// call decodes q and k (no addr_in).
+LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws, bool decodes) {
     LayerPlan lp{};
     const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
-    const int64_t units = static_cast<int64_t>(p->B) * p->H;
     const bool sbf = p->state_dtype == RAMNET_BF16;
     lp.chunked = false;
     if (!step) {
@@ -128,6 +130,7 @@ LayerPlan plan_layer(const ramnet_params *p, bool step, bool addr_in_ws) {
     // The fused decoding step keeps its addresses on chip.
     const bool fused_step = step && ramnet::step_fused_supported(p->K, p->d_p, p->U, p->d_v, p->state_dtype == RAMNET_BF16);
     lp.addr_bytes = addr_in_ws && !fused_step ? 4 * align256(static_cast<size_t>(n) * p->K * 4) : 0;
+    lp.fails_bytes = decodes && !fused_step && p->K <= 32 ? align256(ramnet::decode_fails_bytes(n)) : 0;
     lp.chunk_bytes = lp.chunked ? ramnet::chunk_workspace_bytes(lp.cp) : 0;
     return lp;
 }
@@ -249,7 +252,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         sp[ns++] = span("addr_out.r_idx", addr_out->r_idx, nK4);
         sp[ns++] = span("addr_out.r_wt", addr_out->r_wt, nK4);
     }
-    const LayerPlan lp = plan_layer(p, step, decode && !addr_out);
+    const LayerPlan lp = plan_layer(p, step, decode && !addr_out, decode);
     const size_t need = lp.total();
     if (need > 0) {
         if (!ws || ws_bytes < need)
@@ -308,6 +311,8 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         ramnet::DecodeArgs da = decode_args(p, q, k, pos, n, p->T, addr);
         unit_major = da.unit_major = lp.addr_bytes && lp.chunked;
         da.ld = sd.qk;
+        if (lp.fails_bytes)
+            da.fails = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + lp.addr_bytes);
         hipError_t e = ramnet::launch_decode(da, st);
         if (e != hipSuccess) return hip_status(e, "address decoder launch");
     } else {
@@ -344,7 +349,7 @@ ramnet_status run_layer(const ramnet_params *p, bool step, const void *q, const 
         ramnet::ChunkArgs c{};
         static_cast<ramnet::ScanArgs &>(c) = a;
         c.p = lp.cp;
-        char *cw = static_cast<char *>(ws) + lp.addr_bytes;
+        char *cw = static_cast<char *>(ws) + lp.addr_bytes + lp.fails_bytes;
         if (lp.cp.ws_rbuf) {
             c.rbuf = reinterpret_cast<float *>(cw);
             cw += lp.cp.ws_rbuf;
@@ -410,7 +415,7 @@ FwdPlan plan_forward(const ramnet_params *p, int32_t d_model, bool step) {
     f.o_proj = o; o += align256(rows * pl.N * 2);
     f.o_out = o; o += align256(n * p->d_v * st_bytes(p));
     f.o_out16 = o; o += p->state_dtype == RAMNET_BF16 ? 0 : align256(n * p->d_v * 2);
-    f.o_layer = o; o += plan_layer(p, step, true).total();
+    f.o_layer = o; o += plan_layer(p, step, true, true).total();
     f.total = o;
     return f;
 }
@@ -746,7 +751,7 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
                    ? ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K)
                    : 0;
     if (op != RAMNET_OP_PREFILL && op != RAMNET_OP_STEP) return 0;
-    return plan_layer(p, step, true).total();
+    return plan_layer(p, step, true, true).total();
 }
 
 ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const void *k,
@@ -893,7 +898,8 @@ ramnet_status ramnet_scan_prefill_noalloc(const ramnet_params *p, const void *q,
     if (s) return s;
     // the scratch need is known from the parameters: refuse a call that does
     // not fit before any HIP call is made
-    const LayerPlan lp = plan_layer(p, false, addr_in == nullptr && addr_out == nullptr);
+    const LayerPlan lp = plan_layer(p, false, addr_in == nullptr && addr_out == nullptr,
+                                    addr_in == nullptr);
     if (lp.total() > RAMNET_NOALLOC_SCRATCH_BYTES)
         return fail(RAMNET_EWORKSPACE,
                     "this prefill needs %zu bytes of scratch; the static scratch of "

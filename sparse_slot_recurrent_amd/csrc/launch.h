@@ -23,7 +23,16 @@ struct DecodeArgs {
     int64_t ld;       // elements between tokens (b, t) of q and k; 0: H*U*d_p
     int32_t *w_idx, *r_idx;
     float *w_wt, *r_wt;
+    // NULL: every address is searched in fp64.  Else (bf16 logits, K <= 32)
+    // scratch of decode_fails_bytes(n): the search runs in fixed point,
+    // exact, and the few addresses whose logits span too many binary orders
+    // for 32-bit drops are marked there and searched in fp64; the slots are
+    // the same either way.
+    unsigned long long *fails;
 };
+// Scratch of the fixed-point search for n addresses (of each of q and k):
+// one failure word per wave.
+size_t decode_fails_bytes(int64_t n);
 hipError_t launch_decode(const DecodeArgs &d, hipStream_t st);
 
 // Recurrence over T tokens for B*H units, given addresses.

@@ -616,7 +616,6 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     const uint32_t ver_off = static_cast<uint32_t>(L.ver);
     int *s_rv = reinterpret_cast<int *>(smem + L.rv);
     float *s_rr = reinterpret_cast<float *>(smem + L.rr);
-    TS *ver = reinterpret_cast<TS *>(smem + L.ver);
     float *s_hm = reinterpret_cast<float *>(smem + L.hm);
     constexpr int kCP = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
     constexpr int kLH = CG / kCP;                            // lanes per handed-off slot
@@ -650,7 +649,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
     int pf_wtv[EVT], pf_rv[EVT];
     float pf_ww[EVT], pf_wa[EVT], pf_rr[EVT];
     TIn pf_v[VPT];  // raw: converting at load time would wait for each load
-    int pf_dwo = 0, pf_dnx = 0, pf_nt = 0;  // resident: this slot's write offset, writes | x0
+    int pf_dwo = 0, pf_dnx = 0;  // resident: this slot's write offset, writes | x0
     int pf_nh = 0, pf_hl = 0;               // resident: slots handed off; this thread's one
     auto prefetch = [&](int c) {
         const unsigned char *rec = plan0 + static_cast<int64_t>(c) * P.rec_bytes;
@@ -660,7 +659,6 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
         const float *wa = reinterpret_cast<const float *>(rec + P.o_wa);
         const int *rv = reinterpret_cast<const int *>(rec + P.o_rv);
         const float *rr = reinterpret_cast<const float *>(rec + P.o_rr);
-        pf_nt = reinterpret_cast<const PlanHdr *>(rec)->nt;
         if (HAND) pf_nh = reinterpret_cast<const PlanHdr *>(rec)->nh;
         // every load is independent of every other (no wait on the header):
         // the write list is read to its capacity, entries past its end are
@@ -715,7 +713,7 @@ __global__ __launch_bounds__(kNT) void scan_kernel(ChunkArgs a) {
                 else vbuf[t * VROW + vcc] = to_f32(pf_v[j]);
             }
         }
-        const int my_wo = HAND ? pf_dwo & 0xffff : pf_dwo, my_nx = pf_dnx, nt = pf_nt;
+        const int my_wo = HAND ? pf_dwo & 0xffff : pf_dwo, my_nx = pf_dnx;
         const int my_hp = HAND ? static_cast<int>(static_cast<uint32_t>(pf_dwo) >> 16) - 1 : -1;  // hand-off row
         const int nh = HAND ? pf_nh : 0, my_hl = pf_hl;
         lds_barrier();

@@ -445,24 +445,8 @@ __host__ __device__ inline RScanLds rscan_lds(const ChunkPlan &p, int d_v, int s
     return L;
 }
 
-// Four channels of a version row as fp32 (8 bytes of bf16, 16 of fp32).
-__device__ __forceinline__ void load4(const float *p, float (&x)[4]) {
-    const float4 f = *reinterpret_cast<const float4 *>(p);
-    x[0] = f.x;
-    x[1] = f.y;
-    x[2] = f.z;
-    x[3] = f.w;
-}
-__device__ __forceinline__ void load4(const bf16_t *p, float (&x)[4]) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    x[0] = __uint_as_float(u.x << 16);
-    x[1] = __uint_as_float(u.x & 0xffff0000u);
-    x[2] = __uint_as_float(u.y << 16);
-    x[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-
-// The same from a version row in LDS or in the spill area (Q: the pointer's
-// address-space qualifier).
+// Four channels of a version row as fp32 (8 bytes of bf16, 16 of fp32), from
+// LDS or from the spill area (Q: the pointer's address-space qualifier).
 template <typename Q>
 __device__ __forceinline__ void load4q(const Q *p, float (&x)[4], float) {
     const u32x4 u = *p;

@@ -16,10 +16,12 @@
 //    merge steps per level by log2(KP) parallel ones.  At the first levels,
 //    where every candidate can have a lane of its own (beam entries x d_p
 //    <= KP), one bitonic sort of the candidates gives the same beam in
-//    fewer stages.  The decision is taken
-//    in fp64 (softmax summed in digit order, as the reference definition
-//    writes it).  The digit distributions of all levels are computed first,
-//    one (address, level, digit) per lane, and kept in LDS.
+//    fewer stages.  Candidates rank by the sum of their digits' logits in
+//    fp64 (a slot's weight is exp(that sum - the levels' log-normalisers),
+//    the normalisers being common to all candidates), ties by the smaller
+//    prefix, as in the prefill's decoder; the weights are formed at the end.
+//    Every level's log-normaliser is computed first, one (address, level)
+//    per lane, and kept in LDS.
 //  * Update and read, one round trip to HBM: the masses of the write slots
 //    and every write row and read row of the wave's units are loaded at
 //    once.  Rows move in 16-byte pieces (12 where 16 would not tile a wave):
@@ -45,14 +47,15 @@ struct RowVec {
     T e[CPL];
 };
 
-// (weight, prefix) entries; invalid entries have weight -1 and prefix -1.
+// (logit sum, prefix) entries; invalid entries have sum -inf and prefix -1.
 struct Ent {
     double w;
     int p;
 };
 
-// Weight desc, then prefix asc.  Valid weights are >= 0 and an invalid
-// prefix is the largest unsigned value, so invalid entries rank last.
+// Logit sum desc (weight desc), then prefix asc.  An invalid entry's sum is
+// -inf and its prefix the largest unsigned value, so invalid entries rank
+// last.
 // Branch-free: both comparisons are evaluated.
 __device__ __forceinline__ bool better(const Ent &a, const Ent &b) {
     const bool gt = a.w > b.w, eq = a.w == b.w;
@@ -245,7 +248,7 @@ __host__ __device__ constexpr StepLds step_lds(int UPW, int K, int L, int RPI, i
     o.idx = 0;                                   // int   [UPW][2][K]
     o.wt = o.idx + UPW * 2 * K * 4;              // float [UPW][2][K]
     o.lg = o.wt + UPW * 2 * K * 4;               // float [UPW][2][L]
-    o.pr = (o.lg + UPW * 2 * L * 4 + 7) & ~7;    // double[UPW][2][L]
+    o.pr = (o.lg + UPW * 2 * L * 4 + 7) & ~7;    // double[UPW][2][U]: the levels' log-normalisers
     o.lam = o.pr + UPW * 2 * L * 8;              // float [UPW][K]
     o.cr = o.lam + UPW * K * 4;                  // float [UPW][K]
     o.red = o.cr + UPW * K * 4;                  // float [RPI][DV]
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
     int *sidx = reinterpret_cast<int *>(smem + lo.idx);
     float *swt = reinterpret_cast<float *>(smem + lo.wt);
     float *slg = reinterpret_cast<float *>(smem + lo.lg);
-    double *spr = reinterpret_cast<double *>(smem + lo.pr);
+    double *slse = reinterpret_cast<double *>(smem + lo.pr);
     float *slam = reinterpret_cast<float *>(smem + lo.lam);
     float *scr = reinterpret_cast<float *>(smem + lo.cr);
     float *sred = reinterpret_cast<float *>(smem + lo.red);
@@ -299,32 +302,15 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         slg[i] = to_f32(src[(unit / a.H) * a.ld_qk + (unit % a.H) * L + e]);
     }
     __syncthreads();
-    // digit distributions of every block, one (address, block, digit) per
-    // lane: exp(l - max) in fp64, then the division by the sum taken in
-    // digit order
-    for (int i = lane; i < UPW * 2 * L; i += kWave) {
-        const float *lv = slg + (i - i % dp);
+    // every level's log-normaliser, one (address, level) per lane:
+    // max + log(sum exp(l - max)), the sum in fp64 in digit order
+    for (int i = lane; i < UPW * 2 * U; i += kWave) {
+        const float *lv = slg + i * dp;
         float mx = lv[0];
         for (int d = 1; d < dp; ++d) mx = fmaxf(mx, lv[d]);
-        spr[i] = exp(static_cast<double>(slg[i]) - static_cast<double>(mx));
-    }
-    __syncthreads();
-    double prv[(UPW * 2 * kMaxDigits + kWave - 1) / kWave];
-#pragma unroll
-    for (int t = 0; t < (UPW * 2 * kMaxDigits + kWave - 1) / kWave; ++t) {
-        const int i = lane + t * kWave;
-        if (i < UPW * 2 * L) {
-            const double *ev = spr + (i - i % dp);
-            double sum = 0.0;
-            for (int d = 0; d < dp; ++d) sum += ev[d];
-            prv[t] = spr[i] / sum;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < (UPW * 2 * kMaxDigits + kWave - 1) / kWave; ++t) {
-        const int i = lane + t * kWave;
-        if (i < UPW * 2 * L) spr[i] = prv[t];
+        double sum = 0.0;
+        for (int d = 0; d < dp; ++d) sum += exp(static_cast<double>(lv[d]) - static_cast<double>(mx));
+        slse[i] = static_cast<double>(mx) + log(sum);
     }
     __syncthreads();
 
@@ -333,9 +319,9 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         const int g = lane / KP, r = lane % KP;
         const int ul = g / 2, which = g % 2;  // which 0: key -> write, 1: query -> read
         const int unit = min(u0 + ul, units - 1);  // spare groups decode a copy, never stored
-        const double *pg = spr + g * L;
+        const float *pg = slg + g * L;
         Ent beam;
-        beam.w = r == 0 ? 1.0 : -1.0;
+        beam.w = r == 0 ? 0.0 : -__builtin_inf();
         beam.p = r == 0 ? 0 : -1;
         int nb = 1;  // entries of the beam (the same in every lane)
         for (int u = 0; u < U; ++u) {
@@ -350,7 +336,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                 c.w = __hiloint2double(__shfl(__double2hiint(beam.w), src), __shfl(__double2loint(beam.w), src));
                 c.p = __shfl(beam.p, src);
                 const bool ok = r < nc;
-                c.w = ok ? c.w * pg[u * dp + (ok ? d : 0)] : -1.0;
+                c.w = ok ? c.w + static_cast<double>(pg[u * dp + (ok ? d : 0)]) : -__builtin_inf();
                 c.p = ok ? c.p * dp + d : -1;
                 Ent res;
                 if (nc <= 2) res = bitonic_sort<KP, 2>(c, r);
@@ -359,22 +345,22 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                 else if (KP >= 16 && nc <= 16) res = bitonic_sort<KP, (KP >= 16 ? 16 : 2)>(c, r);
                 else res = bitonic_sort<KP, KP>(c, r);
                 if (r >= K) {
-                    res.w = -1.0;
+                    res.w = -__builtin_inf();
                     res.p = -1;
                 }
                 beam = res;
                 nb = min(K, nc);
                 continue;
             }
-            double pr[8];
+            double lgd[8];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) pr[d] = d < dp ? pg[u * dp + d] : 0.0;
+            for (int d = 0; d < 8; ++d) lgd[d] = d < dp ? static_cast<double>(pg[u * dp + d]) : 0.0;
             // candidate lists and their merge tree
             Ent lst[8];
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 const bool ok = beam.p >= 0 && d < dp;
-                lst[d].w = ok ? beam.w * pr[d] : -1.0;
+                lst[d].w = ok ? beam.w + lgd[d] : -__builtin_inf();
                 lst[d].p = ok ? beam.p * dp + d : -1;
             }
             Ent res = merge_top<KP>(lst[0], lst[1], r);
@@ -383,7 +369,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                 res = merge_top<KP>(res, merge_top<KP>(merge_top<KP>(lst[4], lst[5], r),
                                                        merge_top<KP>(lst[6], lst[7], r), r), r);
             if (r >= K) {  // keep K entries
-                res.w = -1.0;
+                res.w = -__builtin_inf();
                 res.p = -1;
             }
             beam = res;
@@ -395,7 +381,10 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         if (u0 + ul < units && r < K) {
             const int form = head_uses_cape(a.content_heads, unit % a.H) ? a.cape : 0;
             const int slot = form ? cape_slot<0>(beam.p, pos, U, dp, form, M) : beam.p;
-            const float wt = static_cast<float>(beam.w);
+            // the weight exp(logit sum - the levels' log-normalisers)
+            double lse_sum = 0.0;
+            for (int u = 0; u < U; ++u) lse_sum += slse[g * U + u];
+            const float wt = static_cast<float>(exp(beam.w - lse_sum));
             sidx[(ul * 2 + which) * K + r] = slot;
             swt[(ul * 2 + which) * K + r] = wt;
             if (a.out_idx[which]) {

@@ -154,6 +154,47 @@ def check_layer(orc, w, x, out, addr, S, mass, ref, content_heads=0, norm_w=None
     return int(adopted.sum())
 
 
+@pytest.mark.parametrize("logits", ["plain", "ties", "spread"])
+@pytest.mark.parametrize("name", ["prefill_top8", "prefill_top32", "large_state"])
+def test_prefill_decoder_sets_equal_fp64_search(rn, orc, name, logits):
+    """The prefill decodes bf16 logits in fixed point (exact integer drops;
+    rounded drops with a per-cut margin where the logits span more than 30
+    binary orders, the rest left to fp64); the standalone decoder searches
+    in fp64.  Both rank by exact weight, ties by the smaller prefix, so the
+    slot sets agree bit for bit.  "ties": logits on a coarse grid, most cuts
+    exact ties.  "spread": a quarter of the logits scaled by 2^-40, so most
+    addresses take the rounded drops."""
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w, **CUTS[name])
+    if logits == "ties":
+        for n in ("q", "k"):
+            x[n] = (np.round(x[n] * 2) / 2).astype(x[n].dtype)
+    elif logits == "spread":
+        rng = np.random.default_rng(9)
+        for n in ("q", "k"):
+            small = rng.random(x[n].shape) < 0.25
+            x[n] = np.where(small, x[n] * np.float32(2.0 ** -40), x[n]).astype(x[n].dtype)
+    out, paddr, d = run_gpu(rn, w, x)
+    addr = rn.decode_addresses(d["q"], d["k"], d_p=w.d_p, U=w.U, K=w.K,
+                               cape=w.cape, pos0=d["pos0"])
+    torch.cuda.synchronize()
+    for lg, (pi, pw), (fi, fw) in (("k", paddr[:2], (addr.w_idx, addr.w_wt)),
+                                   ("q", paddr[2:], (addr.r_idx, addr.r_wt))):
+        pi, pw, fi, fw = to_np(pi), to_np(pw), to_np(fi), to_np(fw)
+        assert np.array_equal(np.sort(pi, -1), np.sort(fi, -1)), lg
+        po = np.take_along_axis(pw, np.argsort(pi, -1), -1)
+        fo = np.take_along_axis(fw, np.argsort(fi, -1), -1)
+        assert (np.abs(po - fo) <= 1e-5 * np.abs(fo)).all(), lg
+        assert (np.diff(pw, axis=-1) <= 0).all(), lg
+        oi, ow, og = orc.decode_all(x[lg], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"])
+        compare_address_sets(pi, pw, oi, ow, og, weights_fn(orc, w, x, lg, x["pos0"]))
+        near = float((og <= 2.0 ** -16).mean())
+        print(f"{name} {logits} {lg}: {pi.shape[:-1]} addresses, "
+              f"cuts within 2^-16: {near:.3f}")
+        if logits == "ties":
+            assert near > 0.1
+
+
 @pytest.mark.parametrize("name", list(CUTS))
 def test_decode_addresses(rn, orc, name):
     w = synth.WORKLOADS[name]
