@@ -12,7 +12,12 @@
  *      level-by-level prefix search (the exact Top-K paragraph after
  *      "Waveform Modulation").  Block u is digit u counted from the most
  *      significant one.  Weights are the raw products (not renormalised).
- *      Equal weights rank by the smaller slot index.
+ *      Equal weights rank by the smaller slot index.  The ranking is that
+ *      of the exact weights: a weight is exp(sum of the slot's digit logits
+ *      - sum of the blocks' log-normalisers), the normalisers are common to
+ *      every slot, so slots rank by their logit sums, which the decoders
+ *      form exactly (bf16 logits; fp64 sums for fp32 logits), and ties are
+ *      exact ties.  Returned weights are exp(...) in fp64, rounded to fp32.
  *   2. CAPE ("Cyclic Address Positional Embedding" paragraphs): a token at
  *      position P moves every digit of its read and write slots by
  *      (P mod d_p), cyclically within d_p values.  Weights are unchanged.
@@ -118,8 +123,9 @@ typedef struct {
  *   q, k  [B,T,H,U*d_p] in in_dtype: query and key logits.
  *   pos0  [B] int32 or NULL (= 0): position of token t is pos0[b] + t.
  *   out   all four arrays required.
- * The Top-K decision is taken in fp64; weights are returned rounded to
- * fp32. */
+ * The decision follows step 1's rule (fp64 logit sums); weights are
+ * returned rounded to fp32.  The prefill decodes bf16 logits in exact
+ * fixed point instead and takes the same decisions. */
 ramnet_status ramnet_decode_addresses(const ramnet_params *p, const void *q,
                                       const void *k, const int32_t *pos0,
                                       const ramnet_addr *out, void *stream);
@@ -145,11 +151,13 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op);
  *             skipped (treated as weight 0).
  *   addr_out  NULL, or where to export the addresses used.
  *   workspace ramnet_workspace_bytes(p, RAMNET_OP_PREFILL) bytes.  It holds
- *             the decoded addresses (unless addr_out is given) and, on the
+ *             the decoded addresses (unless addr_out is given), the
+ *             decoder's per-wave fallback marks (K <= 32) and, on the
  *             slot-grouped path (T >= 32, M <= 2^22, K <= 63), the per-chunk
- *             slot-grouping plans, the un-normalised reads, per-token sums of
- *             squares and per-slice mass copies.  Its contents on entry do
- *             not matter.
+ *             slot-grouping plans, the un-normalised reads and per-token sums
+ *             of squares (M <= 1024), or the per-range partial reads and
+ *             spilled version rows (larger M).  Its contents on entry do not
+ *             matter.
  * Results are deterministic: every sum is taken in a fixed order, so repeated
  * calls on the same inputs give the same bits. */
 ramnet_status ramnet_scan_prefill(const ramnet_params *p, const void *q,
