@@ -68,7 +68,7 @@ constexpr int kR = kRanges;
 // compute unit at the benchmark's size, 16 waves to hide the latency of the
 // row gathers.
 constexpr int kRT = 1024;
-constexpr int kPTW = 5;  // walk tasks (16-byte row pieces) per scan thread and round
+constexpr int kPTW = 4;  // walk tasks (16-byte row pieces) per scan thread and round
 constexpr int kLW = 1;   // list entries per kind and thread staged (CAPW = CAPR = kLW * kRT)
 
 __device__ __forceinline__ int range_of(int slot) { return slot & (kR - 1); }
@@ -376,17 +376,33 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
         ent_nw[eid] = ewo[eid + 1] - ewo[eid];
         ent_x0[eid] = need[g + 1] > need[g] ? need[g] - vb[r] : -1;
     }
-    // reads: list position and (range-local version row, weight)
+    // reads: list position and (range-local version row, weight).  A read's
+    // rank among its token's reads of the same range: where K divides the
+    // wave, a token's K reads sit on K aligned lanes of one wave, and the
+    // rank is a popcount of the range's ballot below the lane.
+    const bool token_in_wave = (kWave % K) == 0;
     int rp[EPW], rvv[EPW];
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
         rp[j] = -1;
-        if (gv[j] >= 0) {
-            const int e = tid + j * kPRT;
-            const int t = div_by(e, kdiv), k = e - t * K;
-            const int r = range_of(rs[j]);
-            int rank = 0;
+        const int e = tid + j * kPRT;
+        const int t = div_by(e, kdiv), k = e - t * K;
+        const int r = gv[j] >= 0 ? range_of(rs[j]) : -1;
+        int rank = 0;
+        if (token_in_wave) {
+            const int lane = tid & (kWave - 1);
+            const uint64_t below = ((uint64_t(1) << lane) - 1) & ~((uint64_t(1) << (lane - k)) - 1);
+            uint64_t same = 0;
+#pragma unroll
+            for (int q = 0; q < kR; ++q) {
+                const uint64_t bq = __ballot(r == q);
+                same = r == q ? bq : same;
+            }
+            rank = __popcll(same & below);
+        } else if (r >= 0) {
             for (int q = 0; q < k; ++q) rank += rg[t * K + q] == r ? 1 : 0;
+        }
+        if (r >= 0) {
             rp[j] = rt[r * C + t] + rank;
             rvv[j] = need[gv[j]] - vb[r];
         }
@@ -643,6 +659,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     load_values(0);
     load_lists(0, h_cur);
     load_entries(0, 0, h_cur, pe);
+    gather(0, h_cur, pe, rw);
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, Cc = min(C, a.T - t0);
         const Hdr hc = h_cur;
@@ -681,8 +698,10 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         //         round: gather the round's pieces and masses at once, apply
         //         the writes, store the versions reads see, write back
         for (int task0 = 0; task0 < hc.ne * NP; task0 += kRT * kPTW) {
-            if (task0 > 0) load_entries(c, task0, hc, pe);
-            gather(task0, hc, pe, rw);
+            if (task0 > 0) {  // (the first round's rows were gathered during the last reads)
+                load_entries(c, task0, hc, pe);
+                gather(task0, hc, pe, rw);
+            }
 #pragma unroll
             for (int j = 0; j < kPTW; ++j) {
                 const int task = task0 + tid + j * kRT;
@@ -724,14 +743,16 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 }
             }
         }
-        // row write-backs and spilled versions visible to this workgroup
-        __syncthreads();
-        // ---- 4. chunk c + 1's lists and entries go out now and land during
-        //         the reads
+        // ---- 4. chunk c + 1's lists and entries (plan data) go out now
         if (c + 1 < nchunks) {
             load_lists(c + 1, h_nxt);
             load_entries(c + 1, 0, h_nxt, pe);
         }
+        // row write-backs and spilled versions visible to this workgroup
+        __syncthreads();
+        // ... and chunk c + 1's first rows, which may be rows chunk c just
+        // wrote: they land during the reads
+        if (c + 1 < nchunks) gather(0, h_nxt, pe, rw);
         // ---- 5. reads: lane q of a token sums channels [4q, 4q + 4) over the
         //         range's reads of that token in address order; the partial
         //         (zero if none) goes to the workspace
