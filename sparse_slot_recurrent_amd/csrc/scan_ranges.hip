@@ -761,9 +761,8 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             if (t < Cc) {
                 float acc[4] = {0.f, 0.f, 0.f, 0.f};
                 const int j1 = s_rt[t + 1];
-                for (int j = s_rt[t]; j < j1; ++j) {
-                    int vr;
-                    float rho;
+                const int off = 4 * q * static_cast<int>(sizeof(TS));
+                auto entry = [&](int j, int &vr, float &rho) {
                     if (j < CAPR) {
                         vr = s_rv[j];
                         rho = s_rr[j];
@@ -771,13 +770,34 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                         vr = g_rv[j];
                         rho = g_rr[j];
                     }
-                    float x[4];
-                    const int off = 4 * q * static_cast<int>(sizeof(TS));
+                };
+                auto row = [&](int vr, float (&x)[4]) {
                     if (vr < VCAP)
                         load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
                     else
                         load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
                                x, TS{});
+                };
+                // two reads per step: their loads overlap; the sum keeps
+                // address order
+                int j = s_rt[t];
+                for (; j + 1 < j1; j += 2) {
+                    int vr0, vr1;
+                    float rho0, rho1, x0[4], x1[4];
+                    entry(j, vr0, rho0);
+                    entry(j + 1, vr1, rho1);
+                    row(vr0, x0);
+                    row(vr1, x1);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho0, x0[u], acc[u]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho1, x1[u], acc[u]);
+                }
+                if (j < j1) {
+                    int vr;
+                    float rho, x[4];
+                    entry(j, vr, rho);
+                    row(vr, x);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho, x[u], acc[u]);
                 }
