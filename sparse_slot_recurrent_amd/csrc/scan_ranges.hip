@@ -142,9 +142,8 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     RangeHdr *hdr = reinterpret_cast<RangeHdr *>(rec);
     int *rtoff = reinterpret_cast<int *>(rec + P.o_rt);       // [kR][C + 1], per range
     int *ent_slot = reinterpret_cast<int *>(rec + P.o_ent);  // per entry: slot, write offset,
-    int *ent_wo = ent_slot + P.ENTA;                          // writes, version-0 row
-    int *ent_nw = ent_wo + P.ENTA;
-    int *ent_x0 = ent_nw + P.ENTA;
+    int *ent_wo = ent_slot + P.ENTA;                          // writes | (version-0 row + 1) << 16
+    int *ent_nx = ent_wo + P.ENTA;
     int *wtv = reinterpret_cast<int *>(rec + P.o_wtv);
     float *ww = reinterpret_cast<float *>(rec + P.o_ww);
     float *wa = reinterpret_cast<float *>(rec + P.o_wa);
@@ -373,8 +372,8 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
         for (int q = 1; q < kR; ++q) r += eid >= rs0[q] ? 1 : 0;
         const int g = ewo[eid] + eid;
         ent_wo[eid] = ewo[eid];
-        ent_nw[eid] = ewo[eid + 1] - ewo[eid];
-        ent_x0[eid] = need[g + 1] > need[g] ? need[g] - vb[r] : -1;
+        const int x0 = need[g + 1] > need[g] ? need[g] - vb[r] : -1;
+        ent_nx[eid] = (ewo[eid + 1] - ewo[eid]) | ((x0 + 1) << 16);
     }
     // reads: list position and (range-local version row, weight).  A read's
     // rank among its token's reads of the same range: where K divides the
@@ -625,7 +624,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 const int eid = hd.eb + e;
                 pe.slot[j] = ent[eid];
                 pe.wo[j] = ent[P.ENTA + eid];
-                pe.nx[j] = ent[2 * P.ENTA + eid] | ((ent[3 * P.ENTA + eid] + 1) << 16);
+                pe.nx[j] = ent[2 * P.ENTA + eid];
             }
         }
     };
@@ -634,15 +633,21 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         uint4 raw[kPTW];
         float m[kPTW];
     };
+    // (branch-free row loads: a task past the range's entries loads row 0,
+    // so that the loads go out back to back, with no wait between them)
     auto gather = [&](int task0, const Hdr &hd, const Ent &pe, Rows &rw) {
 #pragma unroll
         for (int j = 0; j < kPTW; ++j) {
             const int task = task0 + tid + j * kRT;
             const int e = entry_of_task(task), piece = task - e * NP;
-            if (e < hd.ne) {
-                rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v +
-                                                             piece * CP);
-                if (!MSL && (pe.nx[j] & 0xffff)) rw.m[j] = mass[pe.slot[j]];
+            const int slot = e < hd.ne ? pe.slot[j] : 0;
+            rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(slot) * d_v + piece * CP);
+        }
+        if (!MSL) {
+#pragma unroll
+            for (int j = 0; j < kPTW; ++j) {
+                const int e = entry_of_task(task0 + tid + j * kRT);
+                if (e < hd.ne && (pe.nx[j] & 0xffff)) rw.m[j] = mass[pe.slot[j]];
             }
         }
     };
@@ -937,7 +942,7 @@ ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf
         q.ENTA = (q.ENT + 63) & ~63;
         size_t o = al256(sizeof(RangeHdr));
         q.o_rt = o; o += al256(static_cast<size_t>(kR) * (C + 1) * 4);
-        q.o_ent = o; o += al256(static_cast<size_t>(q.ENTA) * 16);
+        q.o_ent = o; o += al256(static_cast<size_t>(q.ENTA) * 12);
         q.o_map = q.o_hl = o;
         q.o_wtv = o; o += al256(static_cast<size_t>(EV) * 4);
         q.o_ww = o; o += al256(static_cast<size_t>(EV) * 4);
