@@ -566,18 +566,23 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     // ---- the pipeline: chunk c + 1's lists, values and entries are loaded
     //      during chunk c's walk, its rows right after chunk c's write-backs
     //      (during chunk c's reads), and headers two chunks ahead
+    // (the header's words are kept as loaded and the counts formed where
+    // they are used)
     struct Hdr {
-        int eb, ne, wb, nw, rb, nr;
+        int eb, ee, wb, we, rb, re;
+        __device__ int ne() const { return ee - eb; }
+        __device__ int nw() const { return we - wb; }
+        __device__ int nr() const { return re - rb; }
     };
     auto load_header = [&](int c) {
         const RangeHdr *hd = reinterpret_cast<const RangeHdr *>(rec_of(c));
         Hdr x;
         x.eb = hd->ebase[r];
-        x.ne = hd->ebase[r + 1] - x.eb;
+        x.ee = hd->ebase[r + 1];
         x.wb = hd->wbase[r];
-        x.nw = hd->wbase[r + 1] - x.wb;
+        x.we = hd->wbase[r + 1];
         x.rb = hd->rbase[r];
-        x.nr = hd->rbase[r + 1] - x.rb;
+        x.re = hd->rbase[r + 1];
         return x;
     };
     int pf_wtv[kLW], pf_rv[kLW], pf_rt = 0;
@@ -597,12 +602,12 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < kLW; ++j) {
             const int i = tid + j * kRT;
-            if (i < min(hd.nw, CAPW)) {
+            if (i < min(hd.nw(), CAPW)) {
                 pf_wtv[j] = reinterpret_cast<const int *>(rec + P.o_wtv)[hd.wb + i];
                 pf_ww[j] = reinterpret_cast<const float *>(rec + P.o_ww)[hd.wb + i];
                 pf_wa[j] = reinterpret_cast<const float *>(rec + P.o_wa)[hd.wb + i];
             }
-            if (i < min(hd.nr, CAPR)) {
+            if (i < min(hd.nr(), CAPR)) {
                 pf_rv[j] = reinterpret_cast<const int *>(rec + P.o_rv)[hd.rb + i];
                 pf_rr[j] = reinterpret_cast<const float *>(rec + P.o_rr)[hd.rb + i];
             }
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         for (int j = 0; j < kPTW; ++j) {
             const int e = entry_of_task(task0 + tid + j * kRT);
             pe.nx[j] = 0;
-            if (e < hd.ne) {
+            if (e < hd.ne()) {
                 const int eid = hd.eb + e;
                 pe.slot[j] = ent[eid];
                 pe.wo[j] = ent[P.ENTA + eid];
@@ -640,14 +645,14 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         for (int j = 0; j < kPTW; ++j) {
             const int task = task0 + tid + j * kRT;
             const int e = entry_of_task(task), piece = task - e * NP;
-            const int slot = e < hd.ne ? pe.slot[j] : 0;
+            const int slot = e < hd.ne() ? pe.slot[j] : 0;
             rw.raw[j] = *reinterpret_cast<const uint4 *>(S + static_cast<int64_t>(slot) * d_v + piece * CP);
         }
         if (!MSL) {
 #pragma unroll
             for (int j = 0; j < kPTW; ++j) {
                 const int e = entry_of_task(task0 + tid + j * kRT);
-                if (e < hd.ne && (pe.nx[j] & 0xffff)) rw.m[j] = mass[pe.slot[j]];
+                if (e < hd.ne() && (pe.nx[j] & 0xffff)) rw.m[j] = mass[pe.slot[j]];
             }
         }
     };
@@ -672,11 +677,11 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < kLW; ++j) {
             const int i = tid + j * kRT;
-            if (i < min(hc.nw, CAPW)) {
+            if (i < min(hc.nw(), CAPW)) {
                 s_wtv[i] = pf_wtv[j];
                 s_wwa[i] = f32x2{pf_ww[j], pf_wa[j]};
             }
-            if (i < min(hc.nr, CAPR)) {
+            if (i < min(hc.nr(), CAPR)) {
                 s_rv[i] = pf_rv[j];
                 s_rr[i] = pf_rr[j];
             }
@@ -702,7 +707,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         // ---- 3. walk the range's touched slots, kRT * kPTW row pieces per
         //         round: gather the round's pieces and masses at once, apply
         //         the writes, store the versions reads see, write back
-        for (int task0 = 0; task0 < hc.ne * NP; task0 += kRT * kPTW) {
+        for (int task0 = 0; task0 < hc.ne() * NP; task0 += kRT * kPTW) {
             if (task0 > 0) {  // (the first round's rows were gathered during the last reads)
                 load_entries(c, task0, hc, pe);
                 gather(task0, hc, pe, rw);
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             for (int j = 0; j < kPTW; ++j) {
                 const int task = task0 + tid + j * kRT;
                 const int e = entry_of_task(task), piece = task - e * NP;
-                if (e >= hc.ne) continue;
+                if (e >= hc.ne()) continue;
                 float x[CP];
                 unpack_chunk(rw.raw[j], x);
                 const int x0 = (pe.nx[j] >> 16) - 1;
