@@ -587,14 +587,19 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     };
     int pf_wtv[kLW], pf_rv[kLW], pf_rt = 0;
     float pf_ww[kLW], pf_wa[kLW], pf_rr[kLW];
-    TIn pf_v[VPT];
-    const int vcol = tid % d_v, vrow0 = tid / d_v, vstep = kRT / d_v;
+    // values move as 32-bit words (two bf16 channels, or one fp32 channel):
+    // row offsets and d_v are even, so every word is aligned
+    constexpr int VE = 4 / static_cast<int>(sizeof(TIn));  // channels per word
+    constexpr int VW = (VPT + VE - 1) / VE;                 // words per thread and chunk
+    uint32_t pf_v[VW];
+    const int vcol = tid % (d_v / VE), vrow0 = tid / (d_v / VE), vstep = kRT / (d_v / VE);
     auto load_values = [&](int c) {
         const int t0 = c * C, Cc = min(C, a.T - t0);
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int t = vrow0 + j * vstep;  // element tid + j kRT of the chunk's [C][d_v]
-            if (t < C) pf_v[j] = v[static_cast<int64_t>(t0 + min(t, Cc - 1)) * a.ld_v + vcol];
+        for (int j = 0; j < VW; ++j) {
+            const int t = vrow0 + j * vstep;  // word tid + j kRT of the chunk's [C][d_v]
+            if (t < C)
+                pf_v[j] = reinterpret_cast<const uint32_t *>(v + static_cast<int64_t>(t0 + min(t, Cc - 1)) * a.ld_v)[vcol];
         }
     };
     auto load_lists = [&](int c, const Hdr &hd) {
@@ -688,9 +693,9 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         }
         if (tid <= C) s_rt[tid] = pf_rt;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
+        for (int j = 0; j < VW; ++j) {
             const int t = vrow0 + j * vstep;
-            if (t < Cc) vbuf[t * VROW + vcol] = pf_v[j];
+            if (t < Cc) reinterpret_cast<uint32_t *>(vbuf + t * VROW)[vcol] = pf_v[j];
         }
         lds_barrier();
         const unsigned char *rec = rec_of(c);
@@ -765,55 +770,113 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         if (c + 1 < nchunks) gather(0, h_nxt, pe, rw);
         // ---- 5. reads: lane q of a token sums channels [4q, 4q + 4) over the
         //         range's reads of that token in address order; the partial
-        //         (zero if none) goes to the workspace
-        for (int tb = 0; tb < Cc; tb += TPP) {
-            const int t = tb + tid / RL, q = tid % RL;
-            if (t < Cc) {
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                const int j1 = s_rt[t + 1];
+        //         (zero if none) goes to the workspace.  A token with more
+        //         than kHeavy reads here (a token's reads often share their
+        //         low digits, and so a range) is summed by a whole wave
+        //         instead: its lane groups take every G-th read and are added
+        //         in a fixed order, so that no group waits on a long list.
+        {
+            constexpr int kHeavy = 8;
+            const int G = kWave / RL;  // lane groups of a wave
+            auto entry = [&](int j, int &vr, float &rho) {
+                if (j < CAPR) {
+                    vr = s_rv[j];
+                    rho = s_rr[j];
+                } else {
+                    vr = g_rv[j];
+                    rho = g_rr[j];
+                }
+            };
+            auto row = [&](int vr, int q, float (&x)[4]) {
                 const int off = 4 * q * static_cast<int>(sizeof(TS));
-                auto entry = [&](int j, int &vr, float &rho) {
-                    if (j < CAPR) {
-                        vr = s_rv[j];
-                        rho = s_rr[j];
-                    } else {
-                        vr = g_rv[j];
-                        rho = g_rr[j];
-                    }
-                };
-                auto row = [&](int vr, float (&x)[4]) {
-                    if (vr < VCAP)
-                        load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
-                    else
-                        load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
-                               x, TS{});
-                };
-                // two reads per step: their loads overlap; the sum keeps
-                // address order
-                int j = s_rt[t];
-                for (; j + 1 < j1; j += 2) {
-                    int vr0, vr1;
-                    float rho0, rho1, x0[4], x1[4];
-                    entry(j, vr0, rho0);
-                    entry(j + 1, vr1, rho1);
-                    row(vr0, x0);
-                    row(vr1, x1);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho0, x0[u], acc[u]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho1, x1[u], acc[u]);
-                }
-                if (j < j1) {
-                    int vr;
-                    float rho, x[4];
-                    entry(j, vr, rho);
-                    row(vr, x);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho, x[u], acc[u]);
-                }
+                if (vr < VCAP)
+                    load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
+                else
+                    load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
+                           x, TS{});
+            };
+            auto store = [&](int t, int q, const float (&acc)[4]) {
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
                 *reinterpret_cast<float4 *>(a.partial + (th * kR + r) * d_v + 4 * q) =
                     make_float4(acc[0], acc[1], acc[2], acc[3]);
+            };
+            for (int tb = 0; tb < Cc; tb += TPP) {
+                const int t = tb + tid / RL, q = tid % RL;
+                if (t < Cc) {
+                    const int j0 = s_rt[t], j1 = s_rt[t + 1];
+                    if (G > 1 && j1 - j0 > kHeavy) continue;  // summed below
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                    // two reads per step: their loads overlap; the sum keeps
+                    // address order
+                    int j = j0;
+                    for (; j + 1 < j1; j += 2) {
+                        int vr0, vr1;
+                        float rho0, rho1, x0[4], x1[4];
+                        entry(j, vr0, rho0);
+                        entry(j + 1, vr1, rho1);
+                        row(vr0, q, x0);
+                        row(vr1, q, x1);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho0, x0[u], acc[u]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho1, x1[u], acc[u]);
+                    }
+                    if (j < j1) {
+                        int vr;
+                        float rho, x[4];
+                        entry(j, vr, rho);
+                        row(vr, q, x);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho, x[u], acc[u]);
+                    }
+                    store(t, q, acc);
+                }
+            }
+            if (G > 1) {
+                // heavy tokens in token order, the h-th to wave h mod (waves)
+                const int lane = tid & (kWave - 1), wave = tid / kWave;
+                const int gq = lane / RL, q = lane % RL;
+                int h = 0;
+                for (int tw = 0; tw < Cc; tw += kWave) {
+                    const int tt = tw + lane;
+                    uint64_t bits = __ballot(tt < Cc && s_rt[tt + 1] - s_rt[tt] > kHeavy);
+                    while (bits) {
+                        const int t = tw + __builtin_ctzll(bits);
+                        bits &= bits - 1;
+                        if (h++ % (kRT / kWave) != wave) continue;
+                        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                        const int j1 = s_rt[t + 1];
+                        int j = s_rt[t] + gq;
+                        for (; j + G < j1; j += 2 * G) {
+                            int vr0, vr1;
+                            float rho0, rho1, x0[4], x1[4];
+                            entry(j, vr0, rho0);
+                            entry(j + G, vr1, rho1);
+                            row(vr0, q, x0);
+                            row(vr1, q, x1);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho0, x0[u], acc[u]);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho1, x1[u], acc[u]);
+                        }
+                        if (j < j1) {
+                            int vr;
+                            float rho, x[4];
+                            entry(j, vr, rho);
+                            row(vr, q, x);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[u] = fmaf(rho, x[u], acc[u]);
+                        }
+                        // the groups' sums, pairwise in a fixed order (each
+                        // addition is commutative, so every lane holds the
+                        // same bits)
+                        for (int o = RL; o < kWave; o <<= 1) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[u] += __shfl_xor(acc[u], o, kWave);
+                        }
+                        if (gq == 0) store(t, q, acc);
+                    }
+                }
             }
         }
         // LDS is restaged and the spill area rewritten by the next chunk
