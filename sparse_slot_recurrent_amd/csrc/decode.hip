@@ -472,6 +472,16 @@ __device__ __forceinline__ const TIn *logits_of(const DecodeK &d, int64_t a, boo
     return static_cast<const TIn *>(key ? d.k : d.q) + (a / d.H) * d.ld + (a % d.H) * (d.U * DP);
 }
 
+// The i-th address in launch order: token-major ([B,T,H], the address
+// index itself), or, for head-major output ([B,H,T]), a head's tokens one
+// after another, so that a wave's stores fill consecutive rows.
+__device__ __forceinline__ int64_t address_of(const DecodeK &d, int64_t i) {
+    if (!d.unit_major) return i;
+    const int64_t T = d.T, H = d.H;
+    const int64_t b = i / (H * T), h = (i / T) % H, t = i % T;
+    return (b * T + t) * H + h;
+}
+
 // Stores one address's K slots (moved by CAPE) and weights, heaviest first;
 // at(r, slot, w) gives the r-th pre-CAPE slot and its weight.
 template <int DP, int KC, typename At>
@@ -561,9 +571,9 @@ __device__ __forceinline__ void decode64(const DecodeK &d, int64_t a, bool key, 
 template <int DP, int KC, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_kernel(DecodeK d) {
     extern __shared__ unsigned char smem[];
-    const int64_t a = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
-    if (a >= d.n) return;  // no barrier below: lanes are independent
-    decode64<DP, KC, TIn>(d, a, blockIdx.y == 0, smem);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + threadIdx.x;
+    if (i >= d.n) return;  // no barrier below: lanes are independent
+    decode64<DP, KC, TIn>(d, address_of(d, i), blockIdx.y == 0, smem);
 }
 
 // One address per lane in fixed point: an address whose drops fit 32 bits
@@ -574,8 +584,9 @@ template <int DP, int KC, typename TIn>
 __global__ __launch_bounds__(kWave) void decode_fast_kernel(DecodeK d) {
     extern __shared__ unsigned char smem[];
     const int lane = threadIdx.x;
-    const int64_t a = static_cast<int64_t>(blockIdx.x) * kWave + lane;
-    if (a >= d.n) return;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    if (i >= d.n) return;
+    const int64_t a = address_of(d, i);
     const bool key = blockIdx.y == 0;
     uint64_t out[KC];
     double unit, lnz;
@@ -602,7 +613,7 @@ __global__ __launch_bounds__(kWave) void decode_fallback_kernel(DecodeK d) {
     const bool key = i < d.waves;
     const int64_t w0 = (key ? i : i - d.waves) * kWave;
     for (unsigned long long f = d.fails[i]; f != 0; f &= f - 1)
-        decode64<DP, KC, TIn>(d, w0 + __builtin_ctzll(f), key, smem);
+        decode64<DP, KC, TIn>(d, address_of(d, w0 + __builtin_ctzll(f)), key, smem);
 }
 
 template <typename K>

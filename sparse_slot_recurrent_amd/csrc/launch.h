@@ -112,7 +112,7 @@ struct ChunkArgs : ScanArgs {
     float *sumsq;
     float *mass_ws;  // rows on chip: final mass [units][M]
     unsigned char *plan;
-    float *partial;  // rows in HBM: [B,T,H][kRanges][d_v] partial reads
+    float *partial;  // rows in HBM: [B,T,H][kRanges][d_v] partial reads (fp16 for a bf16 state)
     void *spill;     // rows in HBM: [units][kRanges][EV][d_v] version rows beyond VCAP
 };
 

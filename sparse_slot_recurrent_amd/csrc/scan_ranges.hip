@@ -30,7 +30,8 @@
 //     A slot belongs to one range, so the mass is updated in place.
 //   * Reads: per token, four channels per lane, the range's reads summed in
 //     address order (rho * version); every token's partial (zero when the
-//     range holds none of its reads) goes to the workspace.
+//     range holds none of its reads) goes to the workspace, in fp16 where the
+//     state is bf16.
 // gate_partials_kernel: one wave per token-head adds the kRanges partials in
 // range order, then RMSNorm over d_v and the sigmoid gate.
 #include "chunk_common.h"
@@ -493,9 +494,15 @@ __device__ __forceinline__ uint4 pack_piece(const float (&x)[8], bf16_t) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// The partial reads' type: fp16 where the state (and so the output) is
+// bf16, whose 8 significant bits the 11 of fp16 leave intact; else fp32.
+template <typename TS>
+using PartialOf = std::conditional_t<std::is_same_v<TS, bf16_t>, _Float16, float>;
+
 // VPT: value elements per thread and chunk (C * d_v / kRT, at most VPT).
 template <typename TIn, typename TS, int VPT>
 __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
+    using TP = PartialOf<TS>;
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
     const int tid = threadIdx.x;
@@ -797,8 +804,14 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             };
             auto store = [&](int t, int q, const float (&acc)[4]) {
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
-                *reinterpret_cast<float4 *>(a.partial + (th * kR + r) * d_v + 4 * q) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+                TP *dst = reinterpret_cast<TP *>(a.partial) + (th * kR + r) * d_v + 4 * q;
+                if constexpr (std::is_same_v<TP, float>) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                } else {
+                    const _Float16 hv[4] = {static_cast<_Float16>(acc[0]), static_cast<_Float16>(acc[1]),
+                                            static_cast<_Float16>(acc[2]), static_cast<_Float16>(acc[3])};
+                    *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, hv);
+                }
             };
             for (int tb = 0; tb < Cc; tb += TPP) {
                 const int t = tb + tid / RL, q = tid % RL;
@@ -893,8 +906,8 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g) with r the sum of the
 // kRanges partials in range order; one wave per token-head, channel
 // c = lane + 64 i.
-template <typename TIn, typename TO>
-__global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restrict__ partial,
+template <typename TIn, typename TO, typename TP>
+__global__ __launch_bounds__(256) void gate_partials_kernel(const TP *__restrict__ partial,
                                                             const TIn *__restrict__ g, int H,
                                                             int64_t ld_g,
                                                             const float *__restrict__ norm_w,
@@ -906,14 +919,14 @@ __global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restr
     const int nc = d_v / kWave;
     float rv[4];
     float ss = 0.f;
-    const float *pp = partial + th * kR * d_v;
+    const TP *pp = partial + th * kR * d_v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (i < nc) {
             const int c = lane + kWave * i;
             float s = 0.f;
 #pragma unroll
-            for (int q = 0; q < kR; ++q) s += pp[q * d_v + c];
+            for (int q = 0; q < kR; ++q) s += static_cast<float>(pp[q * d_v + c]);
             rv[i] = s;
             ss = fmaf(s, s, ss);
         }
@@ -956,12 +969,14 @@ hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = units * a.T;
     const unsigned g2 = static_cast<unsigned>((n * kWave + 255) / 256);
+    using TP = PartialOf<TS>;
+    const TP *part = reinterpret_cast<const TP *>(a.partial);
     if (a.out_bf16)
-        hipLaunchKernelGGL((gate_partials_kernel<TIn, bf16_t>), dim3(g2), dim3(256), 0, st, a.partial,
+        hipLaunchKernelGGL((gate_partials_kernel<TIn, bf16_t, TP>), dim3(g2), dim3(256), 0, st, part,
                            static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm);
     else
-        hipLaunchKernelGGL((gate_partials_kernel<TIn, TS>), dim3(g2), dim3(256), 0, st, a.partial,
+        hipLaunchKernelGGL((gate_partials_kernel<TIn, TS, TP>), dim3(g2), dim3(256), 0, st, part,
                            static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
                            static_cast<TS *>(a.out), n, a.d_v, a.eps_norm);
     return hipGetLastError();
@@ -1021,7 +1036,7 @@ ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf
         const size_t n = static_cast<size_t>(units) * T;
         q.ws_rbuf = q.ws_sumsq = q.ws_mass = 0;
         q.ws_plan = al256(static_cast<size_t>(units) * q.n_chunks * q.rec_bytes);
-        q.ws_partial = al256(n * kR * d_v * 4);
+        q.ws_partial = al256(n * kR * d_v * (state_bf16 ? 2 : 4));  // fp16 or fp32 partials
         q.ws_spill = al256(static_cast<size_t>(units) * kR * EV * d_v * sbytes);
         q.ok = true;
         // the longest chunk whose typical versions per range (2 EV / kR)
