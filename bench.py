@@ -691,7 +691,7 @@ def main():
         "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        # arithmetic: fp32 (Top-K decisions in fp64); storage in "config"
+        # arithmetic: fp32 (Top-K decisions exact: integer or fp64 logit sums); storage in "config"
         "dtype": "f32", "data": "synthetic",
     })
     for k in ("config", "roofline", "cpu_baseline", "kernels_ms", "algorithmic_bytes",
