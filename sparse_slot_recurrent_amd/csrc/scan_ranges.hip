@@ -71,6 +71,7 @@ constexpr int kR = kRanges;
 constexpr int kRT = 1024;
 constexpr int kPTW = 4;  // walk tasks (16-byte row pieces) per scan thread and round
 constexpr int kLW = 1;   // list entries per kind and thread staged (CAPW = CAPR = kLW * kRT)
+constexpr int kIL = 2;   // row pieces whose write chains a lane walks together
 
 __device__ __forceinline__ int range_of(int slot) { return slot & (kR - 1); }
 
@@ -494,6 +495,62 @@ __device__ __forceinline__ uint4 pack_piece(const float (&x)[8], bf16_t) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Value words of a 16-byte row piece's CP channels (CP * sizeof(TIn) / 4
+// words), loaded as they are stored.
+template <typename TIn, int NW>
+__device__ __forceinline__ void value_words(const TIn *vbuf, int off, uint32_t (&w)[NW]) {
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k) {
+            const u32x4 x = reinterpret_cast<const u32x4 *>(vbuf + off)[k];
+            w[4 * k] = x.x;
+            w[4 * k + 1] = x.y;
+            w[4 * k + 2] = x.z;
+            w[4 * k + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NW / 2; ++k) {
+            const u32x2 x = reinterpret_cast<const u32x2 *>(vbuf + off)[k];
+            w[2 * k] = x.x;
+            w[2 * k + 1] = x.y;
+        }
+    }
+}
+template <int NW> __device__ __forceinline__ float value_at(const uint32_t (&w)[NW], int q, float) {
+    return __uint_as_float(w[q]);
+}
+template <int NW> __device__ __forceinline__ float value_at(const uint32_t (&w)[NW], int q, bf16_t) {
+    return __uint_as_float((q & 1) ? (w[q >> 1] & 0xffff0000u) : (w[q >> 1] << 16));
+}
+
+// One write applied to a row piece held as its stored bits:
+// x <- x + lambda (v - x), rounded to the storage type.
+template <int NW, typename TIn>
+__device__ __forceinline__ uint4 apply_piece(const uint4 &xr, float lam, const uint32_t (&vw)[NW], float, TIn) {
+    const uint32_t w[4] = {xr.x, xr.y, xr.z, xr.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float x = __uint_as_float(w[k]);
+        o[k] = __float_as_uint(fmaf(lam, value_at(vw, k, TIn{}) - x, x));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+template <int NW, typename TIn>
+__device__ __forceinline__ uint4 apply_piece(const uint4 &xr, float lam, const uint32_t (&vw)[NW], bf16_t, TIn) {
+    const uint32_t w[4] = {xr.x, xr.y, xr.z, xr.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float x0 = __uint_as_float(w[k] << 16), x1 = __uint_as_float(w[k] & 0xffff0000u);
+        const float y0 = fmaf(lam, value_at(vw, 2 * k, TIn{}) - x0, x0);
+        const float y1 = fmaf(lam, value_at(vw, 2 * k + 1, TIn{}) - x1, x1);
+        o[k] = static_cast<uint32_t>(bf16_rne(y0).bits) | (static_cast<uint32_t>(bf16_rne(y1).bits) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // The partial reads' type: fp16 where the state (and so the output) is
 // bf16, whose 8 significant bits the 11 of fp16 leave intact; else fp32.
 template <typename TS>
@@ -524,6 +581,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     const int d_v = a.d_v, C = P.C, EV = P.EV;
     const int nchunks = static_cast<int>(P.n_chunks);
     constexpr int CP = 16 / static_cast<int>(sizeof(TS));  // channels per 16-byte piece
+    constexpr int VWP = CP * static_cast<int>(sizeof(TIn)) / 4;  // value words per piece
     const int NP = d_v / CP;                                // pieces per row
     // entry of a walk task (task = entry * NP + piece): a shift when NP is a
     // power of two (d_v 64, 128, 256)
@@ -724,44 +782,66 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 load_entries(c, task0, hc, pe);
                 gather(task0, hc, pe, rw);
             }
+            // pairs of the lane's pieces advance together, one write each
+            // per step, so that their loads overlap (each piece's writes
+            // stay in order).  A piece stays in its stored bits (rw.raw).
 #pragma unroll
-            for (int j = 0; j < kPTW; ++j) {
-                const int task = task0 + tid + j * kRT;
-                const int e = entry_of_task(task), piece = task - e * NP;
-                if (e >= hc.ne()) continue;
-                float x[CP];
-                unpack_chunk(rw.raw[j], x);
-                const int x0 = (pe.nx[j] >> 16) - 1;
-                // (x holds stored values: packing them again gives the same bits)
-                if (x0 >= 0) ver_store(x0, piece * CP, pack_piece(x, TS{}));
-                const int n = pe.nx[j] & 0xffff;
-                if (n == 0) continue;
-                float m = MSL ? ms[pe.slot[j] / kR] : rw.m[j];
-                const int i0 = pe.wo[j] - hc.wb;  // range-local write list index
-                for (int i = i0; i < i0 + n; ++i) {
-                    int tv;
-                    f32x2 wa;
-                    if (i < CAPW) {
-                        tv = s_wtv[i];
-                        wa = s_wwa[i];
-                    } else {
-                        tv = g_wtv[i];
-                        wa = f32x2{g_ww[i], g_wa[i]};
-                    }
-                    const int t = tv & 1023, vr = (tv >> 10) - 1;
-                    float vt[CP];
-                    value_part<CP>(vbuf, t * VROW + piece * CP, vt);
-                    m = fmaf(wa.y, m, wa.x);
-                    const float lam = wa.x * __builtin_amdgcn_rcpf(m + a.eps_gsu);
+            for (int jp = 0; jp < kPTW; jp += kIL) {
+                float m[kIL];
+                int n[kIL], i0[kIL], pc[kIL], nmax = 0;
 #pragma unroll
-                    for (int q = 0; q < CP; ++q) x[q] = stored<TS>(fmaf(lam, vt[q] - x[q], x[q]));
-                    if (vr >= 0) ver_store(vr, piece * CP, pack_piece(x, TS{}));
+                for (int u = 0; u < kIL; ++u) {
+                    const int j = jp + u;
+                    const int task = task0 + tid + j * kRT;
+                    const int e = entry_of_task(task);
+                    const bool live = e < hc.ne();
+                    pc[u] = (task - e * NP) * CP;  // the piece's first channel
+                    const int x0 = live ? (pe.nx[j] >> 16) - 1 : -1;
+                    if (x0 >= 0) ver_store(x0, pc[u], rw.raw[j]);
+                    n[u] = live ? pe.nx[j] & 0xffff : 0;
+                    i0[u] = pe.wo[j] - hc.wb;  // range-local write list index
+                    m[u] = 0.f;
+                    if (n[u]) m[u] = MSL ? ms[pe.slot[j] / kR] : rw.m[j];
+                    nmax = max(nmax, n[u]);
                 }
-                *reinterpret_cast<uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v + piece * CP) =
-                    pack_piece(x, TS{});
-                if (piece == 0) {
-                    if (MSL) ms[pe.slot[j] / kR] = m;
-                    else mass[pe.slot[j]] = m;
+                for (int st = 0; st < nmax; ++st) {
+                    int tv[kIL];
+                    f32x2 wa[kIL];
+                    uint32_t vw[kIL][VWP];
+#pragma unroll
+                    for (int u = 0; u < kIL; ++u) {
+                        // a piece with no write left reads write 0 and keeps its row
+                        const int i = st < n[u] ? i0[u] + st : 0;
+                        if (i < CAPW) {
+                            tv[u] = s_wtv[i];
+                            wa[u] = s_wwa[i];
+                        } else {
+                            tv[u] = g_wtv[i];
+                            wa[u] = f32x2{g_ww[i], g_wa[i]};
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < kIL; ++u) value_words(vbuf, (tv[u] & 1023) * VROW + pc[u], vw[u]);
+#pragma unroll
+                    for (int u = 0; u < kIL; ++u) {
+                        if (st >= n[u]) continue;
+                        const int j = jp + u;
+                        const int vr = (tv[u] >> 10) - 1;
+                        m[u] = fmaf(wa[u].y, m[u], wa[u].x);
+                        const float lam = wa[u].x * __builtin_amdgcn_rcpf(m[u] + a.eps_gsu);
+                        rw.raw[j] = apply_piece(rw.raw[j], lam, vw[u], TS{}, TIn{});
+                        if (vr >= 0) ver_store(vr, pc[u], rw.raw[j]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kIL; ++u) {
+                    const int j = jp + u;
+                    if (n[u] == 0) continue;
+                    *reinterpret_cast<uint4 *>(S + static_cast<int64_t>(pe.slot[j]) * d_v + pc[u]) = rw.raw[j];
+                    if (pc[u] == 0) {
+                        if (MSL) ms[pe.slot[j] / kR] = m[u];
+                        else mass[pe.slot[j]] = m[u];
+                    }
                 }
             }
         }
