@@ -50,9 +50,11 @@ namespace {
 #if defined(__HIP_DEVICE_COMPILE__)
 #define RN_LDS __attribute__((address_space(3)))
 #define RN_GLB __attribute__((address_space(1)))
+#define RN_CONST __attribute__((address_space(4)))
 #else
 #define RN_LDS
 #define RN_GLB
+#define RN_CONST
 #endif
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -107,6 +109,7 @@ __host__ __device__ inline RPlanLds rplan_lds(const ChunkPlan &p, int64_t M) {
 struct RangeHdr {
     int ebase[kR + 1], wbase[kR + 1], rbase[kR + 1], vbase[kR + 1];
 };
+static_assert(sizeof(RangeHdr) == 4 * 4 * (kR + 1), "RangeHdr: four int arrays, no padding");
 
 template <typename TIn, int EPW>
 __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
@@ -481,20 +484,6 @@ __device__ __forceinline__ void load4q(const Q *p, float (&x)[4], bf16_t) {
     x[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
-// A 16-byte row piece (CP channels) from fp32 values into storage type T.
-__device__ __forceinline__ uint4 pack_piece(const float (&x)[4], float) {
-    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
-                      __float_as_uint(x[3]));
-}
-__device__ __forceinline__ uint4 pack_piece(const float (&x)[8], bf16_t) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        w[q] = static_cast<uint32_t>(bf16_rne(x[2 * q]).bits) |
-               (static_cast<uint32_t>(bf16_rne(x[2 * q + 1]).bits) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // Value words of a 16-byte row piece's CP channels (CP * sizeof(TIn) / 4
 // words), loaded as they are stored.
 template <typename TIn, int NW>
@@ -634,20 +623,27 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     // (the header's words are kept as loaded and the counts formed where
     // they are used)
     struct Hdr {
-        int eb, ee, wb, we, rb, re;
+        int eb, ee, wb, we, rb, re, vb, ve;
         __device__ int ne() const { return ee - eb; }
         __device__ int nw() const { return we - wb; }
         __device__ int nr() const { return re - rb; }
+        __device__ int nv() const { return ve - vb; }
     };
+    // (the header is the same for the whole workgroup and is not written
+    // while this kernel runs: scalar loads through the constant address
+    // space keep it in scalar registers)
     auto load_header = [&](int c) {
-        const RangeHdr *hd = reinterpret_cast<const RangeHdr *>(rec_of(c));
+        const RN_CONST int *hd = (const RN_CONST int *)rec_of(c);
+        constexpr int E = 0, W = kR + 1, R = 2 * (kR + 1), V = 3 * (kR + 1);  // RangeHdr's arrays
         Hdr x;
-        x.eb = hd->ebase[r];
-        x.ee = hd->ebase[r + 1];
-        x.wb = hd->wbase[r];
-        x.we = hd->wbase[r + 1];
-        x.rb = hd->rbase[r];
-        x.re = hd->rbase[r + 1];
+        x.eb = hd[E + r];
+        x.ee = hd[E + r + 1];
+        x.wb = hd[W + r];
+        x.we = hd[W + r + 1];
+        x.rb = hd[R + r];
+        x.re = hd[R + r + 1];
+        x.vb = hd[V + r];
+        x.ve = hd[V + r + 1];
         return x;
     };
     int pf_wtv[kLW], pf_rv[kLW], pf_rt = 0;
@@ -769,11 +765,8 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         const RN_GLB float *g_wa = (const RN_GLB float *)(rec + P.o_wa) + hc.wb;
         const RN_GLB int *g_rv = (const RN_GLB int *)(rec + P.o_rv) + hc.rb;
         const RN_GLB float *g_rr = (const RN_GLB float *)(rec + P.o_rr) + hc.rb;
-        // ---- 2. chunk c + 1's header and values go out now
-        if (c + 1 < nchunks) {
-            h_nxt = load_header(c + 1);
-            load_values(c + 1);
-        }
+        // ---- 2. chunk c + 1's header goes out now
+        if (c + 1 < nchunks) h_nxt = load_header(c + 1);
         // ---- 3. walk the range's touched slots, kRT * kPTW row pieces per
         //         round: gather the round's pieces and masses at once, apply
         //         the writes, store the versions reads see, write back
@@ -845,8 +838,11 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 }
             }
         }
-        // ---- 4. chunk c + 1's lists and entries (plan data) go out now
+        // ---- 4. chunk c + 1's values, lists and entries go out now (not
+        //         before the walk: a write step waits for every load in
+        //         flight, so the walk runs with none)
         if (c + 1 < nchunks) {
+            load_values(c + 1);
             load_lists(c + 1, h_nxt);
             load_entries(c + 1, 0, h_nxt, pe);
         }
@@ -862,11 +858,16 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         //         low digits, and so a range) is summed by a whole wave
         //         instead: its lane groups take every G-th read and are added
         //         in a fixed order, so that no group waits on a long list.
-        {
+        // Where the range's reads and version rows all sit in LDS (the usual
+        // case), the reads run in a copy with no global load: a global load
+        // in the loop would make its uses wait for every load in flight,
+        // the next chunk's row gathers included.
+        auto reads = [&](auto lds_only) {
+            constexpr bool LO = decltype(lds_only)::value;
             constexpr int kHeavy = 8;
             const int G = kWave / RL;  // lane groups of a wave
             auto entry = [&](int j, int &vr, float &rho) {
-                if (j < CAPR) {
+                if (LO || j < CAPR) {
                     vr = s_rv[j];
                     rho = s_rr[j];
                 } else {
@@ -876,7 +877,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             };
             auto row = [&](int vr, int q, float (&x)[4]) {
                 const int off = 4 * q * static_cast<int>(sizeof(TS));
-                if (vr < VCAP)
+                if (LO || vr < VCAP)
                     load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
                 else
                     load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
@@ -971,7 +972,9 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                     }
                 }
             }
-        }
+        };
+        if (hc.nr() <= CAPR && hc.nv() <= VCAP) reads(std::true_type{});
+        else reads(std::false_type{});
         // LDS is restaged and the spill area rewritten by the next chunk
         // (every load of this chunk's reads has been consumed by now)
         lds_barrier();
