@@ -484,6 +484,13 @@ __device__ __forceinline__ void load4q(const Q *p, float (&x)[4], bf16_t) {
     x[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
+// Waits for every vector memory access in flight (s_waitcnt vmcnt(0)).
+// Placed inside a rarely taken branch that loads from global memory, so
+// that the common path after the branch has no such load pending: the
+// compiler then adds no wait there, and the loads in flight (prefetches)
+// stay in flight.
+__device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // Value words of a 16-byte row piece's CP channels (CP * sizeof(TIn) / 4
 // words), loaded as they are stored.
 template <typename TIn, int NW>
@@ -811,6 +818,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                         } else {
                             tv[u] = g_wtv[i];
                             wa[u] = f32x2{g_ww[i], g_wa[i]};
+                            wait_vm_loads();
                         }
                     }
 #pragma unroll
@@ -858,30 +866,31 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         //         low digits, and so a range) is summed by a whole wave
         //         instead: its lane groups take every G-th read and are added
         //         in a fixed order, so that no group waits on a long list.
-        // Where the range's reads and version rows all sit in LDS (the usual
-        // case), the reads run in a copy with no global load: a global load
-        // in the loop would make its uses wait for every load in flight,
-        // the next chunk's row gathers included.
-        auto reads = [&](auto lds_only) {
-            constexpr bool LO = decltype(lds_only)::value;
+        // (a read list or version row beyond LDS is loaded from global
+        // memory and waited for in its own branch, so that the common path
+        // does not wait for the next chunk's row gathers)
+        {
             constexpr int kHeavy = 8;
             const int G = kWave / RL;  // lane groups of a wave
             auto entry = [&](int j, int &vr, float &rho) {
-                if (LO || j < CAPR) {
+                if (j < CAPR) {
                     vr = s_rv[j];
                     rho = s_rr[j];
                 } else {
                     vr = g_rv[j];
                     rho = g_rr[j];
+                    wait_vm_loads();
                 }
             };
             auto row = [&](int vr, int q, float (&x)[4]) {
                 const int off = 4 * q * static_cast<int>(sizeof(TS));
-                if (LO || vr < VCAP)
+                if (vr < VCAP) {
                     load4q(reinterpret_cast<const RN_LDS VecOf<TS> *>(ver + vr * rowb + off), x, TS{});
-                else
+                } else {
                     load4q(reinterpret_cast<const RN_GLB VecOf<TS> *>(spill + static_cast<int64_t>(vr) * rowb + off),
                            x, TS{});
+                    wait_vm_loads();
+                }
             };
             auto store = [&](int t, int q, const float (&acc)[4]) {
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
@@ -972,9 +981,7 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                     }
                 }
             }
-        };
-        if (hc.nr() <= CAPR && hc.nv() <= VCAP) reads(std::true_type{});
-        else reads(std::false_type{});
+        }
         // LDS is restaged and the spill area rewritten by the next chunk
         // (every load of this chunk's reads has been consumed by now)
         lds_barrier();
