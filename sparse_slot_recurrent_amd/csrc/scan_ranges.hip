@@ -116,14 +116,7 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const ChunkPlan &P = a.p;
     const int tid = threadIdx.x;
-    // the heads of one (sequence, chunk) are neighbours: their addresses
-    // share cache lines
-    const int h = static_cast<int>(blockIdx.x % a.H);
-    const int chunk = static_cast<int>((blockIdx.x / a.H) % P.n_chunks);
-    const int b = static_cast<int>(blockIdx.x / a.H / P.n_chunks);
-    const int unit = b * a.H + h;
-    const int C = P.C, t0 = chunk * C, Cc = min(C, a.T - t0);
-    const int K = a.K, nev = Cc * K;
+    const int C = P.C, K = a.K;
     const int M = static_cast<int>(a.M);
     const bool hashed = P.HT != 0;
     const int HT = hashed ? P.HT : M;
@@ -143,6 +136,58 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     int *rs0 = wtot + 32;       // first entry id of range r, r <= kR
     int *vb = rs0 + (kR + 1);   // first version row of range r, r <= kR
 
+    // A workgroup plans (unit, chunk) items wi = blockIdx.x, + gridDim.x,
+    // ...; the heads of one (sequence, chunk) are neighbouring items (their
+    // addresses share cache lines).  The next item's events are requested
+    // while this one is planned.
+    const int64_t nwork = static_cast<int64_t>(a.B) * a.H * P.n_chunks;
+    // this thread's events of an item, e = tid + j * kPRT (index t * K + k
+    // within the chunk), writes and reads alike
+    struct Events {
+        int ws[EPW], rs[EPW];
+        float wt[EPW], rtw[EPW], eg[EPW];
+    };
+    auto load_events = [&](int64_t wi, Events &ev) {
+        const int h = static_cast<int>(wi % a.H);
+        const int chunk = static_cast<int>((wi / a.H) % P.n_chunks);
+        const int b = static_cast<int>(wi / a.H / P.n_chunks);
+        const int unit = b * a.H + h;
+        const int t0 = chunk * C, nev = min(C, a.T - t0) * K;
+        const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;
+        const TIn *gam = static_cast<const TIn *>(a.gamma) + static_cast<int64_t>(b) * a.T * a.ld_gamma + h;
+#pragma unroll
+        for (int j = 0; j < EPW; ++j) {
+            const int e = tid + j * kPRT;
+            ev.ws[j] = -1;
+            ev.rs[j] = -1;
+            if (e < nev) {
+                const int t = div_by(e, kdiv), k = e - t * K;
+                const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
+                const int64_t ai = (a.addr_unit_major ? static_cast<int64_t>(unit) * a.T + t0 + t : th) * K + k;
+                ev.ws[j] = a.w_idx[ai];
+                ev.wt[j] = a.w_wt[ai];
+                ev.rs[j] = a.r_idx[ai];
+                ev.rtw[j] = a.r_wt[ai];
+                ev.eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
+            }
+        }
+    };
+    Events cur, nxt;
+    if (static_cast<int64_t>(blockIdx.x) < nwork) load_events(blockIdx.x, cur);
+    for (int64_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+    if (wi + gridDim.x < nwork) load_events(wi + gridDim.x, nxt);
+    // (the thread index is taken afresh per item, so that the compiler does
+    // not keep every address derived from it live across the loop)
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    const int h = static_cast<int>(wi % a.H);
+    const int chunk = static_cast<int>((wi / a.H) % P.n_chunks);
+    const int b = static_cast<int>(wi / a.H / P.n_chunks);
+    const int unit = b * a.H + h;
+    const int t0 = chunk * C, Cc = min(C, a.T - t0);
+    const int nev = Cc * K;
+    (void)t0;
+
     unsigned char *rec = a.plan + (static_cast<int64_t>(unit) * P.n_chunks + chunk) * P.rec_bytes;
     RangeHdr *hdr = reinterpret_cast<RangeHdr *>(rec);
     int *rtoff = reinterpret_cast<int *>(rec + P.o_rt);       // [kR][C + 1], per range
@@ -154,29 +199,12 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     float *wa = reinterpret_cast<float *>(rec + P.o_wa);
     int *rv = reinterpret_cast<int *>(rec + P.o_rv);
     float *rr = reinterpret_cast<float *>(rec + P.o_rr);
-    const int64_t th0 = static_cast<int64_t>(b) * a.T * a.H + h;  // token 0 of the unit
-    const TIn *gam = static_cast<const TIn *>(a.gamma) + static_cast<int64_t>(b) * a.T * a.ld_gamma + h;
+    const int (&ws)[EPW] = cur.ws;
+    const int (&rs)[EPW] = cur.rs;
+    const float (&wt)[EPW] = cur.wt;
+    const float (&rtw)[EPW] = cur.rtw;
+    const float (&eg)[EPW] = cur.eg;
 
-    // ---- 0. this thread's events, e = tid + j * kPRT (index t * K + k within
-    //         the chunk), writes and reads alike; the loads go out first
-    int ws[EPW], rs[EPW];
-    float wt[EPW], rtw[EPW], eg[EPW];
-#pragma unroll
-    for (int j = 0; j < EPW; ++j) {
-        const int e = tid + j * kPRT;
-        ws[j] = -1;
-        rs[j] = -1;
-        if (e < nev) {
-            const int t = div_by(e, kdiv), k = e - t * K;
-            const int64_t th = th0 + static_cast<int64_t>(t0 + t) * a.H;
-            const int64_t ai = (a.addr_unit_major ? static_cast<int64_t>(unit) * a.T + t0 + t : th) * K + k;
-            ws[j] = a.w_idx[ai];
-            wt[j] = a.w_wt[ai];
-            rs[j] = a.r_idx[ai];
-            rtw[j] = a.r_wt[ai];
-            eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
-        }
-    }
     for (int i = tid; i < HT; i += kPRT) {
         tcf[i] = 0;
         if (hashed) tkey[i] = -1;
@@ -442,6 +470,10 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     for (int i = tid; i < nrd; i += kPRT) {
         rv[i] = bk[i];
         rr[i] = __int_as_float(sk[i]);
+    }
+    // the LDS tables are set up again for the next item
+    lds_barrier();
+    cur = nxt;
     }
 }
 
@@ -1048,7 +1080,14 @@ hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
     auto pk = P.EV <= 2048 ? plan_range_kernel<TIn, 2048 / kPRT> : plan_range_kernel<TIn, 3072 / kPRT>;
     hipError_t e = set_lds(pk, P.lds_plan);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(units * P.n_chunks)), dim3(kPRT), P.lds_plan, st, a);
+    // as many plan workgroups as fit the chip at once; each loops over items
+    int dev = 0, ncu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t per_cu = std::max<int64_t>(1, static_cast<int64_t>(kChunkLdsLimit / std::max<size_t>(P.lds_plan, 1)));
+    const int64_t nwork = units * P.n_chunks;
+    const int64_t grid = std::min<int64_t>(nwork, std::max<int64_t>(1, ncu) * per_cu);
+    hipLaunchKernelGGL(pk, dim3(static_cast<unsigned>(grid)), dim3(kPRT), P.lds_plan, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int vpt = (P.C * a.d_v + kRT - 1) / kRT;
     auto sk = vpt <= 4 ? scan_range_kernel<TIn, TS, 4>
