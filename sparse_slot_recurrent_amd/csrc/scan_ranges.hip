@@ -77,12 +77,21 @@ constexpr int kIL = 2;   // row pieces whose write chains a lane walks together
 
 __device__ __forceinline__ int range_of(int slot) { return slot & (kR - 1); }
 
+// Waits for every vector memory access in flight (s_waitcnt vmcnt(0)).
+// Placed where the loads in flight are known to have arrived, or inside a
+// rarely taken branch that loads from global memory, so that the code after
+// it has no such load pending: the compiler then adds no wait there (a wait
+// it adds after stores covers the stores too).
+__device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // LDS of the plan kernel (byte offsets).
 struct RPlanLds {
     size_t key, cf, wo, bk, sk, sa, need, rg, rt, misc, total;
 };
-// The plan kernel of the HBM-row path runs kPRT threads.
+// The plan kernel of the HBM-row path runs kPRT threads; its slot table has
+// at most kPlanSteps * kPRT positions.
 constexpr int kPRT = 1024;
+constexpr int kPlanSteps = 8;
 __host__ __device__ inline RPlanLds rplan_lds(const ChunkPlan &p, int64_t M) {
     RPlanLds L{};
     const size_t ht = p.HT ? static_cast<size_t>(p.HT) : static_cast<size_t>(M);
@@ -145,7 +154,8 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     // within the chunk), writes and reads alike
     struct Events {
         int ws[EPW], rs[EPW];
-        float wt[EPW], rtw[EPW], eg[EPW];
+        float wt[EPW], rtw[EPW];
+        TIn eg[EPW];  // (as stored: a conversion here would wait for the load)
     };
     auto load_events = [&](int64_t wi, Events &ev) {
         const int h = static_cast<int>(wi % a.H);
@@ -168,12 +178,15 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
                 ev.wt[j] = a.w_wt[ai];
                 ev.rs[j] = a.r_idx[ai];
                 ev.rtw[j] = a.r_wt[ai];
-                ev.eg[j] = to_f32(gam[static_cast<int64_t>(t0 + t) * a.ld_gamma]);
+                ev.eg[j] = gam[static_cast<int64_t>(t0 + t) * a.ld_gamma];
             }
         }
     };
     Events cur, nxt;
     if (static_cast<int64_t>(blockIdx.x) < nwork) load_events(blockIdx.x, cur);
+    // (the first item's events are waited for here: otherwise every item's
+    // first use of its events would also wait for the next item's loads)
+    wait_vm_loads();
     for (int64_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
     if (wi + gridDim.x < nwork) load_events(wi + gridDim.x, nxt);
     // (the thread index is taken afresh per item, so that the compiler does
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     const int (&rs)[EPW] = cur.rs;
     const float (&wt)[EPW] = cur.wt;
     const float (&rtw)[EPW] = cur.rtw;
-    const float (&eg)[EPW] = cur.eg;
+    const TIn (&eg)[EPW] = cur.eg;
 
     for (int i = tid; i < HT; i += kPRT) {
         tcf[i] = 0;
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
         if (static_cast<uint32_t>(ws[j]) < static_cast<uint32_t>(M) && wt[j] > 0.f) {
             wpos[j] = entry_of(ws[j]);
             ar[j] = atomicAdd(&tcf[wpos[j]], 1) & (kReadFlag - 1);
-            al[j] = retention_fast(wt[j], expf(eg[j]));
+            al[j] = retention_fast(wt[j], expf(to_f32(eg[j])));
         }
         if (static_cast<uint32_t>(rs[j]) < static_cast<uint32_t>(M)) {
             rpos[j] = entry_of(rs[j]);
@@ -260,16 +273,29 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     //         numbers its entries in that order.  The entry's slot goes to
     //         the record; its write count to ewo.
     int *rsum = vb + (kR + 1);  // packed counts of the ranges before r, r <= kR
+    // this thread's table positions tid + q kPRT (at most kPlanSteps), read
+    // by each pass below with every load out before the first use
     const int nstep = (HT + kPRT - 1) / kPRT;
+    auto read_positions = [&](int (&pc)[kPlanSteps], int (&pk)[kPlanSteps]) {
+#pragma unroll
+        for (int q = 0; q < kPlanSteps; ++q) {
+            const int p = tid + q * kPRT;
+            const bool in = q < nstep && p < HT;
+            pc[q] = in ? tcf[p] : 0;
+            pk[q] = in && hashed ? tkey[p] : p;
+        }
+    };
     {
+        int pc[kPlanSteps], pk[kPlanSteps];
+        read_positions(pc, pk);
         int cnt[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r) cnt[r] = 0;
-        for (int q = 0; q < nstep; ++q) {
-            const int p = tid + q * kPRT;
-            const int c = p < HT ? tcf[p] : 0;
+#pragma unroll
+        for (int q = 0; q < kPlanSteps; ++q) {
+            const int c = pc[q];
             if (c) {
-                const int sr = range_of(hashed ? tkey[p] : p);
+                const int sr = range_of(pk[q]);
                 const int inc = (c & (kReadFlag - 1)) ? 1 : 0x10000;
 #pragma unroll
                 for (int r = 0; r < kR; ++r) cnt[r] += sr == r ? inc : 0;
@@ -294,13 +320,16 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
             nx0[r] = base + (mine & 0xffff) - (pr & 0xffff);
             nx1[r] = base + wr + (mine >> 16) - (pr >> 16);
         }
-        for (int q = 0; q < nstep; ++q) {
+        int pc[kPlanSteps], pk[kPlanSteps];
+        read_positions(pc, pk);
+#pragma unroll
+        for (int q = 0; q < kPlanSteps; ++q) {
             const int p = tid + q * kPRT;
-            if (p >= HT) break;
-            const int c = tcf[p];
+            if (q >= nstep || p >= HT) break;
+            const int c = pc[q];
             int eid = -1;
             if (c) {
-                const int slot = hashed ? tkey[p] : p;
+                const int slot = pk[q];
                 const int sr = range_of(slot);
                 const bool written = (c & (kReadFlag - 1)) != 0;
 #pragma unroll
@@ -381,6 +410,9 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     }
     if (tid == 0) rt[kR * C] = nrd;
     lds_barrier();
+    // the next item's events have long arrived: take them now, before this
+    // item's record stores go out (later, the wait would cover those stores)
+    wait_vm_loads();
 
     // ---- 6. the record: header, per-range token offsets of the reads,
     //         entries, then writes and reads staged in LDS in list order and
@@ -515,13 +547,6 @@ __device__ __forceinline__ void load4q(const Q *p, float (&x)[4], bf16_t) {
     x[2] = __uint_as_float(u.y << 16);
     x[3] = __uint_as_float(u.y & 0xffff0000u);
 }
-
-// Waits for every vector memory access in flight (s_waitcnt vmcnt(0)).
-// Placed inside a rarely taken branch that loads from global memory, so
-// that the common path after the branch has no such load pending: the
-// compiler then adds no wait there, and the loads in flight (prefetches)
-// stay in flight.
-__device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Value words of a 16-byte row piece's CP channels (CP * sizeof(TIn) / 4
 // words), loaded as they are stored.
@@ -1141,6 +1166,7 @@ ChunkPlan plan_ranges(int64_t M, int K, int d_v, int B, int T, int H, bool in_bf
             while (ht * 3 < 2 * EV * 4) ht *= 2;
             q.HT = ht;
         }
+        if ((q.HT ? q.HT : M) > kPlanSteps * kPRT) continue;  // (not reached: EV <= 3072, M <= 4096)
         q.CAPW = q.CAPR = std::min(EV, kLW * kRT);
         q.VCAP = 0;
         // the range's masses stay in LDS where they take at most 32 KiB
