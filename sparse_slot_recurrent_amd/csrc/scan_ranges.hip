@@ -232,11 +232,16 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     //         contributes nothing.
     auto entry_of = [&](int s) -> int {
         if (!hashed) return s;
+        // double hashing: an odd step (from a second multiplicative hash)
+        // visits every position of the power-of-two table, and probe runs
+        // stay short at the table's load of up to 3/4, where linear probing
+        // builds long clusters (a wave waits for its longest probe run)
         uint32_t hp = (static_cast<uint32_t>(s) * 2654435761u) >> hsh;
-        for (;;) {  // linear probing; the table is at most 3/4 full
+        const uint32_t step = ((static_cast<uint32_t>(s) * 0x85ebca6bu) >> hsh) | 1u;
+        for (;;) {
             const int old = atomicCAS(&tkey[hp], -1, s);
             if (old == -1 || old == s) return static_cast<int>(hp);
-            hp = (hp + 1) & static_cast<uint32_t>(HT - 1);
+            hp = (hp + step) & static_cast<uint32_t>(HT - 1);
         }
     };
     int wpos[EPW], ar[EPW], rpos[EPW];
