@@ -332,18 +332,21 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
             const int p = tid + q * kPRT;
             if (q >= nstep || p >= HT) break;
             const int c = pc[q];
+            const int slot = pk[q];
+            const int sr = range_of(slot);
+            const bool written = (c & (kReadFlag - 1)) != 0;
+            // the range's next written or read-only id, by selects (no
+            // branch per range)
             int eid = -1;
-            if (c) {
-                const int slot = pk[q];
-                const int sr = range_of(slot);
-                const bool written = (c & (kReadFlag - 1)) != 0;
 #pragma unroll
-                for (int r = 0; r < kR; ++r) {
-                    if (sr == r) {
-                        if (written) eid = nx0[r]++;
-                        else eid = nx1[r]++;
-                    }
-                }
+            for (int r = 0; r < kR; ++r) {
+                const bool m0 = c != 0 && sr == r && written;
+                const bool m1 = c != 0 && sr == r && !written;
+                eid = m0 ? nx0[r] : m1 ? nx1[r] : eid;
+                nx0[r] += m0 ? 1 : 0;
+                nx1[r] += m1 ? 1 : 0;
+            }
+            if (c) {
                 ewo[eid] = c & (kReadFlag - 1);
                 ent_slot[eid] = slot;
             }
