@@ -10,9 +10,12 @@
 // A unit's (batch, head) slots are split into kRanges ranges by slot mod
 // kRanges, and its sequence into chunks of C tokens.
 //
-// plan_range_kernel: one workgroup per (unit, chunk), all chunks at once
-// (grouping does not depend on the state).  Every valid event finds its
-// slot's entry in an LDS table; entries are numbered range by range, so that
+// plan_range_kernel: the (unit, chunk) items are planned all at once
+// (grouping does not depend on the state), by as many workgroups as fit the
+// chip, each looping over items with the next item's events in flight.
+// Every valid event finds its slot's entry in an LDS table (the slot itself,
+// or a double-hashed table for a large state); entries are numbered range by
+// range, so that
 // each range's entries, its write list (in (slot, token) order, each write
 // with its retention alpha = (1 - w)^exp(gamma_t)), the versions its reads
 // see and its reads (grouped by token) are contiguous sections of the record.
@@ -23,11 +26,12 @@
 //   * The range's write and read lists and the chunk's value rows are staged
 //     in LDS (loaded one chunk ahead).
 //   * Walk: every touched slot's row is gathered whole from HBM, one 16-byte
-//     piece per lane, together with its mass (one request per row and one
-//     per mass).  The lanes of a slot each apply its writes to their piece
-//     (each computing the same mass and rate), store the versions reads see
-//     in LDS (later ones in a spill area) and write the row and mass back.
-//     A slot belongs to one range, so the mass is updated in place.
+//     piece per lane (the first round's rows during the previous chunk's
+//     reads); the range's masses stay in LDS where they fit.  The lanes of a
+//     slot each apply its writes to their piece (each computing the same
+//     mass and rate), two pieces per lane in step, store the versions reads
+//     see in LDS (later ones in a spill area) and write the row and mass
+//     back.  A slot belongs to one range, so the mass is updated in place.
 //   * Reads: per token, four channels per lane, the range's reads summed in
 //     address order (rho * version); every token's partial (zero when the
 //     range holds none of its reads) goes to the workspace, in fp16 where the
