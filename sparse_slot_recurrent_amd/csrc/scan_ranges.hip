@@ -1062,47 +1062,76 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     }
 }
 
+// Four consecutive partial-read channels as fp32 (8 bytes of fp16, 16 of
+// fp32), and four outputs stored at once.
+__device__ __forceinline__ void load4p(const _Float16 *p, float (&x)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    const _Float16 *h = reinterpret_cast<const _Float16 *>(&u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = static_cast<float>(h[i]);
+}
+__device__ __forceinline__ void load4p(const float *p, float (&x)[4]) {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    x[0] = f.x;
+    x[1] = f.y;
+    x[2] = f.z;
+    x[3] = f.w;
+}
+__device__ __forceinline__ void store4(float *p, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4(bf16_t *p, const float (&x)[4]) {
+    const uint32_t w0 = static_cast<uint32_t>(bf16_rne(x[0]).bits) | (static_cast<uint32_t>(bf16_rne(x[1]).bits) << 16);
+    const uint32_t w1 = static_cast<uint32_t>(bf16_rne(x[2]).bits) | (static_cast<uint32_t>(bf16_rne(x[3]).bits) << 16);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(w0, w1);
+}
+
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g) with r the sum of the
-// kRanges partials in range order; one wave per token-head, channel
-// c = lane + 64 i.
-template <typename TIn, typename TO, typename TP>
+// kRanges partials in range order.  A token-head takes d_v / 4 lanes of a
+// group of G (a power of two), four consecutive channels per lane, so that
+// every partial is read in 8- or 16-byte pieces; 64 / G token-heads per wave.
+template <typename TIn, typename TO, typename TP, int G>
 __global__ __launch_bounds__(256) void gate_partials_kernel(const TP *__restrict__ partial,
                                                             const TIn *__restrict__ g, int H,
                                                             int64_t ld_g,
                                                             const float *__restrict__ norm_w,
                                                             TO *__restrict__ out, int64_t n, int d_v,
                                                             float eps) {
-    const int64_t th = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int lane = threadIdx.x % kWave;
-    if (th >= n) return;  // whole waves
-    const int nc = d_v / kWave;
-    float rv[4];
+    const int64_t th = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave * (kWave / G) + lane / G;
+    const int q = lane % G, c = 4 * q;
+    const bool act = th < n && c < d_v;
+    float rv[4] = {0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
-    const TP *pp = partial + th * kR * d_v;
+    if (act) {
+        const TP *pp = partial + th * kR * d_v + c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i < nc) {
-            const int c = lane + kWave * i;
-            float s = 0.f;
+        for (int r = 0; r < kR; ++r) {
+            float x[4];
+            load4p(pp + r * d_v, x);
 #pragma unroll
-            for (int q = 0; q < kR; ++q) s += static_cast<float>(pp[q * d_v + c]);
-            rv[i] = s;
-            ss = fmaf(s, s, ss);
+            for (int i = 0; i < 4; ++i) rv[i] += x[i];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fmaf(rv[i], rv[i], ss);
     }
-    ss = wave_sum(ss);
+    // (every lane takes part in the group's sum)
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if (!act) return;
     const float den = ss / static_cast<float>(d_v) + eps;
     const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-    const TIn *gp = g + (th / H) * ld_g + (th % H) * d_v;
+    const TIn *gp = g + (th / H) * ld_g + (th % H) * d_v + c;
+    float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (i < nc) {
-            const int c = lane + kWave * i;
-            const float om = norm_w ? norm_w[c] : 1.0f;
-            out[th * d_v + c] = from_f32<TO>(rv[i] * inv * om * sigmoid(to_f32(gp[c])));
-        }
+        const float om = norm_w ? norm_w[c + i] : 1.0f;
+        o[i] = rv[i] * inv * om * sigmoid(to_f32(gp[i]));
     }
+    store4(out + th * d_v + c, o);
 }
+
+template <typename T> struct TypeTag { using type = T; };
 
 template <typename K>
 hipError_t set_lds(K kern, size_t lds) {
@@ -1134,17 +1163,24 @@ hipError_t launch_ranges_typed(const ChunkArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(sk, dim3(static_cast<unsigned>(units * kR)), dim3(kRT), P.lds_scan, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = units * a.T;
-    const unsigned g2 = static_cast<unsigned>((n * kWave + 255) / 256);
     using TP = PartialOf<TS>;
     const TP *part = reinterpret_cast<const TP *>(a.partial);
-    if (a.out_bf16)
-        hipLaunchKernelGGL((gate_partials_kernel<TIn, bf16_t, TP>), dim3(g2), dim3(256), 0, st, part,
-                           static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
-                           static_cast<bf16_t *>(a.out_bf16), n, a.d_v, a.eps_norm);
-    else
-        hipLaunchKernelGGL((gate_partials_kernel<TIn, TS, TP>), dim3(g2), dim3(256), 0, st, part,
-                           static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
-                           static_cast<TS *>(a.out), n, a.d_v, a.eps_norm);
+    // a token-head's lanes: d_v / 4, in a group of G (d_v is 64 ... 256)
+    auto gate = [&](auto gt, auto out_t, void *o) {
+        constexpr int G = decltype(gt)::value;
+        using TO = typename decltype(out_t)::type;
+        const int64_t waves = (n + kWave / G - 1) / (kWave / G);
+        hipLaunchKernelGGL((gate_partials_kernel<TIn, TO, TP, G>), dim3(static_cast<unsigned>((waves * kWave + 255) / 256)),
+                           dim3(256), 0, st, part, static_cast<const TIn *>(a.g), a.H, a.ld_g, a.norm_w,
+                           static_cast<TO *>(o), n, a.d_v, a.eps_norm);
+    };
+    auto gate_out = [&](auto out_t, void *o) {
+        if (a.d_v <= 64) gate(std::integral_constant<int, 16>{}, out_t, o);
+        else if (a.d_v <= 128) gate(std::integral_constant<int, 32>{}, out_t, o);
+        else gate(std::integral_constant<int, 64>{}, out_t, o);
+    };
+    if (a.out_bf16) gate_out(TypeTag<bf16_t>{}, a.out_bf16);
+    else gate_out(TypeTag<TS>{}, a.out);
     return hipGetLastError();
 }
 

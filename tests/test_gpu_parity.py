@@ -250,6 +250,10 @@ def test_prefill_with_oracle_addresses(rn, orc, name):
     (4, 5, 16, 64, "f32", 300, 40, 1, 2),
     (4, 6, 8, 64, "bf16", 700, 300, 1, 2),    # 4096 slots: rows in HBM, slot-indexed plan table
     (4, 8, 16, 64, "bf16", 300, 5000, 1, 2),  # 65536 slots: rows in HBM, hashed plan table
+    # rows in HBM at wider rows: fp32 partials and 32-lane norm groups
+    # (d_v 128), 64-lane groups and an odd number of units (d_v 256)
+    (4, 6, 8, 128, "f32", 300, 300, 1, 2),
+    (2, 12, 16, 256, "bf16", 200, 500, 1, 3),
     # 64 units: 16-channel slices, hand-off with four lanes per fp32 row
     # (256 slots) and two lanes per bf16 row (1024 slots)
     (4, 4, 8, 64, "f32", 300, 60, 8, 8),
