@@ -699,18 +699,17 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
     // (the header's words are kept as loaded and the counts formed where
     // they are used)
     struct Hdr {
-        int eb, ee, wb, we, rb, re, vb, ve;
+        int eb, ee, wb, we, rb, re;
         __device__ int ne() const { return ee - eb; }
         __device__ int nw() const { return we - wb; }
         __device__ int nr() const { return re - rb; }
-        __device__ int nv() const { return ve - vb; }
     };
     // (the header is the same for the whole workgroup and is not written
     // while this kernel runs: scalar loads through the constant address
     // space keep it in scalar registers)
     auto load_header = [&](int c) {
         const RN_CONST int *hd = (const RN_CONST int *)rec_of(c);
-        constexpr int E = 0, W = kR + 1, R = 2 * (kR + 1), V = 3 * (kR + 1);  // RangeHdr's arrays
+        constexpr int E = 0, W = kR + 1, R = 2 * (kR + 1);  // RangeHdr's arrays
         Hdr x;
         x.eb = hd[E + r];
         x.ee = hd[E + r + 1];
@@ -718,8 +717,6 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
         x.we = hd[W + r + 1];
         x.rb = hd[R + r];
         x.re = hd[R + r + 1];
-        x.vb = hd[V + r];
-        x.ve = hd[V + r + 1];
         return x;
     };
     int pf_wtv[kLW], pf_rv[kLW], pf_rt = 0;
