@@ -110,8 +110,12 @@ def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
     for b in range(B):
         for h in range(H):
             form = 0 if (content_heads >> min(h, 63)) & 1 else cape
-            rows = list(tS0[b, h].unbind(0))
-            mass = list(tm0[b, h].unbind(0))
+            # the rows and masses the unit has written so far, by slot; every
+            # other slot still holds its starting value
+            base_rows, base_mass = tS0[b, h].unbind(0), tm0[b, h].unbind(0)
+            rows, mass = {}, {}
+            row_of = lambda i: rows[i] if i in rows else base_rows[i]
+            mass_of = lambda i: mass[i] if i in mass else base_mass[i]
             unit_out = []
             for t in range(T):
                 P = int(pos0[b]) + t
@@ -125,19 +129,26 @@ def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
                     if not float(w.detach()) > 0.0:
                         continue
                     i = int(wi[j])
-                    mass[i] = retention(w, e) * mass[i] + w
+                    mass[i] = retention(w, e) * mass_of(i) + w
                     if round_storage:
                         mass[i] = stored(mass[i], False)
                     lam = w / (mass[i] + eps_gsu)
-                    rows[i] = rows[i] + lam * (tv[b, t, h] - rows[i])
+                    rows[i] = row_of(i) + lam * (tv[b, t, h] - row_of(i))
                     if round_storage:
                         rows[i] = stored(rows[i], state_bf16)
-                r = sum(rw[j] * rows[int(ri[j])] for j in range(K))
+                r = sum(rw[j] * row_of(int(ri[j])) for j in range(K))
                 inv = torch.rsqrt(torch.mean(r * r) + eps_norm)
                 unit_out.append(r * inv * tom * torch.sigmoid(tg[b, t, h]))
             outs.append(torch.stack(unit_out))
-            S_fin.append(torch.stack(rows))
-            m_fin.append(torch.stack(mass))
+            # the final state: the starting one with the written slots replaced
+            ws = sorted(rows)
+            if ws:
+                sel = torch.as_tensor(ws, dtype=torch.int64)
+                S_fin.append(tS0[b, h].index_put((sel,), torch.stack([rows[i] for i in ws])))
+                m_fin.append(tm0[b, h].index_put((sel,), torch.stack([mass[i] for i in ws])))
+            else:
+                S_fin.append(tS0[b, h] * 1.0)
+                m_fin.append(tm0[b, h] * 1.0)
     out = torch.stack(outs).view(B, H, T, d_v).permute(0, 2, 1, 3)
     S_f = torch.stack(S_fin).view(B, H, M, d_v)
     m_f = torch.stack(m_fin).view(B, H, M)
