@@ -19,10 +19,10 @@ measured one.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload prefill_top8|prefill_top32|large_state|decode
                                    |layer_top8|layer_decode|backward_top8
-                                   |backward_top32]
+                                   |backward_top32|backward_large_state]
 --workload runs that workload alone (no sub-records).  The layer_* workloads
 add the dense projections either side (the whole layer); backward_top8 /
-backward_top32 time the gradients of those prefills.
+backward_top32 / backward_large_state time the gradients of those prefills.
 """
 from __future__ import annotations
 
@@ -415,7 +415,8 @@ def layer_model(w, D, kind: str):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 # Backward workloads: a prefill configuration's gradients (fp32 state).
-BACKWARD = {"backward_top8": "prefill_top8", "backward_top32": "prefill_top32"}
+BACKWARD = {"backward_top8": "prefill_top8", "backward_top32": "prefill_top32",
+            "backward_large_state": "large_state"}
 
 
 def backward_model(w):
@@ -434,6 +435,11 @@ def backward_model(w):
     b_s = 2 if w.state_dtype == "bf16" else 4
     state = units * (w.M * w.d_v * (b_s + 4) + 8 * w.M)  # S0 read, dS0 (fp32) written
     records = n * (2 * w.K * w.d_v * 4 + 4 * w.K) * 2  # written by the replay, read back
+    if w.M > 1024 or w.d_v != 64:
+        # the per-token walk keeps the state in HBM: per token-head the replay
+        # reads and writes K write rows and reads K read rows, and the adjoint
+        # reads and writes K rows of dS (fp32) for the writes and K for the reads
+        state += n * w.K * w.d_v * (3 * b_s + 4 * 4)
     return {"backward": n * per_th + state, "records": records}
 
 

@@ -218,9 +218,15 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
  * gradient through.  The gradients are those of
  *   sum(out * dout) + sum(S_final * dS_final) + sum(mass_final * dmass_final)
  * with respect to the inputs and the state the forward started from.
- * Built for d_v = 64, M <= 1024 and U*d_p <= 64 (RAMNET_EUNSUPPORTED
- * otherwise); the state may be fp32 or bf16 (the replay rounds it as the
- * forward does), the gradients are fp32.
+ * Built for every d_v and M the forward takes, with U*d_p <= 64
+ * (RAMNET_EUNSUPPORTED otherwise); the state may be fp32 or bf16 (the replay
+ * rounds it as the forward does), the gradients are fp32.  d_v = 64 with
+ * M <= 1024 keeps each slot's row and adjoint on chip and walks the events
+ * grouped by slot; every other shape walks the tokens one by one, with the
+ * replayed state in the workspace and the adjoint accumulated in dS0 and
+ * dmass0 (which then start as dS_final and dmass_final), so it is far slower
+ * per token.  A token may write one slot twice (caller-given addresses): the
+ * writes apply in address order, as in the forward.
  *   q, k, v, gamma, g, norm_w, pos0   the forward's inputs (q, k only read
  *             when dq, dk are given)
  *   S0, mass0 [B,H,M,d_v] state_dtype, [B,H,M] fp32: the state before the
@@ -233,7 +239,8 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
  *   workspace ramnet_workspace_bytes(p, RAMNET_OP_BACKWARD) bytes: the
  *             forward is replayed from S0 and, per token-head, each write's
  *             row and mass before it and each read's row are recorded
- *             ((2 K d_v + 3 K) fp32).
+ *             ((2 K d_v + 3 K) fp32); the token walk adds a copy of S0 and
+ *             mass0.
  * Every sum is taken in a fixed order: repeated calls give the same bits. */
 ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q,
                                    const void *k, const void *v,

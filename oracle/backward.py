@@ -83,12 +83,18 @@ def retention(w, e):
 def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
                 cape: int = 1, pos0=None, norm_w=None, eps_gsu: float = 1e-6,
                 eps_norm: float = 1e-6, content_heads: int = 0, dS_final=None,
-                dm_final=None, round_storage: bool = False, state_bf16: bool = False):
+                dm_final=None, round_storage: bool = False, state_bf16: bool = False,
+                addresses=None):
     """Inputs as for oracle.layer (q, k [B,T,H,U*d_p], v, g [B,T,H,d_v],
     gamma [B,T,H], S0 [B,H,M,d_v], m0 [B,H,M]) plus dout [B,T,H,d_v].
     Returns a dict of fp64 numpy arrays: out, S, mass (the forward), the
     addresses used (w_idx, r_idx post-CAPE, and the oracle's gaps), and the
-    gradients dq, dk, dv, dgamma, dg, dS0, dm0, dnorm_w."""
+    gradients dq, dk, dv, dgamma, dg, dS0, dm0, dnorm_w.
+
+    addresses: None (the exact Top-K of the logits), or given post-CAPE write
+    and read slots (w_idx, r_idx), [B,T,H,K] each, as the backward entry
+    point takes them; their weights are still the Product Softmax weights of
+    the slots' content digits, and the gaps returned are then +inf."""
     q, k, v, gamma, g = (np.asarray(x, np.float64) for x in (q, k, v, gamma, g))
     B, T, H, L = q.shape
     d_v = v.shape[-1]
@@ -99,6 +105,10 @@ def layer_grads(q, k, v, gamma, g, S0, m0, dout, *, d_p: int, U: int, K: int,
                                     pos0=pos0.astype(np.int32), content_heads=content_heads)
     r_idx, _, r_gap = _o.decode_all(q.astype(np.float32), U, d_p, K, cape=cape,
                                     pos0=pos0.astype(np.int32), content_heads=content_heads)
+    if addresses is not None:
+        w_idx, r_idx = (np.asarray(a, np.int32) for a in addresses)
+        w_gap = np.full(w_idx.shape[:3], np.inf)
+        r_gap = np.full(r_idx.shape[:3], np.inf)
 
     leaf = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
     tq, tk, tv, tgam, tg = leaf(q), leaf(k), leaf(v), leaf(gamma), leaf(g)

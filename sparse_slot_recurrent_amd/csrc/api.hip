@@ -748,7 +748,8 @@ size_t ramnet_workspace_bytes(const ramnet_params *p, int32_t op) {
     if (op == RAMNET_OP_DECODE) return 0;
     if (op == RAMNET_OP_BACKWARD)
         return ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, p->state_dtype == RAMNET_BF16)
-                   ? ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K)
+                   ? ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K, p->M, p->d_v,
+                                                      p->state_dtype == RAMNET_BF16)
                    : 0;
     if (op != RAMNET_OP_PREFILL && op != RAMNET_OP_STEP) return 0;
     return plan_layer(p, step, true, true).total();
@@ -765,8 +766,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     ramnet_status s = check_params(p, false);
     if (s) return s;
     if (!ramnet::backward_supported(p->M, p->d_v, p->U, p->d_p, p->state_dtype == RAMNET_BF16))
-        return fail(RAMNET_EUNSUPPORTED,
-                    "the backward pass is built for d_v = 64, M <= 1024 and U*d_p <= 64");
+        return fail(RAMNET_EUNSUPPORTED, "the backward pass is built for U*d_p <= 64");
     const int64_t n = static_cast<int64_t>(p->B) * p->T * p->H;
     const int64_t units = static_cast<int64_t>(p->B) * p->H;
     if (n == 0) return ok();
@@ -784,7 +784,8 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
         return s;
     if (dq && (s = check_ptr("q", q, true))) return s;
     if (dk && (s = check_ptr("k", k, true))) return s;
-    const size_t need = ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K);
+    const size_t need = ramnet::backward_workspace_bytes(p->B, p->T, p->H, p->K, p->M, p->d_v,
+                                                         p->state_dtype == RAMNET_BF16);
     if (!workspace || workspace_bytes < need)
         return fail(RAMNET_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : size_t(0));
@@ -831,6 +832,7 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     a.K = p->K;
     a.U = p->U;
     a.d_p = p->d_p;
+    a.d_v = p->d_v;
     a.cape = p->cape;
     a.content_heads = p->content_heads;
     a.in_bf16 = p->in_dtype == RAMNET_BF16;
@@ -875,6 +877,13 @@ ramnet_status ramnet_scan_backward(const ramnet_params *p, const void *q, const 
     a.dvk = reinterpret_cast<float *>(w2);
     w2 += rows;
     a.dgk = reinterpret_cast<float *>(w2);
+    w2 += align256(nK4);
+    if (!ramnet::backward_slot_owner(p->M, p->d_v)) {
+        // the per-token walk's replayed state and mass
+        a.Sw = w2;
+        w2 += align256(st * p->d_v * st_bytes(p));
+        a.mw = reinterpret_cast<float *>(w2);
+    }
     return hip_status(ramnet::launch_backward(a, static_cast<hipStream_t>(stream)),
                       "backward launch");
 }

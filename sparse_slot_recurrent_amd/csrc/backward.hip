@@ -46,6 +46,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace ramnet {
 namespace {
 
@@ -327,79 +329,117 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_record_kernel(BwdArgs a) {
 }
 
 // Output gate, RMSNorm and read, for all tokens at once (they need only the
-// recorded read rows): one wave per token-head, lane c = channel c.  Writes
-// dg, dr (the read's adjoint, for the serial kernel) and d rho; each wave
-// sums its tokens' d omega, and the workgroup's sum goes to a partial.
+// recorded read rows): one wave per token-head, lane c holding channels
+// c, c + 64, ... (DV / 64 of them).  Writes dg, dr (the read's adjoint, for
+// the serial kernel) and d rho; each wave sums its tokens' d omega, and the
+// workgroup's sum goes to a partial.
 constexpr int kOutWaves = 16, kOutBlocks = kBwdOutBlocks;
 
-template <typename TIn>
+template <typename TIn, int DV>
 __global__ __launch_bounds__(kOutWaves * kWave) void bwd_out_kernel(BwdArgs a) {
-    __shared__ float sdom[kOutWaves][kBwdDv];
+    constexpr int CPL = DV / kWave;
+    __shared__ float sdom[kOutWaves][DV];
     const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
     const int wave = threadIdx.x / kWave, c = threadIdx.x % kWave;
     const int K = a.K, T = a.T;
     const TIn *gg = static_cast<const TIn *>(a.g);
-    const float om = a.norm_w ? a.norm_w[c] : 1.0f;
-    float dom = 0.f;
+    float om[CPL], dom[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        om[i] = a.norm_w ? a.norm_w[c + kWave * i] : 1.0f;
+        dom[i] = 0.f;
+    }
     for (int t = blockIdx.y * kOutWaves + wave; t < T; t += kOutBlocks * kOutWaves) {
         const int64_t th = (static_cast<int64_t>(b) * T + t) * a.H + h;
-        const float *rr = a.rec_r + (static_cast<int64_t>(unit) * T + t) * K * kBwdDv + c;
+        const float *rr = a.rec_r + (static_cast<int64_t>(unit) * T + t) * K * DV + c;
         // lane k holds rho_k; rows load eight at a time (K <= 64)
         const float rw = a.r_wt[th * K + (c < K ? c : 0)];
-        float r = 0.f;
-        for (int k0 = 0; k0 < K; k0 += 8) {
-            float x[8];
+        float r[CPL];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? rr[(k0 + j) * kBwdDv] : 0.f;
+        for (int i = 0; i < CPL; ++i) r[i] = 0.f;
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float x[8][CPL];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (k0 + j < K) r = fmaf(bcast(rw, k0 + j), x[j], r);
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) x[j][i] = k0 + j < K ? rr[(k0 + j) * DV + kWave * i] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (k0 + j < K) {
+                    const float rho = bcast(rw, k0 + j);
+#pragma unroll
+                    for (int i = 0; i < CPL; ++i) r[i] = fmaf(rho, x[j][i], r[i]);
+                }
         }
-        const float den = wave_sum(r * r) / static_cast<float>(kBwdDv) + a.eps_norm;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) ss = fmaf(r[i], r[i], ss);
+        const float den = wave_sum(ss) / static_cast<float>(DV) + a.eps_norm;
         const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-        const float y = r * inv;
-        const float sg = sigmoid(to_f32(gg[th * kBwdDv + c]));
-        const float d_o = a.dout[th * kBwdDv + c];
-        a.dg[th * kBwdDv + c] = d_o * om * y * sg * (1.0f - sg);
-        dom = fmaf(d_o * y, sg, dom);
-        const float dy = d_o * om * sg;
-        const float dyy = wave_sum(dy * y) / static_cast<float>(kBwdDv);
-        const float dr = inv * (dy - y * dyy);
-        a.dr[th * kBwdDv + c] = dr;
+        float y[CPL], dy[CPL], dr[CPL];
+        float dyy = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int64_t o = th * DV + c + kWave * i;
+            y[i] = r[i] * inv;
+            const float sg = sigmoid(to_f32(gg[o]));
+            const float d_o = a.dout[o];
+            a.dg[o] = d_o * om[i] * y[i] * sg * (1.0f - sg);
+            dom[i] = fmaf(d_o * y[i], sg, dom[i]);
+            dy[i] = d_o * om[i] * sg;
+            dyy = fmaf(dy[i], y[i], dyy);
+        }
+        dyy = wave_sum(dyy) / static_cast<float>(DV);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            dr[i] = inv * (dy[i] - y[i] * dyy);
+            a.dr[th * DV + c + kWave * i] = dr[i];
+        }
         if (K >= 16) {
             // lane k takes <dr, S_jk> over its recorded row, dr broadcast
             // channel by channel (cheaper than K wave reductions)
             const int kk = c < K ? c : 0;
-            const Row4 *rk = reinterpret_cast<const Row4 *>(rr - c + kk * kBwdDv);
+            const Row4 *rk = reinterpret_cast<const Row4 *>(rr - c + kk * DV);
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < kBwdDv / 4; ++j) {
-                const Row4 x = rk[j];
+            for (int i = 0; i < CPL; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc = fmaf(bcast(dr, 4 * j + q), x.e[q], acc);
-            }
+                for (int j = 0; j < kWave / 4; ++j) {
+                    const Row4 x = rk[i * (kWave / 4) + j];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = fmaf(bcast(dr[i], 4 * j + q), x.e[q], acc);
+                }
             if (c < K) a.drho[th * K + c] = acc;
         } else {
             for (int k0 = 0; k0 < K; k0 += 8) {
-                float x[8];
+                float x[8][CPL];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? rr[(k0 + j) * kBwdDv] : 0.f;
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < CPL; ++i) x[j][i] = k0 + j < K ? rr[(k0 + j) * DV + kWave * i] : 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (k0 + j < K) {
-                        const float dk = wave_sum(dr * x[j]);
+                        float part = 0.f;
+#pragma unroll
+                        for (int i = 0; i < CPL; ++i) part = fmaf(dr[i], x[j][i], part);
+                        const float dk = wave_sum(part);
                         if (c == 0) a.drho[th * K + k0 + j] = dk;
                     }
                 }
             }
         }
     }
-    sdom[wave][c] = dom;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sdom[wave][c + kWave * i] = dom[i];
     __syncthreads();
     if (wave == 0) {
-        float acc = 0.f;
-        for (int w2 = 0; w2 < kOutWaves; ++w2) acc += sdom[w2][c];
-        a.dom_part[(static_cast<int64_t>(unit) * kOutBlocks + blockIdx.y) * kBwdDv + c] = acc;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            float acc = 0.f;
+            for (int w2 = 0; w2 < kOutWaves; ++w2) acc += sdom[w2][c + kWave * i];
+            a.dom_part[(static_cast<int64_t>(unit) * kOutBlocks + blockIdx.y) * DV + c + kWave * i] = acc;
+        }
     }
 }
 
@@ -518,8 +558,11 @@ __global__ __launch_bounds__(kThreadsOf<HV>) void bwd_adjoint_kernel(BwdArgs a) 
 }
 
 // dv and dgamma of every token: the sums over its writes of lam dS+ and of
-// the gamma terms, in write order (one wave per token-head, lane = channel).
+// the gamma terms, in write order (one wave per token-head, lane c holding
+// channels c, c + 64, ...).
+template <int DV>
 __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
+    constexpr int CPL = DV / kWave;
     const int64_t n = static_cast<int64_t>(a.B) * a.T * a.H;
     const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
     const int c = threadIdx.x % kWave, K = a.K;
@@ -534,17 +577,25 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(BwdArgs a) {
     const bool mine = c < K && a.w_wt[th * K + kk] > 0.f && slot >= 0 && slot < a.M;
     const uint64_t ok = __ballot(mine);
     const float gk = mine ? a.dgk[rec + kk] : 0.f;
-    const float *dv = a.dvk + rec * kBwdDv + c;
-    float acc = 0.f;
-    for (int k0 = 0; k0 < K; k0 += 8) {
-        float x[8];
+    const float *dv = a.dvk + rec * DV + c;
+    float acc[CPL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = k0 + j < K ? dv[static_cast<int64_t>(k0 + j) * kBwdDv] : 0.f;
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        float x[8][CPL];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            if ((ok >> (k0 + j)) & 1u) acc += x[j];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                x[j][i] = k0 + j < K ? dv[static_cast<int64_t>(k0 + j) * DV + kWave * i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if ((ok >> (k0 + j)) & 1u)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) acc[i] += x[j][i];
     }
-    a.dv[th * kBwdDv + c] = acc;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) a.dv[th * DV + c + kWave * i] = acc[i];
     const float gacc = wave_sum(gk);
     if (c == 0) a.dgamma[th] = gacc;
 }
@@ -666,24 +717,433 @@ hipError_t launch_logits(const BwdArgs &a, dim3 grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Sums the partials [n][64] in a fixed order: 16 groups of 64 threads take
+// Sums the partials [n][DV] in a fixed order: 16 groups of 64 threads take
 // interleaved partials, then group 0 adds the 16 group sums in order.
+template <int DV>
 __global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int n, float *out) {
-    __shared__ float gsum[16][kBwdDv];
-    const int c = threadIdx.x % kBwdDv, grp = threadIdx.x / kBwdDv;
-    float acc = 0.f;
-    for (int u = grp; u < n; u += 16) acc += part[static_cast<int64_t>(u) * kBwdDv + c];
-    gsum[grp][c] = acc;
+    constexpr int CPL = DV / kWave;
+    __shared__ float gsum[16][DV];
+    const int c = threadIdx.x % kWave, grp = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        float acc = 0.f;
+        for (int u = grp; u < n; u += 16) acc += part[static_cast<int64_t>(u) * DV + c + kWave * i];
+        gsum[grp][c + kWave * i] = acc;
+    }
     __syncthreads();
     if (grp == 0) {
-        float tot = 0.f;
-        for (int j = 0; j < 16; ++j) tot += gsum[j][c];
-        out[c] = tot;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            float tot = 0.f;
+            for (int j = 0; j < 16; ++j) tot += gsum[j][c + kWave * i];
+            out[c + kWave * i] = tot;
+        }
     }
+}
+
+// ---------------------------------------------------------------- per-token walk
+//
+// Any d_v and any number of slots (rows in HBM): one workgroup per (batch,
+// head) unit walks the tokens in order (the replay) or in reverse (the
+// adjoint).  A token's events run in parallel, one group of kRowLanes lanes
+// per event row, each lane holding DV / kRowLanes adjacent channels.  The
+// replayed state and mass live in the workspace (copied from S0 and mass0
+// first); the adjoint accumulates in dS0 and dmass0 themselves, which start
+// as dS_final and dmass_final.  Within a token:
+//   * a write whose slot an earlier write of the token already took waits
+//     for it (its generation is the number of such earlier writes; the
+//     decoder's slots are distinct, so there is normally one generation);
+//   * a read sees the token's last write to its slot, if any, else the state
+//     before the token.  In the adjoint a read is therefore folded into that
+//     write (its rho dr joins dS+ before the write is undone), and reads of
+//     one slot are summed in read order, so no two lanes update one row.
+constexpr int kSerThreads = 256;
+constexpr int kRowLanes = 16;
+constexpr int kSerGroups = kSerThreads / kRowLanes;
+constexpr int kSerKMax = 64;
+
+struct SerTok {
+    int w[kSerKMax], r[kSerKMax];
+    float wt[kSerKMax], rt[kSerKMax];
+    int gen[kSerKMax];     // writes: earlier writes of the token to the slot
+    int wlast[kSerKMax];   // reads: the token's last write to the slot, or -1
+    int rfirst[kSerKMax];  // reads: whether this is the first read of its slot
+    float rsw[kSerKMax];   // writes (the last to a slot): rho summed over its slot's reads
+    float rsr[kSerKMax];   // reads (the first of a slot): rho summed over the slot's reads
+    int maxgen;
+    float gam;
+};
+
+template <typename TS, int CPL>
+__device__ __forceinline__ void load_cpl(const TS *p, float (&x)[CPL]) {
+    if constexpr (sizeof(TS) == 4) {
+#pragma unroll
+        for (int j = 0; j < CPL / 4; ++j) {
+            const float4 f = reinterpret_cast<const float4 *>(p)[j];
+            x[4 * j] = f.x;
+            x[4 * j + 1] = f.y;
+            x[4 * j + 2] = f.z;
+            x[4 * j + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < CPL / 4; ++j) {
+            const uint2 u = reinterpret_cast<const uint2 *>(p)[j];
+            x[4 * j] = __uint_as_float(u.x << 16);
+            x[4 * j + 1] = __uint_as_float(u.x & 0xffff0000u);
+            x[4 * j + 2] = __uint_as_float(u.y << 16);
+            x[4 * j + 3] = __uint_as_float(u.y & 0xffff0000u);
+        }
+    }
+}
+// x holds values already representable in TS.
+template <typename TS, int CPL>
+__device__ __forceinline__ void store_cpl(TS *p, const float (&x)[CPL]) {
+    if constexpr (sizeof(TS) == 4) {
+#pragma unroll
+        for (int j = 0; j < CPL / 4; ++j)
+            reinterpret_cast<float4 *>(p)[j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < CPL / 4; ++j)
+            reinterpret_cast<uint2 *>(p)[j] =
+                make_uint2((__float_as_uint(x[4 * j]) >> 16) | (__float_as_uint(x[4 * j + 1]) & 0xffff0000u),
+                           (__float_as_uint(x[4 * j + 2]) >> 16) | (__float_as_uint(x[4 * j + 3]) & 0xffff0000u));
+    }
+}
+
+// Stages token t's events, v (or, with ADJ, v and dr) and gamma, and works
+// out the generations and the read-write relations above.  Ends with a
+// barrier.
+template <typename TIn, bool ADJ, int DV>
+__device__ __forceinline__ void ser_stage(const BwdArgs &a, SerTok &tk, float *sv, float *sdr, int b, int h,
+                                          int t) {
+    const int K = a.K, tid = threadIdx.x;
+    const int64_t th = (static_cast<int64_t>(b) * a.T + t) * a.H + h;
+    if (tid < K) {
+        tk.w[tid] = a.w_idx[th * K + tid];
+        tk.wt[tid] = a.w_wt[th * K + tid];
+    } else if (tid < 2 * K) {
+        tk.r[tid - K] = a.r_idx[th * K + tid - K];
+        tk.rt[tid - K] = a.r_wt[th * K + tid - K];
+    }
+    for (int c = tid; c < DV; c += kSerThreads) {
+        sv[c] = to_f32(static_cast<const TIn *>(a.v)[th * DV + c]);
+        if (ADJ) sdr[c] = a.dr[th * DV + c];
+    }
+    if (tid == 0) {
+        tk.gam = to_f32(static_cast<const TIn *>(a.gamma)[th]);
+        tk.maxgen = 0;
+    }
+    __syncthreads();
+    const int64_t M = a.M;
+    auto valid = [&](int s) { return s >= 0 && static_cast<int64_t>(s) < M; };
+    if (tid < K) {
+        const int s = tk.w[tid];
+        int gen = 0;
+        bool last = true;
+        float rs = 0.f;
+        if (valid(s)) {
+            for (int j = 0; j < K; ++j) {
+                if (tk.w[j] == s) {
+                    gen += j < tid ? 1 : 0;
+                    last = last && j <= tid;
+                }
+            }
+            if (last)
+                for (int j = 0; j < K; ++j)
+                    if (tk.r[j] == s) rs += tk.rt[j];
+        }
+        tk.gen[tid] = gen;
+        tk.rsw[tid] = last ? rs : 0.f;
+        if (gen) atomicMax(&tk.maxgen, gen);
+    } else if (tid < 2 * K) {
+        const int k = tid - K, s = tk.r[k];
+        int wl = -1, first = 1;
+        float rs = 0.f;
+        if (valid(s)) {
+            for (int j = 0; j < K; ++j) {
+                if (tk.w[j] == s) wl = j;
+                if (tk.r[j] == s) {
+                    first = first && j >= k;
+                    rs += tk.rt[j];
+                }
+            }
+        }
+        tk.wlast[k] = wl;
+        tk.rfirst[k] = first;
+        tk.rsr[k] = rs;
+    }
+    __syncthreads();
+}
+
+// The replay: records each write's row and mass before it and each read's
+// row after the token's writes, applying the writes to the workspace state.
+// Dynamic LDS: the rows the token's writes leave, [K][DV] fp32.
+template <typename TIn, typename TS, int DV>
+__global__ __launch_bounds__(kSerThreads) void bwd_record_serial_kernel(BwdArgs a) {
+    constexpr int CPL = DV / kRowLanes;
+    extern __shared__ __align__(16) float snew[];
+    __shared__ SerTok tk;
+    __shared__ float sv[DV];
+    const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
+    const int K = a.K, T = a.T;
+    const int64_t M = a.M;
+    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
+    const int glead = (threadIdx.x % kWave) - gl;  // the group's first lane in its wave
+    TS *Su = static_cast<TS *>(a.Sw) + static_cast<int64_t>(unit) * M * DV;
+    float *mu = a.mw + static_cast<int64_t>(unit) * M;
+    for (int t = 0; t < T; ++t) {
+        ser_stage<TIn, false, DV>(a, tk, sv, nullptr, b, h, t);
+        const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
+        for (int g = 0; g <= tk.maxgen; ++g) {
+            const int ne = g == 0 ? 2 * K : K;
+            for (int e = grp; e < ne; e += kSerGroups) {
+                float x[CPL];
+                if (e < K) {
+                    if (tk.gen[e] != g) continue;
+                    const int s = tk.w[e];
+                    float *rw = a.rec_w + (rec0 + e) * DV + c0;
+                    if (s < 0 || static_cast<int64_t>(s) >= M) {
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) x[c] = 0.f;
+                        store_cpl<float, CPL>(rw, x);
+                        if (gl == 0) a.rec_m[rec0 + e] = 0.f;
+                        continue;
+                    }
+                    TS *row = Su + static_cast<int64_t>(s) * DV + c0;
+                    const float m0 = gl == 0 ? mu[s] : 0.f;
+                    load_cpl<TS, CPL>(row, x);
+                    const float m = __shfl(m0, glead, kWave);
+                    store_cpl<float, CPL>(rw, x);
+                    const float w = tk.wt[e];
+                    if (w > 0.f) {
+                        const float alpha = retention(w, expf(tk.gam));
+                        const float mn = fmaf(alpha, m, w);
+                        const float lam = w / (mn + a.eps_gsu);
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) x[c] = stored<TS>(fmaf(lam, sv[c0 + c] - x[c], x[c]));
+                        store_cpl<TS, CPL>(row, x);
+                        if (gl == 0) mu[s] = mn;
+                    }
+                    if (gl == 0) a.rec_m[rec0 + e] = m;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) snew[e * DV + c0 + c] = x[c];
+                } else {
+                    const int k = e - K, s = tk.r[k];
+                    if (tk.wlast[k] >= 0) continue;  // after the barrier, from LDS
+                    float *rr = a.rec_r + (rec0 + k) * DV + c0;
+                    if (s < 0 || static_cast<int64_t>(s) >= M) {
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) x[c] = 0.f;
+                    } else {
+                        load_cpl<TS, CPL>(Su + static_cast<int64_t>(s) * DV + c0, x);
+                    }
+                    store_cpl<float, CPL>(rr, x);
+                }
+            }
+            __syncthreads();
+        }
+        for (int k = grp; k < K; k += kSerGroups) {
+            const int wl = tk.wlast[k];
+            if (wl < 0) continue;
+            float x[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) x[c] = snew[wl * DV + c0 + c];
+            store_cpl<float, CPL>(a.rec_r + (rec0 + k) * DV + c0, x);
+        }
+        __syncthreads();
+    }
+}
+
+// The adjoint, tokens in reverse: a token's reads before its writes (the
+// forward took the writes first), writes in reverse generation order.
+template <typename TIn, int DV>
+__global__ __launch_bounds__(kSerThreads) void bwd_adjoint_serial_kernel(BwdArgs a) {
+    constexpr int CPL = DV / kRowLanes;
+    __shared__ SerTok tk;
+    __shared__ float sv[DV], sdr[DV];
+    const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
+    const int K = a.K, T = a.T;
+    const int64_t M = a.M;
+    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
+    const int glead = (threadIdx.x % kWave) - gl;
+    float *dSu = a.dS0 + static_cast<int64_t>(unit) * M * DV;
+    float *dmu = a.dmass0 + static_cast<int64_t>(unit) * M;
+    for (int t = T - 1; t >= 0; --t) {
+        ser_stage<TIn, true, DV>(a, tk, sv, sdr, b, h, t);
+        const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
+        const int64_t th = (static_cast<int64_t>(b) * T + t) * a.H + h;
+        for (int g = tk.maxgen; g >= 0; --g) {
+            const int ne = g == tk.maxgen ? 2 * K : K;
+            for (int e = grp; e < ne; e += kSerGroups) {
+                float d[CPL];
+                if (e >= K) {
+                    // a read with no write of the token on its slot, the
+                    // first of its slot: dS += (sum of the slot's rho) dr
+                    const int k = e - K, s = tk.r[k];
+                    if (tk.wlast[k] >= 0 || !tk.rfirst[k] || s < 0 || static_cast<int64_t>(s) >= M) continue;
+                    float *row = dSu + static_cast<int64_t>(s) * DV + c0;
+                    load_cpl<float, CPL>(row, d);
+                    const float rs = tk.rsr[k];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) d[c] = fmaf(rs, sdr[c0 + c], d[c]);
+                    store_cpl<float, CPL>(row, d);
+                    continue;
+                }
+                if (tk.gen[e] != g) continue;
+                const int s = tk.w[e];
+                float *dvk = a.dvk + (rec0 + e) * DV + c0;
+                const float w = tk.wt[e];
+                float dw = 0.f, dgk = 0.f;
+                if (s < 0 || static_cast<int64_t>(s) >= M) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) d[c] = 0.f;
+                    store_cpl<float, CPL>(dvk, d);
+                } else {
+                    float *row = dSu + static_cast<int64_t>(s) * DV + c0;
+                    load_cpl<float, CPL>(row, d);
+                    const float rs = tk.rsw[e];
+                    if (rs != 0.f)
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) d[c] = fmaf(rs, sdr[c0 + c], d[c]);
+                    if (w > 0.f) {
+                        float sm[CPL];
+                        load_cpl<float, CPL>(a.rec_w + (rec0 + e) * DV + c0, sm);
+                        const float mm0 = gl == 0 ? a.rec_m[rec0 + e] : 0.f;
+                        const float dm0 = gl == 0 ? dmu[s] : 0.f;
+                        const float mm = __shfl(mm0, glead, kWave);
+                        const float dmp = __shfl(dm0, glead, kWave);
+                        const float eg = expf(tk.gam);
+                        const float alpha = retention(w, eg);
+                        const float mp = fmaf(alpha, mm, w);
+                        const float den = mp + a.eps_gsu;
+                        const float lam = w / den;
+                        float dl = 0.f;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) dl = fmaf(d[c], sv[c0 + c] - sm[c], dl);
+                        // <dS+, v - S-> over the group's lanes (a butterfly:
+                        // every lane of the group gets the same sum)
+#pragma unroll
+                        for (int o = 1; o < kRowLanes; o <<= 1) dl += __shfl_xor(dl, o, kWave);
+                        float dv[CPL];
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            dv[c] = lam * d[c];
+                            d[c] *= 1.0f - lam;
+                        }
+                        store_cpl<float, CPL>(dvk, dv);
+                        const float dmt = dmp - dl * w / (den * den);
+                        const float dalpha = dmt * mm;
+                        dw = dl / den + dmt;
+                        if (w < 1.0f && alpha > 0.f) {
+                            dw -= dalpha * eg * alpha / (1.0f - w);
+                            dgk = dalpha * alpha * log1pf(-w) * eg;
+                        }
+                        if (gl == 0) dmu[s] = dmt * alpha;
+                    } else {
+                        float z[CPL];
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) z[c] = 0.f;
+                        store_cpl<float, CPL>(dvk, z);
+                    }
+                    store_cpl<float, CPL>(row, d);
+                }
+                if (gl == 0) {
+                    a.dgk[rec0 + e] = dgk;
+                    a.dw[th * K + e] = dw;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// dst[i] = src ? src[i] : 0 over n floats (the walk's starting buffers).
+__global__ __launch_bounds__(256) void bwd_copy_kernel(float *dst, const float *src, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] = src ? src[i] : 0.f;
+}
+__global__ __launch_bounds__(256) void bwd_copy16_kernel(uint16_t *dst, const uint16_t *src, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] = src[i];
+}
+
+// The walk for any d_v and any M: the starting buffers, the replay, the
+// output/read kernel, the adjoint.
+template <typename TIn, int DV>
+hipError_t launch_walk(const BwdArgs &a, hipStream_t st) {
+    const int units = a.B * a.H;
+    const int64_t ns = static_cast<int64_t>(units) * a.M;
+    // the replay's LDS holds the token's written rows: up to 64 KiB
+    const size_t lds = static_cast<size_t>(a.K) * DV * 4;
+    const void *rk = a.state_bf16 ? reinterpret_cast<const void *>(bwd_record_serial_kernel<TIn, bf16_t, DV>)
+                                  : reinterpret_cast<const void *>(bwd_record_serial_kernel<TIn, float, DV>);
+    hipError_t e = hipFuncSetAttribute(rk, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    auto grid_of = [](int64_t n) { return dim3(static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096))); };
+    if (a.state_bf16)
+        hipLaunchKernelGGL(bwd_copy16_kernel, grid_of(ns * DV), dim3(256), 0, st,
+                           static_cast<uint16_t *>(a.Sw), static_cast<const uint16_t *>(a.S0), ns * DV);
+    else
+        hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns * DV), dim3(256), 0, st, static_cast<float *>(a.Sw),
+                           static_cast<const float *>(a.S0), ns * DV);
+    hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns), dim3(256), 0, st, a.mw, a.mass0, ns);
+    hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns * DV), dim3(256), 0, st, a.dS0, a.dS_final, ns * DV);
+    hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns), dim3(256), 0, st, a.dmass0, a.dmass_final, ns);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.state_bf16)
+        hipLaunchKernelGGL((bwd_record_serial_kernel<TIn, bf16_t, DV>), dim3(units), dim3(kSerThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((bwd_record_serial_kernel<TIn, float, DV>), dim3(units), dim3(kSerThreads), lds, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_out_kernel<TIn, DV>), dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_adjoint_serial_kernel<TIn, DV>), dim3(units), dim3(kSerThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DV>
+hipError_t launch_tail(const BwdArgs &a, hipStream_t st) {
+    const int units = a.B * a.H;
+    const int64_t n = static_cast<int64_t>(units) * a.T;
+    hipLaunchKernelGGL((bwd_sum_kernel<DV>), dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.dq || a.dk) {
+        e = a.in_bf16 ? launch_logits<bf16_t>(a, dim3(static_cast<unsigned>((n + kWave - 1) / kWave), 2), st)
+                      : launch_logits<float>(a, dim3(static_cast<unsigned>((n + kWave - 1) / kWave), 2), st);
+        if (e != hipSuccess) return e;
+    }
+    if (a.dnorm_w) {
+        hipLaunchKernelGGL((bwd_omega_kernel<DV>), dim3(1), dim3(1024), 0, st, a.dom_part, units * kOutBlocks,
+                           a.dnorm_w);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <typename TIn>
 hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
+    if (!backward_slot_owner(a.M, a.d_v)) {
+        hipError_t e;
+        switch (a.d_v) {
+            case 64: e = launch_walk<TIn, 64>(a, st); break;
+            case 128: e = launch_walk<TIn, 128>(a, st); break;
+            case 192: e = launch_walk<TIn, 192>(a, st); break;
+            case 256: e = launch_walk<TIn, 256>(a, st); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+        switch (a.d_v) {
+            case 64: return launch_tail<64>(a, st);
+            case 128: return launch_tail<128>(a, st);
+            case 192: return launch_tail<192>(a, st);
+            default: return launch_tail<256>(a, st);
+        }
+    }
     const int units = a.B * a.H;
     const dim3 grid(units, static_cast<unsigned>((a.M + kSlotsPerWG - 1) / kSlotsPerWG));
     // Whether the grid has at most one workgroup per CU: then the adjoint
@@ -709,7 +1169,7 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_out_kernel<TIn>, dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
+    hipLaunchKernelGGL((bwd_out_kernel<TIn, kBwdDv>), dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0,
                        st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -719,38 +1179,26 @@ hipError_t launch_in(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_adjoint_kernel<TIn, 2, 2048>), grid, dim3(kThreadsOf<2>), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    {
-        const int64_t n = static_cast<int64_t>(units) * a.T;
-        hipLaunchKernelGGL(bwd_sum_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
-                           st, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (a.dq || a.dk) {
-        const int64_t n = static_cast<int64_t>(units) * a.T;
-        e = launch_logits<TIn>(a, dim3(static_cast<unsigned>((n + kWave - 1) / kWave), 2), st);
-        if (e != hipSuccess) return e;
-    }
-    if (a.dnorm_w) {
-        hipLaunchKernelGGL(bwd_omega_kernel, dim3(1), dim3(1024), 0, st, a.dom_part,
-                           units * kOutBlocks, a.dnorm_w);
-        e = hipGetLastError();
-    }
-    return e;
+    return launch_tail<kBwdDv>(a, st);
 }
 
 }  // namespace
 
-bool backward_supported(int64_t M, int d_v, int U, int d_p, bool) {
-    return d_v == kBwdDv && M <= kBwdNT && U * d_p <= 64;
+bool backward_slot_owner(int64_t M, int d_v) { return d_v == kBwdDv && M <= kBwdNT; }
+
+bool backward_supported(int64_t, int d_v, int U, int d_p, bool) {
+    return d_v % kWave == 0 && d_v <= 256 && U * d_p <= 64;
 }
 
-size_t backward_workspace_bytes(int B, int T, int H, int K) {
+size_t backward_workspace_bytes(int B, int T, int H, int K, int64_t M, int d_v, bool state_bf16) {
     const size_t units = static_cast<size_t>(B) * H;
     const size_t n = units * T;
+    const size_t dv = static_cast<size_t>(d_v);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    return 3 * al(n * K * kBwdDv * 4) + 4 * al(n * K * 4) + al(units * kOutBlocks * kBwdDv * 4) +
-           al(n * kBwdDv * 4);
+    size_t bytes = 3 * al(n * K * dv * 4) + 4 * al(n * K * 4) + al(units * kOutBlocks * dv * 4) + al(n * dv * 4);
+    if (!backward_slot_owner(M, d_v))
+        bytes += al(units * static_cast<size_t>(M) * dv * (state_bf16 ? 2 : 4)) + al(units * static_cast<size_t>(M) * 4);
+    return bytes;
 }
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t st) {

@@ -153,12 +153,14 @@ struct StepArgs {
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
 
-// Backward pass of the recurrence (backward.hip): d_v = 64, M <= 1024,
-// given the forward's addresses; gradients in fp32.
+// Backward pass of the recurrence (backward.hip), given the forward's
+// addresses; gradients in fp32.  d_v = 64 with M <= 1024 takes the
+// slot-owner kernels (state on chip); every other shape the per-token walk
+// with the state in HBM.
 struct BwdArgs {
     int B, T, H;
     int64_t M;
-    int K, U, d_p, cape;
+    int K, U, d_p, cape, d_v;
     uint64_t content_heads;
     bool in_bf16, state_bf16;
     float eps_gsu, eps_norm;
@@ -173,9 +175,15 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dgamma, *dg, *dnorm_w, *dS0, *dmass0;
     // workspace: per token-head records and weight gradients, per unit d omega
     float *rec_w, *rec_r, *rec_m, *dw, *drho, *dom_part, *dr, *dvk, *dgk;
+    // per-token walk only: the replayed state [units][M][d_v] (state dtype)
+    // and mass [units][M]
+    void *Sw;
+    float *mw;
 };
 bool backward_supported(int64_t M, int d_v, int U, int d_p, bool state_bf16);
-size_t backward_workspace_bytes(int B, int T, int H, int K);
+// Whether the slot-owner kernels serve this shape (else the per-token walk).
+bool backward_slot_owner(int64_t M, int d_v);
+size_t backward_workspace_bytes(int B, int T, int H, int K, int64_t M, int d_v, bool state_bf16);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t st);
 
 // Dense projections around the layer (proj.hip).

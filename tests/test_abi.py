@@ -279,11 +279,17 @@ def test_backward_scope_and_arguments(rn):
     p = good(rn, d_v=64, state_dtype=rn.F32)
     assert rn.workspace_bytes(p, rn.OP_BACKWARD) > 0
     assert rn.workspace_bytes(good(rn, state_dtype=rn.BF16), rn.OP_BACKWARD) > 0
-    st, err = call_backward(rn, good(rn, d_v=128))
-    assert st == -2 and "d_v = 64" in err
-    assert rn.workspace_bytes(good(rn, d_v=128), rn.OP_BACKWARD) == 0
-    st, err = call_backward(rn, good(rn, d_p=4, U=6))   # M = 4096
-    assert st == -2
+    # any d_v and M: d_v 64 with M <= 1024 keeps the state on chip, other
+    # shapes walk the tokens with a copy of the state in the workspace
+    dv128 = rn.workspace_bytes(good(rn, d_v=128, state_dtype=rn.BF16), rn.OP_BACKWARD)
+    p4k = good(rn, d_p=4, U=6, state_dtype=rn.BF16)   # M = 4096
+    walk = rn.workspace_bytes(p4k, rn.OP_BACKWARD)
+    assert dv128 > 0 and walk > 0
+    units = p4k.B * p4k.H
+    base = rn.workspace_bytes(good(rn, state_dtype=rn.BF16), rn.OP_BACKWARD)
+    assert walk >= base + units * 4096 * (p4k.d_v * 2 + 4)   # state and mass copies
+    st, err = call_backward(rn, good(rn, d_p=6, U=11))   # U * d_p = 66 logits
+    assert st == -2 and "U*d_p <= 64" in err
     st, err = call_backward(rn, p, dout=None)
     assert st == -1 and "dout is NULL" in err
     st, err = call_backward(rn, p, ws_bytes=16)

@@ -70,6 +70,13 @@ CASES = {
     # compared to 1e-3 (worst seen 2.5e-4); dk, from the writes, keeps the
     # standard tolerance.
     "k1": ("tiny", dict(B=1, T=90, H=2), dict(d_p=4, U=3, K=1, dq_tol=1e-3)),
+    # shapes of the per-token walk (state in HBM): d_v 128 with a bf16 state
+    # (the decoding workload's layer), d_v 192 and 256, 4096 slots, and the
+    # 4^8-slot workload itself (K = 32, bf16 state)
+    "walk_dv128_bf16_state": ("decode", dict(B=1, T=48, H=2), dict(wl=dict(steps=0))),
+    "walk_dv192": ("prefill_top8", dict(B=1, T=40, H=2), dict(wl=dict(d_v=192))),
+    "walk_dv256_m4096": ("tiny", dict(B=1, T=40, H=2), dict(wl=dict(d_v=256, U=6, K=16))),
+    "walk_large_state": ("large_state", dict(B=1, T=40, H=2), dict(wl=dict(steps=0))),
 }
 
 
@@ -112,6 +119,8 @@ def test_backward_matches_oracle(rn, BWo, case):
                                       cape=opt.get("cape", 1))
     if "d_p" in opt:
         w = w.replace(d_p=opt["d_p"], U=opt["U"], K=opt["K"])
+    if "wl" in opt:
+        w = w.replace(**opt["wl"])
     B, T, H = cut["B"], cut["T"], cut["H"]
     x = synth.make_inputs(w, B=B, T=T, H=H)
     r = np.random.default_rng(99)
@@ -224,4 +233,99 @@ def test_full_size_directional_derivatives(rn):
         scale = float((grads[n].double().abs() * dirn.double().abs()).sum())
         print(f"{n}: difference quotient {fd:.6g}, gradient {an:.6g}, |error| / scale "
               f"{abs(fd - an) / scale:.2e}")
+        assert abs(fd - an) <= 1e-4 * scale, (n, fd, an, scale)
+
+
+@pytest.mark.parametrize("case", ["slot_owner_top8", "walk_dv128"])
+def test_backward_given_addresses_with_repeats(rn, BWo, case):
+    """Caller-given addresses in which a token writes one slot twice, reads
+    one slot twice and reads a slot it writes: the writes to one slot apply
+    in address order and a read sees the token's last write, as in the
+    forward.  Both sides take the same addresses, so every unit is compared.
+    Their weights are the Product Softmax weights of the slots' content
+    digits, as the oracle differentiates them."""
+    import oracle as orc
+    name = {"slot_owner_top8": "prefill_top8", "walk_dv128": "decode"}[case]
+    w = synth.WORKLOADS[name].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5), pos0_max=3000, steps=0)
+    B, T, H = 1, 40, 2
+    x = synth.make_inputs(w, B=B, T=T, H=H)
+    wi, _, _ = orc.decode_all(x["k"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"])
+    ri, _, _ = orc.decode_all(x["q"], w.U, w.d_p, w.K, cape=w.cape, pos0=x["pos0"])
+    wi, ri = wi.copy(), ri.copy()
+    wi[:, ::3, :, 1] = wi[:, ::3, :, 0]      # one slot written twice
+    ri[:, ::3, :, 2] = ri[:, ::3, :, 0]      # one slot read twice
+    ri[:, 1::3, :, 3] = wi[:, 1::3, :, 0]    # a read of a slot the token writes
+    fk = weights_of(orc, w, x["k"], x["pos0"], T, H, w.cape, 0, w.U, w.d_p)
+    fq = weights_of(orc, w, x["q"], x["pos0"], T, H, w.cape, 0, w.U, w.d_p)
+    ww = np.stack([fk(f, wi.reshape(-1, w.K)[f]) for f in range(B * T * H)]).reshape(wi.shape)
+    rw = np.stack([fq(f, ri.reshape(-1, w.K)[f]) for f in range(B * T * H)]).reshape(ri.shape)
+    r = np.random.default_rng(3)
+    dout = r.standard_normal((B, T, H, w.d_v)).astype(np.float32)
+    dSf = r.standard_normal(x["S0"].shape).astype(np.float32)
+    dmf = r.standard_normal(x["m0"].shape).astype(np.float32)
+    sbf = w.state_dtype == "bf16"
+    ref = BWo.layer_grads(x["q"], x["k"], x["v"], x["gamma"], x["g"], x["S0"], x["m0"], dout,
+                          d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=x["pos0"], dS_final=dSf,
+                          dm_final=dmf, round_storage=True, state_bf16=sbf, addresses=(wi, ri))
+    bf = w.in_dtype == "bf16"
+    d = {n: dev(x[n], bf) for n in ("q", "k", "v", "gamma", "g")}
+    ti = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    addr = rn.Addresses(ti(wi), dev(ww), ti(ri), dev(rw))
+    got = rn.scan_backward(d["q"], d["k"], d["v"], d["gamma"], d["g"], dev(x["S0"], sbf), dev(x["m0"]),
+                           addr, dev(dout), d_p=w.d_p, U=w.U, K=w.K, cape=w.cape,
+                           pos0=torch.from_numpy(x["pos0"]).cuda(), dS_final=dev(dSf), dmass_final=dev(dmf))
+    torch.cuda.synchronize()
+    tol = GRAD_TOL_BF16 if sbf else GRAD_TOL
+    worst = {n: close(n, to_np(got[n]), ref[n], None, tol) for n in ("dv", "dg", "dgamma", "dq", "dk")}
+    worst["dS0"] = close("dS0", to_np(got["dS0"]), ref["dS0"], None, tol)
+    worst["dm0"] = close("dm0", to_np(got["dmass0"]), ref["dm0"], None, tol)
+    print(case, {k: f"{v:.2e}" for k, v in worst.items()})
+
+
+def test_full_size_large_state_directional_derivatives(rn):
+    """The 4^8-slot workload at full size (B 2, T 32768, H 16, K 32), with an
+    fp32 state so that the loss is smooth at the step sizes used: the
+    gradients of v, gamma, g, S0 and m0 against central differences of the
+    GPU forward's loss along random directions (those inputs do not move the
+    addresses).  Same tolerance as the Top-8 case."""
+    w = synth.WORKLOADS["large_state"].replace(s0_sigma=0.3, m0_uniform=(0.2, 1.5), state_dtype="f32")
+    B, T, H = w.B, w.T, w.H
+    x = synth.make_inputs(w)
+    base = {n: dev(x[n]) for n in ("v", "gamma", "g")}
+    S0, m0 = dev(x["S0"]), dev(x["m0"])
+    pos0 = torch.from_numpy(x["pos0"]).cuda()
+    q32, k32 = dev(x["q"]), dev(x["k"])
+    del x
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    dout = torch.randn(B, T, H, w.d_v, generator=gen, device="cuda")
+    plan = rn.PrefillPlan(B, T, H, w.d_p, w.U, w.K, w.d_v, rn.F32, rn.F32, cape=w.cape)
+    out = torch.empty(B, T, H, w.d_v, device="cuda")
+    addr = rn.new_addresses((B, T, H, w.K), "cuda")
+
+    def loss(v, gamma, g, S, m):
+        S, m = S.clone(), m.clone()
+        plan(q32, k32, v, gamma, g, S, m, out, pos0=pos0)
+        return float((out.double() * dout.double()).sum())
+
+    S, m = S0.clone(), m0.clone()
+    plan(q32, k32, base["v"], base["gamma"], base["g"], S, m, out, pos0=pos0, addr_out=addr)
+    del S, m
+    gr = rn.scan_backward(q32, k32, base["v"], base["gamma"], base["g"], S0, m0, addr, dout,
+                          d_p=w.d_p, U=w.U, K=w.K, cape=w.cape, pos0=pos0, want_logits=False)
+    torch.cuda.synchronize()
+    args = {"v": base["v"], "gamma": base["gamma"], "g": base["g"], "S": S0, "m": m0}
+    grads = {"v": gr["dv"], "gamma": gr["dgamma"], "g": gr["dg"], "S": gr["dS0"], "m": gr["dmass0"]}
+    for n, eps in (("v", 1e-3), ("gamma", 1e-3), ("g", 1e-3), ("S", 1e-3), ("m", 1e-3)):
+        dirn = torch.randn(args[n].shape, generator=gen, device="cuda")
+        if n == "m":
+            dirn = dirn.abs()  # the mass stays positive
+        ap, am = dict(args), dict(args)
+        ap[n] = args[n] + eps * dirn
+        am[n] = args[n] - eps * dirn
+        fd = (loss(**ap) - loss(**am)) / (2 * eps)
+        an = float((grads[n].double() * dirn.double()).sum())
+        scale = float((grads[n].double().abs() * dirn.double().abs()).sum())
+        print(f"{n}: difference quotient {fd:.6g}, gradient {an:.6g}, |error| / scale "
+              f"{abs(fd - an) / scale:.2e}", flush=True)
         assert abs(fd - an) <= 1e-4 * scale, (n, fd, an, scale)
