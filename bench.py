@@ -19,10 +19,13 @@ measured one.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload prefill_top8|prefill_top32|large_state|decode
                                    |layer_top8|layer_decode|backward_top8
-                                   |backward_top32|backward_large_state]
+                                   |backward_top32|backward_large_state
+                                   |decode_tiered]
 --workload runs that workload alone (no sub-records).  The layer_* workloads
 add the dense projections either side (the whole layer); backward_top8 /
-backward_top32 / backward_large_state time the gradients of those prefills.
+backward_top32 / backward_large_state time the gradients of those prefills;
+decode_tiered runs the decoding workload with its rows in pinned host memory
+and a quarter of them cached in HBM.
 """
 from __future__ import annotations
 
@@ -396,6 +399,122 @@ def bench_decode(torch, rn, w, steps, warmup):
 # for the 340M-like layer; 2048 = H*d_v for the 16-head decode layer).
 LAYERS = {"layer_top8": ("prefill_top8", 1024), "layer_decode": ("decode", 2048)}
 
+# The decoding workload on a tiered state (rows in pinned host memory, M / 4
+# rows of each unit cached in HBM, a rebalance every 64 steps).
+TIERED = {"decode_tiered": ("decode", 4, 64)}
+
+
+def host_link_peaks(torch, rn):
+    """Kernel copies between pinned host memory and HBM (64 MiB, 16-byte
+    loads and stores, the probe's grid-stride copy): bytes per second over
+    the host link each way, best of 5 after 2 warm-ups."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "sparse_slot_recurrent_amd", "libramnet_probe.so"))
+    lib.probe_hbm_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int, C.c_void_p]
+    rl = rn.load_library()
+    nbytes = 64 << 20
+    hp = C.c_void_p()
+    if rl.ramnet_host_alloc(nbytes, C.byref(hp)) != 0:
+        raise RuntimeError(rl.ramnet_last_error().decode())
+    dev = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    sp = C.c_void_p(st.cuda_stream)
+
+    def best(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return min(ts)
+    try:
+        dp = C.c_void_p(dev.data_ptr())
+        t_rd = best(lambda: lib.probe_hbm_copy(hp, dp, nbytes // 16, 2048, sp))
+        t_wr = best(lambda: lib.probe_hbm_copy(dp, hp, nbytes // 16, 2048, sp))
+    finally:
+        torch.cuda.synchronize()
+        rl.ramnet_host_free(hp)
+    return {"host_read_gbs": nbytes / t_rd / 1e9, "host_write_gbs": nbytes / t_wr / 1e9,
+            "method": "64 MiB kernel copy pinned host -> HBM and HBM -> pinned host, best of 5"}
+
+
+def bench_decode_tiered(torch, rn, w, frac_den, every, steps, warmup):
+    """The decoding workload's steps on a tiered state: the rows in pinned
+    host memory, M / frac_den rows of each unit cached in HBM, a rebalance
+    after every `every` steps (inside the timed region).  Returns (ms per
+    step, per-kernel ms, tokens per step, extra fields: cache hit fraction of
+    one step's accesses, host-link bytes per step, device bytes held)."""
+    from sparse_slot_recurrent_amd import synth
+    init = synth.make_inputs(w, T=1)
+    S = to_dev(torch, init["S0"], w.state_dtype)
+    mass = to_dev(torch, init["m0"], "f32")
+    pos0 = torch.from_numpy(init["pos0"]).cuda()
+    del init
+    lines = w.M // frac_den
+    ts = rn.TieredState(S, lines)
+    del S
+    ind = rn.BF16 if w.in_dtype == "bf16" else rn.F32
+    sd = rn.BF16 if w.state_dtype == "bf16" else rn.F32
+    p = rn.make_params(w.B, 1, w.H, w.d_p, w.U, w.K, w.d_v, ind, sd, cape=w.cape,
+                       eps_gsu=w.eps_gsu, eps_norm=w.eps_norm)
+    rn.tier_reset(p, ts)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    bdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+    n_in = min(steps, 256)  # distinct inputs, cycled
+
+    def normal(*shape, sigma=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * sigma).to(bdt)
+    q = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
+    k = normal(n_in, w.B, w.H, w.L, sigma=w.logit_sigma)
+    v = normal(n_in, w.B, w.H, w.d_v)
+    gam = normal(n_in, w.B, w.H)
+    g = normal(n_in, w.B, w.H, w.d_v)
+    pos = (pos0[None, :] + torch.arange(n_in, device="cuda", dtype=torch.int32)[:, None]).contiguous()
+    sdt = torch.bfloat16 if w.state_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, w.H, w.d_v), dtype=sdt, device="cuda")
+
+    def one(i):
+        j = i % n_in
+        rn.step_decode_tiered(p, q[j], k[j], v[j], gam[j], g[j], pos[j], ts, mass, out)
+
+    def step(i):
+        one(i)
+        if (i + 1) % every == 0:
+            rn.tier_rebalance(p, ts)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps)
+    ms_step = time_loop(torch, one, min(steps, 64))
+    ms_reb = time_loop(torch, lambda i: rn.tier_rebalance(p, ts), 4)
+    # one step's accesses served from the cache (the maps do not change
+    # during a step)
+    ao = rn.new_addresses((w.B, w.H, w.K), "cuda")
+    rn.step_decode_tiered(p, q[0], k[0], v[0], gam[0], g[0], pos[0], ts, mass, out, addr_out=ao)
+    torch.cuda.synchronize()
+    sl = ts.slot_line.view(w.B * w.H, w.M)
+    u = torch.arange(w.B * w.H, device="cuda")[:, None]
+    hw = (sl[u, ao.w_idx.view(w.B * w.H, w.K).long()] >= 0).float().mean().item()
+    hr = (sl[u, ao.r_idx.view(w.B * w.H, w.K).long()] >= 0).float().mean().item()
+    b_s = 2 if w.state_dtype == "bf16" else 4
+    rb = w.d_v * b_s
+    units = w.B * w.H
+    link = units * w.K * rb * (2 * (1 - hw) + (1 - hr))  # missed rows: writes read + written, reads read
+    dev_bytes = units * (lines * rb + lines * 4 + w.M * 12)  # cache, line map, slot map, counts, mass
+    extra = {"cache_lines_per_unit": lines, "rebalance_every": every,
+             "hit_fraction": {"write_rows": hw, "read_rows": hr},
+             "host_link_bytes_per_step": link, "device_bytes": dev_bytes,
+             "full_state_bytes": units * w.M * (rb + 4)}
+    return ms, {"step_tiered": ms_step, "rebalance": ms_reb}, w.B, extra
+
+
 
 def layer_model(w, D, kind: str):
     """Algorithmic flops and bytes of the two projection stages (bf16
@@ -661,8 +780,11 @@ def main():
         # region (the library's opt-in tuning)
         os.environ["RAMNET_GEMM_TUNE"] = "1"
     backward = name in BACKWARD
+    tiered = name in TIERED
     if backward:
         w = synth.WORKLOADS[BACKWARD[name]]
+    elif tiered:
+        w = synth.WORKLOADS[TIERED[name][0]]
     elif name in LAYERS:
         base, d_model = LAYERS[name]
         w = synth.WORKLOADS[base]
@@ -673,9 +795,17 @@ def main():
     warmup = args.warmup if args.warmup is not None else (8 if kind == "decode" else 2)
     peaks = {} if single else measure_peaks(torch)
     line = {"metric": METRIC}
-    if backward or d_model is not None:
+    if backward or tiered or d_model is not None:
         extra = {}
-        if backward:
+        if tiered:
+            _, den, every = TIERED[name]
+            ms, kms, tokens, extra = bench_decode_tiered(torch, rn, w, den, every, steps, warmup)
+            hl = host_link_peaks(torch, rn)
+            a = extra["host_link_bytes_per_step"] / (kms["step_tiered"] / 1e3) / 1e9
+            peak = min(hl["host_read_gbs"], hl["host_write_gbs"])
+            roof = {"bound": "host_link", "kernel": "step_tiered", "achieved": a, "peak": peak,
+                    "unit": "GB/s", "frac": a / peak, "traffic": None, "host_link": hl}
+        elif backward:
             ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
             bw = backward_model(w)
             extra["backward_model"] = bw

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define RAMNET_VERSION 5
+#define RAMNET_VERSION 6
 /* Largest supported K (Top-K per address). */
 #define RAMNET_KMAX 64
 
@@ -208,6 +208,76 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q,
                                  void *S, float *mass, void *out,
                                  const ramnet_addr *addr_out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * A tiered slot state for decoding loops (AI Radio page, deployment remark:
+ * the sparse access lets only the frequently accessed slots be cached in
+ * VRAM, so the state need not fit the GPU's memory).  The rows live in
+ * host memory; each (batch, head) unit caches at most C of them in device
+ * memory.  The masses stay in device memory ([B,H,M] fp32, 1/16 to 1/128 of
+ * the rows' bytes).  All buffers are the caller's:
+ *   S_host     [B,H,M,d_v] state_dtype, pinned host memory that the device
+ *              addresses at its host address (ramnet_host_alloc): the row of
+ *              every slot that is
+ *              not cached; a cached slot's row here is stale until
+ *              ramnet_tier_flush
+ *   cache      [B,H,C,d_v] state_dtype, device: the cached rows (line i of
+ *              unit u holds the row of slot line_slot[u][i])
+ *   line_slot  [B,H,C] int32, device: slot of each line, -1 for an empty line
+ *   slot_line  [B,H,M] int32, device: line of each slot, -1 if not cached
+ *   hits       [B,H,M] uint32, device: accesses (a token's write and read
+ *              slots, after CAPE) since the last rebalance, halved by it
+ *   C          lines per unit, 1 <= C <= min(M, RAMNET_TIER_CMAX)
+ * The step gives bit-identical results to ramnet_step_decode on the same
+ * state; only where the rows live differs.  Calls on one tiered state must
+ * be ordered (one stream). */
+#define RAMNET_TIER_CMAX 16384
+typedef struct {
+    void *S_host;
+    void *cache;
+    int32_t *line_slot;
+    int32_t *slot_line;
+    uint32_t *hits;
+    int32_t C;
+} ramnet_tiered_state;
+
+/* Pinned host memory for S_host (hipHostMalloc, mapped and portable), whose
+ * device address is checked to equal its host address; freed with
+ * ramnet_host_free.  The only calls that allocate. */
+ramnet_status ramnet_host_alloc(size_t bytes, void **ptr);
+ramnet_status ramnet_host_free(void *ptr);
+
+/* Empties the cache (every line empty, every slot uncached) and zeroes the
+ * counts; S_host must then hold the whole state.  Rows are not moved. */
+ramnet_status ramnet_tier_reset(const ramnet_params *p, const ramnet_tiered_state *ts,
+                                void *stream);
+
+/* One decoding step as ramnet_step_decode, the rows read and written where
+ * they live (a cached slot in its line, any other in S_host, over the host
+ * link), and each accessed slot's count raised.  No workspace.  Only the
+ * fused step's shapes (K <= 32, d_p <= 8, d_v 64..256 as the step takes
+ * them) are supported; RAMNET_EUNSUPPORTED otherwise. */
+ramnet_status ramnet_step_decode_tiered(const ramnet_params *p, const void *q,
+                                        const void *k, const void *v,
+                                        const void *gamma, const void *g,
+                                        const float *norm_w, const int32_t *pos,
+                                        const ramnet_tiered_state *ts, float *mass,
+                                        void *out, const ramnet_addr *addr_out,
+                                        void *stream);
+
+/* Re-chooses each unit's cached slots: the C slots with the highest key
+ * 2 * hits + (1 if cached), the key capped at 255, ties to the smaller
+ * slot, slots with key 0 never cached.  Rows leaving the cache are written
+ * back to S_host; rows entering it are copied from S_host; slots that stay
+ * keep their line; entering slots take the free lines in line order, in
+ * slot order.  Then every count is halved. */
+ramnet_status ramnet_tier_rebalance(const ramnet_params *p, const ramnet_tiered_state *ts,
+                                    void *stream);
+
+/* Writes every cached row back to S_host (the cache keeps it), so that
+ * S_host alone holds the whole state. */
+ramnet_status ramnet_tier_flush(const ramnet_params *p, const ramnet_tiered_state *ts,
+                                void *stream);
 
 /* Backward pass of a prefill (training; the project page's GPU-execution
  * paragraph treats training and prefill alike).  The pages give no backward

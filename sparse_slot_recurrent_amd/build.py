@@ -24,7 +24,7 @@ PROBE_LIB = os.path.join(PKG, "libramnet_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "decode.hip", "scan_serial.hip", "scan_chunked.hip", "scan_ranges.hip",
-           "step_fused.hip", "proj.hip", "backward.hip"]
+           "step_fused.hip", "tier.hip", "proj.hip", "backward.hip"]
 # hipBLASLt carries the dense projections around the layer.
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -608,6 +609,60 @@ ramnet_status scratch_of_current_device(void **out) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- tiered state
+
+namespace {
+
+// Validates a tiered state for p and appends its buffers to sp (all of them
+// written: the step moves rows and counts, the upkeep calls the maps).
+ramnet_status check_tier(const ramnet_params *p, const ramnet_tiered_state *ts, Span *sp, int &ns) {
+    if (!ts) return fail(RAMNET_EINVAL, "ts is NULL");
+    const int64_t lim = std::min<int64_t>(p->M, RAMNET_TIER_CMAX);
+    if (ts->C < 1 || ts->C > lim)
+        return fail(RAMNET_EINVAL, "C = %d outside [1, %lld]", ts->C, static_cast<long long>(lim));
+    ramnet_status s;
+    if ((s = check_ptr("ts->S_host", ts->S_host, true)) || (s = check_ptr("ts->cache", ts->cache, true)) ||
+        (s = check_ptr("ts->line_slot", ts->line_slot, true)) ||
+        (s = check_ptr("ts->slot_line", ts->slot_line, true)) || (s = check_ptr("ts->hits", ts->hits, true)))
+        return s;
+    const size_t units = static_cast<size_t>(p->B) * p->H;
+    const size_t rb = static_cast<size_t>(p->d_v) * st_bytes(p);
+    sp[ns++] = span("ts->S_host", ts->S_host, units * p->M * rb);
+    sp[ns++] = span("ts->cache", ts->cache, units * ts->C * rb);
+    sp[ns++] = span("ts->line_slot", ts->line_slot, units * ts->C * 4);
+    sp[ns++] = span("ts->slot_line", ts->slot_line, units * p->M * 4);
+    sp[ns++] = span("ts->hits", ts->hits, units * p->M * 4);
+    return RAMNET_OK;
+}
+
+ramnet::TierArgs tier_args(const ramnet_params *p, const ramnet_tiered_state *ts) {
+    ramnet::TierArgs a{};
+    a.units = p->B * p->H;
+    a.C = ts->C;
+    a.d_v = p->d_v;
+    a.M = p->M;
+    a.state_bf16 = p->state_dtype == RAMNET_BF16;
+    a.S_host = ts->S_host;
+    a.cache = ts->cache;
+    a.line_slot = ts->line_slot;
+    a.slot_line = ts->slot_line;
+    a.hits = ts->hits;
+    return a;
+}
+
+ramnet_status tier_upkeep(const ramnet_params *p, const ramnet_tiered_state *ts, void *stream,
+                          hipError_t (*launch)(const ramnet::TierArgs &, hipStream_t), const char *what) {
+    ramnet_status s = check_params(p, true);
+    if (s) return s;
+    Span sp[8];
+    int ns = 0;
+    if ((s = check_tier(p, ts, sp, ns)) || (s = check_overlaps(sp, ns, 0))) return s;
+    if (static_cast<int64_t>(p->B) * p->H == 0) return ok();
+    return hip_status(launch(tier_args(p, ts), static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ramnet_layer_workspace_bytes(const ramnet_params *p, int32_t d_model) {
@@ -928,6 +983,114 @@ ramnet_status ramnet_step_decode(const ramnet_params *p, const void *q, const vo
                                  size_t workspace_bytes, void *stream) {
     return run_layer(p, true, q, k, v, gamma, g, norm_w, pos, S, mass, out, nullptr, addr_out,
                      workspace, workspace_bytes, stream);
+}
+
+ramnet_status ramnet_host_alloc(size_t bytes, void **ptr) {
+    if (!ptr) return fail(RAMNET_EINVAL, "ptr is NULL");
+    *ptr = nullptr;
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, bytes ? bytes : 1, hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) return hip_status(e, "hipHostMalloc");
+    void *d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess || d != h) {
+        (void)hipHostFree(h);
+        return e != hipSuccess ? hip_status(e, "hipHostGetDevicePointer")
+                               : fail(RAMNET_EUNSUPPORTED, "pinned memory has another device address");
+    }
+    *ptr = h;
+    return ok();
+}
+
+ramnet_status ramnet_host_free(void *ptr) {
+    if (!ptr) return ok();
+    return hip_status(hipHostFree(ptr), "hipHostFree");
+}
+
+ramnet_status ramnet_tier_reset(const ramnet_params *p, const ramnet_tiered_state *ts, void *stream) {
+    return tier_upkeep(p, ts, stream, ramnet::launch_tier_reset, "tier reset launch");
+}
+
+ramnet_status ramnet_tier_rebalance(const ramnet_params *p, const ramnet_tiered_state *ts, void *stream) {
+    return tier_upkeep(p, ts, stream, ramnet::launch_tier_rebalance, "tier rebalance launch");
+}
+
+ramnet_status ramnet_tier_flush(const ramnet_params *p, const ramnet_tiered_state *ts, void *stream) {
+    return tier_upkeep(p, ts, stream, ramnet::launch_tier_flush, "tier flush launch");
+}
+
+ramnet_status ramnet_step_decode_tiered(const ramnet_params *p, const void *q, const void *k,
+                                        const void *v, const void *gamma, const void *g,
+                                        const float *norm_w, const int32_t *pos,
+                                        const ramnet_tiered_state *ts, float *mass, void *out,
+                                        const ramnet_addr *addr_out, void *stream) {
+    ramnet_status s = check_params(p, true);
+    if (s) return s;
+    if (!ramnet::step_fused_supported(p->K, p->d_p, p->U, p->d_v, p->state_dtype == RAMNET_BF16))
+        return fail(RAMNET_EUNSUPPORTED, "the tiered step takes the fused step's shapes (K <= 32, d_p <= 8)");
+    const int64_t units = static_cast<int64_t>(p->B) * p->H;
+    if ((s = check_ptr("q", q, true)) || (s = check_ptr("k", k, true)) || (s = check_ptr("v", v, true)) ||
+        (s = check_ptr("gamma", gamma, true)) || (s = check_ptr("g", g, true)) ||
+        (s = check_ptr("norm_w", norm_w, false)) || (s = check_ptr("pos", pos, false)) ||
+        (s = check_ptr("mass", mass, true)) || (s = check_ptr("out", out, true)))
+        return s;
+    if (p->cape && !pos) return fail(RAMNET_EINVAL, "pos is required when cape != 0");
+    if (addr_out && (s = check_addr("addr_out", addr_out))) return s;
+    const size_t L = static_cast<size_t>(p->U) * p->d_p;
+    const size_t nK4 = static_cast<size_t>(units) * p->K * 4;
+    Span sp[24];
+    int ns = 0;
+    sp[ns++] = span("q", q, units * L * in_bytes(p));
+    sp[ns++] = span("k", k, units * L * in_bytes(p));
+    if (pos) sp[ns++] = span("pos", pos, p->B * sizeof(int32_t));
+    sp[ns++] = span("v", v, units * p->d_v * in_bytes(p));
+    sp[ns++] = span("gamma", gamma, units * in_bytes(p));
+    sp[ns++] = span("g", g, units * p->d_v * in_bytes(p));
+    if (norm_w) sp[ns++] = span("norm_w", norm_w, p->d_v * sizeof(float));
+    const int first_written = ns;
+    sp[ns++] = span("mass", mass, units * p->M * sizeof(float));
+    sp[ns++] = span("out", out, units * p->d_v * st_bytes(p));
+    if (addr_out) {
+        sp[ns++] = span("addr_out.w_idx", addr_out->w_idx, nK4);
+        sp[ns++] = span("addr_out.w_wt", addr_out->w_wt, nK4);
+        sp[ns++] = span("addr_out.r_idx", addr_out->r_idx, nK4);
+        sp[ns++] = span("addr_out.r_wt", addr_out->r_wt, nK4);
+    }
+    if ((s = check_tier(p, ts, sp, ns)) || (s = check_overlaps(sp, ns, first_written))) return s;
+    if (units == 0) return ok();
+    ramnet::StepArgs sa{};
+    sa.B = p->B;
+    sa.H = p->H;
+    sa.M = p->M;
+    sa.K = p->K;
+    sa.d_v = p->d_v;
+    sa.U = p->U;
+    sa.d_p = p->d_p;
+    sa.cape = p->cape;
+    sa.content_heads = p->content_heads;
+    sa.in_bf16 = p->in_dtype == RAMNET_BF16;
+    sa.state_bf16 = p->state_dtype == RAMNET_BF16;
+    sa.q = q;
+    sa.k = k;
+    sa.v = v;
+    sa.gamma = gamma;
+    sa.g = g;
+    sa.norm_w = norm_w;
+    sa.pos = pos;
+    sa.S = ts->S_host;
+    sa.mass = mass;
+    sa.out = out;
+    sa.out_idx[0] = addr_out ? addr_out->w_idx : nullptr;
+    sa.out_idx[1] = addr_out ? addr_out->r_idx : nullptr;
+    sa.out_wt[0] = addr_out ? addr_out->w_wt : nullptr;
+    sa.out_wt[1] = addr_out ? addr_out->r_wt : nullptr;
+    sa.eps_gsu = p->eps_gsu;
+    sa.eps_norm = p->eps_norm;
+    sa.cache = ts->cache;
+    sa.slot_line = ts->slot_line;
+    sa.hits = ts->hits;
+    sa.C = ts->C;
+    return hip_status(ramnet::launch_step_fused(sa, static_cast<hipStream_t>(stream)), "tiered step launch");
 }
 
 const char *ramnet_status_str(ramnet_status s) {

@@ -149,9 +149,29 @@ struct StepArgs {
     float eps_gsu, eps_norm;
     // elements between sequences b of q and k, v, g, gamma; 0: contiguous
     int64_t ld_qk, ld_v, ld_g, ld_gamma;
+    // tiered state (cache != NULL): S is the host copy, cached slots' rows
+    // live in cache [units][C][d_v] at line slot_line[unit][slot]; hits
+    // counts each accessed slot
+    void *cache;
+    const int32_t *slot_line;
+    uint32_t *hits;
+    int C;
 };
 bool step_fused_supported(int K, int d_p, int U, int d_v, bool state_bf16);
 hipError_t launch_step_fused(const StepArgs &a, hipStream_t st);
+
+// Tiered state maintenance (tier.hip).
+struct TierArgs {
+    int units, C, d_v;
+    int64_t M;
+    bool state_bf16;
+    void *S_host, *cache;
+    int32_t *line_slot, *slot_line;
+    uint32_t *hits;
+};
+hipError_t launch_tier_reset(const TierArgs &a, hipStream_t st);
+hipError_t launch_tier_rebalance(const TierArgs &a, hipStream_t st);
+hipError_t launch_tier_flush(const TierArgs &a, hipStream_t st);
 
 // Backward pass of the recurrence (backward.hip), given the forward's
 // addresses; gradients in fp32.  d_v = 64 with M <= 1024 takes the

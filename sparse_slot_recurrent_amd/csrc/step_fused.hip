@@ -32,6 +32,12 @@
 //    pass over memory.  Every load is consumed before the first store.  The
 //    sub-row partial reads are summed through LDS; RMSNorm over d_v by a
 //    wave reduction; the gate.
+//  * Tiered state (TIER): the rows live in host memory except each unit's
+//    cached ones (AI Radio page, deployment remark: only frequently accessed
+//    slots in VRAM).  The decoding phase also fetches each address's cache
+//    line and counts the access; the row phase takes each row where it
+//    lives.  Nothing else changes, so the results are those of the
+//    all-in-HBM step bit for bit.
 #include "device_common.h"
 #include "launch.h"
 
@@ -241,7 +247,7 @@ __device__ __forceinline__ Words<NW> pack(float *f) {
 
 // Byte offsets of the kernel's LDS arrays.
 struct StepLds {
-    int idx, wt, lg, pr, lam, cr, red, total;
+    int idx, wt, lg, pr, lam, cr, red, ln, total;
 };
 __host__ __device__ constexpr StepLds step_lds(int UPW, int K, int L, int RPI, int DV) {
     StepLds o{};
@@ -252,11 +258,14 @@ __host__ __device__ constexpr StepLds step_lds(int UPW, int K, int L, int RPI, i
     o.lam = o.pr + UPW * 2 * L * 8;              // float [UPW][K]
     o.cr = o.lam + UPW * K * 4;                  // float [UPW][K]
     o.red = o.cr + UPW * K * 4;                  // float [RPI][DV]
-    o.total = o.red + RPI * DV * 4;
+    o.ln = o.red + RPI * DV * 4;                 // int   [UPW][2][K]: cache lines (tiered state)
+    o.total = o.ln + UPW * 2 * K * 4;
     return o;
 }
 
-template <typename TIn, typename TS, int KP, int DV>
+// TIER: the rows of cached slots live in a.cache (line a.slot_line[slot]),
+// the others in a.S (host memory); each accessed slot's count is raised.
+template <typename TIn, typename TS, int KP, int DV, bool TIER>
 __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
     using G = RowGeom<TS, DV>;
     using P = RowPlan<TS, KP, DV>;
@@ -279,6 +288,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
     float *slam = reinterpret_cast<float *>(smem + lo.lam);
     float *scr = reinterpret_cast<float *>(smem + lo.cr);
     float *sred = reinterpret_cast<float *>(smem + lo.red);
+    int *sline = reinterpret_cast<int *>(smem + lo.ln);
 
     // the gates and norm weights of the wave's units do not depend on the
     // addresses: their loads go out first and land during the decoding
@@ -387,6 +397,11 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
             const float wt = static_cast<float>(exp(beam.w - lse_sum));
             sidx[(ul * 2 + which) * K + r] = slot;
             swt[(ul * 2 + which) * K + r] = wt;
+            if constexpr (TIER) {
+                const int64_t si = static_cast<int64_t>(unit) * M + slot;
+                sline[(ul * 2 + which) * K + r] = a.slot_line[si];
+                atomicAdd(&a.hits[si], 1u);
+            }
             if (a.out_idx[which]) {
                 a.out_idx[which][static_cast<int64_t>(unit) * K + r] = slot;
                 a.out_wt[which][static_cast<int64_t>(unit) * K + r] = wt;
@@ -400,6 +415,17 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
     TS *S = static_cast<TS *>(a.S);
     TS *out = static_cast<TS *>(a.out);
     const int npair = nu * K;  // <= 32
+    // where the row of address (ul, which, k) lives
+    auto row_of = [&](int ul, int which, int k) -> TS * {
+        const int i = (ul * 2 + which) * K + k;
+        const int64_t un = u0 + ul;
+        if constexpr (TIER) {
+            const int ln = sline[i];
+            if (static_cast<unsigned>(ln) < static_cast<unsigned>(a.C))
+                return static_cast<TS *>(a.cache) + (un * a.C + ln) * DV;
+        }
+        return S + (un * M + sidx[i]) * DV;
+    };
 
     // ---------------- mass of every write pair: lane l < npair holds pair
     // (unit l / K, rank l % K); the load is issued before the row loads
@@ -428,14 +454,12 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
         for (int i = 0; i < UB; ++i) {
             const int ul = b0 + i;
             if (ul < nu) {
-                const TS *Su = S + static_cast<int64_t>(u0 + ul) * M * DV;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int k = j * RPI + sub;
                     if (k < K) {
-                        const int ws = sidx[(ul * 2) * K + k], rs = sidx[(ul * 2 + 1) * K + k];
-                        wrow[i][j] = *reinterpret_cast<const Words<NW> *>(Su + static_cast<int64_t>(ws) * DV + c0);
-                        rrow[i][j] = *reinterpret_cast<const Words<NW> *>(Su + static_cast<int64_t>(rs) * DV + c0);
+                        wrow[i][j] = *reinterpret_cast<const Words<NW> *>(row_of(ul, 0, k) + c0);
+                        rrow[i][j] = *reinterpret_cast<const Words<NW> *>(row_of(ul, 1, k) + c0);
                     }
                 }
                 const int un = u0 + ul;
@@ -487,7 +511,6 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                     for (int c = 0; c < CPL; ++c) acc[c] = fmaf(rho, x[c], acc[c]);
                 }
             }
-            TS *Su = S + static_cast<int64_t>(u0 + ul) * M * DV;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int k = j * RPI + sub;
@@ -500,8 +523,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) y[c] = fmaf(lam, vin[i][c] - x[c], x[c]);
                         const Words<NW> nw = pack<TS, NW>(y);
-                        const int ws = sidx[(ul * 2) * K + k];
-                        *reinterpret_cast<Words<NW> *>(Su + static_cast<int64_t>(ws) * DV + c0) = nw;
+                        *reinterpret_cast<Words<NW> *>(row_of(ul, 0, k) + c0) = nw;
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) acc[c] = fmaf(cr, y[c] - x[c], acc[c]);
                     }
@@ -546,8 +568,12 @@ hipError_t launch_kd(const StepArgs &a, hipStream_t st) {
         const StepLds lo = step_lds(UPW, a.K, a.U * a.d_p, RowGeom<TS, DV>::RPI, DV);
         const int units = a.B * a.H;
         const unsigned grid = static_cast<unsigned>((units + UPW - 1) / UPW);
-        hipLaunchKernelGGL((step_fused_kernel<TIn, TS, KP, DV>), dim3(grid), dim3(kWave),
-                           static_cast<size_t>(lo.total), st, a);
+        if (a.cache)
+            hipLaunchKernelGGL((step_fused_kernel<TIn, TS, KP, DV, true>), dim3(grid), dim3(kWave),
+                               static_cast<size_t>(lo.total), st, a);
+        else
+            hipLaunchKernelGGL((step_fused_kernel<TIn, TS, KP, DV, false>), dim3(grid), dim3(kWave),
+                               static_cast<size_t>(lo.total), st, a);
         return hipGetLastError();
     }
 }

@@ -24,7 +24,9 @@ EXPORTED = ("ramnet_decode_addresses", "ramnet_workspace_bytes",
             "ramnet_layer_workspace_bytes", "ramnet_project_inputs",
             "ramnet_layer_forward", "ramnet_layer_step",
             "ramnet_packed_weights_bytes", "ramnet_pack_weights",
-            "ramnet_scan_backward", "ramnet_scan_prefill_noalloc")
+            "ramnet_scan_backward", "ramnet_scan_prefill_noalloc",
+            "ramnet_host_alloc", "ramnet_host_free", "ramnet_tier_reset",
+            "ramnet_step_decode_tiered", "ramnet_tier_rebalance", "ramnet_tier_flush")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -47,6 +49,11 @@ class Proj(C.Structure):
                 ("w_v", C.c_void_p), ("w_g", C.c_void_p),
                 ("w_gamma", C.c_void_p), ("w_o", C.c_void_p),
                 ("alpha", C.c_void_p), ("w_in_packed", C.c_void_p)]
+
+
+class TieredStateC(C.Structure):
+    _fields_ = [("S_host", C.c_void_p), ("cache", C.c_void_p), ("line_slot", C.c_void_p),
+                ("slot_line", C.c_void_p), ("hits", C.c_void_p), ("C", C.c_int32)]
 
 
 class RamnetError(RuntimeError):
@@ -107,6 +114,16 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [pp, pw, P, P, P, P, P, P, pa, P, C.c_size_t, P]
         f.restype = C.c_int
+    lib.ramnet_host_alloc.argtypes = [C.c_size_t, C.POINTER(C.c_void_p)]
+    lib.ramnet_host_alloc.restype = C.c_int
+    lib.ramnet_host_free.argtypes = [P]
+    lib.ramnet_host_free.restype = C.c_int
+    pt = C.POINTER(TieredStateC)
+    for f in (lib.ramnet_tier_reset, lib.ramnet_tier_rebalance, lib.ramnet_tier_flush):
+        f.argtypes = [pp, pt, P]
+        f.restype = C.c_int
+    lib.ramnet_step_decode_tiered.argtypes = [pp] + [P] * 7 + [pt, P, P, pa, P]
+    lib.ramnet_step_decode_tiered.restype = C.c_int
     lib.ramnet_status_str.argtypes = [C.c_int]
     lib.ramnet_status_str.restype = C.c_char_p
     lib.ramnet_last_error.restype = C.c_char_p
@@ -398,6 +415,93 @@ def step_decode(q, k, v, gamma, g, pos, S, mass, *, d_p: int, U: int, K: int,
     ao = new_addresses((B, H, K), v.device) if export_addresses else None
     plan(q, k, v, gamma, g, pos, S, mass, out, norm_w=norm_w, addr_out=ao)
     return (out, ao) if export_addresses else out
+
+
+# ---------------------------------------------------------------- tiered state
+
+class TieredState:
+    """A decoding state whose rows live in pinned host memory, with at most C
+    rows per (batch, head) cached in device memory (include/ramnet.h,
+    ramnet_tiered_state).  S_host is filled from `S` (any device or host
+    tensor [B,H,M,d_v] of the state dtype); the cache starts empty."""
+
+    def __init__(self, S, C_lines: int):
+        torch = _torch()
+        B, H, M, d_v = S.shape
+        self.shape = (B, H, M, d_v)
+        self.C = int(C_lines)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        lib = load_library()
+        nbytes = S.numel() * S.element_size()
+        ptr = C.c_void_p()
+        _raise(lib.ramnet_host_alloc(nbytes, C.byref(ptr)))
+        self._host_ptr = ptr.value
+        self._free = lib.ramnet_host_free
+        raw = (C.c_uint8 * max(nbytes, 1)).from_address(ptr.value)
+        self.S_host = torch.frombuffer(raw, dtype=torch.uint8)[:nbytes].view(S.dtype).view(S.shape)
+        self.S_host.copy_(S)
+        self.cache = torch.empty((B, H, self.C, d_v), dtype=S.dtype, device=dev)
+        self.line_slot = torch.empty((B, H, self.C), dtype=torch.int32, device=dev)
+        self.slot_line = torch.empty((B, H, M), dtype=torch.int32, device=dev)
+        self.hits = torch.empty((B, H, M), dtype=torch.int32, device=dev)  # uint32 in C
+
+    def __del__(self):
+        ptr, self._host_ptr = getattr(self, "_host_ptr", None), None
+        if ptr:
+            try:
+                _torch().cuda.synchronize()
+            finally:
+                self._free(C.c_void_p(ptr))
+
+    def struct(self) -> TieredStateC:
+        return TieredStateC(C.c_void_p(self.S_host.data_ptr()), _ptr(self.cache),
+                            _ptr(self.line_slot), _ptr(self.slot_line), _ptr(self.hits), self.C)
+
+
+def _tier_call(name, p: Params, ts: TieredState):
+    if tuple(ts.shape) != (p.B, p.H, p.M, p.d_v):
+        raise ValueError(f"tiered state of shape {ts.shape} for parameters "
+                         f"{(p.B, p.H, p.M, p.d_v)}")
+    st = ts.struct()
+    _raise(getattr(load_library(), name)(C.byref(p), C.byref(st), _stream()))
+
+
+def tier_reset(p: Params, ts: TieredState):
+    _tier_call("ramnet_tier_reset", p, ts)
+
+
+def tier_rebalance(p: Params, ts: TieredState):
+    _tier_call("ramnet_tier_rebalance", p, ts)
+
+
+def tier_flush(p: Params, ts: TieredState):
+    _tier_call("ramnet_tier_flush", p, ts)
+
+
+def step_decode_tiered(p: Params, q, k, v, gamma, g, pos, ts: TieredState, mass, out, *,
+                       norm_w=None, addr_out: Optional[Addresses] = None):
+    """ramnet_step_decode_tiered: one token per sequence on a tiered state;
+    p from make_params with T = 1."""
+    if tuple(ts.shape) != (p.B, p.H, p.M, p.d_v):
+        raise ValueError(f"tiered state of shape {ts.shape} for parameters "
+                         f"{(p.B, p.H, p.M, p.d_v)}")
+    sh = _Shapes(p)
+    torch = _torch()
+    u = (p.B, p.H)
+    f32 = torch.float32
+    ptrs = (_arg(q, "q", u + (sh.L,), sh.ind), _arg(k, "k", u + (sh.L,), sh.ind),
+            _arg(v, "v", u + (p.d_v,), sh.ind), _arg(gamma, "gamma", u, sh.ind),
+            _arg(g, "g", u + (p.d_v,), sh.ind), _arg(norm_w, "norm_w", (p.d_v,), f32, False),
+            _arg(pos, "pos", (p.B,), torch.int32, p.cape != 0))
+    m = _arg(mass, "mass", (p.B, p.H, p.M), f32)
+    o = _arg(out, "out", u + (p.d_v,), sh.std)
+    if ts.cache.dtype != sh.std:
+        raise ValueError(f"tiered state of dtype {ts.cache.dtype}, expected {sh.std}")
+    ao = _addr_struct(addr_out, (p.B, p.H, p.K), "addr_out")
+    st = ts.struct()
+    _raise(load_library().ramnet_step_decode_tiered(
+        C.byref(p), *ptrs, C.byref(st), m, o, C.byref(ao) if ao is not None else None, _stream()))
+    return out
 
 
 # ---------------------------------------------------------------- whole layer

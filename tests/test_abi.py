@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(rn):
 
 def test_version_and_status_strings(rn):
     lib = rn.load_library()
-    assert lib.ramnet_version() == 5
+    assert lib.ramnet_version() == 6
     for code in (0, -1, -2, -3, -4):
         assert lib.ramnet_status_str(code).decode() != "unknown status"
 
@@ -308,3 +308,36 @@ def test_binding_rejects_host_tensors(rn):
     with pytest.raises(ValueError, match="is required"):
         rn._arg(None, "x", (4,), torch.float32)
     assert rn._arg(None, "x", (4,), torch.float32, required=False) is None
+
+
+def test_tiered_state_arguments(rn):
+    """Host-side checks of the tiered-state calls: the cache size, NULL
+    buffers, overlaps and the fused step's shapes (nothing is launched)."""
+    lib = rn.load_library()
+    p = good(rn, T=1, K=16, d_v=128, state_dtype=rn.BF16)
+    M = p.M
+    units = p.B * p.H
+
+    def ts(**kw):
+        base = dict(S_host=FAKE, cache=FAKE + (1 << 32), line_slot=FAKE + (2 << 32),
+                    slot_line=FAKE + (3 << 32), hits=FAKE + (4 << 32), C=64)
+        base.update(kw)
+        return rn.TieredStateC(**base)
+
+    for C_ in (0, -1, M + 1):
+        st = lib.ramnet_tier_rebalance(C.byref(p), C.byref(ts(C=C_)), None)
+        assert st == -1 and "outside" in lib.ramnet_last_error().decode()
+    assert lib.ramnet_tier_flush(C.byref(p), C.byref(ts(hits=None)), None) == -1
+    assert "ts->hits is NULL" in lib.ramnet_last_error().decode()
+    assert lib.ramnet_tier_reset(C.byref(p), None, None) == -1
+    # the cache on top of the host rows
+    st = lib.ramnet_tier_reset(C.byref(p), C.byref(ts(cache=FAKE + units * M * 64)), None)
+    assert st == -1 and "overlaps" in lib.ramnet_last_error().decode()
+    x = [C.c_void_p(FAKE + ((10 + i) << 32)) for i in range(10)]
+    st = lib.ramnet_step_decode_tiered(C.byref(good(rn, T=1, K=40)), *x[:7], C.byref(ts()),
+                                       x[7], x[8], None, None)
+    assert st == -2 and "fused step" in lib.ramnet_last_error().decode()
+    st = lib.ramnet_step_decode_tiered(C.byref(p), *x[:7], C.byref(ts()), x[7], None, None, None)
+    assert st == -1 and "out is NULL" in lib.ramnet_last_error().decode()
+    # a zero-size host allocation is refused by nothing; NULL out pointer is
+    assert lib.ramnet_host_alloc(16, None) == -1

@@ -441,18 +441,28 @@ def test_resume_and_steps(rn, name):
     assert_close(to_np(d2["S"]), to_np(dw["S"]), bf, "steps S", slot_state=True)
 
 
-def decode_steps_check(rn, orc, w, B, n_steps, seqs=None, content_heads=0):
+def decode_steps_check(rn, orc, w, B, n_steps, seqs=None, content_heads=0, tier_lines=None,
+                       rebalance_every=4):
     """Runs n_steps decode steps for all B x H units on the GPU and, for the
     sequences `seqs` (None = all; every head of each), in the oracle.  Each
     step: addresses tie-aware against the oracle's; then the oracle's GSU,
     read, norm and gate on the adopted addresses (its own, or the GPU's where
     a near-tie made both correct), so every step of every sampled unit is
-    compared, and the state and mass at the end.  Returns (units that
-    adopted a GPU set, units compared, steps compared)."""
+    compared, and the state and mass at the end.  With tier_lines, the GPU
+    runs the tiered step (rows in pinned host memory, tier_lines cached per
+    unit, a rebalance every rebalance_every steps) and its state is flushed
+    to host memory at the end.  Returns (units that adopted a GPU set, units
+    compared, steps compared)."""
     H = w.H
     init = synth.make_inputs(w, B=B, T=1)
     S_d = dev(init["S0"], "bf16")
     m_d = dev(init["m0"], "f32")
+    if tier_lines:
+        tp = rn.make_params(B, 1, H, w.d_p, w.U, w.K, w.d_v, rn.BF16, rn.BF16, cape=w.cape,
+                            content_heads=content_heads)
+        ts = rn.TieredState(S_d, tier_lines)
+        rn.tier_reset(tp, ts)
+        del S_d
     seqs = np.arange(B) if seqs is None else np.asarray(seqs)
     # the oracle holds the sampled sequences (all heads) as a batch
     S_o = np.ascontiguousarray(init["S0"][seqs])
@@ -466,9 +476,16 @@ def decode_steps_check(rn, orc, w, B, n_steps, seqs=None, content_heads=0):
     done = 0
     for step in range(n_steps):
         s = synth.make_decode_step(w, step, B=B)
-        plan(dev(s["q"], "bf16"), dev(s["k"], "bf16"), dev(s["v"], "bf16"),
-             dev(s["gamma"], "bf16"), dev(s["g"], "bf16"),
-             torch.from_numpy(pos).cuda(), S_d, m_d, out, addr_out=ao)
+        if tier_lines:
+            rn.step_decode_tiered(tp, dev(s["q"], "bf16"), dev(s["k"], "bf16"), dev(s["v"], "bf16"),
+                                  dev(s["gamma"], "bf16"), dev(s["g"], "bf16"),
+                                  torch.from_numpy(pos).cuda(), ts, m_d, out, addr_out=ao)
+            if (step + 1) % rebalance_every == 0:
+                rn.tier_rebalance(tp, ts)
+        else:
+            plan(dev(s["q"], "bf16"), dev(s["k"], "bf16"), dev(s["v"], "bf16"),
+                 dev(s["gamma"], "bf16"), dev(s["g"], "bf16"),
+                 torch.from_numpy(pos).cuda(), S_d, m_d, out, addr_out=ao)
         torch.cuda.synchronize()
         x = {n: np.ascontiguousarray(s[n][seqs][:, None]) for n in s}  # [b,1,H,*]
         p_u = np.ascontiguousarray(pos[seqs])
@@ -490,6 +507,10 @@ def decode_steps_check(rn, orc, w, B, n_steps, seqs=None, content_heads=0):
         assert_close(to_np(out)[seqs], ref[:, 0], True, f"out step {step}")
         pos = pos + 1
         done += 1
+    if tier_lines:
+        rn.tier_flush(tp, ts)
+        torch.cuda.synchronize()
+        S_d = ts.S_host
     assert_close(to_np(S_d)[seqs], S_o, True, "S", slot_state=True)
     assert_close(to_np(m_d)[seqs], m_o, False, "mass")
     return int(adopted.sum()), adopted.size, done
