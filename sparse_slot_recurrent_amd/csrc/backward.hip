@@ -757,7 +757,7 @@ __global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int 
 //     before the token.  In the adjoint a read is therefore folded into that
 //     write (its rho dr joins dS+ before the write is undone), and reads of
 //     one slot are summed in read order, so no two lanes update one row.
-constexpr int kSerThreads = 256;
+constexpr int kSerThreads = 1024;
 constexpr int kRowLanes = 16;
 constexpr int kSerGroups = kSerThreads / kRowLanes;
 constexpr int kSerKMax = 64;
@@ -812,30 +812,57 @@ __device__ __forceinline__ void store_cpl(TS *p, const float (&x)[CPL]) {
     }
 }
 
-// Stages token t's events, v (or, with ADJ, v and dr) and gamma, and works
-// out the generations and the read-write relations above.  Ends with a
-// barrier.
+// One token's inputs as a thread loads them: events (threads < 2K), v and,
+// with ADJ, dr (threads < DV; DV <= kSerThreads), gamma (thread 0).  The
+// next token's are requested while the current one's rows move.
+struct SerPf {
+    int idx;
+    float wt, v, dr, gam;
+};
+
 template <typename TIn, bool ADJ, int DV>
-__device__ __forceinline__ void ser_stage(const BwdArgs &a, SerTok &tk, float *sv, float *sdr, int b, int h,
-                                          int t) {
+__device__ __forceinline__ SerPf ser_load(const BwdArgs &a, int b, int h, int t) {
     const int K = a.K, tid = threadIdx.x;
     const int64_t th = (static_cast<int64_t>(b) * a.T + t) * a.H + h;
+    SerPf f{};
     if (tid < K) {
-        tk.w[tid] = a.w_idx[th * K + tid];
-        tk.wt[tid] = a.w_wt[th * K + tid];
+        f.idx = a.w_idx[th * K + tid];
+        f.wt = a.w_wt[th * K + tid];
     } else if (tid < 2 * K) {
-        tk.r[tid - K] = a.r_idx[th * K + tid - K];
-        tk.rt[tid - K] = a.r_wt[th * K + tid - K];
+        f.idx = a.r_idx[th * K + tid - K];
+        f.wt = a.r_wt[th * K + tid - K];
     }
-    for (int c = tid; c < DV; c += kSerThreads) {
-        sv[c] = to_f32(static_cast<const TIn *>(a.v)[th * DV + c]);
-        if (ADJ) sdr[c] = a.dr[th * DV + c];
+    if (tid < DV) {
+        f.v = to_f32(static_cast<const TIn *>(a.v)[th * DV + tid]);
+        if (ADJ) f.dr = a.dr[th * DV + tid];
+    }
+    if (tid == 0) f.gam = to_f32(static_cast<const TIn *>(a.gamma)[th]);
+    return f;
+}
+
+// Stages a token's loaded inputs in LDS and works out the generations and
+// the read-write relations above.  Every LDS write of the previous token's
+// walk is behind a barrier already; this ends with one.  Only LDS is
+// ordered here (the state's global hand-offs have their own barriers).
+template <bool ADJ, int DV>
+__device__ __forceinline__ void ser_stage(const BwdArgs &a, SerTok &tk, float *sv, float *sdr, const SerPf &f) {
+    const int K = a.K, tid = threadIdx.x;
+    if (tid < K) {
+        tk.w[tid] = f.idx;
+        tk.wt[tid] = f.wt;
+    } else if (tid < 2 * K) {
+        tk.r[tid - K] = f.idx;
+        tk.rt[tid - K] = f.wt;
+    }
+    if (tid < DV) {
+        sv[tid] = f.v;
+        if (ADJ) sdr[tid] = f.dr;
     }
     if (tid == 0) {
-        tk.gam = to_f32(static_cast<const TIn *>(a.gamma)[th]);
+        tk.gam = f.gam;
         tk.maxgen = 0;
     }
-    __syncthreads();
+    lds_barrier();
     const int64_t M = a.M;
     auto valid = [&](int s) { return s >= 0 && static_cast<int64_t>(s) < M; };
     if (tid < K) {
@@ -874,7 +901,7 @@ __device__ __forceinline__ void ser_stage(const BwdArgs &a, SerTok &tk, float *s
         tk.rfirst[k] = first;
         tk.rsr[k] = rs;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // The replay: records each write's row and mass before it and each read's
@@ -893,8 +920,10 @@ __global__ __launch_bounds__(kSerThreads) void bwd_record_serial_kernel(BwdArgs 
     const int glead = (threadIdx.x % kWave) - gl;  // the group's first lane in its wave
     TS *Su = static_cast<TS *>(a.Sw) + static_cast<int64_t>(unit) * M * DV;
     float *mu = a.mw + static_cast<int64_t>(unit) * M;
+    SerPf pf = ser_load<TIn, false, DV>(a, b, h, 0);
     for (int t = 0; t < T; ++t) {
-        ser_stage<TIn, false, DV>(a, tk, sv, nullptr, b, h, t);
+        ser_stage<false, DV>(a, tk, sv, nullptr, pf);
+        if (t + 1 < T) pf = ser_load<TIn, false, DV>(a, b, h, t + 1);
         const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
         for (int g = 0; g <= tk.maxgen; ++g) {
             const int ne = g == 0 ? 2 * K : K;
@@ -952,7 +981,8 @@ __global__ __launch_bounds__(kSerThreads) void bwd_record_serial_kernel(BwdArgs 
             for (int c = 0; c < CPL; ++c) x[c] = snew[wl * DV + c0 + c];
             store_cpl<float, CPL>(a.rec_r + (rec0 + k) * DV + c0, x);
         }
-        __syncthreads();
+        // these record stores are not read back here: only LDS is ordered
+        lds_barrier();
     }
 }
 
@@ -970,8 +1000,10 @@ __global__ __launch_bounds__(kSerThreads) void bwd_adjoint_serial_kernel(BwdArgs
     const int glead = (threadIdx.x % kWave) - gl;
     float *dSu = a.dS0 + static_cast<int64_t>(unit) * M * DV;
     float *dmu = a.dmass0 + static_cast<int64_t>(unit) * M;
+    SerPf pf = ser_load<TIn, true, DV>(a, b, h, T - 1);
     for (int t = T - 1; t >= 0; --t) {
-        ser_stage<TIn, true, DV>(a, tk, sv, sdr, b, h, t);
+        ser_stage<true, DV>(a, tk, sv, sdr, pf);
+        if (t > 0) pf = ser_load<TIn, true, DV>(a, b, h, t - 1);
         const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
         const int64_t th = (static_cast<int64_t>(b) * T + t) * a.H + h;
         for (int g = tk.maxgen; g >= 0; --g) {
