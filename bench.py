@@ -134,7 +134,7 @@ def measured_traffic(workload: str, stage: str):
         return None
     total, found = 0.0, False
     for name, v in rec[workload]["kernels"].items():
-        if name.split("<")[0] in STAGE_KERNELS.get(stage, ()):
+        if name.split("<")[0].split("(")[0] in STAGE_KERNELS.get(stage, ()):
             total += v["fetch_bytes"] + v["write_bytes"]
             found = True
     return total if found else None
