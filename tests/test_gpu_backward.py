@@ -77,6 +77,9 @@ CASES = {
     "walk_dv192": ("prefill_top8", dict(B=1, T=40, H=2), dict(wl=dict(d_v=192))),
     "walk_dv256_m4096": ("tiny", dict(B=1, T=40, H=2), dict(wl=dict(d_v=256, U=6, K=16))),
     "walk_large_state": ("large_state", dict(B=1, T=40, H=2), dict(wl=dict(steps=0))),
+    # the walk with CAPE form B, a content-only head and a norm weight
+    "walk_dv128_cape2_mask_norm": ("decode", dict(B=2, T=32, H=2),
+                                   dict(wl=dict(steps=0), cape=2, content_heads=0b01, norm=True)),
 }
 
 

@@ -67,6 +67,8 @@ CASES = {
     "m4096_f32": (dict(U=6, K=8, d_v=64, state_dtype="f32", in_dtype="f32"), 24, 512, 10, 1),
     # a cache of one line
     "one_line": (dict(K=4), 8, 1, 8, 2),
+    # CAPE form C, d_v 256, K 32
+    "cape3_dv256_k32": (dict(cape=3, d_v=256, K=32), 8, 64, 6, 2),
 }
 
 
