@@ -291,12 +291,12 @@ ramnet_status ramnet_tier_flush(const ramnet_params *p, const ramnet_tiered_stat
  * Built for every d_v and M the forward takes, with U*d_p <= 64
  * (RAMNET_EUNSUPPORTED otherwise); the state may be fp32 or bf16 (the replay
  * rounds it as the forward does), the gradients are fp32.  d_v = 64 with
- * M <= 1024 keeps each slot's row and adjoint on chip and walks the events
- * grouped by slot; every other shape walks the tokens one by one, with the
- * replayed state in the workspace and the adjoint accumulated in dS0 and
- * dmass0 (which then start as dS_final and dmass_final), so it is far slower
- * per token.  A token may write one slot twice (caller-given addresses): the
- * writes apply in address order, as in the forward.
+ * M <= 1024 keeps each slot's row and adjoint on chip; every other shape
+ * walks slot ranges chunk by chunk with the replayed state in the workspace
+ * and the adjoint accumulated in dS0 and dmass0 (which then start as
+ * dS_final and dmass_final).  Both group each chunk's events by slot.  A
+ * token may write one slot twice (caller-given addresses): the writes apply
+ * in address order, as in the forward.
  *   q, k, v, gamma, g, norm_w, pos0   the forward's inputs (q, k only read
  *             when dq, dk are given)
  *   S0, mass0 [B,H,M,d_v] state_dtype, [B,H,M] fp32: the state before the

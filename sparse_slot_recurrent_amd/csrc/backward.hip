@@ -43,6 +43,14 @@
 //   bwd_sum_kernel      adds each token's lam dS+ and gamma terms over its
 //                       writes, in write order.
 //   bwd_omega_kernel    sums the d omega partials in a fixed order.
+//
+// Other shapes (d_v != 64, or M > 1024 with the rows in HBM) replace the two
+// serial kernels by bwd_record_range_kernel and bwd_adjoint_range_kernel: a
+// unit's slots split into eight ranges (slot mod 8), one workgroup per
+// (unit, range) owning its slots for the whole sequence; per chunk the
+// range's events are sorted by (slot, time) in LDS and a 16-lane group per
+// slot walks them with the slot's row, mass or adjoint in registers and the
+// state, its copy and its adjoint in HBM (the slot-range walk below).
 #include "device_common.h"
 #include "launch.h"
 
@@ -741,38 +749,11 @@ __global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int 
     }
 }
 
-// ---------------------------------------------------------------- per-token walk
+// ---------------------------------------------------------------- rows in HBM
 //
-// Any d_v and any number of slots (rows in HBM): one workgroup per (batch,
-// head) unit walks the tokens in order (the replay) or in reverse (the
-// adjoint).  A token's events run in parallel, one group of kRowLanes lanes
-// per event row, each lane holding DV / kRowLanes adjacent channels.  The
-// replayed state and mass live in the workspace (copied from S0 and mass0
-// first); the adjoint accumulates in dS0 and dmass0 themselves, which start
-// as dS_final and dmass_final.  Within a token:
-//   * a write whose slot an earlier write of the token already took waits
-//     for it (its generation is the number of such earlier writes; the
-//     decoder's slots are distinct, so there is normally one generation);
-//   * a read sees the token's last write to its slot, if any, else the state
-//     before the token.  In the adjoint a read is therefore folded into that
-//     write (its rho dr joins dS+ before the write is undone), and reads of
-//     one slot are summed in read order, so no two lanes update one row.
-constexpr int kSerThreads = 1024;
+// A row of DV channels is moved by kRowLanes lanes, DV / kRowLanes adjacent
+// channels each (fp32, or bf16 in 8-byte pieces).
 constexpr int kRowLanes = 16;
-constexpr int kSerGroups = kSerThreads / kRowLanes;
-constexpr int kSerKMax = 64;
-
-struct SerTok {
-    int w[kSerKMax], r[kSerKMax];
-    float wt[kSerKMax], rt[kSerKMax];
-    int gen[kSerKMax];     // writes: earlier writes of the token to the slot
-    int wlast[kSerKMax];   // reads: the token's last write to the slot, or -1
-    int rfirst[kSerKMax];  // reads: whether this is the first read of its slot
-    float rsw[kSerKMax];   // writes (the last to a slot): rho summed over its slot's reads
-    float rsr[kSerKMax];   // reads (the first of a slot): rho summed over the slot's reads
-    int maxgen;
-    float gam;
-};
 
 template <typename TS, int CPL>
 __device__ __forceinline__ void load_cpl(const TS *p, float (&x)[CPL]) {
@@ -812,282 +793,278 @@ __device__ __forceinline__ void store_cpl(TS *p, const float (&x)[CPL]) {
     }
 }
 
-// One token's inputs as a thread loads them: events (threads < 2K), v and,
-// with ADJ, dr (threads < DV; DV <= kSerThreads), gamma (thread 0).  The
-// next token's are requested while the current one's rows move.
-struct SerPf {
-    int idx;
-    float wt, v, dr, gam;
+// ---------------------------------------------------------------- slot-range walk
+//
+// Any d_v and any number of slots, many tokens per step: a unit's slots are
+// split into kBR ranges (slot mod kBR), one workgroup per (unit, range), which
+// owns its slots for the whole sequence, so the workgroups never wait for one
+// another.  The sequence goes in chunks of br_chunk(K) tokens.  Per chunk:
+//   * the chunk's events on the range (writes and reads) are listed in LDS
+//     with the key slot << 32 | t << 7 | read << 6 | k and sorted (bitonic
+//     network): a slot's events end up together, in forward order (a
+//     token's writes before its reads, writes in address order);
+//   * one group of kRowLanes lanes per slot walks its events with the slot's
+//     row and mass (the replay, forwards: the row and mass before each write
+//     and the row at each read are recorded) or its adjoint dS and dm (the
+//     adjoint, backwards) in registers; the per-event inputs (weights,
+//     gamma, v, dr, the recorded rows) are gathered by token.
+// An event whose slot is outside [0, M) belongs to no range: the workgroup of
+// range k mod kBR writes its zero records or gradients.
+constexpr int kBR = 8;
+constexpr int kBRThreads = 1024;
+constexpr int kBRGroups = kBRThreads / kRowLanes;
+constexpr int kBRCap = 2048;  // events of a chunk (writes and reads)
+
+__host__ __device__ inline int br_chunk(int K) {
+    int c = 64;
+    while (c > 1 && 2 * c * K > kBRCap) c /= 2;
+    return c;
+}
+
+struct BRLds {
+    unsigned long long key[kBRCap];
+    int seg[kBRCap + 1];
+    int wtot[kBRThreads / kWave];
+    int cnt, nseg;
 };
 
-template <typename TIn, bool ADJ, int DV>
-__device__ __forceinline__ SerPf ser_load(const BwdArgs &a, int b, int h, int t) {
+// Lists the range's events of tokens [t0, t0 + Cc), sorts them, and finds
+// the slot segments: afterwards g.seg[0 .. nseg] bound them.  inv(t, k, read)
+// is called for the invalid events this range answers for.
+template <typename Inv>
+__device__ __forceinline__ void br_group(const BwdArgs &a, BRLds &g, int b, int h, int r, int t0, int Cc,
+                                         Inv inv) {
     const int K = a.K, tid = threadIdx.x;
-    const int64_t th = (static_cast<int64_t>(b) * a.T + t) * a.H + h;
-    SerPf f{};
-    if (tid < K) {
-        f.idx = a.w_idx[th * K + tid];
-        f.wt = a.w_wt[th * K + tid];
-    } else if (tid < 2 * K) {
-        f.idx = a.r_idx[th * K + tid - K];
-        f.wt = a.r_wt[th * K + tid - K];
-    }
-    if (tid < DV) {
-        f.v = to_f32(static_cast<const TIn *>(a.v)[th * DV + tid]);
-        if (ADJ) f.dr = a.dr[th * DV + tid];
-    }
-    if (tid == 0) f.gam = to_f32(static_cast<const TIn *>(a.gamma)[th]);
-    return f;
-}
-
-// Stages a token's loaded inputs in LDS and works out the generations and
-// the read-write relations above.  Every LDS write of the previous token's
-// walk is behind a barrier already; this ends with one.  Only LDS is
-// ordered here (the state's global hand-offs have their own barriers).
-template <bool ADJ, int DV>
-__device__ __forceinline__ void ser_stage(const BwdArgs &a, SerTok &tk, float *sv, float *sdr, const SerPf &f) {
-    const int K = a.K, tid = threadIdx.x;
-    if (tid < K) {
-        tk.w[tid] = f.idx;
-        tk.wt[tid] = f.wt;
-    } else if (tid < 2 * K) {
-        tk.r[tid - K] = f.idx;
-        tk.rt[tid - K] = f.wt;
-    }
-    if (tid < DV) {
-        sv[tid] = f.v;
-        if (ADJ) sdr[tid] = f.dr;
-    }
-    if (tid == 0) {
-        tk.gam = f.gam;
-        tk.maxgen = 0;
-    }
-    lds_barrier();
     const int64_t M = a.M;
-    auto valid = [&](int s) { return s >= 0 && static_cast<int64_t>(s) < M; };
-    if (tid < K) {
-        const int s = tk.w[tid];
-        int gen = 0;
-        bool last = true;
-        float rs = 0.f;
-        if (valid(s)) {
-            for (int j = 0; j < K; ++j) {
-                if (tk.w[j] == s) {
-                    gen += j < tid ? 1 : 0;
-                    last = last && j <= tid;
-                }
+    if (tid == 0) g.cnt = 0;
+    __syncthreads();
+    const int nw = Cc * K;
+    for (int e = tid; e < 2 * nw; e += kBRThreads) {
+        const bool rd = e >= nw;
+        const int i = rd ? e - nw : e, t = i / K, k = i - t * K;
+        const int64_t th = (static_cast<int64_t>(b) * a.T + t0 + t) * a.H + h;
+        const int s = (rd ? a.r_idx : a.w_idx)[th * K + k];
+        if (s >= 0 && static_cast<int64_t>(s) < M) {
+            if ((s & (kBR - 1)) == r) {
+                const int pos = atomicAdd(&g.cnt, 1);
+                g.key[pos] = (static_cast<unsigned long long>(s) << 32) |
+                             static_cast<unsigned long long>((t << 7) | ((rd ? 1 : 0) << 6) | k);
             }
-            if (last)
-                for (int j = 0; j < K; ++j)
-                    if (tk.r[j] == s) rs += tk.rt[j];
+        } else if ((k & (kBR - 1)) == r) {
+            inv(t, k, rd);
         }
-        tk.gen[tid] = gen;
-        tk.rsw[tid] = last ? rs : 0.f;
-        if (gen) atomicMax(&tk.maxgen, gen);
-    } else if (tid < 2 * K) {
-        const int k = tid - K, s = tk.r[k];
-        int wl = -1, first = 1;
-        float rs = 0.f;
-        if (valid(s)) {
-            for (int j = 0; j < K; ++j) {
-                if (tk.w[j] == s) wl = j;
-                if (tk.r[j] == s) {
-                    first = first && j >= k;
-                    rs += tk.rt[j];
-                }
-            }
-        }
-        tk.wlast[k] = wl;
-        tk.rfirst[k] = first;
-        tk.rsr[k] = rs;
     }
-    lds_barrier();
-}
-
-// The replay: records each write's row and mass before it and each read's
-// row after the token's writes, applying the writes to the workspace state.
-// Dynamic LDS: the rows the token's writes leave, [K][DV] fp32.
-template <typename TIn, typename TS, int DV>
-__global__ __launch_bounds__(kSerThreads) void bwd_record_serial_kernel(BwdArgs a) {
-    constexpr int CPL = DV / kRowLanes;
-    extern __shared__ __align__(16) float snew[];
-    __shared__ SerTok tk;
-    __shared__ float sv[DV];
-    const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
-    const int K = a.K, T = a.T;
-    const int64_t M = a.M;
-    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
-    const int glead = (threadIdx.x % kWave) - gl;  // the group's first lane in its wave
-    TS *Su = static_cast<TS *>(a.Sw) + static_cast<int64_t>(unit) * M * DV;
-    float *mu = a.mw + static_cast<int64_t>(unit) * M;
-    SerPf pf = ser_load<TIn, false, DV>(a, b, h, 0);
-    for (int t = 0; t < T; ++t) {
-        ser_stage<false, DV>(a, tk, sv, nullptr, pf);
-        if (t + 1 < T) pf = ser_load<TIn, false, DV>(a, b, h, t + 1);
-        const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
-        for (int g = 0; g <= tk.maxgen; ++g) {
-            const int ne = g == 0 ? 2 * K : K;
-            for (int e = grp; e < ne; e += kSerGroups) {
-                float x[CPL];
-                if (e < K) {
-                    if (tk.gen[e] != g) continue;
-                    const int s = tk.w[e];
-                    float *rw = a.rec_w + (rec0 + e) * DV + c0;
-                    if (s < 0 || static_cast<int64_t>(s) >= M) {
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) x[c] = 0.f;
-                        store_cpl<float, CPL>(rw, x);
-                        if (gl == 0) a.rec_m[rec0 + e] = 0.f;
-                        continue;
+    __syncthreads();
+    const int n = g.cnt;
+    int np = 1;
+    while (np < n) np <<= 1;
+    for (int i = n + tid; i < np; i += kBRThreads) g.key[i] = ~0ull;
+    __syncthreads();
+    for (int kk = 2; kk <= np; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < np; i += kBRThreads) {
+                const int ij = i ^ j;
+                if (ij > i) {
+                    const unsigned long long x = g.key[i], y = g.key[ij];
+                    const bool up = (i & kk) == 0;
+                    if ((x > y) == up) {
+                        g.key[i] = y;
+                        g.key[ij] = x;
                     }
-                    TS *row = Su + static_cast<int64_t>(s) * DV + c0;
-                    const float m0 = gl == 0 ? mu[s] : 0.f;
-                    load_cpl<TS, CPL>(row, x);
-                    const float m = __shfl(m0, glead, kWave);
-                    store_cpl<float, CPL>(rw, x);
-                    const float w = tk.wt[e];
-                    if (w > 0.f) {
-                        const float alpha = retention(w, expf(tk.gam));
-                        const float mn = fmaf(alpha, m, w);
-                        const float lam = w / (mn + a.eps_gsu);
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) x[c] = stored<TS>(fmaf(lam, sv[c0 + c] - x[c], x[c]));
-                        store_cpl<TS, CPL>(row, x);
-                        if (gl == 0) mu[s] = mn;
-                    }
-                    if (gl == 0) a.rec_m[rec0 + e] = m;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) snew[e * DV + c0 + c] = x[c];
-                } else {
-                    const int k = e - K, s = tk.r[k];
-                    if (tk.wlast[k] >= 0) continue;  // after the barrier, from LDS
-                    float *rr = a.rec_r + (rec0 + k) * DV + c0;
-                    if (s < 0 || static_cast<int64_t>(s) >= M) {
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) x[c] = 0.f;
-                    } else {
-                        load_cpl<TS, CPL>(Su + static_cast<int64_t>(s) * DV + c0, x);
-                    }
-                    store_cpl<float, CPL>(rr, x);
                 }
             }
             __syncthreads();
         }
-        for (int k = grp; k < K; k += kSerGroups) {
-            const int wl = tk.wlast[k];
-            if (wl < 0) continue;
-            float x[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) x[c] = snew[wl * DV + c0 + c];
-            store_cpl<float, CPL>(a.rec_r + (rec0 + k) * DV + c0, x);
-        }
-        // these record stores are not read back here: only LDS is ordered
-        lds_barrier();
     }
+    // segment starts, in list order: thread i takes positions 2i, 2i + 1
+    int f[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = 2 * tid + q;
+        f[q] = i < n && (i == 0 || (g.key[i] >> 32) != (g.key[i - 1] >> 32)) ? 1 : 0;
+    }
+    const int lane = tid % kWave, wid = tid / kWave;
+    int incl = f[0] + f[1];
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) g.wtot[wid] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < kBRThreads / kWave; ++w) {
+        const int c = g.wtot[w];
+        base += w < wid ? c : 0;
+        tot += c;
+    }
+    int at = base + incl - (f[0] + f[1]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (f[q]) g.seg[at] = 2 * tid + q;
+        at += f[q];
+    }
+    if (tid == 0) {
+        g.nseg = tot;
+        g.seg[tot] = n;
+    }
+    __syncthreads();
 }
 
-// The adjoint, tokens in reverse: a token's reads before its writes (the
-// forward took the writes first), writes in reverse generation order.
-template <typename TIn, int DV>
-__global__ __launch_bounds__(kSerThreads) void bwd_adjoint_serial_kernel(BwdArgs a) {
+template <typename TIn, typename TS, int DV>
+__global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a) {
     constexpr int CPL = DV / kRowLanes;
-    __shared__ SerTok tk;
-    __shared__ float sv[DV], sdr[DV];
-    const int unit = blockIdx.x, b = unit / a.H, h = unit % a.H;
+    __shared__ BRLds g;
+    const int unit = blockIdx.x, r = blockIdx.y, b = unit / a.H, h = unit % a.H;
     const int K = a.K, T = a.T;
     const int64_t M = a.M;
     const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
     const int glead = (threadIdx.x % kWave) - gl;
-    float *dSu = a.dS0 + static_cast<int64_t>(unit) * M * DV;
-    float *dmu = a.dmass0 + static_cast<int64_t>(unit) * M;
-    SerPf pf = ser_load<TIn, true, DV>(a, b, h, T - 1);
-    for (int t = T - 1; t >= 0; --t) {
-        ser_stage<true, DV>(a, tk, sv, sdr, pf);
-        if (t > 0) pf = ser_load<TIn, true, DV>(a, b, h, t - 1);
-        const int64_t rec0 = (static_cast<int64_t>(unit) * T + t) * K;
-        const int64_t th = (static_cast<int64_t>(b) * T + t) * a.H + h;
-        for (int g = tk.maxgen; g >= 0; --g) {
-            const int ne = g == tk.maxgen ? 2 * K : K;
-            for (int e = grp; e < ne; e += kSerGroups) {
-                float d[CPL];
-                if (e >= K) {
-                    // a read with no write of the token on its slot, the
-                    // first of its slot: dS += (sum of the slot's rho) dr
-                    const int k = e - K, s = tk.r[k];
-                    if (tk.wlast[k] >= 0 || !tk.rfirst[k] || s < 0 || static_cast<int64_t>(s) >= M) continue;
-                    float *row = dSu + static_cast<int64_t>(s) * DV + c0;
-                    load_cpl<float, CPL>(row, d);
-                    const float rs = tk.rsr[k];
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) d[c] = fmaf(rs, sdr[c0 + c], d[c]);
-                    store_cpl<float, CPL>(row, d);
+    const int C = br_chunk(K);
+    TS *Su = static_cast<TS *>(a.Sw) + static_cast<int64_t>(unit) * M * DV;
+    float *mu = a.mw + static_cast<int64_t>(unit) * M;
+    const TIn *vin = static_cast<const TIn *>(a.v);
+    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    for (int t0 = 0; t0 < T; t0 += C) {
+        const int Cc = min(C, T - t0);
+        br_group(a, g, b, h, r, t0, Cc, [&](int t, int k, bool rd) {
+            const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+            float *dst = (rd ? a.rec_r : a.rec_w) + rec * DV;
+            for (int c = 0; c < DV; ++c) dst[c] = 0.f;
+            if (!rd) a.rec_m[rec] = 0.f;
+        });
+        const int nseg = g.nseg;
+        for (int sg = grp; sg < nseg; sg += kBRGroups) {
+            const int lo = g.seg[sg], hi = g.seg[sg + 1];
+            const int slot = static_cast<int>(g.key[lo] >> 32);
+            TS *row = Su + static_cast<int64_t>(slot) * DV + c0;
+            float x[CPL];
+            load_cpl<TS, CPL>(row, x);
+            const float m0 = gl == 0 ? mu[slot] : 0.f;
+            float m = __shfl(m0, glead, kWave);
+            for (int i = lo; i < hi; ++i) {
+                const int ek = static_cast<int>(g.key[i] & 0xffffffffu);
+                const int t = ek >> 7, k = ek & 63;
+                const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+                if (ek & 64) {
+                    store_cpl<float, CPL>(a.rec_r + rec * DV + c0, x);
                     continue;
                 }
-                if (tk.gen[e] != g) continue;
-                const int s = tk.w[e];
-                float *dvk = a.dvk + (rec0 + e) * DV + c0;
-                const float w = tk.wt[e];
-                float dw = 0.f, dgk = 0.f;
-                if (s < 0 || static_cast<int64_t>(s) >= M) {
+                store_cpl<float, CPL>(a.rec_w + rec * DV + c0, x);
+                if (gl == 0) a.rec_m[rec] = m;
+                const int64_t th = (static_cast<int64_t>(b) * T + t0 + t) * a.H + h;
+                const float w = a.w_wt[th * K + k];
+                if (w > 0.f) {
+                    const float alpha = retention(w, expf(to_f32(gam[th])));
+                    m = fmaf(alpha, m, w);
+                    const float lam = w / (m + a.eps_gsu);
+                    const TIn *vr = vin + th * DV + c0;
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) d[c] = 0.f;
-                    store_cpl<float, CPL>(dvk, d);
-                } else {
-                    float *row = dSu + static_cast<int64_t>(s) * DV + c0;
-                    load_cpl<float, CPL>(row, d);
-                    const float rs = tk.rsw[e];
-                    if (rs != 0.f)
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) d[c] = fmaf(rs, sdr[c0 + c], d[c]);
-                    if (w > 0.f) {
-                        float sm[CPL];
-                        load_cpl<float, CPL>(a.rec_w + (rec0 + e) * DV + c0, sm);
-                        const float mm0 = gl == 0 ? a.rec_m[rec0 + e] : 0.f;
-                        const float dm0 = gl == 0 ? dmu[s] : 0.f;
-                        const float mm = __shfl(mm0, glead, kWave);
-                        const float dmp = __shfl(dm0, glead, kWave);
-                        const float eg = expf(tk.gam);
-                        const float alpha = retention(w, eg);
-                        const float mp = fmaf(alpha, mm, w);
-                        const float den = mp + a.eps_gsu;
-                        const float lam = w / den;
-                        float dl = 0.f;
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) dl = fmaf(d[c], sv[c0 + c] - sm[c], dl);
-                        // <dS+, v - S-> over the group's lanes (a butterfly:
-                        // every lane of the group gets the same sum)
-#pragma unroll
-                        for (int o = 1; o < kRowLanes; o <<= 1) dl += __shfl_xor(dl, o, kWave);
-                        float dv[CPL];
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) {
-                            dv[c] = lam * d[c];
-                            d[c] *= 1.0f - lam;
-                        }
-                        store_cpl<float, CPL>(dvk, dv);
-                        const float dmt = dmp - dl * w / (den * den);
-                        const float dalpha = dmt * mm;
-                        dw = dl / den + dmt;
-                        if (w < 1.0f && alpha > 0.f) {
-                            dw -= dalpha * eg * alpha / (1.0f - w);
-                            dgk = dalpha * alpha * log1pf(-w) * eg;
-                        }
-                        if (gl == 0) dmu[s] = dmt * alpha;
-                    } else {
-                        float z[CPL];
-#pragma unroll
-                        for (int c = 0; c < CPL; ++c) z[c] = 0.f;
-                        store_cpl<float, CPL>(dvk, z);
-                    }
-                    store_cpl<float, CPL>(row, d);
-                }
-                if (gl == 0) {
-                    a.dgk[rec0 + e] = dgk;
-                    a.dw[th * K + e] = dw;
+                    for (int c = 0; c < CPL; ++c) x[c] = stored<TS>(fmaf(lam, to_f32(vr[c]) - x[c], x[c]));
                 }
             }
-            __syncthreads();
+            store_cpl<TS, CPL>(row, x);
+            if (gl == 0) mu[slot] = m;
         }
+        __syncthreads();  // the rows written here may be another group's next chunk
+    }
+}
+
+template <typename TIn, int DV>
+__global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a) {
+    constexpr int CPL = DV / kRowLanes;
+    __shared__ BRLds g;
+    const int unit = blockIdx.x, r = blockIdx.y, b = unit / a.H, h = unit % a.H;
+    const int K = a.K, T = a.T;
+    const int64_t M = a.M;
+    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
+    const int glead = (threadIdx.x % kWave) - gl;
+    const int C = br_chunk(K);
+    float *dSu = a.dS0 + static_cast<int64_t>(unit) * M * DV;
+    float *dmu = a.dmass0 + static_cast<int64_t>(unit) * M;
+    const TIn *vin = static_cast<const TIn *>(a.v);
+    const TIn *gam = static_cast<const TIn *>(a.gamma);
+    const int nch = (T + C - 1) / C;
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const int t0 = ci * C, Cc = min(C, T - t0);
+        br_group(a, g, b, h, r, t0, Cc, [&](int t, int k, bool rd) {
+            if (rd) return;
+            const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+            for (int c = 0; c < DV; ++c) a.dvk[rec * DV + c] = 0.f;
+            a.dgk[rec] = 0.f;
+            a.dw[((static_cast<int64_t>(b) * T + t0 + t) * a.H + h) * K + k] = 0.f;
+        });
+        const int nseg = g.nseg;
+        for (int sg = grp; sg < nseg; sg += kBRGroups) {
+            const int lo = g.seg[sg], hi = g.seg[sg + 1];
+            const int slot = static_cast<int>(g.key[lo] >> 32);
+            float *row = dSu + static_cast<int64_t>(slot) * DV + c0;
+            float d[CPL];
+            load_cpl<float, CPL>(row, d);
+            const float dm0 = gl == 0 ? dmu[slot] : 0.f;
+            float dm = __shfl(dm0, glead, kWave);
+            for (int i = hi - 1; i >= lo; --i) {
+                const int ek = static_cast<int>(g.key[i] & 0xffffffffu);
+                const int t = ek >> 7, k = ek & 63;
+                const int64_t th = (static_cast<int64_t>(b) * T + t0 + t) * a.H + h;
+                if (ek & 64) {
+                    const float rho = a.r_wt[th * K + k];
+                    float dr[CPL];
+                    load_cpl<float, CPL>(a.dr + th * DV + c0, dr);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) d[c] = fmaf(rho, dr[c], d[c]);
+                    continue;
+                }
+                const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
+                float *dvk = a.dvk + rec * DV + c0;
+                const float w = a.w_wt[th * K + k];
+                float dw = 0.f, dgk = 0.f;
+                if (w > 0.f) {
+                    float sm[CPL];
+                    load_cpl<float, CPL>(a.rec_w + rec * DV + c0, sm);
+                    const TIn *vr = vin + th * DV + c0;
+                    const float mm0 = gl == 0 ? a.rec_m[rec] : 0.f;
+                    const float mm = __shfl(mm0, glead, kWave);
+                    const float eg = expf(to_f32(gam[th]));
+                    const float alpha = retention(w, eg);
+                    const float mp = fmaf(alpha, mm, w);
+                    const float den = mp + a.eps_gsu;
+                    const float lam = w / den;
+                    float dl = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) dl = fmaf(d[c], to_f32(vr[c]) - sm[c], dl);
+#pragma unroll
+                    for (int o = 1; o < kRowLanes; o <<= 1) dl += __shfl_xor(dl, o, kWave);
+                    float dv[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        dv[c] = lam * d[c];
+                        d[c] *= 1.0f - lam;
+                    }
+                    store_cpl<float, CPL>(dvk, dv);
+                    const float dmt = dm - dl * w / (den * den);
+                    const float dalpha = dmt * mm;
+                    dw = dl / den + dmt;
+                    if (w < 1.0f && alpha > 0.f) {
+                        dw -= dalpha * eg * alpha / (1.0f - w);
+                        dgk = dalpha * alpha * log1pf(-w) * eg;
+                    }
+                    dm = dmt * alpha;
+                } else {
+                    float z[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) z[c] = 0.f;
+                    store_cpl<float, CPL>(dvk, z);
+                }
+                if (gl == 0) {
+                    a.dgk[rec] = dgk;
+                    a.dw[th * K + k] = dw;
+                }
+            }
+            store_cpl<float, CPL>(row, d);
+            if (gl == 0) dmu[slot] = dm;
+        }
+        __syncthreads();
     }
 }
 
@@ -1103,18 +1080,12 @@ __global__ __launch_bounds__(256) void bwd_copy16_kernel(uint16_t *dst, const ui
         dst[i] = src[i];
 }
 
-// The walk for any d_v and any M: the starting buffers, the replay, the
-// output/read kernel, the adjoint.
+// The slot-range walk for any d_v and any M: the starting buffers, the
+// replay, the output/read kernel, the adjoint.
 template <typename TIn, int DV>
 hipError_t launch_walk(const BwdArgs &a, hipStream_t st) {
     const int units = a.B * a.H;
     const int64_t ns = static_cast<int64_t>(units) * a.M;
-    // the replay's LDS holds the token's written rows: up to 64 KiB
-    const size_t lds = static_cast<size_t>(a.K) * DV * 4;
-    const void *rk = a.state_bf16 ? reinterpret_cast<const void *>(bwd_record_serial_kernel<TIn, bf16_t, DV>)
-                                  : reinterpret_cast<const void *>(bwd_record_serial_kernel<TIn, float, DV>);
-    hipError_t e = hipFuncSetAttribute(rk, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
     auto grid_of = [](int64_t n) { return dim3(static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096))); };
     if (a.state_bf16)
         hipLaunchKernelGGL(bwd_copy16_kernel, grid_of(ns * DV), dim3(256), 0, st,
@@ -1125,15 +1096,16 @@ hipError_t launch_walk(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns), dim3(256), 0, st, a.mw, a.mass0, ns);
     hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns * DV), dim3(256), 0, st, a.dS0, a.dS_final, ns * DV);
     hipLaunchKernelGGL(bwd_copy_kernel, grid_of(ns), dim3(256), 0, st, a.dmass0, a.dmass_final, ns);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (a.state_bf16)
-        hipLaunchKernelGGL((bwd_record_serial_kernel<TIn, bf16_t, DV>), dim3(units), dim3(kSerThreads), lds, st, a);
+        hipLaunchKernelGGL((bwd_record_range_kernel<TIn, bf16_t, DV>), dim3(units, kBR), dim3(kBRThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((bwd_record_serial_kernel<TIn, float, DV>), dim3(units), dim3(kSerThreads), lds, st, a);
+        hipLaunchKernelGGL((bwd_record_range_kernel<TIn, float, DV>), dim3(units, kBR), dim3(kBRThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_out_kernel<TIn, DV>), dim3(units, kOutBlocks), dim3(kOutWaves * kWave), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_adjoint_serial_kernel<TIn, DV>), dim3(units), dim3(kSerThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_adjoint_range_kernel<TIn, DV>), dim3(units, kBR), dim3(kBRThreads), 0, st, a);
     return hipGetLastError();
 }
 
