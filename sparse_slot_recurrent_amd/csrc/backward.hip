@@ -803,17 +803,20 @@ __device__ __forceinline__ void store_cpl(TS *p, const float (&x)[CPL]) {
 //     with the key slot << 32 | t << 7 | read << 6 | k and sorted (bitonic
 //     network): a slot's events end up together, in forward order (a
 //     token's writes before its reads, writes in address order);
-//   * one group of kRowLanes lanes per slot walks its events with the slot's
-//     row and mass (the replay, forwards: the row and mass before each write
-//     and the row at each read are recorded) or its adjoint dS and dm (the
-//     adjoint, backwards) in registers; the per-event inputs (weights,
-//     gamma, v, dr, the recorded rows) are gathered by token.
+//   * one group of lanes per slot (kBRLanes) walks its events with the
+//     slot's row and mass (the replay, forwards: the row and mass before each
+//     write and the row at each read are recorded) or its adjoint dS and dm
+//     (the adjoint, backwards) in registers; an event's inputs (weights,
+//     gamma, v, dr, the recorded row and mass) are gathered by token, all
+//     requested before any is used.
 // An event whose slot is outside [0, M) belongs to no range: the workgroup of
 // range k mod kBR writes its zero records or gradients.
 constexpr int kBR = 8;
 constexpr int kBRThreads = 1024;
-constexpr int kBRGroups = kBRThreads / kRowLanes;
-constexpr int kBRCap = 2048;  // events of a chunk (writes and reads)
+// lanes per row in the walk: 8 at d_v 64 (8 channels each), else 16
+template <int DV> constexpr int kBRLanes = DV == 64 ? 8 : kRowLanes;
+constexpr int kBRCap = 4096;  // events of a chunk (writes and reads)
+constexpr int kBRPer = kBRCap / kBRThreads;  // list positions per thread in the segment scan
 
 __host__ __device__ inline int br_chunk(int K) {
     int c = 64;
@@ -876,15 +879,16 @@ __device__ __forceinline__ void br_group(const BwdArgs &a, BRLds &g, int b, int 
             __syncthreads();
         }
     }
-    // segment starts, in list order: thread i takes positions 2i, 2i + 1
-    int f[2];
+    // segment starts, in list order: thread i takes positions kBRPer i ..
+    int f[kBRPer], nf = 0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = 2 * tid + q;
+    for (int q = 0; q < kBRPer; ++q) {
+        const int i = kBRPer * tid + q;
         f[q] = i < n && (i == 0 || (g.key[i] >> 32) != (g.key[i - 1] >> 32)) ? 1 : 0;
+        nf += f[q];
     }
     const int lane = tid % kWave, wid = tid / kWave;
-    int incl = f[0] + f[1];
+    int incl = nf;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int y = __shfl_up(incl, off, kWave);
@@ -898,10 +902,10 @@ __device__ __forceinline__ void br_group(const BwdArgs &a, BRLds &g, int b, int 
         base += w < wid ? c : 0;
         tot += c;
     }
-    int at = base + incl - (f[0] + f[1]);
+    int at = base + incl - nf;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        if (f[q]) g.seg[at] = 2 * tid + q;
+    for (int q = 0; q < kBRPer; ++q) {
+        if (f[q]) g.seg[at] = kBRPer * tid + q;
         at += f[q];
     }
     if (tid == 0) {
@@ -913,12 +917,12 @@ __device__ __forceinline__ void br_group(const BwdArgs &a, BRLds &g, int b, int 
 
 template <typename TIn, typename TS, int DV>
 __global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a) {
-    constexpr int CPL = DV / kRowLanes;
+    constexpr int LPR = kBRLanes<DV>, CPL = DV / LPR, kBRGroups = kBRThreads / LPR;
     __shared__ BRLds g;
     const int unit = blockIdx.x, r = blockIdx.y, b = unit / a.H, h = unit % a.H;
     const int K = a.K, T = a.T;
     const int64_t M = a.M;
-    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
+    const int grp = threadIdx.x / LPR, gl = threadIdx.x % LPR, c0 = gl * CPL;
     const int glead = (threadIdx.x % kWave) - gl;
     const int C = br_chunk(K);
     TS *Su = static_cast<TS *>(a.Sw) + static_cast<int64_t>(unit) * M * DV;
@@ -950,17 +954,20 @@ __global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a)
                     store_cpl<float, CPL>(a.rec_r + rec * DV + c0, x);
                     continue;
                 }
-                store_cpl<float, CPL>(a.rec_w + rec * DV + c0, x);
-                if (gl == 0) a.rec_m[rec] = m;
+                // the event's inputs, all requested before any is used
                 const int64_t th = (static_cast<int64_t>(b) * T + t0 + t) * a.H + h;
                 const float w = a.w_wt[th * K + k];
+                const TIn gt = gam[th];
+                float vr[CPL];
+                load_cpl<TIn, CPL>(vin + th * DV + c0, vr);
+                store_cpl<float, CPL>(a.rec_w + rec * DV + c0, x);
+                if (gl == 0) a.rec_m[rec] = m;
                 if (w > 0.f) {
-                    const float alpha = retention(w, expf(to_f32(gam[th])));
+                    const float alpha = retention(w, expf(to_f32(gt)));
                     m = fmaf(alpha, m, w);
                     const float lam = w / (m + a.eps_gsu);
-                    const TIn *vr = vin + th * DV + c0;
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) x[c] = stored<TS>(fmaf(lam, to_f32(vr[c]) - x[c], x[c]));
+                    for (int c = 0; c < CPL; ++c) x[c] = stored<TS>(fmaf(lam, vr[c] - x[c], x[c]));
                 }
             }
             store_cpl<TS, CPL>(row, x);
@@ -972,12 +979,12 @@ __global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a)
 
 template <typename TIn, int DV>
 __global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a) {
-    constexpr int CPL = DV / kRowLanes;
+    constexpr int LPR = kBRLanes<DV>, CPL = DV / LPR, kBRGroups = kBRThreads / LPR;
     __shared__ BRLds g;
     const int unit = blockIdx.x, r = blockIdx.y, b = unit / a.H, h = unit % a.H;
     const int K = a.K, T = a.T;
     const int64_t M = a.M;
-    const int grp = threadIdx.x / kRowLanes, gl = threadIdx.x % kRowLanes, c0 = gl * CPL;
+    const int grp = threadIdx.x / LPR, gl = threadIdx.x % LPR, c0 = gl * CPL;
     const int glead = (threadIdx.x % kWave) - gl;
     const int C = br_chunk(K);
     float *dSu = a.dS0 + static_cast<int64_t>(unit) * M * DV;
@@ -1017,24 +1024,26 @@ __global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a
                 }
                 const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
                 float *dvk = a.dvk + rec * DV + c0;
+                // the event's inputs, all requested before any is used
                 const float w = a.w_wt[th * K + k];
+                float sm[CPL];
+                load_cpl<float, CPL>(a.rec_w + rec * DV + c0, sm);
+                float vr[CPL];
+                load_cpl<TIn, CPL>(vin + th * DV + c0, vr);
+                const float mm = a.rec_m[rec];
+                const TIn gt = gam[th];
                 float dw = 0.f, dgk = 0.f;
                 if (w > 0.f) {
-                    float sm[CPL];
-                    load_cpl<float, CPL>(a.rec_w + rec * DV + c0, sm);
-                    const TIn *vr = vin + th * DV + c0;
-                    const float mm0 = gl == 0 ? a.rec_m[rec] : 0.f;
-                    const float mm = __shfl(mm0, glead, kWave);
-                    const float eg = expf(to_f32(gam[th]));
+                    const float eg = expf(to_f32(gt));
                     const float alpha = retention(w, eg);
                     const float mp = fmaf(alpha, mm, w);
                     const float den = mp + a.eps_gsu;
                     const float lam = w / den;
                     float dl = 0.f;
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) dl = fmaf(d[c], to_f32(vr[c]) - sm[c], dl);
+                    for (int c = 0; c < CPL; ++c) dl = fmaf(d[c], vr[c] - sm[c], dl);
 #pragma unroll
-                    for (int o = 1; o < kRowLanes; o <<= 1) dl += __shfl_xor(dl, o, kWave);
+                    for (int o = 1; o < LPR; o <<= 1) dl += __shfl_xor(dl, o, kWave);
                     float dv[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) {
