@@ -11,7 +11,10 @@ Default: the headline is the largest single-GPU workload, the 4^8-slot
 prefill (large_state: B 2, T 32768, H 16, K 32); the line carries the other
 workloads as sub-records ("subrecords"), each the whole call with its own
 roofline and CPU baseline: the Top-8 and Top-32 prefills (--steps calls
-each) and the decode workload (1024 dependent steps in one HIP graph).
+each) and the decode workload (1024 dependent steps in one HIP graph), then
+the rows beyond the five configurations: the 4^8-slot backward
+(backward_large_state) and the decoding workload on a tiered state
+(decode_tiered).
 Device peaks are measured first (a 256 MiB copy, an LDS read probe) and
 every roofline fraction is given against both the vendor's figure and the
 measured one.
@@ -49,6 +52,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 LDS_PEAK_GBS = 128 * 256 * 2.4
 HEADLINE = "large_state"
 SUBRECORDS = ("prefill_top8", "prefill_top32", "decode")
+# (workload, steps, warmup) of the records beyond the five configurations
+EXTRA_SUBRECORDS = (("backward_large_state", 3, 1), ("decode_tiered", 256, 8))
 
 
 
@@ -737,6 +742,48 @@ def measure_workload(torch, rn, name, steps, warmup, peaks, cpu: bool):
     return rec
 
 
+def measure_extra(torch, rn, name, steps, warmup):
+    """A record for a workload beyond the five configurations: a whole layer
+    (layer_*), a backward pass (backward_*) or the tiered decoding state
+    (decode_tiered)."""
+    from sparse_slot_recurrent_amd import synth
+    backward, tiered = name in BACKWARD, name in TIERED
+    d_model = None
+    if backward:
+        w = synth.WORKLOADS[BACKWARD[name]]
+    elif tiered:
+        w = synth.WORKLOADS[TIERED[name][0]]
+    else:
+        base, d_model = LAYERS[name]
+        w = synth.WORKLOADS[base]
+    kind = "decode" if w.steps else "prefill"
+    extra = {}
+    if tiered:
+        _, den, every = TIERED[name]
+        ms, kms, tokens, extra = bench_decode_tiered(torch, rn, w, den, every, steps, warmup)
+        hl = host_link_peaks(torch, rn)
+        a = extra["host_link_bytes_per_step"] / (kms["step_tiered"] / 1e3) / 1e9
+        peak = min(hl["host_read_gbs"], hl["host_write_gbs"])
+        roof = {"bound": "host_link", "kernel": "step_tiered", "achieved": a, "peak": peak,
+                "unit": "GB/s", "frac": a / peak, "traffic": None, "host_link": hl}
+    elif backward:
+        ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
+        bw = backward_model(w)
+        extra["backward_model"] = bw
+        a = bw["backward"] / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "backward", "achieved": a, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
+                "with_records_gbs": (bw["backward"] + bw["records"]) / (ms / 1e3) / 1e9}
+    else:
+        ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
+        roof = layer_roofline(w, d_model, kind, kms, ms, extra)
+    rec = {"workload": name, "value": tokens / (ms / 1e3), "unit": "tokens/s",
+           "ms_per_step": ms, "steps": steps, "config": workload_config(name, w, kind),
+           "roofline": roof, "kernels_ms": kms}
+    rec.update(extra)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -796,30 +843,7 @@ def main():
     peaks = {} if single else measure_peaks(torch)
     line = {"metric": METRIC}
     if backward or tiered or d_model is not None:
-        extra = {}
-        if tiered:
-            _, den, every = TIERED[name]
-            ms, kms, tokens, extra = bench_decode_tiered(torch, rn, w, den, every, steps, warmup)
-            hl = host_link_peaks(torch, rn)
-            a = extra["host_link_bytes_per_step"] / (kms["step_tiered"] / 1e3) / 1e9
-            peak = min(hl["host_read_gbs"], hl["host_write_gbs"])
-            roof = {"bound": "host_link", "kernel": "step_tiered", "achieved": a, "peak": peak,
-                    "unit": "GB/s", "frac": a / peak, "traffic": None, "host_link": hl}
-        elif backward:
-            ms, kms, tokens, extra = bench_backward(torch, rn, w, steps, warmup)
-            bw = backward_model(w)
-            extra["backward_model"] = bw
-            a = bw["backward"] / (ms / 1e3) / 1e9
-            roof = {"bound": "hbm", "kernel": "backward", "achieved": a, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": a / HBM_PEAK_GBS, "traffic": None,
-                    "with_records_gbs": (bw["backward"] + bw["records"]) / (ms / 1e3) / 1e9}
-        else:
-            ms, kms, tokens, extra = bench_layer(torch, rn, w, d_model, steps, warmup)
-            roof = layer_roofline(w, d_model, kind, kms, ms, extra)
-        rec = {"workload": name, "value": tokens / (ms / 1e3), "unit": "tokens/s",
-               "ms_per_step": ms, "config": workload_config(name, w, kind), "roofline": roof,
-               "kernels_ms": kms}
-        rec.update(extra)
+        rec = measure_extra(torch, rn, name, steps, warmup)
     else:
         rec = measure_workload(torch, rn, name, steps, warmup, peaks, cpu)
         steps = rec["steps"]
@@ -842,6 +866,9 @@ def main():
     if not single and not args.no_subrecords:
         line["subrecords"] = [measure_workload(torch, rn, n, steps if n != "decode" else None,
                                                warmup, peaks, cpu) for n in SUBRECORDS]
+        # rows beyond the five configurations: the 4^8-slot backward and the
+        # tiered decoding state, a few steps each
+        line["subrecords"] += [measure_extra(torch, rn, n, st, wu) for n, st, wu in EXTRA_SUBRECORDS]
     print(json.dumps(line), flush=True)
 
 
