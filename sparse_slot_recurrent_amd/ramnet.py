@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 from typing import NamedTuple, Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -435,9 +436,10 @@ class TieredState:
         nbytes = S.numel() * S.element_size()
         ptr = C.c_void_p()
         _raise(lib.ramnet_host_alloc(nbytes, C.byref(ptr)))
-        self._host_ptr = ptr.value
-        self._free = lib.ramnet_host_free
         raw = (C.c_uint8 * max(nbytes, 1)).from_address(ptr.value)
+        # freed once the buffer is unreachable: S_host and every view of it
+        # keep it alive, so none of them outlives the memory
+        weakref.finalize(raw, _free_host, lib.ramnet_host_free, ptr.value)
         self.S_host = torch.frombuffer(raw, dtype=torch.uint8)[:nbytes].view(S.dtype).view(S.shape)
         self.S_host.copy_(S)
         self.cache = torch.empty((B, H, self.C, d_v), dtype=S.dtype, device=dev)
@@ -445,17 +447,17 @@ class TieredState:
         self.slot_line = torch.empty((B, H, M), dtype=torch.int32, device=dev)
         self.hits = torch.empty((B, H, M), dtype=torch.int32, device=dev)  # uint32 in C
 
-    def __del__(self):
-        ptr, self._host_ptr = getattr(self, "_host_ptr", None), None
-        if ptr:
-            try:
-                _torch().cuda.synchronize()
-            finally:
-                self._free(C.c_void_p(ptr))
-
     def struct(self) -> TieredStateC:
         return TieredStateC(C.c_void_p(self.S_host.data_ptr()), _ptr(self.cache),
                             _ptr(self.line_slot), _ptr(self.slot_line), _ptr(self.hits), self.C)
+
+
+def _free_host(free, ptr):
+    """Frees pinned host memory of a tiered state once no kernel can use it."""
+    try:
+        _torch().cuda.synchronize()
+    finally:
+        free(C.c_void_p(ptr))
 
 
 def _tier_call(name, p: Params, ts: TieredState):
