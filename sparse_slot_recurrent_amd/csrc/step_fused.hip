@@ -29,7 +29,8 @@
 //    taken from the rows as they were before this token's writes, plus, for
 //    each write slot, the read's weight on that slot times the change the
 //    write made; this equals the read after the writes without a second
-//    pass over memory.  Every load is consumed before the first store.  The
+//    pass over memory (non-temporal: a row piece is touched once per step).
+//    Every load is consumed before the first store.  The
 //    sub-row partial reads are summed through LDS; RMSNorm over d_v by a
 //    wave reduction; the gate.
 //  * Tiered state (TIER): the rows live in host memory except each unit's
@@ -211,6 +212,31 @@ template <int NW>
 struct alignas(NW == 4 ? 16 : 4) Words {
     uint32_t w[NW];
 };
+
+typedef unsigned int ntu32x4 __attribute__((ext_vector_type(4)));
+// Row pieces are touched once per step: loads and stores that do not keep
+// them in the caches.
+template <int NW>
+__device__ __forceinline__ Words<NW> nt_load(const void *p) {
+    if constexpr (NW == 4) {
+        const ntu32x4 v = __builtin_nontemporal_load(static_cast<const ntu32x4 *>(p));
+        Words<NW> x;
+        x.w[0] = v.x; x.w[1] = v.y; x.w[2] = v.z; x.w[3] = v.w;
+        return x;
+    } else {
+        return *static_cast<const Words<NW> *>(p);
+    }
+}
+template <int NW>
+__device__ __forceinline__ void nt_store(void *p, const Words<NW> &x) {
+    if constexpr (NW == 4) {
+        ntu32x4 v;
+        v.x = x.w[0]; v.y = x.w[1]; v.z = x.w[2]; v.w = x.w[3];
+        __builtin_nontemporal_store(v, static_cast<ntu32x4 *>(p));
+    } else {
+        *static_cast<Words<NW> *>(p) = x;
+    }
+}
 
 template <typename TS, int NW>
 __device__ __forceinline__ void unpack(const Words<NW> &x, float *f) {
@@ -458,8 +484,8 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
                 for (int j = 0; j < NJ; ++j) {
                     const int k = j * RPI + sub;
                     if (k < K) {
-                        wrow[i][j] = *reinterpret_cast<const Words<NW> *>(row_of(ul, 0, k) + c0);
-                        rrow[i][j] = *reinterpret_cast<const Words<NW> *>(row_of(ul, 1, k) + c0);
+                        wrow[i][j] = nt_load<NW>(row_of(ul, 0, k) + c0);
+                        rrow[i][j] = nt_load<NW>(row_of(ul, 1, k) + c0);
                     }
                 }
                 const int un = u0 + ul;
@@ -523,7 +549,7 @@ __global__ __launch_bounds__(kWave) void step_fused_kernel(StepArgs a) {
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) y[c] = fmaf(lam, vin[i][c] - x[c], x[c]);
                         const Words<NW> nw = pack<TS, NW>(y);
-                        *reinterpret_cast<Words<NW> *>(row_of(ul, 0, k) + c0) = nw;
+                        nt_store<NW>(row_of(ul, 0, k) + c0, nw);
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) acc[c] = fmaf(cr, y[c] - x[c], acc[c]);
                     }
