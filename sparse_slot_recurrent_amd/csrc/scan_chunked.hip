@@ -884,6 +884,33 @@ struct alignas(4 * sizeof(T)) Quad {
     T e[4];
 };
 
+// Four read sums in, four outputs out, each touched once: non-temporal.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ Quad<float> nt_load_quad(const float *p) {
+    const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p));
+    Quad<float> q;
+    q.e[0] = v.x;
+    q.e[1] = v.y;
+    q.e[2] = v.z;
+    q.e[3] = v.w;
+    return q;
+}
+__device__ __forceinline__ void nt_store_quad(float *p, const Quad<float> &q) {
+    nt_f32x4 v;
+    v.x = q.e[0];
+    v.y = q.e[1];
+    v.z = q.e[2];
+    v.w = q.e[3];
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_f32x4 *>(p));
+}
+__device__ __forceinline__ void nt_store_quad(bf16_t *p, const Quad<bf16_t> &q) {
+    nt_u32x2 v;
+    v.x = static_cast<uint32_t>(q.e[0].bits) | (static_cast<uint32_t>(q.e[1].bits) << 16);
+    v.y = static_cast<uint32_t>(q.e[2].bits) | (static_cast<uint32_t>(q.e[3].bits) << 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x2 *>(p));
+}
+
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g), four channels per
 // thread; the per-token square sums of the channel slices are added in
 // slice order.  With an fp32 output, r is held in `out` itself (rbuf ==
@@ -909,7 +936,7 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *rbuf,
     for (int j = 0; j < ncg; ++j) tot += sumsq[th * ncg + j];
     const float den = tot / static_cast<float>(d_v) + eps;
     const float inv = den > 0.f ? 1.0f / sqrtf(den) : 0.f;  // zero read, eps 0
-    const Quad<float> r = *reinterpret_cast<const Quad<float> *>(rbuf + th * d_v + c0);
+    const Quad<float> r = nt_load_quad(rbuf + th * d_v + c0);
     const Quad<TIn> gv = *reinterpret_cast<const Quad<TIn> *>(g + (th / H) * ld_g + (th % H) * d_v + c0);
     Quad<TO> o;
 #pragma unroll
@@ -917,7 +944,7 @@ __global__ __launch_bounds__(256) void rms_gate_kernel(const float *rbuf,
         const float om = norm_w ? norm_w[c0 + j] : 1.0f;
         o.e[j] = from_f32<TO>(r.e[j] * inv * om * sigmoid(to_f32(gv.e[j])));
     }
-    *reinterpret_cast<Quad<TO> *>(out + th * d_v + c0) = o;
+    nt_store_quad(out + th * d_v + c0, o);
 }
 
 template <typename K>

@@ -1060,27 +1060,34 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
 }
 
 // Four consecutive partial-read channels as fp32 (8 bytes of fp16, 16 of
-// fp32), and four outputs stored at once.
+// fp32), and four outputs stored at once; both are touched once, so the
+// accesses are non-temporal.
 __device__ __forceinline__ void load4p(const _Float16 *p, float (&x)[4]) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    const uint2 u = make_uint2(v.x, v.y);
     const _Float16 *h = reinterpret_cast<const _Float16 *>(&u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = static_cast<float>(h[i]);
 }
+typedef float ntf32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void load4p(const float *p, float (&x)[4]) {
-    const float4 f = *reinterpret_cast<const float4 *>(p);
+    const ntf32x4 f = __builtin_nontemporal_load(reinterpret_cast<const ntf32x4 *>(p));
     x[0] = f.x;
     x[1] = f.y;
     x[2] = f.z;
     x[3] = f.w;
 }
 __device__ __forceinline__ void store4(float *p, const float (&x)[4]) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    ntf32x4 f;
+    f.x = x[0]; f.y = x[1]; f.z = x[2]; f.w = x[3];
+    __builtin_nontemporal_store(f, reinterpret_cast<ntf32x4 *>(p));
 }
 __device__ __forceinline__ void store4(bf16_t *p, const float (&x)[4]) {
     const uint32_t w0 = static_cast<uint32_t>(bf16_rne(x[0]).bits) | (static_cast<uint32_t>(bf16_rne(x[1]).bits) << 16);
     const uint32_t w1 = static_cast<uint32_t>(bf16_rne(x[2]).bits) | (static_cast<uint32_t>(bf16_rne(x[3]).bits) << 16);
-    *reinterpret_cast<uint2 *>(p) = make_uint2(w0, w1);
+    u32x2 v;
+    v.x = w0; v.y = w1;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
 }
 
 // out = r / sqrt(mean(r^2) + eps) * omega * sigmoid(g) with r the sum of the
