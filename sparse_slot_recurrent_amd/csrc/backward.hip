@@ -755,6 +755,32 @@ __global__ __launch_bounds__(1024) void bwd_omega_kernel(const float *part, int 
 // channels each (fp32, or bf16 in 8-byte pieces).
 constexpr int kRowLanes = 16;
 
+typedef float bnt_f32x4 __attribute__((ext_vector_type(4)));
+// fp32 records, written once and read once: non-temporal
+template <int CPL>
+__device__ __forceinline__ void nt_load_rec(const float *p, float (&x)[CPL]) {
+#pragma unroll
+    for (int j = 0; j < CPL / 4; ++j) {
+        const bnt_f32x4 f = __builtin_nontemporal_load(reinterpret_cast<const bnt_f32x4 *>(p) + j);
+        x[4 * j] = f.x;
+        x[4 * j + 1] = f.y;
+        x[4 * j + 2] = f.z;
+        x[4 * j + 3] = f.w;
+    }
+}
+template <int CPL>
+__device__ __forceinline__ void nt_store_rec(float *p, const float (&x)[CPL]) {
+#pragma unroll
+    for (int j = 0; j < CPL / 4; ++j) {
+        bnt_f32x4 f;
+        f.x = x[4 * j];
+        f.y = x[4 * j + 1];
+        f.z = x[4 * j + 2];
+        f.w = x[4 * j + 3];
+        __builtin_nontemporal_store(f, reinterpret_cast<bnt_f32x4 *>(p) + j);
+    }
+}
+
 template <typename TS, int CPL>
 __device__ __forceinline__ void load_cpl(const TS *p, float (&x)[CPL]) {
     if constexpr (sizeof(TS) == 4) {
@@ -951,7 +977,7 @@ __global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a)
                 const int t = ek >> 7, k = ek & 63;
                 const int64_t rec = (static_cast<int64_t>(unit) * T + t0 + t) * K + k;
                 if (ek & 64) {
-                    store_cpl<float, CPL>(a.rec_r + rec * DV + c0, x);
+                    nt_store_rec<CPL>(a.rec_r + rec * DV + c0, x);
                     continue;
                 }
                 // the event's inputs, all requested before any is used
@@ -960,7 +986,7 @@ __global__ __launch_bounds__(kBRThreads) void bwd_record_range_kernel(BwdArgs a)
                 const TIn gt = gam[th];
                 float vr[CPL];
                 load_cpl<TIn, CPL>(vin + th * DV + c0, vr);
-                store_cpl<float, CPL>(a.rec_w + rec * DV + c0, x);
+                nt_store_rec<CPL>(a.rec_w + rec * DV + c0, x);
                 if (gl == 0) a.rec_m[rec] = m;
                 if (w > 0.f) {
                     const float alpha = retention(w, expf(to_f32(gt)));
@@ -1027,7 +1053,7 @@ __global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a
                 // the event's inputs, all requested before any is used
                 const float w = a.w_wt[th * K + k];
                 float sm[CPL];
-                load_cpl<float, CPL>(a.rec_w + rec * DV + c0, sm);
+                nt_load_rec<CPL>(a.rec_w + rec * DV + c0, sm);
                 float vr[CPL];
                 load_cpl<TIn, CPL>(vin + th * DV + c0, vr);
                 const float mm = a.rec_m[rec];
@@ -1050,7 +1076,7 @@ __global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a
                         dv[c] = lam * d[c];
                         d[c] *= 1.0f - lam;
                     }
-                    store_cpl<float, CPL>(dvk, dv);
+                    nt_store_rec<CPL>(dvk, dv);
                     const float dmt = dm - dl * w / (den * den);
                     const float dalpha = dmt * mm;
                     dw = dl / den + dmt;
@@ -1063,7 +1089,7 @@ __global__ __launch_bounds__(kBRThreads) void bwd_adjoint_range_kernel(BwdArgs a
                     float z[CPL];
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) z[c] = 0.f;
-                    store_cpl<float, CPL>(dvk, z);
+                    nt_store_rec<CPL>(dvk, z);
                 }
                 if (gl == 0) {
                     a.dgk[rec] = dgk;
