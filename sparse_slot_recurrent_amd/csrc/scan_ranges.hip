@@ -961,12 +961,23 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
             auto store = [&](int t, int q, const float (&acc)[4]) {
                 const int64_t th = th_unit + static_cast<int64_t>(t0 + t) * a.H;
                 TP *dst = reinterpret_cast<TP *>(a.partial) + (th * kR + r) * d_v + 4 * q;
+                // (read once, by the gate: non-temporal)
                 if constexpr (std::is_same_v<TP, float>) {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    typedef float pf32x4 __attribute__((ext_vector_type(4)));
+                    pf32x4 v;
+                    v.x = acc[0];
+                    v.y = acc[1];
+                    v.z = acc[2];
+                    v.w = acc[3];
+                    __builtin_nontemporal_store(v, reinterpret_cast<pf32x4 *>(dst));
                 } else {
                     const _Float16 hv[4] = {static_cast<_Float16>(acc[0]), static_cast<_Float16>(acc[1]),
                                             static_cast<_Float16>(acc[2]), static_cast<_Float16>(acc[3])};
-                    *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, hv);
+                    const uint2 u = __builtin_bit_cast(uint2, hv);
+                    u32x2 v;
+                    v.x = u.x;
+                    v.y = u.y;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(dst));
                 }
             };
             for (int tb = 0; tb < Cc; tb += TPP) {
