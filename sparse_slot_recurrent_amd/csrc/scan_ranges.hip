@@ -736,19 +736,20 @@ __global__ __launch_bounds__(kRT) void scan_range_kernel(ChunkArgs a) {
                 pf_v[j] = reinterpret_cast<const uint32_t *>(v + static_cast<int64_t>(t0 + min(t, Cc - 1)) * a.ld_v)[vcol];
         }
     };
+    // the event lists are read once, here: non-temporal loads
     auto load_lists = [&](int c, const Hdr &hd) {
         const unsigned char *rec = rec_of(c);
 #pragma unroll
         for (int j = 0; j < kLW; ++j) {
             const int i = tid + j * kRT;
             if (i < min(hd.nw(), CAPW)) {
-                pf_wtv[j] = reinterpret_cast<const int *>(rec + P.o_wtv)[hd.wb + i];
-                pf_ww[j] = reinterpret_cast<const float *>(rec + P.o_ww)[hd.wb + i];
-                pf_wa[j] = reinterpret_cast<const float *>(rec + P.o_wa)[hd.wb + i];
+                pf_wtv[j] = __builtin_nontemporal_load(reinterpret_cast<const int *>(rec + P.o_wtv) + hd.wb + i);
+                pf_ww[j] = __builtin_nontemporal_load(reinterpret_cast<const float *>(rec + P.o_ww) + hd.wb + i);
+                pf_wa[j] = __builtin_nontemporal_load(reinterpret_cast<const float *>(rec + P.o_wa) + hd.wb + i);
             }
             if (i < min(hd.nr(), CAPR)) {
-                pf_rv[j] = reinterpret_cast<const int *>(rec + P.o_rv)[hd.rb + i];
-                pf_rr[j] = reinterpret_cast<const float *>(rec + P.o_rr)[hd.rb + i];
+                pf_rv[j] = __builtin_nontemporal_load(reinterpret_cast<const int *>(rec + P.o_rv) + hd.rb + i);
+                pf_rr[j] = __builtin_nontemporal_load(reinterpret_cast<const float *>(rec + P.o_rr) + hd.rb + i);
             }
         }
         if (tid <= C) pf_rt = reinterpret_cast<const int *>(rec + P.o_rt)[r * (C + 1) + tid];
