@@ -428,7 +428,8 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
 
     // ---- 6. the record: header, per-range token offsets of the reads,
     //         entries, then writes and reads staged in LDS in list order and
-    //         stored with consecutive lanes on consecutive words
+    //         stored with consecutive lanes on consecutive words (non-temporal:
+    //         the scan reads the record once, long after)
     if (tid == 0) {
         RangeHdr hd;
         for (int r = 0; r <= kR; ++r) {
@@ -441,16 +442,16 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     }
     for (int i = tid; i < kR * (C + 1); i += kPRT) {
         const int r = i / (C + 1), t = i - r * (C + 1);
-        rtoff[i] = rt[r * C + t] - rt[r * C];  // t == C: the next range's start (or nrd)
+        __builtin_nontemporal_store(rt[r * C + t] - rt[r * C], rtoff + i);  // t == C: the next range's start (or nrd)
     }
     for (int eid = tid; eid < nt; eid += kPRT) {
         int r = 0;
 #pragma unroll
         for (int q = 1; q < kR; ++q) r += eid >= rs0[q] ? 1 : 0;
         const int g = ewo[eid] + eid;
-        ent_wo[eid] = ewo[eid];
+        __builtin_nontemporal_store(ewo[eid], ent_wo + eid);
         const int x0 = need[g + 1] > need[g] ? need[g] - vb[r] : -1;
-        ent_nx[eid] = (ewo[eid + 1] - ewo[eid]) | ((x0 + 1) << 16);
+        __builtin_nontemporal_store((ewo[eid + 1] - ewo[eid]) | ((x0 + 1) << 16), ent_nx + eid);
     }
     // reads: list position and (range-local version row, weight).  A read's
     // rank among its token's reads of the same range: where K divides the
@@ -498,9 +499,9 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     }
     lds_barrier();
     for (int i = tid; i < nwt; i += kPRT) {
-        wtv[i] = bk[i];
-        ww[i] = __int_as_float(sk[i]);
-        wa[i] = __int_as_float(sa[i]);
+        __builtin_nontemporal_store(bk[i], wtv + i);
+        __builtin_nontemporal_store(__int_as_float(sk[i]), ww + i);
+        __builtin_nontemporal_store(__int_as_float(sa[i]), wa + i);
     }
     lds_barrier();
 #pragma unroll
@@ -512,8 +513,8 @@ __global__ __launch_bounds__(kPRT) void plan_range_kernel(ChunkArgs a) {
     }
     lds_barrier();
     for (int i = tid; i < nrd; i += kPRT) {
-        rv[i] = bk[i];
-        rr[i] = __int_as_float(sk[i]);
+        __builtin_nontemporal_store(bk[i], rv + i);
+        __builtin_nontemporal_store(__int_as_float(sk[i]), rr + i);
     }
     // the LDS tables are set up again for the next item
     lds_barrier();
