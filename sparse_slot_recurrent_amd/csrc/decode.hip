@@ -269,18 +269,47 @@ constexpr int kMaxBand = 16;
 // The fixed-point path serves U <= kMaxUFix levels.
 constexpr int kMaxUFix = 16;
 
-// The fixed-point search of one address (KC <= 32).  bkl: this lane's beam,
-// entry r at bkl[r * 64] (KC + 1 entries: the beam and its sentinel).  The
+// A lane's beam in LDS (KC + 1 entries: the beam and its sentinel), entry r
+// of lane l at index r * 64 + l.  Wide: 64-bit keys.  Narrow (every prefix
+// below 2^16, i.e. M <= 65536): the drops in a 32-bit array and the prefixes
+// in a 16-bit one after it, 6 bytes an entry instead of 8, so that 12 waves
+// fit a compute unit's LDS instead of 9.
+template <int KC, bool NARROW>
+struct Beam {
+    unsigned char *base;
+    int lane;
+    static constexpr size_t bytes() { return static_cast<size_t>(KC + 1) * kWave * (NARROW ? 6 : 8); }
+    __device__ __forceinline__ uint64_t ld(int r) const {
+        const int i = r * kWave + lane;
+        if constexpr (NARROW) {
+            const uint32_t t = reinterpret_cast<const uint32_t *>(base)[i];
+            const uint32_t px = reinterpret_cast<const uint16_t *>(base + (KC + 1) * kWave * 4)[i];
+            return mk_key(t, px);
+        } else {
+            return reinterpret_cast<const uint64_t *>(base)[i];
+        }
+    }
+    __device__ __forceinline__ void st(int r, uint64_t k) const {
+        const int i = r * kWave + lane;
+        if constexpr (NARROW) {
+            reinterpret_cast<uint32_t *>(base)[i] = key_t(k);
+            reinterpret_cast<uint16_t *>(base + (KC + 1) * kWave * 4)[i] = static_cast<uint16_t>(key_prefix(k));
+        } else {
+            reinterpret_cast<uint64_t *>(base)[i] = k;
+        }
+    }
+};
+
+// The fixed-point search of one address (KC <= 32), its beam in bkl.  The
 // result is left in `out` (keys, heaviest first), with the drop unit 2^e
 // (unit) and lnz, the sum of the levels' log(sum exp(l - max)) in fp64 (a
 // slot's weight is exp(-T unit - lnz)).  Where the logits span too many
 // binary orders for exact 32-bit drops, the drops are rounded and every cut
 // must clear the rounding error.  Returns false where that fails (a
 // near-tie within the error) or a logit is not finite.
-template <int DP, int KC, typename TIn>
-__device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, uint64_t *bkl,
+template <int DP, int KC, bool NARROW, typename TIn>
+__device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, Beam<KC, NARROW> bkl,
                                            uint64_t (&out)[KC], double &unit, double &lnz) {
-    constexpr int S = kWave;
     // the drop unit and the largest possible T, from every logit
     int e = 1 << 20;
     double tmax = 0.0;  // exact: a sum of at most kMaxUFix fp32 differences
@@ -311,8 +340,8 @@ __device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, uint64_t
     unit = __hiloint2double((1023 + e) << 20, 0);
 
     // the beam before the first digit: one entry of drop 0, prefix 0
-    bkl[0] = mk_key(0u, 0u);
-    bkl[S] = kSentinel;
+    bkl.st(0, mk_key(0u, 0u));
+    bkl.st(1, kSentinel);
     int nb = 1;
     for (int u = 0; u < U; ++u) {
         uint32_t dl[DP];
@@ -335,7 +364,7 @@ __device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, uint64_t
         uint64_t hk[DP];
         int hi[DP];
         {
-            const uint64_t k0 = bkl[0];
+            const uint64_t k0 = bkl.ld(0);
 #pragma unroll
             for (int d = 0; d < DP; ++d) {
                 hk[d] = extend<DP>(k0, dl[d], d);
@@ -360,7 +389,7 @@ __device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, uint64_t
                 bd = c[d] ? static_cast<uint32_t>(d) : bd;
             }
             const int ni = bi + 1;
-            const uint64_t nk = extend<DP>(bkl[ni * S], bdl, bd);
+            const uint64_t nk = extend<DP>(bkl.ld(ni), bdl, bd);
             bool later = false;
 #pragma unroll
             for (int d = DP - 1; d >= 0; --d) {
@@ -419,12 +448,12 @@ __device__ __forceinline__ bool search_fix(const TIn *lg, int U, int K, uint64_t
         if (u + 1 < U || near) {
 #pragma unroll
             for (int r = 0; r < KC; ++r)
-                if (r < nn) bkl[r * S] = out[r];
-            bkl[nn * S] = kSentinel;
+                if (r < nn) bkl.st(r, out[r]);
+            bkl.st(nn, kSentinel);
         }
         if (near && ok) {
             for (int r = nn - 1; r >= 0 && ok; --r) {
-                const uint64_t k = bkl[r * S];
+                const uint64_t k = bkl.ld(r);
                 if (key_t(k) + err < td) break;
                 if (r == nn - 1 - kMaxBand) {
                     ok = false;
@@ -540,10 +569,6 @@ template <int KC>
 constexpr size_t lds64_bytes() {
     return static_cast<size_t>(KC <= 32 ? 1 : 2) * KC * kWave * (sizeof(double) + sizeof(int32_t));
 }
-template <int KC>
-constexpr size_t ldsfix_bytes() {
-    return static_cast<size_t>(KC + 1) * kWave * sizeof(uint64_t);
-}
 
 // The fp64 search of address a and its stores.
 template <int DP, int KC, typename TIn>
@@ -580,8 +605,8 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeK d) {
 // is stored, the others are marked in the wave's failure word for the fp64
 // search.  Every wave of the grid has its lane 0 (a < n), which writes the
 // word.
-template <int DP, int KC, typename TIn>
-__global__ __launch_bounds__(kWave) void decode_fast_kernel(DecodeK d) {
+template <int DP, int KC, bool NARROW, typename TIn>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void decode_fast_kernel(DecodeK d) {
     extern __shared__ unsigned char smem[];
     const int lane = threadIdx.x;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
@@ -591,7 +616,7 @@ __global__ __launch_bounds__(kWave) void decode_fast_kernel(DecodeK d) {
     uint64_t out[KC];
     double unit, lnz;
     const TIn *lg = logits_of<TIn>(d, a, key, DP);
-    const bool ok = search_fix<DP, KC>(lg, d.U, d.K, reinterpret_cast<uint64_t *>(smem) + lane, out, unit, lnz);
+    const bool ok = search_fix<DP, KC>(lg, d.U, d.K, Beam<KC, NARROW>{smem, lane}, out, unit, lnz);
     if (ok) {
         // a slot's weight exp(-T - lnz), T = its drop (exact)
         write_address<DP, KC>(d, a, key, [&](int r, int &s, float &w) {
@@ -636,8 +661,12 @@ hipError_t launch_kc(const DecodeArgs &a, hipStream_t st) {
     hipError_t e;
     if constexpr (KC <= 32) {
         if (a.fails && a.in_bf16 && a.U <= kMaxUFix) {
-            constexpr size_t ldsfix = ldsfix_bytes<KC>();
-            auto fast = decode_fast_kernel<DP, KC, TIn>;
+            // every prefix of the beam is below d_p^U
+            int64_t span = 1;
+            for (int u = 0; u < a.U && span <= 65536; ++u) span *= a.d_p;
+            const bool narrow = span <= 65536;
+            const size_t ldsfix = narrow ? Beam<KC, true>::bytes() : Beam<KC, false>::bytes();
+            auto fast = narrow ? decode_fast_kernel<DP, KC, true, TIn> : decode_fast_kernel<DP, KC, false, TIn>;
             if ((e = set_lds(fast, ldsfix)) != hipSuccess) return e;
             hipLaunchKernelGGL(fast, grid, dim3(kWave), ldsfix, st, d);
             if ((e = hipGetLastError()) != hipSuccess) return e;
